@@ -1,0 +1,194 @@
+/*
+ * qli.h -- C ABI of the quantized lightning indexer for AMD MI355X (gfx950).
+ *
+ * The operation is the one defined on the EngineX-Ascend page
+ * "VllmQuantLightningIndexer" (csrc/attention/vllm_quant_lightning_indexer/
+ * README.md; cited below as QLI-README with its section headings):
+ *
+ *   out = Top-k{ [1]_{1xg} @ [ (W @ [1]_{1xSk}) (.) ReLU( (ScaleQ @ ScaleK^T)
+ *                                                  (.) (Q_index @ K_index^T) ) ] }
+ *   (QLI-README, section 功能说明, formula and steps 1-3)
+ *
+ * For every query token (row) and every key entry it may see, the score is
+ *   score[r][j] = sum_{g<64} W[r][g] * max(0, ScaleQ[r][g] * ScaleK[j] * dot(Q[r][g], K[j]))
+ * and the row returns the indices of its sparse_count highest scores.
+ *
+ * Two calls, as on the page (metadata op, then indexer op):
+ *   qli_plan  host only: validates the scalar problem and the sequence
+ *             lengths and writes a work-split plan (our replacement for the
+ *             page's int32[1024] metadata, QLI-README 参数说明 "metadata").
+ *   qli_run   stream-ordered GPU execution of the whole hot path.
+ *
+ * Conventions for every entry point:
+ *   - All buffers are owned by the caller.  The library allocates no device
+ *     memory and keeps no state between calls; calls are thread-safe.
+ *   - Device pointers are plain HIP device addresses; "stream" is a
+ *     hipStream_t passed as void* (NULL = the default stream).
+ *   - Every scalar argument is validated before anything is launched; a
+ *     violation returns a distinct qli_status and touches nothing.
+ *   - Device-resident data (tensor contents, block_table entries) is not
+ *     validated.  Out-of-contract values (NaN/Inf inputs, negative or
+ *     non-finite dequant scales, block ids outside [0, num_blocks)) give
+ *     undefined results, as the page leaves NaN ordering undefined
+ *     (QLI-README 约束说明).
+ *   - No C++ exception crosses the ABI.
+ */
+#ifndef QLI_H
+#define QLI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+typedef enum qli_status {
+    QLI_OK = 0,
+    QLI_ERR_ARG = 1,         /* an argument breaks a constraint of the page or of this ABI */
+    QLI_ERR_UNSUPPORTED = 2, /* allowed by the page on some hardware, not supported here */
+    QLI_ERR_SIZE = 3,        /* a caller buffer is too small, or a size overflows */
+    QLI_ERR_HIP = 4,         /* the HIP runtime reported an error (launch, device) */
+    QLI_ERR_PLAN = 5         /* the plan does not belong to this problem or is corrupt */
+} qli_status;
+
+/* query / key element type (QLI-README 参数说明: INT8, FLOAT8_e4m3fn). */
+typedef enum qli_qk_dtype { QLI_QK_INT8 = 0, QLI_QK_FP8_E4M3FN = 1 } qli_qk_dtype;
+/* weights / dequant-scale element type (QLI-README 参数说明: FLOAT16, FLOAT32).
+ * Pairings accepted (the page's per-product notes): INT8 with FLOAT16 and
+ * FLOAT8_e4m3fn with FLOAT32; other mixes return QLI_ERR_UNSUPPORTED. */
+typedef enum qli_scale_dtype { QLI_SCALE_F16 = 0, QLI_SCALE_F32 = 1 } qli_scale_dtype;
+/* layout_query (QLI-README 参数说明: BSND or TND).  layout_key is always
+ * PA_BSND (paged). */
+typedef enum qli_layout { QLI_LAYOUT_BSND = 0, QLI_LAYOUT_TND = 1 } qli_layout;
+
+/* The scalar problem (QLI-README 参数说明 attributes and shapes).  Fields
+ * are fixed-width and explicitly padded so that the struct has the same
+ * layout from every language. */
+typedef struct qli_problem {
+    int32_t batch;              /* B.  TND: number of entries of actual_seq_lengths_query */
+    int32_t s1;                 /* BSND: S1 (query tokens per batch); TND: T (total tokens) */
+    int32_t num_heads_q;        /* must be 64 (约束说明) */
+    int32_t num_heads_k;        /* must be 1 (约束说明) */
+    int32_t head_dim;           /* must be 128 (约束说明) */
+    int32_t layout_query;       /* qli_layout */
+    int32_t qk_dtype;           /* qli_qk_dtype */
+    int32_t scale_dtype;        /* qli_scale_dtype */
+    int32_t num_blocks;         /* key cache blocks, >= 1 */
+    int32_t block_size;         /* multiple of 16, 16..1024 (约束说明) */
+    int32_t max_blocks_per_seq; /* second dim of block_table, >= blocks any sequence needs */
+    int32_t reserved0;          /* must be 0 */
+    int64_t key_block_stride;   /* "stride" of key's first axis (参数说明) in elements (= bytes);
+                                   0 = block_size*128; else >= block_size*128 and a multiple of 16 */
+    int32_t sparse_count;       /* k, 1..2048 (参数说明 sparse_count) */
+    int32_t sparse_mode;        /* 0 defaultMask, 3 rightDownCausal (参数说明 sparse_mode) */
+    int32_t cmp_ratio;          /* 1,2,4,...,128 (参数说明 cmp_ratio) */
+    int32_t reserved1;          /* must be 0 */
+    int64_t pre_tokens;         /* reserved by the page; must be INT64_MAX */
+    int64_t next_tokens;        /* reserved by the page; must be INT64_MAX */
+    int32_t query_quant_mode;   /* must be 0 (per-token-head) */
+    int32_t key_quant_mode;     /* must be 0 (per-token-head) */
+    int32_t return_value;       /* 1: also write sparse_values; 0: sparse_values may be NULL */
+    int32_t reserved2;          /* must be 0 */
+} qli_problem;
+
+/* Static description of the string for a status code (never NULL). */
+const char *qli_status_string(int status);
+
+/*
+ * qli_plan -- host-side work split (QLI-README 参数说明 "metadata" and the
+ * VllmQuantLightningIndexerMetadata call of the page's examples).
+ *
+ *   p          the problem; validated as qli_run validates it.
+ *   aslq       host int32[batch]: actual_seq_lengths_query.  BSND: query
+ *              tokens used per batch (each in 0..S1); NULL means S1 for all.
+ *              TND: required; non-decreasing prefix sums, last <= T
+ *              (约束说明).  Rows past a batch's count are padded outputs.
+ *   aslk       host int32[batch], required: actual_seq_lengths_key, the
+ *              ORIGINAL key tokens per batch (>= 0).  The cache stores
+ *              floor(aslk / cmp_ratio) compressed entries per batch, which
+ *              must fit in max_blocks_per_seq blocks.
+ *   plan       host buffer of plan_capacity bytes, or NULL to query sizes.
+ *   plan_bytes       out: bytes the plan needs (always written on QLI_OK or
+ *                    QLI_ERR_SIZE).
+ *   workspace_bytes  out: device workspace qli_run needs (may be 0).
+ *
+ * Returns QLI_ERR_SIZE when plan != NULL and plan_capacity < *plan_bytes.
+ * The plan is position-independent bytes: copy it verbatim to the device
+ * and pass both copies to qli_run.
+ */
+int qli_plan(const qli_problem *p, const int32_t *aslq, const int32_t *aslk,
+             void *plan, size_t plan_capacity, size_t *plan_bytes,
+             size_t *workspace_bytes);
+
+/* Summary of a plan, for callers that size buffers or report throughput. */
+typedef struct qli_plan_info {
+    int64_t rows;            /* output rows: B*S1 (BSND) or T (TND) */
+    int64_t visible_pairs;   /* sum over rows of visible key entries (scored pairs) */
+    int64_t plan_bytes;
+    int64_t workspace_bytes;
+    int32_t score_items;     /* work items of the scoring stage */
+    int32_t select_rows;     /* rows whose visible count exceeds sparse_count */
+    int32_t rows_per_item;
+    int32_t keys_per_chunk;
+} qli_plan_info;
+
+int qli_plan_info_get(const void *plan_host, qli_plan_info *info);
+
+/*
+ * qli_run -- the indexer (QLI-README 功能说明 formula; 参数说明 inputs and
+ * outputs).  Stream-ordered, no host synchronisation.
+ *
+ *   plan_host     the bytes qli_plan wrote (host), for launch geometry.
+ *   plan_dev      a device copy of the same bytes (read by the kernels).
+ *   query         device [B,S1,64,128] (BSND) or [T,64,128] (TND), 8-bit.
+ *   key           device paged cache [num_blocks, block_size, 1, 128],
+ *                 consecutive blocks key_block_stride bytes apart, 16-byte
+ *                 aligned.
+ *   weights       device [B,S1,64] or [T,64], scale dtype, contiguous.
+ *   q_scale       device query_dequant_scale, same shape/dtype as weights.
+ *   k_scale       device key_dequant_scale [num_blocks, block_size, 1],
+ *                 contiguous.
+ *   block_table   device int32 [B, max_blocks_per_seq]; entry [b][i] is the
+ *                 cache block holding entries i*block_size .. of batch b.
+ *   workspace     device, workspace_bytes from qli_plan (NULL if 0).
+ *   sparse_indices device int32 [rows, sparse_count] (out).
+ *   sparse_values  device float [rows, sparse_count] (out) or NULL when
+ *                  return_value == 0.
+ *
+ * Output contract per row r with n = min(sparse_count, visible(r)):
+ *   sparse_indices[r][0:n] = the indices of the n highest scores, ties at
+ *   the threshold broken towards the lower index, listed in ascending index
+ *   order; sparse_values[r][i] = the fp32 score of sparse_indices[r][i];
+ *   slots n..sparse_count-1 hold -1 and -INFINITY.
+ */
+int qli_run(const qli_problem *p, const void *plan_host, const void *plan_dev,
+            const void *query, const void *key, const void *weights,
+            const void *q_scale, const void *k_scale,
+            const int32_t *block_table, void *workspace,
+            int32_t *sparse_indices, float *sparse_values, void *stream);
+
+/*
+ * qli_run_debug -- parity instrumentation: runs the same scoring kernels
+ * with a dump epilogue for rows [row0, row1) and writes, for entry
+ * j < min(visible(r), cols):
+ *   dots_out   [(row1-row0), 64, cols]: int32 dot products (INT8 path) or
+ *              float (FP8 path), exactly as the matrix cores produced them;
+ *   scores_out [(row1-row0), cols] float scores.
+ * Slots past a row's visible count are left untouched.  It also performs
+ * the full qli_run (same outputs).
+ */
+int qli_run_debug(const qli_problem *p, const void *plan_host,
+                  const void *plan_dev, const void *query, const void *key,
+                  const void *weights, const void *q_scale,
+                  const void *k_scale, const int32_t *block_table,
+                  void *workspace, int32_t *sparse_indices,
+                  float *sparse_values, int64_t row0, int64_t row1,
+                  int64_t cols, void *dots_out, float *scores_out,
+                  void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QLI_H */

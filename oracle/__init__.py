@@ -100,13 +100,13 @@ class Oracle:
     def indexer(self, inp: dict, *, scores_cols: int = 0, nthreads: int = 0):
         """Whole operator.  Returns (rc, indices[rows,k], values[rows,k], scores or None)."""
         p = inp["problem"]
-        rows = p["batch"] * p["s1"] if p["layout"] == 0 else p["s1"]
+        rows = p["batch"] * p["s1"] if p["layout_query"] == 0 else p["s1"]
         k = p["sparse_count"]
         idx = np.empty((rows, k), dtype=np.int32)
         val = np.empty((rows, k), dtype=np.float32)
         sc = np.full((rows, scores_cols), np.nan, dtype=np.float64) if scores_cols > 0 else None
         rc = self.lib.qlio_indexer(
-            p["qk_dtype"], p["scale_dtype"], p["layout"], p["batch"], p["s1"],
+            p["qk_dtype"], p["scale_dtype"], p["layout_query"], p["batch"], p["s1"],
             p["num_blocks"], p["block_size"], p["max_blocks_per_seq"], p["key_block_stride"],
             p["sparse_count"], p["sparse_mode"], p["cmp_ratio"],
             _ptr(inp["query"]), _ptr(inp["key"]), _ptr(inp["weights"]), _ptr(inp["q_scale"]),
@@ -121,7 +121,7 @@ class Oracle:
         dots = np.zeros((64, n), dtype=np.float64)
         sc = np.zeros(n, dtype=np.float64)
         vis = self.lib.qlio_row_detail(
-            p["qk_dtype"], p["scale_dtype"], p["layout"], p["batch"], p["s1"],
+            p["qk_dtype"], p["scale_dtype"], p["layout_query"], p["batch"], p["s1"],
             p["block_size"], p["max_blocks_per_seq"], p["key_block_stride"],
             p["sparse_mode"], p["cmp_ratio"],
             _ptr(inp["query"]), _ptr(inp["key"]), _ptr(inp["weights"]), _ptr(inp["q_scale"]),

@@ -163,6 +163,17 @@ static const uint8_t *key_row(const paged_keys *pk, int b, int64_t j,
 /* Dot products Q_index . K_index^T                                   */
 /* ------------------------------------------------------------------ */
 
+/* The value of every e4m3fn code, filled once from qlio_e4m3fn_value so that
+ * the dot loop does not call ldexp per element (same values). */
+static double e4m3_value_of[256];
+
+__attribute__((constructor)) static void fill_e4m3_values(void)
+{
+    int c;
+    for (c = 0; c < 256; c++)
+        e4m3_value_of[c] = qlio_e4m3fn_value((uint8_t)c);
+}
+
 /* [功能说明] step 1: the token's query (g x d) times the key (S_k x d).
  * INT8: exact integer sum.  FLOAT8_e4m3fn: exact in fp64 (see header). */
 static double dot_q_k(const uint8_t *q, const uint8_t *k, int qk_dtype)
@@ -176,7 +187,7 @@ static double dot_q_k(const uint8_t *q, const uint8_t *k, int qk_dtype)
     } else {
         double acc = 0.0;
         for (d = 0; d < QLIO_DIM; d++)
-            acc += qlio_e4m3fn_value(q[d]) * qlio_e4m3fn_value(k[d]);
+            acc += e4m3_value_of[q[d]] * e4m3_value_of[k[d]];
         return acc;
     }
 }

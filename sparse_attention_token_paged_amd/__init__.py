@@ -1,0 +1,217 @@
+"""Quantized lightning indexer for AMD MI355X (gfx950).
+
+Python binding of the C ABI in ``include/qli.h`` (``libqli.so``, built
+in-tree by ``python -m sparse_attention_token_paged_amd.build``).  The
+functions keep the C names and only marshal arguments: every step of the
+indexer runs in the library's HIP kernels.  torch is used for device memory
+and streams.  There is no CPU fallback: calling into a missing library
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libqli.so")
+
+QLI_OK, QLI_ERR_ARG, QLI_ERR_UNSUPPORTED, QLI_ERR_SIZE, QLI_ERR_HIP, QLI_ERR_PLAN = range(6)
+QK_INT8, QK_FP8_E4M3FN = 0, 1
+SCALE_F16, SCALE_F32 = 0, 1
+LAYOUT_BSND, LAYOUT_TND = 0, 1
+INT64_MAX = (1 << 63) - 1
+
+EXPORTED = ("qli_status_string", "qli_plan", "qli_plan_info_get", "qli_run", "qli_run_debug")
+
+c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``qli_problem`` (fixed-width, explicitly padded)."""
+    _fields_ = [
+        ("batch", c_i32), ("s1", c_i32), ("num_heads_q", c_i32), ("num_heads_k", c_i32),
+        ("head_dim", c_i32), ("layout_query", c_i32), ("qk_dtype", c_i32), ("scale_dtype", c_i32),
+        ("num_blocks", c_i32), ("block_size", c_i32), ("max_blocks_per_seq", c_i32), ("reserved0", c_i32),
+        ("key_block_stride", c_i64),
+        ("sparse_count", c_i32), ("sparse_mode", c_i32), ("cmp_ratio", c_i32), ("reserved1", c_i32),
+        ("pre_tokens", c_i64), ("next_tokens", c_i64),
+        ("query_quant_mode", c_i32), ("key_quant_mode", c_i32), ("return_value", c_i32), ("reserved2", c_i32),
+    ]
+
+    @classmethod
+    def from_dict(cls, d: dict) -> "Problem":
+        p = cls()
+        for name, _ in cls._fields_:
+            if name in d:
+                setattr(p, name, int(d[name]))
+        return p
+
+
+class PlanInfo(ctypes.Structure):
+    """Mirror of ``qli_plan_info``."""
+    _fields_ = [("rows", c_i64), ("visible_pairs", c_i64), ("plan_bytes", c_i64),
+                ("workspace_bytes", c_i64), ("score_items", c_i32), ("select_rows", c_i32),
+                ("rows_per_item", c_i32), ("keys_per_chunk", c_i32)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libqli.so; raises RuntimeError if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIBRARY
+        if not os.path.exists(p):
+            raise RuntimeError("libqli.so is missing (%s); build it with "
+                               "`python -m sparse_attention_token_paged_amd.build`" % p)
+        lib = ctypes.CDLL(p)
+        lib.qli_status_string.argtypes = [ctypes.c_int]
+        lib.qli_status_string.restype = ctypes.c_char_p
+        lib.qli_plan.argtypes = [ctypes.POINTER(Problem), c_p, c_p, c_p, c_sz,
+                                 ctypes.POINTER(c_sz), ctypes.POINTER(c_sz)]
+        lib.qli_plan.restype = ctypes.c_int
+        lib.qli_plan_info_get.argtypes = [c_p, ctypes.POINTER(PlanInfo)]
+        lib.qli_plan_info_get.restype = ctypes.c_int
+        lib.qli_run.argtypes = [ctypes.POINTER(Problem), c_p, c_p] + [c_p] * 9 + [c_p]
+        lib.qli_run.restype = ctypes.c_int
+        lib.qli_run_debug.argtypes = ([ctypes.POINTER(Problem), c_p, c_p] + [c_p] * 9 +
+                                      [c_i64, c_i64, c_i64, c_p, c_p, c_p])
+        lib.qli_run_debug.restype = ctypes.c_int
+        if path is None:
+            _lib = lib
+        return lib
+
+
+class QliError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__("%s failed: %s (%d)" % (what, qli_status_string(code), code))
+        self.code = code
+
+
+def qli_status_string(code: int) -> str:
+    return load().qli_status_string(code).decode()
+
+
+def _addr(x) -> Optional[int]:
+    """Device or host address of a torch tensor / numpy array / int / None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, np.ndarray):
+        assert x.flags["C_CONTIGUOUS"]
+        return x.ctypes.data
+    # torch.Tensor
+    assert x.is_contiguous(), "tensors passed to the indexer must be contiguous"
+    return x.data_ptr()
+
+
+def qli_plan(problem: Problem, aslq, aslk):
+    """Returns (status, plan bytes as a uint8 numpy array, workspace bytes)."""
+    lib = load()
+    aq = None if aslq is None else np.ascontiguousarray(aslq, dtype=np.int32)
+    ak = None if aslk is None else np.ascontiguousarray(aslk, dtype=np.int32)
+    nb, ws = c_sz(0), c_sz(0)
+    rc = lib.qli_plan(ctypes.byref(problem), _addr(aq), _addr(ak), None, 0, ctypes.byref(nb), ctypes.byref(ws))
+    if rc != QLI_OK:
+        return rc, None, 0
+    buf = np.zeros(nb.value, dtype=np.uint8)
+    rc = lib.qli_plan(ctypes.byref(problem), _addr(aq), _addr(ak), _addr(buf), buf.size,
+                      ctypes.byref(nb), ctypes.byref(ws))
+    return rc, (buf if rc == QLI_OK else None), ws.value
+
+
+def qli_plan_info_get(plan_host: np.ndarray) -> PlanInfo:
+    info = PlanInfo()
+    rc = load().qli_plan_info_get(_addr(plan_host), ctypes.byref(info))
+    if rc != QLI_OK:
+        raise QliError(rc, "qli_plan_info_get")
+    return info
+
+
+def qli_run(problem: Problem, plan_host, plan_dev, query, key, weights, q_scale, k_scale,
+            block_table, workspace, sparse_indices, sparse_values, stream=None) -> int:
+    return load().qli_run(ctypes.byref(problem), _addr(plan_host), _addr(plan_dev), _addr(query),
+                          _addr(key), _addr(weights), _addr(q_scale), _addr(k_scale),
+                          _addr(block_table), _addr(workspace), _addr(sparse_indices),
+                          _addr(sparse_values), stream)
+
+
+def qli_run_debug(problem: Problem, plan_host, plan_dev, query, key, weights, q_scale, k_scale,
+                  block_table, workspace, sparse_indices, sparse_values, row0, row1, cols,
+                  dots_out, scores_out, stream=None) -> int:
+    return load().qli_run_debug(ctypes.byref(problem), _addr(plan_host), _addr(plan_dev), _addr(query),
+                                _addr(key), _addr(weights), _addr(q_scale), _addr(k_scale),
+                                _addr(block_table), _addr(workspace), _addr(sparse_indices),
+                                _addr(sparse_values), row0, row1, cols, _addr(dots_out),
+                                _addr(scores_out), stream)
+
+
+def current_stream() -> int:
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Indexer:
+    """Plan once, run many times: holds the host plan, its device copy and a
+    zero-filled workspace (torch allocations; marshalling only).
+
+    problem: dict with the qli_problem fields; aslq / aslk: host int arrays.
+    """
+
+    def __init__(self, problem: dict, aslq, aslk, device: str = "cuda"):
+        import torch
+        self.problem = Problem.from_dict(problem)
+        rc, plan, ws = qli_plan(self.problem, aslq, aslk)
+        if rc != QLI_OK:
+            raise QliError(rc, "qli_plan")
+        self.plan_host = plan
+        self.info = qli_plan_info_get(plan)
+        self.plan_dev = torch.from_numpy(plan.copy()).to(device)
+        self.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=device) if ws else None
+        self.device = device
+
+    @property
+    def rows(self) -> int:
+        return int(self.info.rows)
+
+    def alloc_outputs(self):
+        import torch
+        k = self.problem.sparse_count
+        idx = torch.empty((self.rows, k), dtype=torch.int32, device=self.device)
+        val = torch.empty((self.rows, k), dtype=torch.float32, device=self.device) if self.problem.return_value else None
+        return idx, val
+
+    def run(self, query, key, weights, q_scale, k_scale, block_table, out_idx=None, out_val=None,
+            stream: Optional[int] = None):
+        if out_idx is None:
+            out_idx, out_val = self.alloc_outputs()
+        st = current_stream() if stream is None else stream
+        rc = qli_run(self.problem, self.plan_host, self.plan_dev, query, key, weights, q_scale, k_scale,
+                     block_table, self.workspace, out_idx, out_val, st)
+        if rc != QLI_OK:
+            raise QliError(rc, "qli_run")
+        return out_idx, out_val
+
+    def run_debug(self, query, key, weights, q_scale, k_scale, block_table, row0, row1, cols,
+                  stream: Optional[int] = None):
+        import torch
+        out_idx, out_val = self.alloc_outputs()
+        dt = torch.int32 if self.problem.qk_dtype == QK_INT8 else torch.float32
+        dots = torch.zeros(((row1 - row0) * 64 * cols,), dtype=dt, device=self.device)
+        scores = torch.full(((row1 - row0) * cols,), float("nan"), dtype=torch.float32, device=self.device)
+        st = current_stream() if stream is None else stream
+        rc = qli_run_debug(self.problem, self.plan_host, self.plan_dev, query, key, weights, q_scale,
+                           k_scale, block_table, self.workspace, out_idx, out_val, row0, row1, cols,
+                           dots if dots.numel() else None, scores if scores.numel() else None, st)
+        if rc != QLI_OK:
+            raise QliError(rc, "qli_run_debug")
+        return out_idx, out_val, dots.view(row1 - row0, 64, cols), scores.view(row1 - row0, cols)

@@ -1,0 +1,371 @@
+// qli_api.cpp -- the C ABI: validation, the host work-split planner and the
+// launch sequence.  Semantics are documented in include/qli.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "qli_internal.h"
+
+#define QLI_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace qli {
+namespace {
+
+bool is_pow2_upto(int v, int hi) {
+  return v >= 1 && v <= hi && (v & (v - 1)) == 0;
+}
+
+// Scalar validation shared by qli_plan and qli_run.  Each rule cites the
+// QLI-README passage it enforces.
+int validate_problem(const qli_problem* p) {
+  if (!p) return QLI_ERR_ARG;
+  // 约束说明: query N = 64, key N = 1, D = 128.
+  if (p->num_heads_q != kHeads || p->num_heads_k != 1 || p->head_dim != kDim) return QLI_ERR_ARG;
+  // 参数说明 layout_query: BSND or TND.
+  if (p->layout_query != QLI_LAYOUT_BSND && p->layout_query != QLI_LAYOUT_TND) return QLI_ERR_ARG;
+  if (p->qk_dtype != QLI_QK_INT8 && p->qk_dtype != QLI_QK_FP8_E4M3FN) return QLI_ERR_ARG;
+  if (p->scale_dtype != QLI_SCALE_F16 && p->scale_dtype != QLI_SCALE_F32) return QLI_ERR_ARG;
+  // 参数说明 notes: INT8 q/k with FLOAT16 scales, FLOAT8_e4m3fn with FLOAT32.
+  if (!((p->qk_dtype == QLI_QK_INT8 && p->scale_dtype == QLI_SCALE_F16) ||
+        (p->qk_dtype == QLI_QK_FP8_E4M3FN && p->scale_dtype == QLI_SCALE_F32)))
+    return QLI_ERR_UNSUPPORTED;
+  if (p->batch < 0 || p->s1 < 0) return QLI_ERR_ARG;
+  if (p->num_blocks < 1 || p->max_blocks_per_seq < 1) return QLI_ERR_ARG;
+  // 约束说明: block_size a multiple of 16, at most 1024.
+  if (p->block_size < 16 || p->block_size > 1024 || p->block_size % 16 != 0) return QLI_ERR_ARG;
+  // 参数说明 stride: step of key's first axis; at least one whole block.
+  if (p->key_block_stride != 0) {
+    if (p->key_block_stride < (int64_t)p->block_size * kDim) return QLI_ERR_ARG;
+    if (p->key_block_stride % 16 != 0) return QLI_ERR_UNSUPPORTED;  // 16-byte row loads
+  }
+  // 参数说明 sparse_count: [1, 2048].
+  if (p->sparse_count < 1 || p->sparse_count > 2048) return QLI_ERR_ARG;
+  // 参数说明 sparse_mode: 0 or 3.
+  if (p->sparse_mode != 0 && p->sparse_mode != 3) return QLI_ERR_ARG;
+  // 参数说明 cmp_ratio: 1/2/4/8/16/32/64/128.
+  if (!is_pow2_upto(p->cmp_ratio, 128)) return QLI_ERR_ARG;
+  // 参数说明 pre_tokens / next_tokens: reserved, only 2^63-1.
+  if (p->pre_tokens != INT64_MAX || p->next_tokens != INT64_MAX) return QLI_ERR_UNSUPPORTED;
+  // 参数说明 query_quant_mode / key_quant_mode: only 0 (per-token-head).
+  if (p->query_quant_mode != 0 || p->key_quant_mode != 0) return QLI_ERR_UNSUPPORTED;
+  if (p->return_value != 0 && p->return_value != 1) return QLI_ERR_ARG;
+  if (p->reserved0 || p->reserved1 || p->reserved2) return QLI_ERR_ARG;
+  const int64_t rows = p->layout_query == QLI_LAYOUT_BSND ? (int64_t)p->batch * p->s1 : p->s1;
+  if (rows > INT32_MAX / 2) return QLI_ERR_SIZE;
+  return QLI_OK;
+}
+
+// Visible compressed entries of query i (of s1b) in a batch with skb original
+// key tokens.  QLI-README 参数说明: cmp_ratio compresses the key, sparse_mode
+// 0 is no mask and 3 the bottom-right-aligned causal mask.  Reading: only
+// floor(skb / cmp) whole entries exist; query i sits at token position
+// skb - s1b + i and sees entry j once all of its tokens [j*cmp, (j+1)*cmp)
+// are at or before that position.
+int64_t visible_entries(int mode, int cmp, int64_t skb, int64_t s1b, int64_t i) {
+  const int64_t stored = skb / cmp;
+  if (mode == 0) return stored;
+  const int64_t through = skb - s1b + i + 1;  // tokens at or before the query
+  if (through <= 0) return 0;
+  return std::min(through / cmp, stored);
+}
+
+constexpr uint32_t kFnvPrime = 16777619u;
+
+uint64_t fnv_mix(uint64_t h, int64_t v) {
+  for (int b = 0; b < 8; b++) {
+    h ^= (uint64_t)((v >> (8 * b)) & 0xFF);
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+}  // namespace
+
+uint64_t problem_fingerprint(const qli_problem& p) {
+  uint64_t h = 1469598103934665603ull ^ kFnvPrime;
+  const int64_t fields[] = {p.batch, p.s1, p.layout_query, p.qk_dtype, p.scale_dtype,
+                            p.num_blocks, p.block_size, p.max_blocks_per_seq,
+                            p.sparse_count, p.sparse_mode, p.cmp_ratio};
+  for (int64_t f : fields) h = fnv_mix(h, f);
+  return h;
+}
+
+namespace {
+
+struct Built {
+  PlanHeader hdr;
+  std::vector<RowInfo> rows;
+  std::vector<Item> items;
+  std::vector<int32_t> select;
+};
+
+int64_t align16(int64_t v) { return (v + 15) & ~int64_t(15); }
+
+int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, Built& out) {
+  const bool bsnd = p.layout_query == QLI_LAYOUT_BSND;
+  if (p.batch > 0 && !aslk) return QLI_ERR_ARG;  // 约束说明: required for PA_BSND keys
+  if (!bsnd && p.batch > 0 && !aslq) return QLI_ERR_ARG;  // 约束说明: required for TND
+  const int64_t rows = bsnd ? (int64_t)p.batch * p.s1 : p.s1;
+
+  // Per-batch query ranges (约束说明: TND prefix sums non-decreasing, >= 0).
+  std::vector<int64_t> qbeg(p.batch), qcnt(p.batch);
+  int64_t prev = 0;
+  for (int b = 0; b < p.batch; b++) {
+    if (aslk[b] < 0) return QLI_ERR_ARG;
+    const int64_t stored = aslk[b] / p.cmp_ratio;
+    const int64_t need = (stored + p.block_size - 1) / p.block_size;
+    if (need > p.max_blocks_per_seq) return QLI_ERR_ARG;  // 约束说明: block_table second dim
+    if (bsnd) {
+      const int64_t n = aslq ? aslq[b] : p.s1;
+      if (n < 0 || n > p.s1) return QLI_ERR_ARG;
+      qbeg[b] = (int64_t)b * p.s1;
+      qcnt[b] = n;
+    } else {
+      if (aslq[b] < prev || aslq[b] > p.s1) return QLI_ERR_ARG;
+      qbeg[b] = prev;
+      qcnt[b] = aslq[b] - prev;
+      prev = aslq[b];
+    }
+  }
+
+  out.rows.assign(rows, RowInfo{-1, 0, -1});
+  int64_t max_s1b = 0, visible = 0, max_vis = 0;
+  for (int b = 0; b < p.batch; b++) {
+    max_s1b = std::max(max_s1b, qcnt[b]);
+    for (int64_t i = 0; i < qcnt[b]; i++) {
+      const int64_t v = visible_entries(p.sparse_mode, p.cmp_ratio, aslk[b], qcnt[b], i);
+      RowInfo& ri = out.rows[qbeg[b] + i];
+      ri.batch = b;
+      ri.vis = (int32_t)v;
+      visible += v;
+      max_vis = std::max(max_vis, v);
+    }
+  }
+
+  // Tile shape: decode-like problems (few query tokens per sequence) put
+  // 1, 2 or 4 rows in an item so the key chunk is read once for all of
+  // them; prefill-like problems use 8-row tiles.
+  const bool prefill = max_s1b > 4;
+  const int rt = prefill ? 8 : (max_s1b <= 1 ? 1 : (max_s1b <= 2 ? 2 : 4));
+
+  struct Group { int32_t row0, nrows, batch, maxv; };
+  std::vector<Group> groups;
+  for (int b = 0; b < p.batch; b++) {
+    for (int64_t i = 0; i < qcnt[b]; i += rt) {
+      const int32_t n = (int32_t)std::min<int64_t>(rt, qcnt[b] - i);
+      int32_t mv = 0;
+      for (int32_t u = 0; u < n; u++) mv = std::max(mv, out.rows[qbeg[b] + i + u].vis);
+      groups.push_back({(int32_t)(qbeg[b] + i), n, b, mv});
+    }
+  }
+  // Rows that belong to no query token only receive padding.
+  for (int64_t r = 0; r < rows;) {
+    if (out.rows[r].batch >= 0) { r++; continue; }
+    int64_t e = r;
+    while (e < rows && e - r < rt && out.rows[e].batch < 0) e++;
+    groups.push_back({(int32_t)r, (int32_t)(e - r), -1, 0});
+    r = e;
+  }
+
+  // Chunk size: about 1024 items in total for decode (4 per CU on 256 CUs),
+  // whole rows (up to kMaxChunk) for prefill.
+  int64_t key_work = 0;
+  for (const Group& g : groups) key_work += g.maxv;
+  int chunk = kMaxChunk;
+  if (!prefill) {
+    int64_t c = (key_work + 1023) / 1024;
+    c = (c + kTileKeys - 1) / kTileKeys * kTileKeys;
+    chunk = (int)std::min<int64_t>(kMaxChunk, std::max<int64_t>(256, c));
+  }
+
+  for (const Group& g : groups) {
+    if (g.maxv == 0) {
+      out.items.push_back({g.row0, g.nrows, g.batch, 0, 0, kItemPad});
+      continue;
+    }
+    for (int32_t k0 = 0; k0 < g.maxv; k0 += chunk)
+      out.items.push_back({g.row0, g.nrows, g.batch, k0, std::min(chunk, g.maxv - k0),
+                           k0 == 0 ? kItemPad : 0});
+  }
+  if (prefill)  // longest items first
+    std::stable_sort(out.items.begin(), out.items.end(),
+                     [](const Item& a, const Item& b) { return a.nkeys * a.nrows > b.nkeys * b.nrows; });
+  if (out.items.size() > (size_t)INT32_MAX) return QLI_ERR_SIZE;
+
+  // Rows with more visible entries than sparse_count stage their scores in
+  // the workspace and go through the selection stage.
+  int64_t ws = 0;
+  for (int64_t r = 0; r < rows; r++) {
+    RowInfo& ri = out.rows[r];
+    if (ri.vis > p.sparse_count) {
+      ri.ws_off = ws;
+      ws += ri.vis;
+      out.select.push_back((int32_t)r);
+    }
+  }
+
+  PlanHeader& h = out.hdr;
+  std::memset(&h, 0, sizeof(h));
+  h.magic = kPlanMagic;
+  h.version = kPlanVersion;
+  h.fingerprint = problem_fingerprint(p);
+  h.rows = rows;
+  h.visible_pairs = visible;
+  h.ws_scores = ws;
+  h.workspace_bytes = ws * 4;
+  h.kind = prefill ? kKindPrefill : kKindDecode;
+  h.rows_per_item = rt;
+  h.n_items = (int32_t)out.items.size();
+  h.n_select = (int32_t)out.select.size();
+  h.chunk = chunk;
+  h.max_vis = (int32_t)max_vis;
+  h.off_rows = align16(sizeof(PlanHeader));
+  h.off_items = align16(h.off_rows + (int64_t)sizeof(RowInfo) * rows);
+  h.off_select = align16(h.off_items + (int64_t)sizeof(Item) * h.n_items);
+  h.plan_bytes = align16(h.off_select + 4 * (int64_t)h.n_select);
+  return QLI_OK;
+}
+
+bool plan_matches(const qli_problem* p, const void* plan_host) {
+  if (!plan_host) return false;
+  const PlanHeader* h = plan_header(plan_host);
+  return h->magic == kPlanMagic && h->version == kPlanVersion &&
+         h->fingerprint == problem_fingerprint(*p);
+}
+
+int check_run_args(const RunArgs& a) {
+  const PlanHeader* h = a.hdr;
+  if (!a.plan_dev) return QLI_ERR_ARG;
+  if (h->rows == 0) return QLI_OK;
+  if (!a.sparse_indices) return QLI_ERR_ARG;
+  if (a.p->return_value && !a.sparse_values) return QLI_ERR_ARG;
+  if (h->n_items > 0 && (!a.query || !a.key || !a.weights || !a.q_scale || !a.k_scale || !a.block_table))
+    return QLI_ERR_ARG;
+  if (h->workspace_bytes > 0 && !a.workspace) return QLI_ERR_ARG;
+  return QLI_OK;
+}
+
+}  // namespace
+}  // namespace qli
+
+using namespace qli;
+
+QLI_EXPORT const char* qli_status_string(int status) {
+  switch (status) {
+    case QLI_OK: return "ok";
+    case QLI_ERR_ARG: return "invalid argument";
+    case QLI_ERR_UNSUPPORTED: return "unsupported configuration";
+    case QLI_ERR_SIZE: return "buffer too small or size overflow";
+    case QLI_ERR_HIP: return "HIP runtime error";
+    case QLI_ERR_PLAN: return "plan does not match the problem";
+    default: return "unknown status";
+  }
+}
+
+QLI_EXPORT int qli_plan(const qli_problem* p, const int32_t* aslq, const int32_t* aslk,
+                        void* plan, size_t plan_capacity, size_t* plan_bytes,
+                        size_t* workspace_bytes) {
+  try {
+    int rc = validate_problem(p);
+    if (rc != QLI_OK) return rc;
+    Built b;
+    rc = build_plan(*p, aslq, aslk, b);
+    if (rc != QLI_OK) return rc;
+    if (plan_bytes) *plan_bytes = (size_t)b.hdr.plan_bytes;
+    if (workspace_bytes) *workspace_bytes = (size_t)b.hdr.workspace_bytes;
+    if (!plan) return QLI_OK;
+    if (plan_capacity < (size_t)b.hdr.plan_bytes) return QLI_ERR_SIZE;
+    uint8_t* dst = static_cast<uint8_t*>(plan);
+    std::memset(dst, 0, (size_t)b.hdr.plan_bytes);
+    std::memcpy(dst, &b.hdr, sizeof(PlanHeader));
+    if (!b.rows.empty()) std::memcpy(dst + b.hdr.off_rows, b.rows.data(), sizeof(RowInfo) * b.rows.size());
+    if (!b.items.empty()) std::memcpy(dst + b.hdr.off_items, b.items.data(), sizeof(Item) * b.items.size());
+    if (!b.select.empty()) std::memcpy(dst + b.hdr.off_select, b.select.data(), 4 * b.select.size());
+    return QLI_OK;
+  } catch (const std::bad_alloc&) {
+    return QLI_ERR_SIZE;
+  } catch (...) {
+    return QLI_ERR_ARG;
+  }
+}
+
+QLI_EXPORT int qli_plan_info_get(const void* plan_host, qli_plan_info* info) {
+  if (!plan_host || !info) return QLI_ERR_ARG;
+  const PlanHeader* h = plan_header(plan_host);
+  if (h->magic != kPlanMagic || h->version != kPlanVersion) return QLI_ERR_PLAN;
+  info->rows = h->rows;
+  info->visible_pairs = h->visible_pairs;
+  info->plan_bytes = h->plan_bytes;
+  info->workspace_bytes = h->workspace_bytes;
+  info->score_items = h->n_items;
+  info->select_rows = h->n_select;
+  info->rows_per_item = h->rows_per_item;
+  info->keys_per_chunk = h->chunk;
+  return QLI_OK;
+}
+
+static int run_common(const qli_problem* p, const void* plan_host, const void* plan_dev,
+                      const void* query, const void* key, const void* weights,
+                      const void* q_scale, const void* k_scale, const int32_t* block_table,
+                      void* workspace, int32_t* sparse_indices, float* sparse_values,
+                      int64_t row0, int64_t row1, int64_t cols, void* dots_out,
+                      float* scores_out, bool dump, void* stream) {
+  int rc = validate_problem(p);
+  if (rc != QLI_OK) return rc;
+  if (!plan_matches(p, plan_host)) return QLI_ERR_PLAN;
+  RunArgs a;
+  a.p = p;
+  a.plan_dev = plan_dev;
+  a.hdr = plan_header(plan_host);
+  a.query = query;
+  a.key = key;
+  a.weights = weights;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.block_table = block_table;
+  a.workspace = workspace;
+  a.sparse_indices = sparse_indices;
+  a.sparse_values = p->return_value ? sparse_values : nullptr;
+  a.dump_row0 = row0;
+  a.dump_row1 = row1;
+  a.dump_cols = cols;
+  a.dots_out = dots_out;
+  a.scores_out = scores_out;
+  a.stream = stream;
+  rc = check_run_args(a);
+  if (rc != QLI_OK) return rc;
+  if (dump) {
+    if (row0 < 0 || row1 < row0 || row1 > a.hdr->rows || cols < 0) return QLI_ERR_ARG;
+    if (row1 > row0 && cols > 0 && (!dots_out || !scores_out)) return QLI_ERR_ARG;
+  }
+  if (a.hdr->rows == 0) return QLI_OK;
+  if (launch_score(a, dump) != 0) return QLI_ERR_HIP;
+  if (a.hdr->n_select > 0 && launch_select(a) != 0) return QLI_ERR_HIP;
+  return QLI_OK;
+}
+
+QLI_EXPORT int qli_run(const qli_problem* p, const void* plan_host, const void* plan_dev,
+                       const void* query, const void* key, const void* weights,
+                       const void* q_scale, const void* k_scale, const int32_t* block_table,
+                       void* workspace, int32_t* sparse_indices, float* sparse_values,
+                       void* stream) {
+  return run_common(p, plan_host, plan_dev, query, key, weights, q_scale, k_scale, block_table,
+                    workspace, sparse_indices, sparse_values, 0, 0, 0, nullptr, nullptr, false,
+                    stream);
+}
+
+QLI_EXPORT int qli_run_debug(const qli_problem* p, const void* plan_host, const void* plan_dev,
+                             const void* query, const void* key, const void* weights,
+                             const void* q_scale, const void* k_scale,
+                             const int32_t* block_table, void* workspace,
+                             int32_t* sparse_indices, float* sparse_values, int64_t row0,
+                             int64_t row1, int64_t cols, void* dots_out, float* scores_out,
+                             void* stream) {
+  return run_common(p, plan_host, plan_dev, query, key, weights, q_scale, k_scale, block_table,
+                    workspace, sparse_indices, sparse_values, row0, row1, cols, dots_out,
+                    scores_out, true, stream);
+}

@@ -1,0 +1,90 @@
+// qli_internal.h -- plan layout shared by the host planner and the kernels.
+//
+// A plan is position-independent bytes: a header, then a row table, a
+// score-item table and the list of rows that need a selection.  The host
+// reads the header for launch geometry; the kernels read the device copy.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/qli.h"
+
+namespace qli {
+
+constexpr uint32_t kPlanMagic = 0x504C4951u;  // "QILP"
+constexpr uint32_t kPlanVersion = 1;
+constexpr int kHeads = 64;       // query heads (QLI-README 约束说明)
+constexpr int kDim = 128;        // head dim of query and key (约束说明)
+constexpr int kTileKeys = 64;    // keys staged in LDS per pipeline step
+constexpr int kMaxChunk = 4096;  // keys per score item, upper bound
+constexpr int kMaxChunkBlocks = kMaxChunk / 16 + 2;  // block ids one item may touch
+
+enum PlanKind : int32_t { kKindDecode = 0, kKindPrefill = 1 };
+enum ItemFlags : int32_t { kItemPad = 1 };
+
+struct PlanHeader {
+  uint32_t magic;
+  uint32_t version;
+  uint64_t fingerprint;      // hash of the problem fields the plan depends on
+  int64_t plan_bytes;
+  int64_t workspace_bytes;
+  int64_t rows;              // output rows
+  int64_t visible_pairs;     // sum of visible counts
+  int64_t ws_scores;         // fp32 scores staged in the workspace
+  int64_t off_rows;          // byte offset of RowInfo[rows]
+  int64_t off_items;         // byte offset of Item[n_items]
+  int64_t off_select;        // byte offset of int32[n_select]
+  int32_t kind;              // PlanKind
+  int32_t rows_per_item;     // 1, 2, 4 (decode) or 8 (prefill)
+  int32_t n_items;
+  int32_t n_select;
+  int32_t chunk;             // keys per score item (multiple of kTileKeys)
+  int32_t max_vis;
+  int32_t reserved[6];
+};
+static_assert(sizeof(PlanHeader) % 16 == 0, "header keeps the tables aligned");
+
+struct RowInfo {
+  int32_t batch;   // -1 for rows that belong to no query token
+  int32_t vis;     // visible compressed key entries
+  int64_t ws_off;  // element offset of the row's scores in the workspace, -1 = direct output
+};
+
+struct Item {
+  int32_t row0;    // first global row
+  int32_t nrows;   // rows in the item (same batch), <= rows_per_item
+  int32_t batch;   // batch whose keys are scored (-1: padding only)
+  int32_t key0;    // first key entry of the chunk
+  int32_t nkeys;   // entries in the chunk (0: padding only)
+  int32_t flags;   // kItemPad: this item writes the -1 padding of its rows
+};
+
+inline const PlanHeader* plan_header(const void* plan) {
+  return static_cast<const PlanHeader*>(plan);
+}
+
+uint64_t problem_fingerprint(const qli_problem& p);
+
+// Kernel launchers (qli_kernels.hip).  Return a hipError_t value.
+struct RunArgs {
+  const qli_problem* p;
+  const void* plan_dev;
+  const PlanHeader* hdr;
+  const void* query;
+  const void* key;
+  const void* weights;
+  const void* q_scale;
+  const void* k_scale;
+  const int32_t* block_table;
+  void* workspace;
+  int32_t* sparse_indices;
+  float* sparse_values;
+  int64_t dump_row0, dump_row1, dump_cols;
+  void* dots_out;
+  float* scores_out;
+  void* stream;
+};
+int launch_score(const RunArgs& a, bool dump);
+int launch_select(const RunArgs& a);
+
+}  // namespace qli

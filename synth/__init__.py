@@ -130,7 +130,7 @@ def make_inputs(spec: Spec, seed: int) -> dict:
 
     problem = dict(
         batch=B, s1=spec.s1, num_heads_q=64, num_heads_k=1, head_dim=128,
-        layout=spec.layout, qk_dtype=spec.qk, scale_dtype=F16 if spec.qk == INT8 else F32,
+        layout_query=spec.layout, qk_dtype=spec.qk, scale_dtype=F16 if spec.qk == INT8 else F32,
         num_blocks=num_blocks, block_size=bs, max_blocks_per_seq=max_blocks,
         key_block_stride=stride if spec.stride_pad else 0,
         sparse_count=spec.sparse_count, sparse_mode=spec.sparse_mode, cmp_ratio=cmp,

@@ -67,4 +67,4 @@ def brute_dots_int(inp: dict, r: int, b: int, n: int):
 
 
 def rows_of(p: dict) -> int:
-    return p["batch"] * p["s1"] if p["layout"] == 0 else p["s1"]
+    return p["batch"] * p["s1"] if p["layout_query"] == 0 else p["s1"]

@@ -1,0 +1,217 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads and
+exports every entry point include/qli.h declares, qli_plan enforces each
+constraint of the VllmQuantLightningIndexer page with the documented status
+code, and the plan covers every visible (row, key) pair exactly once with
+the visible counts the oracle computes."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="session")
+def qli():
+    import sparse_attention_token_paged_amd as q
+    from sparse_attention_token_paged_amd import build as b
+    if b.stale():
+        b.build()
+    q.load()
+    return q
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "qli.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qli_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(qli):
+    names = declared_functions()
+    assert set(names) == set(qli.EXPORTED)
+    lib = ctypes.CDLL(qli.LIBRARY)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_only_c_abi_symbols_exported(qli):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", qli.LIBRARY], capture_output=True, text=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert {s for s in syms if s.startswith("qli")} == set(declared_functions())
+    assert not [s for s in syms if s.startswith("_ZN3qli")]
+
+
+def test_status_strings(qli):
+    assert qli.qli_status_string(0) == "ok"
+    for c in range(1, 6):
+        assert qli.qli_status_string(c) not in ("ok", "unknown status")
+    assert qli.qli_status_string(99) == "unknown status"
+
+
+def base_problem(**kw):
+    inp = synth.make_inputs(synth.small(**kw), 0)
+    return inp
+
+
+def plan_rc(qli, inp, **over):
+    p = dict(inp["problem"], **over)
+    rc, _, _ = qli.qli_plan(qli.Problem.from_dict(p), inp["aslq"], inp["aslk"])
+    return rc
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_heads_q", 32, 1), ("num_heads_k", 2, 1), ("head_dim", 64, 1),
+    ("layout_query", 2, 1), ("qk_dtype", 2, 1), ("scale_dtype", 1, 2),
+    ("block_size", 24, 1), ("block_size", 8, 1), ("block_size", 1040, 1),
+    ("sparse_count", 0, 1), ("sparse_count", 2049, 1), ("sparse_mode", 1, 1), ("sparse_mode", 2, 1),
+    ("cmp_ratio", 3, 1), ("cmp_ratio", 0, 1), ("cmp_ratio", 256, 1),
+    ("pre_tokens", 1000, 2), ("next_tokens", 0, 2), ("query_quant_mode", 1, 2), ("key_quant_mode", 1, 2),
+    ("return_value", 2, 1), ("reserved0", 1, 1), ("key_block_stride", 100, 1), ("key_block_stride", 64 * 128 + 8, 2),
+    ("batch", -1, 1), ("num_blocks", 0, 1), ("max_blocks_per_seq", 0, 1)])
+def test_plan_validation(qli, field, value, code):
+    inp = base_problem()
+    assert plan_rc(qli, inp) == 0
+    assert plan_rc(qli, inp, **{field: value}) == code
+
+
+def test_plan_length_validation(qli):
+    inp = base_problem(aslk=[300, 200], block_size=64)
+    assert plan_rc(qli, inp, max_blocks_per_seq=4) == 1           # 300 entries need 5 blocks
+    rc, _, _ = qli.qli_plan(qli.Problem.from_dict(inp["problem"]), None, np.array([300, -1], np.int32))
+    assert rc == 1                                                  # negative key length
+    rc, _, _ = qli.qli_plan(qli.Problem.from_dict(inp["problem"]), np.array([1, 3], np.int32), inp["aslk"])
+    assert rc == 1                                                  # BSND count above S1
+    rc, _, _ = qli.qli_plan(qli.Problem.from_dict(inp["problem"]), None, None)
+    assert rc == 1                                                  # key lengths are required
+    tnd = synth.make_inputs(synth.small(layout=synth.TND, s1=6, aslq=[4, 6]), 0)
+    for bad in ([4, 3], [4, 7], [-1, 6]):
+        rc, _, _ = qli.qli_plan(qli.Problem.from_dict(tnd["problem"]), np.array(bad, np.int32), tnd["aslk"])
+        assert rc == 1, bad
+    rc, _, _ = qli.qli_plan(qli.Problem.from_dict(tnd["problem"]), None, tnd["aslk"])
+    assert rc == 1                                                  # TND needs the prefix sums
+
+
+def test_plan_capacity(qli):
+    inp = base_problem()
+    lib = qli.load()
+    prob = qli.Problem.from_dict(inp["problem"])
+    nb, ws = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    ak = np.ascontiguousarray(inp["aslk"])
+    assert lib.qli_plan(ctypes.byref(prob), None, ak.ctypes.data, None, 0, ctypes.byref(nb), ctypes.byref(ws)) == 0
+    small = np.zeros(nb.value - 16, np.uint8)
+    assert lib.qli_plan(ctypes.byref(prob), None, ak.ctypes.data, small.ctypes.data, small.size,
+                        ctypes.byref(nb), ctypes.byref(ws)) == 3
+
+
+# --- plan parsing (layout of qli_internal.h) ---------------------------------
+HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("fingerprint", "<u8"), ("plan_bytes", "<i8"),
+                ("workspace_bytes", "<i8"), ("rows", "<i8"), ("visible_pairs", "<i8"), ("ws_scores", "<i8"),
+                ("off_rows", "<i8"), ("off_items", "<i8"), ("off_select", "<i8"), ("kind", "<i4"),
+                ("rows_per_item", "<i4"), ("n_items", "<i4"), ("n_select", "<i4"), ("chunk", "<i4"),
+                ("max_vis", "<i4"), ("reserved", "<i4", 6)])
+ROW = np.dtype([("batch", "<i4"), ("vis", "<i4"), ("ws_off", "<i8")])
+ITEM = np.dtype([("row0", "<i4"), ("nrows", "<i4"), ("batch", "<i4"), ("key0", "<i4"), ("nkeys", "<i4"),
+                 ("flags", "<i4")])
+
+
+def parse(plan):
+    h = np.frombuffer(plan[:HDR.itemsize].tobytes(), HDR)[0]
+    rows = np.frombuffer(plan[h["off_rows"]:h["off_rows"] + ROW.itemsize * h["rows"]].tobytes(), ROW)
+    items = np.frombuffer(plan[h["off_items"]:h["off_items"] + ITEM.itemsize * h["n_items"]].tobytes(), ITEM)
+    sel = np.frombuffer(plan[h["off_select"]:h["off_select"] + 4 * h["n_select"]].tobytes(), "<i4")
+    return h, rows, items, sel
+
+
+PLAN_CASES = [
+    synth.small(),
+    synth.small(batch=3, s1=4, aslk=[1000, 517, 77], block_size=48, sparse_count=256, sparse_mode=3),
+    synth.small(batch=3, s1=3, aslk=[150, 40, 0], aslq=[3, 2, 3], block_size=32, sparse_count=64,
+                sparse_mode=3, cmp_ratio=2),
+    synth.small(layout=synth.TND, batch=3, s1=210, aslq=[70, 140, 200], aslk=[70, 100, 300], block_size=32,
+                sparse_count=64, sparse_mode=3),
+    synth.small(qk=synth.FP8, batch=5, s1=1, aslk=("uniform", 100, 9000), block_size=64, sparse_count=300),
+    synth.small(batch=0, s1=4, aslk=[]),
+    synth.small(layout=synth.TND, batch=0, s1=5, aslk=[], aslq=[]),
+]
+
+
+@pytest.mark.parametrize("spec", PLAN_CASES, ids=range(len(PLAN_CASES)))
+def test_plan_covers_each_visible_pair_once(qli, ora, spec):
+    inp = synth.make_inputs(spec, 3)
+    p = inp["problem"]
+    rc, plan, ws = qli.qli_plan(qli.Problem.from_dict(p), inp["aslq"], inp["aslk"])
+    assert rc == 0
+    h, rows, items, sel = parse(plan)
+    assert h["magic"] == 0x504C4951
+    nrows = p["batch"] * p["s1"] if p["layout_query"] == 0 else p["s1"]
+    assert h["rows"] == nrows
+    vis = ora.row_visible(p["layout_query"], p["batch"], p["s1"], p["sparse_mode"], p["cmp_ratio"],
+                          inp["aslq"], inp["aslk"]) if nrows else np.zeros(0, np.int64)
+    assert np.array_equal(rows["vis"], vis)
+    assert h["visible_pairs"] == vis.sum()
+    cover = [np.zeros(v, np.int32) for v in vis]
+    padded = np.zeros(nrows, np.int32)
+    for it in items:
+        for r in range(it["row0"], it["row0"] + it["nrows"]):
+            if it["flags"] & 1:
+                padded[r] += 1
+            if it["nkeys"]:
+                assert rows[r]["batch"] == it["batch"]
+                hi = min(it["key0"] + it["nkeys"], vis[r])
+                if hi > it["key0"]:
+                    cover[r][it["key0"]:hi] += 1
+        assert it["nkeys"] <= h["chunk"] and (it["key0"] % 64 == 0)
+    assert all(np.all(c == 1) for c in cover)
+    assert np.all(padded == 1)
+    k = p["sparse_count"]
+    assert list(sel) == [r for r in range(nrows) if vis[r] > k]
+    assert ws == 4 * sum(int(vis[r]) for r in sel)
+    offs = [rows[r]["ws_off"] for r in sel]
+    assert offs == list(np.cumsum([0] + [int(vis[r]) for r in sel])[:-1])
+    info = qli.qli_plan_info_get(plan)
+    assert info.rows == nrows and info.visible_pairs == vis.sum() and info.select_rows == len(sel)
+
+
+def test_run_rejects_bad_arguments_without_launching(qli):
+    inp = base_problem()
+    prob = qli.Problem.from_dict(inp["problem"])
+    rc, plan, ws = qli.qli_plan(prob, inp["aslq"], inp["aslk"])
+    assert rc == 0
+    fake = 1 << 40  # never dereferenced: every call below fails validation first
+    args = [fake] * 9
+    other = qli.Problem.from_dict(dict(inp["problem"], sparse_count=65))
+    assert qli.qli_run(other, plan, fake, *args) == qli.QLI_ERR_PLAN
+    bad = plan.copy()
+    bad[0] ^= 0xFF
+    assert qli.qli_run(prob, bad, fake, *args) == qli.QLI_ERR_PLAN
+    assert qli.qli_run(prob, plan, None, *args) == qli.QLI_ERR_ARG
+    a = list(args)
+    a[7] = None                                                     # sparse_indices
+    assert qli.qli_run(prob, plan, fake, *a) == qli.QLI_ERR_ARG
+    a = list(args)
+    a[8] = None                                                     # sparse_values with return_value=1
+    assert qli.qli_run(prob, plan, fake, *a) == qli.QLI_ERR_ARG
+    a = list(args)
+    a[0] = None                                                     # query
+    assert qli.qli_run(prob, plan, fake, *a) == qli.QLI_ERR_ARG
+    invalid = qli.Problem.from_dict(dict(inp["problem"], sparse_mode=1))
+    assert qli.qli_run(invalid, plan, fake, *args) == qli.QLI_ERR_ARG
+    # debug range checks
+    assert qli.qli_run_debug(prob, plan, fake, *args, 2, 1, 8, fake, fake) == qli.QLI_ERR_ARG
+    assert qli.qli_run_debug(prob, plan, fake, *args, 0, 99, 8, fake, fake) == qli.QLI_ERR_ARG
+    assert qli.qli_run_debug(prob, plan, fake, *args, 0, 1, 8, None, fake) == qli.QLI_ERR_ARG
+
+
+def test_empty_problem_runs_without_device(qli):
+    """Zero rows: validation passes and nothing is launched."""
+    inp = synth.make_inputs(synth.small(batch=0, s1=4, aslk=[]), 0)
+    prob = qli.Problem.from_dict(inp["problem"])
+    rc, plan, ws = qli.qli_plan(prob, None, np.zeros(0, np.int32))
+    assert rc == 0 and ws == 0
+    assert qli.qli_run(prob, plan, 1 << 40, *([None] * 9)) == qli.QLI_OK

@@ -1,0 +1,173 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases are compared on every row and span several 64-key tiles, ragged
+tails, block sizes that are not powers of two, padded block strides, causal
+and compressed visibility, rows below and above sparse_count, TND and BSND.
+The five full-size workloads run in the benchmark's launch configuration;
+every row gets the structural checks and sampled rows the full oracle check.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests._gpu import (ATOL, check_row, check_structure, device_inputs, log, make_indexer, rtol_of,
+                        run_gpu, stable_topk_set)
+from tests._helpers import rows_of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    import torch
+    import sparse_attention_token_paged_amd as qli
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    qli.load()  # fails loudly if the HIP library is missing
+
+
+def vis_of(ora, inp):
+    p = inp["problem"]
+    return ora.row_visible(p["layout_query"], p["batch"], p["s1"], p["sparse_mode"], p["cmp_ratio"],
+                           inp["aslq"], inp["aslk"])
+
+
+SMALL = {
+    "bsnd_int8_causal_bs48_pad": synth.small(batch=3, s1=4, aslk=[700, 389, 1500], block_size=48,
+                                             sparse_count=256, sparse_mode=3, stride_pad=32),
+    "bsnd_int8_mode0_identity": synth.small(batch=2, s1=1, aslk=[1000, 64 + 13], block_size=128,
+                                            sparse_count=512, table="identity"),
+    "bsnd_int8_cmp4_bs16": synth.small(batch=2, s1=2, aslk=[4099, 777], block_size=16, sparse_count=128,
+                                       sparse_mode=3, cmp_ratio=4),
+    "bsnd_int8_unused_rows": synth.small(batch=3, s1=3, aslk=[150, 40, 0], aslq=[3, 2, 3], block_size=32,
+                                         sparse_count=64, sparse_mode=3, cmp_ratio=2),
+    "bsnd_int8_k1": synth.small(batch=2, s1=3, aslk=[333, 97], block_size=32, sparse_count=1, sparse_mode=3),
+    "bsnd_int8_k2048": synth.small(batch=1, s1=2, aslk=[5000], block_size=256, sparse_count=2048,
+                                   sparse_mode=3),
+    "bsnd_int8_vis_equals_k": synth.small(batch=1, s1=1, aslk=[640], block_size=64, sparse_count=640),
+    "bsnd_int8_s1_3": synth.small(batch=2, s1=3, aslk=[900, 2100], block_size=64, sparse_count=300,
+                                  sparse_mode=3),
+    "tnd_int8_prefill_mixed": synth.small(layout=synth.TND, batch=3, s1=210, aslq=[70, 140, 200],
+                                          aslk=[70, 100, 300], block_size=32, sparse_count=64, sparse_mode=3),
+    "tnd_int8_prefill_long": synth.small(layout=synth.TND, batch=1, s1=40, aslq=[40], aslk=[6000],
+                                         block_size=128, sparse_count=100, sparse_mode=3),
+    "bsnd_fp8_mode0": synth.small(qk=synth.FP8, batch=4, s1=1, aslk=[3000, 200, 1777, 64], block_size=64,
+                                  sparse_count=300),
+    "bsnd_fp8_causal_s2": synth.small(qk=synth.FP8, batch=2, s1=2, aslk=[2500, 900], block_size=32,
+                                      sparse_count=128, sparse_mode=3, stride_pad=16),
+    "tnd_fp8_prefill": synth.small(qk=synth.FP8, layout=synth.TND, batch=2, s1=50, aslq=[20, 50],
+                                   aslk=[400, 30], block_size=16, sparse_count=32, sparse_mode=3),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_parity_small(ora, name):
+    inp = synth.make_inputs(SMALL[name], 7)
+    p = inp["problem"]
+    log("case %s: rows=%d k=%d" % (name, rows_of(p), p["sparse_count"]))
+    vis = vis_of(ora, inp)
+    cols = max(1, int(vis.max()) if vis.size else 1)
+    rc, oidx, oval, osc = ora.indexer(inp, scores_cols=cols)
+    assert rc == 0
+    gidx, gval, _ = run_gpu(inp)
+    k = p["sparse_count"]
+    check_structure(gidx, gval, vis, k)
+    for r in range(rows_of(p)):
+        check_row(r, int(vis[r]), k, gidx[r], gval[r], osc[r, :vis[r]], rtol_of(inp))
+
+
+@pytest.mark.parametrize("name", ["bsnd_int8_causal_bs48_pad", "bsnd_int8_cmp4_bs16", "tnd_int8_prefill_mixed",
+                                  "bsnd_fp8_causal_s2"])
+def test_debug_dump(ora, name):
+    """Dots straight from the matrix cores (int8: bit-exact), scores within
+    tolerance, and the selection equal to the stable top-k of the GPU's own
+    fp32 scores (exact: integer/index work)."""
+    import torch
+    inp = synth.make_inputs(SMALL[name], 11)
+    p = inp["problem"]
+    vis = vis_of(ora, inp)
+    rows, k = rows_of(p), p["sparse_count"]
+    cols = int(vis.max())
+    log("case %s: debug dump rows=%d cols=%d" % (name, rows, cols))
+    ix = make_indexer(inp)
+    dev = device_inputs(inp)
+    gidx, gval, dots, scores = ix.run_debug(dev["query"], dev["key"], dev["weights"], dev["q_scale"],
+                                            dev["k_scale"], dev["block_table"], 0, rows, cols)
+    torch.cuda.synchronize()
+    gidx, gval = gidx.cpu().numpy(), gval.cpu().numpy()
+    dots, scores = dots.cpu().numpy(), scores.cpu().numpy()
+    fp8 = p["qk_dtype"] == 1
+    for r in range(rows):
+        v = int(vis[r])
+        if v == 0:
+            continue
+        _, odots, osc = ora.row_detail(inp, r, 0, v)
+        if fp8:
+            # the f8f6f4 MFMA accumulates in fp32 with its own order
+            assert np.all(np.abs(dots[r, :, :v] - odots) <= 1e-3 * (np.abs(odots) + 64.0))
+        else:
+            assert np.array_equal(dots[r, :, :v].astype(np.float64), odots), "row %d: int8 dots differ" % r
+        ref = osc
+        assert np.all(np.abs(scores[r, :v] - ref) <= ATOL + rtol_of(inp) * np.abs(ref)), "row %d scores" % r
+        n = min(k, v)
+        assert np.array_equal(gidx[r, :n], stable_topk_set(scores[r, :v], k)), "row %d selection" % r
+        assert np.array_equal(gval[r, :n], scores[r, gidx[r, :n]]), "row %d values" % r
+
+
+def test_ties_go_to_lower_index(ora):
+    """Identical keys give bit-identical scores; the lowest indices win."""
+    spec = synth.small(batch=2, s1=2, aslk=[1500, 800], block_size=64, sparse_count=200, sparse_mode=3,
+                       table="identity")
+    inp = synth.make_inputs(spec, 5)
+    keys = inp["key"].reshape(-1, 128)
+    keys[:] = keys[0]
+    kb = inp["k_scale"].reshape(-1)
+    kb[:] = kb[0]
+    vis = vis_of(ora, inp)
+    gidx, gval, _ = run_gpu(inp)
+    rc, oidx, oval, osc = ora.indexer(inp, scores_cols=int(vis.max()))
+    for r in range(rows_of(inp["problem"])):
+        n = min(200, int(vis[r]))
+        assert np.array_equal(gidx[r, :n], np.arange(n)), r
+        assert np.all(gval[r, :n] == gval[r, 0])
+
+
+def test_empty_and_degenerate():
+    import sparse_attention_token_paged_amd as qli
+    for spec in (synth.small(batch=0, s1=4, aslk=[]),
+                 synth.small(layout=synth.TND, batch=1, s1=5, aslq=[0], aslk=[50]),
+                 synth.small(batch=2, s1=2, aslk=[0, 0])):
+        inp = synth.make_inputs(spec, 1)
+        gidx, gval, _ = run_gpu(inp)
+        assert np.all(gidx == -1) and (gval is None or np.all(gval == -np.inf))
+
+
+def test_repeat_runs_identical():
+    inp = synth.make_inputs(SMALL["bsnd_int8_causal_bs48_pad"], 3)
+    dev = device_inputs(inp)
+    a_idx, a_val, ix = run_gpu(inp, dev)
+    b_idx, b_val, _ = run_gpu(inp, dev, ix)
+    assert np.array_equal(a_idx, b_idx) and np.array_equal(a_val, b_val)
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_workload_full_size(ora, name):
+    """Each named workload at full size, in the benchmark's configuration:
+    structure on every row, the full oracle check on sampled rows."""
+    inp = synth.workload(name)
+    p = inp["problem"]
+    rows, k = rows_of(p), p["sparse_count"]
+    log("workload %s: rows=%d k=%d" % (name, rows, k))
+    vis = vis_of(ora, inp)
+    gidx, gval, ix = run_gpu(inp)
+    check_structure(gidx, gval, vis, k)
+    rng = np.random.default_rng(123)
+    picks = sorted(set([0, rows - 1] + rng.choice(rows, size=min(rows, 6), replace=False).tolist()))
+    if p["qk_dtype"] == 1:  # keep the fp8 oracle rows short
+        picks = sorted(set([int(np.argmin(vis))] + picks[:3]))
+    for r in picks:
+        v = int(vis[r])
+        log("  oracle row %d vis %d" % (r, v))
+        if v == 0:
+            continue
+        _, _, osc = ora.row_detail(inp, r, 0, v)
+        check_row(r, v, k, gidx[r], gval[r], osc, rtol_of(inp))

@@ -23,7 +23,7 @@ def run(ora, inp, **kw):
 
 def check_rows(ora, inp, idx, val, sc):
     p = inp["problem"]
-    vis = ora.row_visible(p["layout"], p["batch"], p["s1"], p["sparse_mode"], p["cmp_ratio"],
+    vis = ora.row_visible(p["layout_query"], p["batch"], p["s1"], p["sparse_mode"], p["cmp_ratio"],
                           inp["aslq"], inp["aslk"])
     k = p["sparse_count"]
     for r in range(rows_of(p)):
@@ -83,7 +83,7 @@ def test_tnd_equals_bsnd_for_equal_lengths(ora):
                           sparse_mode=3)
     a = synth.make_inputs(bs_spec, 2)
     b = dict(a)
-    b["problem"] = dict(a["problem"], layout=synth.TND, s1=12)
+    b["problem"] = dict(a["problem"], layout_query=synth.TND, s1=12)
     b["aslq"] = np.array([4, 8, 12], dtype=np.int32)
     ia, va, _ = run(ora, a)
     ib, vb, _ = run(ora, b)
