@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized lightning indexer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--calibrate-copy]
+
+One step is one qli_run (scoring kernel + selection kernel) over one batch of
+seeded synthetic input resident in HBM.  Before every timed step a 512 MiB
+fill evicts L2 and the 256 MB Infinity Cache, so the paged key cache and its
+scales stream from HBM.  Then, as in a decode step where the query, weights,
+query scales, block table and plan have just been produced, those small
+per-step tensors are rewritten from pristine copies (this is the headline
+cache state); the fully cold case (no rewrite) is timed as well and
+reported alongside.  Kernel durations come from HIP events attached to the
+launches themselves (hipExtLaunchKernel); the K steps are bracketed by
+torch.cuda.synchronize() on both sides.
+
+Prints one JSON line: metric / value (visible query-token x key pairs scored
+and selected per second), the roofline of the dominant kernel (the scoring
+kernel), and the CPU oracle timed on the host on a bounded sample of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "query-token×key scores/s incl. top-k; HBM GB/s (decode), MFMA % (prefill)"
+DEFAULT_WORKLOAD = "decode_int8_b24_s4_sk8192"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA, TOP/s
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA, TFLOP/s
+FLUSH_BYTES = 512 << 20
+KERNEL_SOURCE = os.path.join(ROOT, "sparse_attention_token_paged_amd", "csrc", "qli_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def hip_runtime():
+    """The HIP runtime torch already loaded (libqli.so binds to the same one)."""
+    for line in open("/proc/self/maps"):
+        path = line.split()[-1]
+        if path.endswith("libamdhip64.so") or ".so." in path and "libamdhip64" in path:
+            lib = ctypes.CDLL(path)
+            lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            return lib
+    raise RuntimeError("HIP runtime not loaded")
+
+
+class Events:
+    def __init__(self, hip, n: int):
+        self.hip = hip
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev.append(e.value)
+
+    def ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        assert self.hip.hipEventSynchronize(ctypes.c_void_p(self.ev[b])) == 0
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(self.ev[a]),
+                                            ctypes.c_void_p(self.ev[b])) == 0
+        return out.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def algorithmic(info, problem) -> dict:
+    """Bytes the method must move and int8/fp8 ops it must do (one step).
+
+    Every visible key entry is read once per batch (with its ScaleK and the
+    block-table entries that reach it), every active query row once (Q, ScaleQ,
+    W), and the outputs written once; masked or duplicate work is not counted.
+    """
+    sb = 2 if problem["scale_dtype"] == 0 else 4
+    k = problem["sparse_count"]
+    out_row = k * (4 + (4 if problem["return_value"] else 0))
+    inputs = (info.key_entries * (128 + sb) + info.table_entries * 4 +
+              info.active_rows * (64 * 128 + 2 * 64 * sb))
+    direct_rows = info.rows - info.select_rows
+    return dict(
+        inputs=inputs,
+        outputs=info.rows * out_row,
+        score_kernel=inputs + direct_rows * out_row,
+        select_kernel=info.select_rows * out_row,
+        total=inputs + info.rows * out_row,
+        ops=2 * 64 * 128 * info.visible_pairs,
+    )
+
+
+def traffic_from_profiles(workload: str):
+    """Measured HBM bytes per scoring-kernel launch from committed rocprofv3
+    counter summaries, if they were taken on the current kernel source."""
+    path = os.path.join(PROFILES, "traffic_score_kernel_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(inp: dict, info, budget_core_s: float = 20.0) -> dict:
+    """The oracle as it stands, on the host, on a bounded prefix of batches."""
+    import numpy as np
+    import oracle
+    ora = oracle.get()
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    p = dict(inp["problem"])
+    macs_per_pair = 64 * 128
+    est_core_s = info.visible_pairs * macs_per_pair * (2.0e-9 if p["qk_dtype"] == 1 else 1.0e-9)
+    B = p["batch"]
+    nb = max(1, min(B, int(B * budget_core_s / max(est_core_s, 1e-9))))
+    sub = dict(inp)
+    if nb < B:
+        if p["layout_query"] == 0:
+            rows = nb * p["s1"]
+            sub["aslq"] = None if inp["aslq"] is None else np.ascontiguousarray(inp["aslq"][:nb])
+        else:
+            rows = int(inp["aslq"][nb - 1])
+            sub["aslq"] = np.ascontiguousarray(inp["aslq"][:nb])
+            p["s1"] = rows
+        p["batch"] = nb
+        sub["query"] = np.ascontiguousarray(inp["query"][:rows])
+        sub["weights"] = np.ascontiguousarray(inp["weights"][:rows])
+        sub["q_scale"] = np.ascontiguousarray(inp["q_scale"][:rows])
+        sub["aslk"] = np.ascontiguousarray(inp["aslk"][:nb])
+        sub["block_table"] = np.ascontiguousarray(inp["block_table"][:nb])
+    sub["problem"] = p
+    vis = ora.row_visible(p["layout_query"], p["batch"], p["s1"], p["sparse_mode"], p["cmp_ratio"],
+                          sub["aslq"], sub["aslk"])
+    t0 = time.perf_counter()
+    rc, _, _, _ = ora.indexer(sub, nthreads=threads)
+    dt = time.perf_counter() - t0
+    assert rc == 0
+    pairs = int(vis.sum())
+    return {"value": pairs / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
+            "sample": "batches 0..%d of %d (%d rows, %d visible pairs), one full oracle pass "
+                      "(fp64 scores, exact dots, stable top-k), %.2f s wall" % (nb - 1, B, vis.size, pairs, dt)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the indexer runs on a single MI355X here; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import sparse_attention_token_paged_amd as qli
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    qli.load()
+    hip = hip_runtime()
+    inp = synth.workload(args.workload)
+    p = inp["problem"]
+    ix = qli.Indexer(p, inp["aslq"], inp["aslk"])
+    info = ix.info
+    t = lambda a: torch.from_numpy(a).cuda()
+    dev = dict(query=t(inp["query"].view("uint8")), key=t(inp["key"]), weights=t(inp["weights"]),
+               q_scale=t(inp["q_scale"]), k_scale=t(inp["k_scale"]), block_table=t(inp["block_table"]))
+    out_idx, out_val = ix.alloc_outputs()
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    args_run = (dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
+                out_idx, out_val)
+
+    # Pristine copies of the per-step tensors, rewritten before each step.
+    fresh = [(dev["query"], dev["query"].clone()), (dev["weights"], dev["weights"].clone()),
+             (dev["q_scale"], dev["q_scale"].clone()), (dev["block_table"], dev["block_table"].clone()),
+             (ix.plan_dev, ix.plan_dev.clone())]
+
+    def run_steps(n: int, refresh: bool):
+        ev = Events(hip, 4 * n)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s_ in range(n):
+            flush.zero_()
+            if refresh:
+                for dst, src in fresh:
+                    dst.copy_(src)
+            ix.run_timed(*args_run, events=ev.ev[4 * s_:4 * s_ + 4])
+        torch.cuda.synchronize()
+        wall_ = time.perf_counter() - t0
+        has_sel = info.select_rows > 0
+        step = [ev.ms(4 * i, 4 * i + 3 if has_sel else 4 * i + 1) for i in range(n)]
+        score = [ev.ms(4 * i, 4 * i + 1) for i in range(n)]
+        sel = [ev.ms(4 * i + 2, 4 * i + 3) if has_sel else 0.0 for i in range(n)]
+        ev.close()
+        return step, score, sel, wall_
+
+    for _ in range(args.warmup):
+        flush.zero_()
+        ix.run(*args_run)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    step_ms, score_ms, select_ms, wall = run_steps(K, refresh=True)
+    cold_step, cold_score, cold_select, _ = run_steps(K, refresh=False)
+
+    # Back-to-back steps without the fill (inputs may hit in the caches): context only.
+    torch.cuda.synchronize()
+    tw = time.perf_counter()
+    for _ in range(K):
+        ix.run(*args_run)
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - tw) * 1e3 / K
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    ms = statistics.mean(step_ms)
+    alg = algorithmic(info, p)
+    score_avg = statistics.mean(score_ms)
+    prefill = info.kind == 1
+    if prefill:
+        peak = FP8_PEAK_TFLOPS if p["qk_dtype"] == 1 else INT8_PEAK_TOPS
+        achieved = alg["ops"] / (score_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s" if p["qk_dtype"] == 1 else "TOP/s", "frac": round(achieved / peak, 4)}
+    else:
+        achieved = alg["score_kernel"] / (score_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = "score_kernel"
+    roof["kernel_ms"] = round(score_avg, 5)
+    roof["algorithmic_bytes" if not prefill else "algorithmic_ops"] = alg["score_kernel"] if not prefill else alg["ops"]
+    roof["traffic"] = traffic_from_profiles(args.workload)
+
+    result = {
+        "metric": METRIC,
+        "value": info.visible_pairs / (ms * 1e-3),
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if p["qk_dtype"] == 0 else "fp8_e4m3fn",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "layout": "BSND" if p["layout_query"] == 0 else "TND",
+            "batch": p["batch"], "s1_or_t": p["s1"], "block_size": p["block_size"],
+            "sparse_count": p["sparse_count"], "sparse_mode": p["sparse_mode"], "cmp_ratio": p["cmp_ratio"],
+            "visible_pairs": info.visible_pairs, "return_value": p["return_value"],
+        },
+        "roofline": roof,
+        "step": {
+            "ms_median": round(statistics.median(step_ms), 5), "ms_min": round(min(step_ms), 5),
+            "score_kernel_ms": round(score_avg, 5), "select_kernel_ms": round(statistics.mean(select_ms), 5),
+            "hbm_gbs_step": round(alg["total"] / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac_step": round(alg["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_step": alg["total"], "warm_back_to_back_ms": round(warm_ms, 5),
+            "timed_wall_s_incl_cache_fill": round(wall, 4),
+            "cache_state": "key cache and key scales evicted (512 MiB fill); query, weights, query "
+                           "scales, block table and plan rewritten before each step",
+            "all_cold": {"ms_mean": round(statistics.mean(cold_step), 5),
+                         "score_kernel_ms": round(statistics.mean(cold_score), 5),
+                         "select_kernel_ms": round(statistics.mean(cold_select), 5),
+                         "value": info.visible_pairs / (statistics.mean(cold_step) * 1e-3)},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, info)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

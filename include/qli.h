@@ -128,10 +128,16 @@ typedef struct qli_plan_info {
     int64_t visible_pairs;   /* sum over rows of visible key entries (scored pairs) */
     int64_t plan_bytes;
     int64_t workspace_bytes;
+    int64_t key_entries;     /* distinct key entries any row sees: sum over batches of the
+                                largest visible count (each is read once per batch) */
+    int64_t table_entries;   /* block_table entries those key entries span */
+    int64_t active_rows;     /* rows that see at least one key entry */
     int32_t score_items;     /* work items of the scoring stage */
     int32_t select_rows;     /* rows whose visible count exceeds sparse_count */
     int32_t rows_per_item;
     int32_t keys_per_chunk;
+    int32_t kind;            /* 0: decode-shaped tiles, 1: prefill-shaped tiles */
+    int32_t reserved;
 } qli_plan_info;
 
 int qli_plan_info_get(const void *plan_host, qli_plan_info *info);
@@ -153,6 +159,9 @@ int qli_plan_info_get(const void *plan_host, qli_plan_info *info);
  *   block_table   device int32 [B, max_blocks_per_seq]; entry [b][i] is the
  *                 cache block holding entries i*block_size .. of batch b.
  *   workspace     device, workspace_bytes from qli_plan (NULL if 0).
+ *   Alignment (QLI_ERR_ARG otherwise): plan_dev, workspace, query and key
+ *   16 bytes; weights / q_scale 8 bytes (FLOAT16) or 16 bytes (FLOAT32);
+ *   k_scale its element size; block_table and the outputs 4 bytes.
  *   sparse_indices device int32 [rows, sparse_count] (out).
  *   sparse_values  device float [rows, sparse_count] (out) or NULL when
  *                  return_value == 0.
@@ -187,6 +196,23 @@ int qli_run_debug(const qli_problem *p, const void *plan_host,
                   float *sparse_values, int64_t row0, int64_t row1,
                   int64_t cols, void *dots_out, float *scores_out,
                   void *stream);
+
+/*
+ * qli_run_timed -- qli_run whose kernel launches also record four
+ * caller-created hipEvent_t handles (passed as void*): events[0] / events[1]
+ * at the start / end of the scoring kernel and events[2] / events[3] at the
+ * start / end of the selection kernel (left unrecorded when no row needs a
+ * selection).  The events are attached to the launches themselves
+ * (hipExtLaunchKernel), so they time the kernels without extra stream
+ * commands.  For throughput measurement; outputs and errors are those of
+ * qli_run.  events must point to 4 handles; any handle may be NULL.
+ */
+int qli_run_timed(const qli_problem *p, const void *plan_host,
+                  const void *plan_dev, const void *query, const void *key,
+                  const void *weights, const void *q_scale,
+                  const void *k_scale, const int32_t *block_table,
+                  void *workspace, int32_t *sparse_indices,
+                  float *sparse_values, void *const *events, void *stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ SCALE_F16, SCALE_F32 = 0, 1
 LAYOUT_BSND, LAYOUT_TND = 0, 1
 INT64_MAX = (1 << 63) - 1
 
-EXPORTED = ("qli_status_string", "qli_plan", "qli_plan_info_get", "qli_run", "qli_run_debug")
+EXPORTED = ("qli_status_string", "qli_plan", "qli_plan_info_get", "qli_run", "qli_run_debug", "qli_run_timed")
 
 c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
@@ -54,8 +54,9 @@ class Problem(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     """Mirror of ``qli_plan_info``."""
     _fields_ = [("rows", c_i64), ("visible_pairs", c_i64), ("plan_bytes", c_i64),
-                ("workspace_bytes", c_i64), ("score_items", c_i32), ("select_rows", c_i32),
-                ("rows_per_item", c_i32), ("keys_per_chunk", c_i32)]
+                ("workspace_bytes", c_i64), ("key_entries", c_i64), ("table_entries", c_i64),
+                ("active_rows", c_i64), ("score_items", c_i32), ("select_rows", c_i32),
+                ("rows_per_item", c_i32), ("keys_per_chunk", c_i32), ("kind", c_i32), ("reserved", c_i32)]
 
 
 _lib = None
@@ -85,6 +86,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.qli_run_debug.argtypes = ([ctypes.POINTER(Problem), c_p, c_p] + [c_p] * 9 +
                                       [c_i64, c_i64, c_i64, c_p, c_p, c_p])
         lib.qli_run_debug.restype = ctypes.c_int
+        lib.qli_run_timed.argtypes = [ctypes.POINTER(Problem), c_p, c_p] + [c_p] * 9 + [c_p, c_p]
+        lib.qli_run_timed.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -145,6 +148,16 @@ def qli_run(problem: Problem, plan_host, plan_dev, query, key, weights, q_scale,
                           _addr(sparse_values), stream)
 
 
+def qli_run_timed(problem: Problem, plan_host, plan_dev, query, key, weights, q_scale, k_scale,
+                  block_table, workspace, sparse_indices, sparse_values, events, stream=None) -> int:
+    """events: 4 raw hipEvent_t handles (ints) or None: score start/end, select start/end."""
+    arr = (c_p * 4)(*[e if e else None for e in events])
+    return load().qli_run_timed(ctypes.byref(problem), _addr(plan_host), _addr(plan_dev), _addr(query),
+                                _addr(key), _addr(weights), _addr(q_scale), _addr(k_scale),
+                                _addr(block_table), _addr(workspace), _addr(sparse_indices),
+                                _addr(sparse_values), arr, stream)
+
+
 def qli_run_debug(problem: Problem, plan_host, plan_dev, query, key, weights, q_scale, k_scale,
                   block_table, workspace, sparse_indices, sparse_values, row0, row1, cols,
                   dots_out, scores_out, stream=None) -> int:
@@ -199,6 +212,15 @@ class Indexer:
                      block_table, self.workspace, out_idx, out_val, st)
         if rc != QLI_OK:
             raise QliError(rc, "qli_run")
+        return out_idx, out_val
+
+    def run_timed(self, query, key, weights, q_scale, k_scale, block_table, out_idx, out_val, events,
+                  stream: Optional[int] = None):
+        st = current_stream() if stream is None else stream
+        rc = qli_run_timed(self.problem, self.plan_host, self.plan_dev, query, key, weights, q_scale, k_scale,
+                           block_table, self.workspace, out_idx, out_val, events, st)
+        if rc != QLI_OK:
+            raise QliError(rc, "qli_run_timed")
         return out_idx, out_val
 
     def run_debug(self, query, key, weights, q_scale, k_scale, block_table, row0, row1, cols,

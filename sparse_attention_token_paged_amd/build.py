@@ -32,6 +32,7 @@ def command(out: str) -> list:
     return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
             "-fvisibility=hidden", "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INCLUDE, "-x", "hip"] + SOURCES + ["-o", out]
 
 

@@ -117,6 +117,7 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   for (int b = 0; b < p.batch; b++) {
     if (aslk[b] < 0) return QLI_ERR_ARG;
     const int64_t stored = aslk[b] / p.cmp_ratio;
+    if (stored >= kMaxEntries) return QLI_ERR_SIZE;
     const int64_t need = (stored + p.block_size - 1) / p.block_size;
     if (need > p.max_blocks_per_seq) return QLI_ERR_ARG;  // 约束说明: block_table second dim
     if (bsnd) {
@@ -133,17 +134,22 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   }
 
   out.rows.assign(rows, RowInfo{-1, 0, -1});
-  int64_t max_s1b = 0, visible = 0, max_vis = 0;
+  int64_t max_s1b = 0, visible = 0, max_vis = 0, key_entries = 0, table_entries = 0, active = 0;
   for (int b = 0; b < p.batch; b++) {
     max_s1b = std::max(max_s1b, qcnt[b]);
+    int64_t batch_max = 0;
     for (int64_t i = 0; i < qcnt[b]; i++) {
       const int64_t v = visible_entries(p.sparse_mode, p.cmp_ratio, aslk[b], qcnt[b], i);
       RowInfo& ri = out.rows[qbeg[b] + i];
       ri.batch = b;
       ri.vis = (int32_t)v;
       visible += v;
-      max_vis = std::max(max_vis, v);
+      active += v > 0;
+      batch_max = std::max(batch_max, v);
     }
+    max_vis = std::max(max_vis, batch_max);
+    key_entries += batch_max;
+    table_entries += (batch_max + p.block_size - 1) / p.block_size;
   }
 
   // Tile shape: decode-like problems (few query tokens per sequence) put
@@ -175,12 +181,10 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   // whole rows (up to kMaxChunk) for prefill.
   int64_t key_work = 0;
   for (const Group& g : groups) key_work += g.maxv;
-  int chunk = kMaxChunk;
-  if (!prefill) {
-    int64_t c = (key_work + 1023) / 1024;
-    c = (c + kTileKeys - 1) / kTileKeys * kTileKeys;
-    chunk = (int)std::min<int64_t>(kMaxChunk, std::max<int64_t>(256, c));
-  }
+  // Decode items stage one whole chunk of kDecodeChunk entries in LDS;
+  // prefill items walk up to kMaxChunk entries in 64-entry tiles.
+  (void)key_work;
+  const int chunk = prefill ? kMaxChunk : kDecodeChunk;
 
   for (const Group& g : groups) {
     if (g.maxv == 0) {
@@ -223,6 +227,9 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   h.n_select = (int32_t)out.select.size();
   h.chunk = chunk;
   h.max_vis = (int32_t)max_vis;
+  h.key_entries = key_entries;
+  h.table_entries = table_entries;
+  h.active_rows = active;
   h.off_rows = align16(sizeof(PlanHeader));
   h.off_items = align16(h.off_rows + (int64_t)sizeof(RowInfo) * rows);
   h.off_select = align16(h.off_items + (int64_t)sizeof(Item) * h.n_items);
@@ -246,6 +253,15 @@ int check_run_args(const RunArgs& a) {
   if (h->n_items > 0 && (!a.query || !a.key || !a.weights || !a.q_scale || !a.k_scale || !a.block_table))
     return QLI_ERR_ARG;
   if (h->workspace_bytes > 0 && !a.workspace) return QLI_ERR_ARG;
+  // Vector loads need aligned bases: 16 bytes for query, key, the fp32
+  // weights / q_scale, plan and workspace; the element size elsewhere.
+  auto aligned = [](const void* ptr, uintptr_t n) { return ((uintptr_t)ptr % n) == 0; };
+  const uintptr_t sb = a.p->scale_dtype == QLI_SCALE_F16 ? 2 : 4;
+  if (!aligned(a.plan_dev, 16) || !aligned(a.workspace, 16) || !aligned(a.query, 16) ||
+      !aligned(a.key, 16) || !aligned(a.weights, 4 * sb) || !aligned(a.q_scale, 4 * sb) ||
+      !aligned(a.k_scale, sb) || !aligned(a.block_table, 4) || !aligned(a.sparse_indices, 4) ||
+      !aligned(a.sparse_values, 4))
+    return QLI_ERR_ARG;
   return QLI_OK;
 }
 
@@ -301,10 +317,15 @@ QLI_EXPORT int qli_plan_info_get(const void* plan_host, qli_plan_info* info) {
   info->visible_pairs = h->visible_pairs;
   info->plan_bytes = h->plan_bytes;
   info->workspace_bytes = h->workspace_bytes;
+  info->key_entries = h->key_entries;
+  info->table_entries = h->table_entries;
+  info->active_rows = h->active_rows;
   info->score_items = h->n_items;
   info->select_rows = h->n_select;
   info->rows_per_item = h->rows_per_item;
   info->keys_per_chunk = h->chunk;
+  info->kind = h->kind;
+  info->reserved = 0;
   return QLI_OK;
 }
 
@@ -313,7 +334,7 @@ static int run_common(const qli_problem* p, const void* plan_host, const void* p
                       const void* q_scale, const void* k_scale, const int32_t* block_table,
                       void* workspace, int32_t* sparse_indices, float* sparse_values,
                       int64_t row0, int64_t row1, int64_t cols, void* dots_out,
-                      float* scores_out, bool dump, void* stream) {
+                      float* scores_out, bool dump, void* const* events, void* stream) {
   int rc = validate_problem(p);
   if (rc != QLI_OK) return rc;
   if (!plan_matches(p, plan_host)) return QLI_ERR_PLAN;
@@ -343,8 +364,8 @@ static int run_common(const qli_problem* p, const void* plan_host, const void* p
     if (row1 > row0 && cols > 0 && (!dots_out || !scores_out)) return QLI_ERR_ARG;
   }
   if (a.hdr->rows == 0) return QLI_OK;
-  if (launch_score(a, dump) != 0) return QLI_ERR_HIP;
-  if (a.hdr->n_select > 0 && launch_select(a) != 0) return QLI_ERR_HIP;
+  if (launch_score(a, dump, events) != 0) return QLI_ERR_HIP;
+  if (a.hdr->n_select > 0 && launch_select(a, events) != 0) return QLI_ERR_HIP;
   return QLI_OK;
 }
 
@@ -355,7 +376,18 @@ QLI_EXPORT int qli_run(const qli_problem* p, const void* plan_host, const void* 
                        void* stream) {
   return run_common(p, plan_host, plan_dev, query, key, weights, q_scale, k_scale, block_table,
                     workspace, sparse_indices, sparse_values, 0, 0, 0, nullptr, nullptr, false,
-                    stream);
+                    nullptr, stream);
+}
+
+QLI_EXPORT int qli_run_timed(const qli_problem* p, const void* plan_host, const void* plan_dev,
+                             const void* query, const void* key, const void* weights,
+                             const void* q_scale, const void* k_scale,
+                             const int32_t* block_table, void* workspace,
+                             int32_t* sparse_indices, float* sparse_values, void* const* events,
+                             void* stream) {
+  return run_common(p, plan_host, plan_dev, query, key, weights, q_scale, k_scale, block_table,
+                    workspace, sparse_indices, sparse_values, 0, 0, 0, nullptr, nullptr, false,
+                    events, stream);
 }
 
 QLI_EXPORT int qli_run_debug(const qli_problem* p, const void* plan_host, const void* plan_dev,
@@ -367,5 +399,5 @@ QLI_EXPORT int qli_run_debug(const qli_problem* p, const void* plan_host, const 
                              void* stream) {
   return run_common(p, plan_host, plan_dev, query, key, weights, q_scale, k_scale, block_table,
                     workspace, sparse_indices, sparse_values, row0, row1, cols, dots_out,
-                    scores_out, true, stream);
+                    scores_out, true, nullptr, stream);
 }

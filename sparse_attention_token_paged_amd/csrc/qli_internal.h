@@ -17,6 +17,8 @@ constexpr int kHeads = 64;       // query heads (QLI-README 约束说明)
 constexpr int kDim = 128;        // head dim of query and key (约束说明)
 constexpr int kTileKeys = 64;    // keys staged in LDS per pipeline step
 constexpr int kMaxChunk = 4096;  // keys per score item, upper bound
+constexpr int kDecodeChunk = 256;        // keys per decode item (whole chunk staged in LDS)
+constexpr int64_t kMaxEntries = 1 << 22;  // compressed entries per sequence (exact reciprocal division)
 constexpr int kMaxChunkBlocks = kMaxChunk / 16 + 2;  // block ids one item may touch
 
 enum PlanKind : int32_t { kKindDecode = 0, kKindPrefill = 1 };
@@ -40,7 +42,11 @@ struct PlanHeader {
   int32_t n_select;
   int32_t chunk;             // keys per score item (multiple of kTileKeys)
   int32_t max_vis;
-  int32_t reserved[6];
+  int32_t reserved[2];
+  int64_t key_entries;       // sum over batches of the largest visible count
+  int64_t table_entries;     // block-table entries spanned by those entries
+  int64_t active_rows;       // rows with at least one visible entry
+  int64_t reserved64;
 };
 static_assert(sizeof(PlanHeader) % 16 == 0, "header keeps the tables aligned");
 
@@ -84,7 +90,9 @@ struct RunArgs {
   float* scores_out;
   void* stream;
 };
-int launch_score(const RunArgs& a, bool dump);
-int launch_select(const RunArgs& a);
+// Optional timing: events[0..1] bracket the scoring kernel, events[2..3] the
+// selection kernel (recorded by the launch itself).
+int launch_score(const RunArgs& a, bool dump, void* const* events);
+int launch_select(const RunArgs& a, void* const* events);
 
 }  // namespace qli

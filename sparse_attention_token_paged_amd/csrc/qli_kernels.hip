@@ -27,9 +27,11 @@
 //   threshold digit found with a block scan; ties at the threshold resolved
 //   towards the lower index with wave ballots and mbcnt prefix counts; the
 //   selected entries written in ascending index order.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "qli_internal.h"
 
@@ -57,7 +59,7 @@ struct ScoreParams {
   int32_t block_size;
   int32_t max_blocks;
   int32_t k;
-  int32_t pad_;
+  uint32_t bs_magic;  // floor(2^32 / block_size) + 1: j / block_size == umulhi(j, bs_magic) for j < 2^22
   int64_t d_row0, d_row1, d_cols;
   void* dots;
   float* dscores;
@@ -70,6 +72,24 @@ __device__ __forceinline__ float load_scale(const void* base, int64_t i) {
     return (float)(static_cast<const _Float16*>(base)[i]);
   else
     return static_cast<const float*>(base)[i];
+}
+
+// Raw bits of a ScaleK element, converted only when staged to LDS.
+template <int QK>
+__device__ __forceinline__ uint32_t load_scale_bits(const void* base, int64_t i) {
+  if constexpr (QK == QLI_QK_INT8)
+    return static_cast<const uint16_t*>(base)[i];
+  else
+    return static_cast<const uint32_t*>(base)[i];
+}
+template <int QK>
+__device__ __forceinline__ float scale_from_bits(uint32_t b) {
+  if constexpr (QK == QLI_QK_INT8) {
+    const uint16_t h = (uint16_t)b;
+    return (float)__builtin_bit_cast(_Float16, h);
+  } else {
+    return __uint_as_float(b);
+  }
 }
 
 // Sum of the four lanes {l%16 + 16m}: permlane32 then permlane16 swaps.
@@ -97,7 +117,8 @@ template <int QK>
 __device__ __forceinline__ int chunk_hi(int q) { return QK == QLI_QK_INT8 ? q + 4 : 2 * q + 1; }
 
 template <int QK, int RW, int WPR, bool DUMP>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams P) {
+__global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(RW == 1 ? 4 : 2)))
+void score_kernel(ScoreParams P) {
   constexpr int NT = 4 / WPR;  // 16-key n-tiles per wave per 64-key tile
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(P.plan);
   const RowInfo* rinfo = reinterpret_cast<const RowInfo*>(P.plan + hdr->off_rows);
@@ -175,6 +196,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams P) {
   // chunk tid%8.  The logical chunk stored there is XOR-swizzled with bits 1..3
   // of the key row so that the MFMA-layout reads (16 rows, same chunk) hit
   // distinct banks.  Block / slot positions advance incrementally per tile.
+  // Two register sets hold the tiles in flight (tile j uses set j % 2); the
+  // ScaleK bits stay raw until the stash so no wait is forced at issue time.
   const int cfetch = (tid & 7) ^ ((tid >> 4) & 7);
   int bi[2], slot[2];
 #pragma unroll
@@ -189,20 +212,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams P) {
     sbi = j / bs - fb;
     sslot = j % bs;
   }
-  int4 kr[2];
-  float skr = 0.f;
+  int4 kr[2][2];
+  uint32_t skr[2] = {0u, 0u};
   __syncthreads();  // lds_blk is ready
 
-  auto fetch = [&](int t) {
+  auto fetch = [&](int t, auto set_) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_)::value;
     const int tb = key0 + t * kTileKeys;
 #pragma unroll
     for (int p = 0; p < 2; p++) {
       const int j = tb + 32 * p + (tid >> 3);
       if (j < kend) {
         const uint8_t* src = P.key + (int64_t)lds_blk[bi[p]] * P.stride + slot[p] * kDim + cfetch * 16;
-        kr[p] = *reinterpret_cast<const int4*>(src);
+        kr[S][p] = *reinterpret_cast<const int4*>(src);
       } else {
-        kr[p] = make_int4(0, 0, 0, 0);
+        kr[S][p] = make_int4(0, 0, 0, 0);
       }
       slot[p] += kTileKeys;
       while (slot[p] >= bs) {
@@ -212,7 +236,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams P) {
     }
     if (tid < kTileKeys) {
       const int j = tb + tid;
-      skr = j < kend ? load_scale<QK>(P.k_scale, (int64_t)lds_blk[sbi] * bs + sslot) : 0.f;
+      skr[S] = j < kend ? load_scale_bits<QK>(P.k_scale, (int64_t)lds_blk[sbi] * bs + sslot) : 0u;
       sslot += kTileKeys;
       while (sslot >= bs) {
         sslot -= bs;
@@ -220,14 +244,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams P) {
       }
     }
   };
-  auto stash = [&](int s) {
+  auto stash = [&](int s, auto set_) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_)::value;
     int4* dst = reinterpret_cast<int4*>(&lds_k[s][0]);
-    dst[tid] = kr[0];
-    dst[kScoreThreads + tid] = kr[1];
-    if (tid < kTileKeys) lds_sk[s][tid] = skr;
+    dst[tid] = kr[S][0];
+    dst[kScoreThreads + tid] = kr[S][1];
+    if (tid < kTileKeys) lds_sk[s][tid] = scale_from_bits<QK>(skr[S]);
   };
 
-  auto compute = [&](int t, int s) {
+  auto compute = [&](int t, int s) __attribute__((always_inline)) {
     const int tb = key0 + t * kTileKeys;
 #pragma unroll
     for (int n = 0; n < NT; n++) {
@@ -241,7 +266,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams P) {
       const int j = tb + kk;
 #pragma unroll
       for (int rr = 0; rr < RW; rr++) {
-        if (!rok[rr]) continue;
+        if (!rok[rr]) break;  // valid rows of a wave are a prefix
         float acc = 0.f;
         v4i di[4];
         v4f df[4];
@@ -303,17 +328,245 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams P) {
     }
   };
 
+  // Pipeline: LDS stages alternate per tile; while tile t is computed, the
+  // loads of tiles t+1 and t+2 are in flight in the two register sets.
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
   const int ntiles = (it.nkeys + kTileKeys - 1) / kTileKeys;
-  fetch(0);
-  stash(0);
-  if (ntiles > 1) fetch(1);
+  fetch(0, Set0{});
+  if (ntiles > 1) fetch(1, Set1{});
+  stash(0, Set0{});
+  if (ntiles > 2) fetch(2, Set0{});
   __syncthreads();
-  for (int t = 0; t < ntiles; t++) {
-    const int s = t & 1;
-    if (t + 1 < ntiles) stash(s ^ 1);
-    if (t + 2 < ntiles) fetch(t + 2);
-    compute(t, s);
+  auto step = [&](int t, auto set_next) __attribute__((always_inline)) {
+    // set_next holds tile t+1; after its stash it receives tile t+3
+    compute(t, t & 1);
+    if (t + 1 < ntiles) stash((t + 1) & 1, set_next);
+    if (t + 3 < ntiles) fetch(t + 3, set_next);
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, Set1{});
+    if (t + 1 < ntiles) step(t + 1, Set0{});
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode-shaped items: one chunk of kDecodeChunk entries, 1, 2 or 4 rows.
+// ---------------------------------------------------------------------------
+
+// Sum over the four lane groups of four per-lane partials, scattered so that
+// lane (q, c) ends with the total of partial q (a reduce-scatter in two
+// permlane steps): after it, lane q*16 + c holds key q*16 + c of the tile.
+__device__ __forceinline__ float reduce_scatter4(float a0, float a1, float a2, float a3) {
+  // halves: the lower 32 lanes keep partials 0/1, the upper 32 keep 2/3
+  auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a2), false, false);
+  auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(a1), __float_as_uint(a3), false, false);
+  const float s02 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  const float s13 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+  // rows of 16: even rows keep the 0/2 partial, odd rows the 1/3 partial
+  auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
+template <int QK, int RT, bool DUMP>
+__global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams P) {
+  constexpr int CH = kDecodeChunk;
+  constexpr int NTILE = CH / kTileKeys;   // 64-entry tiles per chunk
+  constexpr int WPR = 4 / RT;             // waves per row
+  constexpr int LOADS = CH * kDim / (kScoreThreads * 16);  // 16-byte key loads per thread
+  constexpr int SB = QK == QLI_QK_INT8 ? 2 : 4;           // scale bytes
+  typedef __attribute__((address_space(3))) void lds_t;
+
+  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(P.plan);
+  const RowInfo* rinfo = reinterpret_cast<const RowInfo*>(P.plan + hdr->off_rows);
+  const Item it = reinterpret_cast<const Item*>(P.plan + hdr->off_items)[blockIdx.x];
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[CH * kDim];
+  // A 2-byte direct-to-LDS load fills a 4-byte slot per lane (value in the
+  // low half), so ScaleK takes 4 bytes per entry for both dtypes.
+  __shared__ __attribute__((aligned(16))) uint32_t lds_sk[CH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int q = lane >> 4;
+  const int c16 = lane & 15;
+  const int k = P.k;
+
+  if (it.flags & kItemPad) {
+    for (int u = 0; u < it.nrows; u++) {
+      const int64_t r = it.row0 + u;
+      const int vis = rinfo[r].vis;
+      if (vis >= k) continue;
+      for (int pos = vis + tid; pos < k; pos += kScoreThreads) {
+        P.idx_out[r * k + pos] = -1;
+        if (P.val_out) P.val_out[r * k + pos] = -INFINITY;
+      }
+    }
+  }
+  if (it.nkeys <= 0) return;  // uniform across the workgroup
+
+  // Block ids of the chunk: lane l of every wave holds entry fb + l.
+  const int bs = P.block_size;
+  const int key0 = it.key0;
+  const int kend = key0 + it.nkeys;
+  const int fb = (int)__umulhi((uint32_t)key0, P.bs_magic);
+  const int nblk = (int)__umulhi((uint32_t)(kend - 1), P.bs_magic) - fb + 1;
+  const int32_t btv = lane < nblk ? P.block_table[(int64_t)it.batch * P.max_blocks + fb + lane] : 0;
+
+  // The whole chunk goes to LDS with direct-to-LDS loads.  Wave w's load i
+  // fills LDS bytes [(4i + w) * 1024, +1024), lane l the 16 bytes at l*16:
+  // key row kk = 32i + 8w + l/8, physical chunk l%8, which holds logical
+  // chunk (l%8) ^ ((kk>>1)&7) so that MFMA-layout reads are conflict-free.
+#pragma unroll
+  for (int i = 0; i < LOADS; i++) {
+    const int kk = 32 * i + 8 * wave + (lane >> 3);
+    const int j = key0 + kk;
+    // the block id comes from another lane: shuffle with every lane active
+    const int jc = min(j, kend - 1);
+    const int b = (int)__umulhi((uint32_t)jc, P.bs_magic);
+    const int blk = __shfl(btv, b - fb, 64);
+    if (j < kend) {
+      const int slot = j - b * bs;
+      const int c = (lane & 7) ^ ((kk >> 1) & 7);
+      const uint8_t* src = P.key + (int64_t)blk * P.stride + slot * kDim + c * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_t*)&lds_k[(4 * i + wave) * 1024], 16, 0, 0);
+    }
+  }
+  // ScaleK of every entry of the chunk: thread tid fetches entry tid.
+  {
+    const int j = key0 + tid;
+    const int jc = min(j, kend - 1);
+    const int b = (int)__umulhi((uint32_t)jc, P.bs_magic);
+    const int blk = __shfl(btv, b - fb, 64);
+    if (j < kend) {
+      const int slot = j - b * bs;
+      const uint8_t* src = static_cast<const uint8_t*>(P.k_scale) + ((int64_t)blk * bs + slot) * SB;
+      if constexpr (SB == 2)
+        __builtin_amdgcn_global_load_lds(src, (lds_t*)&lds_sk[wave * 64], 2, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(src, (lds_t*)&lds_sk[wave * 64], 4, 0, 0);
+    }
+  }
+
+  // This wave's row: query fragments and folded weights w' = W * ScaleQ.
+  const int u = wave / WPR;
+  const int sub = wave % WPR;
+  const bool rok = u < it.nrows;
+  const int64_t r = it.row0 + (rok ? u : 0);
+  const RowInfo ri = rinfo[r];
+  const int rvis = rok ? ri.vis : 0;
+  const int64_t rws = ri.ws_off;
+  Frag qa[4];
+  float wq[16];
+  {
+    const uint8_t* qrow = P.query + r * (kHeads * kDim);
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      const uint8_t* qh = qrow + (16 * m + c16) * kDim;
+      qa[m].lo = *reinterpret_cast<const v4i*>(qh + 16 * chunk_lo<QK>(q));
+      qa[m].hi = *reinterpret_cast<const v4i*>(qh + 16 * chunk_hi<QK>(q));
+    }
+    // heads 16m + 4q + i, i = 0..3, are consecutive: one vector load per m
+    const int64_t e0 = r * kHeads + 4 * q;
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      if constexpr (QK == QLI_QK_INT8) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const h4 w = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.weights) + e0 + 16 * m);
+        const h4 sq = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.q_scale) + e0 + 16 * m);
+#pragma unroll
+        for (int i = 0; i < 4; i++) wq[4 * m + i] = (float)w[i] * (float)sq[i];
+      } else {
+        const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(P.weights) + e0 + 16 * m);
+        const float4 sq = *reinterpret_cast<const float4*>(static_cast<const float*>(P.q_scale) + e0 + 16 * m);
+        wq[4 * m + 0] = w.x * sq.x;
+        wq[4 * m + 1] = w.y * sq.y;
+        wq[4 * m + 2] = w.z * sq.z;
+        wq[4 * m + 3] = w.w * sq.w;
+      }
+    }
+  }
+  __syncthreads();  // every direct-to-LDS load has landed
+
+  int32_t* oi = P.idx_out + r * k;
+  float* ov = P.val_out ? P.val_out + r * k : nullptr;
+  // This wave's tiles: sub, sub + WPR, ... (64 entries each).
+#pragma unroll
+  for (int tt = 0; tt < NTILE / WPR; tt++) {
+    const int t = sub + tt * WPR;
+    const int tb = key0 + t * kTileKeys;
+    if (!rok || tb >= kend || tb >= rvis) break;  // uniform per wave
+    float part[4];
+#pragma unroll
+    for (int n = 0; n < 4; n++) {
+      const int kk = t * kTileKeys + n * 16 + c16;
+      const uint8_t* krow = &lds_k[kk * kDim];
+      const int sw = (kk >> 1) & 7;
+      Frag b;
+      b.lo = *reinterpret_cast<const v4i*>(krow + ((chunk_lo<QK>(q) ^ sw) << 4));
+      b.hi = *reinterpret_cast<const v4i*>(krow + ((chunk_hi<QK>(q) ^ sw) << 4));
+      float acc = 0.f;
+      v4i di[4];
+      v4f df[4];
+      if constexpr (QK == QLI_QK_INT8) {
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+          di[m] = v4i{0, 0, 0, 0};
+          di[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[m].lo, b.lo, di[m], 0, 0, 0);
+          di[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[m].hi, b.hi, di[m], 0, 0, 0);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) acc = __builtin_fmaf(wq[4 * m + i], (float)max(di[m][i], 0), acc);
+      } else {
+        const v8i bb = __builtin_shufflevector(b.lo, b.hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+          const v8i aa = __builtin_shufflevector(qa[m].lo, qa[m].hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          df[m] = v4f{0.f, 0.f, 0.f, 0.f};
+          df[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa, bb, df[m], 0, 0, 0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) acc = __builtin_fmaf(wq[4 * m + i], __builtin_fmaxf(df[m][i], 0.f), acc);
+      }
+      part[n] = acc;
+      if constexpr (DUMP) {
+        const int j = key0 + kk;
+        if (r >= P.d_row0 && r < P.d_row1 && j < rvis && j < P.d_cols) {
+          const int64_t base = (r - P.d_row0) * kHeads;
+#pragma unroll
+          for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const int64_t o = (base + 16 * m + 4 * q + i) * P.d_cols + j;
+              if constexpr (QK == QLI_QK_INT8)
+                static_cast<int32_t*>(P.dots)[o] = di[m][i];
+              else
+                static_cast<float*>(P.dots)[o] = df[m][i];
+            }
+        }
+      }
+    }
+    // lane l now owns entry t*64 + l of the chunk
+    const int kk = t * kTileKeys + lane;
+    const int j = key0 + kk;
+    const float score = reduce_scatter4(part[0], part[1], part[2], part[3]) * scale_from_bits<QK>(lds_sk[kk]);
+    if (j < rvis) {
+      if (rws >= 0) {
+        P.ws[rws + j] = score;
+      } else {
+        oi[j] = j;
+        if (ov) ov[j] = score;
+      }
+      if constexpr (DUMP) {
+        if (r >= P.d_row0 && r < P.d_row1 && j < P.d_cols) P.dscores[(r - P.d_row0) * P.d_cols + j] = score;
+      }
+    }
   }
 }
 
@@ -362,6 +615,8 @@ __device__ int block_exclusive_scan(int v, int* tmp) {
   return before + incl - v;
 }
 
+constexpr int kSelBatch = 8;  // independent loads in flight per thread
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams S) {
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(S.plan);
   const RowInfo* rinfo = reinterpret_cast<const RowInfo*>(S.plan + hdr->off_rows);
@@ -381,15 +636,45 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams S) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool cached = n <= kSelCache;
-  auto key_at = [&](int e) -> uint32_t { return cached ? cache[e] : order_key(sc[e]); };
 
-  // Bits shared by every key (AND == OR there) need no radix pass.
+  // Visits every score this thread owns (e = tid + i * kSelThreads) as its
+  // order key, kSelBatch loads at a time.
+  auto for_each_key = [&](auto&& f) {
+    for (int base = 0; base < n; base += kSelThreads * kSelBatch) {
+      uint32_t u[kSelBatch];
+#pragma unroll
+      for (int i = 0; i < kSelBatch; i++) {
+        const int e = base + i * kSelThreads + tid;
+        u[i] = e < n ? (cached ? cache[e] : order_key(sc[e])) : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < kSelBatch; i++) {
+        const int e = base + i * kSelThreads + tid;
+        if (e < n) f(e, u[i]);
+      }
+    }
+  };
+
+  // First pass: stage the keys in LDS when they fit, and find the bits every
+  // key shares (AND == OR there), which need no radix pass.
   uint32_t a = 0xFFFFFFFFu, o = 0u;
-  for (int e = tid; e < n; e += kSelThreads) {
-    const uint32_t u = order_key(sc[e]);
-    if (cached) cache[e] = u;
-    a &= u;
-    o |= u;
+  for (int base = 0; base < n; base += kSelThreads * kSelBatch) {
+    float v[kSelBatch];
+#pragma unroll
+    for (int i = 0; i < kSelBatch; i++) {
+      const int e = base + i * kSelThreads + tid;
+      v[i] = e < n ? sc[e] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kSelBatch; i++) {
+      const int e = base + i * kSelThreads + tid;
+      if (e < n) {
+        const uint32_t u = order_key(v[i]);
+        if (cached) cache[e] = u;
+        a &= u;
+        o |= u;
+      }
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -430,10 +715,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams S) {
     const int nb = 1 << width;
     for (int b = tid; b < nb; b += kSelThreads) hist[b] = 0;
     __syncthreads();
-    for (int e = tid; e < n; e += kSelThreads) {
-      const uint32_t u = key_at(e);
+    for_each_key([&](int, uint32_t u) {
       if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1);
-    }
+    });
     __syncthreads();
     // Thread t owns digits nb-1-2t and nb-2-2t (descending order).
     const int d0 = nb - 1 - 2 * tid, d1 = d0 - 1;
@@ -461,22 +745,32 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams S) {
     whole_bin = count == kk;
   }
 
-  // Emit in ascending index order: each wave owns one contiguous segment.
+  // Emit in ascending index order: each wave owns one contiguous segment,
+  // walked 64 entries per step, kSelBatch steps per batch of loads.
   const int seg = (((n + kSelWaves - 1) / kSelWaves) + 63) & ~63;
   const int beg = min(n, wave * seg);
   const int end = min(n, beg + seg);
-  int ngt = 0, neq = 0;
-  for (int e0 = beg; e0 < end; e0 += 64) {
-    const int e = e0 + lane;
-    bool gt = false, eq = false;
-    if (e < end) {
-      const uint32_t m = key_at(e) & mask;
-      gt = m > prefix;
-      eq = m == prefix;
+  auto segment = [&](auto&& f) {
+    for (int e0 = beg; e0 < end; e0 += 64 * kSelBatch) {
+      uint32_t u[kSelBatch];
+#pragma unroll
+      for (int i = 0; i < kSelBatch; i++) {
+        const int e = e0 + 64 * i + lane;
+        u[i] = e < end ? (cached ? cache[e] : order_key(sc[e])) : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < kSelBatch; i++) {
+        const int e = e0 + 64 * i + lane;
+        if (e0 + 64 * i < end) f(e, e < end, u[i]);
+      }
     }
-    ngt += __popcll(__ballot(gt));
-    neq += __popcll(__ballot(eq));
-  }
+  };
+  int ngt = 0, neq = 0;
+  segment([&](int, bool live, uint32_t u) {
+    const uint32_t m = u & mask;
+    ngt += __popcll(__ballot(live && m > prefix));
+    neq += __popcll(__ballot(live && m == prefix));
+  });
   if (lane == 0) {
     cnt_gt[wave] = ngt;
     cnt_eq[wave] = neq;
@@ -490,16 +784,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams S) {
   int32_t* oi = S.idx_out + row * k;
   float* ov = S.val_out ? S.val_out + row * k : nullptr;
   int run_eq = eq_before, run_sel = sel_before;
-  for (int e0 = beg; e0 < end; e0 += 64) {
-    const int e = e0 + lane;
-    bool gt = false, eq = false;
-    uint32_t u = 0u;
-    if (e < end) {
-      u = key_at(e);
-      const uint32_t m = u & mask;
-      gt = m > prefix;
-      eq = m == prefix;
-    }
+  segment([&](int e, bool live, uint32_t u) {
+    const uint32_t m = u & mask;
+    const bool gt = live && m > prefix;
+    const bool eq = live && m == prefix;
     const uint64_t beq = __ballot(eq);
     const bool take = gt || (eq && run_eq + lanes_below(beq) < kk);
     const uint64_t btake = __ballot(take);
@@ -510,25 +798,38 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams S) {
     }
     run_eq += __popcll(beq);
     run_sel += __popcll(btake);
-  }
+  });
+}
+
+template <typename... Args>
+hipError_t launch(void (*kernel)(Args...), dim3 grid, dim3 block, hipStream_t st, void* const* ev, int e0,
+                  Args... args) {
+  void* argv[] = {(void*)&args...};
+  hipEvent_t start = ev ? static_cast<hipEvent_t>(ev[e0]) : nullptr;
+  hipEvent_t stop = ev ? static_cast<hipEvent_t>(ev[e0 + 1]) : nullptr;
+  const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, st,
+                                          start, stop, 0);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 template <int QK, bool DUMP>
-hipError_t launch_score_t(const ScoreParams& P, int rt, int items, hipStream_t st) {
+hipError_t launch_score_t(const ScoreParams& P, int kind, int rt, int items, hipStream_t st, void* const* ev) {
   const dim3 grid(items), block(kScoreThreads);
-  switch (rt) {
-    case 1: score_kernel<QK, 1, 4, DUMP><<<grid, block, 0, st>>>(P); break;
-    case 2: score_kernel<QK, 1, 2, DUMP><<<grid, block, 0, st>>>(P); break;
-    case 4: score_kernel<QK, 1, 1, DUMP><<<grid, block, 0, st>>>(P); break;
-    case 8: score_kernel<QK, 2, 1, DUMP><<<grid, block, 0, st>>>(P); break;
-    default: return hipErrorInvalidValue;
+  if (kind == kKindDecode) {
+    switch (rt) {
+      case 1: return launch(score_decode_kernel<QK, 1, DUMP>, grid, block, st, ev, 0, P);
+      case 2: return launch(score_decode_kernel<QK, 2, DUMP>, grid, block, st, ev, 0, P);
+      case 4: return launch(score_decode_kernel<QK, 4, DUMP>, grid, block, st, ev, 0, P);
+      default: return hipErrorInvalidValue;
+    }
   }
-  return hipGetLastError();
+  if (rt != 8) return hipErrorInvalidValue;
+  return launch(score_kernel<QK, 2, 1, DUMP>, grid, block, st, ev, 0, P);
 }
 
 }  // namespace
 
-int launch_score(const RunArgs& a, bool dump) {
+int launch_score(const RunArgs& a, bool dump, void* const* events) {
   const PlanHeader* h = a.hdr;
   if (h->n_items == 0) return 0;
   ScoreParams P{};
@@ -546,6 +847,7 @@ int launch_score(const RunArgs& a, bool dump) {
   P.block_size = a.p->block_size;
   P.max_blocks = a.p->max_blocks_per_seq;
   P.k = a.p->sparse_count;
+  P.bs_magic = (uint32_t)((1ull << 32) / (uint64_t)a.p->block_size + 1);
   P.d_row0 = a.dump_row0;
   P.d_row1 = a.dump_row1;
   P.d_cols = a.dump_cols;
@@ -554,15 +856,15 @@ int launch_score(const RunArgs& a, bool dump) {
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   hipError_t e;
   if (a.p->qk_dtype == QLI_QK_INT8)
-    e = dump ? launch_score_t<QLI_QK_INT8, true>(P, h->rows_per_item, h->n_items, st)
-             : launch_score_t<QLI_QK_INT8, false>(P, h->rows_per_item, h->n_items, st);
+    e = dump ? launch_score_t<QLI_QK_INT8, true>(P, h->kind, h->rows_per_item, h->n_items, st, events)
+             : launch_score_t<QLI_QK_INT8, false>(P, h->kind, h->rows_per_item, h->n_items, st, events);
   else
-    e = dump ? launch_score_t<QLI_QK_FP8_E4M3FN, true>(P, h->rows_per_item, h->n_items, st)
-             : launch_score_t<QLI_QK_FP8_E4M3FN, false>(P, h->rows_per_item, h->n_items, st);
+    e = dump ? launch_score_t<QLI_QK_FP8_E4M3FN, true>(P, h->kind, h->rows_per_item, h->n_items, st, events)
+             : launch_score_t<QLI_QK_FP8_E4M3FN, false>(P, h->kind, h->rows_per_item, h->n_items, st, events);
   return e == hipSuccess ? 0 : (int)e;
 }
 
-int launch_select(const RunArgs& a) {
+int launch_select(const RunArgs& a, void* const* events) {
   const PlanHeader* h = a.hdr;
   if (h->n_select == 0) return 0;
   SelectParams S{};
@@ -571,8 +873,8 @@ int launch_select(const RunArgs& a) {
   S.idx_out = a.sparse_indices;
   S.val_out = a.sparse_values;
   S.k = a.p->sparse_count;
-  select_kernel<<<dim3(h->n_select), dim3(kSelThreads), 0, static_cast<hipStream_t>(a.stream)>>>(S);
-  const hipError_t e = hipGetLastError();
+  const hipError_t e = launch(select_kernel, dim3(h->n_select), dim3(kSelThreads),
+                              static_cast<hipStream_t>(a.stream), events, 2, S);
   return e == hipSuccess ? 0 : (int)e;
 }
 

@@ -114,7 +114,8 @@ HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("fingerprint", "<u8"), ("
                 ("workspace_bytes", "<i8"), ("rows", "<i8"), ("visible_pairs", "<i8"), ("ws_scores", "<i8"),
                 ("off_rows", "<i8"), ("off_items", "<i8"), ("off_select", "<i8"), ("kind", "<i4"),
                 ("rows_per_item", "<i4"), ("n_items", "<i4"), ("n_select", "<i4"), ("chunk", "<i4"),
-                ("max_vis", "<i4"), ("reserved", "<i4", 6)])
+                ("max_vis", "<i4"), ("reserved", "<i4", 2), ("key_entries", "<i8"), ("table_entries", "<i8"),
+                ("active_rows", "<i8"), ("reserved64", "<i8")])
 ROW = np.dtype([("batch", "<i4"), ("vis", "<i4"), ("ws_off", "<i8")])
 ITEM = np.dtype([("row0", "<i4"), ("nrows", "<i4"), ("batch", "<i4"), ("key0", "<i4"), ("nkeys", "<i4"),
                  ("flags", "<i4")])
@@ -176,6 +177,10 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
     assert offs == list(np.cumsum([0] + [int(vis[r]) for r in sel])[:-1])
     info = qli.qli_plan_info_get(plan)
     assert info.rows == nrows and info.visible_pairs == vis.sum() and info.select_rows == len(sel)
+    assert info.active_rows == int((vis > 0).sum())
+    bmax = [max([int(vis[r]) for r in range(nrows) if rows[r]["batch"] == b] or [0]) for b in range(p["batch"])]
+    assert info.key_entries == sum(bmax)
+    assert info.table_entries == sum((m + p["block_size"] - 1) // p["block_size"] for m in bmax)
 
 
 def test_run_rejects_bad_arguments_without_launching(qli):
