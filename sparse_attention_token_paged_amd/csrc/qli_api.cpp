@@ -117,7 +117,7 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   for (int b = 0; b < p.batch; b++) {
     if (aslk[b] < 0) return QLI_ERR_ARG;
     const int64_t stored = aslk[b] / p.cmp_ratio;
-    if (stored >= kMaxEntries) return QLI_ERR_SIZE;
+    if (stored >= kMaxEntries) return QLI_ERR_SIZE;  // exact reciprocal division in the kernels
     const int64_t need = (stored + p.block_size - 1) / p.block_size;
     if (need > p.max_blocks_per_seq) return QLI_ERR_ARG;  // 约束说明: block_table second dim
     if (bsnd) {
@@ -133,7 +133,7 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
     }
   }
 
-  out.rows.assign(rows, RowInfo{-1, 0, -1});
+  out.rows.assign(rows, RowInfo{-1, 0, -1, 0, 0});
   int64_t max_s1b = 0, visible = 0, max_vis = 0, key_entries = 0, table_entries = 0, active = 0;
   for (int b = 0; b < p.batch; b++) {
     max_s1b = std::max(max_s1b, qcnt[b]);
@@ -177,40 +177,91 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
     r = e;
   }
 
-  // Chunk size: about 1024 items in total for decode (4 per CU on 256 CUs),
-  // whole rows (up to kMaxChunk) for prefill.
+  // Chunk size.  Prefill items walk up to kMaxChunk entries in 64-entry
+  // tiles and write dense scores.  Decode items stream their chunk through
+  // LDS; when there is enough work for chunks of at least 4k entries (and
+  // k <= 1024), each item keeps only its chunk's top-k candidates, which cuts
+  // the final selection's input by 4x or more.  Otherwise chunks are
+  // kDenseChunk entries and every score is staged.
   int64_t key_work = 0;
   for (const Group& g : groups) key_work += g.maxv;
-  // Decode items stage one whole chunk of kDecodeChunk entries in LDS;
-  // prefill items walk up to kMaxChunk entries in 64-entry tiles.
-  (void)key_work;
-  const int chunk = prefill ? kMaxChunk : kDecodeChunk;
+  const int k = p.sparse_count;
+  int chunk = prefill ? kMaxChunk : kDenseChunk;
+  bool local = false;
+  if (!prefill && rt <= 2 && k <= 1024) {
+    int c = 1024;
+    while (c < 4 * k) c *= 2;
+    if (c <= kMaxChunk && c * rt <= kMaxChunk && key_work / c >= 512) {
+      chunk = c;
+      local = true;
+    }
+  }
+
+  // Per-row candidate counts and workspace offsets.  A row that sees more
+  // than k entries stages candidates for the selection stage: every score
+  // (dense), or the top-k of each chunk (local), in ascending index order.
+  auto seen = [&](int64_t vis, int64_t key0) -> int64_t {
+    return std::max<int64_t>(0, std::min<int64_t>(chunk, vis - key0));
+  };
+  int64_t ws = 0;
+  for (int64_t r = 0; r < rows; r++) {
+    RowInfo& ri = out.rows[r];
+    ri.ncand = 0;
+    ri.indexed = 0;
+    if (ri.vis > k) {
+      int64_t n = 0;
+      if (local)
+        for (int64_t k0 = 0; k0 < ri.vis; k0 += chunk) n += std::min<int64_t>(k, seen(ri.vis, k0));
+      else
+        n = ri.vis;
+      ri.ws_off = ws;
+      ri.ncand = (int32_t)n;
+      ri.indexed = local ? 1 : 0;
+      ws += n;
+      out.select.push_back((int32_t)r);
+    }
+  }
 
   for (const Group& g : groups) {
+    Item base{};
+    base.row0 = g.row0;
+    base.nrows = g.nrows;
+    base.batch = g.batch;
+    for (int u = 0; u < kMaxItemRows; u++) {
+      base.vis[u] = 0;
+      base.cand_off[u] = -1;
+    }
+    if (!prefill)
+      for (int u = 0; u < g.nrows; u++) base.vis[u] = out.rows[g.row0 + u].vis;
     if (g.maxv == 0) {
-      out.items.push_back({g.row0, g.nrows, g.batch, 0, 0, kItemPad});
+      base.flags = kItemPad;
+      out.items.push_back(base);
       continue;
     }
-    for (int32_t k0 = 0; k0 < g.maxv; k0 += chunk)
-      out.items.push_back({g.row0, g.nrows, g.batch, k0, std::min(chunk, g.maxv - k0),
-                           k0 == 0 ? kItemPad : 0});
+    for (int32_t k0 = 0; k0 < g.maxv; k0 += chunk) {
+      Item it = base;
+      it.key0 = k0;
+      it.nkeys = std::min(chunk, g.maxv - k0);
+      it.flags = k0 == 0 ? kItemPad : 0;
+      if (!prefill) {
+        for (int u = 0; u < g.nrows; u++) {
+          const RowInfo& ri = out.rows[g.row0 + u];
+          if (ri.ws_off < 0) continue;
+          int64_t before = 0;  // candidates of the chunks before this one
+          if (local)
+            for (int64_t c0 = 0; c0 < k0; c0 += chunk) before += std::min<int64_t>(k, seen(ri.vis, c0));
+          else
+            before = k0;
+          it.cand_off[u] = ri.ws_off + before;
+        }
+      }
+      out.items.push_back(it);
+    }
   }
   if (prefill)  // longest items first
     std::stable_sort(out.items.begin(), out.items.end(),
                      [](const Item& a, const Item& b) { return a.nkeys * a.nrows > b.nkeys * b.nrows; });
   if (out.items.size() > (size_t)INT32_MAX) return QLI_ERR_SIZE;
-
-  // Rows with more visible entries than sparse_count stage their scores in
-  // the workspace and go through the selection stage.
-  int64_t ws = 0;
-  for (int64_t r = 0; r < rows; r++) {
-    RowInfo& ri = out.rows[r];
-    if (ri.vis > p.sparse_count) {
-      ri.ws_off = ws;
-      ws += ri.vis;
-      out.select.push_back((int32_t)r);
-    }
-  }
 
   PlanHeader& h = out.hdr;
   std::memset(&h, 0, sizeof(h));
@@ -220,7 +271,9 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   h.rows = rows;
   h.visible_pairs = visible;
   h.ws_scores = ws;
-  h.workspace_bytes = ws * 4;
+  h.ws_index_offset = align16(ws * 4);
+  h.workspace_bytes = local ? h.ws_index_offset + ws * 4 : ws * 4;
+  h.local_select = local ? 1 : 0;
   h.kind = prefill ? kKindPrefill : kKindDecode;
   h.rows_per_item = rt;
   h.n_items = (int32_t)out.items.size();

@@ -12,14 +12,14 @@
 namespace qli {
 
 constexpr uint32_t kPlanMagic = 0x504C4951u;  // "QILP"
-constexpr uint32_t kPlanVersion = 1;
+constexpr uint32_t kPlanVersion = 2;
 constexpr int kHeads = 64;       // query heads (QLI-README 约束说明)
 constexpr int kDim = 128;        // head dim of query and key (约束说明)
-constexpr int kTileKeys = 64;    // keys staged in LDS per pipeline step
-constexpr int kMaxChunk = 4096;  // keys per score item, upper bound
-constexpr int kDecodeChunk = 256;        // keys per decode item (whole chunk staged in LDS)
-constexpr int64_t kMaxEntries = 1 << 22;  // compressed entries per sequence (exact reciprocal division)
-constexpr int kMaxChunkBlocks = kMaxChunk / 16 + 2;  // block ids one item may touch
+constexpr int kTileKeys = 64;    // keys per MFMA tile step (4 n-tiles of 16)
+constexpr int kMaxChunk = 4096;  // keys per work item, upper bound
+constexpr int kDenseChunk = 256;          // decode chunk when no chunk-local selection is done
+constexpr int kMaxEntries = 1 << 22;      // compressed entries per sequence (exact reciprocal division)
+constexpr int kMaxItemRows = 4;           // rows carried inline by a decode item
 
 enum PlanKind : int32_t { kKindDecode = 0, kKindPrefill = 1 };
 enum ItemFlags : int32_t { kItemPad = 1 };
@@ -32,7 +32,7 @@ struct PlanHeader {
   int64_t workspace_bytes;
   int64_t rows;              // output rows
   int64_t visible_pairs;     // sum of visible counts
-  int64_t ws_scores;         // fp32 scores staged in the workspace
+  int64_t ws_scores;         // fp32 candidate scores staged in the workspace
   int64_t off_rows;          // byte offset of RowInfo[rows]
   int64_t off_items;         // byte offset of Item[n_items]
   int64_t off_select;        // byte offset of int32[n_select]
@@ -40,20 +40,23 @@ struct PlanHeader {
   int32_t rows_per_item;     // 1, 2, 4 (decode) or 8 (prefill)
   int32_t n_items;
   int32_t n_select;
-  int32_t chunk;             // keys per score item (multiple of kTileKeys)
+  int32_t chunk;             // keys per work item
   int32_t max_vis;
-  int32_t reserved[2];
+  int32_t local_select;      // decode items reduce their chunk to its top-k candidates
+  int32_t reserved;
   int64_t key_entries;       // sum over batches of the largest visible count
   int64_t table_entries;     // block-table entries spanned by those entries
   int64_t active_rows;       // rows with at least one visible entry
-  int64_t reserved64;
+  int64_t ws_index_offset;   // byte offset of the int32 candidate-index region in the workspace
 };
 static_assert(sizeof(PlanHeader) % 16 == 0, "header keeps the tables aligned");
 
 struct RowInfo {
   int32_t batch;   // -1 for rows that belong to no query token
   int32_t vis;     // visible compressed key entries
-  int64_t ws_off;  // element offset of the row's scores in the workspace, -1 = direct output
+  int64_t ws_off;  // element offset of the row's candidates in the workspace, -1 = direct output
+  int32_t ncand;   // candidates the row stages for the selection stage
+  int32_t indexed; // 1: candidates carry explicit key indices (chunk-local selection)
 };
 
 struct Item {
@@ -63,7 +66,12 @@ struct Item {
   int32_t key0;    // first key entry of the chunk
   int32_t nkeys;   // entries in the chunk (0: padding only)
   int32_t flags;   // kItemPad: this item writes the -1 padding of its rows
+  int32_t reserved[2];
+  int32_t vis[kMaxItemRows];       // decode items: visible entries of rows row0 + u
+  int64_t cand_off[kMaxItemRows];  // decode items: workspace slot of row u's candidates
+                                   // from this chunk, -1 = direct output
 };
+static_assert(sizeof(Item) == 80, "item layout");
 
 inline const PlanHeader* plan_header(const void* plan) {
   return static_cast<const PlanHeader*>(plan);

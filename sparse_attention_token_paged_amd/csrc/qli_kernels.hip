@@ -53,6 +53,7 @@ struct ScoreParams {
   const void* k_scale;
   const int32_t* block_table;
   float* ws;
+  int32_t* ws_idx;   // candidate indices (chunk-local selection)
   int32_t* idx_out;
   float* val_out;
   int64_t stride;
@@ -126,7 +127,7 @@ void score_kernel(ScoreParams P) {
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kTileKeys * kDim];
   __shared__ float lds_sk[2][kTileKeys];
-  __shared__ int32_t lds_blk[kMaxChunkBlocks];
+  __shared__ int32_t lds_blk[kMaxChunk / 16 + 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -352,12 +353,12 @@ void score_kernel(ScoreParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode-shaped items: one chunk of kDecodeChunk entries, 1, 2 or 4 rows.
+// Shared pieces: lane-group reductions, order keys, LDS-DMA, block selection
 // ---------------------------------------------------------------------------
 
-// Sum over the four lane groups of four per-lane partials, scattered so that
-// lane (q, c) ends with the total of partial q (a reduce-scatter in two
-// permlane steps): after it, lane q*16 + c holds key q*16 + c of the tile.
+// Sum over the four lane groups of per-lane partials, scattered so that lane
+// (q, c) ends with the total of partial q: lane q*16 + c holds key q*16 + c
+// of the 64-key tile (two permlane steps).
 __device__ __forceinline__ float reduce_scatter4(float a0, float a1, float a2, float a3) {
   // halves: the lower 32 lanes keep partials 0/1, the upper 32 keep 2/3
   auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a2), false, false);
@@ -369,23 +370,276 @@ __device__ __forceinline__ float reduce_scatter4(float a0, float a1, float a2, f
   return __uint_as_float(z[0]) + __uint_as_float(z[1]);
 }
 
-template <int QK, int RT, bool DUMP>
+// The same for two partials: lanes of rows 0 and 1 end with the total of a0,
+// rows 2 and 3 with the total of a1 (for key c of the respective n-tile).
+__device__ __forceinline__ float reduce_scatter2(float a0, float a1) {
+  auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
+  const float s = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Direct-to-LDS loads, issued from inline assembly so that the compiler does
+// not add waits for them: each lane's bytes land at m0 + lane * 16 (16-byte
+// form) or in the lane's 4-byte slot m0 + lane * 4 (4- and 2-byte forms).
+// Callers wait with wait_vm<N>() (vmcnt counts them with every other vector
+// memory access; loads complete in issue order).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma16(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory");
+}
+__device__ __forceinline__ void dma2(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(m0) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier that orders LDS (waits for this wave's LDS accesses) but
+// leaves outstanding global loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Exclusive prefix sum over the workgroup in thread order.
+template <int NT>
+__device__ int block_exclusive_scan(int v, int* tmp) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int w = 0; w < NW; w++) before += w < wave ? tmp[w] : 0;
+  __syncthreads();
+  return before + incl - v;
+}
+
+struct SelectShared {
+  uint32_t red_and[16], red_or[16];
+  int scan_tmp[16];
+  int res[4];
+  int cnt_gt[16], cnt_eq[16];
+};
+
+// Top-k of n order keys (key_at(e), e in [0, n)), larger first, ties to the
+// lower position.  Radix select with 11-bit digits that starts below the
+// bits every key shares; LDS histograms (hist: 2048 ints); the threshold
+// digit is found with a block scan.  Then emit(pos, e, key) is called for
+// the k winners with pos = their rank in ascending position order: waves own
+// contiguous segments, and ties at the threshold are ranked with ballots and
+// mbcnt prefix counts.  Requires n > k >= 1 and all NT threads.
+template <int NT, typename KeyAt, typename Emit>
+__device__ void block_select(int n, int k, KeyAt&& key_at, Emit&& emit, int* hist, SelectShared& sh) {
+  constexpr int NW = NT / 64;
+  constexpr int BATCH = 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto for_each = [&](auto&& f) {
+    for (int base = 0; base < n; base += NT * BATCH) {
+      uint32_t u[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; i++) {
+        const int e = base + i * NT + tid;
+        u[i] = e < n ? key_at(e) : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < BATCH; i++) {
+        const int e = base + i * NT + tid;
+        if (e < n) f(e, u[i]);
+      }
+    }
+  };
+  uint32_t a = 0xFFFFFFFFu, o = 0u;
+  for_each([&](int, uint32_t u) {
+    a &= u;
+    o |= u;
+  });
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    a &= __shfl_xor(a, off, 64);
+    o |= __shfl_xor(o, off, 64);
+  }
+  if (lane == 0) {
+    sh.red_and[wave] = a;
+    sh.red_or[wave] = o;
+  }
+  __syncthreads();
+  a = 0xFFFFFFFFu;
+  o = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    a &= sh.red_and[w];
+    o |= sh.red_or[w];
+  }
+  const uint32_t diff = a ^ o;
+  uint32_t mask, prefix;
+  int lo;
+  if (diff == 0u) {
+    mask = 0xFFFFFFFFu;
+    prefix = a;
+    lo = 0;
+  } else {
+    const int hb = 31 - __clz(diff);
+    mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+    prefix = a & mask;
+    lo = hb + 1;
+  }
+  // Invariant: the kk-th largest key has the top bits `prefix` under `mask`,
+  // and kk <= the number of keys that do.
+  int kk = k;
+  bool whole_bin = diff == 0u;
+  while (!whole_bin && lo > 0) {
+    const int width = lo < 11 ? lo : 11;
+    const int shift = lo - width;
+    const int nb = 1 << width;
+    for (int b = tid; b < nb; b += NT) hist[b] = 0;
+    __syncthreads();
+    for_each([&](int, uint32_t u) {
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1);
+    });
+    __syncthreads();
+    // Thread t owns digits in descending order: BPT = 2048 / NT consecutive ones.
+    constexpr int BPT = 2048 / NT;
+    int h[BPT];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; i++) {
+      const int d = nb - 1 - (BPT * tid + i);
+      h[i] = d >= 0 ? hist[d] : 0;
+      local += h[i];
+    }
+    const int before = block_exclusive_scan<NT>(local, sh.scan_tmp);
+    if (before < kk && kk <= before + local) {
+      int acc = before;
+#pragma unroll
+      for (int i = 0; i < BPT; i++) {
+        if (acc < kk && kk <= acc + h[i]) {
+          sh.res[0] = nb - 1 - (BPT * tid + i);
+          sh.res[1] = acc;
+          sh.res[2] = h[i];
+        }
+        acc += h[i];
+      }
+    }
+    __syncthreads();
+    const int digit = sh.res[0], above = sh.res[1], count = sh.res[2];
+    __syncthreads();  // res and hist are rewritten by the next pass
+    kk -= above;
+    prefix |= (uint32_t)digit << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
+    lo = shift;
+    whole_bin = count == kk;
+  }
+
+  // Emission in ascending position order over per-wave contiguous segments.
+  const int seg = (((n + NW - 1) / NW) + 63) & ~63;
+  const int beg = min(n, wave * seg);
+  const int end = min(n, beg + seg);
+  auto segment = [&](auto&& f) {
+    for (int e0 = beg; e0 < end; e0 += 64 * BATCH) {
+      uint32_t u[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; i++) {
+        const int e = e0 + 64 * i + lane;
+        u[i] = e < end ? key_at(e) : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < BATCH; i++) {
+        const int e = e0 + 64 * i + lane;
+        if (e0 + 64 * i < end) f(e, e < end, u[i]);
+      }
+    }
+  };
+  int ngt = 0, neq = 0;
+  segment([&](int, bool live, uint32_t u) {
+    const uint32_t m = u & mask;
+    ngt += __popcll(__ballot(live && m > prefix));
+    neq += __popcll(__ballot(live && m == prefix));
+  });
+  if (lane == 0) {
+    sh.cnt_gt[wave] = ngt;
+    sh.cnt_eq[wave] = neq;
+  }
+  __syncthreads();
+  int eq_before = 0, sel_before = 0;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    if (w < wave) {
+      sel_before += sh.cnt_gt[w] + min(sh.cnt_eq[w], max(0, kk - eq_before));
+      eq_before += sh.cnt_eq[w];
+    }
+  }
+  int run_eq = eq_before, run_sel = sel_before;
+  segment([&](int e, bool live, uint32_t u) {
+    const uint32_t m = u & mask;
+    const bool gt = live && m > prefix;
+    const bool eq = live && m == prefix;
+    const uint64_t beq = __ballot(eq);
+    const bool take = gt || (eq && run_eq + lanes_below(beq) < kk);
+    const uint64_t btake = __ballot(take);
+    const int pos = run_sel + lanes_below(btake);
+    if (take && pos < k) emit(pos, e, u);  // exactly k are taken; the bound guards the slots
+    run_eq += __popcll(beq);
+    run_sel += __popcll(btake);
+  });
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Decode-shaped items: 1, 2 or 4 rows of one batch x a chunk of key entries.
+// ---------------------------------------------------------------------------
+//
+// The chunk streams through a 3-stage LDS ring of 128-entry stages filled by
+// direct-to-LDS loads (every wave issues exactly 4 key loads and 1 ScaleK
+// load per stage, with addresses clamped into the chunk, so per-wave vmcnt
+// arithmetic is exact); two stages are in flight while one is computed.
+// Each wave scores its row against its n-tiles of the stage:
+//   RT = 4: all 8 n-tiles, RT = 2: 4 n-tiles, RT = 1: 2 n-tiles.
+// LOCAL items keep every score of the chunk in LDS and then reduce it to its
+// top-k candidates (score, index) for the final selection.
+template <int QK, int RT, bool LOCAL, bool DUMP>
 __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams P) {
-  constexpr int CH = kDecodeChunk;
-  constexpr int NTILE = CH / kTileKeys;   // 64-entry tiles per chunk
-  constexpr int WPR = 4 / RT;             // waves per row
-  constexpr int LOADS = CH * kDim / (kScoreThreads * 16);  // 16-byte key loads per thread
-  constexpr int SB = QK == QLI_QK_INT8 ? 2 : 4;           // scale bytes
-  typedef __attribute__((address_space(3))) void lds_t;
+  constexpr int SC = 128;                     // entries per LDS stage
+  constexpr int NSTAGE = 3;
+  constexpr int WPR = 4 / RT;                 // waves per row
+  constexpr int NPW = 8 / WPR;                // n-tiles per wave per stage
+  constexpr int KLOADS = SC * kDim / (kScoreThreads * 16);  // 4 key loads per thread per stage
+  constexpr int PER_STAGE = KLOADS + 1;       // + the ScaleK load
+  constexpr int SB = QK == QLI_QK_INT8 ? 2 : 4;
+  constexpr int LCAP = LOCAL ? kMaxChunk / RT : 1;
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(P.plan);
-  const RowInfo* rinfo = reinterpret_cast<const RowInfo*>(P.plan + hdr->off_rows);
-  const Item it = reinterpret_cast<const Item*>(P.plan + hdr->off_items)[blockIdx.x];
+  // read in place: the per-row fields are indexed by a wave-uniform row
+  const Item& it = reinterpret_cast<const Item*>(P.plan + hdr->off_items)[blockIdx.x];
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[CH * kDim];
-  // A 2-byte direct-to-LDS load fills a 4-byte slot per lane (value in the
-  // low half), so ScaleK takes 4 bytes per entry for both dtypes.
-  __shared__ __attribute__((aligned(16))) uint32_t lds_sk[CH];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NSTAGE][SC * kDim];
+  __shared__ uint32_t ring_sk[NSTAGE][SC];   // ScaleK bits, one 4-byte slot per entry
+  __shared__ int32_t lds_bt[kMaxChunk / 16 + 2];
+  __shared__ float lds_scores[RT][LCAP];     // LOCAL: the chunk's scores of each row
+  __shared__ SelectShared sel;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -394,10 +648,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   const int c16 = lane & 15;
   const int k = P.k;
 
+  // Rows that see fewer than k entries: slots vis..k-1 are -1 / -inf.
   if (it.flags & kItemPad) {
     for (int u = 0; u < it.nrows; u++) {
       const int64_t r = it.row0 + u;
-      const int vis = rinfo[r].vis;
+      const int vis = it.vis[u];
       if (vis >= k) continue;
       for (int pos = vis + tid; pos < k; pos += kScoreThreads) {
         P.idx_out[r * k + pos] = -1;
@@ -407,57 +662,24 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   }
   if (it.nkeys <= 0) return;  // uniform across the workgroup
 
-  // Block ids of the chunk: lane l of every wave holds entry fb + l.
   const int bs = P.block_size;
   const int key0 = it.key0;
   const int kend = key0 + it.nkeys;
   const int fb = (int)__umulhi((uint32_t)key0, P.bs_magic);
   const int nblk = (int)__umulhi((uint32_t)(kend - 1), P.bs_magic) - fb + 1;
-  const int32_t btv = lane < nblk ? P.block_table[(int64_t)it.batch * P.max_blocks + fb + lane] : 0;
-
-  // The whole chunk goes to LDS with direct-to-LDS loads.  Wave w's load i
-  // fills LDS bytes [(4i + w) * 1024, +1024), lane l the 16 bytes at l*16:
-  // key row kk = 32i + 8w + l/8, physical chunk l%8, which holds logical
-  // chunk (l%8) ^ ((kk>>1)&7) so that MFMA-layout reads are conflict-free.
-#pragma unroll
-  for (int i = 0; i < LOADS; i++) {
-    const int kk = 32 * i + 8 * wave + (lane >> 3);
-    const int j = key0 + kk;
-    // the block id comes from another lane: shuffle with every lane active
-    const int jc = min(j, kend - 1);
-    const int b = (int)__umulhi((uint32_t)jc, P.bs_magic);
-    const int blk = __shfl(btv, b - fb, 64);
-    if (j < kend) {
-      const int slot = j - b * bs;
-      const int c = (lane & 7) ^ ((kk >> 1) & 7);
-      const uint8_t* src = P.key + (int64_t)blk * P.stride + slot * kDim + c * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_t*)&lds_k[(4 * i + wave) * 1024], 16, 0, 0);
-    }
-  }
-  // ScaleK of every entry of the chunk: thread tid fetches entry tid.
   {
-    const int j = key0 + tid;
-    const int jc = min(j, kend - 1);
-    const int b = (int)__umulhi((uint32_t)jc, P.bs_magic);
-    const int blk = __shfl(btv, b - fb, 64);
-    if (j < kend) {
-      const int slot = j - b * bs;
-      const uint8_t* src = static_cast<const uint8_t*>(P.k_scale) + ((int64_t)blk * bs + slot) * SB;
-      if constexpr (SB == 2)
-        __builtin_amdgcn_global_load_lds(src, (lds_t*)&lds_sk[wave * 64], 2, 0, 0);
-      else
-        __builtin_amdgcn_global_load_lds(src, (lds_t*)&lds_sk[wave * 64], 4, 0, 0);
-    }
+    const int32_t* bt = P.block_table + (int64_t)it.batch * P.max_blocks + fb;
+    for (int t = tid; t < nblk; t += kScoreThreads) lds_bt[t] = bt[t];
   }
 
-  // This wave's row: query fragments and folded weights w' = W * ScaleQ.
+  // This wave's row: query fragments and w' = W * ScaleQ (loads issued before
+  // the barrier, so they share its round trip with the block table).
   const int u = wave / WPR;
   const int sub = wave % WPR;
   const bool rok = u < it.nrows;
   const int64_t r = it.row0 + (rok ? u : 0);
-  const RowInfo ri = rinfo[r];
-  const int rvis = rok ? ri.vis : 0;
-  const int64_t rws = ri.ws_off;
+  const int rvis = rok ? it.vis[u] : 0;
+  const int64_t coff = rok ? it.cand_off[u] : -1;
   Frag qa[4];
   float wq[16];
   {
@@ -477,7 +699,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
         const h4 w = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.weights) + e0 + 16 * m);
         const h4 sq = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.q_scale) + e0 + 16 * m);
 #pragma unroll
-        for (int i = 0; i < 4; i++) wq[4 * m + i] = (float)w[i] * (float)sq[i];
+        for (int i = 0; i < 4; i++) wq[4 * m + i] = __builtin_fmaf((float)w[i], (float)sq[i], 0.f);
       } else {
         const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(P.weights) + e0 + 16 * m);
         const float4 sq = *reinterpret_cast<const float4*>(static_cast<const float*>(P.q_scale) + e0 + 16 * m);
@@ -488,21 +710,50 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
       }
     }
   }
-  __syncthreads();  // every direct-to-LDS load has landed
+  __syncthreads();  // lds_bt ready (and the row loads above have landed)
+
+  // Stage loader: wave w's load i fills stage bytes [(4i + w) * 1024, +1024),
+  // lane l the 16 bytes at l*16: entry kk = 8(4i + w) + l/8, physical chunk
+  // l%8 holding logical chunk (l%8) ^ ((kk>>1)&7) (conflict-free MFMA reads).
+  const int nstages = (it.nkeys + SC - 1) / SC;
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    const int slot_ = st % NSTAGE;
+    const int e_base = key0 + st * SC;
+#pragma unroll
+    for (int i = 0; i < KLOADS; i++) {
+      const int kk = 8 * (4 * i + wave) + (lane >> 3);
+      const int j = min(e_base + kk, kend - 1);
+      const int b = (int)__umulhi((uint32_t)j, P.bs_magic);
+      const int blk = lds_bt[b - fb];
+      const int c = (lane & 7) ^ ((kk >> 1) & 7);
+      const uint8_t* src = P.key + (int64_t)blk * P.stride + (j - b * bs) * kDim + c * 16;
+      dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(&ring[slot_][(4 * i + wave) * 1024])));
+    }
+    if (lane < 32) {  // entries 32w .. 32w + 31 of the stage
+      const int j = min(e_base + 32 * wave + lane, kend - 1);
+      const int b = (int)__umulhi((uint32_t)j, P.bs_magic);
+      const uint8_t* src = static_cast<const uint8_t*>(P.k_scale) +
+                           ((int64_t)lds_bt[b - fb] * bs + (j - b * bs)) * SB;
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(&ring_sk[slot_][32 * wave]));
+      if constexpr (SB == 2)
+        dma2(src, m0);
+      else
+        dma4(src, m0);
+    }
+  };
 
   int32_t* oi = P.idx_out + r * k;
   float* ov = P.val_out ? P.val_out + r * k : nullptr;
-  // This wave's tiles: sub, sub + WPR, ... (64 entries each).
+  const bool direct = rvis <= k;
+
+  // Scores of 64 entries (4 n-tiles) or 32 entries (2 n-tiles) of the stage.
+  auto score_group = [&](int slot_, int st, int n0, auto nt_) __attribute__((always_inline)) {
+    constexpr int NTL = decltype(nt_)::value;
+    float part[NTL];
 #pragma unroll
-  for (int tt = 0; tt < NTILE / WPR; tt++) {
-    const int t = sub + tt * WPR;
-    const int tb = key0 + t * kTileKeys;
-    if (!rok || tb >= kend || tb >= rvis) break;  // uniform per wave
-    float part[4];
-#pragma unroll
-    for (int n = 0; n < 4; n++) {
-      const int kk = t * kTileKeys + n * 16 + c16;
-      const uint8_t* krow = &lds_k[kk * kDim];
+    for (int n = 0; n < NTL; n++) {
+      const int kk = (n0 + n) * 16 + c16;
+      const uint8_t* krow = &ring[slot_][kk * kDim];
       const int sw = (kk >> 1) & 7;
       Frag b;
       b.lo = *reinterpret_cast<const v4i*>(krow + ((chunk_lo<QK>(q) ^ sw) << 4));
@@ -527,6 +778,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
         for (int m = 0; m < 4; m++) {
           const v8i aa = __builtin_shufflevector(qa[m].lo, qa[m].hi, 0, 1, 2, 3, 4, 5, 6, 7);
           df[m] = v4f{0.f, 0.f, 0.f, 0.f};
+          // format 0 (fp8 e4m3) for both operands; scale arguments 0 select the unscaled form
           df[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa, bb, df[m], 0, 0, 0, 0, 0, 0);
         }
 #pragma unroll
@@ -536,7 +788,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
       }
       part[n] = acc;
       if constexpr (DUMP) {
-        const int j = key0 + kk;
+        const int j = key0 + st * SC + kk;
         if (r >= P.d_row0 && r < P.d_row1 && j < rvis && j < P.d_cols) {
           const int64_t base = (r - P.d_row0) * kHeads;
 #pragma unroll
@@ -552,253 +804,153 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
         }
       }
     }
-    // lane l now owns entry t*64 + l of the chunk
-    const int kk = t * kTileKeys + lane;
-    const int j = key0 + kk;
-    const float score = reduce_scatter4(part[0], part[1], part[2], part[3]) * scale_from_bits<QK>(lds_sk[kk]);
-    if (j < rvis) {
-      if (rws >= 0) {
-        P.ws[rws + j] = score;
-      } else {
+    float total;
+    int kk;
+    bool owner;
+    if constexpr (NTL == 4) {
+      total = reduce_scatter4(part[0], part[1], part[2], part[3]);
+      kk = n0 * 16 + lane;
+      owner = true;
+    } else {
+      total = reduce_scatter2(part[0], part[1]);
+      kk = (n0 + (q >> 1)) * 16 + c16;
+      owner = (q & 1) == 0;  // rows 0 and 2 hold the two totals
+    }
+    const int e = st * SC + kk;  // entry within the chunk
+    const int j = key0 + e;
+    const float score = total * scale_from_bits<QK>(ring_sk[slot_][kk]);
+    if (owner && j < rvis) {
+      if (direct) {
         oi[j] = j;
         if (ov) ov[j] = score;
+      } else if constexpr (LOCAL) {
+        lds_scores[u][e] = score;
+      } else {
+        P.ws[coff + e] = score;
       }
       if constexpr (DUMP) {
         if (r >= P.d_row0 && r < P.d_row1 && j < P.d_cols) P.dscores[(r - P.d_row0) * P.d_cols + j] = score;
       }
     }
+  };
+
+  // Pipeline: stages st+1 and st+2 are in flight while st is computed.
+  issue(0);
+  if (nstages > 1) issue(1);
+  for (int st = 0; st < nstages; st++) {
+    if (st + 2 < nstages) issue(st + 2);
+    const int newer = min(st + 2, nstages - 1) - st;  // stages issued after st
+    if (newer >= 2)
+      wait_vm<2 * PER_STAGE>();
+    else if (newer == 1)
+      wait_vm<PER_STAGE>();
+    else
+      wait_vm<0>();
+    lds_barrier();  // every wave's loads of stage st have landed
+    const int slot_ = st % NSTAGE;
+    const int sbase = key0 + st * SC;
+    if (rok && sbase < rvis) {
+      if constexpr (NPW == 8) {
+        score_group(slot_, st, 0, std::integral_constant<int, 4>{});
+        if (sbase + 64 < rvis) score_group(slot_, st, 4, std::integral_constant<int, 4>{});
+      } else if constexpr (NPW == 4) {
+        if (sbase + 64 * sub < rvis) score_group(slot_, st, 4 * sub, std::integral_constant<int, 4>{});
+      } else {
+        if (sbase + 32 * sub < rvis) score_group(slot_, st, 2 * sub, std::integral_constant<int, 2>{});
+      }
+    }
+    lds_barrier();  // the slot is free for stage st + 3
+  }
+
+  if constexpr (LOCAL) {
+    // Reduce each staged row of the chunk to its top-k, in ascending index order.
+    __syncthreads();
+    int* hist = reinterpret_cast<int*>(&ring[0][0]);  // the ring is idle now
+    int32_t* ws_idx = P.ws_idx;
+    for (int uu = 0; uu < it.nrows; uu++) {
+      const int vis = it.vis[uu];
+      const int64_t off = it.cand_off[uu];
+      if (vis <= k || off < 0) continue;  // uniform
+      const int n = min(it.nkeys, vis - key0);
+      if (n <= 0) continue;
+      const float* sc = lds_scores[uu];
+      if (n <= k) {
+        for (int e = tid; e < n; e += kScoreThreads) {
+          P.ws[off + e] = sc[e];
+          ws_idx[off + e] = key0 + e;
+        }
+      } else {
+        block_select<kScoreThreads>(
+            n, k, [&](int e) { return order_key(sc[e]); },
+            [&](int pos, int e, uint32_t key) {
+              P.ws[off + pos] = key_value(key);
+              ws_idx[off + pos] = key0 + e;
+            },
+            hist, sel);
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Selection
+// Final selection: one workgroup of 1024 threads per row that sees more than
+// k entries, over the row's staged candidates (in ascending index order).
 // ---------------------------------------------------------------------------
 
 constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelCache = 32768;  // scores cached in LDS (128 KiB)
+constexpr int kSelCache = 32768;  // candidate keys cached in LDS (128 KiB)
 
 struct SelectParams {
   const uint8_t* plan;
   const float* ws;
+  const int32_t* ws_idx;
   int32_t* idx_out;
   float* val_out;
   int32_t k;
 };
 
-// Order-preserving map of fp32 to uint32 (larger float -> larger key).
-__device__ __forceinline__ uint32_t order_key(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t u) {
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-}
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// Exclusive prefix sum over the workgroup in thread order.
-__device__ int block_exclusive_scan(int v, int* tmp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) tmp[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; w++) before += tmp[w];
-  __syncthreads();
-  return before + incl - v;
-}
-
-constexpr int kSelBatch = 8;  // independent loads in flight per thread
-
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams S) {
+  constexpr int BATCH = 8;
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(S.plan);
   const RowInfo* rinfo = reinterpret_cast<const RowInfo*>(S.plan + hdr->off_rows);
   const int32_t* sel_rows = reinterpret_cast<const int32_t*>(S.plan + hdr->off_select);
   const int64_t row = sel_rows[blockIdx.x];
   const RowInfo ri = rinfo[row];
-  const int n = ri.vis;
+  const int n = ri.ncand;
   const float* sc = S.ws + ri.ws_off;
+  const int32_t* ix = ri.indexed ? S.ws_idx + ri.ws_off : nullptr;
   const int k = S.k;
 
   __shared__ uint32_t cache[kSelCache];
   __shared__ int hist[2048];
-  __shared__ uint32_t red_and[kSelWaves], red_or[kSelWaves];
-  __shared__ int scan_tmp[kSelWaves];
-  __shared__ int res[3];
-  __shared__ int cnt_gt[kSelWaves], cnt_eq[kSelWaves];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ SelectShared sh;
+  const int tid = threadIdx.x;
   const bool cached = n <= kSelCache;
-
-  // Visits every score this thread owns (e = tid + i * kSelThreads) as its
-  // order key, kSelBatch loads at a time.
-  auto for_each_key = [&](auto&& f) {
-    for (int base = 0; base < n; base += kSelThreads * kSelBatch) {
-      uint32_t u[kSelBatch];
+  if (cached) {
+    for (int base = 0; base < n; base += kSelThreads * BATCH) {
+      float v[BATCH];
 #pragma unroll
-      for (int i = 0; i < kSelBatch; i++) {
+      for (int i = 0; i < BATCH; i++) {
         const int e = base + i * kSelThreads + tid;
-        u[i] = e < n ? (cached ? cache[e] : order_key(sc[e])) : 0u;
+        v[i] = e < n ? sc[e] : 0.f;
       }
 #pragma unroll
-      for (int i = 0; i < kSelBatch; i++) {
+      for (int i = 0; i < BATCH; i++) {
         const int e = base + i * kSelThreads + tid;
-        if (e < n) f(e, u[i]);
-      }
-    }
-  };
-
-  // First pass: stage the keys in LDS when they fit, and find the bits every
-  // key shares (AND == OR there), which need no radix pass.
-  uint32_t a = 0xFFFFFFFFu, o = 0u;
-  for (int base = 0; base < n; base += kSelThreads * kSelBatch) {
-    float v[kSelBatch];
-#pragma unroll
-    for (int i = 0; i < kSelBatch; i++) {
-      const int e = base + i * kSelThreads + tid;
-      v[i] = e < n ? sc[e] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < kSelBatch; i++) {
-      const int e = base + i * kSelThreads + tid;
-      if (e < n) {
-        const uint32_t u = order_key(v[i]);
-        if (cached) cache[e] = u;
-        a &= u;
-        o |= u;
-      }
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    a &= __shfl_xor(a, off, 64);
-    o |= __shfl_xor(o, off, 64);
-  }
-  if (lane == 0) {
-    red_and[wave] = a;
-    red_or[wave] = o;
-  }
-  __syncthreads();
-  a = 0xFFFFFFFFu;
-  o = 0u;
-  for (int w = 0; w < kSelWaves; w++) {
-    a &= red_and[w];
-    o |= red_or[w];
-  }
-  const uint32_t diff = a ^ o;
-  uint32_t mask, prefix;
-  int lo;
-  if (diff == 0u) {
-    mask = 0xFFFFFFFFu;
-    prefix = a;
-    lo = 0;
-  } else {
-    const int hb = 31 - __clz(diff);
-    mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
-    prefix = a & mask;
-    lo = hb + 1;
-  }
-  // Invariant: the kk-th largest key has the top bits `prefix` under `mask`,
-  // and kk <= the number of keys that do.
-  int kk = k;
-  bool whole_bin = diff == 0u;
-  while (!whole_bin && lo > 0) {
-    const int width = lo < 11 ? lo : 11;
-    const int shift = lo - width;
-    const int nb = 1 << width;
-    for (int b = tid; b < nb; b += kSelThreads) hist[b] = 0;
-    __syncthreads();
-    for_each_key([&](int, uint32_t u) {
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1);
-    });
-    __syncthreads();
-    // Thread t owns digits nb-1-2t and nb-2-2t (descending order).
-    const int d0 = nb - 1 - 2 * tid, d1 = d0 - 1;
-    const int h0 = d0 >= 0 ? hist[d0] : 0;
-    const int h1 = d1 >= 0 ? hist[d1] : 0;
-    const int before = block_exclusive_scan(h0 + h1, scan_tmp);
-    if (before < kk && kk <= before + h0 + h1) {
-      if (kk <= before + h0) {
-        res[0] = d0;
-        res[1] = before;
-        res[2] = h0;
-      } else {
-        res[0] = d1;
-        res[1] = before + h0;
-        res[2] = h1;
+        if (e < n) cache[e] = order_key(v[i]);
       }
     }
     __syncthreads();
-    const int digit = res[0], above = res[1], count = res[2];
-    __syncthreads();  // res and hist are rewritten by the next pass
-    kk -= above;
-    prefix |= (uint32_t)digit << shift;
-    mask |= (uint32_t)(nb - 1) << shift;
-    lo = shift;
-    whole_bin = count == kk;
-  }
-
-  // Emit in ascending index order: each wave owns one contiguous segment,
-  // walked 64 entries per step, kSelBatch steps per batch of loads.
-  const int seg = (((n + kSelWaves - 1) / kSelWaves) + 63) & ~63;
-  const int beg = min(n, wave * seg);
-  const int end = min(n, beg + seg);
-  auto segment = [&](auto&& f) {
-    for (int e0 = beg; e0 < end; e0 += 64 * kSelBatch) {
-      uint32_t u[kSelBatch];
-#pragma unroll
-      for (int i = 0; i < kSelBatch; i++) {
-        const int e = e0 + 64 * i + lane;
-        u[i] = e < end ? (cached ? cache[e] : order_key(sc[e])) : 0u;
-      }
-#pragma unroll
-      for (int i = 0; i < kSelBatch; i++) {
-        const int e = e0 + 64 * i + lane;
-        if (e0 + 64 * i < end) f(e, e < end, u[i]);
-      }
-    }
-  };
-  int ngt = 0, neq = 0;
-  segment([&](int, bool live, uint32_t u) {
-    const uint32_t m = u & mask;
-    ngt += __popcll(__ballot(live && m > prefix));
-    neq += __popcll(__ballot(live && m == prefix));
-  });
-  if (lane == 0) {
-    cnt_gt[wave] = ngt;
-    cnt_eq[wave] = neq;
-  }
-  __syncthreads();
-  int eq_before = 0, sel_before = 0;
-  for (int w = 0; w < wave; w++) {
-    sel_before += cnt_gt[w] + min(cnt_eq[w], max(0, kk - eq_before));
-    eq_before += cnt_eq[w];
   }
   int32_t* oi = S.idx_out + row * k;
   float* ov = S.val_out ? S.val_out + row * k : nullptr;
-  int run_eq = eq_before, run_sel = sel_before;
-  segment([&](int e, bool live, uint32_t u) {
-    const uint32_t m = u & mask;
-    const bool gt = live && m > prefix;
-    const bool eq = live && m == prefix;
-    const uint64_t beq = __ballot(eq);
-    const bool take = gt || (eq && run_eq + lanes_below(beq) < kk);
-    const uint64_t btake = __ballot(take);
-    const int pos = run_sel + lanes_below(btake);
-    if (take && pos < k) {  // exactly k are taken; the bound only guards the row's slots
-      oi[pos] = e;
-      if (ov) ov[pos] = key_value(u);
-    }
-    run_eq += __popcll(beq);
-    run_sel += __popcll(btake);
-  });
+  block_select<kSelThreads>(
+      n, k, [&](int e) { return cached ? cache[e] : order_key(sc[e]); },
+      [&](int pos, int e, uint32_t key) {
+        oi[pos] = ix ? ix[e] : e;
+        if (ov) ov[pos] = key_value(key);
+      },
+      hist, sh);
 }
 
 template <typename... Args>
@@ -813,17 +965,20 @@ hipError_t launch(void (*kernel)(Args...), dim3 grid, dim3 block, hipStream_t st
 }
 
 template <int QK, bool DUMP>
-hipError_t launch_score_t(const ScoreParams& P, int kind, int rt, int items, hipStream_t st, void* const* ev) {
-  const dim3 grid(items), block(kScoreThreads);
-  if (kind == kKindDecode) {
-    switch (rt) {
-      case 1: return launch(score_decode_kernel<QK, 1, DUMP>, grid, block, st, ev, 0, P);
-      case 2: return launch(score_decode_kernel<QK, 2, DUMP>, grid, block, st, ev, 0, P);
-      case 4: return launch(score_decode_kernel<QK, 4, DUMP>, grid, block, st, ev, 0, P);
+hipError_t launch_score_t(const ScoreParams& P, const PlanHeader* h, hipStream_t st, void* const* ev) {
+  const dim3 grid(h->n_items), block(kScoreThreads);
+  if (h->kind == kKindDecode) {
+    const bool local = h->local_select != 0;
+    switch (h->rows_per_item * 2 + (local ? 1 : 0)) {
+      case 2: return launch(score_decode_kernel<QK, 1, false, DUMP>, grid, block, st, ev, 0, P);
+      case 3: return launch(score_decode_kernel<QK, 1, true, DUMP>, grid, block, st, ev, 0, P);
+      case 4: return launch(score_decode_kernel<QK, 2, false, DUMP>, grid, block, st, ev, 0, P);
+      case 5: return launch(score_decode_kernel<QK, 2, true, DUMP>, grid, block, st, ev, 0, P);
+      case 8: return launch(score_decode_kernel<QK, 4, false, DUMP>, grid, block, st, ev, 0, P);
       default: return hipErrorInvalidValue;
     }
   }
-  if (rt != 8) return hipErrorInvalidValue;
+  if (h->rows_per_item != 8) return hipErrorInvalidValue;
   return launch(score_kernel<QK, 2, 1, DUMP>, grid, block, st, ev, 0, P);
 }
 
@@ -841,6 +996,8 @@ int launch_score(const RunArgs& a, bool dump, void* const* events) {
   P.k_scale = a.k_scale;
   P.block_table = a.block_table;
   P.ws = static_cast<float*>(a.workspace);
+  P.ws_idx = a.workspace ? reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + h->ws_index_offset)
+                         : nullptr;
   P.idx_out = a.sparse_indices;
   P.val_out = a.sparse_values;
   P.stride = a.p->key_block_stride ? a.p->key_block_stride : (int64_t)a.p->block_size * kDim;
@@ -856,11 +1013,11 @@ int launch_score(const RunArgs& a, bool dump, void* const* events) {
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   hipError_t e;
   if (a.p->qk_dtype == QLI_QK_INT8)
-    e = dump ? launch_score_t<QLI_QK_INT8, true>(P, h->kind, h->rows_per_item, h->n_items, st, events)
-             : launch_score_t<QLI_QK_INT8, false>(P, h->kind, h->rows_per_item, h->n_items, st, events);
+    e = dump ? launch_score_t<QLI_QK_INT8, true>(P, h, st, events)
+             : launch_score_t<QLI_QK_INT8, false>(P, h, st, events);
   else
-    e = dump ? launch_score_t<QLI_QK_FP8_E4M3FN, true>(P, h->kind, h->rows_per_item, h->n_items, st, events)
-             : launch_score_t<QLI_QK_FP8_E4M3FN, false>(P, h->kind, h->rows_per_item, h->n_items, st, events);
+    e = dump ? launch_score_t<QLI_QK_FP8_E4M3FN, true>(P, h, st, events)
+             : launch_score_t<QLI_QK_FP8_E4M3FN, false>(P, h, st, events);
   return e == hipSuccess ? 0 : (int)e;
 }
 
@@ -870,6 +1027,7 @@ int launch_select(const RunArgs& a, void* const* events) {
   SelectParams S{};
   S.plan = static_cast<const uint8_t*>(a.plan_dev);
   S.ws = static_cast<const float*>(a.workspace);
+  S.ws_idx = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(a.workspace) + h->ws_index_offset);
   S.idx_out = a.sparse_indices;
   S.val_out = a.sparse_values;
   S.k = a.p->sparse_count;

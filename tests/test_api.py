@@ -114,11 +114,11 @@ HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("fingerprint", "<u8"), ("
                 ("workspace_bytes", "<i8"), ("rows", "<i8"), ("visible_pairs", "<i8"), ("ws_scores", "<i8"),
                 ("off_rows", "<i8"), ("off_items", "<i8"), ("off_select", "<i8"), ("kind", "<i4"),
                 ("rows_per_item", "<i4"), ("n_items", "<i4"), ("n_select", "<i4"), ("chunk", "<i4"),
-                ("max_vis", "<i4"), ("reserved", "<i4", 2), ("key_entries", "<i8"), ("table_entries", "<i8"),
-                ("active_rows", "<i8"), ("reserved64", "<i8")])
-ROW = np.dtype([("batch", "<i4"), ("vis", "<i4"), ("ws_off", "<i8")])
+                ("max_vis", "<i4"), ("local_select", "<i4"), ("reserved", "<i4"), ("key_entries", "<i8"),
+                ("table_entries", "<i8"), ("active_rows", "<i8"), ("ws_index_offset", "<i8")])
+ROW = np.dtype([("batch", "<i4"), ("vis", "<i4"), ("ws_off", "<i8"), ("ncand", "<i4"), ("indexed", "<i4")])
 ITEM = np.dtype([("row0", "<i4"), ("nrows", "<i4"), ("batch", "<i4"), ("key0", "<i4"), ("nkeys", "<i4"),
-                 ("flags", "<i4")])
+                 ("flags", "<i4"), ("reserved", "<i4", 2), ("vis", "<i4", 4), ("cand_off", "<i8", 4)])
 
 
 def parse(plan):
@@ -139,6 +139,8 @@ PLAN_CASES = [
     synth.small(qk=synth.FP8, batch=5, s1=1, aslk=("uniform", 100, 9000), block_size=64, sparse_count=300),
     synth.small(batch=0, s1=4, aslk=[]),
     synth.small(layout=synth.TND, batch=0, s1=5, aslk=[], aslq=[]),
+    synth.small(batch=16, s1=1, aslk=[70000 - 977 * i for i in range(16)], block_size=64, sparse_count=256),
+    synth.small(batch=8, s1=2, aslk=[70000] * 8, block_size=32, sparse_count=256, sparse_mode=3),
 ]
 
 
@@ -172,9 +174,36 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
     assert np.all(padded == 1)
     k = p["sparse_count"]
     assert list(sel) == [r for r in range(nrows) if vis[r] > k]
-    assert ws == 4 * sum(int(vis[r]) for r in sel)
-    offs = [rows[r]["ws_off"] for r in sel]
-    assert offs == list(np.cumsum([0] + [int(vis[r]) for r in sel])[:-1])
+    local = bool(h["local_select"])
+    chunk = int(h["chunk"])
+    # candidates per selected row: every score, or each chunk's top-k
+    ncand = [sum(min(k, max(0, min(chunk, int(vis[r]) - c0))) for c0 in range(0, int(vis[r]), chunk))
+             if local else int(vis[r]) for r in sel]
+    assert [int(rows[r]["ncand"]) for r in sel] == ncand
+    assert all(int(rows[r]["indexed"]) == int(local) for r in sel)
+    offs = [int(rows[r]["ws_off"]) for r in sel]
+    assert offs == list(np.cumsum([0] + ncand)[:-1])
+    assert ws == (int(h["ws_index_offset"]) + 4 * sum(ncand) if local else 4 * sum(ncand))
+    if h["kind"] == 0:
+        # decode items: inline visible counts, and candidate slots that tile each row's range
+        slots = {r: [] for r in sel}
+        for it in items:
+            for u in range(it["nrows"]):
+                r = it["row0"] + u
+                assert it["vis"][u] == vis[r]
+                if it["nkeys"] and r in slots:
+                    n = min(k, max(0, min(chunk, int(vis[r]) - it["key0"]))) if local else \
+                        max(0, min(int(it["nkeys"]), int(vis[r]) - it["key0"]))
+                    slots[r].append((int(it["cand_off"][u]), n))
+                elif it["nkeys"]:
+                    assert it["cand_off"][u] == -1
+        for r, c in slots.items():
+            c.sort()
+            pos = int(rows[r]["ws_off"])
+            for off, n in c:
+                assert off == pos
+                pos += n
+            assert pos == int(rows[r]["ws_off"]) + int(rows[r]["ncand"])
     info = qli.qli_plan_info_get(plan)
     assert info.rows == nrows and info.visible_pairs == vis.sum() and info.select_rows == len(sel)
     assert info.active_rows == int((vis > 0).sum())
