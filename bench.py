@@ -4,22 +4,21 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--calibrate-copy]
 
-One step is one qli_run (scoring kernel + selection kernel) over one batch of
-seeded synthetic input resident in HBM.  Before every timed step a 512 MiB
-read sweep evicts L2 and the 256 MB Infinity Cache, so the paged key cache
-and its scales stream from HBM.  (A read sweep leaves no dirty lines; a
-write fill would leave up to 288 MB of write-backs competing with the step.)  Then, as in a decode step where the query, weights,
-query scales, block table and plan have just been produced, those small
-per-step tensors are rewritten from pristine copies (this is the headline
-cache state); the fully cold case (no rewrite) is timed as well and
-reported alongside.  Kernel durations come from HIP events attached to the
-launches themselves (hipExtLaunchKernel); the K steps are bracketed by
-torch.cuda.synchronize() on both sides.
+One step is one qli_run (scoring kernel + final selection kernel) over one
+batch of seeded synthetic input resident in HBM.  The inputs are held in R
+independent copies (R chosen so that the other copies between two uses of one
+copy span at least 640 MB, more than twice L2 + the 256 MB Infinity Cache);
+step s uses copy s mod R, so every step reads its key cache, scales, query,
+weights and block table cold from HBM, with no cache-eviction work inside the
+timed region.  The K timed steps are launched back to back between one pair
+of HIP events on the launch stream, bracketed by torch.cuda.synchronize() on
+both sides.  The scoring kernel and the selection kernel are then timed the
+same way on their own (qli_run_stage), which gives the roofline of the
+dominant kernel (the scoring kernel).
 
 Prints one JSON line: metric / value (visible query-token x key pairs scored
-and selected per second), the roofline of the dominant kernel (the scoring
-kernel), and the CPU oracle timed on the host on a bounded sample of the
-same workload.
+and selected per second), the roofline of the scoring kernel, and the CPU
+oracle timed on the host on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -28,7 +27,6 @@ import ctypes
 import hashlib
 import json
 import os
-import statistics
 import sys
 import time
 
@@ -40,7 +38,7 @@ DEFAULT_WORKLOAD = "decode_int8_b24_s4_sk8192"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA, TOP/s
 FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA, TFLOP/s
-FLUSH_BYTES = 512 << 20
+ROTATION_BYTES = 640 << 20     # distinct bytes touched between two uses of one input copy
 KERNEL_SOURCE = os.path.join(ROOT, "sparse_attention_token_paged_amd", "csrc", "qli_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -60,6 +58,7 @@ def hip_runtime():
             lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
             lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
             lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
             return lib
     raise RuntimeError("HIP runtime not loaded")
 
@@ -186,57 +185,53 @@ def main() -> int:
     p = inp["problem"]
     ix = qli.Indexer(p, inp["aslq"], inp["aslk"])
     info = ix.info
-    t = lambda a: torch.from_numpy(a).cuda()
-    dev = dict(query=t(inp["query"].view("uint8")), key=t(inp["key"]), weights=t(inp["weights"]),
-               q_scale=t(inp["q_scale"]), k_scale=t(inp["k_scale"]), block_table=t(inp["block_table"]))
+    host = dict(query=inp["query"].view("uint8"), key=inp["key"], weights=inp["weights"],
+                q_scale=inp["q_scale"], k_scale=inp["k_scale"], block_table=inp["block_table"])
     out_idx, out_val = ix.alloc_outputs()
-    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    set_bytes = sum(a.nbytes for a in host.values()) + out_idx.numel() * 4 * (2 if out_val is not None else 1)
+    R = max(2, 1 + -(-ROTATION_BYTES // set_bytes))
+    sets = []
+    for _ in range(R):
+        d = {n: torch.from_numpy(a).cuda() for n, a in host.items()}
+        sets.append((d["query"], d["key"], d["weights"], d["q_scale"], d["k_scale"], d["block_table"],
+                     out_idx, out_val))
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
 
-    def evict():
-        flush.sum()  # reads every line of a buffer twice the size of L2 + MALL
-    args_run = (dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
-                out_idx, out_val)
-
-    # Pristine copies of the per-step tensors, rewritten before each step.
-    fresh = [(dev["query"], dev["query"].clone()), (dev["weights"], dev["weights"].clone()),
-             (dev["q_scale"], dev["q_scale"].clone()), (dev["block_table"], dev["block_table"].clone()),
-             (ix.plan_dev, ix.plan_dev.clone())]
-
-    def run_steps(n: int, refresh: bool):
-        ev = Events(hip, 4 * n)
+    def region(n: int, stages: int) -> float:
+        """Milliseconds per launch of n back-to-back launches, one event pair."""
+        ev = Events(hip, 2)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
+        assert hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), ctypes.c_void_p(st)) == 0
         for s_ in range(n):
-            evict()
-            if refresh:
-                for dst, src in fresh:
-                    dst.copy_(src)
-            ix.run_timed(*args_run, events=ev.ev[4 * s_:4 * s_ + 4])
+            ix.run_stage(*sets[s_ % R], stages=stages, stream=st)
+        assert hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), ctypes.c_void_p(st)) == 0
         torch.cuda.synchronize()
-        wall_ = time.perf_counter() - t0
-        has_sel = info.select_rows > 0
-        step = [ev.ms(4 * i, 4 * i + 3 if has_sel else 4 * i + 1) for i in range(n)]
-        score = [ev.ms(4 * i, 4 * i + 1) for i in range(n)]
-        sel = [ev.ms(4 * i + 2, 4 * i + 3) if has_sel else 0.0 for i in range(n)]
+        ms_ = ev.ms(0, 1) / n
         ev.close()
-        return step, score, sel, wall_
+        return ms_
 
-    for _ in range(args.warmup):
-        evict()
-        ix.run(*args_run)
+    for s_ in range(args.warmup):
+        ix.run_stage(*sets[s_ % R], stages=3, stream=st)
     torch.cuda.synchronize()
 
     K = args.steps
-    step_ms, score_ms, select_ms, wall = run_steps(K, refresh=True)
-    cold_step, cold_score, cold_select, _ = run_steps(K, refresh=False)
-
-    # Back-to-back steps without the fill (inputs may hit in the caches): context only.
-    torch.cuda.synchronize()
     tw = time.perf_counter()
-    for _ in range(K):
-        ix.run(*args_run)
+    ms = region(K, 3)                 # the timed steps
+    wall = time.perf_counter() - tw
+    score_avg = region(K, 1)          # scoring kernel alone
+    select_avg = region(K, 2) if info.select_rows > 0 else 0.0
+
+    # Context only: back-to-back steps on one copy (inputs may hit in the caches).
+    ev = Events(hip, 2)
     torch.cuda.synchronize()
-    warm_ms = (time.perf_counter() - tw) * 1e3 / K
+    hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), ctypes.c_void_p(st))
+    for _ in range(K):
+        ix.run_stage(*sets[0], stages=3, stream=st)
+    hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), ctypes.c_void_p(st))
+    torch.cuda.synchronize()
+    warm_ms = ev.ms(0, 1) / K
+    ev.close()
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -246,9 +241,7 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    ms = statistics.mean(step_ms)
     alg = algorithmic(info, p)
-    score_avg = statistics.mean(score_ms)
     prefill = info.kind == 1
     if prefill:
         peak = FP8_PEAK_TFLOPS if p["qk_dtype"] == 1 else INT8_PEAK_TOPS
@@ -285,18 +278,13 @@ def main() -> int:
         },
         "roofline": roof,
         "step": {
-            "ms_median": round(statistics.median(step_ms), 5), "ms_min": round(min(step_ms), 5),
-            "score_kernel_ms": round(score_avg, 5), "select_kernel_ms": round(statistics.mean(select_ms), 5),
+            "score_kernel_ms": round(score_avg, 5), "select_kernel_ms": round(select_avg, 5),
             "hbm_gbs_step": round(alg["total"] / (ms * 1e-3) / 1e9, 1),
             "hbm_frac_step": round(alg["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes_step": alg["total"], "warm_back_to_back_ms": round(warm_ms, 5),
-            "timed_wall_s_incl_cache_fill": round(wall, 4),
-            "cache_state": "key cache and key scales evicted (512 MiB read sweep); query, weights, query "
-                           "scales, block table and plan rewritten before each step",
-            "all_cold": {"ms_mean": round(statistics.mean(cold_step), 5),
-                         "score_kernel_ms": round(statistics.mean(cold_score), 5),
-                         "select_kernel_ms": round(statistics.mean(cold_select), 5),
-                         "value": info.visible_pairs / (statistics.mean(cold_step) * 1e-3)},
+            "algorithmic_bytes_step": alg["total"], "warm_one_copy_ms": round(warm_ms, 5),
+            "timed_wall_s": round(wall, 4),
+            "cache_state": "every input cold: %d rotated copies of all inputs (%.1f MB each)" % (R, set_bytes / 1e6),
+            "score_items": info.score_items, "select_rows": info.select_rows,
         },
         "cpu_baseline": None,
     }

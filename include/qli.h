@@ -198,21 +198,21 @@ int qli_run_debug(const qli_problem *p, const void *plan_host,
                   void *stream);
 
 /*
- * qli_run_timed -- qli_run whose kernel launches also record four
- * caller-created hipEvent_t handles (passed as void*): events[0] / events[1]
- * at the start / end of the scoring kernel and events[2] / events[3] at the
- * start / end of the selection kernel (left unrecorded when no row needs a
- * selection).  The events are attached to the launches themselves
- * (hipExtLaunchKernel), so they time the kernels without extra stream
- * commands.  For throughput measurement; outputs and errors are those of
- * qli_run.  events must point to 4 handles; any handle may be NULL.
+ * qli_run_stage -- qli_run restricted to some of its two kernels, for
+ * measuring each one on its own: stages = 1 runs only the scoring kernel
+ * (contraction, epilogue, chunk-local selection; rows that see at most
+ * sparse_count entries are finished here), 2 only the final selection
+ * kernel, 3 both (= qli_run).  Stage 2 alone reads whatever the workspace
+ * holds from the last stage-1 run with the same plan and workspace; its
+ * outputs are meaningful only after one.  Returns QLI_ERR_ARG for other
+ * values of stages; otherwise errors are those of qli_run.
  */
-int qli_run_timed(const qli_problem *p, const void *plan_host,
+int qli_run_stage(const qli_problem *p, const void *plan_host,
                   const void *plan_dev, const void *query, const void *key,
                   const void *weights, const void *q_scale,
                   const void *k_scale, const int32_t *block_table,
                   void *workspace, int32_t *sparse_indices,
-                  float *sparse_values, void *const *events, void *stream);
+                  float *sparse_values, int32_t stages, void *stream);
 
 #ifdef __cplusplus
 }

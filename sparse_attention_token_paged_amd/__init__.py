@@ -25,7 +25,7 @@ SCALE_F16, SCALE_F32 = 0, 1
 LAYOUT_BSND, LAYOUT_TND = 0, 1
 INT64_MAX = (1 << 63) - 1
 
-EXPORTED = ("qli_status_string", "qli_plan", "qli_plan_info_get", "qli_run", "qli_run_debug", "qli_run_timed")
+EXPORTED = ("qli_status_string", "qli_plan", "qli_plan_info_get", "qli_run", "qli_run_debug", "qli_run_stage")
 
 c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
@@ -86,8 +86,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.qli_run_debug.argtypes = ([ctypes.POINTER(Problem), c_p, c_p] + [c_p] * 9 +
                                       [c_i64, c_i64, c_i64, c_p, c_p, c_p])
         lib.qli_run_debug.restype = ctypes.c_int
-        lib.qli_run_timed.argtypes = [ctypes.POINTER(Problem), c_p, c_p] + [c_p] * 9 + [c_p, c_p]
-        lib.qli_run_timed.restype = ctypes.c_int
+        lib.qli_run_stage.argtypes = [ctypes.POINTER(Problem), c_p, c_p] + [c_p] * 9 + [c_i32, c_p]
+        lib.qli_run_stage.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -148,14 +148,13 @@ def qli_run(problem: Problem, plan_host, plan_dev, query, key, weights, q_scale,
                           _addr(sparse_values), stream)
 
 
-def qli_run_timed(problem: Problem, plan_host, plan_dev, query, key, weights, q_scale, k_scale,
-                  block_table, workspace, sparse_indices, sparse_values, events, stream=None) -> int:
-    """events: 4 raw hipEvent_t handles (ints) or None: score start/end, select start/end."""
-    arr = (c_p * 4)(*[e if e else None for e in events])
-    return load().qli_run_timed(ctypes.byref(problem), _addr(plan_host), _addr(plan_dev), _addr(query),
+def qli_run_stage(problem: Problem, plan_host, plan_dev, query, key, weights, q_scale, k_scale,
+                  block_table, workspace, sparse_indices, sparse_values, stages: int, stream=None) -> int:
+    """stages: 1 = scoring kernel only, 2 = final selection only, 3 = both (qli_run)."""
+    return load().qli_run_stage(ctypes.byref(problem), _addr(plan_host), _addr(plan_dev), _addr(query),
                                 _addr(key), _addr(weights), _addr(q_scale), _addr(k_scale),
                                 _addr(block_table), _addr(workspace), _addr(sparse_indices),
-                                _addr(sparse_values), arr, stream)
+                                _addr(sparse_values), stages, stream)
 
 
 def qli_run_debug(problem: Problem, plan_host, plan_dev, query, key, weights, q_scale, k_scale,
@@ -214,13 +213,13 @@ class Indexer:
             raise QliError(rc, "qli_run")
         return out_idx, out_val
 
-    def run_timed(self, query, key, weights, q_scale, k_scale, block_table, out_idx, out_val, events,
+    def run_stage(self, query, key, weights, q_scale, k_scale, block_table, out_idx, out_val, stages: int,
                   stream: Optional[int] = None):
         st = current_stream() if stream is None else stream
-        rc = qli_run_timed(self.problem, self.plan_host, self.plan_dev, query, key, weights, q_scale, k_scale,
-                           block_table, self.workspace, out_idx, out_val, events, st)
+        rc = qli_run_stage(self.problem, self.plan_host, self.plan_dev, query, key, weights, q_scale, k_scale,
+                           block_table, self.workspace, out_idx, out_val, stages, st)
         if rc != QLI_OK:
-            raise QliError(rc, "qli_run_timed")
+            raise QliError(rc, "qli_run_stage")
         return out_idx, out_val
 
     def run_debug(self, query, key, weights, q_scale, k_scale, block_table, row0, row1, cols,

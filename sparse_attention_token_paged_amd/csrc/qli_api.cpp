@@ -387,7 +387,7 @@ static int run_common(const qli_problem* p, const void* plan_host, const void* p
                       const void* q_scale, const void* k_scale, const int32_t* block_table,
                       void* workspace, int32_t* sparse_indices, float* sparse_values,
                       int64_t row0, int64_t row1, int64_t cols, void* dots_out,
-                      float* scores_out, bool dump, void* const* events, void* stream) {
+                      float* scores_out, bool dump, int stages, void* stream) {
   int rc = validate_problem(p);
   if (rc != QLI_OK) return rc;
   if (!plan_matches(p, plan_host)) return QLI_ERR_PLAN;
@@ -416,9 +416,10 @@ static int run_common(const qli_problem* p, const void* plan_host, const void* p
     if (row0 < 0 || row1 < row0 || row1 > a.hdr->rows || cols < 0) return QLI_ERR_ARG;
     if (row1 > row0 && cols > 0 && (!dots_out || !scores_out)) return QLI_ERR_ARG;
   }
+  if (stages < 1 || stages > 3) return QLI_ERR_ARG;
   if (a.hdr->rows == 0) return QLI_OK;
-  if (launch_score(a, dump, events) != 0) return QLI_ERR_HIP;
-  if (a.hdr->n_select > 0 && launch_select(a, events) != 0) return QLI_ERR_HIP;
+  if ((stages & 1) && launch_score(a, dump) != 0) return QLI_ERR_HIP;
+  if ((stages & 2) && a.hdr->n_select > 0 && launch_select(a) != 0) return QLI_ERR_HIP;
   return QLI_OK;
 }
 
@@ -429,18 +430,18 @@ QLI_EXPORT int qli_run(const qli_problem* p, const void* plan_host, const void* 
                        void* stream) {
   return run_common(p, plan_host, plan_dev, query, key, weights, q_scale, k_scale, block_table,
                     workspace, sparse_indices, sparse_values, 0, 0, 0, nullptr, nullptr, false,
-                    nullptr, stream);
+                    3, stream);
 }
 
-QLI_EXPORT int qli_run_timed(const qli_problem* p, const void* plan_host, const void* plan_dev,
+QLI_EXPORT int qli_run_stage(const qli_problem* p, const void* plan_host, const void* plan_dev,
                              const void* query, const void* key, const void* weights,
                              const void* q_scale, const void* k_scale,
                              const int32_t* block_table, void* workspace,
-                             int32_t* sparse_indices, float* sparse_values, void* const* events,
+                             int32_t* sparse_indices, float* sparse_values, int32_t stages,
                              void* stream) {
   return run_common(p, plan_host, plan_dev, query, key, weights, q_scale, k_scale, block_table,
                     workspace, sparse_indices, sparse_values, 0, 0, 0, nullptr, nullptr, false,
-                    events, stream);
+                    stages, stream);
 }
 
 QLI_EXPORT int qli_run_debug(const qli_problem* p, const void* plan_host, const void* plan_dev,
@@ -452,5 +453,5 @@ QLI_EXPORT int qli_run_debug(const qli_problem* p, const void* plan_host, const 
                              void* stream) {
   return run_common(p, plan_host, plan_dev, query, key, weights, q_scale, k_scale, block_table,
                     workspace, sparse_indices, sparse_values, row0, row1, cols, dots_out,
-                    scores_out, true, nullptr, stream);
+                    scores_out, true, 3, stream);
 }

@@ -98,9 +98,7 @@ struct RunArgs {
   float* scores_out;
   void* stream;
 };
-// Optional timing: events[0..1] bracket the scoring kernel, events[2..3] the
-// selection kernel (recorded by the launch itself).
-int launch_score(const RunArgs& a, bool dump, void* const* events);
-int launch_select(const RunArgs& a, void* const* events);
+int launch_score(const RunArgs& a, bool dump);
+int launch_select(const RunArgs& a);
 
 }  // namespace qli

@@ -27,7 +27,6 @@
 //   threshold digit found with a block scan; ties at the threshold resolved
 //   towards the lower index with wave ballots and mbcnt prefix counts; the
 //   selected entries written in ascending index order.
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -954,37 +953,32 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams S) {
 }
 
 template <typename... Args>
-hipError_t launch(void (*kernel)(Args...), dim3 grid, dim3 block, hipStream_t st, void* const* ev, int e0,
-                  Args... args) {
-  void* argv[] = {(void*)&args...};
-  hipEvent_t start = ev ? static_cast<hipEvent_t>(ev[e0]) : nullptr;
-  hipEvent_t stop = ev ? static_cast<hipEvent_t>(ev[e0 + 1]) : nullptr;
-  const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, st,
-                                          start, stop, 0);
-  return e != hipSuccess ? e : hipGetLastError();
+hipError_t launch(void (*kernel)(Args...), dim3 grid, dim3 block, hipStream_t st, Args... args) {
+  hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  return hipGetLastError();
 }
 
 template <int QK, bool DUMP>
-hipError_t launch_score_t(const ScoreParams& P, const PlanHeader* h, hipStream_t st, void* const* ev) {
+hipError_t launch_score_t(const ScoreParams& P, const PlanHeader* h, hipStream_t st) {
   const dim3 grid(h->n_items), block(kScoreThreads);
   if (h->kind == kKindDecode) {
     const bool local = h->local_select != 0;
     switch (h->rows_per_item * 2 + (local ? 1 : 0)) {
-      case 2: return launch(score_decode_kernel<QK, 1, false, DUMP>, grid, block, st, ev, 0, P);
-      case 3: return launch(score_decode_kernel<QK, 1, true, DUMP>, grid, block, st, ev, 0, P);
-      case 4: return launch(score_decode_kernel<QK, 2, false, DUMP>, grid, block, st, ev, 0, P);
-      case 5: return launch(score_decode_kernel<QK, 2, true, DUMP>, grid, block, st, ev, 0, P);
-      case 8: return launch(score_decode_kernel<QK, 4, false, DUMP>, grid, block, st, ev, 0, P);
+      case 2: return launch(score_decode_kernel<QK, 1, false, DUMP>, grid, block, st, P);
+      case 3: return launch(score_decode_kernel<QK, 1, true, DUMP>, grid, block, st, P);
+      case 4: return launch(score_decode_kernel<QK, 2, false, DUMP>, grid, block, st, P);
+      case 5: return launch(score_decode_kernel<QK, 2, true, DUMP>, grid, block, st, P);
+      case 8: return launch(score_decode_kernel<QK, 4, false, DUMP>, grid, block, st, P);
       default: return hipErrorInvalidValue;
     }
   }
   if (h->rows_per_item != 8) return hipErrorInvalidValue;
-  return launch(score_kernel<QK, 2, 1, DUMP>, grid, block, st, ev, 0, P);
+  return launch(score_kernel<QK, 2, 1, DUMP>, grid, block, st, P);
 }
 
 }  // namespace
 
-int launch_score(const RunArgs& a, bool dump, void* const* events) {
+int launch_score(const RunArgs& a, bool dump) {
   const PlanHeader* h = a.hdr;
   if (h->n_items == 0) return 0;
   ScoreParams P{};
@@ -1013,15 +1007,15 @@ int launch_score(const RunArgs& a, bool dump, void* const* events) {
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   hipError_t e;
   if (a.p->qk_dtype == QLI_QK_INT8)
-    e = dump ? launch_score_t<QLI_QK_INT8, true>(P, h, st, events)
-             : launch_score_t<QLI_QK_INT8, false>(P, h, st, events);
+    e = dump ? launch_score_t<QLI_QK_INT8, true>(P, h, st)
+             : launch_score_t<QLI_QK_INT8, false>(P, h, st);
   else
-    e = dump ? launch_score_t<QLI_QK_FP8_E4M3FN, true>(P, h, st, events)
-             : launch_score_t<QLI_QK_FP8_E4M3FN, false>(P, h, st, events);
+    e = dump ? launch_score_t<QLI_QK_FP8_E4M3FN, true>(P, h, st)
+             : launch_score_t<QLI_QK_FP8_E4M3FN, false>(P, h, st);
   return e == hipSuccess ? 0 : (int)e;
 }
 
-int launch_select(const RunArgs& a, void* const* events) {
+int launch_select(const RunArgs& a) {
   const PlanHeader* h = a.hdr;
   if (h->n_select == 0) return 0;
   SelectParams S{};
@@ -1032,7 +1026,7 @@ int launch_select(const RunArgs& a, void* const* events) {
   S.val_out = a.sparse_values;
   S.k = a.p->sparse_count;
   const hipError_t e = launch(select_kernel, dim3(h->n_select), dim3(kSelThreads),
-                              static_cast<hipStream_t>(a.stream), events, 2, S);
+                              static_cast<hipStream_t>(a.stream), S);
   return e == hipSuccess ? 0 : (int)e;
 }
 

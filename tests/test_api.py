@@ -236,6 +236,9 @@ def test_run_rejects_bad_arguments_without_launching(qli):
     assert qli.qli_run(prob, plan, fake, *a) == qli.QLI_ERR_ARG
     invalid = qli.Problem.from_dict(dict(inp["problem"], sparse_mode=1))
     assert qli.qli_run(invalid, plan, fake, *args) == qli.QLI_ERR_ARG
+    # stage selection: only 1, 2 and 3 are valid
+    for stages in (0, 4, -1):
+        assert qli.qli_run_stage(prob, plan, fake, *args, stages) == qli.QLI_ERR_ARG
     # debug range checks
     assert qli.qli_run_debug(prob, plan, fake, *args, 2, 1, 8, fake, fake) == qli.QLI_ERR_ARG
     assert qli.qli_run_debug(prob, plan, fake, *args, 0, 99, 8, fake, fake) == qli.QLI_ERR_ARG

@@ -191,6 +191,28 @@ def test_repeat_runs_identical():
     assert np.array_equal(a_idx, b_idx) and np.array_equal(a_val, b_val)
 
 
+@pytest.mark.parametrize("name", ["bsnd_int8_causal_bs48_pad"])
+def test_stages_compose(name):
+    """Scoring stage then selection stage, as two calls, gives qli_run's outputs;
+    also with the local-selection path."""
+    import torch
+    for inp in (synth.make_inputs(SMALL[name], 3), synth.make_inputs(LOCAL["local_rt2_causal"], 2)):
+        dev = device_inputs(inp)
+        a_idx, a_val, ix = run_gpu(inp, dev)
+        b_idx, b_val = ix.alloc_outputs()
+        b_idx.fill_(7)
+        if b_val is not None:
+            b_val.fill_(7.0)
+        args = (dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
+                b_idx, b_val)
+        ix.workspace.zero_()
+        ix.run_stage(*args, stages=1)
+        ix.run_stage(*args, stages=2)
+        torch.cuda.synchronize()
+        assert np.array_equal(a_idx, b_idx.cpu().numpy())
+        assert a_val is None or np.array_equal(a_val, b_val.cpu().numpy())
+
+
 @pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
 def test_workload_full_size(ora, name):
     """Each named workload at full size, in the benchmark's configuration:
