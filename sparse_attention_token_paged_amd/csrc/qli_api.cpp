@@ -100,7 +100,7 @@ struct Built {
   PlanHeader hdr;
   std::vector<RowInfo> rows;
   std::vector<Item> items;
-  std::vector<int32_t> select;
+  std::vector<SelectEntry> select;
 };
 
 int64_t align16(int64_t v) { return (v + 15) & ~int64_t(15); }
@@ -203,7 +203,7 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   auto seen = [&](int64_t vis, int64_t key0) -> int64_t {
     return std::max<int64_t>(0, std::min<int64_t>(chunk, vis - key0));
   };
-  int64_t ws = 0;
+  int64_t ws = 0, max_cand = 0;
   for (int64_t r = 0; r < rows; r++) {
     RowInfo& ri = out.rows[r];
     ri.ncand = 0;
@@ -217,8 +217,14 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
       ri.ws_off = ws;
       ri.ncand = (int32_t)n;
       ri.indexed = local ? 1 : 0;
-      ws += n;
-      out.select.push_back((int32_t)r);
+      ws += (n + 3) & ~int64_t(3);  // 16-byte aligned regions for vector loads
+      SelectEntry se{};
+      se.ws_off = ri.ws_off;
+      se.row = (int32_t)r;
+      se.ncand = ri.ncand;
+      se.indexed = ri.indexed;
+      out.select.push_back(se);
+      max_cand = std::max<int64_t>(max_cand, n);
     }
   }
 
@@ -280,13 +286,14 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   h.n_select = (int32_t)out.select.size();
   h.chunk = chunk;
   h.max_vis = (int32_t)max_vis;
+  h.max_cand = (int32_t)max_cand;
   h.key_entries = key_entries;
   h.table_entries = table_entries;
   h.active_rows = active;
   h.off_rows = align16(sizeof(PlanHeader));
   h.off_items = align16(h.off_rows + (int64_t)sizeof(RowInfo) * rows);
   h.off_select = align16(h.off_items + (int64_t)sizeof(Item) * h.n_items);
-  h.plan_bytes = align16(h.off_select + 4 * (int64_t)h.n_select);
+  h.plan_bytes = align16(h.off_select + (int64_t)sizeof(SelectEntry) * h.n_select);
   return QLI_OK;
 }
 
@@ -353,7 +360,7 @@ QLI_EXPORT int qli_plan(const qli_problem* p, const int32_t* aslq, const int32_t
     std::memcpy(dst, &b.hdr, sizeof(PlanHeader));
     if (!b.rows.empty()) std::memcpy(dst + b.hdr.off_rows, b.rows.data(), sizeof(RowInfo) * b.rows.size());
     if (!b.items.empty()) std::memcpy(dst + b.hdr.off_items, b.items.data(), sizeof(Item) * b.items.size());
-    if (!b.select.empty()) std::memcpy(dst + b.hdr.off_select, b.select.data(), 4 * b.select.size());
+    if (!b.select.empty()) std::memcpy(dst + b.hdr.off_select, b.select.data(), sizeof(SelectEntry) * b.select.size());
     return QLI_OK;
   } catch (const std::bad_alloc&) {
     return QLI_ERR_SIZE;

@@ -12,7 +12,7 @@
 namespace qli {
 
 constexpr uint32_t kPlanMagic = 0x504C4951u;  // "QILP"
-constexpr uint32_t kPlanVersion = 2;
+constexpr uint32_t kPlanVersion = 3;
 constexpr int kHeads = 64;       // query heads (QLI-README 约束说明)
 constexpr int kDim = 128;        // head dim of query and key (约束说明)
 constexpr int kTileKeys = 64;    // keys per MFMA tile step (4 n-tiles of 16)
@@ -35,7 +35,7 @@ struct PlanHeader {
   int64_t ws_scores;         // fp32 candidate scores staged in the workspace
   int64_t off_rows;          // byte offset of RowInfo[rows]
   int64_t off_items;         // byte offset of Item[n_items]
-  int64_t off_select;        // byte offset of int32[n_select]
+  int64_t off_select;        // byte offset of SelectEntry[n_select]
   int32_t kind;              // PlanKind
   int32_t rows_per_item;     // 1, 2, 4 (decode) or 8 (prefill)
   int32_t n_items;
@@ -43,7 +43,7 @@ struct PlanHeader {
   int32_t chunk;             // keys per work item
   int32_t max_vis;
   int32_t local_select;      // decode items reduce their chunk to its top-k candidates
-  int32_t reserved;
+  int32_t max_cand;          // largest candidate count of a selected row
   int64_t key_entries;       // sum over batches of the largest visible count
   int64_t table_entries;     // block-table entries spanned by those entries
   int64_t active_rows;       // rows with at least one visible entry
@@ -58,6 +58,16 @@ struct RowInfo {
   int32_t ncand;   // candidates the row stages for the selection stage
   int32_t indexed; // 1: candidates carry explicit key indices (chunk-local selection)
 };
+
+// One row that the final selection reduces (selection order).
+struct SelectEntry {
+  int64_t ws_off;   // element offset of its candidates (a multiple of 4)
+  int32_t row;
+  int32_t ncand;
+  int32_t indexed;  // 1: candidates carry explicit key indices
+  int32_t reserved[3];
+};
+static_assert(sizeof(SelectEntry) == 32, "select table layout");
 
 struct Item {
   int32_t row0;    // first global row

@@ -44,7 +44,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kScoreThreads = 256;
 
 struct ScoreParams {
-  const uint8_t* plan;
+  const Item* items;      // the plan's item table (one item per workgroup)
+  const RowInfo* rinfo;   // the plan's row table
   const uint8_t* query;
   const uint8_t* key;
   const void* weights;
@@ -120,9 +121,8 @@ template <int QK, int RW, int WPR, bool DUMP>
 __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(RW == 1 ? 4 : 2)))
 void score_kernel(ScoreParams P) {
   constexpr int NT = 4 / WPR;  // 16-key n-tiles per wave per 64-key tile
-  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(P.plan);
-  const RowInfo* rinfo = reinterpret_cast<const RowInfo*>(P.plan + hdr->off_rows);
-  const Item it = reinterpret_cast<const Item*>(P.plan + hdr->off_items)[blockIdx.x];
+  const RowInfo* rinfo = P.rinfo;
+  const Item it = P.items[blockIdx.x];
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kTileKeys * kDim];
   __shared__ float lds_sk[2][kTileKeys];
@@ -437,174 +437,216 @@ __device__ int block_exclusive_scan(int v, int* tmp) {
   return before + incl - v;
 }
 
-struct SelectShared {
-  uint32_t red_and[16], red_or[16];
-  int scan_tmp[16];
-  int res[4];
-  int cnt_gt[16], cnt_eq[16];
+// ---------------------------------------------------------------------------
+// Top-k selection over staged scores.
+// ---------------------------------------------------------------------------
+//
+// The n scores sit in LDS (or, for very long rows, in the workspace), 16-byte
+// aligned and readable up to n rounded up to 4.  Thread t owns the
+// contiguous positions [t*S, t*S + S), S = ceil(n / NT) rounded up to 4, and
+// walks them with a rolled float4 loop in every phase (keys are formed on
+// the fly with order_key), so the executed code stays small.
+//
+// Threshold: the bits every key shares are skipped, then radix passes of up
+// to 11 bits histogram the keys that still match the threshold prefix (LDS
+// atomics into one of two 2048-bin histograms, the other being cleared
+// meanwhile); a block scan over the bins in descending digit order finds
+// the digit of the kk-th largest key.  It stops once the threshold bin is
+// taken whole or all 32 bits are fixed.  Three barriers per pass.
+// Emission: every key above the threshold and the kk lowest-positioned keys
+// equal to it, each at its rank in position order (block scans of the
+// per-thread counts).
+
+// Inclusive prefix sum over the 64 lanes: DPP row shifts within rows of 16,
+// then the row broadcasts.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// AND and OR over the 64 lanes (uniform results): DPP within rows of 16, then
+// one lane per row.
+__device__ __forceinline__ void wave_and_or(uint32_t& a, uint32_t& o) {
+  int x = (int)a, y = (int)o;
+  x &= __builtin_amdgcn_update_dpp(0, x, 0xb1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+  y |= __builtin_amdgcn_update_dpp(0, y, 0xb1, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(0, x, 0x4e, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+  y |= __builtin_amdgcn_update_dpp(0, y, 0x4e, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(0, x, 0x141, 0xf, 0xf, false);  // row_half_mirror
+  y |= __builtin_amdgcn_update_dpp(0, y, 0x141, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(0, x, 0x140, 0xf, 0xf, false);  // row_mirror
+  y |= __builtin_amdgcn_update_dpp(0, y, 0x140, 0xf, 0xf, false);
+  a = (uint32_t)(__builtin_amdgcn_readlane(x, 0) & __builtin_amdgcn_readlane(x, 16) &
+                 __builtin_amdgcn_readlane(x, 32) & __builtin_amdgcn_readlane(x, 48));
+  o = (uint32_t)(__builtin_amdgcn_readlane(y, 0) | __builtin_amdgcn_readlane(y, 16) |
+                 __builtin_amdgcn_readlane(y, 32) | __builtin_amdgcn_readlane(y, 48));
+}
+
+struct SelShared {
+  uint32_t red[2][16];  // per-wave AND / OR
+  int wsum[2][16];      // per-wave scan totals
+  int res[2][4];        // per-pass result: digit, keys above it, keys in it
 };
 
-// Top-k of n order keys (key_at(e), e in [0, n)), larger first, ties to the
-// lower position.  Radix select with 11-bit digits that starts below the
-// bits every key shares; LDS histograms (hist: 2048 ints); the threshold
-// digit is found with a block scan.  Then emit(pos, e, key) is called for
-// the k winners with pos = their rank in ascending position order: waves own
-// contiguous segments, and ties at the threshold are ranked with ballots and
-// mbcnt prefix counts.  Requires n > k >= 1 and all NT threads.
-template <int NT, typename KeyAt, typename Emit>
-__device__ void block_select(int n, int k, KeyAt&& key_at, Emit&& emit, int* hist, SelectShared& sh) {
+// Exclusive prefix over the workgroup of two per-thread counts; also their totals.
+template <int NT>
+__device__ __forceinline__ void block_scan2(int x, int y, int& xb, int& yb, int& xt, int& yt, SelShared& sh) {
   constexpr int NW = NT / 64;
-  constexpr int BATCH = 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int xi = wave_incl_scan(x), yi = wave_incl_scan(y);
+  if (lane == 63) {
+    sh.wsum[0][wave] = xi;
+    sh.wsum[1][wave] = yi;
+  }
+  __syncthreads();
+  xb = xi - x;
+  yb = yi - y;
+  xt = 0;
+  yt = 0;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    const int a = sh.wsum[0][w], b = sh.wsum[1][w];
+    xb += w < wave ? a : 0;
+    yb += w < wave ? b : 0;
+    xt += a;
+    yt += b;
+  }
+}
+
+// Top-k (k <= n) of the scores src[0, n); emit(pos, e, value) for each winner
+// e with pos its rank in position order.  hist: 2 x 2048 ints.  All NT threads.
+template <int NT, typename Emit>
+__device__ __forceinline__ void select_topk(const float* src, int n, int k, int* hist, SelShared& sh,
+                                            Emit&& emit) {
+  constexpr int NW = NT / 64;
+  constexpr int BPT = 2048 / NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  auto for_each = [&](auto&& f) {
-    for (int base = 0; base < n; base += NT * BATCH) {
-      uint32_t u[BATCH];
-#pragma unroll
-      for (int i = 0; i < BATCH; i++) {
-        const int e = base + i * NT + tid;
-        u[i] = e < n ? key_at(e) : 0u;
-      }
-#pragma unroll
-      for (int i = 0; i < BATCH; i++) {
-        const int e = base + i * NT + tid;
-        if (e < n) f(e, u[i]);
-      }
-    }
-  };
+  const int S = (((n + NT - 1) / NT) + 3) & ~3;
+  const int beg = min(n, tid * S), end = min(n, beg + S);
+  const float* mine = src + beg;
+  const int cnt = end - beg;
+
   uint32_t a = 0xFFFFFFFFu, o = 0u;
-  for_each([&](int, uint32_t u) {
-    a &= u;
-    o |= u;
-  });
+#pragma unroll 1
+  for (int j = 0; j < cnt; j += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(mine + j);
+    const uint32_t q[4] = {order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w)};
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    a &= __shfl_xor(a, off, 64);
-    o |= __shfl_xor(o, off, 64);
+    for (int c = 0; c < 4; c++) {
+      a &= j + c < cnt ? q[c] : 0xFFFFFFFFu;
+      o |= j + c < cnt ? q[c] : 0u;
+    }
   }
+  wave_and_or(a, o);
   if (lane == 0) {
-    sh.red_and[wave] = a;
-    sh.red_or[wave] = o;
+    sh.red[0][wave] = a;
+    sh.red[1][wave] = o;
   }
+  for (int b = tid; b < 2048; b += NT) hist[b] = 0;
   __syncthreads();
   a = 0xFFFFFFFFu;
   o = 0u;
 #pragma unroll
   for (int w = 0; w < NW; w++) {
-    a &= sh.red_and[w];
-    o |= sh.red_or[w];
+    a &= sh.red[0][w];
+    o |= sh.red[1][w];
   }
-  const uint32_t diff = a ^ o;
-  uint32_t mask, prefix;
-  int lo;
-  if (diff == 0u) {
-    mask = 0xFFFFFFFFu;
-    prefix = a;
-    lo = 0;
-  } else {
-    const int hb = 31 - __clz(diff);
-    mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
-    prefix = a & mask;
-    lo = hb + 1;
-  }
-  // Invariant: the kk-th largest key has the top bits `prefix` under `mask`,
-  // and kk <= the number of keys that do.
+  // Invariant: the kk-th largest key matches `prefix` under `mask`, and at
+  // least kk keys do.
   int kk = k;
-  bool whole_bin = diff == 0u;
-  while (!whole_bin && lo > 0) {
+  uint32_t mask = 0xFFFFFFFFu, prefix = a;
+  const uint32_t diff = a ^ o;
+  int lo = diff == 0u ? 0 : 32 - __clz(diff);  // bits below lo still differ
+  if (lo > 0) {
+    mask = lo == 32 ? 0u : ~((1u << lo) - 1u);
+    prefix = a & mask;
+  }
+  for (int p = 0; lo > 0; p++) {
     const int width = lo < 11 ? lo : 11;
     const int shift = lo - width;
     const int nb = 1 << width;
-    for (int b = tid; b < nb; b += NT) hist[b] = 0;
+    int* H = hist + (p & 1) * 2048;
+#pragma unroll 1
+    for (int j = 0; j < cnt; j += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(mine + j);
+      const uint32_t q[4] = {order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w)};
+#pragma unroll
+      for (int c = 0; c < 4; c++)
+        if (j + c < cnt && (q[c] & mask) == prefix) atomicAdd(&H[(q[c] >> shift) & (nb - 1)], 1);
+    }
+    int* Hn = hist + ((p + 1) & 1) * 2048;  // read last in pass p - 1, used by pass p + 1
+    for (int b = tid; b < 2048; b += NT) Hn[b] = 0;
     __syncthreads();
-    for_each([&](int, uint32_t u) {
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1);
-    });
-    __syncthreads();
-    // Thread t owns digits in descending order: BPT = 2048 / NT consecutive ones.
-    constexpr int BPT = 2048 / NT;
+    // Thread t owns digits nb-1-BPT*t .. nb-BPT*(t+1) (descending).
     int h[BPT];
     int local = 0;
 #pragma unroll
-    for (int i = 0; i < BPT; i++) {
-      const int d = nb - 1 - (BPT * tid + i);
-      h[i] = d >= 0 ? hist[d] : 0;
-      local += h[i];
+    for (int jj = 0; jj < BPT; jj++) {
+      const int d = nb - 1 - (BPT * tid + jj);
+      h[jj] = d >= 0 ? H[d] : 0;
+      local += h[jj];
     }
-    const int before = block_exclusive_scan<NT>(local, sh.scan_tmp);
+    const int incl = wave_incl_scan(local);
+    if (lane == 63) sh.wsum[p & 1][wave] = incl;
+    __syncthreads();
+    int before = incl - local;
+#pragma unroll
+    for (int w = 0; w < NW; w++) before += w < wave ? sh.wsum[p & 1][w] : 0;
     if (before < kk && kk <= before + local) {
       int acc = before;
 #pragma unroll
-      for (int i = 0; i < BPT; i++) {
-        if (acc < kk && kk <= acc + h[i]) {
-          sh.res[0] = nb - 1 - (BPT * tid + i);
-          sh.res[1] = acc;
-          sh.res[2] = h[i];
+      for (int jj = 0; jj < BPT; jj++) {
+        if (acc < kk && kk <= acc + h[jj]) {
+          sh.res[p & 1][0] = nb - 1 - (BPT * tid + jj);
+          sh.res[p & 1][1] = acc;
+          sh.res[p & 1][2] = h[jj];
         }
-        acc += h[i];
+        acc += h[jj];
       }
     }
     __syncthreads();
-    const int digit = sh.res[0], above = sh.res[1], count = sh.res[2];
-    __syncthreads();  // res and hist are rewritten by the next pass
+    const int digit = sh.res[p & 1][0], above = sh.res[p & 1][1], count = sh.res[p & 1][2];
     kk -= above;
     prefix |= (uint32_t)digit << shift;
     mask |= (uint32_t)(nb - 1) << shift;
     lo = shift;
-    whole_bin = count == kk;
+    if (count == kk) break;  // the whole threshold bin wins
   }
 
-  // Emission in ascending position order over per-wave contiguous segments.
-  const int seg = (((n + NW - 1) / NW) + 63) & ~63;
-  const int beg = min(n, wave * seg);
-  const int end = min(n, beg + seg);
-  auto segment = [&](auto&& f) {
-    for (int e0 = beg; e0 < end; e0 += 64 * BATCH) {
-      uint32_t u[BATCH];
+  int g = 0, q = 0;
+#pragma unroll 1
+  for (int j = 0; j < cnt; j += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(mine + j);
+    const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int i = 0; i < BATCH; i++) {
-        const int e = e0 + 64 * i + lane;
-        u[i] = e < end ? key_at(e) : 0u;
-      }
-#pragma unroll
-      for (int i = 0; i < BATCH; i++) {
-        const int e = e0 + 64 * i + lane;
-        if (e0 + 64 * i < end) f(e, e < end, u[i]);
-      }
-    }
-  };
-  int ngt = 0, neq = 0;
-  segment([&](int, bool live, uint32_t u) {
-    const uint32_t m = u & mask;
-    ngt += __popcll(__ballot(live && m > prefix));
-    neq += __popcll(__ballot(live && m == prefix));
-  });
-  if (lane == 0) {
-    sh.cnt_gt[wave] = ngt;
-    sh.cnt_eq[wave] = neq;
-  }
-  __syncthreads();
-  int eq_before = 0, sel_before = 0;
-#pragma unroll
-  for (int w = 0; w < NW; w++) {
-    if (w < wave) {
-      sel_before += sh.cnt_gt[w] + min(sh.cnt_eq[w], max(0, kk - eq_before));
-      eq_before += sh.cnt_eq[w];
+    for (int c = 0; c < 4; c++) {
+      const uint32_t m = order_key(f[c]) & mask;
+      g += (j + c < cnt && m > prefix) ? 1 : 0;
+      q += (j + c < cnt && m == prefix) ? 1 : 0;
     }
   }
-  int run_eq = eq_before, run_sel = sel_before;
-  segment([&](int e, bool live, uint32_t u) {
-    const uint32_t m = u & mask;
-    const bool gt = live && m > prefix;
-    const bool eq = live && m == prefix;
-    const uint64_t beq = __ballot(eq);
-    const bool take = gt || (eq && run_eq + lanes_below(beq) < kk);
-    const uint64_t btake = __ballot(take);
-    const int pos = run_sel + lanes_below(btake);
-    if (take && pos < k) emit(pos, e, u);  // exactly k are taken; the bound guards the slots
-    run_eq += __popcll(beq);
-    run_sel += __popcll(btake);
-  });
-  __syncthreads();
+  int G, E, gt_total, eq_total;
+  block_scan2<NT>(g, q, G, E, gt_total, eq_total, sh);
+#pragma unroll 1
+  for (int j = 0; j < cnt; j += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(mine + j);
+    const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const uint32_t m = order_key(f[c]) & mask;
+      const bool live = j + c < cnt;
+      const bool gt = live && m > prefix;
+      const bool eq = live && m == prefix;
+      if (gt || (eq && E < kk)) emit(G + min(E, kk), beg + j + c, f[c]);
+      G += gt ? 1 : 0;
+      E += eq ? 1 : 0;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -630,15 +672,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   constexpr int SB = QK == QLI_QK_INT8 ? 2 : 4;
   constexpr int LCAP = LOCAL ? kMaxChunk / RT : 1;
 
-  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(P.plan);
   // read in place: the per-row fields are indexed by a wave-uniform row
-  const Item& it = reinterpret_cast<const Item*>(P.plan + hdr->off_items)[blockIdx.x];
+  const Item& it = P.items[blockIdx.x];
 
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSTAGE][SC * kDim];
   __shared__ uint32_t ring_sk[NSTAGE][SC];   // ScaleK bits, one 4-byte slot per entry
   __shared__ int32_t lds_bt[kMaxChunk / 16 + 2];
-  __shared__ float lds_scores[RT][LCAP];     // LOCAL: the chunk's scores of each row
-  __shared__ SelectShared sel;
+  __shared__ __attribute__((aligned(16))) float lds_scores[RT][LCAP];  // LOCAL: the chunk's scores of each row
+  __shared__ SelShared sel;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -879,13 +920,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
           ws_idx[off + e] = key0 + e;
         }
       } else {
-        block_select<kScoreThreads>(
-            n, k, [&](int e) { return order_key(sc[e]); },
-            [&](int pos, int e, uint32_t key) {
-              P.ws[off + pos] = key_value(key);
-              ws_idx[off + pos] = key0 + e;
-            },
-            hist, sel);
+        select_topk<kScoreThreads>(sc, n, k, hist, sel, [&](int pos, int e, float v) __attribute__((always_inline)) {
+          P.ws[off + pos] = v;
+          ws_idx[off + pos] = key0 + e;
+        });
+        __syncthreads();  // the histograms and shared counters serve the next row
       }
     }
   }
@@ -897,10 +936,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
 // ---------------------------------------------------------------------------
 
 constexpr int kSelThreads = 1024;
-constexpr int kSelCache = 32768;  // candidate keys cached in LDS (128 KiB)
 
 struct SelectParams {
-  const uint8_t* plan;
+  const SelectEntry* rows;  // the plan's selection table
   const float* ws;
   const int32_t* ws_idx;
   int32_t* idx_out;
@@ -908,48 +946,46 @@ struct SelectParams {
   int32_t k;
 };
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams S) {
-  constexpr int BATCH = 8;
-  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(S.plan);
-  const RowInfo* rinfo = reinterpret_cast<const RowInfo*>(S.plan + hdr->off_rows);
-  const int32_t* sel_rows = reinterpret_cast<const int32_t*>(S.plan + hdr->off_select);
-  const int64_t row = sel_rows[blockIdx.x];
-  const RowInfo ri = rinfo[row];
-  const int n = ri.ncand;
-  const float* sc = S.ws + ri.ws_off;
-  const int32_t* ix = ri.indexed ? S.ws_idx + ri.ws_off : nullptr;
-  const int k = S.k;
+// LDS: the row (n <= kSelLdsCap) is staged in LDS once; otherwise every
+// phase reads it from the workspace.  INDEXED: the candidates carry their
+// key indices (chunk-local selection), else a candidate's position is its
+// key index.
+constexpr int kSelLdsCap = 32768;
 
-  __shared__ uint32_t cache[kSelCache];
-  __shared__ int hist[2048];
-  __shared__ SelectShared sh;
+template <bool LDS, bool INDEXED>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams S) {
+  __shared__ int hist[2 * 2048];
+  __shared__ SelShared sh;
+  __shared__ __attribute__((aligned(16))) float cache[LDS ? kSelLdsCap : 4];
+  const SelectEntry se = S.rows[blockIdx.x];
+  const int n = se.ncand;
+  const int k = S.k;
+  const float* sc = S.ws + se.ws_off;
+  const int32_t* ix = S.ws_idx + se.ws_off;
   const int tid = threadIdx.x;
-  const bool cached = n <= kSelCache;
-  if (cached) {
-    for (int base = 0; base < n; base += kSelThreads * BATCH) {
-      float v[BATCH];
+  if constexpr (LDS) {
+    // eight 16-byte loads in flight per thread (addresses clamped into the
+    // row's 16-byte padded region), then the stores
+    constexpr int STEP = kSelThreads * 4;
+    const int last = ((n + 3) & ~3) - 4;
+    float4 v[kSelLdsCap / STEP];
 #pragma unroll
-      for (int i = 0; i < BATCH; i++) {
-        const int e = base + i * kSelThreads + tid;
-        v[i] = e < n ? sc[e] : 0.f;
-      }
+    for (int i = 0; i < kSelLdsCap / STEP; i++)
+      v[i] = *reinterpret_cast<const float4*>(sc + min(i * STEP + tid * 4, last));
 #pragma unroll
-      for (int i = 0; i < BATCH; i++) {
-        const int e = base + i * kSelThreads + tid;
-        if (e < n) cache[e] = order_key(v[i]);
-      }
+    for (int i = 0; i < kSelLdsCap / STEP; i++) {
+      const int e = i * STEP + tid * 4;
+      if (e < n) *reinterpret_cast<float4*>(&cache[e]) = v[i];
     }
     __syncthreads();
   }
-  int32_t* oi = S.idx_out + row * k;
-  float* ov = S.val_out ? S.val_out + row * k : nullptr;
-  block_select<kSelThreads>(
-      n, k, [&](int e) { return cached ? cache[e] : order_key(sc[e]); },
-      [&](int pos, int e, uint32_t key) {
-        oi[pos] = ix ? ix[e] : e;
-        if (ov) ov[pos] = key_value(key);
-      },
-      hist, sh);
+  int32_t* oi = S.idx_out + (int64_t)se.row * k;
+  float* ov = S.val_out ? S.val_out + (int64_t)se.row * k : nullptr;
+  select_topk<kSelThreads>(LDS ? cache : sc, n, k, hist, sh,
+                           [&](int pos, int e, float v) __attribute__((always_inline)) {
+                             oi[pos] = INDEXED ? ix[e] : e;
+                             if (ov) ov[pos] = v;
+                           });
 }
 
 template <typename... Args>
@@ -982,7 +1018,8 @@ int launch_score(const RunArgs& a, bool dump) {
   const PlanHeader* h = a.hdr;
   if (h->n_items == 0) return 0;
   ScoreParams P{};
-  P.plan = static_cast<const uint8_t*>(a.plan_dev);
+  P.items = reinterpret_cast<const Item*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_items);
+  P.rinfo = reinterpret_cast<const RowInfo*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_rows);
   P.query = static_cast<const uint8_t*>(a.query);
   P.key = static_cast<const uint8_t*>(a.key);
   P.weights = a.weights;
@@ -1019,14 +1056,20 @@ int launch_select(const RunArgs& a) {
   const PlanHeader* h = a.hdr;
   if (h->n_select == 0) return 0;
   SelectParams S{};
-  S.plan = static_cast<const uint8_t*>(a.plan_dev);
+  S.rows = reinterpret_cast<const SelectEntry*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_select);
   S.ws = static_cast<const float*>(a.workspace);
   S.ws_idx = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(a.workspace) + h->ws_index_offset);
   S.idx_out = a.sparse_indices;
   S.val_out = a.sparse_values;
   S.k = a.p->sparse_count;
-  const hipError_t e = launch(select_kernel, dim3(h->n_select), dim3(kSelThreads),
-                              static_cast<hipStream_t>(a.stream), S);
+  const dim3 grid(h->n_select), block(kSelThreads);
+  const hipStream_t st = static_cast<hipStream_t>(a.stream);
+  const bool lds = h->max_cand <= kSelLdsCap;
+  const hipError_t e = h->local_select
+                           ? (lds ? launch(select_kernel<true, true>, grid, block, st, S)
+                                  : launch(select_kernel<false, true>, grid, block, st, S))
+                           : (lds ? launch(select_kernel<true, false>, grid, block, st, S)
+                                  : launch(select_kernel<false, false>, grid, block, st, S));
   return e == hipSuccess ? 0 : (int)e;
 }
 

@@ -114,9 +114,10 @@ HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("fingerprint", "<u8"), ("
                 ("workspace_bytes", "<i8"), ("rows", "<i8"), ("visible_pairs", "<i8"), ("ws_scores", "<i8"),
                 ("off_rows", "<i8"), ("off_items", "<i8"), ("off_select", "<i8"), ("kind", "<i4"),
                 ("rows_per_item", "<i4"), ("n_items", "<i4"), ("n_select", "<i4"), ("chunk", "<i4"),
-                ("max_vis", "<i4"), ("local_select", "<i4"), ("reserved", "<i4"), ("key_entries", "<i8"),
+                ("max_vis", "<i4"), ("local_select", "<i4"), ("max_cand", "<i4"), ("key_entries", "<i8"),
                 ("table_entries", "<i8"), ("active_rows", "<i8"), ("ws_index_offset", "<i8")])
 ROW = np.dtype([("batch", "<i4"), ("vis", "<i4"), ("ws_off", "<i8"), ("ncand", "<i4"), ("indexed", "<i4")])
+SEL = np.dtype([("ws_off", "<i8"), ("row", "<i4"), ("ncand", "<i4"), ("indexed", "<i4"), ("reserved", "<i4", 3)])
 ITEM = np.dtype([("row0", "<i4"), ("nrows", "<i4"), ("batch", "<i4"), ("key0", "<i4"), ("nkeys", "<i4"),
                  ("flags", "<i4"), ("reserved", "<i4", 2), ("vis", "<i4", 4), ("cand_off", "<i8", 4)])
 
@@ -125,7 +126,7 @@ def parse(plan):
     h = np.frombuffer(plan[:HDR.itemsize].tobytes(), HDR)[0]
     rows = np.frombuffer(plan[h["off_rows"]:h["off_rows"] + ROW.itemsize * h["rows"]].tobytes(), ROW)
     items = np.frombuffer(plan[h["off_items"]:h["off_items"] + ITEM.itemsize * h["n_items"]].tobytes(), ITEM)
-    sel = np.frombuffer(plan[h["off_select"]:h["off_select"] + 4 * h["n_select"]].tobytes(), "<i4")
+    sel = np.frombuffer(plan[h["off_select"]:h["off_select"] + SEL.itemsize * h["n_select"]].tobytes(), SEL)
     return h, rows, items, sel
 
 
@@ -173,7 +174,10 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
     assert all(np.all(c == 1) for c in cover)
     assert np.all(padded == 1)
     k = p["sparse_count"]
-    assert list(sel) == [r for r in range(nrows) if vis[r] > k]
+    assert list(sel["row"]) == [r for r in range(nrows) if vis[r] > k]
+    assert np.array_equal(sel["ncand"], rows["ncand"][sel["row"]]) and np.array_equal(sel["ws_off"], rows["ws_off"][sel["row"]])
+    assert np.array_equal(sel["indexed"], rows["indexed"][sel["row"]])
+    sel = [int(r) for r in sel["row"]]
     local = bool(h["local_select"])
     chunk = int(h["chunk"])
     # candidates per selected row: every score, or each chunk's top-k
@@ -182,8 +186,10 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
     assert [int(rows[r]["ncand"]) for r in sel] == ncand
     assert all(int(rows[r]["indexed"]) == int(local) for r in sel)
     offs = [int(rows[r]["ws_off"]) for r in sel]
-    assert offs == list(np.cumsum([0] + ncand)[:-1])
-    assert ws == (int(h["ws_index_offset"]) + 4 * sum(ncand) if local else 4 * sum(ncand))
+    padded_n = [(n + 3) // 4 * 4 for n in ncand]  # 16-byte aligned candidate regions
+    assert offs == list(np.cumsum([0] + padded_n)[:-1])
+    assert ws == (int(h["ws_index_offset"]) + 4 * sum(padded_n) if local else 4 * sum(padded_n))
+    assert int(h["max_cand"]) == max(ncand, default=0)
     if h["kind"] == 0:
         # decode items: inline visible counts, and candidate slots that tile each row's range
         slots = {r: [] for r in sel}

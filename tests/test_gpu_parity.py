@@ -155,6 +155,30 @@ def test_parity_local_select(ora, name):
         check_row(r, v, k, gidx[r], gval[r], osc, rtol_of(inp))
 
 
+LONG_DENSE = {
+    # every score staged: 8193..32768 candidates (LDS-staged selection) and beyond (tiles reread)
+    "dense_rows_20k": synth.small(batch=2, s1=3, aslk=[20000, 9000], block_size=64, sparse_count=1500,
+                                  sparse_mode=3),
+    "dense_rows_40k": synth.small(batch=1, s1=3, aslk=[40000], block_size=128, sparse_count=300, sparse_mode=3),
+}
+
+
+@pytest.mark.parametrize("name", list(LONG_DENSE))
+def test_parity_long_dense_rows(ora, name):
+    inp = synth.make_inputs(LONG_DENSE[name], 17)
+    p = inp["problem"]
+    rows, k = rows_of(p), p["sparse_count"]
+    vis = vis_of(ora, inp)
+    ix = make_indexer(inp)
+    log("case %s: rows=%d k=%d max vis=%d" % (name, rows, k, int(vis.max())))
+    gidx, gval, _ = run_gpu(inp, ix=ix)
+    check_structure(gidx, gval, vis, k)
+    rc, _, _, osc = ora.indexer(inp, scores_cols=int(vis.max()))
+    assert rc == 0
+    for r in range(rows):
+        check_row(r, int(vis[r]), k, gidx[r], gval[r], osc[r, :vis[r]], rtol_of(inp))
+
+
 def test_ties_go_to_lower_index(ora):
     """Identical keys give bit-identical scores; the lowest indices win."""
     spec = synth.small(batch=2, s1=2, aslk=[1500, 800], block_size=64, sparse_count=200, sparse_mode=3,
