@@ -12,7 +12,9 @@ step s uses copy s mod R, so every step reads its key cache, scales, query,
 weights and block table cold from HBM, with no cache-eviction work inside the
 timed region.  The K timed steps are launched back to back between one pair
 of HIP events on the launch stream, bracketed by torch.cuda.synchronize() on
-both sides.  The scoring kernel and the selection kernel are then timed the
+both sides; a spin kernel queued ahead of the start event keeps the GPU busy
+while the host enqueues them, so the pair times GPU execution (the host's
+enqueue cost per step is reported beside it).  The scoring kernel and the selection kernel are then timed the
 same way on their own (qli_run_stage), which gives the roofline of the
 dominant kernel (the scoring kernel).
 
@@ -198,40 +200,52 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     st = stream.cuda_stream
 
-    def region(n: int, stages: int) -> float:
-        """Milliseconds per launch of n back-to-back launches, one event pair."""
+    def region(n: int, stages: int, rotate: bool = True):
+        """Milliseconds per launch of n back-to-back launches, one event pair,
+        and the host's enqueue time per launch in microseconds.  A spin
+        kernel ahead of the start event keeps the GPU busy while the host
+        enqueues, so the pair times GPU execution, not the host."""
         ev = Events(hip, 2)
         torch.cuda.synchronize()
+        torch.cuda._sleep(int(spin_cycles_per_us * (1.5 * n * enqueue_us + 200.0)))
         assert hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), ctypes.c_void_p(st)) == 0
+        t0 = time.perf_counter()
         for s_ in range(n):
-            ix.run_stage(*sets[s_ % R], stages=stages, stream=st)
+            ix.run_stage(*sets[s_ % R if rotate else 0], stages=stages, stream=st)
+        host_us = (time.perf_counter() - t0) * 1e6 / n
         assert hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), ctypes.c_void_p(st)) == 0
         torch.cuda.synchronize()
         ms_ = ev.ms(0, 1) / n
         ev.close()
-        return ms_
+        return ms_, host_us
 
     for s_ in range(args.warmup):
         ix.run_stage(*sets[s_ % R], stages=3, stream=st)
     torch.cuda.synchronize()
 
+    # Calibration: the spin kernel's rate, and the host's enqueue cost of one step.
+    ev = Events(hip, 2)
+    for _ in range(2):
+        torch.cuda.synchronize()
+        hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), ctypes.c_void_p(st))
+        torch.cuda._sleep(1000000)
+        hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), ctypes.c_void_p(st))
+        torch.cuda.synchronize()
+    spin_cycles_per_us = 1000000 / (ev.ms(0, 1) * 1e3)
+    ev.close()
+    t0 = time.perf_counter()
+    for s_ in range(20):
+        ix.run_stage(*sets[s_ % R], stages=3, stream=st)
+    enqueue_us = (time.perf_counter() - t0) * 1e6 / 20
+    torch.cuda.synchronize()
+
     K = args.steps
     tw = time.perf_counter()
-    ms = region(K, 3)                 # the timed steps
+    ms, host_us = region(K, 3)        # the timed steps
     wall = time.perf_counter() - tw
-    score_avg = region(K, 1)          # scoring kernel alone
-    select_avg = region(K, 2) if info.select_rows > 0 else 0.0
-
-    # Context only: back-to-back steps on one copy (inputs may hit in the caches).
-    ev = Events(hip, 2)
-    torch.cuda.synchronize()
-    hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), ctypes.c_void_p(st))
-    for _ in range(K):
-        ix.run_stage(*sets[0], stages=3, stream=st)
-    hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), ctypes.c_void_p(st))
-    torch.cuda.synchronize()
-    warm_ms = ev.ms(0, 1) / K
-    ev.close()
+    score_avg, _ = region(K, 1)       # scoring kernel alone
+    select_avg = region(K, 2)[0] if info.select_rows > 0 else 0.0
+    warm_ms, _ = region(K, 3, rotate=False)  # context only: one copy, inputs may hit in the caches
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -283,6 +297,7 @@ def main() -> int:
             "hbm_frac_step": round(alg["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_step": alg["total"], "warm_one_copy_ms": round(warm_ms, 5),
             "timed_wall_s": round(wall, 4),
+            "host_enqueue_us_per_step": round(host_us, 2),
             "cache_state": "every input cold: %d rotated copies of all inputs (%.1f MB each)" % (R, set_bytes / 1e6),
             "score_items": info.score_items, "select_rows": info.select_rows,
         },
