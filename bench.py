@@ -43,6 +43,7 @@ FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA, TFLOP/s
 ROTATION_BYTES = 640 << 20     # distinct bytes touched between two uses of one input copy
 KERNEL_SOURCE = os.path.join(ROOT, "sparse_attention_token_paged_amd", "csrc", "qli_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 256 << 20         # bytes read and bytes written by the counter-calibration kernel
 
 
 def kernel_source_hash() -> str:
@@ -122,6 +123,62 @@ def traffic_from_profiles(workload: str):
     return t.get("bytes_per_launch")
 
 
+def _counter_rows(directory: str):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit("no *counter_collection.csv under %s" % directory)
+    return rows
+
+
+def summarize_counters(workload: str, fetch_dir: str, write_dir: str) -> dict:
+    """HBM bytes per scoring-kernel launch from two rocprofv3 --pmc runs of
+    `bench.py --calibrate-copy` (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch).  Each counter is scaled by COPY_BYTES over what it reads for
+    the calibration kernel (torch.neg over 256 MiB).  Medians over the
+    dispatches, which are cold-input launches but for the warm-context ones."""
+    def per_kernel(rows, counter):
+        out = {}
+        for r in rows:
+            if r.get("Counter_Name") != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+    fetch = per_kernel(_counter_rows(fetch_dir), "FETCH_SIZE")
+    write = per_kernel(_counter_rows(write_dir), "WRITE_SIZE")
+    def pick(d, key):
+        names = [n for n in d if key(n)]
+        if not names:
+            raise SystemExit("no dispatch matched in the counter files")
+        vals = sorted(v for n in names for v in d[n])
+        return vals[len(vals) // 2], names
+    score = lambda n: "score_decode_kernel" in n or "score_kernel" in n
+    neg = lambda n: "neg" in n
+    f_score, names = pick(fetch, score)
+    w_score, _ = pick(write, score)
+    f_neg, _ = pick(fetch, neg)
+    w_neg, _ = pick(write, neg)
+    kf = COPY_BYTES / (f_neg * 1024.0)
+    kw = COPY_BYTES / (w_neg * 1024.0)
+    res = {
+        "workload": workload,
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernels": sorted(set(n.split("(")[0] for n in names)),
+        "fetch_kib_per_launch_raw": f_score, "write_kib_per_launch_raw": w_score,
+        "calibration": {"kernel": "torch.neg over %d MiB (reads and writes that much)" % (COPY_BYTES >> 20),
+                        "fetch_kib_raw": f_neg, "write_kib_raw": w_neg,
+                        "fetch_scale": round(kf, 4), "write_scale": round(kw, 4)},
+        "fetch_bytes_per_launch": round(f_score * 1024.0 * kf),
+        "write_bytes_per_launch": round(w_score * 1024.0 * kw),
+    }
+    res["bytes_per_launch"] = res["fetch_bytes_per_launch"] + res["write_bytes_per_launch"]
+    return res
+
+
 def cpu_baseline(inp: dict, info, budget_core_s: float = 20.0) -> dict:
     """The oracle as it stands, on the host, on a bounded prefix of batches."""
     import numpy as np
@@ -169,8 +226,17 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run a plain 256 MiB device copy (counter calibration under rocprofv3)")
+                    help="also run a 256 MiB read + write elementwise kernel (counter calibration under rocprofv3)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_score_kernel_<workload>.json from two rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.summarize_counters:
+        res = summarize_counters(args.workload, *args.summarize_counters)
+        path = os.path.join(PROFILES, "traffic_score_kernel_%s.json" % args.workload)
+        with open(path, "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the indexer runs on a single MI355X here; "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -248,11 +314,11 @@ def main() -> int:
     warm_ms, _ = region(K, 3, rotate=False)  # context only: one copy, inputs may hit in the caches
 
     if args.calibrate_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        # counter calibration: one elementwise kernel that reads and writes 256 MiB each
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        src.fill_(1)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
 
     alg = algorithmic(info, p)
