@@ -179,7 +179,7 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str) -> dict:
     return res
 
 
-def cpu_baseline(inp: dict, info, budget_core_s: float = 20.0) -> dict:
+def cpu_baseline(inp: dict, info, budget_core_s: float = 20.0, min_wall_s: float = 10.0) -> dict:
     """The oracle as it stands, on the host, on a bounded prefix of batches."""
     import numpy as np
     import oracle
@@ -208,14 +208,19 @@ def cpu_baseline(inp: dict, info, budget_core_s: float = 20.0) -> dict:
     sub["problem"] = p
     vis = ora.row_visible(p["layout_query"], p["batch"], p["s1"], p["sparse_mode"], p["cmp_ratio"],
                           sub["aslq"], sub["aslk"])
-    t0 = time.perf_counter()
-    rc, _, _, _ = ora.indexer(sub, nthreads=threads)
-    dt = time.perf_counter() - t0
-    assert rc == 0
+    passes, t0 = 0, time.perf_counter()
+    while True:  # whole passes until about min_wall_s have elapsed
+        rc, _, _, _ = ora.indexer(sub, nthreads=threads)
+        assert rc == 0
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_wall_s:
+            break
     pairs = int(vis.sum())
-    return {"value": pairs / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
-            "sample": "batches 0..%d of %d (%d rows, %d visible pairs), one full oracle pass "
-                      "(fp64 scores, exact dots, stable top-k), %.2f s wall" % (nb - 1, B, vis.size, pairs, dt)}
+    return {"value": pairs * passes / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
+            "sample": "batches 0..%d of %d (%d rows, %d visible pairs), %d full oracle pass(es) "
+                      "(fp64 scores, exact dots, stable top-k), %.2f s wall"
+                      % (nb - 1, B, vis.size, pairs, passes, dt)}
 
 
 def main() -> int:
@@ -332,7 +337,7 @@ def main() -> int:
         achieved = alg["score_kernel"] / (score_avg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["kernel"] = "score_kernel"
+    roof["kernel"] = "score_kernel" if prefill else "score_decode_kernel"
     roof["kernel_ms"] = round(score_avg, 5)
     roof["algorithmic_bytes" if not prefill else "algorithmic_ops"] = alg["score_kernel"] if not prefill else alg["ops"]
     roof["traffic"] = traffic_from_profiles(args.workload)
