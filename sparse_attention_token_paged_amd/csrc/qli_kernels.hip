@@ -29,8 +29,12 @@
 //   selected entries written in ascending index order.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
+#include <utility>
+#include <vector>
 
 #include "qli_internal.h"
 
@@ -44,7 +48,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kScoreThreads = 256;
 
 struct ScoreParams {
-  const Item* items;      // the plan's item table (one item per workgroup)
+  const Item* items;      // the plan's item table
+  int32_t n_items;
   const RowInfo* rinfo;   // the plan's row table
   const uint8_t* query;
   const uint8_t* key;
@@ -101,6 +106,29 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Sum over the four lane groups of per-lane partials, scattered so that lane
+// (q, c) ends with the total of partial q: lane q*16 + c holds key q*16 + c
+// of the 64-key tile (two permlane steps).
+__device__ __forceinline__ float reduce_scatter4(float a0, float a1, float a2, float a3) {
+  // halves: the lower 32 lanes keep partials 0/1, the upper 32 keep 2/3
+  auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a2), false, false);
+  auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(a1), __float_as_uint(a3), false, false);
+  const float s02 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  const float s13 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+  // rows of 16: even rows keep the 0/2 partial, odd rows the 1/3 partial
+  auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
+// The same for two partials: lanes of rows 0 and 1 end with the total of a0,
+// rows 2 and 3 with the total of a1 (for key c of the respective n-tile).
+__device__ __forceinline__ float reduce_scatter2(float a0, float a1) {
+  auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
+  const float s = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
 // One 32-byte operand fragment: for int8 the two halves feed two K=64
 // MFMAs (dims [0,64) and [64,128)); for fp8 they form the v8i32 of one K=128
 // MFMA.  Lane l covers matrix row/column l%16 and lane group q = l/16.
@@ -117,12 +145,35 @@ __device__ __forceinline__ int chunk_lo(int q) { return QK == QLI_QK_INT8 ? q : 
 template <int QK>
 __device__ __forceinline__ int chunk_hi(int q) { return QK == QLI_QK_INT8 ? q + 4 : 2 * q + 1; }
 
+// w'[4m + i] = W * ScaleQ for heads 16m + 4q + i of row r (i = 0..3 are
+// consecutive, so one 8- or 16-byte load per tensor and m).
+template <int QK>
+__device__ __forceinline__ void load_wq(const ScoreParams& P, int64_t r, int q, float (&wq)[16]) {
+  const int64_t e0 = r * kHeads + 4 * q;
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    if constexpr (QK == QLI_QK_INT8) {
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      const h4 w = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.weights) + e0 + 16 * m);
+      const h4 sq = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.q_scale) + e0 + 16 * m);
+#pragma unroll
+      for (int i = 0; i < 4; i++) wq[4 * m + i] = __builtin_fmaf((float)w[i], (float)sq[i], 0.f);
+    } else {
+      const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(P.weights) + e0 + 16 * m);
+      const float4 sq = *reinterpret_cast<const float4*>(static_cast<const float*>(P.q_scale) + e0 + 16 * m);
+      wq[4 * m + 0] = w.x * sq.x;
+      wq[4 * m + 1] = w.y * sq.y;
+      wq[4 * m + 2] = w.z * sq.z;
+      wq[4 * m + 3] = w.w * sq.w;
+    }
+  }
+}
+
 template <int QK, int RW, int WPR, bool DUMP>
 __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(RW == 1 ? 4 : 2)))
 void score_kernel(ScoreParams P) {
-  constexpr int NT = 4 / WPR;  // 16-key n-tiles per wave per 64-key tile
+  static_assert(WPR == 1, "each wave scores all four n-tiles of a tile");
   const RowInfo* rinfo = P.rinfo;
-  const Item it = P.items[blockIdx.x];
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kTileKeys * kDim];
   __shared__ float lds_sk[2][kTileKeys];
@@ -134,6 +185,17 @@ void score_kernel(ScoreParams P) {
   const int q = lane >> 4;
   const int c16 = lane & 15;
   const int k = P.k;
+
+  // Persistent workgroups: in round t, workgroup b takes item t*G + b (t
+  // even) or t*G + G-1-b (t odd) of the work-sorted item list, which
+  // balances the rounds.  Positions grow with t, so the first one past the
+  // end ends the loop.
+  const int G = gridDim.x;
+  auto pos_of = [&](int t) { return t * G + ((t & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x); };
+  for (int round = 0;; round++) {
+  const int pos = pos_of(round);
+  if (pos >= P.n_items) break;  // uniform
+  const Item it = P.items[pos];
 
   // Rows that see fewer than k entries: slots vis..k-1 are -1 / -inf.
   if (it.flags & kItemPad) {
@@ -147,7 +209,7 @@ void score_kernel(ScoreParams P) {
       }
     }
   }
-  if (it.nkeys <= 0) return;  // uniform across the workgroup
+  if (it.nkeys <= 0) continue;  // uniform across the workgroup
 
   const int bs = P.block_size;
   const int key0 = it.key0;
@@ -183,12 +245,8 @@ void score_kernel(ScoreParams P) {
       const uint8_t* qh = qrow + (16 * m + c16) * kDim;
       qa[rr][m].lo = *reinterpret_cast<const v4i*>(qh + 16 * chunk_lo<QK>(q));
       qa[rr][m].hi = *reinterpret_cast<const v4i*>(qh + 16 * chunk_hi<QK>(q));
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int64_t e = r * kHeads + 16 * m + 4 * q + i;
-        wq[rr][4 * m + i] = load_scale<QK>(P.weights, e) * load_scale<QK>(P.q_scale, e);
-      }
     }
+    load_wq<QK>(P, r, q, wq[rr]);
   }
 
   // Loader: thread tid fetches two 16-byte pieces of each 64-key tile, at LDS
@@ -252,21 +310,24 @@ void score_kernel(ScoreParams P) {
     if (tid < kTileKeys) lds_sk[s][tid] = scale_from_bits<QK>(skr[S]);
   };
 
+  // One 64-key tile: for each n-tile the B fragment is read once and feeds
+  // both rows; each row's four n-tile partials are combined with one
+  // reduce_scatter4, after which lane l holds key tb + l.  Direct-output rows
+  // store 64 consecutive slots per tile with no divergent branch (keys past
+  // the row's visible count get the padding values).
   auto compute = [&](int t, int s) __attribute__((always_inline)) {
     const int tb = key0 + t * kTileKeys;
+    float part[RW][4];
 #pragma unroll
-    for (int n = 0; n < NT; n++) {
-      const int kk = (wk * NT + n) * 16 + c16;
+    for (int n = 0; n < 4; n++) {
+      const int kk = n * 16 + c16;
       const uint8_t* krow = &lds_k[s][kk * kDim];
       const int sw = (kk >> 1) & 7;
       Frag b;
       b.lo = *reinterpret_cast<const v4i*>(krow + ((chunk_lo<QK>(q) ^ sw) << 4));
       b.hi = *reinterpret_cast<const v4i*>(krow + ((chunk_hi<QK>(q) ^ sw) << 4));
-      const float skv = lds_sk[s][kk];
-      const int j = tb + kk;
 #pragma unroll
       for (int rr = 0; rr < RW; rr++) {
-        if (!rok[rr]) break;  // valid rows of a wave are a prefix
         float acc = 0.f;
         v4i di[4];
         v4f df[4];
@@ -297,33 +358,42 @@ void score_kernel(ScoreParams P) {
             for (int i = 0; i < 4; i++)
               acc = __builtin_fmaf(wq[rr][4 * m + i], __builtin_fmaxf(df[m][i], 0.f), acc);
         }
-        acc = sum_lane_groups(acc);
-        const float score = acc * skv;
-        const int64_t r = rowid[rr];
-        if (q == 0 && j < rvis[rr]) {
-          if (rws[rr] >= 0) {
-            P.ws[rws[rr] + j] = score;
-          } else {
-            P.idx_out[r * k + j] = j;
-            if (P.val_out) P.val_out[r * k + j] = score;
-          }
-        }
+        part[rr][n] = acc;
         if constexpr (DUMP) {
-          if (r >= P.d_row0 && r < P.d_row1 && j < rvis[rr] && j < P.d_cols) {
+          const int64_t r = rowid[rr];
+          const int jd = tb + kk;
+          if (rok[rr] && r >= P.d_row0 && r < P.d_row1 && jd < rvis[rr] && jd < P.d_cols) {
             const int64_t base = (r - P.d_row0) * kHeads;
 #pragma unroll
             for (int m = 0; m < 4; m++)
 #pragma unroll
               for (int i = 0; i < 4; i++) {
-                const int64_t o = (base + 16 * m + 4 * q + i) * P.d_cols + j;
+                const int64_t o = (base + 16 * m + 4 * q + i) * P.d_cols + jd;
                 if constexpr (QK == QLI_QK_INT8)
                   static_cast<int32_t*>(P.dots)[o] = di[m][i];
                 else
                   static_cast<float*>(P.dots)[o] = df[m][i];
               }
-            if (q == 0) P.dscores[(r - P.d_row0) * P.d_cols + j] = score;
           }
         }
+      }
+    }
+    const int j = tb + lane;
+    const float skv = lds_sk[s][lane];
+#pragma unroll
+    for (int rr = 0; rr < RW; rr++) {
+      const float score = reduce_scatter4(part[rr][0], part[rr][1], part[rr][2], part[rr][3]) * skv;
+      if (!rok[rr]) break;  // uniform: valid rows of a wave are a prefix
+      const int64_t r = rowid[rr];
+      const bool live = j < rvis[rr];
+      if (rws[rr] >= 0) {  // uniform: the row stages every score for a selection
+        if (live) P.ws[rws[rr] + j] = score;
+      } else if (j < kend && j < k) {  // a row's k slots only
+        P.idx_out[r * k + j] = live ? j : -1;
+        if (P.val_out) P.val_out[r * k + j] = live ? score : -INFINITY;
+      }
+      if constexpr (DUMP) {
+        if (live && r >= P.d_row0 && r < P.d_row1 && j < P.d_cols) P.dscores[(r - P.d_row0) * P.d_cols + j] = score;
       }
     }
   };
@@ -349,34 +419,12 @@ void score_kernel(ScoreParams P) {
     step(t, Set1{});
     if (t + 1 < ntiles) step(t + 1, Set0{});
   }
+  }  // rounds (the last tile's barrier leaves the LDS free for the next item)
 }
 
 // ---------------------------------------------------------------------------
 // Shared pieces: lane-group reductions, order keys, LDS-DMA, block selection
 // ---------------------------------------------------------------------------
-
-// Sum over the four lane groups of per-lane partials, scattered so that lane
-// (q, c) ends with the total of partial q: lane q*16 + c holds key q*16 + c
-// of the 64-key tile (two permlane steps).
-__device__ __forceinline__ float reduce_scatter4(float a0, float a1, float a2, float a3) {
-  // halves: the lower 32 lanes keep partials 0/1, the upper 32 keep 2/3
-  auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a2), false, false);
-  auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(a1), __float_as_uint(a3), false, false);
-  const float s02 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-  const float s13 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-  // rows of 16: even rows keep the 0/2 partial, odd rows the 1/3 partial
-  auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
-  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
-}
-
-// The same for two partials: lanes of rows 0 and 1 end with the total of a0,
-// rows 2 and 3 with the total of a1 (for key c of the respective n-tile).
-__device__ __forceinline__ float reduce_scatter2(float a0, float a1) {
-  auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
-  const float s = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-  auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
-}
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -518,23 +566,49 @@ __device__ __forceinline__ void block_scan2(int x, int y, int& xb, int& yb, int&
   }
 }
 
-// Top-k (k <= n) of the scores src[0, n); emit(pos, e, value) for each winner
-// e with pos its rank in position order.  hist: 2 x 2048 ints.  All NT threads.
-template <int NT, typename Emit>
+// Float4 groups per thread when n scores are split over NT threads: a power
+// of two, so thread t owns positions [4*R*t, 4*R*t + 4*R).
+template <int NT>
+__device__ __forceinline__ int sel_groups(int n) {
+  const int g = (n + 4 * NT - 1) / (4 * NT);
+  return g <= 1 ? 1 : 1 << (32 - __clz(g - 1));
+}
+
+// Position e of a selection over n scores in the transposed layout: float4
+// group q of thread t sits at float4 index q * NT + t, so the lanes of a wave
+// read consecutive 16-byte words (no LDS bank conflicts) while every thread
+// still owns a contiguous range of positions.
+template <int NT>
+__device__ __forceinline__ int sel_slot(int e, int rgroups) {
+  const int g = e >> 2;
+  const int t = g / rgroups, q = g - t * rgroups;  // rgroups is a power of two
+  return ((q * NT + t) << 2) | (e & 3);
+}
+
+// Top-k (k <= n) of the scores at src; emit(pos, e, value) for each winner e
+// with pos its rank in position order.  TR: src holds the scores in the
+// transposed layout (sel_slot), else in position order.  hist: 2 x 2048
+// ints.  All NT threads.
+template <int NT, bool TR, typename Emit>
 __device__ __forceinline__ void select_topk(const float* src, int n, int k, int* hist, SelShared& sh,
                                             Emit&& emit) {
   constexpr int NW = NT / 64;
   constexpr int BPT = 2048 / NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int S = (((n + NT - 1) / NT) + 3) & ~3;
+  const int R = sel_groups<NT>(n);
+  const int S = 4 * R;
   const int beg = min(n, tid * S), end = min(n, beg + S);
-  const float* mine = src + beg;
   const int cnt = end - beg;
+  // float4 group j / 4 of this thread
+  auto group = [&](int j) __attribute__((always_inline)) {
+    return TR ? *reinterpret_cast<const float4*>(src + 4 * ((j >> 2) * NT + tid))
+              : *reinterpret_cast<const float4*>(src + beg + j);
+  };
 
   uint32_t a = 0xFFFFFFFFu, o = 0u;
-#pragma unroll 1
+#pragma unroll 4
   for (int j = 0; j < cnt; j += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(mine + j);
+    const float4 v = group(j);
     const uint32_t q[4] = {order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w)};
 #pragma unroll
     for (int c = 0; c < 4; c++) {
@@ -571,9 +645,9 @@ __device__ __forceinline__ void select_topk(const float* src, int n, int k, int*
     const int shift = lo - width;
     const int nb = 1 << width;
     int* H = hist + (p & 1) * 2048;
-#pragma unroll 1
+#pragma unroll 4
     for (int j = 0; j < cnt; j += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(mine + j);
+      const float4 v = group(j);
       const uint32_t q[4] = {order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w)};
 #pragma unroll
       for (int c = 0; c < 4; c++)
@@ -619,9 +693,9 @@ __device__ __forceinline__ void select_topk(const float* src, int n, int k, int*
   }
 
   int g = 0, q = 0;
-#pragma unroll 1
+#pragma unroll 4
   for (int j = 0; j < cnt; j += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(mine + j);
+    const float4 v = group(j);
     const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int c = 0; c < 4; c++) {
@@ -632,9 +706,9 @@ __device__ __forceinline__ void select_topk(const float* src, int n, int k, int*
   }
   int G, E, gt_total, eq_total;
   block_scan2<NT>(g, q, G, E, gt_total, eq_total, sh);
-#pragma unroll 1
+#pragma unroll 4
   for (int j = 0; j < cnt; j += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(mine + j);
+    const float4 v = group(j);
     const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int c = 0; c < 4; c++) {
@@ -785,6 +859,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   int32_t* oi = P.idx_out + r * k;
   float* ov = P.val_out ? P.val_out + r * k : nullptr;
   const bool direct = rvis <= k;
+  // LOCAL: this row's scores of the chunk, in the selection's transposed layout
+  const int lrg = LOCAL ? sel_groups<kScoreThreads>(max(1, min(it.nkeys, rvis - key0))) : 1;
 
   // Scores of 64 entries (4 n-tiles) or 32 entries (2 n-tiles) of the stage.
   auto score_group = [&](int slot_, int st, int n0, auto nt_) __attribute__((always_inline)) {
@@ -864,7 +940,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
         oi[j] = j;
         if (ov) ov[j] = score;
       } else if constexpr (LOCAL) {
-        lds_scores[u][e] = score;
+        lds_scores[u][sel_slot<kScoreThreads>(e, lrg)] = score;
       } else {
         P.ws[coff + e] = score;
       }
@@ -915,12 +991,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
       if (n <= 0) continue;
       const float* sc = lds_scores[uu];
       if (n <= k) {
+        const int rg = sel_groups<kScoreThreads>(n);
         for (int e = tid; e < n; e += kScoreThreads) {
-          P.ws[off + e] = sc[e];
+          P.ws[off + e] = sc[sel_slot<kScoreThreads>(e, rg)];
           ws_idx[off + e] = key0 + e;
         }
       } else {
-        select_topk<kScoreThreads>(sc, n, k, hist, sel, [&](int pos, int e, float v) __attribute__((always_inline)) {
+        select_topk<kScoreThreads, true>(sc, n, k, hist, sel, [&](int pos, int e, float v) __attribute__((always_inline)) {
           P.ws[off + pos] = v;
           ws_idx[off + pos] = key0 + e;
         });
@@ -968,24 +1045,44 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams S) {
     // row's 16-byte padded region), then the stores
     constexpr int STEP = kSelThreads * 4;
     const int last = ((n + 3) & ~3) - 4;
+    const int rg = sel_groups<kSelThreads>(n);
     float4 v[kSelLdsCap / STEP];
 #pragma unroll
     for (int i = 0; i < kSelLdsCap / STEP; i++)
       v[i] = *reinterpret_cast<const float4*>(sc + min(i * STEP + tid * 4, last));
 #pragma unroll
     for (int i = 0; i < kSelLdsCap / STEP; i++) {
-      const int e = i * STEP + tid * 4;
-      if (e < n) *reinterpret_cast<float4*>(&cache[e]) = v[i];
+      const int e = i * STEP + tid * 4;  // stored in the transposed layout
+      if (e < n) *reinterpret_cast<float4*>(&cache[sel_slot<kSelThreads>(e, rg)]) = v[i];
     }
     __syncthreads();
   }
   int32_t* oi = S.idx_out + (int64_t)se.row * k;
   float* ov = S.val_out ? S.val_out + (int64_t)se.row * k : nullptr;
-  select_topk<kSelThreads>(LDS ? cache : sc, n, k, hist, sh,
+  select_topk<kSelThreads, LDS>(LDS ? cache : sc, n, k, hist, sh,
                            [&](int pos, int e, float v) __attribute__((always_inline)) {
                              oi[pos] = INDEXED ? ix[e] : e;
                              if (ov) ov[pos] = v;
                            });
+}
+
+// Workgroups of `kernel` that the current device holds at once (all CUs),
+// cached per device and kernel; 0 if it cannot be determined.
+int resident_slots(const void* kernel, int threads) {
+  static std::mutex mu;
+  static std::vector<std::pair<std::pair<int, const void*>, int>> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& e : cache)
+    if (e.first.first == dev && e.first.second == kernel) return e.second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+    return 0;
+  const int slots = cus * per_cu;
+  cache.push_back({{dev, kernel}, slots});
+  return slots;
 }
 
 template <typename... Args>
@@ -1009,7 +1106,9 @@ hipError_t launch_score_t(const ScoreParams& P, const PlanHeader* h, hipStream_t
     }
   }
   if (h->rows_per_item != 8) return hipErrorInvalidValue;
-  return launch(score_kernel<QK, 2, 1, DUMP>, grid, block, st, P);
+  const int slots = resident_slots(reinterpret_cast<const void*>(score_kernel<QK, 2, 1, DUMP>), kScoreThreads);
+  const dim3 pgrid(slots > 0 ? std::min<int>(h->n_items, slots) : h->n_items);
+  return launch(score_kernel<QK, 2, 1, DUMP>, pgrid, block, st, P);
 }
 
 }  // namespace
@@ -1020,6 +1119,7 @@ int launch_score(const RunArgs& a, bool dump) {
   ScoreParams P{};
   P.items = reinterpret_cast<const Item*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_items);
   P.rinfo = reinterpret_cast<const RowInfo*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_rows);
+  P.n_items = h->n_items;
   P.query = static_cast<const uint8_t*>(a.query);
   P.key = static_cast<const uint8_t*>(a.key);
   P.weights = a.weights;
