@@ -181,12 +181,12 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   // tiles and write dense scores.  Decode items stream their chunk through
   // LDS; when there is enough work for chunks of at least 4k entries (and
   // k <= 1024), each item keeps only its chunk's top-k candidates, which cuts
-  // the final selection's input by 4x or more.  Otherwise chunks are
-  // kDenseChunk entries and every score is staged.
+  // the final selection's input by 4x or more.  Otherwise every score is
+  // staged, in chunks balanced over the resident workgroups (below).
   int64_t key_work = 0;
   for (const Group& g : groups) key_work += g.maxv;
   const int k = p.sparse_count;
-  int chunk = prefill ? kMaxChunk : kDenseChunk;
+  int chunk = kMaxChunk;  // prefill; decode chunks are set below
   bool local = false;
   if (!prefill && rt <= 2 && k <= 1024) {
     int c = 1024;
@@ -195,6 +195,20 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
       chunk = c;
       local = true;
     }
+  }
+
+  // Dense decode chunks: the smallest multiple of 128 entries for which the
+  // items fit the dense decode kernel's resident workgroups on one MI355X
+  // (256 CUs x 3) in a single round.
+  if (!prefill && !local) {
+    auto items_for = [&](int c) {
+      int64_t n = 0;
+      for (const Group& g : groups) n += (g.maxv + c - 1) / c;
+      return n;
+    };
+    int c = 128;
+    while (c < kMaxChunk && items_for(c) > kDecodeSlots) c += 128;
+    chunk = c;
   }
 
   // Per-row candidate counts and workspace offsets.  A row that sees more
@@ -264,9 +278,9 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
       out.items.push_back(it);
     }
   }
-  if (prefill)  // longest items first
-    std::stable_sort(out.items.begin(), out.items.end(),
-                     [](const Item& a, const Item& b) { return a.nkeys * a.nrows > b.nkeys * b.nrows; });
+  // Longest items first: the kernels hand them out in snake order.
+  std::stable_sort(out.items.begin(), out.items.end(),
+                   [](const Item& a, const Item& b) { return a.nkeys * a.nrows > b.nkeys * b.nrows; });
   if (out.items.size() > (size_t)INT32_MAX) return QLI_ERR_SIZE;
 
   PlanHeader& h = out.hdr;

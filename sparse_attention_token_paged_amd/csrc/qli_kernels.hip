@@ -746,9 +746,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   constexpr int SB = QK == QLI_QK_INT8 ? 2 : 4;
   constexpr int LCAP = LOCAL ? kMaxChunk / RT : 1;
 
-  // read in place: the per-row fields are indexed by a wave-uniform row
-  const Item& it = P.items[blockIdx.x];
-
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSTAGE][SC * kDim];
   __shared__ uint32_t ring_sk[NSTAGE][SC];   // ScaleK bits, one 4-byte slot per entry
   __shared__ int32_t lds_bt[kMaxChunk / 16 + 2];
@@ -762,6 +759,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   const int c16 = lane & 15;
   const int k = P.k;
 
+  // Persistent workgroups over the work-sorted items, in snake order: round t
+  // takes item t*G + b (t even) or t*G + G-1-b (t odd).
+  const int G = gridDim.x;
+  for (int round = 0;; round++) {
+  const int pos = round * G + ((round & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+  if (pos >= P.n_items) break;  // uniform; positions grow with the round
+  // read in place: the per-row fields are indexed by a wave-uniform row
+  const Item& it = P.items[pos];
+
   // Rows that see fewer than k entries: slots vis..k-1 are -1 / -inf.
   if (it.flags & kItemPad) {
     for (int u = 0; u < it.nrows; u++) {
@@ -774,7 +780,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
       }
     }
   }
-  if (it.nkeys <= 0) return;  // uniform across the workgroup
+  if (it.nkeys <= 0) continue;  // uniform across the workgroup
 
   const int bs = P.block_size;
   const int key0 = it.key0;
@@ -1005,6 +1011,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
       }
     }
   }
+  }  // rounds (the item's last barrier leaves the LDS free for the next one)
 }
 
 // ---------------------------------------------------------------------------
@@ -1096,12 +1103,17 @@ hipError_t launch_score_t(const ScoreParams& P, const PlanHeader* h, hipStream_t
   const dim3 grid(h->n_items), block(kScoreThreads);
   if (h->kind == kKindDecode) {
     const bool local = h->local_select != 0;
+    auto go = [&](void (*kern)(ScoreParams)) {
+      const int slots = resident_slots(reinterpret_cast<const void*>(kern), kScoreThreads);
+      const dim3 pgrid(slots > 0 ? std::min<int>(h->n_items, slots) : h->n_items);
+      return launch(kern, pgrid, block, st, P);
+    };
     switch (h->rows_per_item * 2 + (local ? 1 : 0)) {
-      case 2: return launch(score_decode_kernel<QK, 1, false, DUMP>, grid, block, st, P);
-      case 3: return launch(score_decode_kernel<QK, 1, true, DUMP>, grid, block, st, P);
-      case 4: return launch(score_decode_kernel<QK, 2, false, DUMP>, grid, block, st, P);
-      case 5: return launch(score_decode_kernel<QK, 2, true, DUMP>, grid, block, st, P);
-      case 8: return launch(score_decode_kernel<QK, 4, false, DUMP>, grid, block, st, P);
+      case 2: return go(score_decode_kernel<QK, 1, false, DUMP>);
+      case 3: return go(score_decode_kernel<QK, 1, true, DUMP>);
+      case 4: return go(score_decode_kernel<QK, 2, false, DUMP>);
+      case 5: return go(score_decode_kernel<QK, 2, true, DUMP>);
+      case 8: return go(score_decode_kernel<QK, 4, false, DUMP>);
       default: return hipErrorInvalidValue;
     }
   }
