@@ -585,12 +585,13 @@ __device__ __forceinline__ int sel_slot(int e, int rgroups) {
   return ((q * NT + t) << 2) | (e & 3);
 }
 
-// Top-k (k <= n) of the scores at src; emit(pos, e, value) for each winner e
-// with pos its rank in position order.  TR: src holds the scores in the
-// transposed layout (sel_slot), else in position order.  hist: 2 x 2048
-// ints.  All NT threads.
+// Top-k (k <= n) of n scores; emit(pos, e, value) for each winner e with pos
+// its rank in position order.  TR: src holds the order keys of the scores
+// (order_key) in the transposed layout (sel_slot), typically in LDS; else
+// src holds the fp32 scores in position order.  hist: 2 x 2048 ints.  All
+// NT threads.
 template <int NT, bool TR, typename Emit>
-__device__ __forceinline__ void select_topk(const float* src, int n, int k, int* hist, SelShared& sh,
+__device__ __forceinline__ void select_topk(const void* src, int n, int k, int* hist, SelShared& sh,
                                             Emit&& emit) {
   constexpr int NW = NT / 64;
   constexpr int BPT = 2048 / NT;
@@ -599,17 +600,21 @@ __device__ __forceinline__ void select_topk(const float* src, int n, int k, int*
   const int S = 4 * R;
   const int beg = min(n, tid * S), end = min(n, beg + S);
   const int cnt = end - beg;
-  // float4 group j / 4 of this thread
+  // keys of the four positions beg + j .. beg + j + 3 of this thread
   auto group = [&](int j) __attribute__((always_inline)) {
-    return TR ? *reinterpret_cast<const float4*>(src + 4 * ((j >> 2) * NT + tid))
-              : *reinterpret_cast<const float4*>(src + beg + j);
+    if constexpr (TR) {
+      return *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(src) + 4 * ((j >> 2) * NT + tid));
+    } else {
+      const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + beg + j);
+      return make_uint4(order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w));
+    }
   };
 
   uint32_t a = 0xFFFFFFFFu, o = 0u;
 #pragma unroll 4
   for (int j = 0; j < cnt; j += 4) {
-    const float4 v = group(j);
-    const uint32_t q[4] = {order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w)};
+    const uint4 v = group(j);
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int c = 0; c < 4; c++) {
       a &= j + c < cnt ? q[c] : 0xFFFFFFFFu;
@@ -647,8 +652,8 @@ __device__ __forceinline__ void select_topk(const float* src, int n, int k, int*
     int* H = hist + (p & 1) * 2048;
 #pragma unroll 4
     for (int j = 0; j < cnt; j += 4) {
-      const float4 v = group(j);
-      const uint32_t q[4] = {order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w)};
+      const uint4 v = group(j);
+      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int c = 0; c < 4; c++)
         if (j + c < cnt && (q[c] & mask) == prefix) atomicAdd(&H[(q[c] >> shift) & (nb - 1)], 1);
@@ -695,11 +700,11 @@ __device__ __forceinline__ void select_topk(const float* src, int n, int k, int*
   int g = 0, q = 0;
 #pragma unroll 4
   for (int j = 0; j < cnt; j += 4) {
-    const float4 v = group(j);
-    const float f[4] = {v.x, v.y, v.z, v.w};
+    const uint4 v = group(j);
+    const uint32_t f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-      const uint32_t m = order_key(f[c]) & mask;
+      const uint32_t m = f[c] & mask;
       g += (j + c < cnt && m > prefix) ? 1 : 0;
       q += (j + c < cnt && m == prefix) ? 1 : 0;
     }
@@ -708,15 +713,15 @@ __device__ __forceinline__ void select_topk(const float* src, int n, int k, int*
   block_scan2<NT>(g, q, G, E, gt_total, eq_total, sh);
 #pragma unroll 4
   for (int j = 0; j < cnt; j += 4) {
-    const float4 v = group(j);
-    const float f[4] = {v.x, v.y, v.z, v.w};
+    const uint4 v = group(j);
+    const uint32_t f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-      const uint32_t m = order_key(f[c]) & mask;
+      const uint32_t m = f[c] & mask;
       const bool live = j + c < cnt;
       const bool gt = live && m > prefix;
       const bool eq = live && m == prefix;
-      if (gt || (eq && E < kk)) emit(G + min(E, kk), beg + j + c, f[c]);
+      if (gt || (eq && E < kk)) emit(G + min(E, kk), beg + j + c, key_value(f[c]));
       G += gt ? 1 : 0;
       E += eq ? 1 : 0;
     }
@@ -749,7 +754,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSTAGE][SC * kDim];
   __shared__ uint32_t ring_sk[NSTAGE][SC];   // ScaleK bits, one 4-byte slot per entry
   __shared__ int32_t lds_bt[kMaxChunk / 16 + 2];
-  __shared__ __attribute__((aligned(16))) float lds_scores[RT][LCAP];  // LOCAL: the chunk's scores of each row
+  __shared__ __attribute__((aligned(16))) uint32_t lds_keys[RT][LCAP];  // LOCAL: order keys of the chunk's scores per row
   __shared__ SelShared sel;
 
   const int tid = threadIdx.x;
@@ -946,7 +951,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
         oi[j] = j;
         if (ov) ov[j] = score;
       } else if constexpr (LOCAL) {
-        lds_scores[u][sel_slot<kScoreThreads>(e, lrg)] = score;
+        lds_keys[u][sel_slot<kScoreThreads>(e, lrg)] = order_key(score);
       } else {
         P.ws[coff + e] = score;
       }
@@ -995,15 +1000,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
       if (vis <= k || off < 0) continue;  // uniform
       const int n = min(it.nkeys, vis - key0);
       if (n <= 0) continue;
-      const float* sc = lds_scores[uu];
+      const uint32_t* sk = lds_keys[uu];
       if (n <= k) {
         const int rg = sel_groups<kScoreThreads>(n);
         for (int e = tid; e < n; e += kScoreThreads) {
-          P.ws[off + e] = sc[sel_slot<kScoreThreads>(e, rg)];
+          P.ws[off + e] = key_value(sk[sel_slot<kScoreThreads>(e, rg)]);
           ws_idx[off + e] = key0 + e;
         }
       } else {
-        select_topk<kScoreThreads, true>(sc, n, k, hist, sel, [&](int pos, int e, float v) __attribute__((always_inline)) {
+        select_topk<kScoreThreads, true>(sk, n, k, hist, sel, [&](int pos, int e, float v) __attribute__((always_inline)) {
           P.ws[off + pos] = v;
           ws_idx[off + pos] = key0 + e;
         });
@@ -1019,7 +1024,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
 // k entries, over the row's staged candidates (in ascending index order).
 // ---------------------------------------------------------------------------
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 1024;  // 16 waves: the phases are latency-bound, more waves hide it
 
 struct SelectParams {
   const SelectEntry* rows;  // the plan's selection table
@@ -1036,11 +1041,11 @@ struct SelectParams {
 // key index.
 constexpr int kSelLdsCap = 32768;
 
-template <bool LDS, bool INDEXED>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams S) {
+template <int NT, bool LDS, bool INDEXED>
+__global__ __launch_bounds__(NT) void select_kernel(SelectParams S) {
   __shared__ int hist[2 * 2048];
   __shared__ SelShared sh;
-  __shared__ __attribute__((aligned(16))) float cache[LDS ? kSelLdsCap : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t cache[LDS ? kSelLdsCap : 4];
   const SelectEntry se = S.rows[blockIdx.x];
   const int n = se.ncand;
   const int k = S.k;
@@ -1048,29 +1053,33 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams S) {
   const int32_t* ix = S.ws_idx + se.ws_off;
   const int tid = threadIdx.x;
   if constexpr (LDS) {
-    // eight 16-byte loads in flight per thread (addresses clamped into the
-    // row's 16-byte padded region), then the stores
-    constexpr int STEP = kSelThreads * 4;
+    // Order keys in the transposed layout; eight 16-byte loads in flight per
+    // thread (addresses clamped into the row's 16-byte padded region).
+    constexpr int STEP = NT * 4;
     const int last = ((n + 3) & ~3) - 4;
-    const int rg = sel_groups<kSelThreads>(n);
-    float4 v[kSelLdsCap / STEP];
+    const int rg = sel_groups<NT>(n);
+    for (int base = 0; base < n; base += 8 * STEP) {
+      float4 v[8];
 #pragma unroll
-    for (int i = 0; i < kSelLdsCap / STEP; i++)
-      v[i] = *reinterpret_cast<const float4*>(sc + min(i * STEP + tid * 4, last));
+      for (int i = 0; i < 8; i++)
+        v[i] = *reinterpret_cast<const float4*>(sc + min(base + i * STEP + tid * 4, last));
 #pragma unroll
-    for (int i = 0; i < kSelLdsCap / STEP; i++) {
-      const int e = i * STEP + tid * 4;  // stored in the transposed layout
-      if (e < n) *reinterpret_cast<float4*>(&cache[sel_slot<kSelThreads>(e, rg)]) = v[i];
+      for (int i = 0; i < 8; i++) {
+        const int e = base + i * STEP + tid * 4;
+        if (e < n)
+          *reinterpret_cast<uint4*>(&cache[sel_slot<NT>(e, rg)]) =
+              make_uint4(order_key(v[i].x), order_key(v[i].y), order_key(v[i].z), order_key(v[i].w));
+      }
     }
     __syncthreads();
   }
   int32_t* oi = S.idx_out + (int64_t)se.row * k;
   float* ov = S.val_out ? S.val_out + (int64_t)se.row * k : nullptr;
-  select_topk<kSelThreads, LDS>(LDS ? cache : sc, n, k, hist, sh,
-                           [&](int pos, int e, float v) __attribute__((always_inline)) {
-                             oi[pos] = INDEXED ? ix[e] : e;
-                             if (ov) ov[pos] = v;
-                           });
+  select_topk<NT, LDS>(LDS ? static_cast<const void*>(cache) : static_cast<const void*>(sc), n, k, hist, sh,
+                       [&](int pos, int e, float v) __attribute__((always_inline)) {
+                         oi[pos] = INDEXED ? ix[e] : e;
+                         if (ov) ov[pos] = v;
+                       });
 }
 
 // Workgroups of `kernel` that the current device holds at once (all CUs),
@@ -1178,10 +1187,10 @@ int launch_select(const RunArgs& a) {
   const hipStream_t st = static_cast<hipStream_t>(a.stream);
   const bool lds = h->max_cand <= kSelLdsCap;
   const hipError_t e = h->local_select
-                           ? (lds ? launch(select_kernel<true, true>, grid, block, st, S)
-                                  : launch(select_kernel<false, true>, grid, block, st, S))
-                           : (lds ? launch(select_kernel<true, false>, grid, block, st, S)
-                                  : launch(select_kernel<false, false>, grid, block, st, S));
+                           ? (lds ? launch(select_kernel<kSelThreads, true, true>, grid, block, st, S)
+                                  : launch(select_kernel<kSelThreads, false, true>, grid, block, st, S))
+                           : (lds ? launch(select_kernel<kSelThreads, true, false>, grid, block, st, S)
+                                  : launch(select_kernel<kSelThreads, false, false>, grid, block, st, S));
   return e == hipSuccess ? 0 : (int)e;
 }
 
