@@ -278,9 +278,20 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
       out.items.push_back(it);
     }
   }
-  // Longest items first: the kernels hand them out in snake order.
-  std::stable_sort(out.items.begin(), out.items.end(),
-                   [](const Item& a, const Item& b) { return a.nkeys * a.nrows > b.nkeys * b.nrows; });
+  // Regular decode plans: every batch has the same query rows (one group) and
+  // the same visible maximum, so an item's batch, key range and rows follow
+  // from its position, and the kernel can start its block-table and query
+  // loads without waiting for the item.  They keep batch-major order.
+  bool regular = !prefill && p.layout_query == QLI_LAYOUT_BSND && p.batch > 0 && (int64_t)groups.size() == p.batch;
+  for (int b = 0; regular && b < p.batch; b++) {
+    const Group& g = groups[b];
+    regular = g.batch == b && g.nrows == p.s1 && g.row0 == (int64_t)b * p.s1 && g.maxv == groups[0].maxv &&
+              g.maxv > 0;
+  }
+  const int32_t reg_chunks = regular ? (groups[0].maxv + chunk - 1) / chunk : 0;
+  if (!regular)  // longest items first: the kernels hand them out in snake order
+    std::stable_sort(out.items.begin(), out.items.end(),
+                     [](const Item& a, const Item& b) { return a.nkeys * a.nrows > b.nkeys * b.nrows; });
   if (out.items.size() > (size_t)INT32_MAX) return QLI_ERR_SIZE;
 
   PlanHeader& h = out.hdr;
@@ -301,6 +312,9 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   h.chunk = chunk;
   h.max_vis = (int32_t)max_vis;
   h.max_cand = (int32_t)max_cand;
+  h.reg_chunks = reg_chunks;
+  h.reg_rows = regular ? p.s1 : 0;
+  h.reg_maxv = regular ? groups[0].maxv : 0;
   h.key_entries = key_entries;
   h.table_entries = table_entries;
   h.active_rows = active;

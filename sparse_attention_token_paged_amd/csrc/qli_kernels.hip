@@ -50,6 +50,8 @@ constexpr int kScoreThreads = 256;
 struct ScoreParams {
   const Item* items;      // the plan's item table
   int32_t n_items;
+  int32_t chunk;          // keys per item
+  int32_t reg_chunks, reg_rows, reg_maxv;  // regular decode plans (0: not regular)
   const RowInfo* rinfo;   // the plan's row table
   const uint8_t* query;
   const uint8_t* key;
@@ -774,26 +776,45 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   const Item& it = P.items[pos];
 
   // Rows that see fewer than k entries: slots vis..k-1 are -1 / -inf.
-  if (it.flags & kItemPad) {
-    for (int u = 0; u < it.nrows; u++) {
-      const int64_t r = it.row0 + u;
-      const int vis = it.vis[u];
-      if (vis >= k) continue;
-      for (int pos = vis + tid; pos < k; pos += kScoreThreads) {
-        P.idx_out[r * k + pos] = -1;
-        if (P.val_out) P.val_out[r * k + pos] = -INFINITY;
+  auto pad = [&]() __attribute__((always_inline)) {
+    if (it.flags & kItemPad) {
+      for (int u = 0; u < it.nrows; u++) {
+        const int64_t r = it.row0 + u;
+        const int vis = it.vis[u];
+        if (vis >= k) continue;
+        for (int pos = vis + tid; pos < k; pos += kScoreThreads) {
+          P.idx_out[r * k + pos] = -1;
+          if (P.val_out) P.val_out[r * k + pos] = -INFINITY;
+        }
       }
     }
+  };
+  // Regular plans: the item's batch, keys and rows follow from its position,
+  // so the block-table and query loads below need not wait for the item.
+  const bool reg = P.reg_chunks > 0;
+  int batch, key0, nkeys, row0, nrows;
+  if (reg) {
+    batch = pos / P.reg_chunks;
+    key0 = (pos - batch * P.reg_chunks) * P.chunk;
+    nkeys = min(P.chunk, P.reg_maxv - key0);
+    row0 = batch * P.reg_rows;
+    nrows = P.reg_rows;
+  } else {
+    pad();
+    batch = it.batch;
+    key0 = it.key0;
+    nkeys = it.nkeys;
+    row0 = it.row0;
+    nrows = it.nrows;
+    if (nkeys <= 0) continue;  // uniform across the workgroup
   }
-  if (it.nkeys <= 0) continue;  // uniform across the workgroup
 
   const int bs = P.block_size;
-  const int key0 = it.key0;
-  const int kend = key0 + it.nkeys;
+  const int kend = key0 + nkeys;
   const int fb = (int)__umulhi((uint32_t)key0, P.bs_magic);
   const int nblk = (int)__umulhi((uint32_t)(kend - 1), P.bs_magic) - fb + 1;
   {
-    const int32_t* bt = P.block_table + (int64_t)it.batch * P.max_blocks + fb;
+    const int32_t* bt = P.block_table + (int64_t)batch * P.max_blocks + fb;
     for (int t = tid; t < nblk; t += kScoreThreads) lds_bt[t] = bt[t];
   }
 
@@ -801,8 +822,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   // the barrier, so they share its round trip with the block table).
   const int u = wave / WPR;
   const int sub = wave % WPR;
-  const bool rok = u < it.nrows;
-  const int64_t r = it.row0 + (rok ? u : 0);
+  const bool rok = u < nrows;
+  const int64_t r = row0 + (rok ? u : 0);
   const int rvis = rok ? it.vis[u] : 0;
   const int64_t coff = rok ? it.cand_off[u] : -1;
   Frag qa[4];
@@ -840,7 +861,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   // Stage loader: wave w's load i fills stage bytes [(4i + w) * 1024, +1024),
   // lane l the 16 bytes at l*16: entry kk = 8(4i + w) + l/8, physical chunk
   // l%8 holding logical chunk (l%8) ^ ((kk>>1)&7) (conflict-free MFMA reads).
-  const int nstages = (it.nkeys + SC - 1) / SC;
+  const int nstages = (nkeys + SC - 1) / SC;
   auto issue = [&](int st) __attribute__((always_inline)) {
     const int slot_ = st % NSTAGE;
     const int e_base = key0 + st * SC;
@@ -871,7 +892,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   float* ov = P.val_out ? P.val_out + r * k : nullptr;
   const bool direct = rvis <= k;
   // LOCAL: this row's scores of the chunk, in the selection's transposed layout
-  const int lrg = LOCAL ? sel_groups<kScoreThreads>(max(1, min(it.nkeys, rvis - key0))) : 1;
+  const int lrg = LOCAL ? sel_groups<kScoreThreads>(max(1, min(nkeys, rvis - key0))) : 1;
 
   // Scores of 64 entries (4 n-tiles) or 32 entries (2 n-tiles) of the stage.
   auto score_group = [&](int slot_, int st, int n0, auto nt_) __attribute__((always_inline)) {
@@ -994,11 +1015,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     __syncthreads();
     int* hist = reinterpret_cast<int*>(&ring[0][0]);  // the ring is idle now
     int32_t* ws_idx = P.ws_idx;
-    for (int uu = 0; uu < it.nrows; uu++) {
+    for (int uu = 0; uu < nrows; uu++) {
       const int vis = it.vis[uu];
       const int64_t off = it.cand_off[uu];
       if (vis <= k || off < 0) continue;  // uniform
-      const int n = min(it.nkeys, vis - key0);
+      const int n = min(nkeys, vis - key0);
       if (n <= 0) continue;
       const uint32_t* sk = lds_keys[uu];
       if (n <= k) {
@@ -1016,6 +1037,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
       }
     }
   }
+  if (reg) pad();
   }  // rounds (the item's last barrier leaves the LDS free for the next one)
 }
 
@@ -1141,6 +1163,10 @@ int launch_score(const RunArgs& a, bool dump) {
   P.items = reinterpret_cast<const Item*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_items);
   P.rinfo = reinterpret_cast<const RowInfo*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_rows);
   P.n_items = h->n_items;
+  P.chunk = h->chunk;
+  P.reg_chunks = h->reg_chunks;
+  P.reg_rows = h->reg_rows;
+  P.reg_maxv = h->reg_maxv;
   P.query = static_cast<const uint8_t*>(a.query);
   P.key = static_cast<const uint8_t*>(a.key);
   P.weights = a.weights;

@@ -115,7 +115,8 @@ HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("fingerprint", "<u8"), ("
                 ("off_rows", "<i8"), ("off_items", "<i8"), ("off_select", "<i8"), ("kind", "<i4"),
                 ("rows_per_item", "<i4"), ("n_items", "<i4"), ("n_select", "<i4"), ("chunk", "<i4"),
                 ("max_vis", "<i4"), ("local_select", "<i4"), ("max_cand", "<i4"), ("key_entries", "<i8"),
-                ("table_entries", "<i8"), ("active_rows", "<i8"), ("ws_index_offset", "<i8")])
+                ("table_entries", "<i8"), ("active_rows", "<i8"), ("ws_index_offset", "<i8"),
+                ("reg_chunks", "<i4"), ("reg_rows", "<i4"), ("reg_maxv", "<i4"), ("reserved2", "<i4")])
 ROW = np.dtype([("batch", "<i4"), ("vis", "<i4"), ("ws_off", "<i8"), ("ncand", "<i4"), ("indexed", "<i4")])
 SEL = np.dtype([("ws_off", "<i8"), ("row", "<i4"), ("ncand", "<i4"), ("indexed", "<i4"), ("reserved", "<i4", 3)])
 ITEM = np.dtype([("row0", "<i4"), ("nrows", "<i4"), ("batch", "<i4"), ("key0", "<i4"), ("nkeys", "<i4"),
@@ -142,6 +143,8 @@ PLAN_CASES = [
     synth.small(layout=synth.TND, batch=0, s1=5, aslk=[], aslq=[]),
     synth.small(batch=16, s1=1, aslk=[70000 - 977 * i for i in range(16)], block_size=64, sparse_count=256),
     synth.small(batch=8, s1=2, aslk=[70000] * 8, block_size=32, sparse_count=256, sparse_mode=3),
+    synth.small(batch=5, s1=3, aslk=[3000] * 5, block_size=64, sparse_count=256, sparse_mode=3),
+    synth.small(batch=4, s1=1, aslk=[900] * 4, block_size=16, sparse_count=1000),
 ]
 
 
@@ -172,6 +175,15 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
                     cover[r][it["key0"]:hi] += 1
         assert it["nkeys"] <= h["chunk"] and (it["key0"] % 64 == 0)
     assert all(np.all(c == 1) for c in cover)
+    if h["reg_chunks"] > 0:
+        # regular decode plans: an item's batch, keys and rows follow from its position
+        rc_, chunk_, s1_, mv_ = int(h["reg_chunks"]), int(h["chunk"]), int(h["reg_rows"]), int(h["reg_maxv"])
+        assert h["kind"] == 0 and p["layout_query"] == 0 and s1_ == p["s1"] and len(items) == p["batch"] * rc_
+        for i, it in enumerate(items):
+            b, c = divmod(i, rc_)
+            assert it["batch"] == b and it["key0"] == c * chunk_ and it["nkeys"] == min(chunk_, mv_ - c * chunk_)
+            assert it["row0"] == b * s1_ and it["nrows"] == s1_
+            assert max(int(vis[r]) for r in range(b * s1_, (b + 1) * s1_)) == mv_
     assert np.all(padded == 1)
     k = p["sparse_count"]
     assert list(sel["row"]) == [r for r in range(nrows) if vis[r] > k]

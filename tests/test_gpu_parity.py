@@ -56,6 +56,9 @@ SMALL = {
                                       sparse_count=128, sparse_mode=3, stride_pad=16),
     "tnd_fp8_prefill": synth.small(qk=synth.FP8, layout=synth.TND, batch=2, s1=50, aslq=[20, 50],
                                    aslk=[400, 30], block_size=16, sparse_count=32, sparse_mode=3),
+    # every batch alike: items addressed from their position
+    "regular_causal_s3": synth.small(batch=5, s1=3, aslk=[3000] * 5, block_size=64, sparse_count=256, sparse_mode=3),
+    "regular_s1_fp8": synth.small(qk=synth.FP8, batch=4, s1=1, aslk=[900] * 4, block_size=16, sparse_count=300),
 }
 
 
