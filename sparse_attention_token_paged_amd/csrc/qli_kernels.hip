@@ -147,6 +147,12 @@ __device__ __forceinline__ int chunk_lo(int q) { return QK == QLI_QK_INT8 ? q : 
 template <int QK>
 __device__ __forceinline__ int chunk_hi(int q) { return QK == QLI_QK_INT8 ? q + 4 : 2 * q + 1; }
 
+// Workgroup barrier that orders LDS (waits for this wave's LDS accesses) but
+// leaves outstanding global loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // w'[4m + i] = W * ScaleQ for heads 16m + 4q + i of row r (i = 0..3 are
 // consecutive, so one 8- or 16-byte load per tensor and m).
 template <int QK>
@@ -274,7 +280,7 @@ void score_kernel(ScoreParams P) {
   }
   int4 kr[2][2];
   uint32_t skr[2] = {0u, 0u};
-  __syncthreads();  // lds_blk is ready
+  lds_barrier();  // lds_blk is ready; the row loads above stay in flight
 
   auto fetch = [&](int t, auto set_) __attribute__((always_inline)) {
     constexpr int S = decltype(set_)::value;
@@ -409,13 +415,13 @@ void score_kernel(ScoreParams P) {
   if (ntiles > 1) fetch(1, Set1{});
   stash(0, Set0{});
   if (ntiles > 2) fetch(2, Set0{});
-  __syncthreads();
+  lds_barrier();
   auto step = [&](int t, auto set_next) __attribute__((always_inline)) {
     // set_next holds tile t+1; after its stash it receives tile t+3
     compute(t, t & 1);
     if (t + 1 < ntiles) stash((t + 1) & 1, set_next);
     if (t + 3 < ntiles) fetch(t + 3, set_next);
-    __syncthreads();
+    lds_barrier();  // orders the LDS tiles only: the fetches of tiles t+2, t+3 stay in flight
   };
   for (int t = 0; t < ntiles; t += 2) {
     step(t, Set1{});
@@ -460,11 +466,6 @@ __device__ __forceinline__ void dma2(const void* g, uint32_t m0) {
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// Workgroup barrier that orders LDS (waits for this wave's LDS accesses) but
-// leaves outstanding global loads in flight.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Exclusive prefix sum over the workgroup in thread order.
@@ -856,7 +857,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
       }
     }
   }
-  __syncthreads();  // lds_bt ready (and the row loads above have landed)
+  lds_barrier();  // lds_bt ready; the row loads above stay in flight
 
   // Stage loader: wave w's load i fills stage bytes [(4i + w) * 1024, +1024),
   // lane l the 16 bytes at l*16: entry kk = 8(4i + w) + l/8, physical chunk
