@@ -178,29 +178,12 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   }
 
   // Chunk size.  Prefill items walk up to kMaxChunk entries in 64-entry
-  // tiles and write dense scores.  Decode items stream their chunk through
-  // LDS; when there is enough work for chunks of at least 4k entries (and
-  // k <= 1024), each item keeps only its chunk's top-k candidates, which cuts
-  // the final selection's input by 4x or more.  Otherwise every score is
-  // staged, in chunks balanced over the resident workgroups (below).
-  int64_t key_work = 0;
-  for (const Group& g : groups) key_work += g.maxv;
+  // tiles.  Decode chunks are the smallest multiple of 128 entries for which
+  // the items fit the decode kernel's resident workgroups on one MI355X
+  // (256 CUs x 3) in a single round.  Both write every score densely.
   const int k = p.sparse_count;
-  int chunk = kMaxChunk;  // prefill; decode chunks are set below
-  bool local = false;
-  if (!prefill && rt <= 2 && k <= 1024) {
-    int c = 1024;
-    while (c < 4 * k) c *= 2;
-    if (c <= kMaxChunk && c * rt <= kMaxChunk && key_work / c >= 512) {
-      chunk = c;
-      local = true;
-    }
-  }
-
-  // Dense decode chunks: the smallest multiple of 128 entries for which the
-  // items fit the dense decode kernel's resident workgroups on one MI355X
-  // (256 CUs x 3) in a single round.
-  if (!prefill && !local) {
+  int chunk = kMaxChunk;
+  if (!prefill) {
     auto items_for = [&](int c) {
       int64_t n = 0;
       for (const Group& g : groups) n += (g.maxv + c - 1) / c;
@@ -211,36 +194,65 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
     chunk = c;
   }
 
-  // Per-row candidate counts and workspace offsets.  A row that sees more
-  // than k entries stages candidates for the selection stage: every score
-  // (dense), or the top-k of each chunk (local), in ascending index order.
-  auto seen = [&](int64_t vis, int64_t key0) -> int64_t {
-    return std::max<int64_t>(0, std::min<int64_t>(chunk, vis - key0));
-  };
-  int64_t ws = 0, max_cand = 0;
+  // Per-row workspace offsets.  A row that sees more than k entries stages
+  // every score for the selection stage, in ascending key order.
+  int64_t ws = 0, max_cand = 0, max_cand2 = 0;
+  std::vector<SelectEntry> pass2;
+  std::vector<std::pair<size_t, size_t>> pass2_segments;  // each merge's pass-1 entries
+  auto pad4 = [](int64_t n) { return (n + 3) & ~int64_t(3); };  // 16-byte aligned regions
   for (int64_t r = 0; r < rows; r++) {
     RowInfo& ri = out.rows[r];
     ri.ncand = 0;
-    ri.indexed = 0;
     if (ri.vis > k) {
-      int64_t n = 0;
-      if (local)
-        for (int64_t k0 = 0; k0 < ri.vis; k0 += chunk) n += std::min<int64_t>(k, seen(ri.vis, k0));
-      else
-        n = ri.vis;
+      const int64_t n = ri.vis;
       ri.ws_off = ws;
       ri.ncand = (int32_t)n;
-      ri.indexed = local ? 1 : 0;
-      ws += (n + 3) & ~int64_t(3);  // 16-byte aligned regions for vector loads
-      SelectEntry se{};
-      se.ws_off = ri.ws_off;
-      se.row = (int32_t)r;
-      se.ncand = ri.ncand;
-      se.indexed = ri.indexed;
-      out.select.push_back(se);
-      max_cand = std::max<int64_t>(max_cand, n);
+      ws += pad4(n);
+      if (n <= kSelSegment) {
+        SelectEntry se{};
+        se.src_off = ri.ws_off;
+        se.dst_off = -1;
+        se.row = (int32_t)r;
+        se.n = ri.ncand;
+        out.select.push_back(se);
+        max_cand = std::max<int64_t>(max_cand, n);
+      } else {
+        // Segments of kSelSegment candidates first keep their top-k each,
+        // then one selection merges them (regions placed below).
+        const size_t first = out.select.size();
+        int64_t m = 0;
+        for (int64_t s0 = 0; s0 < n; s0 += kSelSegment) {
+          const int64_t sn = std::min<int64_t>(kSelSegment, n - s0);
+          SelectEntry se{};
+          se.src_off = ri.ws_off + s0;
+          se.dst_off = m;  // relative to the row's merge region for now
+          se.row = (int32_t)r;
+          se.n = (int32_t)sn;
+          se.base = (int32_t)s0;
+          out.select.push_back(se);
+          max_cand = std::max<int64_t>(max_cand, sn);
+          m += std::min<int64_t>(k, sn);
+        }
+        SelectEntry fin{};
+        fin.dst_off = -1;
+        fin.row = (int32_t)r;
+        fin.n = (int32_t)m;
+        fin.indexed = 1;
+        pass2.push_back(fin);
+        pass2_segments.push_back({first, out.select.size()});
+        max_cand2 = std::max<int64_t>(max_cand2, m);
+      }
     }
   }
+  // The merge regions (scores, and key indices in the index region) follow
+  // every row's candidate region.
+  for (size_t i = 0; i < pass2.size(); i++) {
+    pass2[i].src_off = ws;
+    for (size_t e = pass2_segments[i].first; e < pass2_segments[i].second; e++) out.select[e].dst_off += ws;
+    ws += pad4(pass2[i].n);
+  }
+  const size_t n_pass1 = out.select.size();
+  out.select.insert(out.select.end(), pass2.begin(), pass2.end());
 
   for (const Group& g : groups) {
     Item base{};
@@ -266,13 +278,7 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
       if (!prefill) {
         for (int u = 0; u < g.nrows; u++) {
           const RowInfo& ri = out.rows[g.row0 + u];
-          if (ri.ws_off < 0) continue;
-          int64_t before = 0;  // candidates of the chunks before this one
-          if (local)
-            for (int64_t c0 = 0; c0 < k0; c0 += chunk) before += std::min<int64_t>(k, seen(ri.vis, c0));
-          else
-            before = k0;
-          it.cand_off[u] = ri.ws_off + before;
+          if (ri.ws_off >= 0) it.cand_off[u] = ri.ws_off + k0;
         }
       }
       out.items.push_back(it);
@@ -303,15 +309,16 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   h.visible_pairs = visible;
   h.ws_scores = ws;
   h.ws_index_offset = align16(ws * 4);
-  h.workspace_bytes = local ? h.ws_index_offset + ws * 4 : ws * 4;
-  h.local_select = local ? 1 : 0;
+  h.workspace_bytes = n_pass1 < out.select.size() ? h.ws_index_offset + ws * 4 : ws * 4;
   h.kind = prefill ? kKindPrefill : kKindDecode;
   h.rows_per_item = rt;
   h.n_items = (int32_t)out.items.size();
-  h.n_select = (int32_t)out.select.size();
+  h.n_select = (int32_t)n_pass1;
   h.chunk = chunk;
   h.max_vis = (int32_t)max_vis;
   h.max_cand = (int32_t)max_cand;
+  h.n_select2 = (int32_t)pass2.size();
+  h.max_cand2 = (int32_t)max_cand2;
   h.reg_chunks = reg_chunks;
   h.reg_rows = regular ? p.s1 : 0;
   h.reg_maxv = regular ? groups[0].maxv : 0;
@@ -321,7 +328,7 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   h.off_rows = align16(sizeof(PlanHeader));
   h.off_items = align16(h.off_rows + (int64_t)sizeof(RowInfo) * rows);
   h.off_select = align16(h.off_items + (int64_t)sizeof(Item) * h.n_items);
-  h.plan_bytes = align16(h.off_select + (int64_t)sizeof(SelectEntry) * h.n_select);
+  h.plan_bytes = align16(h.off_select + (int64_t)sizeof(SelectEntry) * (h.n_select + h.n_select2));
   return QLI_OK;
 }
 
@@ -409,7 +416,12 @@ QLI_EXPORT int qli_plan_info_get(const void* plan_host, qli_plan_info* info) {
   info->table_entries = h->table_entries;
   info->active_rows = h->active_rows;
   info->score_items = h->n_items;
-  info->select_rows = h->n_select;
+  {  // rows with a final selection: pass-1 entries that write a row, plus the merges
+    const SelectEntry* table = reinterpret_cast<const SelectEntry*>(static_cast<const uint8_t*>(plan_host) + h->off_select);
+    int32_t finals = h->n_select2;
+    for (int32_t i = 0; i < h->n_select; i++) finals += table[i].dst_off < 0 ? 1 : 0;
+    info->select_rows = finals;
+  }
   info->rows_per_item = h->rows_per_item;
   info->keys_per_chunk = h->chunk;
   info->kind = h->kind;

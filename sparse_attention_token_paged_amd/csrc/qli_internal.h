@@ -12,12 +12,12 @@
 namespace qli {
 
 constexpr uint32_t kPlanMagic = 0x504C4951u;  // "QILP"
-constexpr uint32_t kPlanVersion = 4;
+constexpr uint32_t kPlanVersion = 6;
 constexpr int kHeads = 64;       // query heads (QLI-README 约束说明)
 constexpr int kDim = 128;        // head dim of query and key (约束说明)
 constexpr int kTileKeys = 64;    // keys per MFMA tile step (4 n-tiles of 16)
 constexpr int kMaxChunk = 4096;  // keys per work item, upper bound
-constexpr int kDecodeSlots = 768;         // dense decode workgroups resident at once on MI355X (256 CUs x 3)          // decode chunk when no chunk-local selection is done
+constexpr int kDecodeSlots = 768;         // decode workgroups resident at once on MI355X (256 CUs x 3)
 constexpr int kMaxEntries = 1 << 22;      // compressed entries per sequence (exact reciprocal division)
 constexpr int kMaxItemRows = 4;           // rows carried inline by a decode item
 
@@ -42,8 +42,8 @@ struct PlanHeader {
   int32_t n_select;
   int32_t chunk;             // keys per work item
   int32_t max_vis;
-  int32_t local_select;      // decode items reduce their chunk to its top-k candidates
-  int32_t max_cand;          // largest candidate count of a selected row
+  int32_t reserved1;
+  int32_t max_cand;          // largest candidate count of a pass-1 selection
   int64_t key_entries;       // sum over batches of the largest visible count
   int64_t table_entries;     // block-table entries spanned by those entries
   int64_t active_rows;       // rows with at least one visible entry
@@ -54,7 +54,9 @@ struct PlanHeader {
   int32_t reg_chunks;
   int32_t reg_rows;
   int32_t reg_maxv;
-  int32_t reserved2;
+  int32_t n_select2;         // pass-2 selections (after the n_select pass-1 entries)
+  int32_t max_cand2;         // largest candidate count of a pass-2 selection
+  int32_t reserved2[3];
 };
 static_assert(sizeof(PlanHeader) % 16 == 0, "header keeps the tables aligned");
 
@@ -62,18 +64,23 @@ struct RowInfo {
   int32_t batch;   // -1 for rows that belong to no query token
   int32_t vis;     // visible compressed key entries
   int64_t ws_off;  // element offset of the row's candidates in the workspace, -1 = direct output
-  int32_t ncand;   // candidates the row stages for the selection stage
-  int32_t indexed; // 1: candidates carry explicit key indices (chunk-local selection)
+  int32_t ncand;   // scores the row stages for the selection stage (0: direct output)
+  int32_t reserved;
 };
 
-// One row that the final selection reduces (selection order).
+// One selection of the selection stage: the top min(k, n) of n candidates.
+// Pass 1 holds the rows of at most kSelSegment candidates (final) and the
+// segments of longer rows; pass 2 merges each long row's segment results.
 struct SelectEntry {
-  int64_t ws_off;   // element offset of its candidates (a multiple of 4)
-  int32_t row;
-  int32_t ncand;
-  int32_t indexed;  // 1: candidates carry explicit key indices
-  int32_t reserved[3];
+  int64_t src_off;  // element offset of the candidate scores (a multiple of 4); their
+                    // key indices sit at the same offset of the index region when indexed
+  int64_t dst_off;  // >= 0: write the winners as indexed candidates here; -1: final, to row `row`
+  int32_t row;      // output row
+  int32_t n;        // candidates
+  int32_t base;     // key index of candidate 0 when they carry no indices
+  int32_t indexed;  // 1: the candidates carry key indices (pass-2 merges)
 };
+constexpr int kSelSegment = 8192;  // candidates per first-pass selection of a long row
 static_assert(sizeof(SelectEntry) == 32, "select table layout");
 
 struct Item {

@@ -60,7 +60,6 @@ struct ScoreParams {
   const void* k_scale;
   const int32_t* block_table;
   float* ws;
-  int32_t* ws_idx;   // candidate indices (chunk-local selection)
   int32_t* idx_out;
   float* val_out;
   int64_t stride;
@@ -98,14 +97,6 @@ __device__ __forceinline__ float scale_from_bits(uint32_t b) {
   } else {
     return __uint_as_float(b);
   }
-}
-
-// Sum of the four lanes {l%16 + 16m}: permlane32 then permlane16 swaps.
-__device__ __forceinline__ float sum_lane_groups(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Sum over the four lane groups of per-lane partials, scattered so that lane
@@ -442,9 +433,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 __device__ __forceinline__ float key_value(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
 
 // Direct-to-LDS loads, issued from inline assembly so that the compiler does
 // not add waits for them: each lane's bytes land at m0 + lane * 16 (16-byte
@@ -554,7 +542,7 @@ __device__ __forceinline__ void block_scan2(int x, int y, int& xb, int& yb, int&
     sh.wsum[0][wave] = xi;
     sh.wsum[1][wave] = yi;
   }
-  __syncthreads();
+  lds_barrier();
   xb = xi - x;
   yb = yi - y;
   xt = 0;
@@ -630,7 +618,7 @@ __device__ __forceinline__ void select_topk(const void* src, int n, int k, int* 
     sh.red[1][wave] = o;
   }
   for (int b = tid; b < 2048; b += NT) hist[b] = 0;
-  __syncthreads();
+  lds_barrier();
   a = 0xFFFFFFFFu;
   o = 0u;
 #pragma unroll
@@ -663,7 +651,7 @@ __device__ __forceinline__ void select_topk(const void* src, int n, int k, int* 
     }
     int* Hn = hist + ((p + 1) & 1) * 2048;  // read last in pass p - 1, used by pass p + 1
     for (int b = tid; b < 2048; b += NT) Hn[b] = 0;
-    __syncthreads();
+    lds_barrier();
     // Thread t owns digits nb-1-BPT*t .. nb-BPT*(t+1) (descending).
     int h[BPT];
     int local = 0;
@@ -675,7 +663,7 @@ __device__ __forceinline__ void select_topk(const void* src, int n, int k, int* 
     }
     const int incl = wave_incl_scan(local);
     if (lane == 63) sh.wsum[p & 1][wave] = incl;
-    __syncthreads();
+    lds_barrier();
     int before = incl - local;
 #pragma unroll
     for (int w = 0; w < NW; w++) before += w < wave ? sh.wsum[p & 1][w] : 0;
@@ -691,7 +679,7 @@ __device__ __forceinline__ void select_topk(const void* src, int n, int k, int* 
         acc += h[jj];
       }
     }
-    __syncthreads();
+    lds_barrier();
     const int digit = sh.res[p & 1][0], above = sh.res[p & 1][1], count = sh.res[p & 1][2];
     kk -= above;
     prefix |= (uint32_t)digit << shift;
@@ -741,9 +729,7 @@ __device__ __forceinline__ void select_topk(const void* src, int n, int k, int* 
 // arithmetic is exact); two stages are in flight while one is computed.
 // Each wave scores its row against its n-tiles of the stage:
 //   RT = 4: all 8 n-tiles, RT = 2: 4 n-tiles, RT = 1: 2 n-tiles.
-// LOCAL items keep every score of the chunk in LDS and then reduce it to its
-// top-k candidates (score, index) for the final selection.
-template <int QK, int RT, bool LOCAL, bool DUMP>
+template <int QK, int RT, bool DUMP>
 __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams P) {
   constexpr int SC = 128;                     // entries per LDS stage
   constexpr int NSTAGE = 3;
@@ -752,13 +738,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   constexpr int KLOADS = SC * kDim / (kScoreThreads * 16);  // 4 key loads per thread per stage
   constexpr int PER_STAGE = KLOADS + 1;       // + the ScaleK load
   constexpr int SB = QK == QLI_QK_INT8 ? 2 : 4;
-  constexpr int LCAP = LOCAL ? kMaxChunk / RT : 1;
 
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSTAGE][SC * kDim];
   __shared__ uint32_t ring_sk[NSTAGE][SC];   // ScaleK bits, one 4-byte slot per entry
   __shared__ int32_t lds_bt[kMaxChunk / 16 + 2];
-  __shared__ __attribute__((aligned(16))) uint32_t lds_keys[RT][LCAP];  // LOCAL: order keys of the chunk's scores per row
-  __shared__ SelShared sel;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -770,99 +753,42 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   // Persistent workgroups over the work-sorted items, in snake order: round t
   // takes item t*G + b (t even) or t*G + G-1-b (t odd).
   const int G = gridDim.x;
-  for (int round = 0;; round++) {
-  const int pos = round * G + ((round & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
-  if (pos >= P.n_items) break;  // uniform; positions grow with the round
-  // read in place: the per-row fields are indexed by a wave-uniform row
-  const Item& it = P.items[pos];
+  auto pos_of = [&](int t) { return t * G + ((t & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x); };
+  const bool reg = P.reg_chunks > 0;
+  const int bs = P.block_size;
+  const int u = wave / WPR;  // this wave's row of the item
+  const int sub = wave % WPR;
 
-  // Rows that see fewer than k entries: slots vis..k-1 are -1 / -inf.
-  auto pad = [&]() __attribute__((always_inline)) {
-    if (it.flags & kItemPad) {
-      for (int u = 0; u < it.nrows; u++) {
-        const int64_t r = it.row0 + u;
-        const int vis = it.vis[u];
+  // State of the item being streamed (set by begin()).
+  int batch = 0, key0 = 0, nkeys = 0, row0 = 0, nrows = 0, kend = 0, fb = 0;
+  bool rok = false;
+  int64_t r = 0;
+  int rvis = 0;
+  int64_t coff = -1;
+  Frag qa[4];
+  float wq[16];
+  int32_t* oi = nullptr;   // this row's outputs
+  float* ov = nullptr;
+  bool direct = false;     // the row sees at most k entries: scores go straight to the outputs
+
+  // Rows of an item that see fewer than k entries: slots vis..k-1 are -1 / -inf.
+  auto pad = [&](const Item& itp) __attribute__((always_inline)) {
+    if (itp.flags & kItemPad) {
+      for (int uu = 0; uu < itp.nrows; uu++) {
+        const int64_t rr = itp.row0 + uu;
+        const int vis = itp.vis[uu];
         if (vis >= k) continue;
-        for (int pos = vis + tid; pos < k; pos += kScoreThreads) {
-          P.idx_out[r * k + pos] = -1;
-          if (P.val_out) P.val_out[r * k + pos] = -INFINITY;
+        for (int e = vis + tid; e < k; e += kScoreThreads) {
+          P.idx_out[rr * k + e] = -1;
+          if (P.val_out) P.val_out[rr * k + e] = -INFINITY;
         }
       }
     }
   };
-  // Regular plans: the item's batch, keys and rows follow from its position,
-  // so the block-table and query loads below need not wait for the item.
-  const bool reg = P.reg_chunks > 0;
-  int batch, key0, nkeys, row0, nrows;
-  if (reg) {
-    batch = pos / P.reg_chunks;
-    key0 = (pos - batch * P.reg_chunks) * P.chunk;
-    nkeys = min(P.chunk, P.reg_maxv - key0);
-    row0 = batch * P.reg_rows;
-    nrows = P.reg_rows;
-  } else {
-    pad();
-    batch = it.batch;
-    key0 = it.key0;
-    nkeys = it.nkeys;
-    row0 = it.row0;
-    nrows = it.nrows;
-    if (nkeys <= 0) continue;  // uniform across the workgroup
-  }
-
-  const int bs = P.block_size;
-  const int kend = key0 + nkeys;
-  const int fb = (int)__umulhi((uint32_t)key0, P.bs_magic);
-  const int nblk = (int)__umulhi((uint32_t)(kend - 1), P.bs_magic) - fb + 1;
-  {
-    const int32_t* bt = P.block_table + (int64_t)batch * P.max_blocks + fb;
-    for (int t = tid; t < nblk; t += kScoreThreads) lds_bt[t] = bt[t];
-  }
-
-  // This wave's row: query fragments and w' = W * ScaleQ (loads issued before
-  // the barrier, so they share its round trip with the block table).
-  const int u = wave / WPR;
-  const int sub = wave % WPR;
-  const bool rok = u < nrows;
-  const int64_t r = row0 + (rok ? u : 0);
-  const int rvis = rok ? it.vis[u] : 0;
-  const int64_t coff = rok ? it.cand_off[u] : -1;
-  Frag qa[4];
-  float wq[16];
-  {
-    const uint8_t* qrow = P.query + r * (kHeads * kDim);
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-      const uint8_t* qh = qrow + (16 * m + c16) * kDim;
-      qa[m].lo = *reinterpret_cast<const v4i*>(qh + 16 * chunk_lo<QK>(q));
-      qa[m].hi = *reinterpret_cast<const v4i*>(qh + 16 * chunk_hi<QK>(q));
-    }
-    // heads 16m + 4q + i, i = 0..3, are consecutive: one vector load per m
-    const int64_t e0 = r * kHeads + 4 * q;
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-      if constexpr (QK == QLI_QK_INT8) {
-        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-        const h4 w = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.weights) + e0 + 16 * m);
-        const h4 sq = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.q_scale) + e0 + 16 * m);
-#pragma unroll
-        for (int i = 0; i < 4; i++) wq[4 * m + i] = __builtin_fmaf((float)w[i], (float)sq[i], 0.f);
-      } else {
-        const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(P.weights) + e0 + 16 * m);
-        const float4 sq = *reinterpret_cast<const float4*>(static_cast<const float*>(P.q_scale) + e0 + 16 * m);
-        wq[4 * m + 0] = w.x * sq.x;
-        wq[4 * m + 1] = w.y * sq.y;
-        wq[4 * m + 2] = w.z * sq.z;
-        wq[4 * m + 3] = w.w * sq.w;
-      }
-    }
-  }
-  lds_barrier();  // lds_bt ready; the row loads above stay in flight
 
   // Stage loader: wave w's load i fills stage bytes [(4i + w) * 1024, +1024),
   // lane l the 16 bytes at l*16: entry kk = 8(4i + w) + l/8, physical chunk
   // l%8 holding logical chunk (l%8) ^ ((kk>>1)&7) (conflict-free MFMA reads).
-  const int nstages = (nkeys + SC - 1) / SC;
   auto issue = [&](int st) __attribute__((always_inline)) {
     const int slot_ = st % NSTAGE;
     const int e_base = key0 + st * SC;
@@ -889,11 +815,72 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     }
   };
 
-  int32_t* oi = P.idx_out + r * k;
-  float* ov = P.val_out ? P.val_out + r * k : nullptr;
-  const bool direct = rvis <= k;
-  // LOCAL: this row's scores of the chunk, in the selection's transposed layout
-  const int lrg = LOCAL ? sel_groups<kScoreThreads>(max(1, min(nkeys, rvis - key0))) : 1;
+
+  // Starts item pos: its fields (from the position for regular plans, so the
+  // loads below need not wait for the item), its block-table slice in LDS,
+  // this wave's query fragments and w' = W * ScaleQ, and the loads of its
+  // stages 0 and 1.  False for an item without keys (padding only).
+  auto begin = [&](int pos) __attribute__((always_inline)) {
+    const Item& itb = P.items[pos];
+    if (reg) {
+      batch = pos / P.reg_chunks;
+      key0 = (pos - batch * P.reg_chunks) * P.chunk;
+      nkeys = min(P.chunk, P.reg_maxv - key0);
+      row0 = batch * P.reg_rows;
+      nrows = P.reg_rows;
+    } else {
+      pad(itb);
+      batch = itb.batch;
+      key0 = itb.key0;
+      nkeys = itb.nkeys;
+      row0 = itb.row0;
+      nrows = itb.nrows;
+      if (nkeys <= 0) return false;  // uniform across the workgroup
+    }
+    kend = key0 + nkeys;
+    fb = (int)__umulhi((uint32_t)key0, P.bs_magic);
+    const int nblk = (int)__umulhi((uint32_t)(kend - 1), P.bs_magic) - fb + 1;
+    {
+      const int32_t* bt = P.block_table + (int64_t)batch * P.max_blocks + fb;
+      for (int t = tid; t < nblk; t += kScoreThreads) lds_bt[t] = bt[t];
+    }
+    rok = u < nrows;
+    r = row0 + (rok ? u : 0);
+    rvis = rok ? itb.vis[u] : 0;
+    coff = rok ? itb.cand_off[u] : -1;
+    {
+      const uint8_t* qrow = P.query + r * (kHeads * kDim);
+  #pragma unroll
+      for (int m = 0; m < 4; m++) {
+        const uint8_t* qh = qrow + (16 * m + c16) * kDim;
+        qa[m].lo = *reinterpret_cast<const v4i*>(qh + 16 * chunk_lo<QK>(q));
+        qa[m].hi = *reinterpret_cast<const v4i*>(qh + 16 * chunk_hi<QK>(q));
+      }
+      // heads 16m + 4q + i, i = 0..3, are consecutive: one vector load per m
+      const int64_t e0 = r * kHeads + 4 * q;
+  #pragma unroll
+      for (int m = 0; m < 4; m++) {
+        if constexpr (QK == QLI_QK_INT8) {
+          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+          const h4 w = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.weights) + e0 + 16 * m);
+          const h4 sq = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.q_scale) + e0 + 16 * m);
+  #pragma unroll
+          for (int i = 0; i < 4; i++) wq[4 * m + i] = __builtin_fmaf((float)w[i], (float)sq[i], 0.f);
+        } else {
+          const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(P.weights) + e0 + 16 * m);
+          const float4 sq = *reinterpret_cast<const float4*>(static_cast<const float*>(P.q_scale) + e0 + 16 * m);
+          wq[4 * m + 0] = w.x * sq.x;
+          wq[4 * m + 1] = w.y * sq.y;
+          wq[4 * m + 2] = w.z * sq.z;
+          wq[4 * m + 3] = w.w * sq.w;
+        }
+      }
+    }
+    lds_barrier();  // lds_bt ready; the row loads above stay in flight
+    issue(0);
+    if (nkeys > SC) issue(1);
+    return true;
+  };
 
   // Scores of 64 entries (4 n-tiles) or 32 entries (2 n-tiles) of the stage.
   auto score_group = [&](int slot_, int st, int n0, auto nt_) __attribute__((always_inline)) {
@@ -972,8 +959,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
       if (direct) {
         oi[j] = j;
         if (ov) ov[j] = score;
-      } else if constexpr (LOCAL) {
-        lds_keys[u][sel_slot<kScoreThreads>(e, lrg)] = order_key(score);
       } else {
         P.ws[coff + e] = score;
       }
@@ -983,9 +968,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     }
   };
 
+
+  for (int round = 0;; round++) {
+  const int pos = pos_of(round);
+  if (pos >= P.n_items) break;  // uniform; positions grow with the round
+  if (!begin(pos)) continue;
+  const int nstages = (nkeys + SC - 1) / SC;
+  oi = P.idx_out + r * k;
+  ov = P.val_out ? P.val_out + r * k : nullptr;
+  direct = rvis <= k;
+
   // Pipeline: stages st+1 and st+2 are in flight while st is computed.
-  issue(0);
-  if (nstages > 1) issue(1);
   for (int st = 0; st < nstages; st++) {
     if (st + 2 < nstages) issue(st + 2);
     const int newer = min(st + 2, nstages - 1) - st;  // stages issued after st
@@ -1011,34 +1004,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     lds_barrier();  // the slot is free for stage st + 3
   }
 
-  if constexpr (LOCAL) {
-    // Reduce each staged row of the chunk to its top-k, in ascending index order.
-    __syncthreads();
-    int* hist = reinterpret_cast<int*>(&ring[0][0]);  // the ring is idle now
-    int32_t* ws_idx = P.ws_idx;
-    for (int uu = 0; uu < nrows; uu++) {
-      const int vis = it.vis[uu];
-      const int64_t off = it.cand_off[uu];
-      if (vis <= k || off < 0) continue;  // uniform
-      const int n = min(nkeys, vis - key0);
-      if (n <= 0) continue;
-      const uint32_t* sk = lds_keys[uu];
-      if (n <= k) {
-        const int rg = sel_groups<kScoreThreads>(n);
-        for (int e = tid; e < n; e += kScoreThreads) {
-          P.ws[off + e] = key_value(sk[sel_slot<kScoreThreads>(e, rg)]);
-          ws_idx[off + e] = key0 + e;
-        }
-      } else {
-        select_topk<kScoreThreads, true>(sk, n, k, hist, sel, [&](int pos, int e, float v) __attribute__((always_inline)) {
-          P.ws[off + pos] = v;
-          ws_idx[off + pos] = key0 + e;
-        });
-        __syncthreads();  // the histograms and shared counters serve the next row
-      }
-    }
-  }
-  if (reg) pad();
+  if (reg) pad(P.items[pos]);
   }  // rounds (the item's last barrier leaves the LDS free for the next one)
 }
 
@@ -1048,36 +1014,62 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
 // ---------------------------------------------------------------------------
 
 constexpr int kSelThreads = 1024;  // 16 waves: the phases are latency-bound, more waves hide it
+constexpr int kSelLdsCap = 32768;  // candidates a selection stages in LDS (128 KiB of keys)
 
 struct SelectParams {
-  const SelectEntry* rows;  // the plan's selection table
-  const float* ws;
-  const int32_t* ws_idx;
+  const SelectEntry* rows;  // this pass's entries of the plan's selection table
+  float* ws;
+  int32_t* ws_idx;
   int32_t* idx_out;
   float* val_out;
   int32_t k;
 };
 
-// LDS: the row (n <= kSelLdsCap) is staged in LDS once; otherwise every
-// phase reads it from the workspace.  INDEXED: the candidates carry their
-// key indices (chunk-local selection), else a candidate's position is its
-// key index.
-constexpr int kSelLdsCap = 32768;
-
-template <int NT, bool LDS, bool INDEXED>
+// CAP > 0: the candidates (n <= CAP) are staged once in LDS as order keys in
+// the transposed layout; CAP = 0: every phase reads them from the workspace.
+// An entry keeps the top min(k, n) of its candidates, either as a row's final
+// output or as indexed candidates for a later merge.
+template <int NT, int CAP>
 __global__ __launch_bounds__(NT) void select_kernel(SelectParams S) {
+  constexpr bool LDS = CAP > 0;
   __shared__ int hist[2 * 2048];
   __shared__ SelShared sh;
-  __shared__ __attribute__((aligned(16))) uint32_t cache[LDS ? kSelLdsCap : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t cache[LDS ? CAP : 4];
   const SelectEntry se = S.rows[blockIdx.x];
-  const int n = se.ncand;
-  const int k = S.k;
-  const float* sc = S.ws + se.ws_off;
-  const int32_t* ix = S.ws_idx + se.ws_off;
+  const int n = se.n;
+  const int kk = min(S.k, n);
+  const float* sc = S.ws + se.src_off;
+  const int32_t* ix = S.ws_idx + se.src_off;
+  const bool indexed = se.indexed != 0;
   const int tid = threadIdx.x;
+  int32_t* oi = nullptr;
+  float* ov = nullptr;
+  float* dv = nullptr;
+  int32_t* di = nullptr;
+  if (se.dst_off < 0) {
+    oi = S.idx_out + (int64_t)se.row * S.k;
+    ov = S.val_out ? S.val_out + (int64_t)se.row * S.k : nullptr;
+  } else {
+    dv = S.ws + se.dst_off;
+    di = S.ws_idx + se.dst_off;
+  }
+  auto emit = [&](int pos, int e, float v) __attribute__((always_inline)) {
+    const int32_t key = indexed ? ix[e] : se.base + e;
+    if (oi) {
+      oi[pos] = key;
+      if (ov) ov[pos] = v;
+    } else {
+      dv[pos] = v;
+      di[pos] = key;
+    }
+  };
+  if (n <= kk) {  // every candidate is kept (a short last segment)
+    for (int e = tid; e < n; e += NT) emit(e, e, sc[e]);
+    return;
+  }
   if constexpr (LDS) {
     // Order keys in the transposed layout; eight 16-byte loads in flight per
-    // thread (addresses clamped into the row's 16-byte padded region).
+    // thread (addresses clamped into the 16-byte padded candidate region).
     constexpr int STEP = NT * 4;
     const int last = ((n + 3) & ~3) - 4;
     const int rg = sel_groups<NT>(n);
@@ -1096,13 +1088,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectParams S) {
     }
     __syncthreads();
   }
-  int32_t* oi = S.idx_out + (int64_t)se.row * k;
-  float* ov = S.val_out ? S.val_out + (int64_t)se.row * k : nullptr;
-  select_topk<NT, LDS>(LDS ? static_cast<const void*>(cache) : static_cast<const void*>(sc), n, k, hist, sh,
-                       [&](int pos, int e, float v) __attribute__((always_inline)) {
-                         oi[pos] = INDEXED ? ix[e] : e;
-                         if (ov) ov[pos] = v;
-                       });
+  select_topk<NT, LDS>(LDS ? static_cast<const void*>(cache) : static_cast<const void*>(sc), n, kk, hist, sh,
+                       emit);
 }
 
 // Workgroups of `kernel` that the current device holds at once (all CUs),
@@ -1134,18 +1121,15 @@ template <int QK, bool DUMP>
 hipError_t launch_score_t(const ScoreParams& P, const PlanHeader* h, hipStream_t st) {
   const dim3 grid(h->n_items), block(kScoreThreads);
   if (h->kind == kKindDecode) {
-    const bool local = h->local_select != 0;
     auto go = [&](void (*kern)(ScoreParams)) {
       const int slots = resident_slots(reinterpret_cast<const void*>(kern), kScoreThreads);
       const dim3 pgrid(slots > 0 ? std::min<int>(h->n_items, slots) : h->n_items);
       return launch(kern, pgrid, block, st, P);
     };
-    switch (h->rows_per_item * 2 + (local ? 1 : 0)) {
-      case 2: return go(score_decode_kernel<QK, 1, false, DUMP>);
-      case 3: return go(score_decode_kernel<QK, 1, true, DUMP>);
-      case 4: return go(score_decode_kernel<QK, 2, false, DUMP>);
-      case 5: return go(score_decode_kernel<QK, 2, true, DUMP>);
-      case 8: return go(score_decode_kernel<QK, 4, false, DUMP>);
+    switch (h->rows_per_item) {
+      case 1: return go(score_decode_kernel<QK, 1, DUMP>);
+      case 2: return go(score_decode_kernel<QK, 2, DUMP>);
+      case 4: return go(score_decode_kernel<QK, 4, DUMP>);
       default: return hipErrorInvalidValue;
     }
   }
@@ -1175,8 +1159,6 @@ int launch_score(const RunArgs& a, bool dump) {
   P.k_scale = a.k_scale;
   P.block_table = a.block_table;
   P.ws = static_cast<float*>(a.workspace);
-  P.ws_idx = a.workspace ? reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + h->ws_index_offset)
-                         : nullptr;
   P.idx_out = a.sparse_indices;
   P.val_out = a.sparse_values;
   P.stride = a.p->key_block_stride ? a.p->key_block_stride : (int64_t)a.p->block_size * kDim;
@@ -1204,20 +1186,23 @@ int launch_select(const RunArgs& a) {
   const PlanHeader* h = a.hdr;
   if (h->n_select == 0) return 0;
   SelectParams S{};
-  S.rows = reinterpret_cast<const SelectEntry*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_select);
-  S.ws = static_cast<const float*>(a.workspace);
-  S.ws_idx = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(a.workspace) + h->ws_index_offset);
+  const SelectEntry* table = reinterpret_cast<const SelectEntry*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_select);
+  S.ws = static_cast<float*>(a.workspace);
+  S.ws_idx = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + h->ws_index_offset);
   S.idx_out = a.sparse_indices;
   S.val_out = a.sparse_values;
   S.k = a.p->sparse_count;
-  const dim3 grid(h->n_select), block(kSelThreads);
   const hipStream_t st = static_cast<hipStream_t>(a.stream);
-  const bool lds = h->max_cand <= kSelLdsCap;
-  const hipError_t e = h->local_select
-                           ? (lds ? launch(select_kernel<kSelThreads, true, true>, grid, block, st, S)
-                                  : launch(select_kernel<kSelThreads, false, true>, grid, block, st, S))
-                           : (lds ? launch(select_kernel<kSelThreads, true, false>, grid, block, st, S)
-                                  : launch(select_kernel<kSelThreads, false, false>, grid, block, st, S));
+  const dim3 block(kSelThreads);
+  auto pass = [&](const SelectEntry* rows, int count, int max_n) {
+    S.rows = rows;
+    const dim3 grid(count);
+    if (max_n <= kSelSegment) return launch(select_kernel<kSelThreads, kSelSegment>, grid, block, st, S);
+    if (max_n <= kSelLdsCap) return launch(select_kernel<kSelThreads, kSelLdsCap>, grid, block, st, S);
+    return launch(select_kernel<kSelThreads, 0>, grid, block, st, S);
+  };
+  hipError_t e = pass(table, h->n_select, h->max_cand);
+  if (e == hipSuccess && h->n_select2 > 0) e = pass(table + h->n_select, h->n_select2, h->max_cand2);
   return e == hipSuccess ? 0 : (int)e;
 }
 

@@ -114,11 +114,14 @@ HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("fingerprint", "<u8"), ("
                 ("workspace_bytes", "<i8"), ("rows", "<i8"), ("visible_pairs", "<i8"), ("ws_scores", "<i8"),
                 ("off_rows", "<i8"), ("off_items", "<i8"), ("off_select", "<i8"), ("kind", "<i4"),
                 ("rows_per_item", "<i4"), ("n_items", "<i4"), ("n_select", "<i4"), ("chunk", "<i4"),
-                ("max_vis", "<i4"), ("local_select", "<i4"), ("max_cand", "<i4"), ("key_entries", "<i8"),
+                ("max_vis", "<i4"), ("reserved1", "<i4"), ("max_cand", "<i4"), ("key_entries", "<i8"),
                 ("table_entries", "<i8"), ("active_rows", "<i8"), ("ws_index_offset", "<i8"),
-                ("reg_chunks", "<i4"), ("reg_rows", "<i4"), ("reg_maxv", "<i4"), ("reserved2", "<i4")])
-ROW = np.dtype([("batch", "<i4"), ("vis", "<i4"), ("ws_off", "<i8"), ("ncand", "<i4"), ("indexed", "<i4")])
-SEL = np.dtype([("ws_off", "<i8"), ("row", "<i4"), ("ncand", "<i4"), ("indexed", "<i4"), ("reserved", "<i4", 3)])
+                ("reg_chunks", "<i4"), ("reg_rows", "<i4"), ("reg_maxv", "<i4"), ("n_select2", "<i4"),
+                ("max_cand2", "<i4"), ("reserved2", "<i4", 3)])
+ROW = np.dtype([("batch", "<i4"), ("vis", "<i4"), ("ws_off", "<i8"), ("ncand", "<i4"), ("reserved", "<i4")])
+SEL = np.dtype([("src_off", "<i8"), ("dst_off", "<i8"), ("row", "<i4"), ("n", "<i4"), ("base", "<i4"),
+                ("indexed", "<i4")])
+SEGMENT = 8192  # candidates per first-pass selection of a long row
 ITEM = np.dtype([("row0", "<i4"), ("nrows", "<i4"), ("batch", "<i4"), ("key0", "<i4"), ("nkeys", "<i4"),
                  ("flags", "<i4"), ("reserved", "<i4", 2), ("vis", "<i4", 4), ("cand_off", "<i8", 4)])
 
@@ -127,7 +130,8 @@ def parse(plan):
     h = np.frombuffer(plan[:HDR.itemsize].tobytes(), HDR)[0]
     rows = np.frombuffer(plan[h["off_rows"]:h["off_rows"] + ROW.itemsize * h["rows"]].tobytes(), ROW)
     items = np.frombuffer(plan[h["off_items"]:h["off_items"] + ITEM.itemsize * h["n_items"]].tobytes(), ITEM)
-    sel = np.frombuffer(plan[h["off_select"]:h["off_select"] + SEL.itemsize * h["n_select"]].tobytes(), SEL)
+    nsel = int(h["n_select"]) + int(h["n_select2"])
+    sel = np.frombuffer(plan[h["off_select"]:h["off_select"] + SEL.itemsize * nsel].tobytes(), SEL)
     return h, rows, items, sel
 
 
@@ -186,22 +190,47 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
             assert max(int(vis[r]) for r in range(b * s1_, (b + 1) * s1_)) == mv_
     assert np.all(padded == 1)
     k = p["sparse_count"]
-    assert list(sel["row"]) == [r for r in range(nrows) if vis[r] > k]
-    assert np.array_equal(sel["ncand"], rows["ncand"][sel["row"]]) and np.array_equal(sel["ws_off"], rows["ws_off"][sel["row"]])
-    assert np.array_equal(sel["indexed"], rows["indexed"][sel["row"]])
-    sel = [int(r) for r in sel["row"]]
-    local = bool(h["local_select"])
-    chunk = int(h["chunk"])
-    # candidates per selected row: every score, or each chunk's top-k
-    ncand = [sum(min(k, max(0, min(chunk, int(vis[r]) - c0))) for c0 in range(0, int(vis[r]), chunk))
-             if local else int(vis[r]) for r in sel]
-    assert [int(rows[r]["ncand"]) for r in sel] == ncand
-    assert all(int(rows[r]["indexed"]) == int(local) for r in sel)
-    offs = [int(rows[r]["ws_off"]) for r in sel]
-    padded_n = [(n + 3) // 4 * 4 for n in ncand]  # 16-byte aligned candidate regions
-    assert offs == list(np.cumsum([0] + padded_n)[:-1])
-    assert ws == (int(h["ws_index_offset"]) + 4 * sum(padded_n) if local else 4 * sum(padded_n))
-    assert int(h["max_cand"]) == max(ncand, default=0)
+    selected = [r for r in range(nrows) if vis[r] > k]
+    # a selected row stages every score it sees; the others none
+    ncand = {r: int(vis[r]) for r in selected}
+    assert [int(x) for x in rows["ncand"]] == [ncand.get(r, 0) for r in range(nrows)]
+    pad4 = lambda n: (n + 3) // 4 * 4  # 16-byte aligned candidate regions
+    offs = [int(rows[r]["ws_off"]) for r in selected]
+    assert offs == list(np.cumsum([0] + [pad4(ncand[r]) for r in selected])[:-1])
+    # The selection table: pass 1 = short rows (final) and segments of long rows,
+    # pass 2 = one merge per long row over its segments' winners.
+    n1, n2 = int(h["n_select"]), int(h["n_select2"])
+    p1, p2 = sel[:n1], sel[n1:]
+    long_rows = [r for r in selected if ncand[r] > SEGMENT]
+    assert list(p2["row"]) == long_rows and np.all(p2["dst_off"] == -1) and np.all(p2["indexed"] == 1)
+    region_end = sum(pad4(ncand[r]) for r in selected)
+    merge_off = region_end
+    i1 = 0
+    for r in selected:
+        n = ncand[r]
+        if n <= SEGMENT:
+            e = p1[i1]
+            i1 += 1
+            assert (e["row"], e["n"], e["src_off"], e["dst_off"], e["base"], e["indexed"]) == \
+                (r, n, rows[r]["ws_off"], -1, 0, 0)
+            continue
+        dst, m = merge_off, 0
+        for s0 in range(0, n, SEGMENT):
+            e = p1[i1]
+            i1 += 1
+            sn = min(SEGMENT, n - s0)
+            assert (e["row"], e["n"], e["src_off"], e["dst_off"], e["base"], e["indexed"]) == \
+                (r, sn, rows[r]["ws_off"] + s0, dst + m, s0, 0)
+            m += min(k, sn)
+        fin = p2[long_rows.index(r)]
+        assert fin["src_off"] == merge_off and fin["n"] == m
+        merge_off += pad4(m)
+    assert i1 == n1
+    assert np.all(sel["src_off"] % 4 == 0)
+    assert int(h["max_cand"]) == max([int(e["n"]) for e in p1], default=0)
+    assert int(h["max_cand2"]) == max([int(e["n"]) for e in p2], default=0)
+    assert ws == (int(h["ws_index_offset"]) + 4 * merge_off if n2 > 0 else 4 * merge_off)
+    sel = selected
     if h["kind"] == 0:
         # decode items: inline visible counts, and candidate slots that tile each row's range
         slots = {r: [] for r in sel}
@@ -210,8 +239,7 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
                 r = it["row0"] + u
                 assert it["vis"][u] == vis[r]
                 if it["nkeys"] and r in slots:
-                    n = min(k, max(0, min(chunk, int(vis[r]) - it["key0"]))) if local else \
-                        max(0, min(int(it["nkeys"]), int(vis[r]) - it["key0"]))
+                    n = max(0, min(int(it["nkeys"]), int(vis[r]) - it["key0"]))
                     slots[r].append((int(it["cand_off"][u]), n))
                 elif it["nkeys"]:
                     assert it["cand_off"][u] == -1
