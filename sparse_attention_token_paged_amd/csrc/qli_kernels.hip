@@ -427,8 +427,8 @@ void score_kernel(ScoreParams P) {
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t order_key(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f);  // negative: all bits flip; else the sign bit is set
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float key_value(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
@@ -480,18 +480,18 @@ __device__ int block_exclusive_scan(int v, int* tmp) {
 // Top-k selection over staged scores.
 // ---------------------------------------------------------------------------
 //
-// The n scores sit in LDS (or, for very long rows, in the workspace), 16-byte
-// aligned and readable up to n rounded up to 4.  Thread t owns the
-// contiguous positions [t*S, t*S + S), S = ceil(n / NT) rounded up to 4, and
-// walks them with a rolled float4 loop in every phase (keys are formed on
-// the fly with order_key), so the executed code stays small.
+// The n scores sit in the workspace, 16-byte aligned and readable up to n
+// rounded up to 4.  Thread t owns the contiguous positions [t*S, t*S + S):
+// up to 32768 scores are loaded once into registers as order keys (S = 4R
+// per thread, R = 1, 2, 4 or 8); longer lists are re-read in every phase.
 //
 // Threshold: the bits every key shares are skipped, then radix passes of up
 // to 11 bits histogram the keys that still match the threshold prefix (LDS
 // atomics into one of two 2048-bin histograms, the other being cleared
 // meanwhile); a block scan over the bins in descending digit order finds
 // the digit of the kk-th largest key.  It stops once the threshold bin is
-// taken whole or all 32 bits are fixed.  Three barriers per pass.
+// taken whole or all 32 bits are fixed.  Three barriers per pass; cross-wave
+// sums and reductions take one DPP row of 16 lanes.
 // Emission: every key above the threshold and the kk lowest-positioned keys
 // equal to it, each at its rank in position order (block scans of the
 // per-thread counts).
@@ -526,6 +526,44 @@ __device__ __forceinline__ void wave_and_or(uint32_t& a, uint32_t& o) {
                  __builtin_amdgcn_readlane(y, 32) | __builtin_amdgcn_readlane(y, 48));
 }
 
+// Inclusive prefix sum over the 16 lanes of each row (row shifts only).
+__device__ __forceinline__ int row_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  return v;
+}
+
+// Per-wave totals tot[0 .. NW) (NW <= 16, published before a barrier): the
+// sum over the waves below `wave` (uniform) and the sum over all of them.
+template <int NW>
+__device__ __forceinline__ void waves_prefix(const int* tot, int wave, int& below, int& total) {
+  static_assert(NW <= 16, "one DPP row holds the wave totals");
+  const int lane = threadIdx.x & 63;
+  const int v = row_incl_scan(lane < NW ? tot[lane] : 0);
+  const int b = __builtin_amdgcn_readlane(v, wave > 0 ? wave - 1 : 0);
+  below = wave > 0 ? b : 0;
+  total = __builtin_amdgcn_readlane(v, NW - 1);
+}
+
+// AND and OR of the per-wave values red[0][0 .. NW), red[1][0 .. NW) (uniform).
+template <int NW>
+__device__ __forceinline__ void waves_and_or(const uint32_t (*red)[16], uint32_t& a, uint32_t& o) {
+  const int lane = threadIdx.x & 63;
+  int x = lane < NW ? (int)red[0][lane] : -1, y = lane < NW ? (int)red[1][lane] : 0;
+  x &= __builtin_amdgcn_update_dpp(0, x, 0xb1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+  y |= __builtin_amdgcn_update_dpp(0, y, 0xb1, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(0, x, 0x4e, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+  y |= __builtin_amdgcn_update_dpp(0, y, 0x4e, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(0, x, 0x141, 0xf, 0xf, false);  // row_half_mirror
+  y |= __builtin_amdgcn_update_dpp(0, y, 0x141, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(0, x, 0x140, 0xf, 0xf, false);  // row_mirror
+  y |= __builtin_amdgcn_update_dpp(0, y, 0x140, 0xf, 0xf, false);
+  a = (uint32_t)__builtin_amdgcn_readlane(x, 0);
+  o = (uint32_t)__builtin_amdgcn_readlane(y, 0);
+}
+
 struct SelShared {
   uint32_t red[2][16];  // per-wave AND / OR
   int wsum[2][16];      // per-wave scan totals
@@ -536,73 +574,108 @@ struct SelShared {
 template <int NT>
 __device__ __forceinline__ void block_scan2(int x, int y, int& xb, int& yb, int& xt, int& yt, SelShared& sh) {
   constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int xi = wave_incl_scan(x), yi = wave_incl_scan(y);
   if (lane == 63) {
     sh.wsum[0][wave] = xi;
     sh.wsum[1][wave] = yi;
   }
   lds_barrier();
-  xb = xi - x;
-  yb = yi - y;
-  xt = 0;
-  yt = 0;
-#pragma unroll
-  for (int w = 0; w < NW; w++) {
-    const int a = sh.wsum[0][w], b = sh.wsum[1][w];
-    xb += w < wave ? a : 0;
-    yb += w < wave ? b : 0;
-    xt += a;
-    yt += b;
-  }
+  int xw, yw;
+  waves_prefix<NW>(sh.wsum[0], wave, xw, xt);
+  waves_prefix<NW>(sh.wsum[1], wave, yw, yt);
+  xb = xw + xi - x;
+  yb = yw + yi - y;
 }
 
-// Float4 groups per thread when n scores are split over NT threads: a power
-// of two, so thread t owns positions [4*R*t, 4*R*t + 4*R).
-template <int NT>
-__device__ __forceinline__ int sel_groups(int n) {
-  const int g = (n + 4 * NT - 1) / (4 * NT);
-  return g <= 1 ? 1 : 1 << (32 - __clz(g - 1));
-}
-
-// Position e of a selection over n scores in the transposed layout: float4
-// group q of thread t sits at float4 index q * NT + t, so the lanes of a wave
-// read consecutive 16-byte words (no LDS bank conflicts) while every thread
-// still owns a contiguous range of positions.
-template <int NT>
-__device__ __forceinline__ int sel_slot(int e, int rgroups) {
-  const int g = e >> 2;
-  const int t = g / rgroups, q = g - t * rgroups;  // rgroups is a power of two
-  return ((q * NT + t) << 2) | (e & 3);
-}
-
-// Top-k (k <= n) of n scores; emit(pos, e, value) for each winner e with pos
-// its rank in position order.  TR: src holds the order keys of the scores
-// (order_key) in the transposed layout (sel_slot), typically in LDS; else
-// src holds the fp32 scores in position order.  hist: 2 x 2048 ints.  All
-// NT threads.
-template <int NT, bool TR, typename Emit>
-__device__ __forceinline__ void select_topk(const void* src, int n, int k, int* hist, SelShared& sh,
-                                            Emit&& emit) {
+// One radix pass over the keys that match the threshold prefix so far:
+// histogram of the next digit, then the digit that holds the kk-th largest
+// key.  count_into(H) adds every matching key's digit to the LDS histogram
+// H; Hn (the other buffer) is cleared for the next pass.  Updates kk, mask,
+// prefix and lo (uniform); false once the threshold bin is taken whole.
+template <int NT, typename CountInto>
+__device__ __forceinline__ bool radix_pass(int p, int& kk, uint32_t& mask, uint32_t& prefix, int& lo, int* hist,
+                                           SelShared& sh, CountInto&& count_into) {
   constexpr int NW = NT / 64;
   constexpr int BPT = 2048 / NT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int R = sel_groups<NT>(n);
-  const int S = 4 * R;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int width = lo < 11 ? lo : 11;
+  const int shift = lo - width;
+  const int nb = 1 << width;
+  int* H = hist + (p & 1) * 2048;
+  count_into(H, shift, nb - 1);
+  int* Hn = hist + ((p + 1) & 1) * 2048;  // read last in pass p - 1, used by pass p + 1
+  for (int b = tid; b < 2048; b += NT) Hn[b] = 0;
+  lds_barrier();
+  // Thread t owns digits nb-1-BPT*t .. nb-BPT*(t+1) (descending).
+  int h[BPT];
+  int local = 0;
+#pragma unroll
+  for (int jj = 0; jj < BPT; jj++) {
+    const int d = nb - 1 - (BPT * tid + jj);
+    h[jj] = d >= 0 ? H[d] : 0;
+    local += h[jj];
+  }
+  const int incl = wave_incl_scan(local);
+  if (lane == 63) sh.wsum[p & 1][wave] = incl;
+  lds_barrier();
+  int below, total;
+  waves_prefix<NW>(sh.wsum[p & 1], wave, below, total);
+  const int before = below + incl - local;
+  if (before < kk && kk <= before + local) {
+    int acc = before;
+#pragma unroll
+    for (int jj = 0; jj < BPT; jj++) {
+      if (acc < kk && kk <= acc + h[jj]) {
+        sh.res[p & 1][0] = nb - 1 - (BPT * tid + jj);
+        sh.res[p & 1][1] = acc;
+        sh.res[p & 1][2] = h[jj];
+      }
+      acc += h[jj];
+    }
+  }
+  lds_barrier();
+  const int digit = __builtin_amdgcn_readfirstlane(sh.res[p & 1][0]);
+  const int above = __builtin_amdgcn_readfirstlane(sh.res[p & 1][1]);
+  const int count = __builtin_amdgcn_readfirstlane(sh.res[p & 1][2]);
+  kk -= above;
+  prefix |= (uint32_t)digit << shift;
+  mask |= (uint32_t)(nb - 1) << shift;
+  lo = shift;
+  return count != kk;
+}
+
+// Bits every key shares (a = AND, o = OR): the threshold search starts below them.
+__device__ __forceinline__ void common_prefix(uint32_t a, uint32_t o, uint32_t& mask, uint32_t& prefix, int& lo) {
+  const uint32_t diff = a ^ o;
+  lo = diff == 0u ? 0 : 32 - __clz(diff);  // bits below lo still differ
+  mask = lo == 32 ? 0u : ~((1u << lo) - 1u);
+  prefix = a & mask;
+}
+
+// Top-k (k < n) of n fp32 scores read from global memory in every phase (for
+// candidate lists too long to hold in registers); emit(pos, e, value) for
+// each winner e with pos its rank in position order.  hist: 2 x 2048 ints.
+// Thread t walks the contiguous positions [4*R*t, 4*R*t + 4*R).
+template <int NT, typename Emit>
+__device__ __forceinline__ void select_topk_global(const float* src, int n, int k, int* hist, SelShared& sh,
+                                                   Emit&& emit) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = (n + 4 * NT - 1) / (4 * NT);
+  const int S = 4 * (g4 <= 1 ? 1 : 1 << (32 - __clz(g4 - 1)));
   const int beg = min(n, tid * S), end = min(n, beg + S);
   const int cnt = end - beg;
-  // keys of the four positions beg + j .. beg + j + 3 of this thread
   auto group = [&](int j) __attribute__((always_inline)) {
-    if constexpr (TR) {
-      return *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(src) + 4 * ((j >> 2) * NT + tid));
-    } else {
-      const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + beg + j);
-      return make_uint4(order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w));
-    }
+    const float4 v = *reinterpret_cast<const float4*>(src + beg + j);
+    return make_uint4(order_key(v.x), order_key(v.y), order_key(v.z), order_key(v.w));
   };
 
   uint32_t a = 0xFFFFFFFFu, o = 0u;
-#pragma unroll 4
+#pragma unroll 2
   for (int j = 0; j < cnt; j += 4) {
     const uint4 v = group(j);
     const uint32_t q[4] = {v.x, v.y, v.z, v.w};
@@ -619,77 +692,26 @@ __device__ __forceinline__ void select_topk(const void* src, int n, int k, int* 
   }
   for (int b = tid; b < 2048; b += NT) hist[b] = 0;
   lds_barrier();
-  a = 0xFFFFFFFFu;
-  o = 0u;
-#pragma unroll
-  for (int w = 0; w < NW; w++) {
-    a &= sh.red[0][w];
-    o |= sh.red[1][w];
-  }
-  // Invariant: the kk-th largest key matches `prefix` under `mask`, and at
-  // least kk keys do.
-  int kk = k;
-  uint32_t mask = 0xFFFFFFFFu, prefix = a;
-  const uint32_t diff = a ^ o;
-  int lo = diff == 0u ? 0 : 32 - __clz(diff);  // bits below lo still differ
-  if (lo > 0) {
-    mask = lo == 32 ? 0u : ~((1u << lo) - 1u);
-    prefix = a & mask;
-  }
+  waves_and_or<NW>(sh.red, a, o);
+  int kk = k, lo;
+  uint32_t mask, prefix;
+  common_prefix(a, o, mask, prefix, lo);
   for (int p = 0; lo > 0; p++) {
-    const int width = lo < 11 ? lo : 11;
-    const int shift = lo - width;
-    const int nb = 1 << width;
-    int* H = hist + (p & 1) * 2048;
-#pragma unroll 4
-    for (int j = 0; j < cnt; j += 4) {
-      const uint4 v = group(j);
-      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+    auto count_into = [&](int* H, int shift, uint32_t dmask) __attribute__((always_inline)) {
+#pragma unroll 2
+      for (int j = 0; j < cnt; j += 4) {
+        const uint4 v = group(j);
+        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int c = 0; c < 4; c++)
-        if (j + c < cnt && (q[c] & mask) == prefix) atomicAdd(&H[(q[c] >> shift) & (nb - 1)], 1);
-    }
-    int* Hn = hist + ((p + 1) & 1) * 2048;  // read last in pass p - 1, used by pass p + 1
-    for (int b = tid; b < 2048; b += NT) Hn[b] = 0;
-    lds_barrier();
-    // Thread t owns digits nb-1-BPT*t .. nb-BPT*(t+1) (descending).
-    int h[BPT];
-    int local = 0;
-#pragma unroll
-    for (int jj = 0; jj < BPT; jj++) {
-      const int d = nb - 1 - (BPT * tid + jj);
-      h[jj] = d >= 0 ? H[d] : 0;
-      local += h[jj];
-    }
-    const int incl = wave_incl_scan(local);
-    if (lane == 63) sh.wsum[p & 1][wave] = incl;
-    lds_barrier();
-    int before = incl - local;
-#pragma unroll
-    for (int w = 0; w < NW; w++) before += w < wave ? sh.wsum[p & 1][w] : 0;
-    if (before < kk && kk <= before + local) {
-      int acc = before;
-#pragma unroll
-      for (int jj = 0; jj < BPT; jj++) {
-        if (acc < kk && kk <= acc + h[jj]) {
-          sh.res[p & 1][0] = nb - 1 - (BPT * tid + jj);
-          sh.res[p & 1][1] = acc;
-          sh.res[p & 1][2] = h[jj];
-        }
-        acc += h[jj];
+        for (int c = 0; c < 4; c++)
+          if (j + c < cnt && (q[c] & mask) == prefix) atomicAdd(&H[(q[c] >> shift) & dmask], 1);
       }
-    }
-    lds_barrier();
-    const int digit = sh.res[p & 1][0], above = sh.res[p & 1][1], count = sh.res[p & 1][2];
-    kk -= above;
-    prefix |= (uint32_t)digit << shift;
-    mask |= (uint32_t)(nb - 1) << shift;
-    lo = shift;
-    if (count == kk) break;  // the whole threshold bin wins
+    };
+    if (!radix_pass<NT>(p, kk, mask, prefix, lo, hist, sh, count_into)) break;
   }
 
   int g = 0, q = 0;
-#pragma unroll 4
+#pragma unroll 2
   for (int j = 0; j < cnt; j += 4) {
     const uint4 v = group(j);
     const uint32_t f[4] = {v.x, v.y, v.z, v.w};
@@ -702,7 +724,7 @@ __device__ __forceinline__ void select_topk(const void* src, int n, int k, int* 
   }
   int G, E, gt_total, eq_total;
   block_scan2<NT>(g, q, G, E, gt_total, eq_total, sh);
-#pragma unroll 4
+#pragma unroll 2
   for (int j = 0; j < cnt; j += 4) {
     const uint4 v = group(j);
     const uint32_t f[4] = {v.x, v.y, v.z, v.w};
@@ -1009,12 +1031,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
 }
 
 // ---------------------------------------------------------------------------
-// Final selection: one workgroup of 1024 threads per row that sees more than
-// k entries, over the row's staged candidates (in ascending index order).
+// Selection stage: one workgroup of 1024 threads per entry of the plan's
+// selection table, over candidates staged in ascending position order.
 // ---------------------------------------------------------------------------
 
 constexpr int kSelThreads = 1024;  // 16 waves: the phases are latency-bound, more waves hide it
-constexpr int kSelLdsCap = 32768;  // candidates a selection stages in LDS (128 KiB of keys)
+constexpr int kSelRegMax = 4 * 8 * kSelThreads;  // candidates held in registers (8 float4 per thread)
 
 struct SelectParams {
   const SelectEntry* rows;  // this pass's entries of the plan's selection table
@@ -1025,71 +1047,149 @@ struct SelectParams {
   int32_t k;
 };
 
-// CAP > 0: the candidates (n <= CAP) are staged once in LDS as order keys in
-// the transposed layout; CAP = 0: every phase reads them from the workspace.
-// An entry keeps the top min(k, n) of its candidates, either as a row's final
-// output or as indexed candidates for a later merge.
-template <int NT, int CAP>
-__global__ __launch_bounds__(NT) void select_kernel(SelectParams S) {
-  constexpr bool LDS = CAP > 0;
-  __shared__ int hist[2 * 2048];
+// Where an entry's winners go: a row of the outputs, or (for a later merge)
+// indexed candidates in the workspace.
+struct SelectDst {
+  int32_t* idx;
+  float* val;  // may be null for a final row without values
+  __device__ SelectDst(const SelectEntry& se, const SelectParams& S) {
+    if (se.dst_off < 0) {
+      idx = S.idx_out + (int64_t)se.row * S.k;
+      val = S.val_out ? S.val_out + (int64_t)se.row * S.k : nullptr;
+    } else {
+      idx = S.ws_idx + se.dst_off;
+      val = S.ws + se.dst_off;
+    }
+  }
+  __device__ void put(int pos, int32_t key, float v) const {
+    idx[pos] = key;
+    if (val) val[pos] = v;
+  }
+};
+
+// Up to 4*R*NT candidates: thread t loads positions [4R*t, 4R*t + 4R) once as
+// order keys (and key indices when indexed) into registers; the winners are
+// ranked into LDS and written out coalesced.
+template <int NT, int R>
+__global__ __launch_bounds__(NT) void select_reg_kernel(SelectParams S) {
+  constexpr int NW = NT / 64;
+  constexpr int SPT = 4 * R;
+  __shared__ __attribute__((aligned(16))) int hist[2 * 2048];  // the histograms, then the ranked winners
   __shared__ SelShared sh;
-  __shared__ __attribute__((aligned(16))) uint32_t cache[LDS ? CAP : 4];
   const SelectEntry se = S.rows[blockIdx.x];
   const int n = se.n;
-  const int kk = min(S.k, n);
+  const int k = min(S.k, n);
   const float* sc = S.ws + se.src_off;
   const int32_t* ix = S.ws_idx + se.src_off;
   const bool indexed = se.indexed != 0;
-  const int tid = threadIdx.x;
-  int32_t* oi = nullptr;
-  float* ov = nullptr;
-  float* dv = nullptr;
-  int32_t* di = nullptr;
-  if (se.dst_off < 0) {
-    oi = S.idx_out + (int64_t)se.row * S.k;
-    ov = S.val_out ? S.val_out + (int64_t)se.row * S.k : nullptr;
-  } else {
-    dv = S.ws + se.dst_off;
-    di = S.ws_idx + se.dst_off;
-  }
-  auto emit = [&](int pos, int e, float v) __attribute__((always_inline)) {
-    const int32_t key = indexed ? ix[e] : se.base + e;
-    if (oi) {
-      oi[pos] = key;
-      if (ov) ov[pos] = v;
-    } else {
-      dv[pos] = v;
-      di[pos] = key;
-    }
-  };
-  if (n <= kk) {  // every candidate is kept (a short last segment)
-    for (int e = tid; e < n; e += NT) emit(e, e, sc[e]);
+  const SelectDst dst(se, S);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (n <= k) {  // every candidate is kept (a short last segment)
+    for (int e = tid; e < n; e += NT) dst.put(e, indexed ? ix[e] : se.base + e, sc[e]);
     return;
   }
-  if constexpr (LDS) {
-    // Order keys in the transposed layout; eight 16-byte loads in flight per
-    // thread (addresses clamped into the 16-byte padded candidate region).
-    constexpr int STEP = NT * 4;
-    const int last = ((n + 3) & ~3) - 4;
-    const int rg = sel_groups<NT>(n);
-    for (int base = 0; base < n; base += 8 * STEP) {
-      float4 v[8];
+  const int beg = tid * SPT;
+  const int cnt = max(0, min(SPT, n - beg));
+  const bool full = (wave + 1) * 64 * SPT <= n;  // uniform: every position of this wave is a candidate
+
+  float4 v[R];
+  int4 w[R];
 #pragma unroll
-      for (int i = 0; i < 8; i++)
-        v[i] = *reinterpret_cast<const float4*>(sc + min(base + i * STEP + tid * 4, last));
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const int e = base + i * STEP + tid * 4;
-        if (e < n)
-          *reinterpret_cast<uint4*>(&cache[sel_slot<NT>(e, rg)]) =
-              make_uint4(order_key(v[i].x), order_key(v[i].y), order_key(v[i].z), order_key(v[i].w));
-      }
-    }
-    __syncthreads();
+  for (int i = 0; i < R; i++) {
+    const bool in = beg + 4 * i < n;  // the region is readable up to n rounded up to 4
+    v[i] = in ? *reinterpret_cast<const float4*>(sc + beg + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    w[i] = in && indexed ? *reinterpret_cast<const int4*>(ix + beg + 4 * i) : make_int4(0, 0, 0, 0);
   }
-  select_topk<NT, LDS>(LDS ? static_cast<const void*>(cache) : static_cast<const void*>(sc), n, kk, hist, sh,
-                       emit);
+  uint32_t q[SPT];  // order keys; 0 (below every finite score) past n
+  int32_t id[SPT];
+  uint32_t a = 0xFFFFFFFFu, o = 0u;
+#pragma unroll
+  for (int i = 0; i < R; i++) {
+    const float f[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    const int32_t g[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const int j = 4 * i + c;
+      const bool live = j < cnt;
+      q[j] = live ? order_key(f[c]) : 0u;
+      id[j] = indexed ? g[c] : se.base + beg + j;
+      a &= live ? q[j] : 0xFFFFFFFFu;
+      o |= q[j];
+    }
+  }
+  wave_and_or(a, o);
+  if (lane == 0) {
+    sh.red[0][wave] = a;
+    sh.red[1][wave] = o;
+  }
+  for (int b = tid; b < 2048; b += NT) hist[b] = 0;
+  lds_barrier();
+  waves_and_or<NW>(sh.red, a, o);
+  int kk = k, lo;
+  uint32_t mask, prefix;
+  common_prefix(a, o, mask, prefix, lo);
+  for (int p = 0; lo > 0; p++) {
+    auto count_into = [&](int* H, int shift, uint32_t dmask) __attribute__((always_inline)) {
+      if (full) {
+#pragma unroll
+        for (int j = 0; j < SPT; j++)
+          if ((q[j] & mask) == prefix) atomicAdd(&H[(q[j] >> shift) & dmask], 1);
+      } else {
+#pragma unroll
+        for (int j = 0; j < SPT; j++)
+          if (j < cnt && (q[j] & mask) == prefix) atomicAdd(&H[(q[j] >> shift) & dmask], 1);
+      }
+    };
+    if (!radix_pass<NT>(p, kk, mask, prefix, lo, hist, sh, count_into)) break;
+  }
+
+  // Keys above the threshold and keys equal to it, as bit masks over j.
+  uint32_t gm = 0u, em = 0u;
+#pragma unroll
+  for (int j = 0; j < SPT; j++) {
+    const uint32_t m = q[j] & mask;
+    gm |= (m > prefix ? 1u : 0u) << j;
+    em |= (m == prefix && (full || j < cnt) ? 1u : 0u) << j;
+  }
+  int G, E, gt_total, eq_total;
+  block_scan2<NT>(__builtin_popcount(gm), __builtin_popcount(em), G, E, gt_total, eq_total, sh);
+  int* rank_idx = hist;  // the histograms are no longer read
+  float* rank_val = reinterpret_cast<float*>(hist + 2048);
+#pragma unroll
+  for (int j = 0; j < SPT; j++) {
+    const bool gt = (gm >> j) & 1u, eq = (em >> j) & 1u;
+    if (gt || (eq && E < kk)) {
+      const int pos = G + min(E, kk);
+      rank_idx[pos] = id[j];
+      rank_val[pos] = key_value(q[j]);
+    }
+    G += gt ? 1 : 0;
+    E += eq ? 1 : 0;
+  }
+  lds_barrier();
+  for (int e = tid; e < k; e += NT) dst.put(e, rank_idx[e], rank_val[e]);
+}
+
+// Longer candidate lists: every phase re-reads the scores from the workspace.
+template <int NT>
+__global__ __launch_bounds__(NT) void select_global_kernel(SelectParams S) {
+  __shared__ int hist[2 * 2048];
+  __shared__ SelShared sh;
+  const SelectEntry se = S.rows[blockIdx.x];
+  const int n = se.n;
+  const int k = min(S.k, n);
+  const float* sc = S.ws + se.src_off;
+  const int32_t* ix = S.ws_idx + se.src_off;
+  const bool indexed = se.indexed != 0;
+  const SelectDst dst(se, S);
+  if (n <= k) {
+    for (int e = threadIdx.x; e < n; e += NT) dst.put(e, indexed ? ix[e] : se.base + e, sc[e]);
+    return;
+  }
+  select_topk_global<NT>(sc, n, k, hist, sh, [&](int pos, int e, float v) __attribute__((always_inline)) {
+    dst.put(pos, indexed ? ix[e] : se.base + e, v);
+  });
 }
 
 // Workgroups of `kernel` that the current device holds at once (all CUs),
@@ -1197,9 +1297,11 @@ int launch_select(const RunArgs& a) {
   auto pass = [&](const SelectEntry* rows, int count, int max_n) {
     S.rows = rows;
     const dim3 grid(count);
-    if (max_n <= kSelSegment) return launch(select_kernel<kSelThreads, kSelSegment>, grid, block, st, S);
-    if (max_n <= kSelLdsCap) return launch(select_kernel<kSelThreads, kSelLdsCap>, grid, block, st, S);
-    return launch(select_kernel<kSelThreads, 0>, grid, block, st, S);
+    if (max_n <= kSelRegMax / 8) return launch(select_reg_kernel<kSelThreads, 1>, grid, block, st, S);
+    if (max_n <= kSelRegMax / 4) return launch(select_reg_kernel<kSelThreads, 2>, grid, block, st, S);
+    if (max_n <= kSelRegMax / 2) return launch(select_reg_kernel<kSelThreads, 4>, grid, block, st, S);
+    if (max_n <= kSelRegMax) return launch(select_reg_kernel<kSelThreads, 8>, grid, block, st, S);
+    return launch(select_global_kernel<kSelThreads>, grid, block, st, S);
   };
   hipError_t e = pass(table, h->n_select, h->max_cand);
   if (e == hipSuccess && h->n_select2 > 0) e = pass(table + h->n_select, h->n_select2, h->max_cand2);

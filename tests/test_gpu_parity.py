@@ -124,6 +124,11 @@ LONG = {
                                     sparse_mode=3),
     "long_rt1_fp8": synth.small(qk=synth.FP8, batch=12, s1=1, aslk=[60000 + 1111 * i for i in range(12)],
                                  block_size=64, sparse_count=200),
+    # merges of 5, 13 and 18 segments' winners (k = 2048): 10240, 26624 and 36864 candidates,
+    # i.e. the 4- and 8-group register selections and the re-reading one
+    "long_merge_r4": synth.small(batch=2, s1=1, aslk=[40000, 38500], block_size=64, sparse_count=2048),
+    "long_merge_r8": synth.small(batch=1, s1=1, aslk=[100000], block_size=128, sparse_count=2048),
+    "long_merge_global": synth.small(batch=1, s1=1, aslk=[140000], block_size=128, sparse_count=2048)
 }
 
 
@@ -140,7 +145,7 @@ def test_parity_long_rows(ora, name):
     assert int(vis.max()) > 8192  # rows selected in two passes (segments, then a merge)
     log("case %s: rows=%d k=%d chunk=%d" % (name, rows, k, ix.info.keys_per_chunk))
     dev = device_inputs(inp)
-    dump_rows = 2
+    dump_rows = min(2, rows)
     cols = int(vis[:dump_rows].max())
     gidx, gval, dots, scores = ix.run_debug(dev["query"], dev["key"], dev["weights"], dev["q_scale"],
                                             dev["k_scale"], dev["block_table"], 0, dump_rows, cols)
@@ -159,7 +164,7 @@ def test_parity_long_rows(ora, name):
 
 
 LONG_DENSE = {
-    # every score staged: 8193..32768 candidates (LDS-staged selection) and beyond (tiles reread)
+    # every score staged: rows of 8193..40000 candidates (segment selections, then merges)
     "dense_rows_20k": synth.small(batch=2, s1=3, aslk=[20000, 9000], block_size=64, sparse_count=1500,
                                   sparse_mode=3),
     "dense_rows_40k": synth.small(batch=1, s1=3, aslk=[40000], block_size=128, sparse_count=300, sparse_mode=3),
