@@ -862,10 +862,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     kend = key0 + nkeys;
     fb = (int)__umulhi((uint32_t)key0, P.bs_magic);
     const int nblk = (int)__umulhi((uint32_t)(kend - 1), P.bs_magic) - fb + 1;
-    {
-      const int32_t* bt = P.block_table + (int64_t)batch * P.max_blocks + fb;
-      for (int t = tid; t < nblk; t += kScoreThreads) lds_bt[t] = bt[t];
-    }
+    // Block-table slice (nblk <= kMaxChunk / 16 + 2 <= 2 * kScoreThreads
+    // entries): loaded now, written to LDS once the query and weight loads
+    // below have been issued, so the three round trips overlap.
+    static_assert(kMaxChunk / 16 + 2 <= 2 * kScoreThreads, "two block-table entries per thread");
+    const int32_t* bt = P.block_table + (int64_t)batch * P.max_blocks + fb;
+    const int bt0 = tid < nblk ? bt[tid] : 0;
+    const int bt1 = tid + kScoreThreads < nblk ? bt[tid + kScoreThreads] : 0;
     rok = u < nrows;
     r = row0 + (rok ? u : 0);
     rvis = rok ? itb.vis[u] : 0;
@@ -898,7 +901,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
         }
       }
     }
-    lds_barrier();  // lds_bt ready; the row loads above stay in flight
+    if (tid < nblk) lds_bt[tid] = bt0;
+    if (tid + kScoreThreads < nblk) lds_bt[tid + kScoreThreads] = bt1;
+    lds_barrier();  // lds_bt ready
     issue(0);
     if (nkeys > SC) issue(1);
     return true;
