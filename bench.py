@@ -167,7 +167,8 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str) -> dict:
     res = {
         "workload": workload,
         "kernel_source_sha256_16": kernel_source_hash(),
-        "kernels": sorted(set(n.split("(")[0] for n in names)),
+        "kernels": sorted(set(n.replace("qli::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+                              for n in names)),
         "fetch_kib_per_launch_raw": f_score, "write_kib_per_launch_raw": w_score,
         "calibration": {"kernel": "torch.neg over %d MiB (reads and writes that much)" % (COPY_BYTES >> 20),
                         "fetch_kib_raw": f_neg, "write_kib_raw": w_neg,
