@@ -180,7 +180,11 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   // Chunk size.  Prefill items walk up to kMaxChunk entries in 64-entry
   // tiles.  Decode chunks are the smallest multiple of 128 entries for which
   // the items fit the decode kernel's resident workgroups on one MI355X
-  // (256 CUs x 3) in a single round.  Both write every score densely.
+  // (256 CUs x 3) in a single round.  When every group has the same rows and
+  // visible maximum (all items equal), a longer chunk is taken if it lowers
+  // the keys of the busiest CU, the items being dealt evenly over the CUs
+  // (e.g. 512 items of 512 keys, 2 per CU, rather than 688 of 384, 3 on
+  // most CUs).  Both write every score densely.
   const int k = p.sparse_count;
   int chunk = kMaxChunk;
   if (!prefill) {
@@ -191,6 +195,16 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
     };
     int c = 128;
     while (c < kMaxChunk && items_for(c) > kDecodeSlots) c += 128;
+    bool equal = !groups.empty();
+    for (const Group& g : groups)
+      equal = equal && g.batch >= 0 && g.nrows == groups[0].nrows && g.maxv == groups[0].maxv;
+    if (equal) {
+      auto busiest = [&](int cc) { return (items_for(cc) + kCUs - 1) / kCUs * cc; };
+      int best = c;
+      for (int cc = c + 128; cc <= kMaxChunk; cc += 128)
+        if (busiest(cc) < busiest(best)) best = cc;
+      c = best;
+    }
     chunk = c;
   }
 

@@ -17,7 +17,8 @@ constexpr int kHeads = 64;       // query heads (QLI-README 约束说明)
 constexpr int kDim = 128;        // head dim of query and key (约束说明)
 constexpr int kTileKeys = 64;    // keys per MFMA tile step (4 n-tiles of 16)
 constexpr int kMaxChunk = 4096;  // keys per work item, upper bound
-constexpr int kDecodeSlots = 768;         // decode workgroups resident at once on MI355X (256 CUs x 3)
+constexpr int kCUs = 256;                 // compute units of one MI355X
+constexpr int kDecodeSlots = 3 * kCUs;    // decode workgroups resident at once (3 per CU)
 constexpr int kMaxEntries = 1 << 22;      // compressed entries per sequence (exact reciprocal division)
 constexpr int kMaxItemRows = 4;           // rows carried inline by a decode item
 
