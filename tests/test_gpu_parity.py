@@ -59,6 +59,21 @@ SMALL = {
     # every batch alike: items addressed from their position
     "regular_causal_s3": synth.small(batch=5, s1=3, aslk=[3000] * 5, block_size=64, sparse_count=256, sparse_mode=3),
     "regular_s1_fp8": synth.small(qk=synth.FP8, batch=4, s1=1, aslk=[900] * 4, block_size=16, sparse_count=300),
+    # the remaining compression ratios and the largest block sizes (参数说明 cmp_ratio, 约束说明 block_size)
+    "bsnd_int8_cmp8_causal": synth.small(batch=2, s1=3, aslk=[9000, 3001], block_size=64, sparse_count=256,
+                                         sparse_mode=3, cmp_ratio=8),
+    "bsnd_int8_cmp16_mode0": synth.small(batch=3, s1=2, aslk=[20000, 7777, 15], block_size=32, sparse_count=200,
+                                         cmp_ratio=16),
+    "tnd_int8_cmp32_causal": synth.small(layout=synth.TND, batch=2, s1=10, aslq=[3, 10], aslk=[40000, 9000],
+                                         block_size=128, sparse_count=300, sparse_mode=3, cmp_ratio=32),
+    "bsnd_fp8_cmp64_causal": synth.small(qk=synth.FP8, batch=2, s1=2, aslk=[70000, 20000], block_size=64,
+                                         sparse_count=128, sparse_mode=3, cmp_ratio=64),
+    "bsnd_int8_cmp128_bs16": synth.small(batch=2, s1=1, aslk=[130000, 1000], block_size=16, sparse_count=100,
+                                         cmp_ratio=128),
+    "bsnd_int8_bs1024": synth.small(batch=2, s1=2, aslk=[5000, 2100], block_size=1024, sparse_count=512,
+                                    sparse_mode=3),
+    "bsnd_fp8_bs512_pad": synth.small(qk=synth.FP8, batch=2, s1=1, aslk=[3000, 1500], block_size=512,
+                                      sparse_count=700, stride_pad=64),
 }
 
 
@@ -79,7 +94,7 @@ def test_parity_small(ora, name):
 
 
 @pytest.mark.parametrize("name", ["bsnd_int8_causal_bs48_pad", "bsnd_int8_cmp4_bs16", "tnd_int8_prefill_mixed",
-                                  "bsnd_fp8_causal_s2"])
+                                  "bsnd_fp8_causal_s2", "bsnd_int8_cmp8_causal", "bsnd_int8_bs1024"])
 def test_debug_dump(ora, name):
     """Dots straight from the matrix cores (int8: bit-exact), scores within
     tolerance, and the selection equal to the stable top-k of the GPU's own
@@ -225,24 +240,27 @@ def test_repeat_runs_identical():
 
 @pytest.mark.parametrize("name", ["bsnd_int8_causal_bs48_pad"])
 def test_stages_compose(name):
-    """Scoring stage then selection stage, as two calls, gives qli_run's outputs;
-    also with two-pass selections of long rows."""
+    """Scoring stage then selection stage, as two calls, gives qli_run's outputs,
+    also for long rows (segment selections, then merges), from a workspace that
+    starts as garbage, and the selection stage alone gives them again."""
     import torch
     for inp in (synth.make_inputs(SMALL[name], 3), synth.make_inputs(LONG["long_rt2_causal"], 2)):
         dev = device_inputs(inp)
         a_idx, a_val, ix = run_gpu(inp, dev)
         b_idx, b_val = ix.alloc_outputs()
-        b_idx.fill_(7)
-        if b_val is not None:
-            b_val.fill_(7.0)
         args = (dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
                 b_idx, b_val)
-        ix.workspace.zero_()
+        if ix.workspace is not None:
+            ix.workspace.fill_(0x5A)
         ix.run_stage(*args, stages=1)
-        ix.run_stage(*args, stages=2)
-        torch.cuda.synchronize()
-        assert np.array_equal(a_idx, b_idx.cpu().numpy())
-        assert a_val is None or np.array_equal(a_val, b_val.cpu().numpy())
+        for rep in range(3):
+            b_idx.fill_(7)
+            if b_val is not None:
+                b_val.fill_(7.0)
+            ix.run_stage(*args, stages=2)
+            torch.cuda.synchronize()
+            assert np.array_equal(a_idx, b_idx.cpu().numpy()), "selection %d" % rep
+            assert a_val is None or np.array_equal(a_val, b_val.cpu().numpy()), "selection %d" % rep
 
 
 @pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
