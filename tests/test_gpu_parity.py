@@ -238,6 +238,40 @@ def test_repeat_runs_identical():
     assert np.array_equal(a_idx, b_idx) and np.array_equal(a_val, b_val)
 
 
+@pytest.mark.parametrize("case", ["regular_causal_s3", "long_rt2_causal"])
+def test_graph_replay(case):
+    """qli_run captured in a HIP graph (no host synchronisation, no memset
+    nodes) and replayed: every replay, with eager work in between, gives the
+    eager outputs.  Plan, workspace and outputs keep their addresses."""
+    import torch
+    inp = synth.make_inputs(SMALL[case] if case in SMALL else LONG[case], 5)
+    dev = device_inputs(inp)
+    a_idx, a_val, ix = run_gpu(inp, dev)
+    b_idx, b_val = ix.alloc_outputs()
+    args = (dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
+            b_idx, b_val)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ix.run(*args)  # first launches (occupancy queries) outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ix.run(*args)
+    for rep in range(4):
+        b_idx.fill_(-7)
+        if b_val is not None:
+            b_val.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(a_idx, b_idx.cpu().numpy()), "replay %d" % rep
+        assert a_val is None or np.array_equal(a_val, b_val.cpu().numpy()), "replay %d" % rep
+        ix.run(*args)  # eager work between replays
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("name", ["bsnd_int8_causal_bs48_pad"])
 def test_stages_compose(name):
     """Scoring stage then selection stage, as two calls, gives qli_run's outputs,
