@@ -214,6 +214,42 @@ int qli_run_stage(const qli_problem *p, const void *plan_host,
                   void *workspace, int32_t *sparse_indices,
                   float *sparse_values, int32_t stages, void *stream);
 
+/*
+ * Bounded decode: the indexer without a host plan, for serving loops that
+ * keep actual_seq_lengths_key on the device and capture the call in a graph
+ * once.  The page's metadata op runs on the device for the same reason
+ * (QLI-README 参数说明 "metadata"; the operator supports graph mode); here the
+ * launch geometry comes from a host bound on the key length alone, and the
+ * kernels read the lengths themselves.
+ *
+ * Scope: BSND query layout, S1 <= 4 query rows per batch, all of them active
+ * (no actual_seq_lengths_query).  Every other parameter as for qli_plan.
+ *
+ * qli_bounded_workspace -- workspace bytes that qli_run_bounded needs for
+ *   these problem sizes and any key lengths in [0, max_seq_len_key] original
+ *   tokens.  QLI_ERR_ARG if the bound breaks a constraint (it must be >= 0,
+ *   its compressed entries must fit max_blocks_per_seq blocks),
+ *   QLI_ERR_UNSUPPORTED outside the scope above.
+ *
+ * qli_run_bounded -- the same outputs as qli_plan + qli_run would give for
+ *   actual_seq_lengths_key = aslk_dev[0..B) (device int32; each value is
+ *   clamped to [0, max_seq_len_key], so reads stay within the bound).
+ *   Stream-ordered, no host synchronisation, no host reads of device data:
+ *   a graph captured once replays correctly after aslk_dev (or any input)
+ *   changes.  workspace: qli_bounded_workspace bytes, 16-byte aligned.
+ *   Other arguments, alignment and the output contract as for qli_run.
+ */
+int qli_bounded_workspace(const qli_problem *p, int64_t max_seq_len_key,
+                          size_t *workspace_bytes);
+
+int qli_run_bounded(const qli_problem *p, int64_t max_seq_len_key,
+                    const int32_t *aslk_dev, const void *query,
+                    const void *key, const void *weights,
+                    const void *q_scale, const void *k_scale,
+                    const int32_t *block_table, void *workspace,
+                    int32_t *sparse_indices, float *sparse_values,
+                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

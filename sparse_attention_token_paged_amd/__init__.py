@@ -25,7 +25,8 @@ SCALE_F16, SCALE_F32 = 0, 1
 LAYOUT_BSND, LAYOUT_TND = 0, 1
 INT64_MAX = (1 << 63) - 1
 
-EXPORTED = ("qli_status_string", "qli_plan", "qli_plan_info_get", "qli_run", "qli_run_debug", "qli_run_stage")
+EXPORTED = ("qli_status_string", "qli_plan", "qli_plan_info_get", "qli_run", "qli_run_debug", "qli_run_stage",
+            "qli_bounded_workspace", "qli_run_bounded")
 
 c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
@@ -88,6 +89,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.qli_run_debug.restype = ctypes.c_int
         lib.qli_run_stage.argtypes = [ctypes.POINTER(Problem), c_p, c_p] + [c_p] * 9 + [c_i32, c_p]
         lib.qli_run_stage.restype = ctypes.c_int
+        lib.qli_bounded_workspace.argtypes = [ctypes.POINTER(Problem), c_i64, ctypes.POINTER(c_sz)]
+        lib.qli_bounded_workspace.restype = ctypes.c_int
+        lib.qli_run_bounded.argtypes = [ctypes.POINTER(Problem), c_i64] + [c_p] * 10 + [c_p]
+        lib.qli_run_bounded.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -170,6 +175,54 @@ def qli_run_debug(problem: Problem, plan_host, plan_dev, query, key, weights, q_
 def current_stream() -> int:
     import torch
     return torch.cuda.current_stream().cuda_stream
+
+
+def qli_bounded_workspace(problem: Problem, max_seq_len_key: int):
+    """Returns (status, workspace bytes) for qli_run_bounded."""
+    ws = c_sz(0)
+    rc = load().qli_bounded_workspace(ctypes.byref(problem), int(max_seq_len_key), ctypes.byref(ws))
+    return rc, int(ws.value)
+
+
+def qli_run_bounded(problem: Problem, max_seq_len_key: int, aslk_dev, query, key, weights, q_scale, k_scale,
+                    block_table, workspace, sparse_indices, sparse_values, stream=None) -> int:
+    return load().qli_run_bounded(ctypes.byref(problem), int(max_seq_len_key), _addr(aslk_dev), _addr(query),
+                                  _addr(key), _addr(weights), _addr(q_scale), _addr(k_scale),
+                                  _addr(block_table), _addr(workspace), _addr(sparse_indices),
+                                  _addr(sparse_values), stream)
+
+
+class BoundedIndexer:
+    """Bounded decode: no host plan; the key lengths stay on the device and
+    may change between calls (or graph replays) up to max_seq_len_key.
+    Holds the problem, the bound and a workspace (torch; marshalling only)."""
+
+    def __init__(self, problem: dict, max_seq_len_key: int, device: str = "cuda"):
+        import torch
+        self.problem = Problem.from_dict(problem)
+        self.max_seq_len_key = int(max_seq_len_key)
+        rc, ws = qli_bounded_workspace(self.problem, self.max_seq_len_key)
+        if rc != QLI_OK:
+            raise QliError(rc, "qli_bounded_workspace")
+        self.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=device) if ws else None
+        self.device = device
+
+    def alloc_outputs(self):
+        import torch
+        rows = self.problem.batch * self.problem.s1
+        k = self.problem.sparse_count
+        idx = torch.empty((rows, k), dtype=torch.int32, device=self.device)
+        val = torch.empty((rows, k), dtype=torch.float32, device=self.device) if self.problem.return_value else None
+        return idx, val
+
+    def run(self, aslk_dev, query, key, weights, q_scale, k_scale, block_table, out_idx, out_val,
+            stream: Optional[int] = None):
+        st = current_stream() if stream is None else stream
+        rc = qli_run_bounded(self.problem, self.max_seq_len_key, aslk_dev, query, key, weights, q_scale, k_scale,
+                             block_table, self.workspace, out_idx, out_val, st)
+        if rc != QLI_OK:
+            raise QliError(rc, "qli_run_bounded")
+        return out_idx, out_val
 
 
 class Indexer:

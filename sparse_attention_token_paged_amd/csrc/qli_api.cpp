@@ -59,20 +59,6 @@ int validate_problem(const qli_problem* p) {
   return QLI_OK;
 }
 
-// Visible compressed entries of query i (of s1b) in a batch with skb original
-// key tokens.  QLI-README 参数说明: cmp_ratio compresses the key, sparse_mode
-// 0 is no mask and 3 the bottom-right-aligned causal mask.  Reading: only
-// floor(skb / cmp) whole entries exist; query i sits at token position
-// skb - s1b + i and sees entry j once all of its tokens [j*cmp, (j+1)*cmp)
-// are at or before that position.
-int64_t visible_entries(int mode, int cmp, int64_t skb, int64_t s1b, int64_t i) {
-  const int64_t stored = skb / cmp;
-  if (mode == 0) return stored;
-  const int64_t through = skb - s1b + i + 1;  // tokens at or before the query
-  if (through <= 0) return 0;
-  return std::min(through / cmp, stored);
-}
-
 constexpr uint32_t kFnvPrime = 16777619u;
 
 uint64_t fnv_mix(uint64_t h, int64_t v) {
@@ -104,6 +90,30 @@ struct Built {
 };
 
 int64_t align16(int64_t v) { return (v + 15) & ~int64_t(15); }
+
+// Decode chunk for row groups with visible maxima maxv (all alike when
+// equal): the smallest multiple of 128 entries for which the items fit the
+// decode kernel's resident workgroups on one MI355X (256 CUs x 3) in a
+// single round; for equal groups, a longer chunk if it lowers the keys of the
+// busiest CU, the items being dealt evenly over the CUs (e.g. 512 items of
+// 512 keys, 2 per CU, rather than 688 of 384, 3 on most CUs).
+int decode_chunk(const std::vector<int32_t>& maxv, bool equal) {
+  auto items_for = [&](int c) {
+    int64_t n = 0;
+    for (int32_t m : maxv) n += (m + c - 1) / c;
+    return n;
+  };
+  int c = 128;
+  while (c < kMaxChunk && items_for(c) > kDecodeSlots) c += 128;
+  if (equal) {
+    auto busiest = [&](int cc) { return (items_for(cc) + kCUs - 1) / kCUs * cc; };
+    int best = c;
+    for (int cc = c + 128; cc <= kMaxChunk; cc += 128)
+      if (busiest(cc) < busiest(best)) best = cc;
+    c = best;
+  }
+  return c;
+}
 
 int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, Built& out) {
   const bool bsnd = p.layout_query == QLI_LAYOUT_BSND;
@@ -178,34 +188,17 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   }
 
   // Chunk size.  Prefill items walk up to kMaxChunk entries in 64-entry
-  // tiles.  Decode chunks are the smallest multiple of 128 entries for which
-  // the items fit the decode kernel's resident workgroups on one MI355X
-  // (256 CUs x 3) in a single round.  When every group has the same rows and
-  // visible maximum (all items equal), a longer chunk is taken if it lowers
-  // the keys of the busiest CU, the items being dealt evenly over the CUs
-  // (e.g. 512 items of 512 keys, 2 per CU, rather than 688 of 384, 3 on
-  // most CUs).  Both write every score densely.
+  // tiles; decode chunks follow decode_chunk.  Both write every score densely.
   const int k = p.sparse_count;
   int chunk = kMaxChunk;
   if (!prefill) {
-    auto items_for = [&](int c) {
-      int64_t n = 0;
-      for (const Group& g : groups) n += (g.maxv + c - 1) / c;
-      return n;
-    };
-    int c = 128;
-    while (c < kMaxChunk && items_for(c) > kDecodeSlots) c += 128;
+    std::vector<int32_t> maxv;
     bool equal = !groups.empty();
-    for (const Group& g : groups)
+    for (const Group& g : groups) {
+      maxv.push_back(g.maxv);
       equal = equal && g.batch >= 0 && g.nrows == groups[0].nrows && g.maxv == groups[0].maxv;
-    if (equal) {
-      auto busiest = [&](int cc) { return (items_for(cc) + kCUs - 1) / kCUs * cc; };
-      int best = c;
-      for (int cc = c + 128; cc <= kMaxChunk; cc += 128)
-        if (busiest(cc) < busiest(best)) best = cc;
-      c = best;
     }
-    chunk = c;
+    chunk = decode_chunk(maxv, equal);
   }
 
   // Per-row workspace offsets.  A row that sees more than k entries stages
@@ -355,7 +348,7 @@ bool plan_matches(const qli_problem* p, const void* plan_host) {
 
 int check_run_args(const RunArgs& a) {
   const PlanHeader* h = a.hdr;
-  if (!a.plan_dev) return QLI_ERR_ARG;
+  if (!a.plan_dev && !a.aslk) return QLI_ERR_ARG;  // a plan, or bounded decode
   if (h->rows == 0) return QLI_OK;
   if (!a.sparse_indices) return QLI_ERR_ARG;
   if (a.p->return_value && !a.sparse_values) return QLI_ERR_ARG;
@@ -366,7 +359,7 @@ int check_run_args(const RunArgs& a) {
   // weights / q_scale, plan and workspace; the element size elsewhere.
   auto aligned = [](const void* ptr, uintptr_t n) { return ((uintptr_t)ptr % n) == 0; };
   const uintptr_t sb = a.p->scale_dtype == QLI_SCALE_F16 ? 2 : 4;
-  if (!aligned(a.plan_dev, 16) || !aligned(a.workspace, 16) || !aligned(a.query, 16) ||
+  if ((a.plan_dev && !aligned(a.plan_dev, 16)) || !aligned(a.workspace, 16) || !aligned(a.query, 16) ||
       !aligned(a.key, 16) || !aligned(a.weights, 4 * sb) || !aligned(a.q_scale, 4 * sb) ||
       !aligned(a.k_scale, sb) || !aligned(a.block_table, 4) || !aligned(a.sparse_indices, 4) ||
       !aligned(a.sparse_values, 4))
@@ -443,6 +436,58 @@ QLI_EXPORT int qli_plan_info_get(const void* plan_host, qli_plan_info* info) {
   return QLI_OK;
 }
 
+// Launch geometry of bounded decode (no plan): the regular decode mapping
+// over B batches of S1 rows and nmax = max_len / cmp_ratio entries (at least
+// one item per batch, so rows that see nothing are still padded); row r's
+// scores at element r * stride when it may see more than k entries, nseg
+// segments per row, merge candidates at merge_base + r * mstride.
+struct Bounded {
+  PlanHeader h;
+  int64_t stride, mstride, merge_base;
+  int32_t nseg;
+};
+
+int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
+  if (max_len < 0) return QLI_ERR_ARG;
+  if (p.layout_query != QLI_LAYOUT_BSND || p.s1 > kMaxItemRows) return QLI_ERR_UNSUPPORTED;
+  const int64_t nmax = max_len / p.cmp_ratio;
+  if (nmax >= kMaxEntries) return QLI_ERR_SIZE;
+  if ((nmax + p.block_size - 1) / p.block_size > p.max_blocks_per_seq) return QLI_ERR_ARG;
+  std::memset(&g, 0, sizeof(g));
+  PlanHeader& h = g.h;
+  const int64_t rows = (int64_t)p.batch * p.s1;
+  const int k = p.sparse_count;
+  h.rows = rows;
+  h.kind = kKindDecode;
+  h.rows_per_item = p.s1 <= 1 ? 1 : (p.s1 <= 2 ? 2 : 4);
+  if (rows == 0) return QLI_OK;
+  h.chunk = decode_chunk(std::vector<int32_t>(p.batch, (int32_t)nmax), true);
+  h.reg_chunks = (int32_t)std::max<int64_t>(1, (nmax + h.chunk - 1) / h.chunk);
+  h.reg_rows = p.s1;
+  h.reg_maxv = (int32_t)nmax;
+  const int64_t items = (int64_t)p.batch * h.reg_chunks;
+  if (items > INT32_MAX) return QLI_ERR_SIZE;
+  h.n_items = (int32_t)items;
+  if (nmax <= k) return QLI_OK;  // every row is written by the scoring kernel
+  auto pad4 = [](int64_t n) { return (n + 3) & ~int64_t(3); };
+  g.nseg = (int32_t)((nmax + kSelSegment - 1) / kSelSegment);
+  g.stride = pad4(nmax);
+  g.merge_base = rows * g.stride;
+  g.mstride = g.nseg > 1 ? pad4((int64_t)g.nseg * k) : 0;
+  const int64_t total = g.merge_base + rows * g.mstride;
+  if (rows * g.nseg > INT32_MAX) return QLI_ERR_SIZE;
+  h.n_select = (int32_t)(rows * g.nseg);
+  h.max_cand = (int32_t)std::min<int64_t>(nmax, kSelSegment);
+  if (g.nseg > 1) {
+    h.n_select2 = (int32_t)rows;
+    h.max_cand2 = (g.nseg - 1) * k + (int32_t)std::min<int64_t>(k, nmax - (int64_t)(g.nseg - 1) * kSelSegment);
+  }
+  h.ws_scores = total;
+  h.ws_index_offset = align16(total * 4);
+  h.workspace_bytes = g.nseg > 1 ? h.ws_index_offset + total * 4 : total * 4;
+  return QLI_OK;
+}
+
 static int run_common(const qli_problem* p, const void* plan_host, const void* plan_dev,
                       const void* query, const void* key, const void* weights,
                       const void* q_scale, const void* k_scale, const int32_t* block_table,
@@ -503,6 +548,67 @@ QLI_EXPORT int qli_run_stage(const qli_problem* p, const void* plan_host, const 
   return run_common(p, plan_host, plan_dev, query, key, weights, q_scale, k_scale, block_table,
                     workspace, sparse_indices, sparse_values, 0, 0, 0, nullptr, nullptr, false,
                     stages, stream);
+}
+
+QLI_EXPORT int qli_bounded_workspace(const qli_problem* p, int64_t max_seq_len_key, size_t* workspace_bytes) {
+  try {
+    int rc = validate_problem(p);
+    if (rc != QLI_OK) return rc;
+    if (!workspace_bytes) return QLI_ERR_ARG;
+    Bounded g;
+    rc = bounded_geometry(*p, max_seq_len_key, g);
+    if (rc != QLI_OK) return rc;
+    *workspace_bytes = (size_t)g.h.workspace_bytes;
+    return QLI_OK;
+  } catch (...) {
+    return QLI_ERR_SIZE;
+  }
+}
+
+QLI_EXPORT int qli_run_bounded(const qli_problem* p, int64_t max_seq_len_key, const int32_t* aslk_dev,
+                               const void* query, const void* key, const void* weights,
+                               const void* q_scale, const void* k_scale, const int32_t* block_table,
+                               void* workspace, int32_t* sparse_indices, float* sparse_values,
+                               void* stream) {
+  try {
+    int rc = validate_problem(p);
+    if (rc != QLI_OK) return rc;
+    Bounded g;
+    rc = bounded_geometry(*p, max_seq_len_key, g);
+    if (rc != QLI_OK) return rc;
+    if (g.h.rows == 0) return QLI_OK;
+    if (!aslk_dev || ((uintptr_t)aslk_dev % 4) != 0) return QLI_ERR_ARG;
+    RunArgs a;
+    a.p = p;
+    a.plan_dev = nullptr;
+    a.hdr = &g.h;
+    a.query = query;
+    a.key = key;
+    a.weights = weights;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.block_table = block_table;
+    a.workspace = workspace;
+    a.sparse_indices = sparse_indices;
+    a.sparse_values = p->return_value ? sparse_values : nullptr;
+    a.dump_row0 = a.dump_row1 = a.dump_cols = 0;
+    a.dots_out = nullptr;
+    a.scores_out = nullptr;
+    a.stream = stream;
+    a.aslk = aslk_dev;
+    a.max_len = max_seq_len_key;
+    a.stride = g.stride;
+    a.mstride = g.mstride;
+    a.merge_base = g.merge_base;
+    a.nseg = g.nseg;
+    rc = check_run_args(a);
+    if (rc != QLI_OK) return rc;
+    if (launch_score(a, false) != 0) return QLI_ERR_HIP;
+    if (g.h.n_select > 0 && launch_select(a) != 0) return QLI_ERR_HIP;
+    return QLI_OK;
+  } catch (...) {
+    return QLI_ERR_ARG;
+  }
 }
 
 QLI_EXPORT int qli_run_debug(const qli_problem* p, const void* plan_host, const void* plan_dev,

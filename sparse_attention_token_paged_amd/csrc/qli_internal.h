@@ -82,6 +82,23 @@ struct SelectEntry {
   int32_t indexed;  // 1: the candidates carry key indices (pass-2 merges)
 };
 constexpr int kSelSegment = 8192;  // candidates per first-pass selection of a long row
+
+// Visible compressed entries of query i (of s1b) in a batch with skb original
+// key tokens (QLI-README 参数说明 cmp_ratio and sparse_mode; the planner and
+// the bounded decode kernels both use it).  Only floor(skb / cmp) whole
+// entries exist; under mode 3 query i sits at token position skb - s1b + i
+// and sees entry j once all of its tokens [j*cmp, (j+1)*cmp) are at or
+// before that position.
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline int64_t visible_entries(int mode, int cmp, int64_t skb, int64_t s1b, int64_t i) {
+  const int64_t stored = skb / cmp;
+  if (mode == 0) return stored;
+  const int64_t through = skb - s1b + i + 1;  // tokens at or before the query
+  if (through <= 0) return 0;
+  return through / cmp < stored ? through / cmp : stored;
+}
 static_assert(sizeof(SelectEntry) == 32, "select table layout");
 
 struct Item {
@@ -122,6 +139,14 @@ struct RunArgs {
   void* dots_out;
   float* scores_out;
   void* stream;
+  // Bounded decode (no plan on the device; aslk != nullptr): the kernels read
+  // the key lengths, clamp them to max_len tokens and derive each item's rows
+  // and each selection from them.  Row r's scores sit at element r * stride,
+  // its merge candidates at merge_base + r * mstride; nseg segments per row.
+  const int32_t* aslk = nullptr;
+  int64_t max_len = 0;
+  int64_t stride = 0, mstride = 0, merge_base = 0;
+  int32_t nseg = 0;
 };
 int launch_score(const RunArgs& a, bool dump);
 int launch_select(const RunArgs& a);

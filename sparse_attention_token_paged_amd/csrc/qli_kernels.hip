@@ -62,6 +62,10 @@ struct ScoreParams {
   float* ws;
   int32_t* idx_out;
   float* val_out;
+  const int32_t* aslk;  // bounded decode: key lengths on the device (else null)
+  int64_t max_len;      //   clamp for them (original tokens)
+  int64_t bstride;      //   workspace elements per row
+  int32_t mode, cmp;    //   sparse_mode, cmp_ratio
   int64_t stride;
   int32_t block_size;
   int32_t max_blocks;
@@ -808,6 +812,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     }
   };
 
+  // Bounded decode: the rows of the current batch (key length skb) that see
+  // fewer than k entries get -1 / -inf in slots vis..k-1.
+  const bool bnd = P.aslk != nullptr;
+  int64_t skb = 0;
+  auto pad_bounded = [&]() __attribute__((always_inline)) {
+    for (int uu = 0; uu < nrows; uu++) {
+      const int64_t rr = row0 + uu;
+      const int vis = (int)visible_entries(P.mode, P.cmp, skb, nrows, uu);
+      for (int e = vis + tid; e < k; e += kScoreThreads) {
+        P.idx_out[rr * k + e] = -1;
+        if (P.val_out) P.val_out[rr * k + e] = -INFINITY;
+      }
+    }
+  };
+
   // Stage loader: wave w's load i fills stage bytes [(4i + w) * 1024, +1024),
   // lane l the 16 bytes at l*16: entry kk = 8(4i + w) + l/8, physical chunk
   // l%8 holding logical chunk (l%8) ^ ((kk>>1)&7) (conflict-free MFMA reads).
@@ -843,20 +862,27 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   // this wave's query fragments and w' = W * ScaleQ, and the loads of its
   // stages 0 and 1.  False for an item without keys (padding only).
   auto begin = [&](int pos) __attribute__((always_inline)) {
-    const Item& itb = P.items[pos];
+    const Item* itp = P.items + pos;  // no item table in bounded decode
     if (reg) {
       batch = pos / P.reg_chunks;
       key0 = (pos - batch * P.reg_chunks) * P.chunk;
       nkeys = min(P.chunk, P.reg_maxv - key0);
       row0 = batch * P.reg_rows;
       nrows = P.reg_rows;
+      if (bnd) {
+        // This batch's key length, clamped to the bound; its last row sees the most entries.
+        skb = min<int64_t>(max(P.aslk[batch], 0), P.max_len);
+        if (key0 == 0) pad_bounded();
+        nkeys = min(P.chunk, (int)visible_entries(P.mode, P.cmp, skb, nrows, nrows - 1) - key0);
+        if (nkeys <= 0) return false;  // uniform across the workgroup
+      }
     } else {
-      pad(itb);
-      batch = itb.batch;
-      key0 = itb.key0;
-      nkeys = itb.nkeys;
-      row0 = itb.row0;
-      nrows = itb.nrows;
+      pad(*itp);
+      batch = itp->batch;
+      key0 = itp->key0;
+      nkeys = itp->nkeys;
+      row0 = itp->row0;
+      nrows = itp->nrows;
       if (nkeys <= 0) return false;  // uniform across the workgroup
     }
     kend = key0 + nkeys;
@@ -871,8 +897,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     const int bt1 = tid + kScoreThreads < nblk ? bt[tid + kScoreThreads] : 0;
     rok = u < nrows;
     r = row0 + (rok ? u : 0);
-    rvis = rok ? itb.vis[u] : 0;
-    coff = rok ? itb.cand_off[u] : -1;
+    if (bnd) {
+      rvis = rok ? (int)visible_entries(P.mode, P.cmp, skb, nrows, u) : 0;
+      coff = rvis > k ? r * P.bstride + key0 : -1;
+    } else {
+      rvis = rok ? itp->vis[u] : 0;
+      coff = rok ? itp->cand_off[u] : -1;
+    }
     {
       const uint8_t* qrow = P.query + r * (kHeads * kDim);
   #pragma unroll
@@ -1031,7 +1062,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     lds_barrier();  // the slot is free for stage st + 3
   }
 
-  if (reg) pad(P.items[pos]);
+  if (reg && !bnd) pad(P.items[pos]);
   }  // rounds (the item's last barrier leaves the LDS free for the next one)
 }
 
@@ -1050,7 +1081,50 @@ struct SelectParams {
   int32_t* idx_out;
   float* val_out;
   int32_t k;
+  // Bounded decode (aslk != null): no table; workgroup w of pass 1 takes
+  // segment w % nseg of row w / nseg, workgroup r of pass 2 the merge of row r.
+  const int32_t* aslk;
+  int64_t max_len, stride, mstride, merge_base;
+  int32_t s1, mode, cmp, nseg, pass;
 };
+
+// The selection of this workgroup in bounded decode, from the row's key
+// length: false if there is none (the row sees at most k entries, or fewer
+// segments, or needs no merge).  Row r's scores sit at r * stride in key
+// order; segment s keeps its winners at merge_base + r * mstride + s * k, so
+// a row's merge candidates are contiguous (every segment but the last holds
+// kSelSegment >= k scores).
+__device__ __forceinline__ bool bounded_entry(const SelectParams& S, SelectEntry& se) {
+  const int w = (int)blockIdx.x;
+  const int r = S.pass == 1 ? w / S.nseg : w;
+  const int s = S.pass == 1 ? w - r * S.nseg : 0;
+  const int64_t skb = min<int64_t>(max(S.aslk[r / S.s1], 0), S.max_len);
+  const int vis = (int)visible_entries(S.mode, S.cmp, skb, S.s1, r % S.s1);
+  if (vis <= S.k) return false;
+  const int nsr = (vis + kSelSegment - 1) / kSelSegment;  // segments of this row
+  se.row = r;
+  se.base = 0;
+  se.indexed = 0;
+  se.dst_off = -1;
+  if (S.pass == 2) {
+    if (nsr == 1) return false;
+    se.src_off = S.merge_base + (int64_t)r * S.mstride;
+    se.n = (nsr - 1) * S.k + min(S.k, vis - (nsr - 1) * kSelSegment);
+    se.indexed = 1;
+    return true;
+  }
+  if (nsr == 1) {
+    se.src_off = (int64_t)r * S.stride;
+    se.n = vis;
+    return s == 0;
+  }
+  if (s >= nsr) return false;
+  se.src_off = (int64_t)r * S.stride + (int64_t)s * kSelSegment;
+  se.dst_off = S.merge_base + (int64_t)r * S.mstride + (int64_t)s * S.k;
+  se.n = min(kSelSegment, vis - s * kSelSegment);
+  se.base = s * kSelSegment;
+  return true;
+}
 
 // Where an entry's winners go: a row of the outputs, or (for a later merge)
 // indexed candidates in the workspace.
@@ -1081,7 +1155,12 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(SelectParams S) {
   constexpr int SPT = 4 * R;
   __shared__ __attribute__((aligned(16))) int hist[2 * 2048];  // the histograms, then the ranked winners
   __shared__ SelShared sh;
-  const SelectEntry se = S.rows[blockIdx.x];
+  SelectEntry se;
+  if (S.aslk) {
+    if (!bounded_entry(S, se)) return;  // uniform
+  } else {
+    se = S.rows[blockIdx.x];
+  }
   const int n = se.n;
   const int k = min(S.k, n);
   const float* sc = S.ws + se.src_off;
@@ -1181,7 +1260,12 @@ template <int NT>
 __global__ __launch_bounds__(NT) void select_global_kernel(SelectParams S) {
   __shared__ int hist[2 * 2048];
   __shared__ SelShared sh;
-  const SelectEntry se = S.rows[blockIdx.x];
+  SelectEntry se;
+  if (S.aslk) {
+    if (!bounded_entry(S, se)) return;  // uniform
+  } else {
+    se = S.rows[blockIdx.x];
+  }
   const int n = se.n;
   const int k = min(S.k, n);
   const float* sc = S.ws + se.src_off;
@@ -1250,8 +1334,15 @@ int launch_score(const RunArgs& a, bool dump) {
   const PlanHeader* h = a.hdr;
   if (h->n_items == 0) return 0;
   ScoreParams P{};
-  P.items = reinterpret_cast<const Item*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_items);
-  P.rinfo = reinterpret_cast<const RowInfo*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_rows);
+  if (a.plan_dev) {
+    P.items = reinterpret_cast<const Item*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_items);
+    P.rinfo = reinterpret_cast<const RowInfo*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_rows);
+  }
+  P.aslk = a.aslk;  // bounded decode (the header then describes the bound)
+  P.max_len = a.max_len;
+  P.bstride = a.stride;
+  P.mode = a.p->sparse_mode;
+  P.cmp = a.p->cmp_ratio;
   P.n_items = h->n_items;
   P.chunk = h->chunk;
   P.reg_chunks = h->reg_chunks;
@@ -1291,7 +1382,18 @@ int launch_select(const RunArgs& a) {
   const PlanHeader* h = a.hdr;
   if (h->n_select == 0) return 0;
   SelectParams S{};
-  const SelectEntry* table = reinterpret_cast<const SelectEntry*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_select);
+  const SelectEntry* table =
+      a.plan_dev ? reinterpret_cast<const SelectEntry*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_select)
+                 : nullptr;
+  S.aslk = a.aslk;
+  S.max_len = a.max_len;
+  S.stride = a.stride;
+  S.mstride = a.mstride;
+  S.merge_base = a.merge_base;
+  S.s1 = a.p->s1;
+  S.mode = a.p->sparse_mode;
+  S.cmp = a.p->cmp_ratio;
+  S.nseg = a.nseg;
   S.ws = static_cast<float*>(a.workspace);
   S.ws_idx = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + h->ws_index_offset);
   S.idx_out = a.sparse_indices;
@@ -1299,8 +1401,9 @@ int launch_select(const RunArgs& a) {
   S.k = a.p->sparse_count;
   const hipStream_t st = static_cast<hipStream_t>(a.stream);
   const dim3 block(kSelThreads);
-  auto pass = [&](const SelectEntry* rows, int count, int max_n) {
+  auto pass = [&](int which, const SelectEntry* rows, int count, int max_n) {
     S.rows = rows;
+    S.pass = which;
     const dim3 grid(count);
     if (max_n <= kSelRegMax / 8) return launch(select_reg_kernel<kSelThreads, 1>, grid, block, st, S);
     if (max_n <= kSelRegMax / 4) return launch(select_reg_kernel<kSelThreads, 2>, grid, block, st, S);
@@ -1308,8 +1411,8 @@ int launch_select(const RunArgs& a) {
     if (max_n <= kSelRegMax) return launch(select_reg_kernel<kSelThreads, 8>, grid, block, st, S);
     return launch(select_global_kernel<kSelThreads>, grid, block, st, S);
   };
-  hipError_t e = pass(table, h->n_select, h->max_cand);
-  if (e == hipSuccess && h->n_select2 > 0) e = pass(table + h->n_select, h->n_select2, h->max_cand2);
+  hipError_t e = pass(1, table, h->n_select, h->max_cand);
+  if (e == hipSuccess && h->n_select2 > 0) e = pass(2, table ? table + h->n_select : nullptr, h->n_select2, h->max_cand2);
   return e == hipSuccess ? 0 : (int)e;
 }
 

@@ -298,3 +298,56 @@ def test_empty_problem_runs_without_device(qli):
     rc, plan, ws = qli.qli_plan(prob, None, np.zeros(0, np.int32))
     assert rc == 0 and ws == 0
     assert qli.qli_run(prob, plan, 1 << 40, *([None] * 9)) == qli.QLI_OK
+
+
+# --- bounded decode (no host plan) --------------------------------------------
+def bounded_workspace_expected(p, max_len):
+    """Workspace of bounded decode, from its layout: rows that may see more than
+    k entries keep every score (16-byte aligned row stride); rows longer than one
+    selection segment also keep each segment's k winners for the merge, with
+    their key indices in a mirrored int32 region."""
+    rows, k = p["batch"] * p["s1"], p["sparse_count"]
+    nmax = max_len // p["cmp_ratio"]
+    if rows == 0 or nmax <= k:
+        return 0
+    pad4 = lambda n: (n + 3) // 4 * 4
+    nseg = -(-nmax // SEGMENT)
+    total = rows * pad4(nmax) + (rows * pad4(nseg * k) if nseg > 1 else 0)
+    return ((4 * total + 15) // 16 * 16) + 4 * total if nseg > 1 else 4 * total
+
+
+@pytest.mark.parametrize("s1,k,cmp,max_len", [(1, 512, 1, 1000), (4, 2048, 1, 8192), (2, 256, 4, 70000),
+                                                (3, 100, 1, 0), (1, 2048, 1, 140000)])
+def test_bounded_workspace(qli, s1, k, cmp, max_len):
+    spec = synth.small(batch=3, s1=s1, aslk=[max(max_len, 1)] * 3, block_size=64, sparse_count=k,
+                       sparse_mode=3, cmp_ratio=cmp)
+    p = synth.make_inputs(spec, 1)["problem"]
+    rc, ws = qli.qli_bounded_workspace(qli.Problem.from_dict(p), max_len)
+    assert rc == 0 and ws == bounded_workspace_expected(p, max_len)
+
+
+def test_bounded_rejects_without_launching(qli):
+    spec = synth.small(batch=2, s1=2, aslk=[5000, 5000], block_size=64, sparse_count=256, sparse_mode=3)
+    p = synth.make_inputs(spec, 1)["problem"]
+    prob = qli.Problem.from_dict(p)
+    bound = 5000
+    fake = 1 << 40  # never dereferenced: every call below fails validation first
+    args = [fake] * 10
+    assert qli.qli_bounded_workspace(prob, -1)[0] == qli.QLI_ERR_ARG
+    blocks = p["max_blocks_per_seq"]
+    assert qli.qli_bounded_workspace(prob, (blocks + 1) * 64)[0] == qli.QLI_ERR_ARG  # beyond the block table
+    tnd = qli.Problem.from_dict(dict(p, layout_query=synth.TND))
+    assert qli.qli_bounded_workspace(tnd, bound)[0] == qli.QLI_ERR_UNSUPPORTED
+    assert qli.qli_run_bounded(tnd, bound, *args) == qli.QLI_ERR_UNSUPPORTED
+    wide = qli.Problem.from_dict(dict(p, s1=5))
+    assert qli.qli_bounded_workspace(wide, bound)[0] == qli.QLI_ERR_UNSUPPORTED
+    a = list(args)
+    a[0] = None                                                     # actual_seq_lengths_key
+    assert qli.qli_run_bounded(prob, bound, *a) == qli.QLI_ERR_ARG
+    a = list(args)
+    a[8] = None                                                     # sparse_indices
+    assert qli.qli_run_bounded(prob, bound, *a) == qli.QLI_ERR_ARG
+    a = list(args)
+    a[1] = fake + 4                                                 # query not 16-byte aligned
+    assert qli.qli_run_bounded(prob, bound, *a) == qli.QLI_ERR_ARG
+    assert qli.qli_run_bounded(qli.Problem.from_dict(dict(p, sparse_mode=1)), bound, *args) == qli.QLI_ERR_ARG

@@ -319,3 +319,88 @@ def test_workload_full_size(ora, name):
             continue
         _, _, osc = ora.row_detail(inp, r, 0, v)
         check_row(r, v, k, gidx[r], gval[r], osc, rtol_of(inp))
+
+
+# --- bounded decode: no host plan, key lengths on the device -------------------
+BOUNDED = {
+    # (spec with every batch at the bound: the cache and block table hold that much; actual lengths)
+    "int8_s4_merges": (synth.small(batch=3, s1=4, aslk=[24000] * 3, block_size=64, sparse_count=2048,
+                                   sparse_mode=3), [20000, 5000, 0]),
+    "fp8_s1_mode0": (synth.small(qk=synth.FP8, batch=3, s1=1, aslk=[9000] * 3, block_size=64, sparse_count=300),
+                     [3000, 100, 9000]),
+    "int8_s2_cmp4": (synth.small(batch=2, s1=2, aslk=[40000] * 2, block_size=128, sparse_count=512,
+                                 sparse_mode=3, cmp_ratio=4), [40000, 39999]),
+    "int8_s3_short": (synth.small(batch=2, s1=3, aslk=[1500] * 2, block_size=32, sparse_count=256,
+                                  sparse_mode=3), [1500, 700]),
+}
+
+
+def bounded_case(name, seed=4):
+    import torch
+    spec, lens = BOUNDED[name]
+    inp = synth.make_inputs(spec, seed)
+    bound = int(spec.aslk[0])
+    dev = device_inputs(inp)
+    bix = qli_mod().BoundedIndexer(inp["problem"], bound)
+    return inp, dev, bix, bound, lens
+
+
+def qli_mod():
+    import sparse_attention_token_paged_amd as q
+    return q
+
+
+def planned(inp, dev, lens):
+    """qli_plan + qli_run for the same inputs with actual key lengths lens."""
+    sub = dict(inp, aslk=np.asarray(lens, dtype=np.int32))
+    idx, val, _ = run_gpu(sub, dev)
+    return idx, val
+
+
+@pytest.mark.parametrize("name", list(BOUNDED))
+def test_bounded_matches_planned(ora, name):
+    """qli_run_bounded gives exactly qli_run's outputs (same kernels, same
+    arithmetic; the lengths are read on the device), checked against the
+    oracle's structure too."""
+    import torch
+    inp, dev, bix, bound, lens = bounded_case(name)
+    log("bounded %s: bound %d lens %s" % (name, bound, lens))
+    aslk = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    idx, val = bix.alloc_outputs()
+    bix.run(aslk, dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
+            idx, val)
+    torch.cuda.synchronize()
+    p_idx, p_val = planned(inp, dev, lens)
+    assert np.array_equal(idx.cpu().numpy(), p_idx)
+    assert p_val is None or np.array_equal(val.cpu().numpy(), p_val)
+    p = inp["problem"]
+    vis = ora.row_visible(p["layout_query"], p["batch"], p["s1"], p["sparse_mode"], p["cmp_ratio"],
+                          inp["aslq"], np.asarray(lens, dtype=np.int32))
+    check_structure(idx.cpu().numpy(), None if val is None else val.cpu().numpy(), vis, p["sparse_count"])
+
+
+def test_bounded_graph_replay():
+    """qli_run_bounded captured once in a HIP graph, replayed after the device
+    key lengths change: every replay equals qli_plan + qli_run for the new
+    lengths (including a batch that sees nothing and one longer than a segment)."""
+    import torch
+    inp, dev, bix, bound, _ = bounded_case("int8_s4_merges", seed=6)
+    aslk = torch.tensor([bound] * inp["problem"]["batch"], dtype=torch.int32, device="cuda")
+    idx, val = bix.alloc_outputs()
+    args = (aslk, dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
+            idx, val)
+    bix.run(*args)  # first launches (occupancy queries) outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bix.run(*args)
+    for lens in ([24000, 24000, 24000], [9000, 0, 23999], [1, 2048, 12000], [3000, 17000, 8193]):
+        aslk.copy_(torch.tensor(lens, dtype=torch.int32))
+        idx.fill_(-7)
+        val.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        p_idx, p_val = planned(inp, dev, lens)
+        assert np.array_equal(idx.cpu().numpy(), p_idx), "lengths %s" % lens
+        assert np.array_equal(val.cpu().numpy(), p_val), "lengths %s" % lens
