@@ -272,17 +272,21 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     st = stream.cuda_stream
 
-    def region(n: int, stages: int, rotate: bool = True):
+    def region(n: int, stages: int, rotate: bool = True, launch=None):
         """Milliseconds per launch of n back-to-back launches, one event pair,
         and the host's enqueue time per launch in microseconds.  A spin
         kernel ahead of the start event keeps the GPU busy while the host
-        enqueues, so the pair times GPU execution, not the host."""
+        enqueues, so the pair times GPU execution, not the host.  launch(set)
+        replaces the planned run when given."""
         ev = Events(hip, 2)
         torch.cuda.synchronize()
         torch.cuda._sleep(int(spin_cycles_per_us * (1.5 * n * enqueue_us + 200.0)))
         assert hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), ctypes.c_void_p(st)) == 0
         t0 = time.perf_counter()
         for s_ in range(n):
+            if launch is not None:
+                launch(sets[s_ % R if rotate else 0])
+                continue
             ix.run_stage(*sets[s_ % R if rotate else 0], stages=stages, stream=st)
         host_us = (time.perf_counter() - t0) * 1e6 / n
         assert hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), ctypes.c_void_p(st)) == 0
@@ -318,6 +322,16 @@ def main() -> int:
     score_avg, _ = region(K, 1)       # scoring kernel alone
     select_avg = region(K, 2)[0] if info.select_rows > 0 else 0.0
     warm_ms, _ = region(K, 3, rotate=False)  # context only: one copy, inputs may hit in the caches
+    # Context only: bounded decode (no host plan; lengths read on the device), bound = the longest key.
+    bounded_ms = None
+    aslq = inp["aslq"]
+    if p["layout_query"] == 0 and 1 <= p["s1"] <= 4 and (aslq is None or all(int(v) == p["s1"] for v in aslq)):
+        bix = qli.BoundedIndexer(p, int(max(inp["aslk"])))
+        aslk_dev = torch.from_numpy(inp["aslk"].astype("int32")).cuda()
+        run_b = lambda t: bix.run(aslk_dev, *t, stream=st)
+        for s_ in range(3):
+            run_b(sets[s_ % R])
+        bounded_ms, _ = region(K, 3, launch=run_b)
 
     if args.calibrate_copy:
         # counter calibration: one elementwise kernel that reads and writes 256 MiB each
@@ -372,6 +386,7 @@ def main() -> int:
             "host_enqueue_us_per_step": round(host_us, 2),
             "cache_state": "every input cold: %d rotated copies of all inputs (%.1f MB each)" % (R, set_bytes / 1e6),
             "score_items": info.score_items, "select_rows": info.select_rows,
+            "bounded_decode_ms_per_step": None if bounded_ms is None else round(bounded_ms, 5),
         },
         "cpu_baseline": None,
     }
