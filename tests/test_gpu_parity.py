@@ -404,3 +404,56 @@ def test_bounded_graph_replay():
         p_idx, p_val = planned(inp, dev, lens)
         assert np.array_equal(idx.cpu().numpy(), p_idx), "lengths %s" % lens
         assert np.array_equal(val.cpu().numpy(), p_val), "lengths %s" % lens
+
+
+# --- seeded random problems -----------------------------------------------------
+def random_spec(i: int):
+    """A random small problem (seeded by i): dtype, layout, batch, ragged key
+    lengths (zeros included), query counts, compression, mode, block size,
+    sparse_count and stride padding, resampled until it has at most 300k
+    visible pairs (so the oracle scores every row quickly)."""
+    rng = np.random.default_rng(20260 + i)
+    while True:
+        qk = int(rng.choice([synth.INT8, synth.FP8]))
+        layout = int(rng.choice([synth.BSND, synth.TND], p=[0.7, 0.3]))
+        batch = int(rng.integers(1, 5))
+        cmp = int(rng.choice([1, 1, 2, 4, 8, 16]))
+        aslk = [int(rng.integers(0, 12000)) if rng.random() > 0.1 else 0 for _ in range(batch)]
+        kw = dict(qk=qk, layout=layout, batch=batch, aslk=aslk, cmp_ratio=cmp,
+                  sparse_mode=int(rng.choice([0, 3])), block_size=int(rng.choice([16, 32, 48, 64, 128, 256, 512])),
+                  sparse_count=int(rng.choice([1, 7, 64, 300, 1000, 2048])),
+                  stride_pad=int(rng.choice([0, 0, 16, 64])))
+        if layout == synth.BSND:
+            s1 = int(rng.integers(1, 9))
+            kw["s1"] = s1
+            if rng.random() < 0.3:
+                kw["aslq"] = [int(rng.integers(0, s1 + 1)) for _ in range(batch)]
+        else:
+            counts = [int(rng.integers(0, 40)) for _ in range(batch)]
+            kw["aslq"] = list(np.cumsum(counts))
+            kw["s1"] = int(sum(counts)) + int(rng.integers(0, 5))
+        spec = synth.small(name="random%d" % i, **kw)
+        rows_vis = 0
+        for b in range(batch):
+            nq = (kw["aslq"][b] if "aslq" in kw and layout == synth.BSND else kw["s1"]) if layout == synth.BSND \
+                else counts[b]
+            rows_vis += nq * (aslk[b] // cmp)
+        if 0 < rows_vis <= 300000:
+            return spec
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_parity_random(ora, i):
+    spec = random_spec(i)
+    inp = synth.make_inputs(spec, i)
+    p = inp["problem"]
+    log("random %d: %s" % (i, spec))
+    vis = vis_of(ora, inp)
+    cols = max(1, int(vis.max()) if vis.size else 1)
+    rc, oidx, oval, osc = ora.indexer(inp, scores_cols=cols)
+    assert rc == 0
+    gidx, gval, _ = run_gpu(inp)
+    k = p["sparse_count"]
+    check_structure(gidx, gval, vis, k)
+    for r in range(rows_of(p)):
+        check_row(r, int(vis[r]), k, gidx[r], gval[r], osc[r, :vis[r]], rtol_of(inp))
