@@ -231,6 +231,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bounded", action="store_true",
+                    help="also time qli_run_bounded (bound = the longest key) as context")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB read + write elementwise kernel (counter calibration under rocprofv3)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -325,7 +327,8 @@ def main() -> int:
     # Context only: bounded decode (no host plan; lengths read on the device), bound = the longest key.
     bounded_ms = None
     aslq = inp["aslq"]
-    if p["layout_query"] == 0 and 1 <= p["s1"] <= 4 and (aslq is None or all(int(v) == p["s1"] for v in aslq)):
+    if args.bounded and p["layout_query"] == 0 and 1 <= p["s1"] <= 4 and \
+            (aslq is None or all(int(v) == p["s1"] for v in aslq)):
         bix = qli.BoundedIndexer(p, int(max(inp["aslk"])))
         aslk_dev = torch.from_numpy(inp["aslk"].astype("int32")).cuda()
         run_b = lambda t: bix.run(aslk_dev, *t, stream=st)
