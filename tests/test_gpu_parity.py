@@ -457,3 +457,31 @@ def test_parity_random(ora, i):
     check_structure(gidx, gval, vis, k)
     for r in range(rows_of(p)):
         check_row(r, int(vis[r]), k, gidx[r], gval[r], osc[r, :vis[r]], rtol_of(inp))
+
+
+@pytest.mark.parametrize("case", ["bsnd_int8_causal_bs48_pad", "long_rt2_causal", "tnd_int8_prefill_mixed"])
+def test_without_values(case):
+    """return_value = 0 (参数说明: sparse_values optional): no value buffer, the
+    same indices as with values."""
+    inp = synth.make_inputs(SMALL[case] if case in SMALL else LONG[case], 8)
+    dev = device_inputs(inp)
+    a_idx, a_val, _ = run_gpu(inp, dev)
+    assert a_val is not None
+    noval = dict(inp, problem=dict(inp["problem"], return_value=0))
+    b_idx, b_val, _ = run_gpu(noval, dev)
+    assert b_val is None and np.array_equal(a_idx, b_idx)
+
+
+def test_bounded_without_values():
+    import torch
+    inp, dev, _, bound, lens = bounded_case("int8_s4_merges")
+    p0 = dict(inp["problem"], return_value=0)
+    bix = qli_mod().BoundedIndexer(p0, bound)
+    aslk = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    idx, val = bix.alloc_outputs()
+    assert val is None
+    bix.run(aslk, dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
+            idx, None)
+    torch.cuda.synchronize()
+    p_idx, _ = planned(inp, dev, lens)
+    assert np.array_equal(idx.cpu().numpy(), p_idx)
