@@ -198,14 +198,16 @@ int qli_run_debug(const qli_problem *p, const void *plan_host,
                   void *stream);
 
 /*
- * qli_run_stage -- qli_run restricted to some of its two kernels, for
- * measuring each one on its own: stages = 1 runs only the scoring kernel
- * (contraction, epilogue, chunk-local selection; rows that see at most
- * sparse_count entries are finished here), 2 only the final selection
- * kernel, 3 both (= qli_run).  Stage 2 alone reads whatever the workspace
- * holds from the last stage-1 run with the same plan and workspace; its
- * outputs are meaningful only after one.  Returns QLI_ERR_ARG for other
- * values of stages; otherwise errors are those of qli_run.
+ * qli_run_stage -- qli_run restricted to one of its two stages, for
+ * measuring each on its own: stages = 1 runs only the scoring kernel
+ * (gather, contraction and epilogue; rows that see at most sparse_count
+ * entries are finished here, the others stage every score in the
+ * workspace), 2 only the selection (the segment top-k launch, then the
+ * merge launch for rows longer than one segment), 3 both (= qli_run).
+ * Stage 2 alone reads whatever the workspace holds from the last stage-1
+ * run with the same plan and workspace; its outputs are meaningful only
+ * after one.  Returns QLI_ERR_ARG for other values of stages; otherwise
+ * errors are those of qli_run.
  */
 int qli_run_stage(const qli_problem *p, const void *plan_host,
                   const void *plan_dev, const void *query, const void *key,
