@@ -4,29 +4,33 @@
 // section 功能说明: score = sum_g W[g] * ReLU(ScaleQ[g] * ScaleK[s] * Q[g].K[s]),
 // then the Top-k key indices per query token.
 //
-// Stage 1, score_kernel (one work item per workgroup, 4 waves):
-//   * the item's key chunk is walked in tiles of 64 entries; each tile is
-//     gathered through block_table with 16-byte loads (8 lanes per 128-byte
-//     key row, so every row is one fully used cache line) and staged in a
-//     double-buffered, XOR-swizzled LDS tile;
-//   * int8 keys use v_mfma_i32_16x16x64_i8 (exact int32 dots), e4m3fn keys
-//     v_mfma_f32_16x16x128_f8f6f4; the 64 query heads of a row are the M
-//     dimension (4 tiles of 16), 16 keys the N dimension, D=128 the K one;
+// Stage 1 scores every visible (row, key) pair of a plan's work items:
+//   * score_kernel (prefill-shaped items of 8 rows) walks the item's key
+//     chunk in tiles of 64 entries, gathered through block_table with
+//     16-byte loads (8 lanes per 128-byte key row, so every row is one fully
+//     used cache line) into a double-buffered, XOR-swizzled LDS tile;
+//   * score_decode_kernel (items of 1, 2 or 4 rows of one batch) streams the
+//     chunk through a 3-stage LDS ring filled by direct-to-LDS loads, so the
+//     rows share every key byte read from HBM;
+//   * both: int8 keys use v_mfma_i32_16x16x64_i8 (exact int32 dots), e4m3fn
+//     keys v_mfma_f32_16x16x128_f8f6f4; the 64 query heads of a row are the
+//     M dimension (4 tiles of 16), 16 keys the N dimension, D=128 the K one;
 //   * fused epilogue: ScaleQ is folded into W once per row (w' = W*ScaleQ,
 //     exact in fp32 for fp16 inputs), so each (head, key) element costs
-//     max + convert + fma; the head sum finishes with two permlane swaps and
-//     one multiply by ScaleK[s].  This reordering needs ScaleQ, ScaleK >= 0,
-//     which is the contract (dequant scales are magnitudes).
+//     max + convert + fma; the head sum finishes with permlane swaps and one
+//     multiply by ScaleK[s].  This reordering needs ScaleQ, ScaleK >= 0,
+//     which is the contract (dequant scales are magnitudes);
 //   * rows that see at most sparse_count entries return every visible index
 //     (the top-k of a set no larger than k is the set), so their indices and
 //     scores are written straight to the outputs; other rows stage fp32
 //     scores in the workspace.
-// Stage 2, select_kernel (one workgroup of 1024 threads per staged row):
-//   radix select over order-preserving uint32 keys of the scores with 11-bit
-//   digits, starting below the bits every score shares; LDS histograms; the
-//   threshold digit found with a block scan; ties at the threshold resolved
-//   towards the lower index with wave ballots and mbcnt prefix counts; the
-//   selected entries written in ascending index order.
+// Stage 2 selects (select_reg_kernel, select_global_kernel; one workgroup of
+// 1024 threads per selection): rows of at most 8192 staged scores, and each
+// 8192-score segment of longer rows, keep their top-k; a second launch
+// merges a long row's segment winners.  Radix select over order-preserving
+// uint32 keys held in registers (11-bit digits, starting below the bits
+// every key shares, LDS histograms, block scans); ties at the threshold go to
+// the lower index; the winners are written in ascending index order.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
