@@ -27,6 +27,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import os
 import sys
@@ -41,14 +42,24 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA, TOP/s
 FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA, TFLOP/s
 ROTATION_BYTES = 640 << 20     # distinct bytes touched between two uses of one input copy
-KERNEL_SOURCE = os.path.join(ROOT, "sparse_attention_token_paged_amd", "csrc", "qli_kernels.hip")
+# The sources that decide what the kernels do and how they are launched.
+KERNEL_SOURCES = [os.path.join(ROOT, "sparse_attention_token_paged_amd", "csrc", f)
+                  for f in ("qli_kernels.hip", "qli_internal.h", "qli_api.cpp")]
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 256 << 20         # bytes read and bytes written by the counter-calibration kernel
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the code (comments and whitespace removed) of the kernel and
+    launch sources: traffic measured on other code is not reported."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def hip_runtime():
