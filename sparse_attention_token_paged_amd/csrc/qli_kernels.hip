@@ -107,6 +107,21 @@ __device__ __forceinline__ float scale_from_bits(uint32_t b) {
   }
 }
 
+// int8 epilogue without an int->float conversion.  A non-negative int32 d
+// read as fp32 bits is the denormal d * 2^-149, exactly (|dot| <= 2^21).  With
+// w' carried as w' * 2^95 (w' = W * ScaleQ < 2^32 for fp16 inputs, so it does
+// not overflow) each product w' * 2^95 * d * 2^-149 = w' * d * 2^-54 is a
+// normal float (w' >= 2^-48 when non-zero, d >= 1), so every fma rounds as it
+// would on w' * d and the head sum is the same fp32 value times 2^-54; the
+// 2^54 is folded into ScaleK.  The kernels run with fp32 denormals preserved
+// (the code objects' float_denorm_mode_32 is 3), so the fma takes the denormal
+// operand as it is: max + fma per (head, key) instead of max + convert + fma.
+template <int QK>
+__device__ constexpr float w_scale() { return QK == QLI_QK_INT8 ? 0x1p95f : 1.f; }
+template <int QK>
+__device__ constexpr float sk_scale() { return QK == QLI_QK_INT8 ? 0x1p54f : 1.f; }
+__device__ __forceinline__ float relu_bits(int d) { return __int_as_float(max(d, 0)); }
+
 // Sum over the four lane groups of per-lane partials, scattered so that lane
 // (q, c) ends with the total of partial q: lane q*16 + c holds key q*16 + c
 // of the 64-key tile (two permlane steps).
@@ -152,8 +167,8 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// w'[4m + i] = W * ScaleQ for heads 16m + 4q + i of row r (i = 0..3 are
-// consecutive, so one 8- or 16-byte load per tensor and m).
+// w'[4m + i] = W * ScaleQ (times w_scale) for heads 16m + 4q + i of row r
+// (i = 0..3 are consecutive, so one 8- or 16-byte load per tensor and m).
 template <int QK>
 __device__ __forceinline__ void load_wq(const ScoreParams& P, int64_t r, int q, float (&wq)[16]) {
   const int64_t e0 = r * kHeads + 4 * q;
@@ -164,7 +179,7 @@ __device__ __forceinline__ void load_wq(const ScoreParams& P, int64_t r, int q, 
       const h4 w = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.weights) + e0 + 16 * m);
       const h4 sq = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.q_scale) + e0 + 16 * m);
 #pragma unroll
-      for (int i = 0; i < 4; i++) wq[4 * m + i] = __builtin_fmaf((float)w[i], (float)sq[i], 0.f);
+      for (int i = 0; i < 4; i++) wq[4 * m + i] = __builtin_fmaf((float)w[i] * w_scale<QK>(), (float)sq[i], 0.f);
     } else {
       const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(P.weights) + e0 + 16 * m);
       const float4 sq = *reinterpret_cast<const float4*>(static_cast<const float*>(P.q_scale) + e0 + 16 * m);
@@ -314,7 +329,7 @@ void score_kernel(ScoreParams P) {
     int4* dst = reinterpret_cast<int4*>(&lds_k[s][0]);
     dst[tid] = kr[S][0];
     dst[kScoreThreads + tid] = kr[S][1];
-    if (tid < kTileKeys) lds_sk[s][tid] = scale_from_bits<QK>(skr[S]);
+    if (tid < kTileKeys) lds_sk[s][tid] = scale_from_bits<QK>(skr[S]) * sk_scale<QK>();
   };
 
   // One 64-key tile: for each n-tile the B fragment is read once and feeds
@@ -349,7 +364,7 @@ void score_kernel(ScoreParams P) {
           for (int m = 0; m < 4; m++)
 #pragma unroll
             for (int i = 0; i < 4; i++)
-              acc = __builtin_fmaf(wq[rr][4 * m + i], (float)max(di[m][i], 0), acc);
+              acc = __builtin_fmaf(wq[rr][4 * m + i], relu_bits(di[m][i]), acc);
         } else {
           const v8i bb = __builtin_shufflevector(b.lo, b.hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
@@ -916,26 +931,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
         qa[m].lo = *reinterpret_cast<const v4i*>(qh + 16 * chunk_lo<QK>(q));
         qa[m].hi = *reinterpret_cast<const v4i*>(qh + 16 * chunk_hi<QK>(q));
       }
-      // heads 16m + 4q + i, i = 0..3, are consecutive: one vector load per m
-      const int64_t e0 = r * kHeads + 4 * q;
-  #pragma unroll
-      for (int m = 0; m < 4; m++) {
-        if constexpr (QK == QLI_QK_INT8) {
-          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-          const h4 w = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.weights) + e0 + 16 * m);
-          const h4 sq = *reinterpret_cast<const h4*>(static_cast<const _Float16*>(P.q_scale) + e0 + 16 * m);
-  #pragma unroll
-          for (int i = 0; i < 4; i++) wq[4 * m + i] = __builtin_fmaf((float)w[i], (float)sq[i], 0.f);
-        } else {
-          const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(P.weights) + e0 + 16 * m);
-          const float4 sq = *reinterpret_cast<const float4*>(static_cast<const float*>(P.q_scale) + e0 + 16 * m);
-          wq[4 * m + 0] = w.x * sq.x;
-          wq[4 * m + 1] = w.y * sq.y;
-          wq[4 * m + 2] = w.z * sq.z;
-          wq[4 * m + 3] = w.w * sq.w;
-        }
-      }
     }
+    load_wq<QK>(P, r, q, wq);
     if (tid < nblk) lds_bt[tid] = bt0;
     if (tid + kScoreThreads < nblk) lds_bt[tid + kScoreThreads] = bt1;
     lds_barrier();  // lds_bt ready
@@ -969,7 +966,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
 #pragma unroll
         for (int m = 0; m < 4; m++)
 #pragma unroll
-          for (int i = 0; i < 4; i++) acc = __builtin_fmaf(wq[4 * m + i], (float)max(di[m][i], 0), acc);
+          for (int i = 0; i < 4; i++) acc = __builtin_fmaf(wq[4 * m + i], relu_bits(di[m][i]), acc);
       } else {
         const v8i bb = __builtin_shufflevector(b.lo, b.hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
@@ -1016,7 +1013,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     }
     const int e = st * SC + kk;  // entry within the chunk
     const int j = key0 + e;
-    const float score = total * scale_from_bits<QK>(ring_sk[slot_][kk]);
+    const float score = total * (scale_from_bits<QK>(ring_sk[slot_][kk]) * sk_scale<QK>());
     if (owner && j < rvis) {
       if (direct) {
         oi[j] = j;
