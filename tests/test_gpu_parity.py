@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import synth
-from tests._gpu import (ATOL, check_row, check_structure, device_inputs, log, make_indexer, rtol_of,
+from tests._gpu import (ATOL, INT8_RTOL, check_row, check_structure, device_inputs, log, make_indexer, rtol_of,
                         run_gpu, stable_topk_set)
 from tests._helpers import rows_of
 
@@ -200,6 +200,64 @@ def test_parity_long_dense_rows(ora, name):
     assert rc == 0
     for r in range(rows):
         check_row(r, int(vis[r]), k, gidx[r], gval[r], osc[r, :vis[r]], rtol_of(inp))
+
+
+def _extreme_fp16(rng, shape):
+    """fp16 values over the whole non-negative range: zeros, the smallest
+    subnormal and normal, the largest finite value, and log-uniform values
+    between 2^-24 and 65504."""
+    special = np.array([0.0, 2.0 ** -24, 2.0 ** -14, 0.5, 1.0, 65504.0])
+    v = np.exp2(rng.uniform(-24.0, 15.99, size=shape))
+    pick = rng.random(shape) < 0.3
+    v[pick] = rng.choice(special, size=int(pick.sum()))
+    return v.astype(np.float16)
+
+
+EXTREME = {
+    "decode_bsnd_causal": synth.small(batch=3, s1=4, aslk=[1500, 700, 2300], block_size=64, sparse_count=256,
+                                      sparse_mode=3),
+    "prefill_tnd_causal": synth.small(layout=synth.TND, batch=2, s1=150, aslq=[70, 150], aslk=[300, 900],
+                                      block_size=32, sparse_count=128, sparse_mode=3),
+}
+
+
+@pytest.mark.parametrize("name", list(EXTREME))
+def test_extreme_fp16_scales(ora, name):
+    """int8 path with weights and both dequant scales spanning every fp16
+    exponent (0, subnormals, 65504): the epilogue carries W * ScaleQ and
+    ScaleK with fixed power-of-two factors and reads relu'd int32 dots as fp32
+    denormals, which is exact only if no product or partial sum leaves the
+    normal range; dots bit-exact, scores within the int8 tolerance, selection
+    consistent with the GPU's own scores."""
+    import torch
+    inp = synth.make_inputs(EXTREME[name], 17)
+    rng = np.random.default_rng(1234)
+    for key in ("weights", "q_scale", "k_scale"):
+        inp[key] = _extreme_fp16(rng, inp[key].shape)
+    p = inp["problem"]
+    vis = vis_of(ora, inp)
+    rows, k = rows_of(p), p["sparse_count"]
+    cols = int(vis.max())
+    log("case %s: extreme fp16 scales rows=%d cols=%d" % (name, rows, cols))
+    ix = make_indexer(inp)
+    dev = device_inputs(inp)
+    gidx, gval, dots, scores = ix.run_debug(dev["query"], dev["key"], dev["weights"], dev["q_scale"],
+                                            dev["k_scale"], dev["block_table"], 0, rows, cols)
+    torch.cuda.synchronize()
+    gidx, gval = gidx.cpu().numpy(), gval.cpu().numpy()
+    dots, scores = dots.cpu().numpy(), scores.cpu().numpy()
+    check_structure(gidx, gval, vis, k)
+    for r in range(rows):
+        v = int(vis[r])
+        if v == 0:
+            continue
+        _, odots, osc = ora.row_detail(inp, r, 0, v)
+        assert np.array_equal(dots[r, :, :v].astype(np.float64), odots), "row %d: int8 dots differ" % r
+        assert np.all(np.isfinite(scores[r, :v])), "row %d: non-finite score" % r
+        assert np.all(np.abs(scores[r, :v] - osc) <= ATOL + INT8_RTOL * np.abs(osc)), "row %d scores" % r
+        n = min(k, v)
+        assert np.array_equal(gidx[r, :n], stable_topk_set(scores[r, :v], k)), "row %d selection" % r
+        assert np.array_equal(gval[r, :n], scores[r, gidx[r, :n]]), "row %d values" % r
 
 
 def test_ties_go_to_lower_index(ora):
