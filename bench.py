@@ -191,6 +191,52 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str) -> dict:
     return res
 
 
+SQ_COUNTERS = ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+               "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU"]
+SIMDS = 1024                   # 256 CUs x 4 SIMDs
+SHADER_ENGINES = 32            # 8 XCDs x 4; SQ_BUSY_CYCLES sums one count per engine
+
+
+def summarize_sq(workload: str, sq_dir: str) -> dict:
+    """Issue counters of the scoring kernel from one rocprofv3 --pmc run of
+    the SQ_COUNTERS (medians over its dispatches).  MFMA busy
+    (SQ_VALU_MFMA_BUSY_CYCLES, SIMD cycles) and VALU active
+    (SQ_ACTIVE_INST_VALU, counted in quad-cycles) are given as fractions of
+    SIMDS x the dispatch time at the nominal 2.4 GHz shader clock, and of
+    SIMDS x the cycles the sequencers were busy (SQ_BUSY_CYCLES, one count per
+    shader engine; shorter than the dispatch when waves are not resident)."""
+    rows = _counter_rows(sq_dir)
+    per = {}
+    for r in rows:
+        n = r["Kernel_Name"]
+        if "score_decode_kernel" not in n and "score_kernel" not in n:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {"name": n})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    disp = [d for d in per.values() if all(c in d for c in SQ_COUNTERS)]
+    if not disp:
+        raise SystemExit("no scoring-kernel dispatch with every SQ counter under %s" % sq_dir)
+    med = lambda key: sorted(d[key] for d in disp)[len(disp) // 2]
+    ns = med("ns")
+    nominal = SIMDS * ns * 2.4                          # SIMD cycles at 2.4 GHz over the dispatch
+    busy = SIMDS * med("SQ_BUSY_CYCLES") / SHADER_ENGINES  # SIMD cycles while the sequencers were busy
+    mfma, valu = med("SQ_VALU_MFMA_BUSY_CYCLES"), 4.0 * med("SQ_ACTIVE_INST_VALU")
+    res = {"workload": workload, "kernel_source_sha256_16": kernel_source_hash(),
+           "kernels": sorted(set(d["name"].replace("qli::(anonymous namespace)::", "").replace("void ", "")
+                                 .split("(")[0] for d in disp)),
+           "dispatches": len(disp), "dispatch_ns_median": ns}
+    res.update({c: med(c) for c in SQ_COUNTERS})
+    res["mfma_busy_frac_of_dispatch_at_2p4ghz"] = round(mfma / nominal, 4)
+    res["valu_active_frac_of_dispatch_at_2p4ghz"] = round(valu / nominal, 4)
+    res["sq_busy_cycles_per_engine_over_dispatch_ghz"] = round(med("SQ_BUSY_CYCLES") / SHADER_ENGINES / ns, 3)
+    res["mfma_busy_frac_of_sq_busy"] = round(mfma / busy, 4)
+    res["valu_active_frac_of_sq_busy"] = round(valu / busy, 4)
+    res["valu_insts_per_wave"] = round(med("SQ_INSTS_VALU") / med("SQ_WAVES"), 1)
+    res["mfma_insts_per_wave"] = round(med("SQ_INSTS_MFMA") / med("SQ_WAVES"), 1)
+    return res
+
+
 def cpu_baseline(inp: dict, info, budget_core_s: float = 20.0, min_wall_s: float = 10.0) -> dict:
     """The oracle as it stands, on the host, on a bounded prefix of batches."""
     import numpy as np
@@ -248,7 +294,16 @@ def main() -> int:
                     help="also run a 256 MiB read + write elementwise kernel (counter calibration under rocprofv3)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_score_kernel_<workload>.json from two rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-sq", metavar="SQ_DIR",
+                    help="write profiles/issue_score_kernel_<workload>.json from a rocprofv3 --pmc run of "
+                         + " ".join(SQ_COUNTERS))
     args = ap.parse_args()
+    if args.summarize_sq:
+        res = summarize_sq(args.workload, args.summarize_sq)
+        with open(os.path.join(PROFILES, "issue_score_kernel_%s.json" % args.workload), "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res))
+        return 0
     if args.summarize_counters:
         res = summarize_counters(args.workload, *args.summarize_counters)
         path = os.path.join(PROFILES, "traffic_score_kernel_%s.json" % args.workload)
