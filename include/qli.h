@@ -252,6 +252,71 @@ int qli_run_bounded(const qli_problem *p, int64_t max_seq_len_key,
                     int32_t *sparse_indices, float *sparse_values,
                     void *stream);
 
+/*
+ * Producer side: per-token-head quantization of the index query and key, the
+ * step before the indexer.  QLI-README 功能说明 states that query and key are
+ * quantized so that both are stored and computed in 8 bits, and 参数说明
+ * names per-token-head as the only quantization mode (query_quant_mode,
+ * key_quant_mode = 0); it gives no formula.  The reading adopted here is
+ * symmetric absmax quantization of each 128-element head vector, matching the
+ * indexer's dequantization ScaleQ * ScaleK * (q . k).  Every step is fixed in
+ * fp32 so that the codes are reproducible bit for bit:
+ *
+ *   x      the row's 128 bf16 values, widened exactly to fp32
+ *   amax   max_i |x_i|
+ *   int8 codes, fp16 scale (the page's INT8 + FLOAT16 pairing):
+ *     s    = fp16(amax / 127)     fp32 division, rounded to nearest-even fp16,
+ *                                 65504 if that overflows
+ *     r    = 1 / float(s)         fp32 division (correctly rounded)
+ *     q_i  = clamp(rint(x_i * r), -127, 127), rint = nearest, ties to even;
+ *            all q_i = 0 when s == 0
+ *   e4m3fn codes, fp32 scale (the FLOAT8_e4m3fn + FLOAT32 pairing):
+ *     s    = amax / 448           fp32 division
+ *     r    = 1 / s                fp32 division
+ *     q_i  = e4m3fn(clamp(x_i * r, -448, 448)), rounded to nearest, ties to
+ *            even (OCP E4M3FN: bias 7, subnormals m * 2^-9, max 448);
+ *            all q_i = 0 when s == 0 or r is not finite (amax < 448 * 2^-128)
+ *   s is the dequant scale written beside the codes; s * q_i approximates x_i.
+ *
+ * Inputs must be finite (NaN / Inf give undefined codes).  Pointers are
+ * device addresses; x 16-byte aligned, q_out 8-byte aligned; nothing is
+ * allocated; a row count of 0 launches nothing.  Errors: QLI_ERR_ARG for a
+ * negative count, a NULL or misaligned pointer, or a cache geometry that
+ * breaks the indexer's constraints; QLI_ERR_UNSUPPORTED for another
+ * qk_dtype; QLI_ERR_HIP if the launch fails.
+ */
+
+/*
+ * qli_quantize_query -- rows = tokens * 64 head vectors of a query
+ *   [tokens, 64, 128] bf16 (row-major) -> q_out [rows, 128] codes (qli_qk_dtype)
+ *   and scale_out [rows] (fp16 for int8, fp32 for e4m3fn): the query and
+ *   query_dequant_scale inputs of qli_run, row for row.
+ */
+int qli_quantize_query(int32_t qk_dtype, int64_t rows, const void *x,
+                       void *q_out, void *scale_out, void *stream);
+
+/*
+ * qli_append_keys -- quantizes n key entries (bf16 [n, 128]; when cmp_ratio >
+ *   1 these are compressed entries, produced upstream) and writes entry e into
+ *   the paged key cache at entry position pos[e] of sequence batch_idx[e]:
+ *   block blk = block_table[batch_idx[e] * max_blocks_per_seq + pos[e] /
+ *   block_size], slot o = pos[e] % block_size; codes at key_cache + blk *
+ *   stride + o * 128, scale at k_scale[blk * block_size + o] (the key and
+ *   key_dequant_scale layouts of qli_run; stride = key_block_stride, or
+ *   block_size * 128 when 0).  An entry whose batch_idx is outside
+ *   [0, batch_count), whose pos is negative or past max_blocks_per_seq *
+ *   block_size, or whose block id is outside [0, num_blocks) is skipped, so no
+ *   write leaves the cache.  Entries must address distinct slots (two entries
+ *   for one slot race).  block_size, stride and num_blocks follow the
+ *   constraints of qli_problem.
+ */
+int qli_append_keys(int32_t qk_dtype, int64_t n, const void *x,
+                    const int32_t *batch_idx, const int32_t *pos,
+                    const int32_t *block_table, int32_t batch_count,
+                    int32_t max_blocks_per_seq, int32_t num_blocks,
+                    int32_t block_size, int64_t key_block_stride,
+                    void *key_cache, void *k_scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

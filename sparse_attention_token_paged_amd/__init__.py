@@ -26,7 +26,7 @@ LAYOUT_BSND, LAYOUT_TND = 0, 1
 INT64_MAX = (1 << 63) - 1
 
 EXPORTED = ("qli_status_string", "qli_plan", "qli_plan_info_get", "qli_run", "qli_run_debug", "qli_run_stage",
-            "qli_bounded_workspace", "qli_run_bounded")
+            "qli_bounded_workspace", "qli_run_bounded", "qli_quantize_query", "qli_append_keys")
 
 c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
@@ -93,6 +93,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.qli_bounded_workspace.restype = ctypes.c_int
         lib.qli_run_bounded.argtypes = [ctypes.POINTER(Problem), c_i64] + [c_p] * 10 + [c_p]
         lib.qli_run_bounded.restype = ctypes.c_int
+        lib.qli_quantize_query.argtypes = [c_i32, c_i64, c_p, c_p, c_p, c_p]
+        lib.qli_quantize_query.restype = ctypes.c_int
+        lib.qli_append_keys.argtypes = [c_i32, c_i64, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i64,
+                                        c_p, c_p, c_p]
+        lib.qli_append_keys.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -190,6 +195,38 @@ def qli_run_bounded(problem: Problem, max_seq_len_key: int, aslk_dev, query, key
                                   _addr(key), _addr(weights), _addr(q_scale), _addr(k_scale),
                                   _addr(block_table), _addr(workspace), _addr(sparse_indices),
                                   _addr(sparse_values), stream)
+
+
+def qli_quantize_query(qk_dtype: int, rows: int, x, q_out, scale_out, stream=None) -> int:
+    """x: bf16 [rows, 128] (rows = tokens * 64 heads); q_out: [rows, 128] int8 or
+    e4m3fn codes; scale_out: [rows] fp16 (int8) or fp32 (e4m3fn)."""
+    return load().qli_quantize_query(int(qk_dtype), int(rows), _addr(x), _addr(q_out), _addr(scale_out), stream)
+
+
+def qli_append_keys(qk_dtype: int, n: int, x, batch_idx, pos, block_table, batch_count: int,
+                    max_blocks_per_seq: int, num_blocks: int, block_size: int, key_block_stride: int,
+                    key_cache, k_scale, stream=None) -> int:
+    """x: bf16 [n, 128] key entries; entry e goes to position pos[e] of sequence
+    batch_idx[e] in the paged cache key_cache / k_scale through block_table."""
+    return load().qli_append_keys(int(qk_dtype), int(n), _addr(x), _addr(batch_idx), _addr(pos),
+                                  _addr(block_table), int(batch_count), int(max_blocks_per_seq),
+                                  int(num_blocks), int(block_size), int(key_block_stride),
+                                  _addr(key_cache), _addr(k_scale), stream)
+
+
+def quantize_query(x, qk_dtype: int = QK_INT8, stream: Optional[int] = None):
+    """Per-token-head quantization of a bf16 query [..., 64, 128] (torch, on
+    the GPU): returns (codes uint8 [..., 64, 128], scales [..., 64]) as the
+    query / query_dequant_scale inputs of the indexer."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.shape[-1] == 128 and x.is_contiguous()
+    rows = x.numel() // 128
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    sc = torch.empty(x.shape[:-1], dtype=torch.float16 if qk_dtype == QK_INT8 else torch.float32, device=x.device)
+    rc = qli_quantize_query(qk_dtype, rows, x, q, sc, current_stream() if stream is None else stream)
+    if rc != QLI_OK:
+        raise QliError(rc, "qli_quantize_query")
+    return q, sc
 
 
 class BoundedIndexer:

@@ -351,3 +351,43 @@ def test_bounded_rejects_without_launching(qli):
     a[1] = fake + 4                                                 # query not 16-byte aligned
     assert qli.qli_run_bounded(prob, bound, *a) == qli.QLI_ERR_ARG
     assert qli.qli_run_bounded(qli.Problem.from_dict(dict(p, sparse_mode=1)), bound, *args) == qli.QLI_ERR_ARG
+
+
+# Producer entry points: argument checks return before anything is launched
+# (the fake device addresses below are never dereferenced).
+A16, A8 = 0x10000, 0x20000
+
+
+def test_quantize_query_rejects_bad_arguments(qli):
+    f = qli.qli_quantize_query
+    assert f(2, 4, A16, A16, A16) == qli.QLI_ERR_UNSUPPORTED
+    assert f(0, -1, A16, A16, A16) == qli.QLI_ERR_ARG
+    assert f(0, 0, None, None, None) == qli.QLI_OK  # nothing to do, nothing launched
+    assert f(0, 4, None, A16, A16) == qli.QLI_ERR_ARG
+    assert f(0, 4, A16, None, A16) == qli.QLI_ERR_ARG
+    assert f(0, 4, A16, A16, None) == qli.QLI_ERR_ARG
+    assert f(0, 4, A16 + 8, A16, A16) == qli.QLI_ERR_ARG   # x must be 16-byte aligned
+    assert f(0, 4, A16, A16 + 4, A16) == qli.QLI_ERR_ARG   # codes 8-byte aligned
+    assert f(0, 4, A16, A16, A16 + 1) == qli.QLI_ERR_ARG   # fp16 scales 2-byte aligned
+    assert f(1, 4, A16, A16, A16 + 2) == qli.QLI_ERR_ARG   # fp32 scales 4-byte aligned
+
+
+def test_append_keys_rejects_bad_arguments(qli):
+    def call(qk=0, n=8, x=A16, bidx=A16, pos=A16, bt=A16, batches=2, mb=4, nb=8, bs=32, stride=0,
+             kc=A16, ks=A16):
+        return qli.qli_append_keys(qk, n, x, bidx, pos, bt, batches, mb, nb, bs, stride, kc, ks)
+    assert call(qk=3) == qli.QLI_ERR_UNSUPPORTED
+    for bs in (0, 8, 24, 1040):
+        assert call(bs=bs) == qli.QLI_ERR_ARG, bs
+    assert call(nb=0) == qli.QLI_ERR_ARG
+    assert call(mb=0) == qli.QLI_ERR_ARG
+    assert call(batches=-1) == qli.QLI_ERR_ARG
+    assert call(stride=32 * 128 - 16) == qli.QLI_ERR_ARG   # below block_size * 128
+    assert call(stride=32 * 128 + 8) == qli.QLI_ERR_ARG    # not a multiple of 16
+    assert call(n=-1) == qli.QLI_ERR_ARG
+    assert call(n=0, x=None, bidx=None, pos=None, bt=None, kc=None, ks=None) == qli.QLI_OK
+    for k in ("x", "bidx", "pos", "bt", "kc", "ks"):
+        assert call(**{k: None}) == qli.QLI_ERR_ARG, k
+    assert call(x=A16 + 4) == qli.QLI_ERR_ARG
+    assert call(kc=A16 + 8) == qli.QLI_ERR_ARG
+    assert call(qk=1, ks=A16 + 2) == qli.QLI_ERR_ARG
