@@ -281,6 +281,117 @@ def cpu_baseline(inp: dict, info, budget_core_s: float = 20.0, min_wall_s: float
                       % (nb - 1, B, vis.size, pairs, passes, dt)}
 
 
+def producer_bench(args) -> dict:
+    """Producer kernels (per-token-head quantization) on a producer workload:
+    K back-to-back launches over rotated cold copies, timed like the indexer
+    steps; HBM roofline from the algorithmic bytes; outputs of one launch
+    checked against the oracle on a sample of rows; the oracle timed on the
+    host beside it."""
+    import numpy as np
+    import torch
+    import synth
+    import sparse_attention_token_paged_amd as qli
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    qli.load()
+    hip = hip_runtime()
+    w = synth.producer_inputs(args.workload)
+    qk, x = w["qk"], w["x"]
+    n = x.shape[0]
+    sb = 2 if qk == 0 else 4
+    sdt = torch.float16 if qk == 0 else torch.float32
+    st = torch.cuda.current_stream().cuda_stream
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    if w["kind"] == "query":
+        alg = n * (256 + 128 + sb)                       # bf16 row in, codes and scale out
+        R = max(2, 1 + -(-ROTATION_BYTES // alg))
+        sets = [(dev(x.view(np.int16)), torch.empty((n, 128), dtype=torch.uint8, device="cuda"),
+                 torch.empty((n,), dtype=sdt, device="cuda")) for _ in range(R)]
+
+        def launch(sset):
+            return qli.qli_quantize_query(qk, n, sset[0], sset[1], sset[2], st)
+        kernel = "quantize_kernel<%d, false>" % qk
+    else:
+        bs, nb, stride = w["block_size"], w["num_blocks"], w["stride"]
+        ents = np.bincount(w["batch_idx"], minlength=w["batch"])
+        alg = n * (256 + 128 + sb + 8) + int(np.sum(-(-ents // bs))) * 4  # + batch/pos per entry, table entries
+        R = max(2, 1 + -(-ROTATION_BYTES // alg))
+        bt = dev(w["block_table"])
+        sets = [(dev(x.view(np.int16)), dev(w["batch_idx"]), dev(w["pos"]),
+                 torch.zeros(nb * stride, dtype=torch.uint8, device="cuda"),
+                 torch.zeros(nb * bs, dtype=sdt, device="cuda")) for _ in range(R)]
+
+        def launch(sset):
+            return qli.qli_append_keys(qk, n, sset[0], sset[1], sset[2], bt, w["batch"], w["max_blocks"], nb, bs,
+                                       stride, sset[3], sset[4], st)
+        kernel = "quantize_kernel<%d, true>" % qk
+    for i in range(args.warmup):
+        assert launch(sets[i % R]) == qli.QLI_OK
+    torch.cuda.synchronize()
+    ev = Events(hip, 2)
+    for _ in range(2):
+        torch.cuda.synchronize()
+        hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), ctypes.c_void_p(st))
+        torch.cuda._sleep(1000000)
+        hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), ctypes.c_void_p(st))
+        torch.cuda.synchronize()
+    spin_cycles_per_us = 1000000 / (ev.ms(0, 1) * 1e3)
+    t0 = time.perf_counter()
+    for i in range(20):
+        launch(sets[i % R])
+    enqueue_us = (time.perf_counter() - t0) * 1e6 / 20
+    torch.cuda.synchronize()
+    K = args.steps
+    torch.cuda._sleep(int(spin_cycles_per_us * (1.5 * K * enqueue_us + 200.0)))
+    assert hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), ctypes.c_void_p(st)) == 0
+    for i in range(K):
+        launch(sets[i % R])
+    assert hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), ctypes.c_void_p(st)) == 0
+    torch.cuda.synchronize()
+    ms = ev.ms(0, 1) / K
+    ev.close()
+    # the launch's own outputs against the oracle on a sample of rows
+    import oracle.quantize as oq
+    sample = np.arange(0, n, max(1, n // 4096))
+    codes, scales = oq.quantize_rows(x[sample], qk)
+    last = sets[(K - 1) % R]
+    if w["kind"] == "query":
+        got_c = last[1].cpu().numpy()[sample]
+        got_s = last[2].cpu().numpy()[sample]
+    else:
+        blk = w["block_table"][w["batch_idx"][sample], w["pos"][sample] // w["block_size"]].astype(np.int64)
+        o = (w["pos"][sample] % w["block_size"]).astype(np.int64)
+        kc = last[3].cpu().numpy()
+        got_c = np.stack([kc[b * w["stride"] + oo * 128: b * w["stride"] + oo * 128 + 128] for b, oo in zip(blk, o)])
+        got_s = last[4].cpu().numpy()[blk * w["block_size"] + o]
+    parity = bool(np.array_equal(got_c, codes) and np.array_equal(got_s, scales))
+    achieved = alg / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "head vectors quantized/s", "value": n / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16->%s" % ("int8" if qk == 0 else "fp8_e4m3fn"),
+        "data": "synthetic",
+        "config": {"workload": args.workload, "rows": n, "kind": w["kind"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": kernel, "kernel_ms": round(ms, 5),
+                     "algorithmic_bytes": alg, "traffic": None},
+        "step": {"cache_state": "every input cold: %d rotated copies (%.1f MB each)" % (R, alg / 1e6),
+                 "host_enqueue_us_per_step": round(enqueue_us, 2),
+                 "sampled_rows_match_oracle": parity, "sampled_rows": int(sample.size)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < 10.0 and done < n:
+            oq.quantize_rows(x[done:done + 8192], qk)
+            done += min(8192, n - done)
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": done / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "sample": "rows 0..%d of %d (numpy, one thread), %.2f s wall" % (done, n, el)}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +405,9 @@ def main() -> int:
                     help="also run a 256 MiB read + write elementwise kernel (counter calibration under rocprofv3)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_score_kernel_<workload>.json from two rocprofv3 --pmc runs")
+    ap.add_argument("--producer", action="store_true",
+                    help="time the producer kernels on a producer workload (%s)" % ", ".join(
+                        ["quantize_query_prefill_t8192", "append_keys_decode_b24_sk8192"]))
     ap.add_argument("--summarize-sq", metavar="SQ_DIR",
                     help="write profiles/issue_score_kernel_<workload>.json from a rocprofv3 --pmc run of "
                          + " ".join(SQ_COUNTERS))
@@ -315,6 +429,11 @@ def main() -> int:
         print("bench.py measures one GPU only: the indexer runs on a single MI355X here; "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         return 2
+    if args.producer:
+        if args.workload == DEFAULT_WORKLOAD:
+            args.workload = "quantize_query_prefill_t8192"
+        print(json.dumps(producer_bench(args)), flush=True)
+        return 0
 
     import torch
     import synth

@@ -153,3 +153,51 @@ def small(name: str = "tiny", **kw) -> Spec:
                 block_size=64, sparse_count=64, sparse_mode=0, cmp_ratio=1)
     base.update(kw)
     return Spec(**base)
+
+
+# ---------------------------------------------------------------------------
+# Producer workloads: bf16 head vectors before quantization.
+# ---------------------------------------------------------------------------
+# Recipe: PCG64(seed); each 128-element row is standard normal times a
+# per-row factor 2^U(-4, 4) (activation-like spread of row magnitudes), cast
+# to bf16 with round-to-nearest-even.  Key appends write every entry of every
+# sequence of an indexer workload's paged cache (positions 0 .. entries-1,
+# as a prefill writing its context), through that workload's block table.
+
+PRODUCER_WORKLOADS = {
+    # the prefill workload's query: 8192 tokens x 64 heads
+    "quantize_query_prefill_t8192": dict(kind="query", tokens=8192, qk=INT8),
+    # the headline decode workload's whole key cache: 24 sequences x 8192 entries, block 128, permuted
+    "append_keys_decode_b24_sk8192": dict(kind="keys", base="decode_int8_b24_s4_sk8192", qk=INT8),
+}
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def bf16_rows(rng: np.random.Generator, n: int) -> np.ndarray:
+    x = rng.standard_normal((n, 128), dtype=np.float32)
+    x *= np.exp2(rng.uniform(-4.0, 4.0, (n, 1))).astype(np.float32)
+    return to_bf16_bits(x)
+
+
+def producer_inputs(name: str, seed: Optional[int] = None) -> dict:
+    """bf16 rows (uint16 [n, 128]) and, for key appends, the destination of each
+    entry (batch_idx, pos) and the cache geometry of the base workload."""
+    w = PRODUCER_WORKLOADS[name]
+    rng = np.random.default_rng(list(PRODUCER_WORKLOADS).index(name) + 100 if seed is None else seed)
+    if w["kind"] == "query":
+        return dict(kind="query", qk=w["qk"], x=bf16_rows(rng, w["tokens"] * 64))
+    base = workload(w["base"])
+    p = base["problem"]
+    cmp = p["cmp_ratio"]
+    ents = [int(v) // cmp for v in base["aslk"]]
+    bidx = np.concatenate([np.full(n, b, np.int32) for b, n in enumerate(ents)])
+    pos = np.concatenate([np.arange(n, dtype=np.int32) for n in ents])
+    return dict(kind="keys", qk=w["qk"], x=bf16_rows(rng, bidx.size), batch_idx=bidx, pos=pos,
+                block_table=base["block_table"], batch=p["batch"], max_blocks=p["max_blocks_per_seq"],
+                num_blocks=p["num_blocks"], block_size=p["block_size"],
+                stride=p["key_block_stride"] or p["block_size"] * 128)
