@@ -154,3 +154,78 @@ def test_quantized_inputs_feed_the_indexer(ora, qk):
     check_structure(idx, val, vis, p["sparse_count"])
     for r in range(rows):
         check_row(r, int(vis[r]), p["sparse_count"], idx[r], val[r], sc[r, :vis[r]], rtol_of(inp))
+
+
+def test_chain_graph_replay():
+    """One decode step as a HIP graph captured once: quantize the bf16 query,
+    append each sequence's newest bf16 key entries into the paged cache, run
+    the indexer with the key lengths read on the device (no host plan).
+    Replayed with new inputs, positions and lengths (written eagerly between
+    replays, from a restored cache each time), every replay equals the same
+    chain run eagerly, bit for bit."""
+    import torch
+    import sparse_attention_token_paged_amd as qli
+    spec = synth.small(batch=3, s1=2, aslk=[1500, 900, 1200], block_size=64, sparse_count=128, sparse_mode=3)
+    inp = synth.make_inputs(spec, 9)
+    p = inp["problem"]
+    B, S1, bs, mb, nb = p["batch"], p["s1"], p["block_size"], p["max_blocks_per_seq"], p["num_blocks"]
+    stride = p["key_block_stride"] or bs * 128
+    rows, new = B * S1, 16
+    bound = 1500
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    st = qli.current_stream
+    # static buffers of the captured step
+    qb, kb = torch.empty((rows * 64, 128), dtype=torch.int16, device="cuda"), \
+        torch.empty((B * new, 128), dtype=torch.int16, device="cuda")
+    bidx = dev(np.repeat(np.arange(B, dtype=np.int32), new))
+    pos = torch.empty((B * new,), dtype=torch.int32, device="cuda")
+    aslk = torch.empty((B,), dtype=torch.int32, device="cuda")
+    q, qs = torch.empty((rows * 64, 128), dtype=torch.uint8, device="cuda"), \
+        torch.empty((rows * 64,), dtype=torch.float16, device="cuda")
+    pristine_k, pristine_ks = dev(inp["key"]), dev(inp["k_scale"].reshape(-1))
+    key, ks = pristine_k.clone(), pristine_ks.clone()
+    w, bt = dev(inp["weights"]), dev(inp["block_table"])
+    bix = qli.BoundedIndexer(p, bound)
+    idx, val = bix.alloc_outputs()
+
+    def step():
+        assert qli.qli_quantize_query(0, rows * 64, qb, q, qs, st()) == qli.QLI_OK
+        assert qli.qli_append_keys(0, B * new, kb, bidx, pos, bt, B, mb, nb, bs, stride, key, ks, st()) == qli.QLI_OK
+        bix.run(aslk, q, key, w, qs, ks, bt, idx, val)
+
+    def load_inputs(seed):
+        rng = np.random.default_rng(seed)
+        lens = rng.integers(200, bound + 1, B).astype(np.int32)
+        qb.copy_(dev(bf16_bits(rng.standard_normal((rows * 64, 128)).astype(np.float32)).view(np.int16)))
+        kb.copy_(dev(bf16_bits(rng.standard_normal((B * new, 128)).astype(np.float32)).view(np.int16)))
+        pos.copy_(dev(np.concatenate([np.arange(n - new, n, dtype=np.int32) for n in lens])))
+        aslk.copy_(dev(lens))
+        key.copy_(pristine_k)
+        ks.copy_(pristine_ks)
+
+    load_inputs(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # first launches (occupancy queries) outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        log("chain graph replay %d" % rep)
+        load_inputs(100 + rep)
+        idx.fill_(-7)
+        val.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        g_idx, g_val, g_key = idx.cpu().numpy(), val.cpu().numpy(), key.cpu().numpy()
+        load_inputs(100 + rep)
+        step()
+        torch.cuda.synchronize()
+        assert np.array_equal(g_key, key.cpu().numpy()), "replay %d: cache differs" % rep
+        assert np.array_equal(g_idx, idx.cpu().numpy()), "replay %d: indices differ" % rep
+        assert np.array_equal(g_val, val.cpu().numpy()), "replay %d: values differ" % rep
+        assert (g_idx[:, 0] >= 0).all()
