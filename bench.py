@@ -512,7 +512,7 @@ def main() -> int:
     # Context only: bounded decode (no host plan; lengths read on the device), bound = the longest key.
     bounded_ms = None
     aslq = inp["aslq"]
-    if args.bounded and p["layout_query"] == 0 and 1 <= p["s1"] <= 4 and \
+    if args.bounded and p["layout_query"] == 0 and p["s1"] >= 1 and \
             (aslq is None or all(int(v) == p["s1"] for v in aslq)):
         bix = qli.BoundedIndexer(p, int(max(inp["aslk"])))
         aslk_dev = torch.from_numpy(inp["aslk"].astype("int32")).cuda()

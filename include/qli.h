@@ -217,15 +217,17 @@ int qli_run_stage(const qli_problem *p, const void *plan_host,
                   float *sparse_values, int32_t stages, void *stream);
 
 /*
- * Bounded decode: the indexer without a host plan, for serving loops that
+ * Bounded runs: the indexer without a host plan, for serving loops that
  * keep actual_seq_lengths_key on the device and capture the call in a graph
  * once.  The page's metadata op runs on the device for the same reason
  * (QLI-README 参数说明 "metadata"; the operator supports graph mode); here the
  * launch geometry comes from a host bound on the key length alone, and the
  * kernels read the lengths themselves.
  *
- * Scope: BSND query layout, S1 <= 4 query rows per batch, all of them active
- * (no actual_seq_lengths_query).  Every other parameter as for qli_plan.
+ * Scope: BSND query layout, every one of the S1 query rows of every batch
+ * active (no actual_seq_lengths_query); any S1 (decode items for S1 <= 4,
+ * 8-row prefill tiles above, as qli_plan chooses).  TND returns
+ * QLI_ERR_UNSUPPORTED.  Every other parameter as for qli_plan.
  *
  * qli_bounded_workspace -- workspace bytes that qli_run_bounded needs for
  *   these problem sizes and any key lengths in [0, max_seq_len_key] original

@@ -449,7 +449,7 @@ struct Bounded {
 
 int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
   if (max_len < 0) return QLI_ERR_ARG;
-  if (p.layout_query != QLI_LAYOUT_BSND || p.s1 > kMaxItemRows) return QLI_ERR_UNSUPPORTED;
+  if (p.layout_query != QLI_LAYOUT_BSND) return QLI_ERR_UNSUPPORTED;
   const int64_t nmax = max_len / p.cmp_ratio;
   if (nmax >= kMaxEntries) return QLI_ERR_SIZE;
   if ((nmax + p.block_size - 1) / p.block_size > p.max_blocks_per_seq) return QLI_ERR_ARG;
@@ -458,14 +458,15 @@ int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
   const int64_t rows = (int64_t)p.batch * p.s1;
   const int k = p.sparse_count;
   h.rows = rows;
-  h.kind = kKindDecode;
-  h.rows_per_item = p.s1 <= 1 ? 1 : (p.s1 <= 2 ? 2 : 4);
+  const bool prefill = p.s1 > kMaxItemRows;  // 8-row prefill tiles, as qli_plan would choose
+  h.kind = prefill ? kKindPrefill : kKindDecode;
+  h.rows_per_item = prefill ? 8 : (p.s1 <= 1 ? 1 : (p.s1 <= 2 ? 2 : 4));
   if (rows == 0) return QLI_OK;
-  h.chunk = decode_chunk(std::vector<int32_t>(p.batch, (int32_t)nmax), true);
+  h.chunk = prefill ? kMaxChunk : decode_chunk(std::vector<int32_t>(p.batch, (int32_t)nmax), true);
   h.reg_chunks = (int32_t)std::max<int64_t>(1, (nmax + h.chunk - 1) / h.chunk);
   h.reg_rows = p.s1;
   h.reg_maxv = (int32_t)nmax;
-  const int64_t items = (int64_t)p.batch * h.reg_chunks;
+  const int64_t items = (int64_t)p.batch * h.reg_chunks * (prefill ? (p.s1 + 7) / 8 : 1);
   if (items > INT32_MAX) return QLI_ERR_SIZE;
   h.n_items = (int32_t)items;
   if (nmax <= k) return QLI_OK;  // every row is written by the scoring kernel

@@ -217,13 +217,45 @@ void score_kernel(ScoreParams P) {
   for (int round = 0;; round++) {
   const int pos = pos_of(round);
   if (pos >= P.n_items) break;  // uniform
-  const Item it = P.items[pos];
+  // Bounded prefill (key lengths on the device, BSND, all S1 = reg_rows query
+  // rows of every batch active): position pos is chunk pos % reg_chunks of
+  // 8-row group (pos / reg_chunks) % groups of batch pos / (reg_chunks *
+  // groups); rows' visible counts follow from the batch's length, clamped to
+  // the bound, and a row that sees more than k entries stages its scores at
+  // r * bstride of the workspace.  Otherwise the item and the rows come from
+  // the plan's tables.
+  Item it;
+  int64_t skb = 0;
+  if (P.aslk) {
+    const int s1 = P.reg_rows;
+    const int groups = (s1 + 7) / 8;
+    const int b = pos / (P.reg_chunks * groups);
+    const int rem = pos - b * P.reg_chunks * groups;
+    const int g = rem / P.reg_chunks;
+    const int c = rem - g * P.reg_chunks;
+    skb = min<int64_t>(max(P.aslk[b], 0), P.max_len);
+    it.batch = b;
+    it.row0 = b * s1 + 8 * g;
+    it.nrows = min(8, s1 - 8 * g);
+    int maxv = 0;
+    for (int u = 0; u < it.nrows; u++)
+      maxv = max(maxv, (int)visible_entries(P.mode, P.cmp, skb, s1, 8 * g + u));
+    it.key0 = c * P.chunk;
+    it.nkeys = min(P.chunk, maxv - it.key0);
+    it.flags = c == 0 ? kItemPad : 0;
+  } else {
+    it = P.items[pos];
+  }
+  auto row_vis = [&](int64_t r) __attribute__((always_inline)) {
+    return P.aslk ? (int)visible_entries(P.mode, P.cmp, skb, P.reg_rows, r - (int64_t)it.batch * P.reg_rows)
+                  : rinfo[r].vis;
+  };
 
   // Rows that see fewer than k entries: slots vis..k-1 are -1 / -inf.
   if (it.flags & kItemPad) {
     for (int u = 0; u < it.nrows; u++) {
       const int64_t r = it.row0 + u;
-      const int vis = rinfo[r].vis;
+      const int vis = row_vis(r);
       if (vis >= k) continue;
       for (int pos = vis + tid; pos < k; pos += kScoreThreads) {
         P.idx_out[r * k + pos] = -1;
@@ -258,9 +290,15 @@ void score_kernel(ScoreParams P) {
     rok[rr] = u < it.nrows;
     const int64_t r = it.row0 + (rok[rr] ? u : 0);
     rowid[rr] = r;
-    const RowInfo ri = rinfo[r];
-    rvis[rr] = rok[rr] ? ri.vis : 0;
-    rws[rr] = ri.ws_off;
+    if (P.aslk) {
+      const int v = row_vis(r);
+      rvis[rr] = rok[rr] ? v : 0;
+      rws[rr] = v > k ? r * P.bstride : -1;
+    } else {
+      const RowInfo ri = rinfo[r];
+      rvis[rr] = rok[rr] ? ri.vis : 0;
+      rws[rr] = ri.ws_off;
+    }
     const uint8_t* qrow = P.query + r * (kHeads * kDim);
 #pragma unroll
     for (int m = 0; m < 4; m++) {

@@ -317,7 +317,8 @@ def bounded_workspace_expected(p, max_len):
 
 
 @pytest.mark.parametrize("s1,k,cmp,max_len", [(1, 512, 1, 1000), (4, 2048, 1, 8192), (2, 256, 4, 70000),
-                                                (3, 100, 1, 0), (1, 2048, 1, 140000)])
+                                                (3, 100, 1, 0), (1, 2048, 1, 140000), (8, 256, 1, 3000),
+                                                (13, 2048, 1, 20000), (64, 512, 2, 10000)])
 def test_bounded_workspace(qli, s1, k, cmp, max_len):
     spec = synth.small(batch=3, s1=s1, aslk=[max(max_len, 1)] * 3, block_size=64, sparse_count=k,
                        sparse_mode=3, cmp_ratio=cmp)
@@ -339,8 +340,8 @@ def test_bounded_rejects_without_launching(qli):
     tnd = qli.Problem.from_dict(dict(p, layout_query=synth.TND))
     assert qli.qli_bounded_workspace(tnd, bound)[0] == qli.QLI_ERR_UNSUPPORTED
     assert qli.qli_run_bounded(tnd, bound, *args) == qli.QLI_ERR_UNSUPPORTED
-    wide = qli.Problem.from_dict(dict(p, s1=5))
-    assert qli.qli_bounded_workspace(wide, bound)[0] == qli.QLI_ERR_UNSUPPORTED
+    wide = qli.Problem.from_dict(dict(p, s1=5))  # prefill tiles: supported, same workspace layout
+    assert qli.qli_bounded_workspace(wide, bound) == (qli.QLI_OK, bounded_workspace_expected(dict(p, s1=5), bound))
     a = list(args)
     a[0] = None                                                     # actual_seq_lengths_key
     assert qli.qli_run_bounded(prob, bound, *a) == qli.QLI_ERR_ARG

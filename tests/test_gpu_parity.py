@@ -390,6 +390,15 @@ BOUNDED = {
                                  sparse_mode=3, cmp_ratio=4), [40000, 39999]),
     "int8_s3_short": (synth.small(batch=2, s1=3, aslk=[1500] * 2, block_size=32, sparse_count=256,
                                   sparse_mode=3), [1500, 700]),
+    # more than 4 query rows per batch: the prefill tiles (8 rows, key chunks of 4096)
+    "int8_s8_prefill": (synth.small(batch=2, s1=8, aslk=[3000] * 2, block_size=64, sparse_count=256,
+                                    sparse_mode=3), [3000, 1200]),
+    "int8_s13_chunks_merges": (synth.small(batch=2, s1=13, aslk=[20000] * 2, block_size=128, sparse_count=2048,
+                                           sparse_mode=3), [20000, 9000]),
+    "fp8_s6_mode0": (synth.small(qk=synth.FP8, batch=3, s1=6, aslk=[5000] * 3, block_size=32, sparse_count=300),
+                     [5000, 17, 0]),
+    "int8_s64_cmp2": (synth.small(batch=1, s1=64, aslk=[10000], block_size=128, sparse_count=512, sparse_mode=3,
+                                  cmp_ratio=2), [9999]),
 }
 
 
@@ -437,12 +446,19 @@ def test_bounded_matches_planned(ora, name):
     check_structure(idx.cpu().numpy(), None if val is None else val.cpu().numpy(), vis, p["sparse_count"])
 
 
-def test_bounded_graph_replay():
+GRAPH_LENS = {
+    "int8_s4_merges": ([24000, 24000, 24000], [9000, 0, 23999], [1, 2048, 12000], [3000, 17000, 8193]),
+    "int8_s13_chunks_merges": ([20000, 20000], [0, 4097], [8193, 12], [19999, 5000]),
+}
+
+
+@pytest.mark.parametrize("case", list(GRAPH_LENS))
+def test_bounded_graph_replay(case):
     """qli_run_bounded captured once in a HIP graph, replayed after the device
     key lengths change: every replay equals qli_plan + qli_run for the new
     lengths (including a batch that sees nothing and one longer than a segment)."""
     import torch
-    inp, dev, bix, bound, _ = bounded_case("int8_s4_merges", seed=6)
+    inp, dev, bix, bound, _ = bounded_case(case, seed=6)
     aslk = torch.tensor([bound] * inp["problem"]["batch"], dtype=torch.int32, device="cuda")
     idx, val = bix.alloc_outputs()
     args = (aslk, dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
@@ -452,7 +468,7 @@ def test_bounded_graph_replay():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         bix.run(*args)
-    for lens in ([24000, 24000, 24000], [9000, 0, 23999], [1, 2048, 12000], [3000, 17000, 8193]):
+    for lens in GRAPH_LENS[case]:
         aslk.copy_(torch.tensor(lens, dtype=torch.int32))
         idx.fill_(-7)
         val.fill_(3.0)
