@@ -509,14 +509,15 @@ def main() -> int:
     score_avg, _ = region(K, 1)       # scoring kernel alone
     select_avg = region(K, 2)[0] if info.select_rows > 0 else 0.0
     warm_ms, _ = region(K, 3, rotate=False)  # context only: one copy, inputs may hit in the caches
-    # Context only: bounded decode (no host plan; lengths read on the device), bound = the longest key.
+    # Context only: bounded run (no host plan; lengths read on the device), bound = the longest key.
     bounded_ms = None
     aslq = inp["aslq"]
-    if args.bounded and p["layout_query"] == 0 and p["s1"] >= 1 and \
-            (aslq is None or all(int(v) == p["s1"] for v in aslq)):
+    tnd = p["layout_query"] == 1
+    if args.bounded and p["s1"] >= 1 and (tnd or aslq is None or all(int(v) == p["s1"] for v in aslq)):
         bix = qli.BoundedIndexer(p, int(max(inp["aslk"])))
         aslk_dev = torch.from_numpy(inp["aslk"].astype("int32")).cuda()
-        run_b = lambda t: bix.run(aslk_dev, *t, stream=st)
+        aslq_dev = torch.from_numpy(aslq.astype("int32")).cuda() if tnd else None
+        run_b = lambda t: bix.run(aslk_dev, *t, stream=st, aslq_dev=aslq_dev)
         for s_ in range(3):
             run_b(sets[s_ % R])
         bounded_ms, _ = region(K, 3, launch=run_b)

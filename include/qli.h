@@ -224,10 +224,12 @@ int qli_run_stage(const qli_problem *p, const void *plan_host,
  * launch geometry comes from a host bound on the key length alone, and the
  * kernels read the lengths themselves.
  *
- * Scope: BSND query layout, every one of the S1 query rows of every batch
- * active (no actual_seq_lengths_query); any S1 (decode items for S1 <= 4,
- * 8-row prefill tiles above, as qli_plan chooses).  TND returns
- * QLI_ERR_UNSUPPORTED.  Every other parameter as for qli_plan.
+ * Scope: qli_run_bounded takes the BSND query layout with every one of the
+ * S1 query rows of every batch active (no actual_seq_lengths_query); any S1
+ * (decode items for S1 <= 4, 8-row prefill tiles above, as qli_plan
+ * chooses).  qli_run_bounded_tnd takes the TND layout with
+ * actual_seq_lengths_query on the device too (batch <= 4096).  Every other
+ * parameter as for qli_plan.
  *
  * qli_bounded_workspace -- workspace bytes that qli_run_bounded needs for
  *   these problem sizes and any key lengths in [0, max_seq_len_key] original
@@ -253,6 +255,25 @@ int qli_run_bounded(const qli_problem *p, int64_t max_seq_len_key,
                     const int32_t *block_table, void *workspace,
                     int32_t *sparse_indices, float *sparse_values,
                     void *stream);
+
+/*
+ * qli_run_bounded_tnd -- the same for the TND layout: aslq_dev (device int32[B],
+ *   actual_seq_lengths_query as prefix sums, 4-byte aligned) and aslk_dev are
+ *   both read on the device, so a graph captured once replays correctly after
+ *   either changes.  A first small kernel turns aslq into row and group tables
+ *   in the workspace (the prefix sums are taken as their running maximum
+ *   clamped to [0, T], so any contents give a valid partition of the T rows;
+ *   rows past the last prefix sum are padding).  Query rows are scored in
+ *   8-row tiles within each batch.  Returns QLI_ERR_UNSUPPORTED for BSND or
+ *   batch > 4096; otherwise as qli_run_bounded.
+ */
+int qli_run_bounded_tnd(const qli_problem *p, int64_t max_seq_len_key,
+                        const int32_t *aslq_dev, const int32_t *aslk_dev,
+                        const void *query, const void *key,
+                        const void *weights, const void *q_scale,
+                        const void *k_scale, const int32_t *block_table,
+                        void *workspace, int32_t *sparse_indices,
+                        float *sparse_values, void *stream);
 
 /*
  * Producer side: per-token-head quantization of the index query and key, the

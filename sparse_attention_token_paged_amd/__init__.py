@@ -26,7 +26,8 @@ LAYOUT_BSND, LAYOUT_TND = 0, 1
 INT64_MAX = (1 << 63) - 1
 
 EXPORTED = ("qli_status_string", "qli_plan", "qli_plan_info_get", "qli_run", "qli_run_debug", "qli_run_stage",
-            "qli_bounded_workspace", "qli_run_bounded", "qli_quantize_query", "qli_append_keys")
+            "qli_bounded_workspace", "qli_run_bounded", "qli_run_bounded_tnd", "qli_quantize_query",
+            "qli_append_keys")
 
 c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
@@ -93,6 +94,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.qli_bounded_workspace.restype = ctypes.c_int
         lib.qli_run_bounded.argtypes = [ctypes.POINTER(Problem), c_i64] + [c_p] * 10 + [c_p]
         lib.qli_run_bounded.restype = ctypes.c_int
+        lib.qli_run_bounded_tnd.argtypes = [ctypes.POINTER(Problem), c_i64] + [c_p] * 11 + [c_p]
+        lib.qli_run_bounded_tnd.restype = ctypes.c_int
         lib.qli_quantize_query.argtypes = [c_i32, c_i64, c_p, c_p, c_p, c_p]
         lib.qli_quantize_query.restype = ctypes.c_int
         lib.qli_append_keys.argtypes = [c_i32, c_i64, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i64,
@@ -229,6 +232,14 @@ def quantize_query(x, qk_dtype: int = QK_INT8, stream: Optional[int] = None):
     return q, sc
 
 
+def qli_run_bounded_tnd(problem: Problem, max_seq_len_key: int, aslq_dev, aslk_dev, query, key, weights, q_scale,
+                        k_scale, block_table, workspace, sparse_indices, sparse_values, stream=None) -> int:
+    return load().qli_run_bounded_tnd(ctypes.byref(problem), int(max_seq_len_key), _addr(aslq_dev), _addr(aslk_dev),
+                                      _addr(query), _addr(key), _addr(weights), _addr(q_scale), _addr(k_scale),
+                                      _addr(block_table), _addr(workspace), _addr(sparse_indices),
+                                      _addr(sparse_values), stream)
+
+
 class BoundedIndexer:
     """Bounded decode: no host plan; the key lengths stay on the device and
     may change between calls (or graph replays) up to max_seq_len_key.
@@ -246,17 +257,23 @@ class BoundedIndexer:
 
     def alloc_outputs(self):
         import torch
-        rows = self.problem.batch * self.problem.s1
+        tnd = self.problem.layout_query == LAYOUT_TND
+        rows = self.problem.s1 if tnd else self.problem.batch * self.problem.s1
         k = self.problem.sparse_count
         idx = torch.empty((rows, k), dtype=torch.int32, device=self.device)
         val = torch.empty((rows, k), dtype=torch.float32, device=self.device) if self.problem.return_value else None
         return idx, val
 
     def run(self, aslk_dev, query, key, weights, q_scale, k_scale, block_table, out_idx, out_val,
-            stream: Optional[int] = None):
+            stream: Optional[int] = None, aslq_dev=None):
+        """aslq_dev: device actual_seq_lengths_query (TND layout only)."""
         st = current_stream() if stream is None else stream
-        rc = qli_run_bounded(self.problem, self.max_seq_len_key, aslk_dev, query, key, weights, q_scale, k_scale,
-                             block_table, self.workspace, out_idx, out_val, st)
+        if self.problem.layout_query == LAYOUT_TND:
+            rc = qli_run_bounded_tnd(self.problem, self.max_seq_len_key, aslq_dev, aslk_dev, query, key, weights,
+                                     q_scale, k_scale, block_table, self.workspace, out_idx, out_val, st)
+        else:
+            rc = qli_run_bounded(self.problem, self.max_seq_len_key, aslk_dev, query, key, weights, q_scale,
+                                 k_scale, block_table, self.workspace, out_idx, out_val, st)
         if rc != QLI_OK:
             raise QliError(rc, "qli_run_bounded")
         return out_idx, out_val

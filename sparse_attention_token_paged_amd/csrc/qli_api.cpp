@@ -445,20 +445,24 @@ struct Bounded {
   PlanHeader h;
   int64_t stride, mstride, merge_base;
   int32_t nseg;
+  int64_t tab_off;  // TND: byte offset of the row and group tables in the workspace
 };
 
 int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
   if (max_len < 0) return QLI_ERR_ARG;
-  if (p.layout_query != QLI_LAYOUT_BSND) return QLI_ERR_UNSUPPORTED;
+  const bool tnd = p.layout_query == QLI_LAYOUT_TND;
+  if (tnd && p.batch > kTndMaxBatch) return QLI_ERR_UNSUPPORTED;
   const int64_t nmax = max_len / p.cmp_ratio;
   if (nmax >= kMaxEntries) return QLI_ERR_SIZE;
   if ((nmax + p.block_size - 1) / p.block_size > p.max_blocks_per_seq) return QLI_ERR_ARG;
   std::memset(&g, 0, sizeof(g));
   PlanHeader& h = g.h;
-  const int64_t rows = (int64_t)p.batch * p.s1;
+  const int64_t rows = tnd ? (int64_t)p.s1 : (int64_t)p.batch * p.s1;
   const int k = p.sparse_count;
   h.rows = rows;
-  const bool prefill = p.s1 > kMaxItemRows;  // 8-row prefill tiles, as qli_plan would choose
+  // 8-row prefill tiles as qli_plan would choose for S1 > 4; always for TND,
+  // whose rows per batch are known only on the device
+  const bool prefill = tnd || p.s1 > kMaxItemRows;
   h.kind = prefill ? kKindPrefill : kKindDecode;
   h.rows_per_item = prefill ? 8 : (p.s1 <= 1 ? 1 : (p.s1 <= 2 ? 2 : 4));
   if (rows == 0) return QLI_OK;
@@ -466,10 +470,20 @@ int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
   h.reg_chunks = (int32_t)std::max<int64_t>(1, (nmax + h.chunk - 1) / h.chunk);
   h.reg_rows = p.s1;
   h.reg_maxv = (int32_t)nmax;
-  const int64_t items = (int64_t)p.batch * h.reg_chunks * (prefill ? (p.s1 + 7) / 8 : 1);
+  const int64_t items = tnd ? tnd_groups(p.batch, p.s1) * h.reg_chunks
+                            : (int64_t)p.batch * h.reg_chunks * (prefill ? (p.s1 + 7) / 8 : 1);
   if (items > INT32_MAX) return QLI_ERR_SIZE;
   h.n_items = (int32_t)items;
-  if (nmax <= k) return QLI_OK;  // every row is written by the scoring kernel
+  // TND: the row and group tables follow whatever the selection needs
+  auto add_tables = [&]() {
+    if (!tnd) return;
+    g.tab_off = align16(h.workspace_bytes);
+    h.workspace_bytes = g.tab_off + 4 * tnd_tables(p.batch, p.s1).total;
+  };
+  if (nmax <= k) {  // every row is written by the scoring kernel
+    add_tables();
+    return QLI_OK;
+  }
   auto pad4 = [](int64_t n) { return (n + 3) & ~int64_t(3); };
   g.nseg = (int32_t)((nmax + kSelSegment - 1) / kSelSegment);
   g.stride = pad4(nmax);
@@ -486,6 +500,7 @@ int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
   h.ws_scores = total;
   h.ws_index_offset = align16(total * 4);
   h.workspace_bytes = g.nseg > 1 ? h.ws_index_offset + total * 4 : total * 4;
+  add_tables();
   return QLI_OK;
 }
 
@@ -566,47 +581,77 @@ QLI_EXPORT int qli_bounded_workspace(const qli_problem* p, int64_t max_seq_len_k
   }
 }
 
+static int run_bounded_common(const qli_problem* p, int64_t max_seq_len_key, const int32_t* aslq_dev,
+                              const int32_t* aslk_dev, const void* query, const void* key, const void* weights,
+                              const void* q_scale, const void* k_scale, const int32_t* block_table,
+                              void* workspace, int32_t* sparse_indices, float* sparse_values, void* stream) {
+  int rc = validate_problem(p);
+  if (rc != QLI_OK) return rc;
+  Bounded g;
+  rc = bounded_geometry(*p, max_seq_len_key, g);
+  if (rc != QLI_OK) return rc;
+  if (g.h.rows == 0) return QLI_OK;
+  if (!aslk_dev || ((uintptr_t)aslk_dev % 4) != 0) return QLI_ERR_ARG;
+  const bool tnd = p->layout_query == QLI_LAYOUT_TND;
+  if (tnd && (!aslq_dev || ((uintptr_t)aslq_dev % 4) != 0)) return QLI_ERR_ARG;
+  RunArgs a;
+  a.p = p;
+  a.plan_dev = nullptr;
+  a.hdr = &g.h;
+  a.query = query;
+  a.key = key;
+  a.weights = weights;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.block_table = block_table;
+  a.workspace = workspace;
+  a.sparse_indices = sparse_indices;
+  a.sparse_values = p->return_value ? sparse_values : nullptr;
+  a.dump_row0 = a.dump_row1 = a.dump_cols = 0;
+  a.dots_out = nullptr;
+  a.scores_out = nullptr;
+  a.stream = stream;
+  a.aslk = aslk_dev;
+  a.max_len = max_seq_len_key;
+  a.stride = g.stride;
+  a.mstride = g.mstride;
+  a.merge_base = g.merge_base;
+  a.nseg = g.nseg;
+  if (tnd) {
+    a.aslq = aslq_dev;
+    a.tab_off = g.tab_off;
+  }
+  rc = check_run_args(a);
+  if (rc != QLI_OK) return rc;
+  if (tnd && launch_tnd_tables(a) != 0) return QLI_ERR_HIP;
+  if (launch_score(a, false) != 0) return QLI_ERR_HIP;
+  if (g.h.n_select > 0 && launch_select(a) != 0) return QLI_ERR_HIP;
+  return QLI_OK;
+}
+
 QLI_EXPORT int qli_run_bounded(const qli_problem* p, int64_t max_seq_len_key, const int32_t* aslk_dev,
                                const void* query, const void* key, const void* weights,
                                const void* q_scale, const void* k_scale, const int32_t* block_table,
                                void* workspace, int32_t* sparse_indices, float* sparse_values,
                                void* stream) {
   try {
-    int rc = validate_problem(p);
-    if (rc != QLI_OK) return rc;
-    Bounded g;
-    rc = bounded_geometry(*p, max_seq_len_key, g);
-    if (rc != QLI_OK) return rc;
-    if (g.h.rows == 0) return QLI_OK;
-    if (!aslk_dev || ((uintptr_t)aslk_dev % 4) != 0) return QLI_ERR_ARG;
-    RunArgs a;
-    a.p = p;
-    a.plan_dev = nullptr;
-    a.hdr = &g.h;
-    a.query = query;
-    a.key = key;
-    a.weights = weights;
-    a.q_scale = q_scale;
-    a.k_scale = k_scale;
-    a.block_table = block_table;
-    a.workspace = workspace;
-    a.sparse_indices = sparse_indices;
-    a.sparse_values = p->return_value ? sparse_values : nullptr;
-    a.dump_row0 = a.dump_row1 = a.dump_cols = 0;
-    a.dots_out = nullptr;
-    a.scores_out = nullptr;
-    a.stream = stream;
-    a.aslk = aslk_dev;
-    a.max_len = max_seq_len_key;
-    a.stride = g.stride;
-    a.mstride = g.mstride;
-    a.merge_base = g.merge_base;
-    a.nseg = g.nseg;
-    rc = check_run_args(a);
-    if (rc != QLI_OK) return rc;
-    if (launch_score(a, false) != 0) return QLI_ERR_HIP;
-    if (g.h.n_select > 0 && launch_select(a) != 0) return QLI_ERR_HIP;
-    return QLI_OK;
+    if (p && p->layout_query == QLI_LAYOUT_TND) return QLI_ERR_UNSUPPORTED;  // needs the query lengths
+    return run_bounded_common(p, max_seq_len_key, nullptr, aslk_dev, query, key, weights, q_scale, k_scale,
+                              block_table, workspace, sparse_indices, sparse_values, stream);
+  } catch (...) {
+    return QLI_ERR_ARG;
+  }
+}
+
+QLI_EXPORT int qli_run_bounded_tnd(const qli_problem* p, int64_t max_seq_len_key, const int32_t* aslq_dev,
+                                   const int32_t* aslk_dev, const void* query, const void* key,
+                                   const void* weights, const void* q_scale, const void* k_scale,
+                                   const int32_t* block_table, void* workspace, int32_t* sparse_indices,
+                                   float* sparse_values, void* stream) {
+  try {
+    if (p && p->layout_query != QLI_LAYOUT_TND) return QLI_ERR_UNSUPPORTED;
+    return run_bounded_common(p, max_seq_len_key, aslq_dev, aslk_dev, query, key, weights, q_scale, k_scale,
+                              block_table, workspace, sparse_indices, sparse_values, stream);
   } catch (...) {
     return QLI_ERR_ARG;
   }

@@ -115,6 +115,31 @@ struct Item {
 };
 static_assert(sizeof(Item) == 80, "item layout");
 
+// Bounded TND runs: tables written into the workspace (at byte offset
+// tab_off, int32 elements) by a one-workgroup kernel from the device
+// actual_seq_lengths_query, before the scoring kernel:
+//   rows_end[B]          running maximum of the prefix sums clamped to [0, T]:
+//                        batch b owns rows [rows_end[b-1], rows_end[b])
+//   group_start[B + 1]   8-row groups of the batches before b
+//   group_batch[groups]  batch of each group, -1 past the last real group
+//   row_batch[T]         batch of each row, -1 for rows past rows_end[B-1]
+// groups = T / 8 + B + 2 bounds the real groups (at most T/8 + B) plus the
+// groups of rows that belong to no batch (padding only).
+constexpr int kTndMaxBatch = 4096;  // the table kernel keeps both prefix tables in LDS
+struct TndTables {
+  int64_t rows_end, group_start, group_batch, row_batch, total;  // element offsets, element count
+};
+inline int64_t tnd_groups(int64_t batch, int64_t t) { return t / 8 + batch + 2; }
+inline TndTables tnd_tables(int64_t batch, int64_t t) {
+  TndTables x;
+  x.rows_end = 0;
+  x.group_start = (batch + 3) & ~int64_t(3);
+  x.group_batch = x.group_start + ((batch + 1 + 3) & ~int64_t(3));
+  x.row_batch = x.group_batch + ((tnd_groups(batch, t) + 3) & ~int64_t(3));
+  x.total = x.row_batch + t;
+  return x;
+}
+
 inline const PlanHeader* plan_header(const void* plan) {
   return static_cast<const PlanHeader*>(plan);
 }
@@ -147,8 +172,13 @@ struct RunArgs {
   int64_t max_len = 0;
   int64_t stride = 0, mstride = 0, merge_base = 0;
   int32_t nseg = 0;
+  // Bounded TND runs: device actual_seq_lengths_query and the byte offset of
+  // the tables (TndTables) in the workspace.
+  const int32_t* aslq = nullptr;
+  int64_t tab_off = 0;
 };
 int launch_score(const RunArgs& a, bool dump);
 int launch_select(const RunArgs& a);
+int launch_tnd_tables(const RunArgs& a);
 
 }  // namespace qli

@@ -66,6 +66,10 @@ struct ScoreParams {
   float* ws;
   int32_t* idx_out;
   float* val_out;
+  const int32_t* rows_end;     // bounded TND: the tables (TndTables), else null
+  const int32_t* group_start;
+  const int32_t* group_batch;
+  int32_t nbatch, trows;       //   batches, rows T
   const int32_t* aslk;  // bounded decode: key lengths on the device (else null)
   int64_t max_len;      //   clamp for them (original tokens)
   int64_t bstride;      //   workspace elements per row
@@ -224,22 +228,45 @@ void score_kernel(ScoreParams P) {
   // the bound, and a row that sees more than k entries stages its scores at
   // r * bstride of the workspace.  Otherwise the item and the rows come from
   // the plan's tables.
+  // Bounded TND (rows_end set): position pos is chunk pos % reg_chunks of
+  // group pos / reg_chunks in the tables' group order; groups past the real
+  // ones cover the rows that belong to no batch (padding only).
   Item it;
   int64_t skb = 0;
+  int rstart = 0, s1b = 0;  // bounded: the item's batch starts at row rstart and has s1b rows
   if (P.aslk) {
-    const int s1 = P.reg_rows;
-    const int groups = (s1 + 7) / 8;
-    const int b = pos / (P.reg_chunks * groups);
-    const int rem = pos - b * P.reg_chunks * groups;
-    const int g = rem / P.reg_chunks;
-    const int c = rem - g * P.reg_chunks;
-    skb = min<int64_t>(max(P.aslk[b], 0), P.max_len);
+    int b, g, c;
+    if (P.rows_end) {
+      g = pos / P.reg_chunks;
+      c = pos - g * P.reg_chunks;
+      const int real = P.group_start[P.nbatch];
+      if (g < real) {
+        b = P.group_batch[g];
+        rstart = b > 0 ? P.rows_end[b - 1] : 0;
+        s1b = P.rows_end[b] - rstart;
+        g -= P.group_start[b];
+      } else {
+        b = -1;
+        rstart = P.nbatch > 0 ? P.rows_end[P.nbatch - 1] : 0;
+        s1b = P.trows - rstart;
+        g -= real;
+      }
+    } else {
+      const int groups = (P.reg_rows + 7) / 8;
+      b = pos / (P.reg_chunks * groups);
+      const int rem = pos - b * P.reg_chunks * groups;
+      g = rem / P.reg_chunks;
+      c = rem - g * P.reg_chunks;
+      rstart = b * P.reg_rows;
+      s1b = P.reg_rows;
+    }
+    skb = b >= 0 ? min<int64_t>(max(P.aslk[b], 0), P.max_len) : 0;
     it.batch = b;
-    it.row0 = b * s1 + 8 * g;
-    it.nrows = min(8, s1 - 8 * g);
+    it.row0 = rstart + 8 * g;
+    it.nrows = max(0, min(8, s1b - 8 * g));
     int maxv = 0;
-    for (int u = 0; u < it.nrows; u++)
-      maxv = max(maxv, (int)visible_entries(P.mode, P.cmp, skb, s1, 8 * g + u));
+    for (int u = 0; u < it.nrows && b >= 0; u++)
+      maxv = max(maxv, (int)visible_entries(P.mode, P.cmp, skb, s1b, 8 * g + u));
     it.key0 = c * P.chunk;
     it.nkeys = min(P.chunk, maxv - it.key0);
     it.flags = c == 0 ? kItemPad : 0;
@@ -247,8 +274,8 @@ void score_kernel(ScoreParams P) {
     it = P.items[pos];
   }
   auto row_vis = [&](int64_t r) __attribute__((always_inline)) {
-    return P.aslk ? (int)visible_entries(P.mode, P.cmp, skb, P.reg_rows, r - (int64_t)it.batch * P.reg_rows)
-                  : rinfo[r].vis;
+    if (!P.aslk) return rinfo[r].vis;
+    return it.batch < 0 ? 0 : (int)visible_entries(P.mode, P.cmp, skb, s1b, r - rstart);
   };
 
   // Rows that see fewer than k entries: slots vis..k-1 are -1 / -inf.
@@ -1125,6 +1152,8 @@ struct SelectParams {
   const int32_t* aslk;
   int64_t max_len, stride, mstride, merge_base;
   int32_t s1, mode, cmp, nseg, pass;
+  const int32_t* rows_end;   // bounded TND: the tables (TndTables), else null
+  const int32_t* row_batch;
 };
 
 // The selection of this workgroup in bounded decode, from the row's key
@@ -1137,8 +1166,20 @@ __device__ __forceinline__ bool bounded_entry(const SelectParams& S, SelectEntry
   const int w = (int)blockIdx.x;
   const int r = S.pass == 1 ? w / S.nseg : w;
   const int s = S.pass == 1 ? w - r * S.nseg : 0;
-  const int64_t skb = min<int64_t>(max(S.aslk[r / S.s1], 0), S.max_len);
-  const int vis = (int)visible_entries(S.mode, S.cmp, skb, S.s1, r % S.s1);
+  int b, i, s1b;
+  if (S.row_batch) {  // TND: the row's batch from the tables; rows of no batch need no selection
+    b = S.row_batch[r];
+    if (b < 0) return false;
+    const int rstart = b > 0 ? S.rows_end[b - 1] : 0;
+    s1b = S.rows_end[b] - rstart;
+    i = r - rstart;
+  } else {
+    b = r / S.s1;
+    s1b = S.s1;
+    i = r - b * S.s1;
+  }
+  const int64_t skb = min<int64_t>(max(S.aslk[b], 0), S.max_len);
+  const int vis = (int)visible_entries(S.mode, S.cmp, skb, s1b, i);
   if (vis <= S.k) return false;
   const int nsr = (vis + kSelSegment - 1) / kSelSegment;  // segments of this row
   se.row = r;
@@ -1378,6 +1419,15 @@ int launch_score(const RunArgs& a, bool dump) {
     P.rinfo = reinterpret_cast<const RowInfo*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_rows);
   }
   P.aslk = a.aslk;  // bounded decode (the header then describes the bound)
+  if (a.aslq) {
+    const TndTables t = tnd_tables(a.p->batch, a.p->s1);
+    const int32_t* tab = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(a.workspace) + a.tab_off);
+    P.rows_end = tab + t.rows_end;
+    P.group_start = tab + t.group_start;
+    P.group_batch = tab + t.group_batch;
+    P.nbatch = a.p->batch;
+    P.trows = a.p->s1;
+  }
   P.max_len = a.max_len;
   P.bstride = a.stride;
   P.mode = a.p->sparse_mode;
@@ -1425,6 +1475,12 @@ int launch_select(const RunArgs& a) {
       a.plan_dev ? reinterpret_cast<const SelectEntry*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_select)
                  : nullptr;
   S.aslk = a.aslk;
+  if (a.aslq) {
+    const TndTables t = tnd_tables(a.p->batch, a.p->s1);
+    const int32_t* tab = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(a.workspace) + a.tab_off);
+    S.rows_end = tab + t.rows_end;
+    S.row_batch = tab + t.row_batch;
+  }
   S.max_len = a.max_len;
   S.stride = a.stride;
   S.mstride = a.mstride;
@@ -1452,6 +1508,98 @@ int launch_select(const RunArgs& a) {
   };
   hipError_t e = pass(1, table, h->n_select, h->max_cand);
   if (e == hipSuccess && h->n_select2 > 0) e = pass(2, table ? table + h->n_select : nullptr, h->n_select2, h->max_cand2);
+  return e == hipSuccess ? 0 : (int)e;
+}
+
+// ---------------------------------------------------------------------------
+// Bounded TND runs: the row and group tables (TndTables) from the device
+// actual_seq_lengths_query.  One workgroup: inclusive scans over the
+// batches, 1024 at a time with a carry (a running maximum clamped to [0, T]
+// makes any input a valid partition of the rows), then a binary search per
+// group and per row over the prefix tables held in LDS.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kTabThreads = 1024;
+
+__device__ int block_incl_scan(int v, bool use_max, int* buf) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kTabThreads; off <<= 1) {
+    const int o = tid >= off ? buf[tid - off] : 0;  // 0 is the identity of both (values are >= 0)
+    __syncthreads();
+    buf[tid] = use_max ? max(buf[tid], o) : buf[tid] + o;
+    __syncthreads();
+  }
+  const int r = buf[tid];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kTabThreads) void tnd_tables_kernel(const int32_t* aslq, int32_t nb, int32_t t,
+                                                                 int32_t groups, int32_t* tab, TndTables lay) {
+  __shared__ int32_t s_end[kTndMaxBatch];
+  __shared__ int32_t s_grp[kTndMaxBatch + 1];
+  __shared__ int32_t buf[kTabThreads];
+  const int tid = threadIdx.x;
+  int carry_end = 0, carry_grp = 0;
+  if (tid == 0) s_grp[0] = 0;
+  for (int base = 0; base < nb; base += kTabThreads) {
+    const int b = base + tid;
+    const int v = b < nb ? min(max(aslq[b], 0), t) : 0;
+    const int end = max(block_incl_scan(v, true, buf), carry_end);
+    if (b < nb) s_end[b] = end;
+    __syncthreads();
+    const int before = b == 0 ? 0 : (tid > 0 ? s_end[b - 1] : carry_end);
+    const int rows_b = b < nb ? end - before : 0;
+    const int grp = block_incl_scan((rows_b + 7) / 8, false, buf) + carry_grp;
+    if (b < nb) s_grp[b + 1] = grp;
+    __syncthreads();
+    const int last = min(nb - 1, base + kTabThreads - 1);
+    carry_end = s_end[last];
+    carry_grp = s_grp[last + 1];
+    __syncthreads();
+  }
+  __syncthreads();  // s_grp[0] (no batches: the loop above has no barrier)
+  for (int b = tid; b < nb; b += kTabThreads) tab[lay.rows_end + b] = s_end[b];
+  for (int b = tid; b <= nb; b += kTabThreads) tab[lay.group_start + b] = s_grp[b];
+  const int real = s_grp[nb];
+  for (int g = tid; g < groups; g += kTabThreads) {
+    int b = -1;
+    if (g < real) {  // the batch with s_grp[b] <= g < s_grp[b + 1]: the last b with s_grp[b] <= g
+      int lo = 0, hi = nb - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_grp[mid] <= g) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+    }
+    tab[lay.group_batch + g] = b;
+  }
+  const int used = nb > 0 ? s_end[nb - 1] : 0;
+  for (int r = tid; r < t; r += kTabThreads) {
+    int b = -1;
+    if (r < used) {  // the first b with s_end[b] > r
+      int lo = 0, hi = nb - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_end[mid] > r) hi = mid; else lo = mid + 1;
+      }
+      b = lo;
+    }
+    tab[lay.row_batch + r] = b;
+  }
+}
+
+}  // namespace
+
+int launch_tnd_tables(const RunArgs& a) {
+  const TndTables lay = tnd_tables(a.p->batch, a.p->s1);
+  int32_t* tab = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + a.tab_off);
+  const int groups = (int)tnd_groups(a.p->batch, a.p->s1);
+  const hipError_t e = launch(tnd_tables_kernel, dim3(1), dim3(kTabThreads), static_cast<hipStream_t>(a.stream),
+                              a.aslq, (int32_t)a.p->batch, (int32_t)a.p->s1, (int32_t)groups, tab, lay);
   return e == hipSuccess ? 0 : (int)e;
 }
 

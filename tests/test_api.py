@@ -316,6 +316,25 @@ def bounded_workspace_expected(p, max_len):
     return ((4 * total + 15) // 16 * 16) + 4 * total if nseg > 1 else 4 * total
 
 
+def bounded_tnd_workspace_expected(p, max_len):
+    """TND: the BSND layout over T rows, then (16-byte aligned) the row and group
+    tables: rows_end[B], group_start[B + 1], group_batch[T // 8 + B + 2] (each
+    padded to 4 elements) and row_batch[T], int32."""
+    b, t = p["batch"], p["s1"]
+    base = bounded_workspace_expected(dict(p, batch=1, s1=t), max_len)
+    up4 = lambda n: (n + 3) // 4 * 4
+    return (base + 15) // 16 * 16 + 4 * (up4(b) + up4(b + 1) + up4(t // 8 + b + 2) + t)
+
+
+@pytest.mark.parametrize("b,t,k,max_len", [(3, 40, 256, 5000), (1, 7, 2048, 100), (5, 300, 64, 20000)])
+def test_bounded_tnd_workspace(qli, b, t, k, max_len):
+    spec = synth.small(layout=synth.TND, batch=b, s1=t, aslq=[t] * b, aslk=[max(max_len, 1)] * b, block_size=64,
+                       sparse_count=k, sparse_mode=3)
+    p = synth.make_inputs(spec, 1)["problem"]
+    rc, ws = qli.qli_bounded_workspace(qli.Problem.from_dict(p), max_len)
+    assert rc == 0 and ws == bounded_tnd_workspace_expected(p, max_len)
+
+
 @pytest.mark.parametrize("s1,k,cmp,max_len", [(1, 512, 1, 1000), (4, 2048, 1, 8192), (2, 256, 4, 70000),
                                                 (3, 100, 1, 0), (1, 2048, 1, 140000), (8, 256, 1, 3000),
                                                 (13, 2048, 1, 20000), (64, 512, 2, 10000)])
@@ -338,8 +357,14 @@ def test_bounded_rejects_without_launching(qli):
     blocks = p["max_blocks_per_seq"]
     assert qli.qli_bounded_workspace(prob, (blocks + 1) * 64)[0] == qli.QLI_ERR_ARG  # beyond the block table
     tnd = qli.Problem.from_dict(dict(p, layout_query=synth.TND))
-    assert qli.qli_bounded_workspace(tnd, bound)[0] == qli.QLI_ERR_UNSUPPORTED
-    assert qli.qli_run_bounded(tnd, bound, *args) == qli.QLI_ERR_UNSUPPORTED
+    assert qli.qli_bounded_workspace(tnd, bound) == (qli.QLI_OK, bounded_tnd_workspace_expected(
+        dict(p, layout_query=synth.TND), bound))
+    assert qli.qli_run_bounded(tnd, bound, *args) == qli.QLI_ERR_UNSUPPORTED     # TND needs the query lengths
+    assert qli.qli_run_bounded_tnd(prob, bound, fake, *args) == qli.QLI_ERR_UNSUPPORTED  # BSND
+    assert qli.qli_run_bounded_tnd(tnd, bound, None, *args) == qli.QLI_ERR_ARG   # actual_seq_lengths_query
+    assert qli.qli_run_bounded_tnd(tnd, bound, fake + 2, *args) == qli.QLI_ERR_ARG
+    many = qli.Problem.from_dict(dict(p, layout_query=synth.TND, batch=4097))
+    assert qli.qli_bounded_workspace(many, bound)[0] == qli.QLI_ERR_UNSUPPORTED
     wide = qli.Problem.from_dict(dict(p, s1=5))  # prefill tiles: supported, same workspace layout
     assert qli.qli_bounded_workspace(wide, bound) == (qli.QLI_OK, bounded_workspace_expected(dict(p, s1=5), bound))
     a = list(args)

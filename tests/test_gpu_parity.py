@@ -480,6 +480,98 @@ def test_bounded_graph_replay(case):
         assert np.array_equal(val.cpu().numpy(), p_val), "lengths %s" % lens
 
 
+BOUNDED_TND = {
+    # (spec whose cache holds the bound for every batch, device aslq, actual key lengths)
+    "tnd_mixed_padding_rows": (synth.small(layout=synth.TND, batch=3, s1=40, aslq=[5, 25, 33], aslk=[2000] * 3,
+                                           block_size=64, sparse_count=256, sparse_mode=3), [5, 25, 33],
+                               [300, 2000, 900]),
+    "tnd_chunks_merges": (synth.small(layout=synth.TND, batch=2, s1=20, aslq=[7, 20], aslk=[20000] * 2,
+                                      block_size=128, sparse_count=2048, sparse_mode=3), [7, 20], [20000, 9000]),
+    "tnd_fp8_mode0_empty_batches": (synth.small(qk=synth.FP8, layout=synth.TND, batch=4, s1=30,
+                                                aslq=[0, 10, 10, 28], aslk=[5000] * 4, block_size=32,
+                                                sparse_count=300), [0, 10, 10, 28], [100, 5000, 300, 0]),
+    "tnd_decode_like_cmp2": (synth.small(layout=synth.TND, batch=4, s1=8, aslq=[2, 4, 6, 8], aslk=[3000] * 4,
+                                         block_size=64, sparse_count=256, sparse_mode=3, cmp_ratio=2),
+                             [2, 4, 6, 8], [3000, 100, 2500, 1]),
+}
+
+
+def bounded_tnd_run(name, aslq, lens, seed=4):
+    import torch
+    spec = BOUNDED_TND[name][0]
+    inp = synth.make_inputs(spec, seed)
+    dev = device_inputs(inp)
+    bix = qli_mod().BoundedIndexer(inp["problem"], int(spec.aslk[0]))
+    q = torch.tensor(aslq, dtype=torch.int32, device="cuda")
+    k = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    idx, val = bix.alloc_outputs()
+    bix.run(k, dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
+            idx, val, aslq_dev=q)
+    torch.cuda.synchronize()
+    return inp, dev, idx.cpu().numpy(), val.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", list(BOUNDED_TND))
+def test_bounded_tnd_matches_planned(ora, name):
+    """qli_run_bounded_tnd (query and key lengths read on the device) against
+    qli_plan + qli_run: bit-identical where the plan also uses the 8-row tiles
+    (some batch has more than 4 rows), else within the parity rule of the
+    oracle; every row's structure checked."""
+    _, aslq, lens = BOUNDED_TND[name]
+    log("bounded tnd %s: aslq %s lens %s" % (name, aslq, lens))
+    inp, dev, idx, val = bounded_tnd_run(name, aslq, lens)
+    p = inp["problem"]
+    aq, ak = np.asarray(aslq, dtype=np.int32), np.asarray(lens, dtype=np.int32)
+    vis = ora.row_visible(p["layout_query"], p["batch"], p["s1"], p["sparse_mode"], p["cmp_ratio"], aq, ak)
+    check_structure(idx, val, vis, p["sparse_count"])
+    per_batch = np.diff(np.concatenate([[0], aq]))
+    sub = dict(inp, aslq=aq, aslk=ak)
+    if per_batch.max() > 4:
+        p_idx, p_val = planned(sub, dev, lens)
+        assert np.array_equal(idx, p_idx) and np.array_equal(val, p_val)
+    else:
+        rc, _, _, sc = ora.indexer(sub, scores_cols=max(1, int(vis.max())))
+        assert rc == 0
+        for r in range(vis.size):
+            check_row(r, int(vis[r]), p["sparse_count"], idx[r], val[r], sc[r, :vis[r]], rtol_of(inp))
+
+
+def test_bounded_tnd_graph_replay():
+    """qli_run_bounded_tnd captured once; between replays both the device query
+    prefix sums and the key lengths change (rows move between batches, batches
+    empty out, rows fall past the last prefix sum): every replay equals
+    qli_plan + qli_run for the new lengths."""
+    import torch
+    name = "tnd_chunks_merges"
+    spec = BOUNDED_TND[name][0]
+    inp = synth.make_inputs(spec, 6)
+    dev = device_inputs(inp)
+    bound = int(spec.aslk[0])
+    bix = qli_mod().BoundedIndexer(inp["problem"], bound)
+    q = torch.tensor([7, 20], dtype=torch.int32, device="cuda")
+    k = torch.tensor([bound, bound], dtype=torch.int32, device="cuda")
+    idx, val = bix.alloc_outputs()
+    args = (k, dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"], idx, val)
+    bix.run(*args, aslq_dev=q)  # first launches outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bix.run(*args, aslq_dev=q)
+    for aslq, lens in (([7, 20], [20000, 20000]), ([0, 12], [5000, 8193]), ([20, 20], [12, 20000]),
+                       ([3, 9], [19999, 0])):
+        q.copy_(torch.tensor(aslq, dtype=torch.int32))
+        k.copy_(torch.tensor(lens, dtype=torch.int32))
+        idx.fill_(-7)
+        val.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        sub = dict(inp, aslq=np.asarray(aslq, dtype=np.int32))
+        p_idx, p_val = planned(sub, dev, lens)
+        assert np.array_equal(idx.cpu().numpy(), p_idx), "aslq %s lens %s" % (aslq, lens)
+        assert np.array_equal(val.cpu().numpy(), p_val), "aslq %s lens %s" % (aslq, lens)
+
+
 # --- seeded random problems -----------------------------------------------------
 def random_spec(i: int):
     """A random small problem (seeded by i): dtype, layout, batch, ragged key
