@@ -575,7 +575,7 @@ def main() -> int:
             "host_enqueue_us_per_step": round(host_us, 2),
             "cache_state": "every input cold: %d rotated copies of all inputs (%.1f MB each)" % (R, set_bytes / 1e6),
             "score_items": info.score_items, "select_rows": info.select_rows,
-            "bounded_decode_ms_per_step": None if bounded_ms is None else round(bounded_ms, 5),
+            "bounded_ms_per_step": None if bounded_ms is None else round(bounded_ms, 5),
         },
         "cpu_baseline": None,
     }
