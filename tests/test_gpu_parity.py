@@ -625,6 +625,44 @@ def test_parity_random(ora, i):
         check_row(r, int(vis[r]), k, gidx[r], gval[r], osc[r, :vis[r]], rtol_of(inp))
 
 
+@pytest.mark.parametrize("i", range(12))
+def test_bounded_random(ora, i):
+    """Seeded random problems (the generator above; BSND with every query row
+    active) run without a host plan, lengths on the device and the bound at the
+    longest key: bit-identical to qli_plan + qli_run where the plan uses the
+    same tiles (every BSND problem, TND with a batch of more than 4 rows),
+    else within the parity rule of the oracle."""
+    import dataclasses
+    import torch
+    spec = random_spec(100 + i)
+    if spec.layout == synth.BSND:
+        spec = dataclasses.replace(spec, aslq=None)
+    inp = synth.make_inputs(spec, i)
+    p = inp["problem"]
+    log("bounded random %d: %s" % (i, spec))
+    dev = device_inputs(inp)
+    bound = max(1, int(max(inp["aslk"])))
+    bix = qli_mod().BoundedIndexer(p, bound)
+    k_dev = torch.from_numpy(inp["aslk"].astype(np.int32)).cuda()
+    q_dev = torch.from_numpy(np.asarray(inp["aslq"], dtype=np.int32)).cuda() if spec.layout == synth.TND else None
+    idx, val = bix.alloc_outputs()
+    bix.run(k_dev, dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
+            idx, val, aslq_dev=q_dev)
+    torch.cuda.synchronize()
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    vis = vis_of(ora, inp)
+    check_structure(idx, val, vis, p["sparse_count"])
+    tiles_match = spec.layout == synth.BSND or np.diff(np.concatenate([[0], inp["aslq"]])).max() > 4
+    if tiles_match:
+        p_idx, p_val, _ = run_gpu(inp, dev)
+        assert np.array_equal(idx, p_idx) and np.array_equal(val, p_val)
+    else:
+        rc, _, _, sc = ora.indexer(inp, scores_cols=max(1, int(vis.max())))
+        assert rc == 0
+        for r in range(rows_of(p)):
+            check_row(r, int(vis[r]), p["sparse_count"], idx[r], val[r], sc[r, :vis[r]], rtol_of(inp))
+
+
 @pytest.mark.parametrize("case", ["bsnd_int8_causal_bs48_pad", "long_rt2_causal", "tnd_int8_prefill_mixed"])
 def test_without_values(case):
     """return_value = 0 (参数说明: sparse_values optional): no value buffer, the
