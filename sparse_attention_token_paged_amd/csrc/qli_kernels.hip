@@ -221,16 +221,16 @@ void score_kernel(ScoreParams P) {
   for (int round = 0;; round++) {
   const int pos = pos_of(round);
   if (pos >= P.n_items) break;  // uniform
-  // Bounded prefill (key lengths on the device, BSND, all S1 = reg_rows query
-  // rows of every batch active): position pos is chunk pos % reg_chunks of
-  // 8-row group (pos / reg_chunks) % groups of batch pos / (reg_chunks *
-  // groups); rows' visible counts follow from the batch's length, clamped to
-  // the bound, and a row that sees more than k entries stages its scores at
-  // r * bstride of the workspace.  Otherwise the item and the rows come from
-  // the plan's tables.
-  // Bounded TND (rows_end set): position pos is chunk pos % reg_chunks of
-  // group pos / reg_chunks in the tables' group order; groups past the real
-  // ones cover the rows that belong to no batch (padding only).
+  // Without a plan (key lengths on the device: aslk set) the item follows
+  // from its position: chunk pos % reg_chunks of an 8-row group.  BSND (all
+  // reg_rows query rows of every batch active): group (pos / reg_chunks) %
+  // groups of batch pos / (reg_chunks * groups).  TND (rows_end set): group
+  // pos / reg_chunks in the order of the row and group tables; groups past
+  // the real ones cover the rows that belong to no batch (padding only).
+  // Rows' visible counts follow from the batch's length, clamped to the
+  // bound, and a row that sees more than k entries stages its scores at
+  // r * bstride of the workspace.  With a plan, the item and the rows come
+  // from its tables.
   Item it;
   int64_t skb = 0;
   int rstart = 0, s1b = 0;  // bounded: the item's batch starts at row rstart and has s1b rows
