@@ -107,16 +107,14 @@ __device__ __forceinline__ uint2 encode8(const float (&f)[8], float amax, uint32
 // stores.  For key entries the destination (sequence, position, then the
 // block-table entry) is requested before the row data, so the dependent
 // block-table load waits only for the destination loads (vector loads
-// complete in issue order).  Queries take 2 groups (39 VGPRs, 8 waves per
-// SIMD: 4 groups at 6 waves measured 44.8 against 40.9 us for the prefill
-// query); key entries take 4 (their block-table round trip needs the depth:
-// 24.0 against 24.6 us for the headline cache).
-template <bool PAGED>
-constexpr int groups_per_iteration() { return PAGED ? 4 : 2; }
+// complete in issue order).  Two groups (39 VGPRs, 8 waves per SIMD) beat
+// deeper ones, whose registers cost occupancy: the headline decode cache's
+// append took 21.6, 20.6, 23.7 and 25.1 us with 1, 2, 4 and 8 groups, and
+// the prefill query 40.9 us with 2 groups against 44.8 with 4.
+constexpr int kGroups = 2;
 
 template <int QK, bool PAGED>
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams P) {
-  constexpr int kGroups = groups_per_iteration<PAGED>();
   const int lane = threadIdx.x & 63;
   const int piece = lane & 15;  // elements [8 * piece, 8 * piece + 8) of the row
   const int64_t waves = (int64_t)gridDim.x * (kQuantThreads / 64);
@@ -188,7 +186,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams P) 
 
 int launch_quantize(int32_t qk, bool paged, const QuantParams& P, void* stream) {
   const int64_t groups = (P.n + 3) / 4;
-  const int64_t per_wg = (kQuantThreads / 64) * (paged ? groups_per_iteration<true>() : groups_per_iteration<false>());
+  const int64_t per_wg = (kQuantThreads / 64) * kGroups;  // row groups per workgroup and iteration
   const int64_t wgs = std::min<int64_t>((groups + per_wg - 1) / per_wg, kQuantMaxGrid);
   if (wgs <= 0) return QLI_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
