@@ -20,7 +20,7 @@
  * (every e4m3 product is a multiple of 2^-18 below 2^18, and 128 of them
  * need fewer than 53 bits); the score formula is evaluated in fp64 in the
  * literal order of the formula.  Readings of points the page leaves open
- * are marked "reading:" and listed in the design doc.
+ * are marked "reading:" where they are applied.
  *
  * Every function here is pinned by tests under tests/ (test_oracle_*.py)
  * against brute force, closed forms, invariants or library routines.

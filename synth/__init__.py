@@ -5,7 +5,7 @@ distributions of the workloads; it holds none of the indexer's arithmetic.
 It is the one module that both the HIP path's tests/benchmark and the CPU
 oracle consume.
 
-Recipe (also in DESIGN.md): ``numpy.random.Generator(PCG64(seed))``; draw
+Recipe: ``numpy.random.Generator(PCG64(seed))``; draw
 order: key lengths (when random), block permutation, K, ScaleK, Q, ScaleQ, W.
   * int8 q/k: integers in [-128, 127] (both ends included)
   * e4m3fn q/k: uniform(-8, 8) in float32, rounded to float8_e4m3fn (RNE)
