@@ -536,6 +536,20 @@ def test_bounded_tnd_matches_planned(ora, name):
             check_row(r, int(vis[r]), p["sparse_count"], idx[r], val[r], sc[r, :vis[r]], rtol_of(inp))
 
 
+def test_bounded_tnd_prefix_sums_out_of_contract():
+    """Device query prefix sums that break the contract (decreasing, beyond T,
+    negative) are taken as their running maximum clamped to [0, T]: the run
+    completes and equals qli_plan + qli_run on that partition."""
+    name = "tnd_mixed_padding_rows"
+    spec = BOUNDED_TND[name][0]
+    bad, lens = [30, -4, 70], [2000, 700, 1500]
+    clamped = list(np.minimum(np.maximum.accumulate(np.maximum(bad, 0)), spec.s1))
+    inp, dev, idx, val = bounded_tnd_run(name, bad, lens)
+    sub = dict(inp, aslq=np.asarray(clamped, dtype=np.int32))
+    p_idx, p_val = planned(sub, dev, lens)
+    assert np.array_equal(idx, p_idx) and np.array_equal(val, p_val)
+
+
 def test_bounded_tnd_graph_replay():
     """qli_run_bounded_tnd captured once; between replays both the device query
     prefix sums and the key lengths change (rows move between batches, batches
