@@ -417,3 +417,12 @@ def test_append_keys_rejects_bad_arguments(qli):
     assert call(x=A16 + 4) == qli.QLI_ERR_ARG
     assert call(kc=A16 + 8) == qli.QLI_ERR_ARG
     assert call(qk=1, ks=A16 + 2) == qli.QLI_ERR_ARG
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with a message, before touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and not r.stdout.strip()
