@@ -229,3 +229,39 @@ def test_chain_graph_replay():
         assert np.array_equal(g_idx, idx.cpu().numpy()), "replay %d: indices differ" % rep
         assert np.array_equal(g_val, val.cpu().numpy()), "replay %d: values differ" % rep
         assert (g_idx[:, 0] >= 0).all()
+
+
+@pytest.mark.parametrize("name", ["quantize_query_prefill_t8192", "append_keys_decode_b24_sk8192"])
+def test_producer_full_size(name):
+    """The producer workloads at the benchmark's sizes (524288 query head
+    vectors; the headline decode cache's 196608 key entries through its
+    permuted block table), every row against the oracle, bit-exact."""
+    import torch
+    import sparse_attention_token_paged_amd as qli
+    w = synth.producer_inputs(name)
+    qk, x = w["qk"], w["x"]
+    n = x.shape[0]
+    log("producer full size %s: %d rows" % (name, n))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    sdt = torch.float16 if qk == 0 else torch.float32
+    if w["kind"] == "query":
+        q = torch.full((n, 128), 0x5A, dtype=torch.uint8, device="cuda")
+        s = torch.zeros((n,), dtype=sdt, device="cuda")
+        assert qli.qli_quantize_query(qk, n, dev(x.view(np.int16)), q, s, qli.current_stream()) == qli.QLI_OK
+        torch.cuda.synchronize()
+        codes, scales = oq.quantize_rows(x, qk)
+        assert np.array_equal(q.cpu().numpy(), codes)
+        assert np.array_equal(s.cpu().numpy().view(np.uint16), scales.view(np.uint16))
+    else:
+        bs, nb, stride = w["block_size"], w["num_blocks"], w["stride"]
+        kc0 = np.full(nb * stride, 0xA5, np.uint8)
+        ks0 = np.full(nb * bs, 7.0, np.float16 if qk == 0 else np.float32)
+        kc, ks = dev(kc0), dev(ks0)
+        assert qli.qli_append_keys(qk, n, dev(x.view(np.int16)), dev(w["batch_idx"]), dev(w["pos"]),
+                                   dev(w["block_table"]), w["batch"], w["max_blocks"], nb, bs, stride, kc, ks,
+                                   qli.current_stream()) == qli.QLI_OK
+        torch.cuda.synchronize()
+        oq.append_keys(x, w["batch_idx"], w["pos"], w["block_table"], w["batch"], w["max_blocks"], nb, bs, stride,
+                       kc0, ks0, qk)
+        assert np.array_equal(kc.cpu().numpy(), kc0)
+        assert np.array_equal(ks.cpu().numpy(), ks0)
