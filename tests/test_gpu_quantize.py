@@ -265,3 +265,45 @@ def test_producer_full_size(name):
                        kc0, ks0, qk)
         assert np.array_equal(kc.cpu().numpy(), kc0)
         assert np.array_equal(ks.cpu().numpy(), ks0)
+
+
+@pytest.mark.parametrize("qk,n", [(0, 1), (1, 3), (0, 5)])
+def test_quantize_query_tiny(qk, n):
+    """1, 3 and 5 rows: a partial 4-row group (and one group plus a partial)."""
+    import torch
+    import sparse_attention_token_paged_amd as qli
+    xb = query_rows(61 + n, max(n, 7))[:n]
+    q = torch.full((n, 128), 0x5A, dtype=torch.uint8, device="cuda")
+    s = torch.zeros((n,), dtype=torch.float16 if qk == 0 else torch.float32, device="cuda")
+    assert qli.qli_quantize_query(qk, n, torch.from_numpy(xb.view(np.int16)).cuda(), q, s,
+                                  qli.current_stream()) == qli.QLI_OK
+    torch.cuda.synchronize()
+    codes, scales = oq.quantize_rows(xb, qk)
+    assert np.array_equal(q.cpu().numpy(), codes)
+    dt = np.uint16 if qk == 0 else np.uint32
+    assert np.array_equal(s.cpu().numpy().view(dt), scales.view(dt))
+
+
+@pytest.mark.parametrize("qk", [0, 1], ids=["int8", "e4m3fn"])
+def test_append_keys_block_1024(qk):
+    """The largest block size (1024 entries per block, 128 KiB blocks) with a padded stride."""
+    import torch
+    import sparse_attention_token_paged_amd as qli
+    rng = np.random.default_rng(71)
+    B, mb, bs = 2, 3, 1024
+    nb, stride = B * mb + 1, bs * 128 + 32
+    table = rng.permutation(nb)[:B * mb].astype(np.int32).reshape(B, mb)
+    slots = rng.permutation(B * mb * bs)[:3000]
+    bidx, pos = (slots // (mb * bs)).astype(np.int32), (slots % (mb * bs)).astype(np.int32)
+    xb = query_rows(72, bidx.size)
+    kc0 = np.full(nb * stride, 0xA5, np.uint8)
+    ks0 = np.full(nb * bs, 7.0, np.float16 if qk == 0 else np.float32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    kc, ks = dev(kc0), dev(ks0)
+    assert qli.qli_append_keys(qk, bidx.size, dev(xb.view(np.int16)), dev(bidx), dev(pos), dev(table), B, mb, nb,
+                               bs, stride, kc, ks, qli.current_stream()) == qli.QLI_OK
+    torch.cuda.synchronize()
+    oq.append_keys(xb, bidx, pos, table, B, mb, nb, bs, stride, kc0, ks0, qk)
+    assert np.array_equal(kc.cpu().numpy(), kc0)
+    dt = np.uint16 if qk == 0 else np.uint32
+    assert np.array_equal(ks.cpu().numpy().view(dt), ks0.view(dt))
