@@ -307,3 +307,53 @@ def test_append_keys_block_1024(qk):
     assert np.array_equal(kc.cpu().numpy(), kc0)
     dt = np.uint16 if qk == 0 else np.uint32
     assert np.array_equal(ks.cpu().numpy().view(dt), ks0.view(dt))
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_producer_random(i):
+    """Seeded random producer problems: dtype, query row count, cache geometry
+    (block size, padded stride, sequences, table width, spare blocks), a random
+    subset of distinct slots plus entries outside the cache; query codes and
+    the whole cache bit-exact against the oracle."""
+    import torch
+    import sparse_attention_token_paged_amd as qli
+    rng = np.random.default_rng(9000 + i)
+    qk = int(rng.integers(0, 2))
+    dt = np.uint16 if qk == 0 else np.uint32
+    sdt = torch.float16 if qk == 0 else torch.float32
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    # query
+    n = int(rng.integers(1, 3000))
+    xb = query_rows(9100 + i, max(n, 7))[:n]
+    q = torch.full((n, 128), 0x5A, dtype=torch.uint8, device="cuda")
+    s = torch.zeros((n,), dtype=sdt, device="cuda")
+    assert qli.qli_quantize_query(qk, n, dev(xb.view(np.int16)), q, s, qli.current_stream()) == qli.QLI_OK
+    # key cache
+    bs = int(rng.choice([16, 32, 48, 64, 128, 256, 512]))
+    B, mb = int(rng.integers(1, 5)), int(rng.integers(1, 6))
+    nb = B * mb + int(rng.integers(0, 3))
+    stride = bs * 128 + 16 * int(rng.integers(0, 4))
+    table = rng.permutation(nb)[:B * mb].astype(np.int32).reshape(B, mb)
+    m = int(rng.integers(1, B * mb * bs + 1))
+    slots = rng.permutation(B * mb * bs)[:m]
+    bidx = np.concatenate([slots // (mb * bs), rng.integers(-2, B + 2, 4)]).astype(np.int32)
+    pos = np.concatenate([slots % (mb * bs), rng.integers(-3, mb * bs + 3, 4)]).astype(np.int32)
+    # the random extra entries must not collide with a chosen slot: move colliding ones out of range
+    taken = set(zip((slots // (mb * bs)).tolist(), (slots % (mb * bs)).tolist()))
+    for e in range(m, bidx.size):
+        if (int(bidx[e]), int(pos[e])) in taken:
+            pos[e] = -1
+    kb = query_rows(9200 + i, max(bidx.size, 7))[:bidx.size]
+    log("producer random %d: qk %d n %d bs %d B %d mb %d entries %d" % (i, qk, n, bs, B, mb, bidx.size))
+    kc0 = np.full(nb * stride, 0xA5, np.uint8)
+    ks0 = np.full(nb * bs, 7.0, np.float16 if qk == 0 else np.float32)
+    kc, ks = dev(kc0), dev(ks0)
+    assert qli.qli_append_keys(qk, bidx.size, dev(kb.view(np.int16)), dev(bidx), dev(pos), dev(table), B, mb, nb,
+                               bs, stride, kc, ks, qli.current_stream()) == qli.QLI_OK
+    torch.cuda.synchronize()
+    codes, scales = oq.quantize_rows(xb, qk)
+    assert np.array_equal(q.cpu().numpy(), codes)
+    assert np.array_equal(s.cpu().numpy().view(dt), scales.view(dt))
+    oq.append_keys(kb, bidx, pos, table, B, mb, nb, bs, stride, kc0, ks0, qk)
+    assert np.array_equal(kc.cpu().numpy(), kc0)
+    assert np.array_equal(ks.cpu().numpy().view(dt), ks0.view(dt))
