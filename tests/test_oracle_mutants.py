@@ -39,6 +39,13 @@ MUTANTS = [
     ("value padding", "ov[j] = -INFINITY;", "ov[j] = 0.0f;"),
     ("TND local index", "*i = r - start;", "*i = r;"),
     ("BSND query counts ignored", "int64_t n = p->aslq ? p->aslq[bb] : p->s1_or_t;", "int64_t n = p->s1_or_t;"),
+    # the FLOAT32 scale / weight decoding of the FLOAT8_e4m3fn pairing
+    ("fp32 element stride 2", "memcpy(&f, (const char *)base + 4 * i, 4);",
+     "memcpy(&f, (const char *)base + 8 * i, 4);"),
+    ("fp32 scales read as fp16", "if (scale_dtype == 0) {", "if (scale_dtype >= 0) {"),
+    ("fp32 weight ignored", "double w = scale_value(p->weights, r * QLIO_HEADS + g, p->scale_dtype);",
+     "double w = p->scale_dtype == 1 ? 1.0 : scale_value(p->weights, r * QLIO_HEADS + g, p->scale_dtype);"),
+    ("fp32 values read as 1.0", "    return (double)f;\n}", "    return 1.0;\n}"),
 ]
 
 PINS = [
@@ -49,6 +56,10 @@ PINS = [
     vis.test_row_visible_layouts,
     vis.test_long_context_edges,
     sco.test_worked_example,
+    sco.test_worked_example_fp8_f32,
+    sco.test_single_head_special_case_fp32,
+    sco.test_nonnegative_inputs_reduce_to_gemv_fp32,
+    sco.test_linearity_fp32,
     lambda o: sco.test_int8_dots_brute_force(o, 0),
     lambda o: sco.test_int8_dots_brute_force(o, 48),
     sco.test_int8_dot_closed_forms,
