@@ -37,7 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "query-token×key scores/s incl. top-k; HBM GB/s (decode), MFMA % (prefill)"
-DEFAULT_WORKLOAD = "decode_int8_b24_s4_sk8192"
+DEFAULT_WORKLOAD = "prefill_int8_tnd_4x2048"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA, TOP/s
 FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA, TFLOP/s
@@ -237,6 +237,18 @@ def summarize_sq(workload: str, sq_dir: str) -> dict:
     return res
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the baseline record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp: dict, info, budget_core_s: float = 20.0, min_wall_s: float = 10.0) -> dict:
     """The oracle as it stands, on the host, on a bounded prefix of batches."""
     import numpy as np
@@ -276,6 +288,7 @@ def cpu_baseline(inp: dict, info, budget_core_s: float = 20.0, min_wall_s: float
             break
     pairs = int(vis.sum())
     return {"value": pairs * passes / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "batches 0..%d of %d (%d rows, %d visible pairs), %d full oracle pass(es) "
                       "(fp64 scores, exact dots, stable top-k), %.2f s wall"
                       % (nb - 1, B, vis.size, pairs, passes, dt)}
@@ -388,6 +401,7 @@ def producer_bench(args) -> dict:
             done += min(8192, n - done)
         el = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": done / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "cpu_model": cpu_model(),
                                "sample": "rows 0..%d of %d (numpy, one thread), %.2f s wall" % (done, n, el)}
     return res
 

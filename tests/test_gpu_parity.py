@@ -3,8 +3,10 @@
 Small cases are compared on every row and span several 64-key tiles, ragged
 tails, block sizes that are not powers of two, padded block strides, causal
 and compressed visibility, rows below and above sparse_count, TND and BSND.
-The five full-size workloads run in the benchmark's launch configuration;
-every row gets the structural checks and sampled rows the full oracle check.
+The five full-size workloads run in the benchmark's launch configuration,
+every row against the oracle; int8 dots of sampled full-size rows bit-exact.
+Runs without a host plan (bounded) and graph replays are checked against
+the oracle on every row as well as against the planned run.
 """
 import numpy as np
 import pytest
@@ -297,14 +299,16 @@ def test_repeat_runs_identical():
 
 
 @pytest.mark.parametrize("case", ["regular_causal_s3", "long_rt2_causal"])
-def test_graph_replay(case):
+def test_graph_replay(ora, case):
     """qli_run captured in a HIP graph (no host synchronisation, no memset
     nodes) and replayed: every replay, with eager work in between, gives the
-    eager outputs.  Plan, workspace and outputs keep their addresses."""
+    eager outputs, which match the oracle on every row.  Plan, workspace and
+    outputs keep their addresses."""
     import torch
     inp = synth.make_inputs(SMALL[case] if case in SMALL else LONG[case], 5)
     dev = device_inputs(inp)
     a_idx, a_val, ix = run_gpu(inp, dev)
+    oracle_check(ora, inp, a_idx, a_val)
     b_idx, b_val = ix.alloc_outputs()
     args = (dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
             b_idx, b_val)
@@ -357,8 +361,10 @@ def test_stages_compose(name):
 
 @pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
 def test_workload_full_size(ora, name):
-    """Each named workload at full size, in the benchmark's configuration:
-    structure on every row, the full oracle check on sampled rows."""
+    """Each named workload at full size, in the benchmark's launch
+    configuration: structure and the full oracle check (scores within
+    tolerance, index sets exact up to ties) on every row."""
+    import time
     inp = synth.workload(name)
     p = inp["problem"]
     rows, k = rows_of(p), p["sparse_count"]
@@ -366,17 +372,51 @@ def test_workload_full_size(ora, name):
     vis = vis_of(ora, inp)
     gidx, gval, ix = run_gpu(inp)
     check_structure(gidx, gval, vis, k)
-    rng = np.random.default_rng(123)
-    picks = sorted(set([0, rows - 1] + rng.choice(rows, size=min(rows, 6), replace=False).tolist()))
-    if p["qk_dtype"] == 1:  # keep the fp8 oracle rows short
-        picks = sorted(set([int(np.argmin(vis))] + picks[:3]))
-    for r in picks:
+    t0 = time.perf_counter()
+    rc, _, _, osc = ora.indexer(inp, scores_cols=max(1, int(vis.max())), nthreads=0)
+    assert rc == 0
+    log("  oracle over %d rows (%d visible pairs) in %.1f s" % (rows, int(vis.sum()), time.perf_counter() - t0))
+    for r in range(rows):
+        check_row(r, int(vis[r]), k, gidx[r], gval[r], osc[r, :vis[r]], rtol_of(inp))
+
+
+# Full-size int8 dumps: rows [row0, row1) of a workload, dots bit-exact and
+# scores within tolerance against the oracle, the selection equal to the
+# stable top-k of the GPU's own scores.
+FULL_DUMPS = [
+    ("decode_int8_b24_s4_sk8192", 0, 2),
+    ("decode_int8_b24_s4_sk8192", 94, 96),
+    ("longctx_int8_b8_s2_sk131072_cmp4", 0, 2),
+    ("longctx_int8_b8_s2_sk131072_cmp4", 14, 16),
+    ("prefill_int8_tnd_4x2048", 2045, 2049),
+    ("prefill_int8_tnd_4x2048", 8190, 8192),
+]
+
+
+@pytest.mark.parametrize("name,row0,row1", FULL_DUMPS, ids=["%s-%d" % (n, a) for n, a, _ in FULL_DUMPS])
+def test_workload_full_size_dump(ora, name, row0, row1):
+    import torch
+    inp = synth.workload(name)
+    p = inp["problem"]
+    k = p["sparse_count"]
+    vis = vis_of(ora, inp)
+    cols = int(vis[row0:row1].max())
+    log("workload dump %s rows [%d, %d) cols %d" % (name, row0, row1, cols))
+    ix = make_indexer(inp)
+    dev = device_inputs(inp)
+    gidx, gval, dots, scores = ix.run_debug(dev["query"], dev["key"], dev["weights"], dev["q_scale"],
+                                            dev["k_scale"], dev["block_table"], row0, row1, cols)
+    torch.cuda.synchronize()
+    gidx, gval = gidx.cpu().numpy(), gval.cpu().numpy()
+    dots, scores = dots.cpu().numpy(), scores.cpu().numpy()
+    for u, r in enumerate(range(row0, row1)):
         v = int(vis[r])
-        log("  oracle row %d vis %d" % (r, v))
-        if v == 0:
-            continue
-        _, _, osc = ora.row_detail(inp, r, 0, v)
-        check_row(r, v, k, gidx[r], gval[r], osc, rtol_of(inp))
+        _, odots, osc = ora.row_detail(inp, r, 0, v)
+        assert np.array_equal(dots[u, :, :v].astype(np.float64), odots), "row %d: int8 dots differ" % r
+        assert np.all(np.abs(scores[u, :v] - osc) <= ATOL + INT8_RTOL * np.abs(osc)), "row %d scores" % r
+        n = min(k, v)
+        assert np.array_equal(gidx[r, :n], stable_topk_set(scores[u, :v], k)), "row %d selection" % r
+        assert np.array_equal(gval[r, :n], scores[u, gidx[r, :n]]), "row %d values" % r
 
 
 # --- bounded decode: no host plan, key lengths on the device -------------------
@@ -440,10 +480,20 @@ def test_bounded_matches_planned(ora, name):
     p_idx, p_val = planned(inp, dev, lens)
     assert np.array_equal(idx.cpu().numpy(), p_idx)
     assert p_val is None or np.array_equal(val.cpu().numpy(), p_val)
+    oracle_check(ora, dict(inp, aslk=np.asarray(lens, dtype=np.int32)), idx.cpu().numpy(),
+                 None if val is None else val.cpu().numpy())
+
+
+def oracle_check(ora, inp, idx, val):
+    """Structure and the full oracle check on every row."""
     p = inp["problem"]
-    vis = ora.row_visible(p["layout_query"], p["batch"], p["s1"], p["sparse_mode"], p["cmp_ratio"],
-                          inp["aslq"], np.asarray(lens, dtype=np.int32))
-    check_structure(idx.cpu().numpy(), None if val is None else val.cpu().numpy(), vis, p["sparse_count"])
+    vis = vis_of(ora, inp)
+    k = p["sparse_count"]
+    check_structure(idx, val, vis, k)
+    rc, _, _, sc = ora.indexer(inp, scores_cols=max(1, int(vis.max()) if vis.size else 1))
+    assert rc == 0
+    for r in range(vis.size):
+        check_row(r, int(vis[r]), k, idx[r], None if val is None else val[r], sc[r, :vis[r]], rtol_of(inp))
 
 
 GRAPH_LENS = {
@@ -453,7 +503,7 @@ GRAPH_LENS = {
 
 
 @pytest.mark.parametrize("case", list(GRAPH_LENS))
-def test_bounded_graph_replay(case):
+def test_bounded_graph_replay(ora, case):
     """qli_run_bounded captured once in a HIP graph, replayed after the device
     key lengths change: every replay equals qli_plan + qli_run for the new
     lengths (including a batch that sees nothing and one longer than a segment)."""
@@ -478,6 +528,7 @@ def test_bounded_graph_replay(case):
         p_idx, p_val = planned(inp, dev, lens)
         assert np.array_equal(idx.cpu().numpy(), p_idx), "lengths %s" % lens
         assert np.array_equal(val.cpu().numpy(), p_val), "lengths %s" % lens
+        oracle_check(ora, dict(inp, aslk=np.asarray(lens, dtype=np.int32)), idx.cpu().numpy(), val.cpu().numpy())
 
 
 BOUNDED_TND = {
@@ -529,14 +580,10 @@ def test_bounded_tnd_matches_planned(ora, name):
     if per_batch.max() > 4:
         p_idx, p_val = planned(sub, dev, lens)
         assert np.array_equal(idx, p_idx) and np.array_equal(val, p_val)
-    else:
-        rc, _, _, sc = ora.indexer(sub, scores_cols=max(1, int(vis.max())))
-        assert rc == 0
-        for r in range(vis.size):
-            check_row(r, int(vis[r]), p["sparse_count"], idx[r], val[r], sc[r, :vis[r]], rtol_of(inp))
+    oracle_check(ora, sub, idx, val)
 
 
-def test_bounded_tnd_prefix_sums_out_of_contract():
+def test_bounded_tnd_prefix_sums_out_of_contract(ora):
     """Device query prefix sums that break the contract (decreasing, beyond T,
     negative) are taken as their running maximum clamped to [0, T]: the run
     completes and equals qli_plan + qli_run on that partition."""
@@ -548,9 +595,10 @@ def test_bounded_tnd_prefix_sums_out_of_contract():
     sub = dict(inp, aslq=np.asarray(clamped, dtype=np.int32))
     p_idx, p_val = planned(sub, dev, lens)
     assert np.array_equal(idx, p_idx) and np.array_equal(val, p_val)
+    oracle_check(ora, dict(sub, aslk=np.asarray(lens, dtype=np.int32)), idx, val)
 
 
-def test_bounded_tnd_graph_replay():
+def test_bounded_tnd_graph_replay(ora):
     """qli_run_bounded_tnd captured once; between replays both the device query
     prefix sums and the key lengths change (rows move between batches, batches
     empty out, rows fall past the last prefix sum): every replay equals
@@ -584,6 +632,7 @@ def test_bounded_tnd_graph_replay():
         p_idx, p_val = planned(sub, dev, lens)
         assert np.array_equal(idx.cpu().numpy(), p_idx), "aslq %s lens %s" % (aslq, lens)
         assert np.array_equal(val.cpu().numpy(), p_val), "aslq %s lens %s" % (aslq, lens)
+        oracle_check(ora, dict(sub, aslk=np.asarray(lens, dtype=np.int32)), idx.cpu().numpy(), val.cpu().numpy())
 
 
 # --- seeded random problems -----------------------------------------------------
@@ -670,11 +719,7 @@ def test_bounded_random(ora, i):
     if tiles_match:
         p_idx, p_val, _ = run_gpu(inp, dev)
         assert np.array_equal(idx, p_idx) and np.array_equal(val, p_val)
-    else:
-        rc, _, _, sc = ora.indexer(inp, scores_cols=max(1, int(vis.max())))
-        assert rc == 0
-        for r in range(rows_of(p)):
-            check_row(r, int(vis[r]), p["sparse_count"], idx[r], val[r], sc[r, :vis[r]], rtol_of(inp))
+    oracle_check(ora, inp, idx, val)
 
 
 @pytest.mark.parametrize("case", ["bsnd_int8_causal_bs48_pad", "long_rt2_causal", "tnd_int8_prefill_mixed"])

@@ -156,16 +156,18 @@ def test_quantized_inputs_feed_the_indexer(ora, qk):
         check_row(r, int(vis[r]), p["sparse_count"], idx[r], val[r], sc[r, :vis[r]], rtol_of(inp))
 
 
-def test_chain_graph_replay():
+def test_chain_graph_replay(ora):
     """One decode step as a HIP graph captured once: quantize the bf16 query,
     append each sequence's newest bf16 key entries into the paged cache, run
     the indexer with the key lengths read on the device (no host plan).
     Replayed with new inputs, positions and lengths (written eagerly between
     replays, from a restored cache each time), every replay equals the same
-    chain run eagerly, bit for bit."""
+    chain run eagerly, bit for bit, and the oracle's chain (its quantizer,
+    its cache append and its indexer on the same bf16 inputs) on every row."""
     import torch
     import sparse_attention_token_paged_amd as qli
-    spec = synth.small(batch=3, s1=2, aslk=[1500, 900, 1200], block_size=64, sparse_count=128, sparse_mode=3)
+    # every sequence's block table covers the bound, so any drawn length reads only real blocks
+    spec = synth.small(batch=3, s1=2, aslk=[1500] * 3, block_size=64, sparse_count=128, sparse_mode=3)
     inp = synth.make_inputs(spec, 9)
     p = inp["problem"]
     B, S1, bs, mb, nb = p["batch"], p["s1"], p["block_size"], p["max_blocks_per_seq"], p["num_blocks"]
@@ -196,12 +198,30 @@ def test_chain_graph_replay():
     def load_inputs(seed):
         rng = np.random.default_rng(seed)
         lens = rng.integers(200, bound + 1, B).astype(np.int32)
-        qb.copy_(dev(bf16_bits(rng.standard_normal((rows * 64, 128)).astype(np.float32)).view(np.int16)))
-        kb.copy_(dev(bf16_bits(rng.standard_normal((B * new, 128)).astype(np.float32)).view(np.int16)))
-        pos.copy_(dev(np.concatenate([np.arange(n - new, n, dtype=np.int32) for n in lens])))
+        qh = bf16_bits(rng.standard_normal((rows * 64, 128)).astype(np.float32))
+        kh = bf16_bits(rng.standard_normal((B * new, 128)).astype(np.float32))
+        ph = np.concatenate([np.arange(n - new, n, dtype=np.int32) for n in lens])
+        qb.copy_(dev(qh.view(np.int16)))
+        kb.copy_(dev(kh.view(np.int16)))
+        pos.copy_(dev(ph))
         aslk.copy_(dev(lens))
         key.copy_(pristine_k)
         ks.copy_(pristine_ks)
+        return qh, kh, ph, lens
+
+    def oracle_chain(qh, kh, ph, lens):
+        """The same step on the CPU: oracle quantizer, oracle append, oracle indexer."""
+        qc, qsc = oq.quantize_rows(qh, 0)
+        kc = inp["key"].copy()
+        ksc = inp["k_scale"].reshape(-1).copy()
+        oq.append_keys(kh, np.repeat(np.arange(B, dtype=np.int32), new), ph, inp["block_table"], B, mb, nb, bs,
+                       stride, kc.view(np.uint8), ksc, 0)
+        sub = dict(inp, query=qc.reshape(rows, 64, 128).view(inp["query"].dtype), q_scale=qsc.reshape(rows, 64),
+                   key=kc, k_scale=ksc.reshape(inp["k_scale"].shape), aslk=lens)
+        vis = ora.row_visible(p["layout_query"], B, S1, p["sparse_mode"], p["cmp_ratio"], None, lens)
+        rc, _, _, sc = ora.indexer(sub, scores_cols=int(vis.max()))
+        assert rc == 0
+        return sub, vis, sc
 
     load_inputs(0)
     side = torch.cuda.Stream()
@@ -215,7 +235,7 @@ def test_chain_graph_replay():
         step()
     for rep in range(4):
         log("chain graph replay %d" % rep)
-        load_inputs(100 + rep)
+        host = load_inputs(100 + rep)
         idx.fill_(-7)
         val.fill_(3.0)
         torch.cuda.synchronize()
@@ -229,6 +249,10 @@ def test_chain_graph_replay():
         assert np.array_equal(g_idx, idx.cpu().numpy()), "replay %d: indices differ" % rep
         assert np.array_equal(g_val, val.cpu().numpy()), "replay %d: values differ" % rep
         assert (g_idx[:, 0] >= 0).all()
+        sub, vis, sc = oracle_chain(*host)
+        check_structure(g_idx, g_val, vis, p["sparse_count"])
+        for r in range(rows):
+            check_row(r, int(vis[r]), p["sparse_count"], g_idx[r], g_val[r], sc[r, :vis[r]], rtol_of(sub))
 
 
 @pytest.mark.parametrize("name", ["quantize_query_prefill_t8192", "append_keys_decode_b24_sk8192"])
