@@ -252,7 +252,8 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
     }
   }
   // The merge regions (scores, and key indices in the index region) follow
-  // every row's candidate region.
+  // every row's candidate region; only they carry key indices.
+  const int64_t merge_start = ws;
   for (size_t i = 0; i < pass2.size(); i++) {
     pass2[i].src_off = ws;
     for (size_t e = pass2_segments[i].first; e < pass2_segments[i].second; e++) out.select[e].dst_off += ws;
@@ -315,8 +316,11 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   h.rows = rows;
   h.visible_pairs = visible;
   h.ws_scores = ws;
-  h.ws_index_offset = align16(ws * 4);
-  h.workspace_bytes = n_pass1 < out.select.size() ? h.ws_index_offset + ws * 4 : ws * 4;
+  // Index region: the key indices of the merge regions [merge_start, ws),
+  // placed after the scores so that candidate e's index sits at byte
+  // ws_index_offset + 4e (merge_start is a multiple of 4 elements).
+  h.ws_index_offset = align16(ws * 4) - merge_start * 4;
+  h.workspace_bytes = n_pass1 < out.select.size() ? align16(ws * 4) + (ws - merge_start) * 4 : ws * 4;
   h.kind = prefill ? kKindPrefill : kKindDecode;
   h.rows_per_item = rt;
   h.n_items = (int32_t)out.items.size();
@@ -498,8 +502,9 @@ int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
     h.max_cand2 = (g.nseg - 1) * k + (int32_t)std::min<int64_t>(k, nmax - (int64_t)(g.nseg - 1) * kSelSegment);
   }
   h.ws_scores = total;
-  h.ws_index_offset = align16(total * 4);
-  h.workspace_bytes = g.nseg > 1 ? h.ws_index_offset + total * 4 : total * 4;
+  // key indices for the merge regions only (see build_plan)
+  h.ws_index_offset = align16(total * 4) - g.merge_base * 4;
+  h.workspace_bytes = g.nseg > 1 ? align16(total * 4) + (total - g.merge_base) * 4 : total * 4;
   add_tables();
   return QLI_OK;
 }

@@ -12,7 +12,7 @@
 namespace qli {
 
 constexpr uint32_t kPlanMagic = 0x504C4951u;  // "QILP"
-constexpr uint32_t kPlanVersion = 6;
+constexpr uint32_t kPlanVersion = 7;
 constexpr int kHeads = 64;       // query heads (QLI-README 约束说明)
 constexpr int kDim = 128;        // head dim of query and key (约束说明)
 constexpr int kTileKeys = 64;    // keys per MFMA tile step (4 n-tiles of 16)
@@ -48,7 +48,9 @@ struct PlanHeader {
   int64_t key_entries;       // sum over batches of the largest visible count
   int64_t table_entries;     // block-table entries spanned by those entries
   int64_t active_rows;       // rows with at least one visible entry
-  int64_t ws_index_offset;   // byte offset of the int32 candidate-index region in the workspace
+  int64_t ws_index_offset;   // the int32 key index of merge candidate e (an element offset of a
+                             // merge region) sits at workspace byte ws_index_offset + 4e; only
+                             // merge regions carry indices, stored after every score
   // Regular decode plans (every batch: the same rows, one group, the same
   // visible maximum): item i covers batch i / reg_chunks, keys from
   // (i % reg_chunks) * chunk, rows batch * reg_rows .. + reg_rows.  0 = not regular.

@@ -229,7 +229,14 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
     assert np.all(sel["src_off"] % 4 == 0)
     assert int(h["max_cand"]) == max([int(e["n"]) for e in p1], default=0)
     assert int(h["max_cand2"]) == max([int(e["n"]) for e in p2], default=0)
-    assert ws == (int(h["ws_index_offset"]) + 4 * merge_off if n2 > 0 else 4 * merge_off)
+    # key indices of the merge regions [region_end, merge_off) follow every score, 16-byte aligned:
+    # the index of candidate e sits at byte ws_index_offset + 4e
+    a16 = (4 * merge_off + 15) // 16 * 16
+    if n2 > 0:
+        assert int(h["ws_index_offset"]) == a16 - 4 * region_end
+        assert ws == a16 + 4 * (merge_off - region_end)
+    else:
+        assert ws == 4 * merge_off
     sel = selected
     if h["kind"] == 0:
         # decode items: inline visible counts, and candidate slots that tile each row's range
@@ -305,15 +312,16 @@ def bounded_workspace_expected(p, max_len):
     """Workspace of bounded decode, from its layout: rows that may see more than
     k entries keep every score (16-byte aligned row stride); rows longer than one
     selection segment also keep each segment's k winners for the merge, with
-    their key indices in a mirrored int32 region."""
+    their key indices in an int32 region after every score (merge regions only)."""
     rows, k = p["batch"] * p["s1"], p["sparse_count"]
     nmax = max_len // p["cmp_ratio"]
     if rows == 0 or nmax <= k:
         return 0
     pad4 = lambda n: (n + 3) // 4 * 4
     nseg = -(-nmax // SEGMENT)
-    total = rows * pad4(nmax) + (rows * pad4(nseg * k) if nseg > 1 else 0)
-    return ((4 * total + 15) // 16 * 16) + 4 * total if nseg > 1 else 4 * total
+    merges = rows * pad4(nseg * k) if nseg > 1 else 0
+    total = rows * pad4(nmax) + merges
+    return ((4 * total + 15) // 16 * 16) + 4 * merges if nseg > 1 else 4 * total
 
 
 def bounded_tnd_workspace_expected(p, max_len):
