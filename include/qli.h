@@ -21,7 +21,10 @@
  *
  * Conventions for every entry point:
  *   - All buffers are owned by the caller.  The library allocates no device
- *     memory and keeps no state between calls; calls are thread-safe.
+ *     memory at run time and keeps no state between calls; calls are
+ *     thread-safe.  One exception, for callers that cannot allocate:
+ *     qli_run_bounded_static works in a static device workspace that every
+ *     GPU the library is loaded on holds from load to process exit.
  *   - Device pointers are plain HIP device addresses; "stream" is a
  *     hipStream_t passed as void* (NULL = the default stream).
  *   - Every scalar argument is validated before anything is launched; a
@@ -274,6 +277,32 @@ int qli_run_bounded_tnd(const qli_problem *p, int64_t max_seq_len_key,
                         const void *k_scale, const int32_t *block_table,
                         void *workspace, int32_t *sparse_indices,
                         float *sparse_values, void *stream);
+
+/*
+ * qli_run_bounded_static -- qli_run_bounded for callers that cannot allocate
+ *   device memory: code under HIP graph capture, tight serving loops, hosts
+ *   that forbid hipMalloc.  Same arguments, semantics and outputs as
+ *   qli_run_bounded (BSND layout), minus the workspace: the library uses its
+ *   own static device workspace of 32 MiB per GPU (a file-scope device array,
+ *   allocated when the library is loaded on a device and held until the
+ *   process ends).  The call itself allocates nothing, host or device.
+ *   Limit: QLI_ERR_SIZE when qli_bounded_workspace reports more than
+ *   33554432 bytes for the problem and bound (e.g. 64 sequences of 65536 key
+ *   entries at sparse_count 512 need about 18 MiB).  QLI_ERR_UNSUPPORTED for
+ *   the TND layout.  QLI_ERR_HIP if the workspace's device address cannot be
+ *   obtained.
+ *   Every call on one GPU shares that GPU's workspace, and nothing in it needs
+ *   to start at zero (each call writes what it later reads).  Calls that may
+ *   overlap on one GPU -- on different streams, or from different host threads
+ *   -- race on the workspace and give undefined outputs: serialize them (one
+ *   stream, or events).
+ */
+int qli_run_bounded_static(const qli_problem *p, int64_t max_seq_len_key,
+                           const int32_t *aslk_dev, const void *query,
+                           const void *key, const void *weights,
+                           const void *q_scale, const void *k_scale,
+                           const int32_t *block_table, int32_t *sparse_indices,
+                           float *sparse_values, void *stream);
 
 /*
  * Producer side: per-token-head quantization of the index query and key, the

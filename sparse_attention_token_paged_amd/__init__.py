@@ -26,8 +26,8 @@ LAYOUT_BSND, LAYOUT_TND = 0, 1
 INT64_MAX = (1 << 63) - 1
 
 EXPORTED = ("qli_status_string", "qli_plan", "qli_plan_info_get", "qli_run", "qli_run_debug", "qli_run_stage",
-            "qli_bounded_workspace", "qli_run_bounded", "qli_run_bounded_tnd", "qli_quantize_query",
-            "qli_append_keys")
+            "qli_bounded_workspace", "qli_run_bounded", "qli_run_bounded_tnd", "qli_run_bounded_static",
+            "qli_quantize_query", "qli_append_keys")
 
 c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
@@ -96,6 +96,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.qli_run_bounded.restype = ctypes.c_int
         lib.qli_run_bounded_tnd.argtypes = [ctypes.POINTER(Problem), c_i64] + [c_p] * 11 + [c_p]
         lib.qli_run_bounded_tnd.restype = ctypes.c_int
+        lib.qli_run_bounded_static.argtypes = [ctypes.POINTER(Problem), c_i64] + [c_p] * 9 + [c_p]
+        lib.qli_run_bounded_static.restype = ctypes.c_int
         lib.qli_quantize_query.argtypes = [c_i32, c_i64, c_p, c_p, c_p, c_p]
         lib.qli_quantize_query.restype = ctypes.c_int
         lib.qli_append_keys.argtypes = [c_i32, c_i64, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i64,
@@ -198,6 +200,15 @@ def qli_run_bounded(problem: Problem, max_seq_len_key: int, aslk_dev, query, key
                                   _addr(key), _addr(weights), _addr(q_scale), _addr(k_scale),
                                   _addr(block_table), _addr(workspace), _addr(sparse_indices),
                                   _addr(sparse_values), stream)
+
+
+def qli_run_bounded_static(problem: Problem, max_seq_len_key: int, aslk_dev, query, key, weights, q_scale,
+                           k_scale, block_table, sparse_indices, sparse_values, stream=None) -> int:
+    """qli_run_bounded without a workspace argument (the library's static one)."""
+    return load().qli_run_bounded_static(ctypes.byref(problem), int(max_seq_len_key), _addr(aslk_dev),
+                                         _addr(query), _addr(key), _addr(weights), _addr(q_scale),
+                                         _addr(k_scale), _addr(block_table), _addr(sparse_indices),
+                                         _addr(sparse_values), stream)
 
 
 def qli_quantize_query(qk_dtype: int, rows: int, x, q_out, scale_out, stream=None) -> int:

@@ -97,12 +97,8 @@ int64_t align16(int64_t v) { return (v + 15) & ~int64_t(15); }
 // single round; for equal groups, a longer chunk if it lowers the keys of the
 // busiest CU, the items being dealt evenly over the CUs (e.g. 512 items of
 // 512 keys, 2 per CU, rather than 688 of 384, 3 on most CUs).
-int decode_chunk(const std::vector<int32_t>& maxv, bool equal) {
-  auto items_for = [&](int c) {
-    int64_t n = 0;
-    for (int32_t m : maxv) n += (m + c - 1) / c;
-    return n;
-  };
+template <typename ItemsFor>
+int decode_chunk_for(ItemsFor&& items_for, bool equal) {
   int c = 128;
   while (c < kMaxChunk && items_for(c) > kDecodeSlots) c += 128;
   if (equal) {
@@ -113,6 +109,21 @@ int decode_chunk(const std::vector<int32_t>& maxv, bool equal) {
     c = best;
   }
   return c;
+}
+
+int decode_chunk(const std::vector<int32_t>& maxv, bool equal) {
+  return decode_chunk_for(
+      [&](int c) {
+        int64_t n = 0;
+        for (int32_t m : maxv) n += (m + c - 1) / c;
+        return n;
+      },
+      equal);
+}
+
+// The same for `groups` equal groups of maxv entries (no allocation).
+int decode_chunk_equal(int64_t groups, int32_t maxv) {
+  return decode_chunk_for([&](int c) { return groups * ((maxv + c - 1) / c); }, groups > 0);
 }
 
 int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, Built& out) {
@@ -350,7 +361,8 @@ bool plan_matches(const qli_problem* p, const void* plan_host) {
          h->fingerprint == problem_fingerprint(*p);
 }
 
-int check_run_args(const RunArgs& a) {
+// internal_ws: the workspace is the library's own (checked by the caller).
+int check_run_args(const RunArgs& a, bool internal_ws = false) {
   const PlanHeader* h = a.hdr;
   if (!a.plan_dev && !a.aslk) return QLI_ERR_ARG;  // a plan, or bounded decode
   if (h->rows == 0) return QLI_OK;
@@ -358,12 +370,12 @@ int check_run_args(const RunArgs& a) {
   if (a.p->return_value && !a.sparse_values) return QLI_ERR_ARG;
   if (h->n_items > 0 && (!a.query || !a.key || !a.weights || !a.q_scale || !a.k_scale || !a.block_table))
     return QLI_ERR_ARG;
-  if (h->workspace_bytes > 0 && !a.workspace) return QLI_ERR_ARG;
+  if (!internal_ws && h->workspace_bytes > 0 && !a.workspace) return QLI_ERR_ARG;
   // Vector loads need aligned bases: 16 bytes for query, key, the fp32
   // weights / q_scale, plan and workspace; the element size elsewhere.
   auto aligned = [](const void* ptr, uintptr_t n) { return ((uintptr_t)ptr % n) == 0; };
   const uintptr_t sb = a.p->scale_dtype == QLI_SCALE_F16 ? 2 : 4;
-  if ((a.plan_dev && !aligned(a.plan_dev, 16)) || !aligned(a.workspace, 16) || !aligned(a.query, 16) ||
+  if ((a.plan_dev && !aligned(a.plan_dev, 16)) || (!internal_ws && !aligned(a.workspace, 16)) || !aligned(a.query, 16) ||
       !aligned(a.key, 16) || !aligned(a.weights, 4 * sb) || !aligned(a.q_scale, 4 * sb) ||
       !aligned(a.k_scale, sb) || !aligned(a.block_table, 4) || !aligned(a.sparse_indices, 4) ||
       !aligned(a.sparse_values, 4))
@@ -470,7 +482,7 @@ int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
   h.kind = prefill ? kKindPrefill : kKindDecode;
   h.rows_per_item = prefill ? 8 : (p.s1 <= 1 ? 1 : (p.s1 <= 2 ? 2 : 4));
   if (rows == 0) return QLI_OK;
-  h.chunk = prefill ? kMaxChunk : decode_chunk(std::vector<int32_t>(p.batch, (int32_t)nmax), true);
+  h.chunk = prefill ? kMaxChunk : decode_chunk_equal(p.batch, (int32_t)nmax);
   h.reg_chunks = (int32_t)std::max<int64_t>(1, (nmax + h.chunk - 1) / h.chunk);
   h.reg_rows = p.s1;
   h.reg_maxv = (int32_t)nmax;
@@ -586,15 +598,18 @@ QLI_EXPORT int qli_bounded_workspace(const qli_problem* p, int64_t max_seq_len_k
   }
 }
 
+// static_ws: use the library's static workspace (workspace is ignored).
 static int run_bounded_common(const qli_problem* p, int64_t max_seq_len_key, const int32_t* aslq_dev,
                               const int32_t* aslk_dev, const void* query, const void* key, const void* weights,
                               const void* q_scale, const void* k_scale, const int32_t* block_table,
-                              void* workspace, int32_t* sparse_indices, float* sparse_values, void* stream) {
+                              void* workspace, int32_t* sparse_indices, float* sparse_values, void* stream,
+                              bool static_ws = false) {
   int rc = validate_problem(p);
   if (rc != QLI_OK) return rc;
   Bounded g;
   rc = bounded_geometry(*p, max_seq_len_key, g);
   if (rc != QLI_OK) return rc;
+  if (static_ws && g.h.workspace_bytes > (int64_t)kScratchBytes) return QLI_ERR_SIZE;
   if (g.h.rows == 0) return QLI_OK;
   if (!aslk_dev || ((uintptr_t)aslk_dev % 4) != 0) return QLI_ERR_ARG;
   const bool tnd = p->layout_query == QLI_LAYOUT_TND;
@@ -626,8 +641,9 @@ static int run_bounded_common(const qli_problem* p, int64_t max_seq_len_key, con
     a.aslq = aslq_dev;
     a.tab_off = g.tab_off;
   }
-  rc = check_run_args(a);
+  rc = check_run_args(a, static_ws);
   if (rc != QLI_OK) return rc;
+  if (static_ws && g.h.workspace_bytes > 0 && scratch_address(&a.workspace) != 0) return QLI_ERR_HIP;
   if (tnd && launch_tnd_tables(a) != 0) return QLI_ERR_HIP;
   if (launch_score(a, false) != 0) return QLI_ERR_HIP;
   if (g.h.n_select > 0 && launch_select(a) != 0) return QLI_ERR_HIP;
@@ -657,6 +673,19 @@ QLI_EXPORT int qli_run_bounded_tnd(const qli_problem* p, int64_t max_seq_len_key
     if (p && p->layout_query != QLI_LAYOUT_TND) return QLI_ERR_UNSUPPORTED;
     return run_bounded_common(p, max_seq_len_key, aslq_dev, aslk_dev, query, key, weights, q_scale, k_scale,
                               block_table, workspace, sparse_indices, sparse_values, stream);
+  } catch (...) {
+    return QLI_ERR_ARG;
+  }
+}
+
+QLI_EXPORT int qli_run_bounded_static(const qli_problem* p, int64_t max_seq_len_key, const int32_t* aslk_dev,
+                                      const void* query, const void* key, const void* weights,
+                                      const void* q_scale, const void* k_scale, const int32_t* block_table,
+                                      int32_t* sparse_indices, float* sparse_values, void* stream) {
+  try {
+    if (p && p->layout_query == QLI_LAYOUT_TND) return QLI_ERR_UNSUPPORTED;  // needs the query lengths
+    return run_bounded_common(p, max_seq_len_key, nullptr, aslk_dev, query, key, weights, q_scale, k_scale,
+                              block_table, nullptr, sparse_indices, sparse_values, stream, true);
   } catch (...) {
     return QLI_ERR_ARG;
   }

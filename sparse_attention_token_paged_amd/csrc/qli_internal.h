@@ -180,6 +180,14 @@ struct RunArgs {
   int64_t tab_off = 0;
 };
 int launch_score(const RunArgs& a, bool dump);
+
+// The allocation-free bounded runs' workspace: kScratchBytes of device memory
+// per GPU (a file-scope array of qli_kernels.hip).  scratch_address() writes
+// the current device's address of it (looked up once per device); returns a
+// hipError_t value.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+int scratch_address(void** out);
 int launch_select(const RunArgs& a);
 int launch_tnd_tables(const RunArgs& a);
 

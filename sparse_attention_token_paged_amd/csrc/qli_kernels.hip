@@ -1363,21 +1363,28 @@ __global__ __launch_bounds__(NT) void select_global_kernel(SelectParams S) {
 }
 
 // Workgroups of `kernel` that the current device holds at once (all CUs),
-// cached per device and kernel; 0 if it cannot be determined.
+// cached per device and kernel in a fixed table (no allocation after the
+// first query); 0 if it cannot be determined.
 int resident_slots(const void* kernel, int threads) {
+  struct Slot {
+    int dev;
+    const void* kernel;
+    int slots;
+  };
   static std::mutex mu;
-  static std::vector<std::pair<std::pair<int, const void*>, int>> cache;
+  static Slot cache[256];
+  static int used = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   std::lock_guard<std::mutex> lock(mu);
-  for (const auto& e : cache)
-    if (e.first.first == dev && e.first.second == kernel) return e.second;
+  for (int i = 0; i < used; i++)
+    if (cache[i].dev == dev && cache[i].kernel == kernel) return cache[i].slots;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
     return 0;
   const int slots = cus * per_cu;
-  cache.push_back({{dev, kernel}, slots});
+  if (used < 256) cache[used++] = Slot{dev, kernel, slots};
   return slots;
 }
 
@@ -1410,6 +1417,29 @@ hipError_t launch_score_t(const ScoreParams& P, const PlanHeader* h, hipStream_t
 }
 
 }  // namespace
+
+// Workspace of the allocation-free bounded runs: a file-scope device array,
+// one copy per GPU the library runs on, kept until the process ends.  In host
+// code its name is only a stand-in; the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return 0;
+}
 
 int launch_score(const RunArgs& a, bool dump) {
   const PlanHeader* h = a.hdr;

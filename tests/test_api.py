@@ -434,3 +434,34 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and not r.stdout.strip()
+
+
+def test_bounded_static_rejects_without_launching(qli):
+    """qli_run_bounded_static: every argument check returns before the library
+    touches a device (the fake addresses are never dereferenced)."""
+    spec = synth.small(batch=2, s1=2, aslk=[5000, 5000], block_size=64, sparse_count=256, sparse_mode=3)
+    p = synth.make_inputs(spec, 1)["problem"]
+    prob = qli.Problem.from_dict(p)
+    fake = 1 << 40
+    args = [fake] * 9
+    f = qli.qli_run_bounded_static
+    tnd = qli.Problem.from_dict(dict(p, layout_query=synth.TND))
+    assert f(tnd, 5000, *args) == qli.QLI_ERR_UNSUPPORTED
+    assert f(prob, -1, *args) == qli.QLI_ERR_ARG
+    a = list(args)
+    a[0] = None                                                     # actual_seq_lengths_key
+    assert f(prob, 5000, *a) == qli.QLI_ERR_ARG
+    a = list(args)
+    a[7] = None                                                     # sparse_indices
+    assert f(prob, 5000, *a) == qli.QLI_ERR_ARG
+    a = list(args)
+    a[1] = fake + 4                                                 # query not 16-byte aligned
+    assert f(prob, 5000, *a) == qli.QLI_ERR_ARG
+    # beyond the 32 MiB static workspace: 64 rows of 140000 staged scores
+    big = dict(p, batch=64, s1=1, max_blocks_per_seq=140000 // 64 + 1, sparse_count=512, sparse_mode=0)
+    rc, ws = qli.qli_bounded_workspace(qli.Problem.from_dict(big), 140000)
+    assert rc == qli.QLI_OK and ws > 32 << 20
+    assert f(qli.Problem.from_dict(big), 140000, *args) == qli.QLI_ERR_SIZE
+    # the fp8 decode shape at its longest (64 x 65536 entries, k = 512) fits
+    rc, ws = qli.qli_bounded_workspace(qli.Problem.from_dict(big), 65536)
+    assert rc == qli.QLI_OK and ws <= 32 << 20
