@@ -201,3 +201,51 @@ def producer_inputs(name: str, seed: Optional[int] = None) -> dict:
                 block_table=base["block_table"], batch=p["batch"], max_blocks=p["max_blocks_per_seq"],
                 num_blocks=p["num_blocks"], block_size=p["block_size"],
                 stride=p["key_block_stride"] or p["block_size"] * 128)
+
+
+# ---------------------------------------------------------------------------
+# Consumer inputs: sparse attention over the indexer's selected entries.
+# ---------------------------------------------------------------------------
+# Recipe: PCG64(seed); query [rows, heads, 128] and the key / value caches
+# [num_blocks, block_size, 128] (one head, the indexer workload's block
+# geometry and block table) are standard normal cast to bf16 (round to
+# nearest even).  Unless given, each row's list holds min(k, n_b) distinct
+# entries drawn uniformly from the n_b = aslk[b] // cmp_ratio entries its
+# batch's cache stores, in ascending order, padded with -1 (the shape of the
+# indexer's sparse_indices).
+
+
+def attention_inputs(inp: dict, heads: int, seed: int, indices=None, kv_stride_pad: int = 0,
+                     scale: Optional[float] = None) -> dict:
+    """Consumer inputs over an indexer input dict ``inp`` (its layout, rows,
+    lengths, block table and sparse_count): bf16 bit patterns (uint16) for q,
+    k_cache and v_cache; indices int32 [rows, k]."""
+    p = inp["problem"]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = p["batch"] * p["s1"] if p["layout_query"] == BSND else p["s1"]
+    bs, nb = p["block_size"], p["num_blocks"]
+    dim = 128
+    stride = bs * dim + kv_stride_pad
+    q = to_bf16_bits(rng.standard_normal((rows, heads, dim), dtype=np.float32))
+    kc = to_bf16_bits(rng.standard_normal(nb * stride, dtype=np.float32))
+    vc = to_bf16_bits(rng.standard_normal(nb * stride, dtype=np.float32))
+    k = p["sparse_count"]
+    if indices is None:
+        ents = inp["aslk"].astype(np.int64) // p["cmp_ratio"]
+        indices = np.full((rows, k), -1, dtype=np.int32)
+        if p["layout_query"] == BSND:
+            batch_of = np.repeat(np.arange(p["batch"]), p["s1"])
+        else:
+            ends = np.asarray(inp["aslq"], dtype=np.int64)
+            batch_of = np.searchsorted(ends, np.arange(rows), side="right")
+        for r in range(rows):
+            b = int(batch_of[r])
+            if b >= p["batch"]:
+                continue
+            n = int(min(k, ents[b]))
+            indices[r, :n] = np.sort(rng.choice(int(ents[b]), size=n, replace=False))
+    return dict(layout=p["layout_query"], batch=p["batch"], s1=p["s1"], aslq=inp["aslq"], heads=heads,
+                block_size=bs, max_blocks=p["max_blocks_per_seq"], num_blocks=nb,
+                kv_stride=stride if kv_stride_pad else 0, q=q, k_cache=kc, v_cache=vc,
+                block_table=inp["block_table"], indices=np.ascontiguousarray(indices, dtype=np.int32),
+                scale=(1.0 / np.sqrt(dim)) if scale is None else scale)
