@@ -369,6 +369,74 @@ int qli_append_keys(int32_t qk_dtype, int64_t n, const void *x,
                     int32_t block_size, int64_t key_block_stride,
                     void *key_cache, void *k_scale, void *stream);
 
+/*
+ * Consumer: sparse attention over the indexer's output.  The page calls the
+ * indexer the preprocessing of sparse attention: its Top-k indices are the
+ * input of Attention (QLI-README 功能说明 step 3), sparse_indices are the
+ * tokens taking part in the sparse attention, and block_table maps the KV
+ * storage of PageAttention (参数说明).  The page does not write the attention
+ * out; the reading implemented here is, for query row r of batch b and query
+ * head h,
+ *   S_r       = { sparse_indices[r][i] : i < sparse_count, value >= 0 }
+ *   out[r][h] = sum_{j in S_r} softmax_j(softmax_scale * q[r][h] . K_b[j]) * V_b[j]
+ *   lse[r][h] = log sum_{j in S_r} exp(softmax_scale * q[r][h] . K_b[j])
+ * with one key / value head shared by every query head; K_b[j], V_b[j] is
+ * entry j of batch b in the paged caches: block block_table[b][j / block_size],
+ * slot j % block_size (the index space of the indexer's output).  A row with
+ * no listed entry gets out = 0 and lse = -INFINITY.  Rows map to batches as
+ * in the indexer: BSND row r is batch r / S1; TND rows follow the prefix sums
+ * of actual_seq_lengths_query (rows past the last one attend to nothing).
+ */
+typedef struct qli_attn_problem {
+    int32_t batch;              /* B (TND: entries of actual_seq_lengths_query) */
+    int32_t s1;                 /* BSND: S1; TND: T */
+    int32_t layout_query;       /* qli_layout */
+    int32_t num_heads;          /* query heads H: 16, 32, 64 or 128 (else QLI_ERR_UNSUPPORTED) */
+    int32_t head_dim;           /* must be 128 (else QLI_ERR_UNSUPPORTED) */
+    int32_t num_blocks;         /* blocks of the key and value caches, >= 1 */
+    int32_t block_size;         /* multiple of 16, 16..1024 (as the indexer's key cache) */
+    int32_t max_blocks_per_seq; /* second dim of block_table */
+    int64_t kv_block_stride;    /* elements (bf16) between consecutive blocks of either cache;
+                                   0 = block_size * 128; else >= that and a multiple of 8 */
+    int32_t sparse_count;       /* columns of sparse_indices, 1..2048 */
+    float softmax_scale;        /* > 0 and finite (e.g. 1 / sqrt(128)) */
+    int32_t return_lse;         /* 1: write lse */
+    int32_t reserved0;          /* must be 0 */
+    int32_t reserved1;          /* must be 0 */
+    int32_t reserved2;          /* must be 0 */
+} qli_attn_problem;
+
+/*
+ * qli_sparse_attention_workspace -- device workspace bytes qli_sparse_attention
+ *   needs (0 when every row is finished by one workgroup; otherwise fp32
+ *   partials of rows whose list is split across workgroups).
+ */
+int qli_sparse_attention_workspace(const qli_attn_problem *p, size_t *workspace_bytes);
+
+/*
+ * qli_sparse_attention -- stream-ordered, no host synchronisation.
+ *   aslq            device int32[B] prefix sums (TND only; NULL for BSND)
+ *   q               device bf16 [rows, H, 128], 16-byte aligned
+ *   k_cache, v_cache device bf16 [num_blocks, block_size, 128] (block stride
+ *                   kv_block_stride), 16-byte aligned
+ *   block_table     device int32 [B, max_blocks_per_seq]
+ *   sparse_indices  device int32 [rows, sparse_count] (the indexer's output)
+ *   workspace       device, qli_sparse_attention_workspace bytes, 16-byte
+ *                   aligned (NULL if 0)
+ *   out             device bf16 [rows, H, 128] (written), 8-byte aligned
+ *   lse             device float [rows, H] (written when return_lse), or NULL
+ * Listed entries at or past max_blocks_per_seq * block_size, or whose block
+ * id lies outside [0, num_blocks), are skipped, so no read leaves the caches;
+ * listing an entry the batch does not store (a block-table slot of another
+ * sequence) is out of contract.  Errors: QLI_ERR_ARG / QLI_ERR_UNSUPPORTED for
+ * a scalar or pointer that breaks the rules above, before anything is
+ * launched; QLI_ERR_HIP if a launch fails.
+ */
+int qli_sparse_attention(const qli_attn_problem *p, const int32_t *aslq, const void *q,
+                         const void *k_cache, const void *v_cache, const int32_t *block_table,
+                         const int32_t *sparse_indices, void *workspace, void *out, float *lse,
+                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ INT64_MAX = (1 << 63) - 1
 
 EXPORTED = ("qli_status_string", "qli_plan", "qli_plan_info_get", "qli_run", "qli_run_debug", "qli_run_stage",
             "qli_bounded_workspace", "qli_run_bounded", "qli_run_bounded_tnd", "qli_run_bounded_static",
-            "qli_quantize_query", "qli_append_keys")
+            "qli_quantize_query", "qli_append_keys", "qli_sparse_attention_workspace", "qli_sparse_attention")
 
 c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
@@ -50,6 +50,25 @@ class Problem(ctypes.Structure):
         for name, _ in cls._fields_:
             if name in d:
                 setattr(p, name, int(d[name]))
+        return p
+
+
+class AttnProblem(ctypes.Structure):
+    """Mirror of ``qli_attn_problem`` (the sparse-attention consumer)."""
+    _fields_ = [
+        ("batch", c_i32), ("s1", c_i32), ("layout_query", c_i32), ("num_heads", c_i32),
+        ("head_dim", c_i32), ("num_blocks", c_i32), ("block_size", c_i32), ("max_blocks_per_seq", c_i32),
+        ("kv_block_stride", c_i64),
+        ("sparse_count", c_i32), ("softmax_scale", ctypes.c_float), ("return_lse", c_i32), ("reserved0", c_i32),
+        ("reserved1", c_i32), ("reserved2", c_i32),
+    ]
+
+    @classmethod
+    def from_dict(cls, d: dict) -> "AttnProblem":
+        p = cls()
+        for name, _ in cls._fields_:
+            if name in d:
+                setattr(p, name, float(d[name]) if name == "softmax_scale" else int(d[name]))
         return p
 
 
@@ -98,6 +117,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.qli_run_bounded_tnd.restype = ctypes.c_int
         lib.qli_run_bounded_static.argtypes = [ctypes.POINTER(Problem), c_i64] + [c_p] * 9 + [c_p]
         lib.qli_run_bounded_static.restype = ctypes.c_int
+        lib.qli_sparse_attention_workspace.argtypes = [ctypes.POINTER(AttnProblem), ctypes.POINTER(c_sz)]
+        lib.qli_sparse_attention_workspace.restype = ctypes.c_int
+        lib.qli_sparse_attention.argtypes = [ctypes.POINTER(AttnProblem)] + [c_p] * 10
+        lib.qli_sparse_attention.restype = ctypes.c_int
         lib.qli_quantize_query.argtypes = [c_i32, c_i64, c_p, c_p, c_p, c_p]
         lib.qli_quantize_query.restype = ctypes.c_int
         lib.qli_append_keys.argtypes = [c_i32, c_i64, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i64,
@@ -354,3 +377,54 @@ class Indexer:
         if rc != QLI_OK:
             raise QliError(rc, "qli_run_debug")
         return out_idx, out_val, dots.view(row1 - row0, 64, cols), scores.view(row1 - row0, cols)
+
+
+def qli_sparse_attention_workspace(problem: AttnProblem):
+    """Returns (status, workspace bytes) for qli_sparse_attention."""
+    ws = c_sz(0)
+    rc = load().qli_sparse_attention_workspace(ctypes.byref(problem), ctypes.byref(ws))
+    return rc, int(ws.value)
+
+
+def qli_sparse_attention(problem: AttnProblem, aslq_dev, q, k_cache, v_cache, block_table, sparse_indices,
+                         workspace, out, lse, stream=None) -> int:
+    return load().qli_sparse_attention(ctypes.byref(problem), _addr(aslq_dev), _addr(q), _addr(k_cache),
+                                       _addr(v_cache), _addr(block_table), _addr(sparse_indices),
+                                       _addr(workspace), _addr(out), _addr(lse), stream)
+
+
+class SparseAttention:
+    """The consumer of sparse_indices: holds the problem and its workspace
+    (torch; marshalling only).  problem: dict with the qli_attn_problem fields."""
+
+    def __init__(self, problem: dict, device: str = "cuda"):
+        import torch
+        self.problem = AttnProblem.from_dict(problem)
+        rc, ws = qli_sparse_attention_workspace(self.problem)
+        if rc != QLI_OK:
+            raise QliError(rc, "qli_sparse_attention_workspace")
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device) if ws else None
+        self.device = device
+
+    @property
+    def rows(self) -> int:
+        p = self.problem
+        return p.batch * p.s1 if p.layout_query == LAYOUT_BSND else p.s1
+
+    def alloc_outputs(self):
+        import torch
+        p = self.problem
+        out = torch.empty((self.rows, p.num_heads, p.head_dim), dtype=torch.bfloat16, device=self.device)
+        lse = torch.empty((self.rows, p.num_heads), dtype=torch.float32, device=self.device) if p.return_lse else None
+        return out, lse
+
+    def run(self, q, k_cache, v_cache, block_table, sparse_indices, out=None, lse=None, aslq_dev=None,
+            stream: Optional[int] = None):
+        if out is None:
+            out, lse = self.alloc_outputs()
+        st = current_stream() if stream is None else stream
+        rc = qli_sparse_attention(self.problem, aslq_dev, q, k_cache, v_cache, block_table, sparse_indices,
+                                  self.workspace, out, lse, st)
+        if rc != QLI_OK:
+            raise QliError(rc, "qli_sparse_attention")
+        return out, lse

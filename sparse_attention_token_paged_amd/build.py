@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libqli.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("qli_api.cpp", "qli_kernels.hip", "qli_quant.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("qli_api.cpp", "qli_kernels.hip", "qli_quant.hip",
+                                          "qli_attention.hip")]
 HEADERS = [os.path.join(CSRC, "qli_internal.h"), os.path.join(INCLUDE, "qli.h")]
 ARCH = "gfx950"
 

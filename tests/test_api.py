@@ -465,3 +465,52 @@ def test_bounded_static_rejects_without_launching(qli):
     # the fp8 decode shape at its longest (64 x 65536 entries, k = 512) fits
     rc, ws = qli.qli_bounded_workspace(qli.Problem.from_dict(big), 65536)
     assert rc == qli.QLI_OK and ws <= 32 << 20
+
+
+def test_sparse_attention_rejects_without_launching(qli):
+    """The consumer's scalar and pointer checks return before any launch (the
+    fake addresses are never dereferenced)."""
+    base = dict(batch=2, s1=4, layout_query=synth.BSND, num_heads=64, head_dim=128, num_blocks=10,
+                block_size=64, max_blocks_per_seq=5, kv_block_stride=0, sparse_count=2048, softmax_scale=0.088,
+                return_lse=1)
+    P = lambda **kw: qli.AttnProblem.from_dict(dict(base, **kw))
+    fake = 1 << 40
+    args = [None, fake, fake, fake, fake, fake, fake, fake, fake]   # aslq, q, k, v, table, indices, ws, out, lse
+    f = qli.qli_sparse_attention
+    def expected_ws(rows, k, heads):
+        """Rows split into enough workgroups for two per CU, at least 256 entries
+        each (64-entry stages): fp32 partials O[128], max and sum per split and head."""
+        ns = max(1, min(-(-512 // rows), -(-k // 256)))
+        chunk = -(-(-(-k // ns)) // 64) * 64
+        ns = -(-k // chunk)
+        return 0 if ns == 1 else rows * ns * heads * 130 * 4
+    for rows, k in ((8, 2048), (8, 256), (96, 2048), (300, 2048), (1, 100), (33, 1000)):
+        rc, ws = qli.qli_sparse_attention_workspace(P(batch=rows, s1=1, sparse_count=k))
+        assert rc == qli.QLI_OK and ws == expected_ws(rows, k, 64), (rows, k)
+    assert expected_ws(8, 2048, 64) == 8 * 8 * 64 * 130 * 4
+    for kw, code in [(dict(num_heads=48), qli.QLI_ERR_UNSUPPORTED), (dict(head_dim=64), qli.QLI_ERR_UNSUPPORTED),
+                     (dict(block_size=40), qli.QLI_ERR_ARG), (dict(block_size=2048), qli.QLI_ERR_ARG),
+                     (dict(sparse_count=0), qli.QLI_ERR_ARG), (dict(sparse_count=2049), qli.QLI_ERR_ARG),
+                     (dict(softmax_scale=0.0), qli.QLI_ERR_ARG), (dict(softmax_scale=float("inf")), qli.QLI_ERR_ARG),
+                     (dict(kv_block_stride=100), qli.QLI_ERR_ARG), (dict(kv_block_stride=64 * 128 + 4),
+                                                                     qli.QLI_ERR_UNSUPPORTED),
+                     (dict(layout_query=2), qli.QLI_ERR_ARG), (dict(return_lse=2), qli.QLI_ERR_ARG),
+                     (dict(reserved1=1), qli.QLI_ERR_ARG), (dict(num_blocks=0), qli.QLI_ERR_ARG)]:
+        assert f(P(**kw), *args) == code, kw
+        assert qli.qli_sparse_attention_workspace(P(**kw))[0] == code, kw
+    a = list(args)
+    a[1] = None                                                      # q
+    assert f(P(), *a) == qli.QLI_ERR_ARG
+    a = list(args)
+    a[1] = fake + 2                                                  # q not 16-byte aligned
+    assert f(P(), *a) == qli.QLI_ERR_ARG
+    a = list(args)
+    a[8] = None                                                      # lse with return_lse = 1
+    assert f(P(), *a) == qli.QLI_ERR_ARG
+    a = list(args)
+    a[6] = None                                                      # workspace needed (split rows)
+    assert f(P(), *a) == qli.QLI_ERR_ARG
+    assert f(P(layout_query=synth.TND, s1=8), *args) == qli.QLI_ERR_ARG   # TND needs the prefix sums
+    assert f(P(batch=0), *args) == qli.QLI_OK                        # no rows: nothing to launch
+    rc, ws = qli.qli_sparse_attention_workspace(P(batch=300))        # enough rows: one workgroup per row
+    assert rc == qli.QLI_OK and ws == 0
