@@ -45,15 +45,16 @@ ROTATION_BYTES = 640 << 20     # distinct bytes touched between two uses of one 
 # The sources that decide what the kernels do and how they are launched.
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_attention_token_paged_amd", "csrc", f)
                   for f in ("qli_kernels.hip", "qli_internal.h", "qli_api.cpp")]
+CONSUMER_SOURCES = [os.path.join(ROOT, "sparse_attention_token_paged_amd", "csrc", "qli_attention.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 256 << 20         # bytes read and bytes written by the counter-calibration kernel
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(consumer: bool = False) -> str:
     """Hash of the code (comments and whitespace removed) of the kernel and
     launch sources: traffic measured on other code is not reported."""
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in (CONSUMER_SOURCES if consumer else KERNEL_SOURCES):
         with open(path) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -121,15 +122,15 @@ def algorithmic(info, problem) -> dict:
     )
 
 
-def traffic_from_profiles(workload: str):
-    """Measured HBM bytes per scoring-kernel launch from committed rocprofv3
-    counter summaries, if they were taken on the current kernel source."""
-    path = os.path.join(PROFILES, "traffic_score_kernel_%s.json" % workload)
+def traffic_from_profiles(workload: str, prefix: str = "traffic_score_kernel"):
+    """Measured HBM bytes per launch of the dominant kernel from committed
+    rocprofv3 counter summaries, if they were taken on the current kernel source."""
+    path = os.path.join(PROFILES, "%s_%s.json" % (prefix, workload))
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(prefix.startswith("traffic_attention")):
         return None
     return t.get("bytes_per_launch")
 
@@ -146,7 +147,7 @@ def _counter_rows(directory: str):
     return rows
 
 
-def summarize_counters(workload: str, fetch_dir: str, write_dir: str) -> dict:
+def summarize_counters(workload: str, fetch_dir: str, write_dir: str, consumer: bool = False) -> dict:
     """HBM bytes per scoring-kernel launch from two rocprofv3 --pmc runs of
     `bench.py --calibrate-copy` (FETCH_SIZE, then WRITE_SIZE; KiB per
     dispatch).  Each counter is scaled by COPY_BYTES over what it reads for
@@ -167,7 +168,8 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str) -> dict:
             raise SystemExit("no dispatch matched in the counter files")
         vals = sorted(v for n in names for v in d[n])
         return vals[len(vals) // 2], names
-    score = lambda n: "score_decode_kernel" in n or "score_kernel" in n
+    score = (lambda n: "attention_kernel" in n) if consumer else \
+        (lambda n: "score_decode_kernel" in n or "score_kernel" in n)
     neg = lambda n: "neg" in n
     f_score, names = pick(fetch, score)
     w_score, _ = pick(write, score)
@@ -177,7 +179,7 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str) -> dict:
     kw = COPY_BYTES / (w_neg * 1024.0)
     res = {
         "workload": workload,
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_source_sha256_16": kernel_source_hash(consumer),
         "kernels": sorted(set(n.replace("qli::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
                               for n in names)),
         "fetch_kib_per_launch_raw": f_score, "write_kib_per_launch_raw": w_score,
@@ -406,6 +408,113 @@ def producer_bench(args) -> dict:
     return res
 
 
+def consumer_bench(args) -> dict:
+    """The sparse-attention consumer on an indexer workload's shape: every
+    query row attends over sparse_count listed entries of bf16 key / value
+    caches with the workload's block table.  K back-to-back launches over
+    rotated cold copies, timed like the indexer steps; HBM roofline from the
+    algorithmic bytes; the oracle timed on a bounded sample of rows."""
+    import numpy as np
+    import torch
+    import synth
+    import sparse_attention_token_paged_amd as qli
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    qli.load()
+    hip = hip_runtime()
+    heads = args.heads
+    inp = synth.workload(args.workload)
+    a = synth.attention_inputs(inp, heads, 1000)
+    rows, k = a["indices"].shape
+    listed = int((a["indices"] >= 0).sum())
+    prob = dict(batch=a["batch"], s1=a["s1"], layout_query=a["layout"], num_heads=heads, head_dim=128,
+                num_blocks=a["num_blocks"], block_size=a["block_size"], max_blocks_per_seq=a["max_blocks"],
+                kv_block_stride=0, sparse_count=k, softmax_scale=a["scale"], return_lse=1)
+    att = qli.SparseAttention(prob)
+    # bytes the method moves: each listed entry's key and value rows once per row (bf16, 256 + 256),
+    # its block-table entry, the row's list, its query, output and lse
+    alg = listed * (512 + 4) + rows * (k * 4 + heads * 128 * 2 * 2 + heads * 4)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    cache_bytes = a["k_cache"].nbytes * 2
+    R = max(2, 1 + -(-ROTATION_BYTES // max(alg, cache_bytes)))
+    aslq = t(np.asarray(a["aslq"], dtype=np.int32)) if a["layout"] == synth.TND else None
+    sets = []
+    for _ in range(R):
+        out, lse = att.alloc_outputs()
+        sets.append((t(a["q"].view(np.int16)), t(a["k_cache"].view(np.int16)), t(a["v_cache"].view(np.int16)),
+                     t(a["block_table"]), t(a["indices"]), out, lse))
+    st = torch.cuda.current_stream().cuda_stream
+
+    def launch(s_):
+        return att.run(s_[0], s_[1], s_[2], s_[3], s_[4], s_[5], s_[6], aslq_dev=aslq, stream=st)
+    for i in range(args.warmup):
+        launch(sets[i % R])
+    torch.cuda.synchronize()
+    ev = Events(hip, 2)
+    for _ in range(2):
+        torch.cuda.synchronize()
+        hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), ctypes.c_void_p(st))
+        torch.cuda._sleep(1000000)
+        hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), ctypes.c_void_p(st))
+        torch.cuda.synchronize()
+    spin_cycles_per_us = 1000000 / (ev.ms(0, 1) * 1e3)
+    t0 = time.perf_counter()
+    for i in range(20):
+        launch(sets[i % R])
+    enqueue_us = (time.perf_counter() - t0) * 1e6 / 20
+    torch.cuda.synchronize()
+    K = args.steps
+    torch.cuda._sleep(int(spin_cycles_per_us * (1.5 * K * enqueue_us + 200.0)))
+    assert hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), ctypes.c_void_p(st)) == 0
+    for i in range(K):
+        launch(sets[i % R])
+    assert hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), ctypes.c_void_p(st)) == 0
+    torch.cuda.synchronize()
+    ms = ev.ms(0, 1) / K
+    ev.close()
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+    achieved = alg / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "listed (query-token, entry) pairs attended/s", "value": listed / (ms * 1e-3),
+        "unit": "pairs/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "attention_%s_h%d" % (args.workload, heads), "rows": rows, "heads": heads,
+                   "sparse_count": k, "listed": listed, "block_size": a["block_size"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "kernel": "attention_kernel (+ combine_kernel for split rows)", "kernel_ms": round(ms, 5),
+                     "algorithmic_bytes": alg,
+                     "traffic": traffic_from_profiles("%s_h%d" % (args.workload, heads), "traffic_attention_kernel")},
+        "step": {"cache_state": "every input cold: %d rotated copies" % R,
+                 "host_enqueue_us_per_step": round(enqueue_us, 2),
+                 "workspace_bytes": 0 if att.workspace is None else int(att.workspace.numel())},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle.attention as oa
+        aor = oa.get()
+        threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+        n = rows
+        done, passes, t0 = 0, 0, time.perf_counter()
+        while True:
+            rc, _, _ = aor.attention(a, nthreads=threads)
+            assert rc == 0
+            passes += 1
+            if time.perf_counter() - t0 >= 10.0:
+                break
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": listed * passes / el, "unit": "pairs/s", "cores": threads, "kind": "oracle",
+                               "cpu_model": cpu_model(),
+                               "sample": "all %d rows, %d full oracle pass(es) (fp64), %.2f s wall"
+                                         % (n, passes, el)}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -422,6 +531,10 @@ def main() -> int:
     ap.add_argument("--producer", action="store_true",
                     help="time the producer kernels on a producer workload (%s)" % ", ".join(
                         ["quantize_query_prefill_t8192", "append_keys_decode_b24_sk8192"]))
+    ap.add_argument("--consumer", action="store_true",
+                    help="time the sparse-attention consumer on the workload's shape (default: the headline "
+                         "decode workload)")
+    ap.add_argument("--heads", type=int, default=64, help="query heads of the consumer (16, 32, 64, 128)")
     ap.add_argument("--summarize-sq", metavar="SQ_DIR",
                     help="write profiles/issue_score_kernel_<workload>.json from a rocprofv3 --pmc run of "
                          + " ".join(SQ_COUNTERS))
@@ -433,8 +546,9 @@ def main() -> int:
         print(json.dumps(res))
         return 0
     if args.summarize_counters:
-        res = summarize_counters(args.workload, *args.summarize_counters)
-        path = os.path.join(PROFILES, "traffic_score_kernel_%s.json" % args.workload)
+        res = summarize_counters(args.workload, *args.summarize_counters, consumer=args.consumer)
+        path = os.path.join(PROFILES, ("traffic_attention_kernel_%s_h%d.json" % (args.workload, args.heads))
+                            if args.consumer else "traffic_score_kernel_%s.json" % args.workload)
         with open(path, "w") as f:
             json.dump(res, f, indent=1)
         print(json.dumps(res))
@@ -443,6 +557,11 @@ def main() -> int:
         print("bench.py measures one GPU only: the indexer runs on a single MI355X here; "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         return 2
+    if args.consumer:
+        if args.workload == DEFAULT_WORKLOAD:
+            args.workload = "decode_int8_b24_s4_sk8192"
+        print(json.dumps(consumer_bench(args)), flush=True)
+        return 0
     if args.producer:
         if args.workload == DEFAULT_WORKLOAD:
             args.workload = "quantize_query_prefill_t8192"

@@ -44,9 +44,9 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kDim = 128;         // head dim (the same D as the indexer's)
-constexpr int kStage = 64;        // entries per LDS stage
+constexpr int kStage = 32;        // entries per LDS stage
+constexpr int kRing = 4;          // stages in the LDS ring (three load while one is computed)
 constexpr int kMaxList = 2048;    // entries one workgroup compacts (sparse_count <= 2048)
-constexpr int kVtStride = 136;    // bytes per d-row of the transposed value tile (64 entries + 8 pad)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -94,66 +94,43 @@ __device__ int row_batch(const Params& P, int r) {
   return lo < P.batch ? lo : -1;
 }
 
+// Workgroup barrier without a memory fence: waits for this wave's LDS
+// accesses only, so direct-to-LDS loads of later stages stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <int HPW, int NW>
 __global__ __launch_bounds__(64 * NW) void attention_kernel(Params P) {
   constexpr int NT = 64 * NW;
-  constexpr int HG = HPW / 16;            // 16-head groups per wave
-  constexpr int KL = kStage * 256 / (NT * 16);  // 16-byte loads per thread per stage (keys, and values)
+  constexpr int HG = HPW / 16;                   // 16-head groups per wave
+  constexpr int KL = kStage * 256 / (NT * 16);   // 16-byte loads per thread per stage, of keys and of values
+  constexpr int PER = 2 * KL;                    // vector memory operations per thread per stage
+  constexpr int IPT = 8;                         // list slots per thread per compaction pass
 
-  // Two buffers of each tile as separate arrays: the compiler then tells a
-  // stage's key DMA apart from the reads of the other stage and does not wait
-  // for the loads in flight before computing.
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[kStage * 256];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[kStage * 256];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_vt0[kDim * kVtStride];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_vt1[kDim * kVtStride];
+  // The ring: kRing stages of kStage entries, keys and values as separate
+  // arrays per slot (row-major, 256 bytes per entry, 16-byte chunks stored at
+  // position chunk ^ (entry % 16)).
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kRing][kStage * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[kRing][kStage * 256];
   __shared__ int32_t lds_blk[kMaxList];
   __shared__ uint16_t lds_slot[kMaxList];
-  __shared__ int32_t lds_scan[NW + 1];
+  __shared__ int32_t lds_cnt[IPT][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, c16 = lane & 15;
   const int r = (int)blockIdx.x / P.nsplit;
   const int split = (int)blockIdx.x - r * P.nsplit;
-  const int b = row_batch(P, r);
   const int p0 = split * P.chunk;
   const int p1 = min(P.k, p0 + P.chunk);
   const int jmax = P.max_blocks * P.block_size;
 
-  // 1. Compact the split's valid entries (listed, inside the block table, on a
-  //    block of the cache) into LDS, in list order.
-  int nvalid = 0;
-  for (int base = p0; base < p1; base += NT) {
-    const int pos = base + tid;
-    int blk = -1, slot = 0;
-    if (b >= 0 && pos < p1) {
-      const int j = P.indices[(int64_t)r * P.k + pos];
-      if (j >= 0 && j < jmax) {
-        const int bb = P.block_table[(int64_t)b * P.max_blocks + j / P.block_size];
-        if (bb >= 0 && bb < P.num_blocks) {
-          blk = bb;
-          slot = j % P.block_size;
-        }
-      }
-    }
-    const bool v = blk >= 0;
-    const unsigned long long m = __ballot(v);
-    const int below = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) lds_scan[wave] = __popcll(m);
-    __syncthreads();
-    int before = nvalid;
-    for (int w = 0; w < wave; w++) before += lds_scan[w];
-    if (v) {
-      lds_blk[before + below] = blk;
-      lds_slot[before + below] = (uint16_t)slot;
-    }
-    int tot = 0;
-    for (int w = 0; w < NW; w++) tot += lds_scan[w];
-    nvalid += tot;
-    __syncthreads();
-  }
-
-  // 2. This wave's query heads as MFMA B operands (Q^T: K = d, N = head).
+  // 1. This wave's query heads as MFMA B operands (Q^T: K = d, N = head),
+  //    requested first: they do not depend on the list.
   bf16x8 qf[HG][4];
   const int h0 = wave * HPW;
 #pragma unroll
@@ -161,6 +138,51 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(Params P) {
     const uint16_t* qh = P.q + ((int64_t)r * P.heads + h0 + 16 * g + c16) * kDim + 8 * q4;
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) qf[g][ks] = *reinterpret_cast<const bf16x8*>(qh + 32 * ks);
+  }
+
+  // 2. Compact the split's valid entries (listed, inside the block table, on a
+  //    block of the cache) into LDS in list order: per pass, every list slot
+  //    and its block-table entry are requested at once, then one barrier.
+  const int b = row_batch(P, r);
+  int nvalid = 0;
+  for (int base = p0; base < p1; base += IPT * NT) {
+    int jv[IPT], bv[IPT];
+#pragma unroll
+    for (int i = 0; i < IPT; i++) {
+      const int pos = base + i * NT + tid;
+      jv[i] = (b >= 0 && pos < p1) ? P.indices[(int64_t)r * P.k + pos] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < IPT; i++) {
+      const int j = jv[i];
+      bv[i] = (j >= 0 && j < jmax) ? P.block_table[(int64_t)b * P.max_blocks + j / P.block_size] : -1;
+    }
+    unsigned long long m[IPT];
+#pragma unroll
+    for (int i = 0; i < IPT; i++) {
+      const bool v = bv[i] >= 0 && bv[i] < P.num_blocks;
+      m[i] = __ballot(v);
+      if (lane == 0) lds_cnt[i][wave] = __popcll(m[i]);
+    }
+    __syncthreads();
+    int before = nvalid;
+#pragma unroll
+    for (int i = 0; i < IPT; i++) {
+      int below_w = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; w++) {
+        below_w += w < wave ? lds_cnt[i][w] : 0;
+        tot += lds_cnt[i][w];
+      }
+      if ((m[i] >> lane) & 1ull) {
+        const int at = before + below_w + __popcll(m[i] & ((1ull << lane) - 1ull));
+        lds_blk[at] = bv[i];
+        lds_slot[at] = (uint16_t)(jv[i] % P.block_size);
+      }
+      before += tot;
+    }
+    nvalid = before;
+    __syncthreads();
   }
 
   v4f o[HG][8];
@@ -173,140 +195,134 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(Params P) {
     for (int t = 0; t < 8; t++) o[g][t] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Loader: the thread's piece i of a stage is entry kk = 4 (i NW + wave) +
-  // lane / 16, 16-byte chunk lane % 16.  Keys: direct-to-LDS, the chunk
-  // stored at physical position lane % 16 holding logical chunk
-  // (lane % 16) ^ (kk % 16).  Values: into registers (logical chunk lane % 16).
+  // Loader: piece i of a stage is entry kk = 4 (i NW + wave) + lane / 16 of
+  // the stage, 16-byte chunk lane % 16; the chunk stored at position
+  // lane % 16 of the entry's row is the logical chunk (lane % 16) ^ (kk % 16).
+  // Entries past the list load its last entry again (masked when scored).
   const int nst = (nvalid + kStage - 1) / kStage;
-  uint4 vr[KL];
-  auto entry_off = [&](int e) -> int64_t {  // element offset of compacted entry e (clamped into the list)
-    const int ee = min(e, nvalid - 1);
-    return (int64_t)lds_blk[ee] * P.stride + (int64_t)lds_slot[ee] * kDim;
-  };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  auto issue = [&](int st, auto buf_) __attribute__((always_inline)) {
-    uint8_t* kb = decltype(buf_)::value ? lds_k1 : lds_k0;
+  auto issue = [&](int st, auto slot_) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_)::value;
 #pragma unroll
     for (int i = 0; i < KL; i++) {
       const int kk = 4 * (i * NW + wave) + q4;
-      const int64_t off = entry_off(st * kStage + kk);
-      const int lc = c16 ^ (kk & 15);
-      __builtin_amdgcn_global_load_lds(P.kc + off + 8 * lc,
-                                       (__attribute__((address_space(3))) void*)&kb[(i * NW + wave) * 1024],
+      const int e = min(st * kStage + kk, nvalid - 1);
+      const int64_t off = (int64_t)lds_blk[e] * P.stride + (int64_t)lds_slot[e] * kDim + 8 * (c16 ^ (kk & 15));
+      __builtin_amdgcn_global_load_lds(P.kc + off, (__attribute__((address_space(3))) void*)&lds_k[S][(i * NW + wave) * 1024],
                                        16, 0, 0);
-      vr[i] = *reinterpret_cast<const uint4*>(P.vc + off + 8 * c16);
+      __builtin_amdgcn_global_load_lds(P.vc + off, (__attribute__((address_space(3))) void*)&lds_v[S][(i * NW + wave) * 1024],
+                                       16, 0, 0);
     }
   };
-  // Values of piece i: entry kk, dims 8 (lane % 16) .. +7, into column kk of the [d][entry] tile.
-  auto stash_v = [&](auto buf_) __attribute__((always_inline)) {
-    uint8_t* vt = decltype(buf_)::value ? lds_vt1 : lds_vt0;
+
+  // Stage st: computed from ring slot st % kRing once its loads have landed.
+  auto compute = [&](int st, auto slot_) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_)::value;
+    const int live = nvalid - st * kStage;  // entries of this stage that exist (>= 1)
+    const uint8_t* kt = lds_k[S];
+    const uint8_t* vt = lds_v[S];
+    // S^T for kStage entries x 16 heads per group: A = keys (rows), B = Q^T.
+    bf16x8 ka[2][4];
 #pragma unroll
-    for (int i = 0; i < KL; i++) {
-      const int kk = 4 * (i * NW + wave) + q4;
-      const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+    for (int kt2 = 0; kt2 < 2; kt2++) {
+      const int key = 16 * kt2 + c16;
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const uint16_t h = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-        *reinterpret_cast<uint16_t*>(vt + (8 * c16 + e) * kVtStride + 2 * kk) = h;
+      for (int ks = 0; ks < 4; ks++) {
+        const int pc = (4 * ks + q4) ^ c16;
+        ka[kt2][ks] = *reinterpret_cast<const bf16x8*>(kt + key * 256 + pc * 16);
       }
     }
-  };
-
-  if (nst > 0) {
-    issue(0, B0{});
-    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) and lgkmcnt(0): stage 0 landed
-    stash_v(B0{});
-    __syncthreads();
-  }
-
-  // Stage st computes from buffer st % 2 while stage st + 1 loads into the other.
-  auto step = [&](int st, auto buf_) __attribute__((always_inline)) {
-    constexpr int BUF = decltype(buf_)::value;
-    using Next = std::integral_constant<int, BUF ^ 1>;
-    if (st + 1 < nst) issue(st + 1, Next{});
-    const int live = nvalid - st * kStage;  // entries of this stage that exist (>= 1)
-    const uint8_t* kt = BUF ? lds_k1 : lds_k0;
-    const uint8_t* vt = BUF ? lds_vt1 : lds_vt0;
+    // V^T operands of the 8 d-tiles: row d = 16 t + lane % 16, K positions
+    // 8 q .. 8 q + 7 <-> entries 4 q + {0..3} and 16 + 4 q + {0..3}; element
+    // (entry e, dim d) sits in chunk (d / 8) ^ (e % 16) of row e.
+    bf16x8 va[8];
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      if (32 * u >= live) break;  // uniform
-      // S^T for 32 entries x 16 heads per group: A = keys (rows), B = Q^T.
-      bf16x8 ka[2][4];
+    for (int t = 0; t < 8; t++) {
+      const int d = 16 * t + c16;
+#pragma unroll
+      for (int x = 0; x < 8; x++) {
+        const int e = (x < 4 ? 0 : 16) + 4 * q4 + (x & 3);
+        const int pc = (d >> 3) ^ (e & 15);
+        va[t][x] = *reinterpret_cast<const __bf16*>(vt + e * 256 + pc * 16 + 2 * (d & 7));
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < HG; g++) {
+      v4f sc[2];
 #pragma unroll
       for (int kt2 = 0; kt2 < 2; kt2++) {
-        const int key = 32 * u + 16 * kt2 + c16;
+        sc[kt2] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-          const int pc = (4 * ks + q4) ^ c16;
-          ka[kt2][ks] = *reinterpret_cast<const bf16x8*>(kt + key * 256 + pc * 16);
-        }
+        for (int ks = 0; ks < 4; ks++)
+          sc[kt2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kt2][ks], qf[g][ks], sc[kt2], 0, 0, 0);
       }
-      // V^T operands of the 8 d-tiles: row d = 16 t + lane % 16, K positions
-      // 8 q .. 8 q + 7 <-> entries 32 u + 4 q + {0..3} and 32 u + 16 + 4 q + {0..3}.
-      bf16x8 va[8];
+      // lane: head 16 g + lane % 16; entries 16 kt2 + 4 q + i
+      float x[8];
+      float mt = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < 8; t++) {
-        const uint8_t* row = vt + (16 * t + c16) * kVtStride + 2 * (32 * u + 4 * q4);
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 32);
-        va[t] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+      for (int kt2 = 0; kt2 < 2; kt2++)
 #pragma unroll
-      for (int g = 0; g < HG; g++) {
-        v4f s[2];
-#pragma unroll
-        for (int kt2 = 0; kt2 < 2; kt2++) {
-          s[kt2] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ks++)
-            s[kt2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kt2][ks], qf[g][ks], s[kt2], 0, 0, 0);
+        for (int i = 0; i < 4; i++) {
+          const int e = 16 * kt2 + 4 * q4 + i;
+          const float v = e < live ? sc[kt2][i] * P.scale_log2 : -INFINITY;
+          x[4 * kt2 + i] = v;
+          mt = fmaxf(mt, v);
         }
-        // lane: head 16 g + lane % 16; entries 32 u + 16 kt2 + 4 q + i
-        float x[8];
-        float mt = -INFINITY;
+      mt = max4(mt);
+      const float m_new = fmaxf(m_run[g], mt);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;  // nothing seen yet: every p is 0
+      const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_use);
+      m_run[g] = m_new;
+      float ps = 0.f;
 #pragma unroll
-        for (int kt2 = 0; kt2 < 2; kt2++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int e = 32 * u + 16 * kt2 + 4 * q4 + i;
-            const float v = e < live ? s[kt2][i] * P.scale_log2 : -INFINITY;
-            x[4 * kt2 + i] = v;
-            mt = fmaxf(mt, v);
-          }
-        mt = max4(mt);
-        const float m_new = fmaxf(m_run[g], mt);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // nothing seen yet: every p is 0
-        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_use);
-        m_run[g] = m_new;
-        float ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-          x[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
-          ps += x[e];
-        }
-        l_run[g] = l_run[g] * alpha + ps;
-#pragma unroll
-        for (int t = 0; t < 8; t++) o[g][t] *= alpha;
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; e++) pb[e] = (__bf16)x[e];
-#pragma unroll
-        for (int t = 0; t < 8; t++) o[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[t], pb, o[g][t], 0, 0, 0);
+      for (int e = 0; e < 8; e++) {
+        x[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+        ps += x[e];
       }
+      l_run[g] = l_run[g] * alpha + ps;
+#pragma unroll
+      for (int t = 0; t < 8; t++) o[g][t] *= alpha;
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; e++) pb[e] = (__bf16)x[e];
+#pragma unroll
+      for (int t = 0; t < 8; t++) o[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[t], pb, o[g][t], 0, 0, 0);
     }
-    if (st + 1 < nst) {
-      __builtin_amdgcn_s_waitcnt(0);  // stage st + 1 landed (keys in LDS, values in registers)
-      stash_v(Next{});
-    }
-    __syncthreads();
   };
-  for (int st = 0; st < nst; st += 2) {
-    step(st, B0{});
-    if (st + 1 < nst) step(st + 1, B1{});
+
+  // 3. The ring: stages st + 1 .. st + kRing - 1 load while stage st is
+  //    computed.  At the top of step st, this wave's pieces of stages st ..
+  //    min(st + kRing - 2, nst - 1) are outstanding; waiting until only the
+  //    newer ones are leaves stage st landed, and the barrier makes every
+  //    wave's pieces visible and frees the slot computed in step st - 1, which
+  //    then receives stage st + kRing - 1.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  static_assert(kRing == 4, "the step below names four slots");
+  if (nst > 0) issue(0, S0{});
+  if (nst > 1) issue(1, S1{});
+  if (nst > 2) issue(2, S2{});
+  auto step = [&](int st, auto slot_, auto prev_) __attribute__((always_inline)) {
+    const int newer = min(st + kRing - 2, nst - 1) - st;
+    if (newer >= 2)
+      wait_vm<2 * PER>();
+    else if (newer == 1)
+      wait_vm<PER>();
+    else
+      wait_vm<0>();
+    lds_barrier();
+    if (st + kRing - 1 < nst) issue(st + kRing - 1, prev_);
+    compute(st, slot_);
+  };
+  for (int st = 0; st < nst; st += kRing) {
+    step(st, S0{}, S3{});
+    if (st + 1 < nst) step(st + 1, S1{}, S0{});
+    if (st + 2 < nst) step(st + 2, S2{}, S1{});
+    if (st + 3 < nst) step(st + 3, S3{}, S2{});
   }
 
-  // 3. Finish: lane holds head h0 + 16 g + lane % 16, dims 16 t + 4 q + {0..3}.
+  // 4. Finish: lane holds head h0 + 16 g + lane % 16, dims 16 t + 4 q + {0..3}.
 #pragma unroll
   for (int g = 0; g < HG; g++) {
     const int h = h0 + 16 * g + c16;
@@ -337,45 +353,44 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(Params P) {
 }
 
 // Merge of a split row's partials: M = max_s m_s, L = sum_s l_s 2^(m_s - M),
-// out = sum_s O_s 2^(m_s - M) / L, lse = (M + log2 L) ln 2.  One workgroup per
-// row; thread t handles float4 column groups of (head, dims).
+// out = sum_s O_s 2^(m_s - M) / L, lse = (M + log2 L) ln 2.  32 threads per
+// (row, head), one float4 of dims each; workgroups of 8 heads.
 __global__ __launch_bounds__(256) void combine_kernel(Params P) {
-  const int r = blockIdx.x;
-  const int groups = P.heads * (kDim / 4);
-  for (int gi = threadIdx.x; gi < groups; gi += 256) {
-    const int h = gi / (kDim / 4), d4 = gi - h * (kDim / 4);
-    float M = -INFINITY;
-    for (int s = 0; s < P.nsplit; s++) M = fmaxf(M, P.part_ml[2 * (((int64_t)r * P.nsplit + s) * P.heads + h)]);
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    float L = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < P.nsplit; s++) {
-        const int64_t slot = ((int64_t)r * P.nsplit + s) * P.heads + h;
-        const float ms = P.part_ml[2 * slot];
-        if (ms == -INFINITY) continue;
-        const float w = __builtin_amdgcn_exp2f(ms - M);
-        L += P.part_ml[2 * slot + 1] * w;
-        acc += *reinterpret_cast<const v4f*>(P.part_o + slot * kDim + 4 * d4) * w;
-      }
+  const int64_t pair = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);  // row * heads + head
+  const int d4 = threadIdx.x & 31;
+  const int64_t rows_heads = (int64_t)gridDim.x * 8;
+  if (pair >= rows_heads) return;
+  const int r = (int)(pair / P.heads), h = (int)(pair - (int64_t)r * P.heads);
+  float M = -INFINITY;
+  for (int s = 0; s < P.nsplit; s++) M = fmaxf(M, P.part_ml[2 * (((int64_t)r * P.nsplit + s) * P.heads + h)]);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < P.nsplit; s++) {
+      const int64_t slot = ((int64_t)r * P.nsplit + s) * P.heads + h;
+      const float ms = P.part_ml[2 * slot];
+      if (ms == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(ms - M);
+      L += P.part_ml[2 * slot + 1] * w;
+      acc += *reinterpret_cast<const v4f*>(P.part_o + slot * kDim + 4 * d4) * w;
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    bf16x4 v;
-#pragma unroll
-    for (int i = 0; i < 4; i++) v[i] = (__bf16)(acc[i] * inv);
-    *reinterpret_cast<bf16x4*>(P.out + ((int64_t)r * P.heads + h) * kDim + 4 * d4) = v;
-    if (P.lse && d4 == 0)
-      P.lse[(int64_t)r * P.heads + h] = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
   }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  bf16x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; i++) v[i] = (__bf16)(acc[i] * inv);
+  *reinterpret_cast<bf16x4*>(P.out + pair * kDim + 4 * d4) = v;
+  if (P.lse && d4 == 0) P.lse[pair] = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
 }
 
-// Split of each row's list: enough workgroups to cover the chip (two per CU)
-// without going below 256 entries per split.
+// Split of each row's list: as many workgroups as the chip holds at once
+// (two per CU) without going below 256 entries per split.
 struct Split {
   int nsplit, chunk;
 };
 Split choose_split(int64_t rows, int k) {
-  const int64_t target = 2 * 256;
-  int64_t ns = rows > 0 ? (target + rows - 1) / rows : 1;
+  const int64_t target = 2 * 256;  // resident workgroups: every split runs in one round
+  int64_t ns = rows > 0 ? target / rows : 1;
   const int64_t cap = (k + 255) / 256;
   ns = ns < 1 ? 1 : (ns > cap ? cap : ns);
   int chunk = (int)((k + ns - 1) / ns);
@@ -491,7 +506,8 @@ QLI_EXPORT int qli_sparse_attention(const qli_attn_problem* p, const int32_t* as
     default: e = launch_attention<32, 4>(P, rows, st); break;
   }
   if (e == hipSuccess && s.nsplit > 1) {
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)rows), dim3(256), 0, st, P);
+    // rows * heads is a multiple of 8 (heads is)
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(rows * p->num_heads / 8)), dim3(256), 0, st, P);
     e = hipGetLastError();
   }
   return e == hipSuccess ? QLI_OK : QLI_ERR_HIP;
