@@ -478,16 +478,17 @@ def test_sparse_attention_rejects_without_launching(qli):
     args = [None, fake, fake, fake, fake, fake, fake, fake, fake]   # aslq, q, k, v, table, indices, ws, out, lse
     f = qli.qli_sparse_attention
     def expected_ws(rows, k, heads):
-        """Rows split into enough workgroups for two per CU, at least 256 entries
-        each (64-entry stages): fp32 partials O[128], max and sum per split and head."""
-        ns = max(1, min(-(-512 // rows), -(-k // 256)))
-        chunk = -(-(-(-k // ns)) // 64) * 64
+        """Rows split so that every workgroup fits one round of two per CU, at
+        least 256 entries each (32-entry stages): fp32 partials O[128], max and
+        sum per split and head."""
+        ns = max(1, min(512 // rows, -(-k // 256)))
+        chunk = -(-(-(-k // ns)) // 32) * 32
         ns = -(-k // chunk)
         return 0 if ns == 1 else rows * ns * heads * 130 * 4
     for rows, k in ((8, 2048), (8, 256), (96, 2048), (300, 2048), (1, 100), (33, 1000)):
         rc, ws = qli.qli_sparse_attention_workspace(P(batch=rows, s1=1, sparse_count=k))
         assert rc == qli.QLI_OK and ws == expected_ws(rows, k, 64), (rows, k)
-    assert expected_ws(8, 2048, 64) == 8 * 8 * 64 * 130 * 4
+    assert expected_ws(8, 2048, 64) == 8 * 8 * 64 * 130 * 4 and expected_ws(96, 2048, 64) == 96 * 5 * 64 * 130 * 4
     for kw, code in [(dict(num_heads=48), qli.QLI_ERR_UNSUPPORTED), (dict(head_dim=64), qli.QLI_ERR_UNSUPPORTED),
                      (dict(block_size=40), qli.QLI_ERR_ARG), (dict(block_size=2048), qli.QLI_ERR_ARG),
                      (dict(sparse_count=0), qli.QLI_ERR_ARG), (dict(sparse_count=2049), qli.QLI_ERR_ARG),
