@@ -17,6 +17,8 @@ import threading
 
 import numpy as np
 
+INT64_MAX = (1 << 63) - 1  # the pre_tokens / next_tokens default: no window
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "qli_oracle.c")
 LIBRARY = os.path.join(_HERE, "liboracle.so")
@@ -66,7 +68,11 @@ class Oracle:
         lib.qlio_topk.restype = i64
         lib.qlio_row_visible.argtypes = [i32, i32, i32, i32, i32, c_p, c_p, c_p]
         lib.qlio_row_visible.restype = i32
-        lib.qlio_indexer.argtypes = [i32] * 8 + [i64] + [i32] * 3 + [c_p] * 10 + [c_p, i64, i32]
+        lib.qlio_visible_range.argtypes = [i32, i32, i64, i64, i64, i64, i64, c_p]
+        lib.qlio_visible_range.restype = i64
+        lib.qlio_row_range.argtypes = [i32, i32, i32, i32, i32, c_p, c_p, i64, i64, c_p, c_p]
+        lib.qlio_row_range.restype = i32
+        lib.qlio_indexer.argtypes = [i32] * 8 + [i64] + [i32] * 3 + [i64, i64] + [c_p] * 10 + [c_p, i64, i32]
         lib.qlio_indexer.restype = i32
         lib.qlio_row_detail.argtypes = [i32] * 7 + [i64] + [i32, i32] + [c_p] * 8 + [i64, i64, i64, c_p, c_p]
         lib.qlio_row_detail.restype = i64
@@ -97,6 +103,26 @@ class Oracle:
         self.lib.qlio_row_visible(layout, batch, s1_or_t, sparse_mode, cmp_ratio, _ptr(aq), _ptr(ak), _ptr(out))
         return out
 
+    def visible_range(self, sparse_mode: int, cmp_ratio: int, skb: int, s1b: int, i: int,
+                      pre_tokens: int = INT64_MAX, next_tokens: int = INT64_MAX):
+        """(lo, hi): query i sees entries [lo, hi)."""
+        lo = ctypes.c_int64(0)
+        hi = self.lib.qlio_visible_range(sparse_mode, cmp_ratio, skb, s1b, i, pre_tokens, next_tokens,
+                                         ctypes.byref(lo))
+        return lo.value, hi
+
+    def row_range(self, layout, batch, s1_or_t, sparse_mode, cmp_ratio, aslq, aslk,
+                  pre_tokens=INT64_MAX, next_tokens=INT64_MAX):
+        """(lo[rows], hi[rows]): row r sees entries [lo[r], hi[r])."""
+        rows = batch * s1_or_t if layout == 0 else s1_or_t
+        lo = np.zeros(rows, dtype=np.int64)
+        hi = np.zeros(rows, dtype=np.int64)
+        aq = None if aslq is None else np.ascontiguousarray(aslq, dtype=np.int32)
+        ak = np.ascontiguousarray(aslk, dtype=np.int32)
+        self.lib.qlio_row_range(layout, batch, s1_or_t, sparse_mode, cmp_ratio, _ptr(aq), _ptr(ak),
+                                pre_tokens, next_tokens, _ptr(lo), _ptr(hi))
+        return lo, hi
+
     def indexer(self, inp: dict, *, scores_cols: int = 0, nthreads: int = 0):
         """Whole operator.  Returns (rc, indices[rows,k], values[rows,k], scores or None)."""
         p = inp["problem"]
@@ -109,6 +135,7 @@ class Oracle:
             p["qk_dtype"], p["scale_dtype"], p["layout_query"], p["batch"], p["s1"],
             p["num_blocks"], p["block_size"], p["max_blocks_per_seq"], p["key_block_stride"],
             p["sparse_count"], p["sparse_mode"], p["cmp_ratio"],
+            p.get("pre_tokens", INT64_MAX), p.get("next_tokens", INT64_MAX),
             _ptr(inp["query"]), _ptr(inp["key"]), _ptr(inp["weights"]), _ptr(inp["q_scale"]),
             _ptr(inp["k_scale"]), _ptr(inp["aslq"]), _ptr(inp["aslk"]), _ptr(inp["block_table"]),
             _ptr(idx), _ptr(val), _ptr(sc), scores_cols, nthreads)

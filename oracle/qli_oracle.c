@@ -129,6 +129,50 @@ int64_t qlio_visible(int sparse_mode, int cmp_ratio, int64_t skb, int64_t s1b,
     return v < stored ? v : stored;
 }
 
+/* Is original token t inside the window of a query at position pos?
+ * Written with differences of small numbers only, so that the default
+ * 2^63-1 of either bound cannot overflow. */
+static int in_window(int64_t t, int64_t pos, int64_t pre_tokens, int64_t next_tokens)
+{
+    if (t < pos && pos - t > pre_tokens)
+        return 0;
+    if (t > pos && t - pos > next_tokens)
+        return 0;
+    return 1;
+}
+
+/* Visible range [*lo, return value) of query i, windows included.
+ *  [参数说明] pre_tokens / next_tokens: the page marks both as reserved
+ *    parameters (only the default 2^63-1 accepted) that say how many tokens
+ *    before (after) a query the attention relates to.  reading, for other
+ *    values: query i sits at the original position pos = skb - s1b + i (the
+ *    same bottom-right alignment as sparse_mode 3, for both modes); token t
+ *    is inside its window when pos - pre_tokens <= t <= pos + next_tokens;
+ *    an entry is visible when sparse_mode lets the query see it and every
+ *    token it covers is inside the window.  The window is an interval, so
+ *    the visible entries are consecutive; with the defaults the range is
+ *    [0, qlio_visible).  Both bounds are >= 0 (validate). */
+int64_t qlio_visible_range(int sparse_mode, int cmp_ratio, int64_t skb, int64_t s1b, int64_t i,
+                           int64_t pre_tokens, int64_t next_tokens, int64_t *lo_out)
+{
+    int64_t n = qlio_visible(sparse_mode, cmp_ratio, skb, s1b, i);
+    int64_t pos = skb - s1b + i;
+    int64_t j, lo = -1, hi = -1;
+    for (j = 0; j < n; j++) {
+        int64_t first = j * cmp_ratio, last = (j + 1) * cmp_ratio - 1;
+        if (in_window(first, pos, pre_tokens, next_tokens) &&
+            in_window(last, pos, pre_tokens, next_tokens)) {
+            if (lo < 0)
+                lo = j;
+            hi = j + 1;
+        }
+    }
+    if (lo < 0)
+        lo = hi = 0;
+    *lo_out = lo;
+    return hi;
+}
+
 /* ------------------------------------------------------------------ */
 /* Paged key access                                                   */
 /* ------------------------------------------------------------------ */
@@ -205,6 +249,8 @@ typedef struct {
     int sparse_count;
     int sparse_mode;
     int cmp_ratio;
+    int64_t pre_tokens;
+    int64_t next_tokens;
     const uint8_t *query;
     const void *weights;
     const void *q_scale;
@@ -250,12 +296,16 @@ static int locate_row(const oracle_problem *p, int64_t r, int *b, int64_t *i,
     }
 }
 
-static int64_t row_visible(const oracle_problem *p, int64_t r, int *b)
+/* Visible range [*lo, return value) of output row r (empty for rows that
+ * belong to no query token). */
+static int64_t row_range(const oracle_problem *p, int64_t r, int *b, int64_t *lo)
 {
     int64_t i, s1b;
+    *lo = 0;
     if (!locate_row(p, r, b, &i, &s1b))
         return 0;
-    return qlio_visible(p->sparse_mode, p->cmp_ratio, p->aslk[*b], s1b, i);
+    return qlio_visible_range(p->sparse_mode, p->cmp_ratio, p->aslk[*b], s1b, i, p->pre_tokens,
+                              p->next_tokens, lo);
 }
 
 /* One score, literally as the [功能说明] formula reads:
@@ -345,6 +395,10 @@ static int validate(const oracle_problem *p, int num_blocks, int max_blocks)
         return QLIO_E_ARG;
     if (p->sparse_mode != 0 && p->sparse_mode != 3)
         return QLIO_E_ARG;
+    /* pre_tokens / next_tokens: the window reading (qlio_visible_range)
+     * takes bounds >= 0. */
+    if (p->pre_tokens < 0 || p->next_tokens < 0)
+        return QLIO_E_ARG;
     for (c = 1; c <= 128 && c != p->cmp_ratio; c *= 2)
         ;
     if (c > 128)
@@ -396,7 +450,8 @@ static int validate(const oracle_problem *p, int num_blocks, int max_blocks)
 static int fill_problem(oracle_problem *p, int qk_dtype, int scale_dtype,
                         int layout, int batch, int s1_or_t, int block_size,
                         int max_blocks, int64_t key_stride, int sparse_count,
-                        int sparse_mode, int cmp_ratio, const void *query,
+                        int sparse_mode, int cmp_ratio, int64_t pre_tokens,
+                        int64_t next_tokens, const void *query,
                         const void *key, const void *weights,
                         const void *q_scale, const void *k_scale,
                         const int32_t *aslq, const int32_t *aslk,
@@ -410,6 +465,8 @@ static int fill_problem(oracle_problem *p, int qk_dtype, int scale_dtype,
     p->sparse_count = sparse_count;
     p->sparse_mode = sparse_mode;
     p->cmp_ratio = cmp_ratio;
+    p->pre_tokens = pre_tokens;
+    p->next_tokens = next_tokens;
     p->query = (const uint8_t *)query;
     p->weights = weights;
     p->q_scale = q_scale;
@@ -430,10 +487,12 @@ static int64_t total_rows(const oracle_problem *p)
     return p->layout == 0 ? (int64_t)p->batch * p->s1_or_t : (int64_t)p->s1_or_t;
 }
 
-/* Visible-entry count of every output row (rows = B*S1 for BSND, T for TND). */
-int qlio_row_visible(int layout, int batch, int s1_or_t, int sparse_mode,
-                     int cmp_ratio, const int32_t *aslq, const int32_t *aslk,
-                     int64_t *vis_out)
+/* Visible range of every output row (rows = B*S1 for BSND, T for TND):
+ * entries [lo_out[r], hi_out[r]). */
+int qlio_row_range(int layout, int batch, int s1_or_t, int sparse_mode,
+                   int cmp_ratio, const int32_t *aslq, const int32_t *aslk,
+                   int64_t pre_tokens, int64_t next_tokens, int64_t *lo_out,
+                   int64_t *hi_out)
 {
     oracle_problem p;
     int64_t r, n;
@@ -443,31 +502,60 @@ int qlio_row_visible(int layout, int batch, int s1_or_t, int sparse_mode,
     p.s1_or_t = s1_or_t;
     p.sparse_mode = sparse_mode;
     p.cmp_ratio = cmp_ratio;
+    p.pre_tokens = pre_tokens;
+    p.next_tokens = next_tokens;
     p.aslq = aslq;
     p.aslk = aslk;
     n = total_rows(&p);
     for (r = 0; r < n; r++) {
         int b;
-        vis_out[r] = row_visible(&p, r, &b);
+        hi_out[r] = row_range(&p, r, &b, &lo_out[r]);
+    }
+    return QLIO_OK;
+}
+
+/* Visible-entry count of every output row without a window. */
+int qlio_row_visible(int layout, int batch, int s1_or_t, int sparse_mode,
+                     int cmp_ratio, const int32_t *aslq, const int32_t *aslk,
+                     int64_t *vis_out)
+{
+    oracle_problem p;
+    int64_t r, n, lo;
+    memset(&p, 0, sizeof(p));
+    p.layout = layout;
+    p.batch = batch;
+    p.s1_or_t = s1_or_t;
+    p.sparse_mode = sparse_mode;
+    p.cmp_ratio = cmp_ratio;
+    p.pre_tokens = INT64_MAX;
+    p.next_tokens = INT64_MAX;
+    p.aslq = aslq;
+    p.aslk = aslk;
+    n = total_rows(&p);
+    for (r = 0; r < n; r++) {
+        int b;
+        vis_out[r] = row_range(&p, r, &b, &lo);
     }
     return QLIO_OK;
 }
 
 /* The whole operator.
  *  Outputs ([参数说明] sparse_indices INT32 / sparse_values FLOAT32),
- *  shaped [rows, sparse_count]:
+ *  shaped [rows, sparse_count]; row r sees entries [lo, hi) (row_range),
+ *  vis = hi - lo of them:
  *    sparse_indices[r, 0:n] = top-n entry indices (n = min(k, vis)), in the
  *      order score descending, index ascending; sparse_indices[r, n:k] = -1.
  *    sparse_values[r, 0:n] = the fp32 rounding of those scores; the rest
  *      -INFINITY.  (reading: the page defines sparse_values as the values of
  *      the returned indices.)
  *  Optional: scores[r * score_cols + j] = fp64 score of visible entry j
- *    (entries past vis(r) are left untouched).
+ *    (entries outside [lo, hi) are left untouched).
  *  nthreads <= 0 uses the OpenMP default. */
 int qlio_indexer(int qk_dtype, int scale_dtype, int layout, int batch,
                  int s1_or_t, int num_blocks, int block_size, int max_blocks,
                  int64_t key_stride, int sparse_count, int sparse_mode,
-                 int cmp_ratio, const void *query, const void *key,
+                 int cmp_ratio, int64_t pre_tokens, int64_t next_tokens,
+                 const void *query, const void *key,
                  const void *weights, const void *q_scale, const void *k_scale,
                  const int32_t *aslq, const int32_t *aslk,
                  const int32_t *block_table, int32_t *sparse_indices,
@@ -479,8 +567,8 @@ int qlio_indexer(int qk_dtype, int scale_dtype, int layout, int batch,
     int rc, failed = 0;
     fill_problem(&p, qk_dtype, scale_dtype, layout, batch, s1_or_t,
                  block_size, max_blocks, key_stride, sparse_count, sparse_mode,
-                 cmp_ratio, query, key, weights, q_scale, k_scale, aslq, aslk,
-                 block_table);
+                 cmp_ratio, pre_tokens, next_tokens, query, key, weights,
+                 q_scale, k_scale, aslq, aslk, block_table);
     rc = validate(&p, num_blocks, max_blocks);
     if (rc != QLIO_OK)
         return rc;
@@ -492,7 +580,7 @@ int qlio_indexer(int qk_dtype, int scale_dtype, int layout, int batch,
 #endif
     for (r = 0; r < rows; r++) {
         int b = 0;
-        int64_t vis = row_visible(&p, r, &b), j, n;
+        int64_t lo, hi = row_range(&p, r, &b, &lo), vis = hi - lo, j, n;
         int32_t *oi = sparse_indices + r * sparse_count;
         float *ov = sparse_values ? sparse_values + r * sparse_count : NULL;
         double *sc;
@@ -512,17 +600,18 @@ int qlio_indexer(int qk_dtype, int scale_dtype, int layout, int batch,
             failed = 1;
             continue;
         }
+        /* sc[e] = score of entry lo + e; the top-k positions map back by + lo */
         for (j = 0; j < vis; j++)
-            sc[j] = score_one(&p, r, b, j, NULL, 0);
+            sc[j] = score_one(&p, r, b, lo + j, NULL, 0);
         n = qlio_topk(sc, vis, sparse_count, top);
         for (j = 0; j < n; j++) {
-            oi[j] = (int32_t)top[j];
+            oi[j] = (int32_t)(lo + top[j]);
             if (ov)
                 ov[j] = (float)sc[top[j]];
         }
         if (scores)
-            for (j = 0; j < vis && j < score_cols; j++)
-                scores[r * score_cols + j] = sc[j];
+            for (j = 0; j < vis && lo + j < score_cols; j++)
+                scores[r * score_cols + lo + j] = sc[j];
         free(sc);
         free(top);
     }
@@ -545,12 +634,13 @@ int64_t qlio_row_detail(int qk_dtype, int scale_dtype, int layout, int batch,
 {
     oracle_problem p;
     int b = 0;
-    int64_t vis, j;
+    int64_t vis, lo, j;
+    /* the score of an entry does not depend on a window: none is applied */
     fill_problem(&p, qk_dtype, scale_dtype, layout, batch, s1_or_t,
                  block_size, max_blocks, key_stride, 1, sparse_mode, cmp_ratio,
-                 query, key, weights, q_scale, k_scale, aslq, aslk,
-                 block_table);
-    vis = row_visible(&p, row, &b);
+                 INT64_MAX, INT64_MAX, query, key, weights, q_scale, k_scale,
+                 aslq, aslk, block_table);
+    vis = row_range(&p, row, &b, &lo);
     if (j0 < 0 || j1 < j0 || j1 > vis)
         return -1;
     for (j = j0; j < j1; j++) {

@@ -52,6 +52,8 @@ class Spec:
     qk_hi: float = 8.0
     scale_hi: float = 10.0
     weight_hi: float = 0.01
+    pre_tokens: int = INT64_MAX  # window bounds (INT64_MAX: none)
+    next_tokens: int = INT64_MAX
 
 
 WORKLOADS = {
@@ -134,7 +136,7 @@ def make_inputs(spec: Spec, seed: int) -> dict:
         num_blocks=num_blocks, block_size=bs, max_blocks_per_seq=max_blocks,
         key_block_stride=stride if spec.stride_pad else 0,
         sparse_count=spec.sparse_count, sparse_mode=spec.sparse_mode, cmp_ratio=cmp,
-        pre_tokens=INT64_MAX, next_tokens=INT64_MAX,
+        pre_tokens=spec.pre_tokens, next_tokens=spec.next_tokens,
         query_quant_mode=0, key_quant_mode=0, return_value=1)
     return dict(problem=problem, query=np.ascontiguousarray(query), key=np.ascontiguousarray(key),
                 weights=np.ascontiguousarray(weights), q_scale=np.ascontiguousarray(q_scale),

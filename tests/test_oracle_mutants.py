@@ -46,6 +46,15 @@ MUTANTS = [
     ("fp32 weight ignored", "double w = scale_value(p->weights, r * QLIO_HEADS + g, p->scale_dtype);",
      "double w = p->scale_dtype == 1 ? 1.0 : scale_value(p->weights, r * QLIO_HEADS + g, p->scale_dtype);"),
     ("fp32 values read as 1.0", "    return (double)f;\n}", "    return 1.0;\n}"),
+    # pre_tokens / next_tokens windows
+    ("window checks the last token only",
+     "if (in_window(first, pos, pre_tokens, next_tokens) &&\n            in_window(last,",
+     "if (in_window(last, pos, pre_tokens, next_tokens) &&\n            in_window(last,"),
+    ("next_tokens ignored", "if (t > pos && t - pos > next_tokens)", "if (t > pos && t - pos > next_tokens && 0)"),
+    ("pre_tokens off by one", "pos - t > pre_tokens", "pos - t >= pre_tokens"),
+    ("window start dropped from the indices", "oi[j] = (int32_t)(lo + top[j]);", "oi[j] = (int32_t)top[j];"),
+    ("window scores from entry 0", "sc[j] = score_one(&p, r, b, lo + j, NULL, 0);",
+     "sc[j] = score_one(&p, r, b, j, NULL, 0);"),
 ]
 
 PINS = [
@@ -55,6 +64,10 @@ PINS = [
     vis.test_visible_matches_token_brute_force,
     vis.test_row_visible_layouts,
     vis.test_long_context_edges,
+    vis.test_window_matches_token_brute_force,
+    vis.test_window_defaults_and_special_cases,
+    lambda o: op.test_window_restricts_the_candidates(o, 3, 4, 7, 5),
+    lambda o: op.test_window_restricts_the_candidates(o, 0, 2, 100, 30),
     sco.test_worked_example,
     sco.test_worked_example_fp8_f32,
     sco.test_single_head_special_case_fp32,

@@ -140,3 +140,33 @@ def test_validation_tables(ora):
     assert ora.indexer(inp)[0] == 1                     # 300 entries need 5 blocks of 64
     inp = synth.make_inputs(synth.small(layout=synth.TND, s1=6, aslq=[4, 3]), 1)
     assert ora.indexer(inp)[0] == 1                     # prefix sums must not decrease
+
+
+@pytest.mark.parametrize("mode,cmp,pre,nxt", [(3, 1, 40, 0), (0, 2, 100, 30), (3, 4, 7, 5), (0, 1, 0, 0)])
+def test_window_restricts_the_candidates(ora, mode, cmp, pre, nxt):
+    """With a window, each row's result is the stable top-k of the unwindowed
+    scores restricted to the row's window (entries [lo, hi))."""
+    import math
+    spec = synth.small(batch=2, s1=5, aslk=[700, 260], block_size=32, sparse_count=24, sparse_mode=mode,
+                       cmp_ratio=cmp, pre_tokens=pre, next_tokens=nxt)
+    inp = synth.make_inputs(spec, 31)
+    full = dict(inp, problem=dict(inp["problem"], pre_tokens=synth.INT64_MAX, next_tokens=synth.INT64_MAX))
+    _, _, sc = run(ora, full, scores_cols=800)
+    idx, val, _ = run(ora, inp)
+    p = inp["problem"]
+    lo, hi = ora.row_range(0, 2, 5, mode, cmp, None, inp["aslk"], pre, nxt)
+    k = p["sparse_count"]
+    for r in range(10):
+        cand = list(range(lo[r], hi[r]))
+        # Python's sort: score descending, then index ascending
+        top = sorted(cand, key=lambda j: (-sc[r, j], j))[:k]
+        assert list(idx[r, :len(top)]) == top and np.all(idx[r, len(top):] == -1)
+        assert all(val[r, i] == np.float32(sc[r, j]) for i, j in enumerate(top))
+        assert all(not math.isnan(sc[r, j]) for j in cand)
+
+
+def test_window_bounds_validated(ora):
+    inp = synth.make_inputs(synth.small(pre_tokens=-1), 0)
+    assert ora.indexer(inp)[0] == 1
+    inp = synth.make_inputs(synth.small(next_tokens=-5), 0)
+    assert ora.indexer(inp)[0] == 1
