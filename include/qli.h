@@ -69,6 +69,16 @@ typedef enum qli_layout { QLI_LAYOUT_BSND = 0, QLI_LAYOUT_TND = 1 } qli_layout;
 /* The scalar problem (QLI-README 参数说明 attributes and shapes).  Fields
  * are fixed-width and explicitly padded so that the struct has the same
  * layout from every language. */
+/* pre_tokens / next_tokens: the page lists both as reserved attributes that
+ * bound how many tokens before (after) a query the attention relates to, and
+ * accepts only 2^63-1.  Other values (>= 0; negative ones are QLI_ERR_ARG)
+ * are taken as a token window: query i of a batch with S1 query and Sk key
+ * tokens sits at position pos = Sk - S1 + i (both sparse modes), and sees a
+ * compressed entry only when sparse_mode lets it and every token the entry
+ * covers lies in [pos - pre_tokens, pos + next_tokens].  A row's visible
+ * entries are then consecutive, [lo, hi); its outputs list the top
+ * min(k, hi - lo) of them, padded as usual.  qli_plan / qli_run only: the
+ * bounded entry points return QLI_ERR_UNSUPPORTED for a window. */
 typedef struct qli_problem {
     int32_t batch;              /* B.  TND: number of entries of actual_seq_lengths_query */
     int32_t s1;                 /* BSND: S1 (query tokens per batch); TND: T (total tokens) */
@@ -88,8 +98,8 @@ typedef struct qli_problem {
     int32_t sparse_mode;        /* 0 defaultMask, 3 rightDownCausal (参数说明 sparse_mode) */
     int32_t cmp_ratio;          /* 1,2,4,...,128 (参数说明 cmp_ratio) */
     int32_t reserved1;          /* must be 0 */
-    int64_t pre_tokens;         /* reserved by the page; must be INT64_MAX */
-    int64_t next_tokens;        /* reserved by the page; must be INT64_MAX */
+    int64_t pre_tokens;         /* token window, >= 0; INT64_MAX (the page's default) = none */
+    int64_t next_tokens;        /* token window, >= 0; INT64_MAX (the page's default) = none */
     int32_t query_quant_mode;   /* must be 0 (per-token-head) */
     int32_t key_quant_mode;     /* must be 0 (per-token-head) */
     int32_t return_value;       /* 1: also write sparse_values; 0: sparse_values may be NULL */
@@ -131,8 +141,9 @@ typedef struct qli_plan_info {
     int64_t visible_pairs;   /* sum over rows of visible key entries (scored pairs) */
     int64_t plan_bytes;
     int64_t workspace_bytes;
-    int64_t key_entries;     /* distinct key entries any row sees: sum over batches of the
-                                largest visible count (each is read once per batch) */
+    int64_t key_entries;     /* key entries some row sees: sum over batches of the span from
+                                the smallest window start to the largest visible end (each is
+                                read once per batch) */
     int64_t table_entries;   /* block_table entries those key entries span */
     int64_t active_rows;     /* rows that see at least one key entry */
     int32_t score_items;     /* work items of the scoring stage */
@@ -169,7 +180,8 @@ int qli_plan_info_get(const void *plan_host, qli_plan_info *info);
  *   sparse_values  device float [rows, sparse_count] (out) or NULL when
  *                  return_value == 0.
  *
- * Output contract per row r with n = min(sparse_count, visible(r)):
+ * Output contract per row r with n = min(sparse_count, visible(r)), where
+ * visible(r) counts the row's visible entries (window applied):
  *   sparse_indices[r][0:n] = the indices of the n highest scores, ties at
  *   the threshold broken towards the lower index, listed in ascending index
  *   order; sparse_values[r][i] = the fp32 score of sparse_indices[r][i];
@@ -183,12 +195,12 @@ int qli_run(const qli_problem *p, const void *plan_host, const void *plan_dev,
 
 /*
  * qli_run_debug -- parity instrumentation: runs the same scoring kernels
- * with a dump epilogue for rows [row0, row1) and writes, for entry
- * j < min(visible(r), cols):
+ * with a dump epilogue for rows [row0, row1) and writes, for each visible
+ * entry j < cols of row r (entry index j, window applied):
  *   dots_out   [(row1-row0), 64, cols]: int32 dot products (INT8 path) or
  *              float (FP8 path), exactly as the matrix cores produced them;
  *   scores_out [(row1-row0), cols] float scores.
- * Slots past a row's visible count are left untouched.  It also performs
+ * Slots of entries the row does not see are left untouched.  It also performs
  * the full qli_run (same outputs).
  */
 int qli_run_debug(const qli_problem *p, const void *plan_host,

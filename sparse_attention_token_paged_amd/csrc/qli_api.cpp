@@ -48,8 +48,10 @@ int validate_problem(const qli_problem* p) {
   if (p->sparse_mode != 0 && p->sparse_mode != 3) return QLI_ERR_ARG;
   // 参数说明 cmp_ratio: 1/2/4/8/16/32/64/128.
   if (!is_pow2_upto(p->cmp_ratio, 128)) return QLI_ERR_ARG;
-  // 参数说明 pre_tokens / next_tokens: reserved, only 2^63-1.
-  if (p->pre_tokens != INT64_MAX || p->next_tokens != INT64_MAX) return QLI_ERR_UNSUPPORTED;
+  // 参数说明 pre_tokens / next_tokens: reserved there (only 2^63-1); other
+  // values are taken as a token window around the query (visible_window),
+  // whose bounds are >= 0.
+  if (p->pre_tokens < 0 || p->next_tokens < 0) return QLI_ERR_ARG;
   // 参数说明 query_quant_mode / key_quant_mode: only 0 (per-token-head).
   if (p->query_quant_mode != 0 || p->key_quant_mode != 0) return QLI_ERR_UNSUPPORTED;
   if (p->return_value != 0 && p->return_value != 1) return QLI_ERR_ARG;
@@ -75,7 +77,7 @@ uint64_t problem_fingerprint(const qli_problem& p) {
   uint64_t h = 1469598103934665603ull ^ kFnvPrime;
   const int64_t fields[] = {p.batch, p.s1, p.layout_query, p.qk_dtype, p.scale_dtype,
                             p.num_blocks, p.block_size, p.max_blocks_per_seq,
-                            p.sparse_count, p.sparse_mode, p.cmp_ratio};
+                            p.sparse_count, p.sparse_mode, p.cmp_ratio, p.pre_tokens, p.next_tokens};
   for (int64_t f : fields) h = fnv_mix(h, f);
   return h;
 }
@@ -154,24 +156,35 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
     }
   }
 
+  // Row r sees entries [lo, vis) (visible_window; lo = 0 without a window).
   out.rows.assign(rows, RowInfo{-1, 0, -1, 0, 0});
   int64_t max_s1b = 0, visible = 0, max_vis = 0, key_entries = 0, table_entries = 0, active = 0;
   for (int b = 0; b < p.batch; b++) {
     max_s1b = std::max(max_s1b, qcnt[b]);
-    int64_t batch_max = 0;
+    int64_t batch_lo = INT64_MAX, batch_hi = 0;
     for (int64_t i = 0; i < qcnt[b]; i++) {
-      const int64_t v = visible_entries(p.sparse_mode, p.cmp_ratio, aslk[b], qcnt[b], i);
+      int64_t lo = 0;
+      const int64_t hi = visible_window(p.sparse_mode, p.cmp_ratio, aslk[b], qcnt[b], i, p.pre_tokens,
+                                        p.next_tokens, lo);
+      const int64_t v = hi - lo;
       RowInfo& ri = out.rows[qbeg[b] + i];
       ri.batch = b;
-      ri.vis = (int32_t)v;
+      ri.vis = (int32_t)hi;
+      ri.lo = (int32_t)lo;
       visible += v;
       active += v > 0;
-      batch_max = std::max(batch_max, v);
+      max_vis = std::max(max_vis, v);
+      if (v > 0) {
+        batch_lo = std::min(batch_lo, lo);
+        batch_hi = std::max(batch_hi, hi);
+      }
     }
-    max_vis = std::max(max_vis, batch_max);
-    key_entries += batch_max;
-    table_entries += (batch_max + p.block_size - 1) / p.block_size;
+    if (batch_hi > 0) {  // the entries some row of the batch sees lie in [batch_lo, batch_hi)
+      key_entries += batch_hi - batch_lo;
+      table_entries += (batch_hi - 1) / p.block_size - batch_lo / p.block_size + 1;
+    }
   }
+  const bool windowed = p.pre_tokens != INT64_MAX || p.next_tokens != INT64_MAX;
 
   // Tile shape: decode-like problems (few query tokens per sequence) put
   // 1, 2 or 4 rows in an item so the key chunk is read once for all of
@@ -179,14 +192,23 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   const bool prefill = max_s1b > 4;
   const int rt = prefill ? 8 : (max_s1b <= 1 ? 1 : (max_s1b <= 2 ? 2 : 4));
 
-  struct Group { int32_t row0, nrows, batch, maxv; };
+  // A group's items cover the entries [start, start + maxv) that some row of
+  // it sees (start: the smallest lo rounded down to a 64-entry tile).
+  struct Group { int32_t row0, nrows, batch, maxv, start; };
   std::vector<Group> groups;
   for (int b = 0; b < p.batch; b++) {
     for (int64_t i = 0; i < qcnt[b]; i += rt) {
       const int32_t n = (int32_t)std::min<int64_t>(rt, qcnt[b] - i);
-      int32_t mv = 0;
-      for (int32_t u = 0; u < n; u++) mv = std::max(mv, out.rows[qbeg[b] + i + u].vis);
-      groups.push_back({(int32_t)(qbeg[b] + i), n, b, mv});
+      int32_t lo = INT32_MAX, hi = 0;
+      for (int32_t u = 0; u < n; u++) {
+        const RowInfo& ri = out.rows[qbeg[b] + i + u];
+        if (ri.vis > ri.lo) {
+          lo = std::min(lo, ri.lo);
+          hi = std::max(hi, ri.vis);
+        }
+      }
+      const int32_t start = hi > 0 ? lo / kTileKeys * kTileKeys : 0;
+      groups.push_back({(int32_t)(qbeg[b] + i), n, b, hi - start, start});
     }
   }
   // Rows that belong to no query token only receive padding.
@@ -194,7 +216,7 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
     if (out.rows[r].batch >= 0) { r++; continue; }
     int64_t e = r;
     while (e < rows && e - r < rt && out.rows[e].batch < 0) e++;
-    groups.push_back({(int32_t)r, (int32_t)(e - r), -1, 0});
+    groups.push_back({(int32_t)r, (int32_t)(e - r), -1, 0, 0});
     r = e;
   }
 
@@ -221,8 +243,8 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   for (int64_t r = 0; r < rows; r++) {
     RowInfo& ri = out.rows[r];
     ri.ncand = 0;
-    if (ri.vis > k) {
-      const int64_t n = ri.vis;
+    if (ri.vis - ri.lo > k) {
+      const int64_t n = ri.vis - ri.lo;
       ri.ws_off = ws;
       ri.ncand = (int32_t)n;
       ws += pad4(n);
@@ -232,6 +254,7 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
         se.dst_off = -1;
         se.row = (int32_t)r;
         se.n = ri.ncand;
+        se.base = ri.lo;
         out.select.push_back(se);
         max_cand = std::max<int64_t>(max_cand, n);
       } else {
@@ -246,7 +269,7 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
           se.dst_off = m;  // relative to the row's merge region for now
           se.row = (int32_t)r;
           se.n = (int32_t)sn;
-          se.base = (int32_t)s0;
+          se.base = (int32_t)(ri.lo + s0);
           out.select.push_back(se);
           max_cand = std::max<int64_t>(max_cand, sn);
           m += std::min<int64_t>(k, sn);
@@ -280,24 +303,28 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
     base.batch = g.batch;
     for (int u = 0; u < kMaxItemRows; u++) {
       base.vis[u] = 0;
+      base.lo[u] = 0;
       base.cand_off[u] = -1;
     }
     if (!prefill)
-      for (int u = 0; u < g.nrows; u++) base.vis[u] = out.rows[g.row0 + u].vis;
+      for (int u = 0; u < g.nrows; u++) {
+        base.vis[u] = out.rows[g.row0 + u].vis;
+        base.lo[u] = out.rows[g.row0 + u].lo;
+      }
     if (g.maxv == 0) {
       base.flags = kItemPad;
       out.items.push_back(base);
       continue;
     }
-    for (int32_t k0 = 0; k0 < g.maxv; k0 += chunk) {
+    for (int32_t c0 = 0; c0 < g.maxv; c0 += chunk) {
       Item it = base;
-      it.key0 = k0;
-      it.nkeys = std::min(chunk, g.maxv - k0);
-      it.flags = k0 == 0 ? kItemPad : 0;
+      it.key0 = g.start + c0;
+      it.nkeys = std::min(chunk, g.maxv - c0);
+      it.flags = c0 == 0 ? kItemPad : 0;
       if (!prefill) {
         for (int u = 0; u < g.nrows; u++) {
           const RowInfo& ri = out.rows[g.row0 + u];
-          if (ri.ws_off >= 0) it.cand_off[u] = ri.ws_off + k0;
+          if (ri.ws_off >= 0) it.cand_off[u] = ri.ws_off + it.key0 - ri.lo;
         }
       }
       out.items.push_back(it);
@@ -307,7 +334,8 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   // the same visible maximum, so an item's batch, key range and rows follow
   // from its position, and the kernel can start its block-table and query
   // loads without waiting for the item.  They keep batch-major order.
-  bool regular = !prefill && p.layout_query == QLI_LAYOUT_BSND && p.batch > 0 && (int64_t)groups.size() == p.batch;
+  bool regular = !prefill && !windowed && p.layout_query == QLI_LAYOUT_BSND && p.batch > 0 &&
+                 (int64_t)groups.size() == p.batch;
   for (int b = 0; regular && b < p.batch; b++) {
     const Group& g = groups[b];
     regular = g.batch == b && g.nrows == p.s1 && g.row0 == (int64_t)b * p.s1 && g.maxv == groups[0].maxv &&
@@ -466,6 +494,8 @@ struct Bounded {
 
 int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
   if (max_len < 0) return QLI_ERR_ARG;
+  // Visible ranges computed on the device start at entry 0: no window.
+  if (p.pre_tokens != INT64_MAX || p.next_tokens != INT64_MAX) return QLI_ERR_UNSUPPORTED;
   const bool tnd = p.layout_query == QLI_LAYOUT_TND;
   if (tnd && p.batch > kTndMaxBatch) return QLI_ERR_UNSUPPORTED;
   const int64_t nmax = max_len / p.cmp_ratio;

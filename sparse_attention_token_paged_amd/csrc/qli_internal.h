@@ -12,7 +12,7 @@
 namespace qli {
 
 constexpr uint32_t kPlanMagic = 0x504C4951u;  // "QILP"
-constexpr uint32_t kPlanVersion = 7;
+constexpr uint32_t kPlanVersion = 8;
 constexpr int kHeads = 64;       // query heads (QLI-README 约束说明)
 constexpr int kDim = 128;        // head dim of query and key (约束说明)
 constexpr int kTileKeys = 64;    // keys per MFMA tile step (4 n-tiles of 16)
@@ -45,7 +45,7 @@ struct PlanHeader {
   int32_t max_vis;
   int32_t reserved1;
   int32_t max_cand;          // largest candidate count of a pass-1 selection
-  int64_t key_entries;       // sum over batches of the largest visible count
+  int64_t key_entries;       // sum over batches of the entries some row of the batch sees
   int64_t table_entries;     // block-table entries spanned by those entries
   int64_t active_rows;       // rows with at least one visible entry
   int64_t ws_index_offset;   // the int32 key index of merge candidate e (an element offset of a
@@ -63,12 +63,15 @@ struct PlanHeader {
 };
 static_assert(sizeof(PlanHeader) % 16 == 0, "header keeps the tables aligned");
 
+// Row r sees the compressed entries [lo, vis): vis - lo of them (lo = 0
+// without a pre_tokens window).
 struct RowInfo {
   int32_t batch;   // -1 for rows that belong to no query token
-  int32_t vis;     // visible compressed key entries
-  int64_t ws_off;  // element offset of the row's candidates in the workspace, -1 = direct output
+  int32_t vis;     // end of the visible range
+  int64_t ws_off;  // element offset of the row's candidates in the workspace, -1 = direct output;
+                   // candidate e is entry lo + e
   int32_t ncand;   // scores the row stages for the selection stage (0: direct output)
-  int32_t reserved;
+  int32_t lo;      // start of the visible range
 };
 
 // One selection of the selection stage: the top min(k, n) of n candidates.
@@ -101,6 +104,32 @@ inline int64_t visible_entries(int mode, int cmp, int64_t skb, int64_t s1b, int6
   if (through <= 0) return 0;
   return through / cmp < stored ? through / cmp : stored;
 }
+
+// The same query with pre_tokens / next_tokens windows (QLI-README 参数说明
+// marks both reserved, default 2^63-1; reading for other values: the query
+// sits at token position pos = skb - s1b + i in both modes and sees an entry
+// only when all of its tokens lie in [pos - pre, pos + next]).  Returns the
+// end of the visible range and sets lo to its start; an empty range is
+// [0, 0).  pre, next >= 0.  Entry j's first token j*cmp >= pos - pre holds
+// from j = ceil((pos - pre) / cmp); its last token (j+1)*cmp - 1 <= pos + next
+// holds below floor((pos + next + 1) / cmp), a bound that cuts nothing once
+// next >= s1b (then pos + next + 1 >= skb).
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline int64_t visible_window(int mode, int cmp, int64_t skb, int64_t s1b, int64_t i, int64_t pre, int64_t next,
+                              int64_t& lo) {
+  int64_t hi = visible_entries(mode, cmp, skb, s1b, i);
+  const int64_t pos = skb - s1b + i;
+  lo = pre < pos ? (pos - pre + cmp - 1) / cmp : 0;
+  if (next < s1b) {
+    const int64_t end = pos + next + 1;  // tokens before end are inside the window
+    const int64_t cut = end > 0 ? end / cmp : 0;
+    if (cut < hi) hi = cut;
+  }
+  if (hi <= lo) lo = hi = 0;
+  return hi;
+}
 static_assert(sizeof(SelectEntry) == 32, "select table layout");
 
 struct Item {
@@ -111,11 +140,12 @@ struct Item {
   int32_t nkeys;   // entries in the chunk (0: padding only)
   int32_t flags;   // kItemPad: this item writes the -1 padding of its rows
   int32_t reserved[2];
-  int32_t vis[kMaxItemRows];       // decode items: visible entries of rows row0 + u
-  int64_t cand_off[kMaxItemRows];  // decode items: workspace slot of row u's candidates
-                                   // from this chunk, -1 = direct output
+  int32_t vis[kMaxItemRows];       // decode items: end of the visible range of row row0 + u
+  int64_t cand_off[kMaxItemRows];  // decode items: workspace slot of entry key0 of row u
+                                   // (the row's region starts at its entry lo), -1 = direct output
+  int32_t lo[kMaxItemRows];        // decode items: start of the visible range of row row0 + u
 };
-static_assert(sizeof(Item) == 80, "item layout");
+static_assert(sizeof(Item) == 96, "item layout");
 
 // Bounded TND runs: tables written into the workspace (at byte offset
 // tab_off, int32 elements) by a one-workgroup kernel from the device

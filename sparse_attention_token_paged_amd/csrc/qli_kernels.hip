@@ -273,18 +273,25 @@ void score_kernel(ScoreParams P) {
   } else {
     it = P.items[pos];
   }
-  auto row_vis = [&](int64_t r) __attribute__((always_inline)) {
-    if (!P.aslk) return rinfo[r].vis;
+  // Row r sees entries [lo, hi): from the plan, or [0, visible count) when
+  // bounded (no window there).
+  auto row_range = [&](int64_t r, int& lo) __attribute__((always_inline)) {
+    if (!P.aslk) {
+      lo = rinfo[r].lo;
+      return rinfo[r].vis;
+    }
+    lo = 0;
     return it.batch < 0 ? 0 : (int)visible_entries(P.mode, P.cmp, skb, s1b, r - rstart);
   };
 
-  // Rows that see fewer than k entries: slots vis..k-1 are -1 / -inf.
+  // Rows that see fewer than k entries: slots count..k-1 are -1 / -inf.
   if (it.flags & kItemPad) {
     for (int u = 0; u < it.nrows; u++) {
       const int64_t r = it.row0 + u;
-      const int vis = row_vis(r);
-      if (vis >= k) continue;
-      for (int pos = vis + tid; pos < k; pos += kScoreThreads) {
+      int lo;
+      const int cnt = row_range(r, lo) - lo;
+      if (cnt >= k) continue;
+      for (int pos = cnt + tid; pos < k; pos += kScoreThreads) {
         P.idx_out[r * k + pos] = -1;
         if (P.val_out) P.val_out[r * k + pos] = -INFINITY;
       }
@@ -307,7 +314,7 @@ void score_kernel(ScoreParams P) {
   const int wk = wave % WPR;
   bool rok[RW];
   int64_t rowid[RW];
-  int rvis[RW];
+  int rvis[RW], rlo[RW];  // the row sees entries [rlo, rvis)
   int64_t rws[RW];
   Frag qa[RW][4];
   float wq[RW][16];
@@ -318,12 +325,15 @@ void score_kernel(ScoreParams P) {
     const int64_t r = it.row0 + (rok[rr] ? u : 0);
     rowid[rr] = r;
     if (P.aslk) {
-      const int v = row_vis(r);
+      int lo;
+      const int v = row_range(r, lo);
       rvis[rr] = rok[rr] ? v : 0;
+      rlo[rr] = 0;
       rws[rr] = v > k ? r * P.bstride : -1;
     } else {
       const RowInfo ri = rinfo[r];
       rvis[rr] = rok[rr] ? ri.vis : 0;
+      rlo[rr] = rok[rr] ? ri.lo : 0;
       rws[rr] = ri.ws_off;
     }
     const uint8_t* qrow = P.query + r * (kHeads * kDim);
@@ -449,7 +459,7 @@ void score_kernel(ScoreParams P) {
         if constexpr (DUMP) {
           const int64_t r = rowid[rr];
           const int jd = tb + kk;
-          if (rok[rr] && r >= P.d_row0 && r < P.d_row1 && jd < rvis[rr] && jd < P.d_cols) {
+          if (rok[rr] && r >= P.d_row0 && r < P.d_row1 && jd >= rlo[rr] && jd < rvis[rr] && jd < P.d_cols) {
             const int64_t base = (r - P.d_row0) * kHeads;
 #pragma unroll
             for (int m = 0; m < 4; m++)
@@ -472,12 +482,13 @@ void score_kernel(ScoreParams P) {
       const float score = reduce_scatter4(part[rr][0], part[rr][1], part[rr][2], part[rr][3]) * skv;
       if (!rok[rr]) break;  // uniform: valid rows of a wave are a prefix
       const int64_t r = rowid[rr];
-      const bool live = j < rvis[rr];
+      const int e = j - rlo[rr];  // position in the row's visible range
+      const bool live = e >= 0 && j < rvis[rr];
       if (rws[rr] >= 0) {  // uniform: the row stages every score for a selection
-        if (live) P.ws[rws[rr] + j] = score;
-      } else if (j < kend && j < k) {  // a row's k slots only
-        P.idx_out[r * k + j] = live ? j : -1;
-        if (P.val_out) P.val_out[r * k + j] = live ? score : -INFINITY;
+        if (live) P.ws[rws[rr] + e] = score;
+      } else if (j < kend && e >= 0 && e < k) {  // a row's k slots only
+        P.idx_out[r * k + e] = live ? j : -1;
+        if (P.val_out) P.val_out[r * k + e] = live ? score : -INFINITY;
       }
       if constexpr (DUMP) {
         if (live && r >= P.d_row0 && r < P.d_row1 && j < P.d_cols) P.dscores[(r - P.d_row0) * P.d_cols + j] = score;
@@ -873,7 +884,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   int batch = 0, key0 = 0, nkeys = 0, row0 = 0, nrows = 0, kend = 0, fb = 0;
   bool rok = false;
   int64_t r = 0;
-  int rvis = 0;
+  int rvis = 0, rlo = 0;  // this wave's row sees entries [rlo, rvis)
   int64_t coff = -1;
   Frag qa[4];
   float wq[16];
@@ -881,14 +892,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   float* ov = nullptr;
   bool direct = false;     // the row sees at most k entries: scores go straight to the outputs
 
-  // Rows of an item that see fewer than k entries: slots vis..k-1 are -1 / -inf.
+  // Rows of an item that see fewer than k entries: slots count..k-1 are -1 / -inf.
   auto pad = [&](const Item& itp) __attribute__((always_inline)) {
     if (itp.flags & kItemPad) {
       for (int uu = 0; uu < itp.nrows; uu++) {
         const int64_t rr = itp.row0 + uu;
-        const int vis = itp.vis[uu];
-        if (vis >= k) continue;
-        for (int e = vis + tid; e < k; e += kScoreThreads) {
+        const int cnt = itp.vis[uu] - itp.lo[uu];
+        if (cnt >= k) continue;
+        for (int e = cnt + tid; e < k; e += kScoreThreads) {
           P.idx_out[rr * k + e] = -1;
           if (P.val_out) P.val_out[rr * k + e] = -INFINITY;
         }
@@ -983,9 +994,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     r = row0 + (rok ? u : 0);
     if (bnd) {
       rvis = rok ? (int)visible_entries(P.mode, P.cmp, skb, nrows, u) : 0;
+      rlo = 0;
       coff = rvis > k ? r * P.bstride + key0 : -1;
     } else {
       rvis = rok ? itp->vis[u] : 0;
+      rlo = rok ? itp->lo[u] : 0;
       coff = rok ? itp->cand_off[u] : -1;
     }
     {
@@ -1049,7 +1062,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
       part[n] = acc;
       if constexpr (DUMP) {
         const int j = key0 + st * SC + kk;
-        if (r >= P.d_row0 && r < P.d_row1 && j < rvis && j < P.d_cols) {
+        if (r >= P.d_row0 && r < P.d_row1 && j >= rlo && j < rvis && j < P.d_cols) {
           const int64_t base = (r - P.d_row0) * kHeads;
 #pragma unroll
           for (int m = 0; m < 4; m++)
@@ -1079,10 +1092,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     const int e = st * SC + kk;  // entry within the chunk
     const int j = key0 + e;
     const float score = total * (scale_from_bits<QK>(ring_sk[slot_][kk]) * sk_scale<QK>());
-    if (owner && j < rvis) {
+    if (owner && j >= rlo && j < rvis) {
       if (direct) {
-        oi[j] = j;
-        if (ov) ov[j] = score;
+        oi[j - rlo] = j;
+        if (ov) ov[j - rlo] = score;
       } else {
         P.ws[coff + e] = score;
       }
@@ -1100,7 +1113,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   const int nstages = (nkeys + SC - 1) / SC;
   oi = P.idx_out + r * k;
   ov = P.val_out ? P.val_out + r * k : nullptr;
-  direct = rvis <= k;
+  direct = rvis - rlo <= k;
 
   // Pipeline: stages st+1 and st+2 are in flight while st is computed.
   for (int st = 0; st < nstages; st++) {

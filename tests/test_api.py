@@ -71,7 +71,7 @@ def plan_rc(qli, inp, **over):
     ("block_size", 24, 1), ("block_size", 8, 1), ("block_size", 1040, 1),
     ("sparse_count", 0, 1), ("sparse_count", 2049, 1), ("sparse_mode", 1, 1), ("sparse_mode", 2, 1),
     ("cmp_ratio", 3, 1), ("cmp_ratio", 0, 1), ("cmp_ratio", 256, 1),
-    ("pre_tokens", 1000, 2), ("next_tokens", 0, 2), ("query_quant_mode", 1, 2), ("key_quant_mode", 1, 2),
+    ("pre_tokens", -1, 1), ("next_tokens", -1, 1), ("query_quant_mode", 1, 2), ("key_quant_mode", 1, 2),
     ("return_value", 2, 1), ("reserved0", 1, 1), ("key_block_stride", 100, 1), ("key_block_stride", 64 * 128 + 8, 2),
     ("batch", -1, 1), ("num_blocks", 0, 1), ("max_blocks_per_seq", 0, 1)])
 def test_plan_validation(qli, field, value, code):
@@ -118,12 +118,13 @@ HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("fingerprint", "<u8"), ("
                 ("table_entries", "<i8"), ("active_rows", "<i8"), ("ws_index_offset", "<i8"),
                 ("reg_chunks", "<i4"), ("reg_rows", "<i4"), ("reg_maxv", "<i4"), ("n_select2", "<i4"),
                 ("max_cand2", "<i4"), ("reserved2", "<i4", 3)])
-ROW = np.dtype([("batch", "<i4"), ("vis", "<i4"), ("ws_off", "<i8"), ("ncand", "<i4"), ("reserved", "<i4")])
+ROW = np.dtype([("batch", "<i4"), ("vis", "<i4"), ("ws_off", "<i8"), ("ncand", "<i4"), ("lo", "<i4")])
 SEL = np.dtype([("src_off", "<i8"), ("dst_off", "<i8"), ("row", "<i4"), ("n", "<i4"), ("base", "<i4"),
                 ("indexed", "<i4")])
 SEGMENT = 8192  # candidates per first-pass selection of a long row
 ITEM = np.dtype([("row0", "<i4"), ("nrows", "<i4"), ("batch", "<i4"), ("key0", "<i4"), ("nkeys", "<i4"),
-                 ("flags", "<i4"), ("reserved", "<i4", 2), ("vis", "<i4", 4), ("cand_off", "<i8", 4)])
+                 ("flags", "<i4"), ("reserved", "<i4", 2), ("vis", "<i4", 4), ("cand_off", "<i8", 4),
+                 ("lo", "<i4", 4)])
 
 
 def parse(plan):
@@ -149,6 +150,15 @@ PLAN_CASES = [
     synth.small(batch=8, s1=2, aslk=[70000] * 8, block_size=32, sparse_count=256, sparse_mode=3),
     synth.small(batch=5, s1=3, aslk=[3000] * 5, block_size=64, sparse_count=256, sparse_mode=3),
     synth.small(batch=4, s1=1, aslk=[900] * 4, block_size=16, sparse_count=1000),
+    # pre_tokens / next_tokens windows: decode rows, prefill rows, long staged rows
+    synth.small(batch=3, s1=4, aslk=[5000, 700, 90], block_size=64, sparse_count=256, sparse_mode=3,
+                pre_tokens=1000, next_tokens=0),
+    synth.small(batch=2, s1=40, aslk=[3000, 2500], block_size=32, sparse_count=64, sparse_mode=0,
+                cmp_ratio=2, pre_tokens=300, next_tokens=50),
+    synth.small(batch=2, s1=2, aslk=[70000, 65000], block_size=128, sparse_count=512, sparse_mode=3,
+                pre_tokens=30000, next_tokens=synth.INT64_MAX),
+    synth.small(layout=synth.TND, batch=2, s1=30, aslq=[12, 30], aslk=[500, 4000], block_size=32,
+                sparse_count=128, sparse_mode=3, cmp_ratio=4, pre_tokens=777, next_tokens=0),
 ]
 
 
@@ -162,11 +172,15 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
     assert h["magic"] == 0x504C4951
     nrows = p["batch"] * p["s1"] if p["layout_query"] == 0 else p["s1"]
     assert h["rows"] == nrows
-    vis = ora.row_visible(p["layout_query"], p["batch"], p["s1"], p["sparse_mode"], p["cmp_ratio"],
-                          inp["aslq"], inp["aslk"]) if nrows else np.zeros(0, np.int64)
-    assert np.array_equal(rows["vis"], vis)
+    if nrows:
+        lo, hi = ora.row_range(p["layout_query"], p["batch"], p["s1"], p["sparse_mode"], p["cmp_ratio"],
+                               inp["aslq"], inp["aslk"], p["pre_tokens"], p["next_tokens"])
+    else:
+        lo = hi = np.zeros(0, np.int64)
+    assert np.array_equal(rows["vis"], hi) and np.array_equal(rows["lo"], lo)
+    vis = hi - lo                                   # visible counts
     assert h["visible_pairs"] == vis.sum()
-    cover = [np.zeros(v, np.int32) for v in vis]
+    cover = [np.zeros(v, np.int32) for v in hi]     # entries [0, hi); those below lo must stay uncovered
     padded = np.zeros(nrows, np.int32)
     for it in items:
         for r in range(it["row0"], it["row0"] + it["nrows"]):
@@ -174,11 +188,16 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
                 padded[r] += 1
             if it["nkeys"]:
                 assert rows[r]["batch"] == it["batch"]
-                hi = min(it["key0"] + it["nkeys"], vis[r])
-                if hi > it["key0"]:
-                    cover[r][it["key0"]:hi] += 1
+                e = min(it["key0"] + it["nkeys"], hi[r])
+                if e > it["key0"]:
+                    cover[r][it["key0"]:e] += 1
+                if h["kind"] == 0 and it["nkeys"]:   # decode items carry the rows' ranges
+                    u = r - it["row0"]
+                    assert (it["vis"][u], it["lo"][u]) == (hi[r], lo[r])
+                    if rows[r]["ws_off"] >= 0:
+                        assert it["cand_off"][u] == rows[r]["ws_off"] + it["key0"] - lo[r]
         assert it["nkeys"] <= h["chunk"] and (it["key0"] % 64 == 0)
-    assert all(np.all(c == 1) for c in cover)
+    assert all(np.all(c[lo[r]:] == 1) for r, c in enumerate(cover))
     if h["reg_chunks"] > 0:
         # regular decode plans: an item's batch, keys and rows follow from its position
         rc_, chunk_, s1_, mv_ = int(h["reg_chunks"]), int(h["chunk"]), int(h["reg_rows"]), int(h["reg_maxv"])
@@ -187,7 +206,7 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
             b, c = divmod(i, rc_)
             assert it["batch"] == b and it["key0"] == c * chunk_ and it["nkeys"] == min(chunk_, mv_ - c * chunk_)
             assert it["row0"] == b * s1_ and it["nrows"] == s1_
-            assert max(int(vis[r]) for r in range(b * s1_, (b + 1) * s1_)) == mv_
+            assert max(int(hi[r]) for r in range(b * s1_, (b + 1) * s1_)) == mv_
     assert np.all(padded == 1)
     k = p["sparse_count"]
     selected = [r for r in range(nrows) if vis[r] > k]
@@ -212,7 +231,7 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
             e = p1[i1]
             i1 += 1
             assert (e["row"], e["n"], e["src_off"], e["dst_off"], e["base"], e["indexed"]) == \
-                (r, n, rows[r]["ws_off"], -1, 0, 0)
+                (r, n, rows[r]["ws_off"], -1, lo[r], 0)
             continue
         dst, m = merge_off, 0
         for s0 in range(0, n, SEGMENT):
@@ -220,7 +239,7 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
             i1 += 1
             sn = min(SEGMENT, n - s0)
             assert (e["row"], e["n"], e["src_off"], e["dst_off"], e["base"], e["indexed"]) == \
-                (r, sn, rows[r]["ws_off"] + s0, dst + m, s0, 0)
+                (r, sn, rows[r]["ws_off"] + s0, dst + m, lo[r] + s0, 0)
             m += min(k, sn)
         fin = p2[long_rows.index(r)]
         assert fin["src_off"] == merge_off and fin["n"] == m
@@ -244,10 +263,12 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
         for it in items:
             for u in range(it["nrows"]):
                 r = it["row0"] + u
-                assert it["vis"][u] == vis[r]
+                assert it["vis"][u] == hi[r]
                 if it["nkeys"] and r in slots:
-                    n = max(0, min(int(it["nkeys"]), int(vis[r]) - it["key0"]))
-                    slots[r].append((int(it["cand_off"][u]), n))
+                    a = max(int(it["key0"]), int(lo[r]))
+                    n = min(int(it["key0"] + it["nkeys"]), int(hi[r])) - a
+                    if n > 0:   # cand_off is the slot of entry key0; the row's own slots start at lo
+                        slots[r].append((int(it["cand_off"][u]) + a - int(it["key0"]), n))
                 elif it["nkeys"]:
                     assert it["cand_off"][u] == -1
         for r, c in slots.items():
@@ -260,9 +281,15 @@ def test_plan_covers_each_visible_pair_once(qli, ora, spec):
     info = qli.qli_plan_info_get(plan)
     assert info.rows == nrows and info.visible_pairs == vis.sum() and info.select_rows == len(sel)
     assert info.active_rows == int((vis > 0).sum())
-    bmax = [max([int(vis[r]) for r in range(nrows) if rows[r]["batch"] == b] or [0]) for b in range(p["batch"])]
-    assert info.key_entries == sum(bmax)
-    assert info.table_entries == sum((m + p["block_size"] - 1) // p["block_size"] for m in bmax)
+    # per batch, the entries some row sees: [smallest lo, largest hi) over rows that see any
+    spans = []
+    for b in range(p["batch"]):
+        rs = [r for r in range(nrows) if rows[r]["batch"] == b and vis[r] > 0]
+        if rs:
+            spans.append((min(int(lo[r]) for r in rs), max(int(hi[r]) for r in rs)))
+    bs = p["block_size"]
+    assert info.key_entries == sum(e - a for a, e in spans)
+    assert info.table_entries == sum((e - 1) // bs - a // bs + 1 for a, e in spans)
 
 
 def test_run_rejects_bad_arguments_without_launching(qli):
@@ -515,3 +542,19 @@ def test_sparse_attention_rejects_without_launching(qli):
     assert f(P(batch=0), *args) == qli.QLI_OK                        # no rows: nothing to launch
     rc, ws = qli.qli_sparse_attention_workspace(P(batch=300))        # enough rows: one workgroup per row
     assert rc == qli.QLI_OK and ws == 0
+
+
+def test_bounded_entry_points_reject_windows(qli):
+    """Bounded runs derive visible ranges on the device from entry 0: a
+    pre_tokens / next_tokens window is QLI_ERR_UNSUPPORTED there (qli_plan
+    accepts it)."""
+    spec = synth.small(batch=2, s1=2, aslk=[3000] * 2, block_size=64, sparse_count=256, sparse_mode=3,
+                       pre_tokens=500)
+    p = synth.make_inputs(spec, 1)["problem"]
+    rc, _ = qli.qli_bounded_workspace(qli.Problem.from_dict(p), 3000)
+    assert rc == qli.QLI_ERR_UNSUPPORTED
+    rc, _ = qli.qli_bounded_workspace(qli.Problem.from_dict(dict(p, pre_tokens=synth.INT64_MAX, next_tokens=9)),
+                                      3000)
+    assert rc == qli.QLI_ERR_UNSUPPORTED
+    rc, _ = qli.qli_bounded_workspace(qli.Problem.from_dict(dict(p, pre_tokens=synth.INT64_MAX)), 3000)
+    assert rc == qli.QLI_OK

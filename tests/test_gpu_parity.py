@@ -748,3 +748,57 @@ def test_bounded_without_values():
     torch.cuda.synchronize()
     p_idx, _ = planned(inp, dev, lens)
     assert np.array_equal(idx.cpu().numpy(), p_idx)
+
+
+# --- pre_tokens / next_tokens windows (qli_plan / qli_run) -------------------
+WINDOWED = {
+    # decode items (4 rows): staged rows with a window start, and short direct rows
+    "win_decode_rt4_staged": synth.small(batch=3, s1=4, aslk=[5000, 700, 90], block_size=64, sparse_count=256,
+                                         sparse_mode=3, pre_tokens=1000, next_tokens=0),
+    # one-row items, mode 0 with a window on both sides: direct rows whose range starts past 0
+    "win_decode_rt1_direct": synth.small(batch=4, s1=1, aslk=[3000, 2000, 100, 64], block_size=32,
+                                         sparse_count=300, pre_tokens=200, next_tokens=5),
+    # prefill items, compressed keys, staged rows
+    "win_prefill_mode0_cmp2": synth.small(batch=2, s1=40, aslk=[3000, 2500], block_size=32, sparse_count=64,
+                                          cmp_ratio=2, pre_tokens=300, next_tokens=50),
+    # TND prefill, direct rows with a window start
+    "win_tnd_prefill_direct": synth.small(layout=synth.TND, batch=2, s1=30, aslq=[12, 30], aslk=[500, 4000],
+                                          block_size=32, sparse_count=128, sparse_mode=3, cmp_ratio=4,
+                                          pre_tokens=300, next_tokens=0),
+    # windows longer than one selection segment: segments based at the window start, then a merge
+    "win_long_segments": synth.small(batch=2, s1=2, aslk=[70000, 65000], block_size=128, sparse_count=512,
+                                     sparse_mode=3, pre_tokens=30000),
+    "win_fp8_decode": synth.small(qk=synth.FP8, batch=3, s1=1, aslk=[9000, 4000, 300], block_size=64,
+                                  sparse_count=200, pre_tokens=2500, next_tokens=0),
+    # pre = next = 0: each row sees its own position only
+    "win_zero_width": synth.small(batch=2, s1=5, aslk=[100, 50], block_size=16, sparse_count=8,
+                                  pre_tokens=0, next_tokens=0),
+}
+
+
+def check_windowed(ora, inp, gidx, gval):
+    """Every row against the oracle's scores of its window [lo, hi): positions
+    relative to lo go through the same checks as unwindowed rows."""
+    p = inp["problem"]
+    lo, hi = ora.row_range(p["layout_query"], p["batch"], p["s1"], p["sparse_mode"], p["cmp_ratio"], inp["aslq"],
+                           inp["aslk"], p["pre_tokens"], p["next_tokens"])
+    rc, _, _, osc = ora.indexer(inp, scores_cols=max(1, int(hi.max()) if hi.size else 1))
+    assert rc == 0
+    k = p["sparse_count"]
+    rel = np.where(gidx >= 0, gidx - lo[:, None], -1)
+    check_structure(rel, gval, hi - lo, k)
+    for r in range(rows_of(p)):
+        check_row(r, int(hi[r] - lo[r]), k, rel[r], None if gval is None else gval[r], osc[r, lo[r]:hi[r]],
+                  rtol_of(inp))
+    return lo, hi
+
+
+@pytest.mark.parametrize("name", list(WINDOWED))
+def test_parity_windowed(ora, name):
+    inp = synth.make_inputs(WINDOWED[name], 17)
+    p = inp["problem"]
+    log("case %s: rows=%d k=%d pre=%d next=%d" % (name, rows_of(p), p["sparse_count"], p["pre_tokens"],
+                                                   p["next_tokens"]))
+    gidx, gval, _ = run_gpu(inp)
+    lo, hi = check_windowed(ora, inp, gidx, gval)
+    assert lo.max() > 0   # every case has rows whose window starts past entry 0
