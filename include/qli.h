@@ -103,7 +103,7 @@ typedef struct qli_problem {
     int32_t query_quant_mode;   /* must be 0 (per-token-head) */
     int32_t key_quant_mode;     /* must be 0 (per-token-head) */
     int32_t return_value;       /* 1: also write sparse_values; 0: sparse_values may be NULL */
-    int32_t reserved2;          /* must be 0 */
+    int32_t sort_output;        /* 0: slots in ascending index order; 1: in descending score order */
 } qli_problem;
 
 /* Static description of the string for a status code (never NULL). */
@@ -184,8 +184,12 @@ int qli_plan_info_get(const void *plan_host, qli_plan_info *info);
  * visible(r) counts the row's visible entries (window applied):
  *   sparse_indices[r][0:n] = the indices of the n highest scores, ties at
  *   the threshold broken towards the lower index, listed in ascending index
- *   order; sparse_values[r][i] = the fp32 score of sparse_indices[r][i];
- *   slots n..sparse_count-1 hold -1 and -INFINITY.
+ *   order (sort_output = 0) or in descending fp32 score order, equal scores
+ *   by ascending index (sort_output = 1: the order in which the page's
+ *   Top-k step ranks them); sparse_values[r][i] = the fp32 score of
+ *   sparse_indices[r][i]; slots n..sparse_count-1 hold -1 and -INFINITY.
+ *   With sort_output = 1 and return_value = 0 the workspace also holds the
+ *   rows' values ([rows, sparse_count] fp32, counted in workspace_bytes).
  */
 int qli_run(const qli_problem *p, const void *plan_host, const void *plan_dev,
             const void *query, const void *key, const void *weights,

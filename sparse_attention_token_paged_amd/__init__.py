@@ -41,7 +41,7 @@ class Problem(ctypes.Structure):
         ("key_block_stride", c_i64),
         ("sparse_count", c_i32), ("sparse_mode", c_i32), ("cmp_ratio", c_i32), ("reserved1", c_i32),
         ("pre_tokens", c_i64), ("next_tokens", c_i64),
-        ("query_quant_mode", c_i32), ("key_quant_mode", c_i32), ("return_value", c_i32), ("reserved2", c_i32),
+        ("query_quant_mode", c_i32), ("key_quant_mode", c_i32), ("return_value", c_i32), ("sort_output", c_i32),
     ]
 
     @classmethod

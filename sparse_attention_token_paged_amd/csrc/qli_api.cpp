@@ -55,7 +55,8 @@ int validate_problem(const qli_problem* p) {
   // 参数说明 query_quant_mode / key_quant_mode: only 0 (per-token-head).
   if (p->query_quant_mode != 0 || p->key_quant_mode != 0) return QLI_ERR_UNSUPPORTED;
   if (p->return_value != 0 && p->return_value != 1) return QLI_ERR_ARG;
-  if (p->reserved0 || p->reserved1 || p->reserved2) return QLI_ERR_ARG;
+  if (p->sort_output != 0 && p->sort_output != 1) return QLI_ERR_ARG;
+  if (p->reserved0 || p->reserved1) return QLI_ERR_ARG;
   const int64_t rows = p->layout_query == QLI_LAYOUT_BSND ? (int64_t)p->batch * p->s1 : p->s1;
   if (rows > INT32_MAX / 2) return QLI_ERR_SIZE;
   return QLI_OK;
@@ -77,7 +78,8 @@ uint64_t problem_fingerprint(const qli_problem& p) {
   uint64_t h = 1469598103934665603ull ^ kFnvPrime;
   const int64_t fields[] = {p.batch, p.s1, p.layout_query, p.qk_dtype, p.scale_dtype,
                             p.num_blocks, p.block_size, p.max_blocks_per_seq,
-                            p.sparse_count, p.sparse_mode, p.cmp_ratio, p.pre_tokens, p.next_tokens};
+                            p.sparse_count, p.sparse_mode, p.cmp_ratio, p.pre_tokens, p.next_tokens,
+                            p.return_value, p.sort_output};
   for (int64_t f : fields) h = fnv_mix(h, f);
   return h;
 }
@@ -92,6 +94,17 @@ struct Built {
 };
 
 int64_t align16(int64_t v) { return (v + 15) & ~int64_t(15); }
+
+// Score-ordered output: the reordering reads each row's values, so a caller
+// that takes none gets a [rows, k] fp32 region at the end of the workspace.
+void add_values_region(const qli_problem& p, PlanHeader& h) {
+  h.sort_output = p.sort_output;
+  h.ws_values_offset = -1;
+  if (p.sort_output && !p.return_value && h.rows > 0) {
+    h.ws_values_offset = align16(h.workspace_bytes);
+    h.workspace_bytes = h.ws_values_offset + h.rows * p.sparse_count * 4;
+  }
+}
 
 // Decode chunk for row groups with visible maxima maxv (all alike when
 // equal): the smallest multiple of 128 entries for which the items fit the
@@ -375,6 +388,7 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   h.key_entries = key_entries;
   h.table_entries = table_entries;
   h.active_rows = active;
+  add_values_region(p, h);
   h.off_rows = align16(sizeof(PlanHeader));
   h.off_items = align16(h.off_rows + (int64_t)sizeof(RowInfo) * rows);
   h.off_select = align16(h.off_items + (int64_t)sizeof(Item) * h.n_items);
@@ -492,7 +506,7 @@ struct Bounded {
   int64_t tab_off;  // TND: byte offset of the row and group tables in the workspace
 };
 
-int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
+int bounded_geometry_scores(const qli_problem& p, int64_t max_len, Bounded& g) {
   if (max_len < 0) return QLI_ERR_ARG;
   // Visible ranges computed on the device start at entry 0: no window.
   if (p.pre_tokens != INT64_MAX || p.next_tokens != INT64_MAX) return QLI_ERR_UNSUPPORTED;
@@ -551,6 +565,21 @@ int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
   return QLI_OK;
 }
 
+int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
+  const int rc = bounded_geometry_scores(p, max_len, g);
+  if (rc == QLI_OK) add_values_region(p, g.h);
+  return rc;
+}
+
+// The values the kernels write: the caller's, or the workspace region kept
+// for the score ordering.
+float* values_target(const RunArgs& a, float* sparse_values) {
+  if (a.p->return_value) return sparse_values;
+  if (a.hdr->ws_values_offset >= 0)
+    return reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) + a.hdr->ws_values_offset);
+  return nullptr;
+}
+
 static int run_common(const qli_problem* p, const void* plan_host, const void* plan_dev,
                       const void* query, const void* key, const void* weights,
                       const void* q_scale, const void* k_scale, const int32_t* block_table,
@@ -587,8 +616,10 @@ static int run_common(const qli_problem* p, const void* plan_host, const void* p
   }
   if (stages < 1 || stages > 3) return QLI_ERR_ARG;
   if (a.hdr->rows == 0) return QLI_OK;
+  a.sparse_values = values_target(a, a.sparse_values);
   if ((stages & 1) && launch_score(a, dump) != 0) return QLI_ERR_HIP;
   if ((stages & 2) && a.hdr->n_select > 0 && launch_select(a) != 0) return QLI_ERR_HIP;
+  if ((stages & 2) && a.hdr->sort_output && launch_sort(a) != 0) return QLI_ERR_HIP;
   return QLI_OK;
 }
 
@@ -674,9 +705,11 @@ static int run_bounded_common(const qli_problem* p, int64_t max_seq_len_key, con
   rc = check_run_args(a, static_ws);
   if (rc != QLI_OK) return rc;
   if (static_ws && g.h.workspace_bytes > 0 && scratch_address(&a.workspace) != 0) return QLI_ERR_HIP;
+  a.sparse_values = values_target(a, a.sparse_values);
   if (tnd && launch_tnd_tables(a) != 0) return QLI_ERR_HIP;
   if (launch_score(a, false) != 0) return QLI_ERR_HIP;
   if (g.h.n_select > 0 && launch_select(a) != 0) return QLI_ERR_HIP;
+  if (g.h.sort_output && launch_sort(a) != 0) return QLI_ERR_HIP;
   return QLI_OK;
 }
 

@@ -59,7 +59,11 @@ struct PlanHeader {
   int32_t reg_maxv;
   int32_t n_select2;         // pass-2 selections (after the n_select pass-1 entries)
   int32_t max_cand2;         // largest candidate count of a pass-2 selection
-  int32_t reserved2[3];
+  int32_t sort_output;       // 1: each row's slots are reordered by score after the selection
+  int32_t reserved2[2];
+  int64_t ws_values_offset;  // byte offset of [rows, k] fp32 values kept in the workspace for the
+                             // reordering when the caller takes no values; -1 = none
+  int64_t reserved3;
 };
 static_assert(sizeof(PlanHeader) % 16 == 0, "header keeps the tables aligned");
 
@@ -219,6 +223,7 @@ constexpr size_t kScratchBytes = size_t(32) << 20;
 constexpr int kMaxDevices = 64;
 int scratch_address(void** out);
 int launch_select(const RunArgs& a);
+int launch_sort(const RunArgs& a);
 int launch_tnd_tables(const RunArgs& a);
 
 }  // namespace qli

@@ -1560,6 +1560,73 @@ int launch_select(const RunArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
+// Score-ordered output (sort_output): after the selection, one workgroup per
+// row reorders the row's slots by descending score, equal scores by
+// ascending index, with a bitonic sort of 64-bit keys in LDS.  Key of slot
+// (index j, value v): order_key(v) above ~j, so the descending order is the
+// wanted one and every listed slot's key is nonzero; -1 slots take key 0 and
+// sink to the tail, where they stay -1 / -inf.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kSortThreads = 256;
+constexpr int kSortMax = 2048;  // sparse_count bound
+
+__global__ __launch_bounds__(kSortThreads) void sort_rows_kernel(int32_t* idx, float* val, int k, int np2,
+                                                                 int64_t rows) {
+  __shared__ uint64_t key[kSortMax];
+  const int tid = threadIdx.x;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    int32_t* oi = idx + r * k;
+    float* ov = val + r * k;
+    for (int e = tid; e < np2; e += kSortThreads) {
+      uint64_t kv = 0;
+      if (e < k) {
+        const int32_t j = oi[e];
+        if (j >= 0) kv = ((uint64_t)order_key(ov[e]) << 32) | (uint64_t)(~(uint32_t)j);
+      }
+      key[e] = kv;
+    }
+    __syncthreads();
+    for (int size = 2; size <= np2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int t = tid; t < np2 / 2; t += kSortThreads) {
+          const int i = 2 * t - (t & (stride - 1));  // pair (i, i + stride)
+          const bool desc = (i & size) == 0;         // runs of `size` alternate; the last is descending
+          const uint64_t a = key[i], b = key[i + stride];
+          if ((a < b) == desc) {
+            key[i] = b;
+            key[i + stride] = a;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int e = tid; e < k; e += kSortThreads) {
+      const uint64_t kv = key[e];
+      oi[e] = kv ? (int32_t)(~(uint32_t)kv) : -1;
+      ov[e] = kv ? key_value((uint32_t)(kv >> 32)) : -INFINITY;
+    }
+    __syncthreads();  // the keys are free for the next row
+  }
+}
+
+}  // namespace
+
+int launch_sort(const RunArgs& a) {
+  const PlanHeader* h = a.hdr;
+  const int k = a.p->sparse_count;
+  if (!h->sort_output || k <= 1 || h->rows == 0) return 0;
+  int np2 = 2;
+  while (np2 < k) np2 <<= 1;
+  const int64_t grid = std::min<int64_t>(h->rows, 1 << 20);
+  const hipError_t e = launch(sort_rows_kernel, dim3((unsigned)grid), dim3(kSortThreads),
+                              static_cast<hipStream_t>(a.stream), a.sparse_indices, a.sparse_values, k, np2,
+                              h->rows);
+  return e == hipSuccess ? 0 : (int)e;
+}
+
+// ---------------------------------------------------------------------------
 // Bounded TND runs: the row and group tables (TndTables) from the device
 // actual_seq_lengths_query.  One workgroup: inclusive scans over the
 // batches, 1024 at a time with a carry (a running maximum clamped to [0, T]

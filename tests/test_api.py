@@ -72,7 +72,7 @@ def plan_rc(qli, inp, **over):
     ("sparse_count", 0, 1), ("sparse_count", 2049, 1), ("sparse_mode", 1, 1), ("sparse_mode", 2, 1),
     ("cmp_ratio", 3, 1), ("cmp_ratio", 0, 1), ("cmp_ratio", 256, 1),
     ("pre_tokens", -1, 1), ("next_tokens", -1, 1), ("query_quant_mode", 1, 2), ("key_quant_mode", 1, 2),
-    ("return_value", 2, 1), ("reserved0", 1, 1), ("key_block_stride", 100, 1), ("key_block_stride", 64 * 128 + 8, 2),
+    ("return_value", 2, 1), ("sort_output", 2, 1), ("reserved0", 1, 1), ("key_block_stride", 100, 1), ("key_block_stride", 64 * 128 + 8, 2),
     ("batch", -1, 1), ("num_blocks", 0, 1), ("max_blocks_per_seq", 0, 1)])
 def test_plan_validation(qli, field, value, code):
     inp = base_problem()
@@ -117,7 +117,8 @@ HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("fingerprint", "<u8"), ("
                 ("max_vis", "<i4"), ("reserved1", "<i4"), ("max_cand", "<i4"), ("key_entries", "<i8"),
                 ("table_entries", "<i8"), ("active_rows", "<i8"), ("ws_index_offset", "<i8"),
                 ("reg_chunks", "<i4"), ("reg_rows", "<i4"), ("reg_maxv", "<i4"), ("n_select2", "<i4"),
-                ("max_cand2", "<i4"), ("reserved2", "<i4", 3)])
+                ("max_cand2", "<i4"), ("sort_output", "<i4"), ("reserved2", "<i4", 2),
+                ("ws_values_offset", "<i8"), ("reserved3", "<i8")])
 ROW = np.dtype([("batch", "<i4"), ("vis", "<i4"), ("ws_off", "<i8"), ("ncand", "<i4"), ("lo", "<i4")])
 SEL = np.dtype([("src_off", "<i8"), ("dst_off", "<i8"), ("row", "<i4"), ("n", "<i4"), ("base", "<i4"),
                 ("indexed", "<i4")])
@@ -558,3 +559,24 @@ def test_bounded_entry_points_reject_windows(qli):
     assert rc == qli.QLI_ERR_UNSUPPORTED
     rc, _ = qli.qli_bounded_workspace(qli.Problem.from_dict(dict(p, pre_tokens=synth.INT64_MAX)), 3000)
     assert rc == qli.QLI_OK
+
+
+@pytest.mark.parametrize("return_value", [1, 0])
+def test_sorted_output_workspace(qli, return_value):
+    """sort_output keeps the plan's tables; without returned values the
+    workspace grows by a [rows, k] fp32 region, 16-byte aligned at its end."""
+    inp = base_problem(batch=3, s1=4, aslk=[5000, 700, 90], block_size=64, sparse_count=256, sparse_mode=3)
+    p = dict(inp["problem"], return_value=return_value)
+    rc0, plan0, ws0 = qli.qli_plan(qli.Problem.from_dict(p), inp["aslq"], inp["aslk"])
+    rc1, plan1, ws1 = qli.qli_plan(qli.Problem.from_dict(dict(p, sort_output=1)), inp["aslq"], inp["aslk"])
+    assert rc0 == rc1 == 0
+    h0, h1 = parse(plan0)[0], parse(plan1)[0]
+    assert h0["sort_output"] == 0 and h1["sort_output"] == 1
+    rows, k = 12, 256
+    if return_value:
+        assert ws1 == ws0 and h1["ws_values_offset"] == -1
+    else:
+        assert h1["ws_values_offset"] == (ws0 + 15) // 16 * 16 and ws1 == h1["ws_values_offset"] + 4 * rows * k
+    rc, bws0 = qli.qli_bounded_workspace(qli.Problem.from_dict(p), 5000)
+    rc, bws1 = qli.qli_bounded_workspace(qli.Problem.from_dict(dict(p, sort_output=1)), 5000)
+    assert bws1 == (bws0 if return_value else (bws0 + 15) // 16 * 16 + 4 * rows * k)
