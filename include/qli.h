@@ -246,9 +246,16 @@ int qli_run_stage(const qli_problem *p, const void *plan_host,
  * Scope: qli_run_bounded takes the BSND query layout with every one of the
  * S1 query rows of every batch active (no actual_seq_lengths_query); any S1
  * (decode items for S1 <= 4, 8-row prefill tiles above, as qli_plan
- * chooses).  qli_run_bounded_tnd takes the TND layout with
- * actual_seq_lengths_query on the device too (batch <= 4096).  Every other
+ * chooses).  qli_run_bounded_aslq takes BSND with actual_seq_lengths_query
+ * on the device; qli_run_bounded_tnd the TND layout with
+ * actual_seq_lengths_query on the device too (batch <= 4096).  No
+ * pre_tokens / next_tokens window (QLI_ERR_UNSUPPORTED).  Every other
  * parameter as for qli_plan.
+ *
+ * Decode problems (BSND, S1 <= 4): a first one-workgroup kernel splits every
+ * batch by its own length into items, with the chunk rule of qli_plan, into
+ * the workspace; the scoring kernel reads that item table as it reads a
+ * plan's, so ragged lengths cost what they cost under qli_plan.
  *
  * qli_bounded_workspace -- workspace bytes that qli_run_bounded needs for
  *   these problem sizes and any key lengths in [0, max_seq_len_key] original
@@ -274,6 +281,24 @@ int qli_run_bounded(const qli_problem *p, int64_t max_seq_len_key,
                     const int32_t *block_table, void *workspace,
                     int32_t *sparse_indices, float *sparse_values,
                     void *stream);
+
+/*
+ * qli_run_bounded_aslq -- qli_run_bounded for BSND with
+ *   actual_seq_lengths_query on the device: aslq_dev (device int32[B], 4-byte
+ *   aligned, required) gives the query rows used per batch; each value is
+ *   clamped to [0, S1], so any contents are safe.  Rows past a batch's count
+ *   see no entry and return only padding; the used rows' visibility follows
+ *   from the count as in qli_plan (sparse_mode 3 aligns the last used row
+ *   with the last key).  The workspace is qli_bounded_workspace's.  Returns
+ *   QLI_ERR_UNSUPPORTED for TND; otherwise as qli_run_bounded.
+ */
+int qli_run_bounded_aslq(const qli_problem *p, int64_t max_seq_len_key,
+                         const int32_t *aslq_dev, const int32_t *aslk_dev,
+                         const void *query, const void *key,
+                         const void *weights, const void *q_scale,
+                         const void *k_scale, const int32_t *block_table,
+                         void *workspace, int32_t *sparse_indices,
+                         float *sparse_values, void *stream);
 
 /*
  * qli_run_bounded_tnd -- the same for the TND layout: aslq_dev (device int32[B],

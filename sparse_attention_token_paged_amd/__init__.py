@@ -26,7 +26,7 @@ LAYOUT_BSND, LAYOUT_TND = 0, 1
 INT64_MAX = (1 << 63) - 1
 
 EXPORTED = ("qli_status_string", "qli_plan", "qli_plan_info_get", "qli_run", "qli_run_debug", "qli_run_stage",
-            "qli_bounded_workspace", "qli_run_bounded", "qli_run_bounded_tnd", "qli_run_bounded_static",
+            "qli_bounded_workspace", "qli_run_bounded", "qli_run_bounded_aslq", "qli_run_bounded_tnd", "qli_run_bounded_static",
             "qli_quantize_query", "qli_append_keys", "qli_sparse_attention_workspace", "qli_sparse_attention")
 
 c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
@@ -115,6 +115,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.qli_run_bounded.restype = ctypes.c_int
         lib.qli_run_bounded_tnd.argtypes = [ctypes.POINTER(Problem), c_i64] + [c_p] * 11 + [c_p]
         lib.qli_run_bounded_tnd.restype = ctypes.c_int
+        lib.qli_run_bounded_aslq.argtypes = [ctypes.POINTER(Problem), c_i64] + [c_p] * 11 + [c_p]
+        lib.qli_run_bounded_aslq.restype = ctypes.c_int
         lib.qli_run_bounded_static.argtypes = [ctypes.POINTER(Problem), c_i64] + [c_p] * 9 + [c_p]
         lib.qli_run_bounded_static.restype = ctypes.c_int
         lib.qli_sparse_attention_workspace.argtypes = [ctypes.POINTER(AttnProblem), ctypes.POINTER(c_sz)]
@@ -266,6 +268,14 @@ def quantize_query(x, qk_dtype: int = QK_INT8, stream: Optional[int] = None):
     return q, sc
 
 
+def qli_run_bounded_aslq(problem: Problem, max_seq_len_key: int, aslq_dev, aslk_dev, query, key, weights, q_scale,
+                         k_scale, block_table, workspace, sparse_indices, sparse_values, stream=None) -> int:
+    return load().qli_run_bounded_aslq(ctypes.byref(problem), int(max_seq_len_key), _addr(aslq_dev), _addr(aslk_dev),
+                                       _addr(query), _addr(key), _addr(weights), _addr(q_scale), _addr(k_scale),
+                                       _addr(block_table), _addr(workspace), _addr(sparse_indices),
+                                       _addr(sparse_values), stream)
+
+
 def qli_run_bounded_tnd(problem: Problem, max_seq_len_key: int, aslq_dev, aslk_dev, query, key, weights, q_scale,
                         k_scale, block_table, workspace, sparse_indices, sparse_values, stream=None) -> int:
     return load().qli_run_bounded_tnd(ctypes.byref(problem), int(max_seq_len_key), _addr(aslq_dev), _addr(aslk_dev),
@@ -300,11 +310,15 @@ class BoundedIndexer:
 
     def run(self, aslk_dev, query, key, weights, q_scale, k_scale, block_table, out_idx, out_val,
             stream: Optional[int] = None, aslq_dev=None):
-        """aslq_dev: device actual_seq_lengths_query (TND layout only)."""
+        """aslq_dev: device actual_seq_lengths_query (TND: required prefix sums;
+        BSND: optional per-batch query counts)."""
         st = current_stream() if stream is None else stream
         if self.problem.layout_query == LAYOUT_TND:
             rc = qli_run_bounded_tnd(self.problem, self.max_seq_len_key, aslq_dev, aslk_dev, query, key, weights,
                                      q_scale, k_scale, block_table, self.workspace, out_idx, out_val, st)
+        elif aslq_dev is not None:
+            rc = qli_run_bounded_aslq(self.problem, self.max_seq_len_key, aslq_dev, aslk_dev, query, key, weights,
+                                      q_scale, k_scale, block_table, self.workspace, out_idx, out_val, st)
         else:
             rc = qli_run_bounded(self.problem, self.max_seq_len_key, aslk_dev, query, key, weights, q_scale,
                                  k_scale, block_table, self.workspace, out_idx, out_val, st)

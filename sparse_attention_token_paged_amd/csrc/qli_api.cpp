@@ -504,6 +504,7 @@ struct Bounded {
   int64_t stride, mstride, merge_base;
   int32_t nseg;
   int64_t tab_off;  // TND: byte offset of the row and group tables in the workspace
+  int64_t items_off, count_off;  // decode: the device-built item table and its count (-1: none)
 };
 
 int bounded_geometry_scores(const qli_problem& p, int64_t max_len, Bounded& g) {
@@ -567,8 +568,22 @@ int bounded_geometry_scores(const qli_problem& p, int64_t max_len, Bounded& g) {
 
 int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
   const int rc = bounded_geometry_scores(p, max_len, g);
-  if (rc == QLI_OK) add_values_region(p, g.h);
-  return rc;
+  if (rc != QLI_OK) return rc;
+  g.items_off = -1;
+  PlanHeader& h = g.h;
+  if (h.kind == kKindDecode && h.rows > 0) {
+    // decode: items built on the device from the lengths (decode_items_kernel),
+    // after the scores; h.n_items bounds their number for the launch
+    const int64_t cap = device_items_capacity(p.batch, max_len / p.cmp_ratio);
+    if (cap > INT32_MAX) return QLI_ERR_SIZE;
+    g.items_off = align16(h.workspace_bytes);
+    g.count_off = g.items_off + (int64_t)sizeof(Item) * cap;
+    h.workspace_bytes = g.count_off + 16;
+    h.n_items = (int32_t)cap;
+    h.reg_chunks = 0;
+  }
+  add_values_region(p, h);
+  return QLI_OK;
 }
 
 // The values the kernels write: the caller's, or the workspace region kept
@@ -675,6 +690,7 @@ static int run_bounded_common(const qli_problem* p, int64_t max_seq_len_key, con
   if (!aslk_dev || ((uintptr_t)aslk_dev % 4) != 0) return QLI_ERR_ARG;
   const bool tnd = p->layout_query == QLI_LAYOUT_TND;
   if (tnd && (!aslq_dev || ((uintptr_t)aslq_dev % 4) != 0)) return QLI_ERR_ARG;
+  if (aslq_dev && ((uintptr_t)aslq_dev % 4) != 0) return QLI_ERR_ARG;
   RunArgs a;
   a.p = p;
   a.plan_dev = nullptr;
@@ -701,12 +717,17 @@ static int run_bounded_common(const qli_problem* p, int64_t max_seq_len_key, con
   if (tnd) {
     a.aslq = aslq_dev;
     a.tab_off = g.tab_off;
+  } else {
+    a.aslq_bsnd = aslq_dev;  // null: every row of every batch is used
   }
+  a.items_off = g.items_off;
+  a.count_off = g.count_off;
   rc = check_run_args(a, static_ws);
   if (rc != QLI_OK) return rc;
   if (static_ws && g.h.workspace_bytes > 0 && scratch_address(&a.workspace) != 0) return QLI_ERR_HIP;
   a.sparse_values = values_target(a, a.sparse_values);
   if (tnd && launch_tnd_tables(a) != 0) return QLI_ERR_HIP;
+  if (launch_decode_items(a) != 0) return QLI_ERR_HIP;
   if (launch_score(a, false) != 0) return QLI_ERR_HIP;
   if (g.h.n_select > 0 && launch_select(a) != 0) return QLI_ERR_HIP;
   if (g.h.sort_output && launch_sort(a) != 0) return QLI_ERR_HIP;
@@ -721,6 +742,21 @@ QLI_EXPORT int qli_run_bounded(const qli_problem* p, int64_t max_seq_len_key, co
   try {
     if (p && p->layout_query == QLI_LAYOUT_TND) return QLI_ERR_UNSUPPORTED;  // needs the query lengths
     return run_bounded_common(p, max_seq_len_key, nullptr, aslk_dev, query, key, weights, q_scale, k_scale,
+                              block_table, workspace, sparse_indices, sparse_values, stream);
+  } catch (...) {
+    return QLI_ERR_ARG;
+  }
+}
+
+QLI_EXPORT int qli_run_bounded_aslq(const qli_problem* p, int64_t max_seq_len_key, const int32_t* aslq_dev,
+                                    const int32_t* aslk_dev, const void* query, const void* key,
+                                    const void* weights, const void* q_scale, const void* k_scale,
+                                    const int32_t* block_table, void* workspace, int32_t* sparse_indices,
+                                    float* sparse_values, void* stream) {
+  try {
+    if (p && p->layout_query != QLI_LAYOUT_BSND) return QLI_ERR_UNSUPPORTED;
+    if (!aslq_dev) return QLI_ERR_ARG;
+    return run_bounded_common(p, max_seq_len_key, aslq_dev, aslk_dev, query, key, weights, q_scale, k_scale,
                               block_table, workspace, sparse_indices, sparse_values, stream);
   } catch (...) {
     return QLI_ERR_ARG;

@@ -4,6 +4,7 @@
 // score-item table and the list of rows that need a selection.  The host
 // reads the header for launch geometry; the kernels read the device copy.
 #pragma once
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 
@@ -102,11 +103,12 @@ constexpr int kSelSegment = 8192;  // candidates per first-pass selection of a l
 __host__ __device__
 #endif
 inline int64_t visible_entries(int mode, int cmp, int64_t skb, int64_t s1b, int64_t i) {
-  const int64_t stored = skb / cmp;
+  const int sh = __builtin_ctz((unsigned)cmp);  // cmp is a power of two: x / cmp == x >> sh for x >= 0
+  const int64_t stored = skb >> sh;             // skb >= 0
   if (mode == 0) return stored;
   const int64_t through = skb - s1b + i + 1;  // tokens at or before the query
   if (through <= 0) return 0;
-  return through / cmp < stored ? through / cmp : stored;
+  return (through >> sh) < stored ? (through >> sh) : stored;
 }
 
 // The same query with pre_tokens / next_tokens windows (QLI-README 参数说明
@@ -200,10 +202,12 @@ struct RunArgs {
   void* dots_out;
   float* scores_out;
   void* stream;
-  // Bounded decode (no plan on the device; aslk != nullptr): the kernels read
-  // the key lengths, clamp them to max_len tokens and derive each item's rows
-  // and each selection from them.  Row r's scores sit at element r * stride,
-  // its merge candidates at merge_base + r * mstride; nseg segments per row.
+  // Bounded runs (no host plan; aslk != nullptr): the kernels read the key
+  // lengths and clamp them to max_len tokens; decode items come from the
+  // table decode_items_kernel builds, prefill items and each selection are
+  // derived from the lengths directly.  Row r's scores sit at element
+  // r * stride, its merge candidates at merge_base + r * mstride; nseg
+  // segments per row.
   const int32_t* aslk = nullptr;
   int64_t max_len = 0;
   int64_t stride = 0, mstride = 0, merge_base = 0;
@@ -212,7 +216,23 @@ struct RunArgs {
   // the tables (TndTables) in the workspace.
   const int32_t* aslq = nullptr;
   int64_t tab_off = 0;
+  // Bounded BSND runs with actual_seq_lengths_query on the device (rows past a
+  // batch's count see nothing), else null.
+  const int32_t* aslq_bsnd = nullptr;
+  // Bounded decode: byte offsets in the workspace of the item table the device
+  // planner builds (decode_items_kernel) and of its item count; -1 = none.
+  int64_t items_off = -1, count_off = 0;
 };
+
+// Bounded decode's device-built item table: one workgroup picks the chunk as
+// qli_plan does (the smallest multiple of 128 entries whose items fit the
+// decode slots; for equal batches the one that lowers the busiest CU's keys)
+// and writes max(1, ceil(visible maximum / chunk)) items per batch.  Upper
+// bound on their number, for the workspace.
+inline int64_t device_items_capacity(int64_t batch, int64_t nmax) {
+  const int64_t most = batch * std::max<int64_t>(1, (nmax + kMaxChunk - 1) / kMaxChunk);
+  return std::max<int64_t>(kDecodeSlots + batch, most);
+}
 int launch_score(const RunArgs& a, bool dump);
 
 // The allocation-free bounded runs' workspace: kScratchBytes of device memory
@@ -224,6 +244,7 @@ constexpr int kMaxDevices = 64;
 int scratch_address(void** out);
 int launch_select(const RunArgs& a);
 int launch_sort(const RunArgs& a);
+int launch_decode_items(const RunArgs& a);
 int launch_tnd_tables(const RunArgs& a);
 
 }  // namespace qli

@@ -54,6 +54,7 @@ constexpr int kScoreThreads = 256;
 struct ScoreParams {
   const Item* items;      // the plan's item table
   int32_t n_items;
+  const int32_t* n_items_dev;  // bounded decode: the item count the device planner wrote (else null)
   int32_t chunk;          // keys per item
   int32_t reg_chunks, reg_rows, reg_maxv;  // regular decode plans (0: not regular)
   const RowInfo* rinfo;   // the plan's row table
@@ -70,7 +71,8 @@ struct ScoreParams {
   const int32_t* group_start;
   const int32_t* group_batch;
   int32_t nbatch, trows;       //   batches, rows T
-  const int32_t* aslk;  // bounded decode: key lengths on the device (else null)
+  const int32_t* aslk;  // bounded prefill-shaped runs: key lengths on the device (else null)
+  const int32_t* aslq_bsnd;  // bounded BSND: per-batch query counts (else null: all S1 rows used)
   int64_t max_len;      //   clamp for them (original tokens)
   int64_t bstride;      //   workspace elements per row
   int32_t mode, cmp;    //   sparse_mode, cmp_ratio
@@ -233,7 +235,8 @@ void score_kernel(ScoreParams P) {
   // from its tables.
   Item it;
   int64_t skb = 0;
-  int rstart = 0, s1b = 0;  // bounded: the item's batch starts at row rstart and has s1b rows
+  int rstart = 0, s1b = 0;  // bounded: the item's batch starts at row rstart and has s1b rows,
+  int s1q = 0;              //   the first s1q of them used (BSND query counts)
   if (P.aslk) {
     int b, g, c;
     if (P.rows_end) {
@@ -260,13 +263,14 @@ void score_kernel(ScoreParams P) {
       rstart = b * P.reg_rows;
       s1b = P.reg_rows;
     }
+    s1q = P.aslq_bsnd && b >= 0 ? min(max(P.aslq_bsnd[b], 0), s1b) : s1b;
     skb = b >= 0 ? min<int64_t>(max(P.aslk[b], 0), P.max_len) : 0;
     it.batch = b;
     it.row0 = rstart + 8 * g;
     it.nrows = max(0, min(8, s1b - 8 * g));
     int maxv = 0;
-    for (int u = 0; u < it.nrows && b >= 0; u++)
-      maxv = max(maxv, (int)visible_entries(P.mode, P.cmp, skb, s1b, 8 * g + u));
+    for (int u = 0; u < it.nrows && b >= 0 && 8 * g + u < s1q; u++)
+      maxv = max(maxv, (int)visible_entries(P.mode, P.cmp, skb, s1q, 8 * g + u));
     it.key0 = c * P.chunk;
     it.nkeys = min(P.chunk, maxv - it.key0);
     it.flags = c == 0 ? kItemPad : 0;
@@ -281,7 +285,7 @@ void score_kernel(ScoreParams P) {
       return rinfo[r].vis;
     }
     lo = 0;
-    return it.batch < 0 ? 0 : (int)visible_entries(P.mode, P.cmp, skb, s1b, r - rstart);
+    return it.batch < 0 || r - rstart >= s1q ? 0 : (int)visible_entries(P.mode, P.cmp, skb, s1q, r - rstart);
   };
 
   // Rows that see fewer than k entries: slots count..k-1 are -1 / -inf.
@@ -907,21 +911,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     }
   };
 
-  // Bounded decode: the rows of the current batch (key length skb) that see
-  // fewer than k entries get -1 / -inf in slots vis..k-1.
-  const bool bnd = P.aslk != nullptr;
-  int64_t skb = 0;
-  auto pad_bounded = [&]() __attribute__((always_inline)) {
-    for (int uu = 0; uu < nrows; uu++) {
-      const int64_t rr = row0 + uu;
-      const int vis = (int)visible_entries(P.mode, P.cmp, skb, nrows, uu);
-      for (int e = vis + tid; e < k; e += kScoreThreads) {
-        P.idx_out[rr * k + e] = -1;
-        if (P.val_out) P.val_out[rr * k + e] = -INFINITY;
-      }
-    }
-  };
-
   // Stage loader: wave w's load i fills stage bytes [(4i + w) * 1024, +1024),
   // lane l the 16 bytes at l*16: entry kk = 8(4i + w) + l/8, physical chunk
   // l%8 holding logical chunk (l%8) ^ ((kk>>1)&7) (conflict-free MFMA reads).
@@ -957,20 +946,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   // this wave's query fragments and w' = W * ScaleQ, and the loads of its
   // stages 0 and 1.  False for an item without keys (padding only).
   auto begin = [&](int pos) __attribute__((always_inline)) {
-    const Item* itp = P.items + pos;  // no item table in bounded decode
+    const Item* itp = P.items + pos;  // a plan's table or the one the bounded run built on the device
     if (reg) {
       batch = pos / P.reg_chunks;
       key0 = (pos - batch * P.reg_chunks) * P.chunk;
       nkeys = min(P.chunk, P.reg_maxv - key0);
       row0 = batch * P.reg_rows;
       nrows = P.reg_rows;
-      if (bnd) {
-        // This batch's key length, clamped to the bound; its last row sees the most entries.
-        skb = min<int64_t>(max(P.aslk[batch], 0), P.max_len);
-        if (key0 == 0) pad_bounded();
-        nkeys = min(P.chunk, (int)visible_entries(P.mode, P.cmp, skb, nrows, nrows - 1) - key0);
-        if (nkeys <= 0) return false;  // uniform across the workgroup
-      }
     } else {
       pad(*itp);
       batch = itp->batch;
@@ -992,15 +974,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     const int bt1 = tid + kScoreThreads < nblk ? bt[tid + kScoreThreads] : 0;
     rok = u < nrows;
     r = row0 + (rok ? u : 0);
-    if (bnd) {
-      rvis = rok ? (int)visible_entries(P.mode, P.cmp, skb, nrows, u) : 0;
-      rlo = 0;
-      coff = rvis > k ? r * P.bstride + key0 : -1;
-    } else {
-      rvis = rok ? itp->vis[u] : 0;
-      rlo = rok ? itp->lo[u] : 0;
-      coff = rok ? itp->cand_off[u] : -1;
-    }
+    rvis = rok ? itp->vis[u] : 0;
+    rlo = rok ? itp->lo[u] : 0;
+    coff = rok ? itp->cand_off[u] : -1;
     {
       const uint8_t* qrow = P.query + r * (kHeads * kDim);
   #pragma unroll
@@ -1106,9 +1082,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   };
 
 
+  const int n_items = P.n_items_dev ? *P.n_items_dev : P.n_items;
   for (int round = 0;; round++) {
   const int pos = pos_of(round);
-  if (pos >= P.n_items) break;  // uniform; positions grow with the round
+  if (pos >= n_items) break;  // uniform; positions grow with the round
   if (!begin(pos)) continue;
   const int nstages = (nkeys + SC - 1) / SC;
   oi = P.idx_out + r * k;
@@ -1141,7 +1118,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     lds_barrier();  // the slot is free for stage st + 3
   }
 
-  if (reg && !bnd) pad(P.items[pos]);
+  if (reg) pad(P.items[pos]);
   }  // rounds (the item's last barrier leaves the LDS free for the next one)
 }
 
@@ -1168,6 +1145,7 @@ struct SelectParams {
   int32_t s1, mode, cmp, nseg, pass;
   const int32_t* rows_end;   // bounded TND: the tables (TndTables), else null
   const int32_t* row_batch;
+  const int32_t* aslq_bsnd;  // bounded BSND: per-batch query counts, else null (all S1 rows)
 };
 
 // The selection of this workgroup in bounded decode, from the row's key
@@ -1191,6 +1169,10 @@ __device__ __forceinline__ bool bounded_entry(const SelectParams& S, SelectEntry
     b = r / S.s1;
     s1b = S.s1;
     i = r - b * S.s1;
+    if (S.aslq_bsnd) {  // rows past the batch's query count see nothing
+      s1b = min(max(S.aslq_bsnd[b], 0), S.s1);
+      if (i >= s1b) return false;
+    }
   }
   const int64_t skb = min<int64_t>(max(S.aslk[b], 0), S.max_len);
   const int vis = (int)visible_entries(S.mode, S.cmp, skb, s1b, i);
@@ -1463,6 +1445,7 @@ int launch_score(const RunArgs& a, bool dump) {
     P.rinfo = reinterpret_cast<const RowInfo*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_rows);
   }
   P.aslk = a.aslk;  // bounded decode (the header then describes the bound)
+  P.aslq_bsnd = a.aslq_bsnd;
   if (a.aslq) {
     const TndTables t = tnd_tables(a.p->batch, a.p->s1);
     const int32_t* tab = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(a.workspace) + a.tab_off);
@@ -1477,6 +1460,11 @@ int launch_score(const RunArgs& a, bool dump) {
   P.mode = a.p->sparse_mode;
   P.cmp = a.p->cmp_ratio;
   P.n_items = h->n_items;
+  if (a.items_off >= 0) {  // bounded decode with a device-built item table: it reads like a plan's
+    P.items = reinterpret_cast<const Item*>(static_cast<const uint8_t*>(a.workspace) + a.items_off);
+    P.n_items_dev = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(a.workspace) + a.count_off);
+    P.aslk = nullptr;
+  }
   P.chunk = h->chunk;
   P.reg_chunks = h->reg_chunks;
   P.reg_rows = h->reg_rows;
@@ -1525,6 +1513,7 @@ int launch_select(const RunArgs& a) {
     S.rows_end = tab + t.rows_end;
     S.row_batch = tab + t.row_batch;
   }
+  S.aslq_bsnd = a.aslq_bsnd;
   S.max_len = a.max_len;
   S.stride = a.stride;
   S.mstride = a.mstride;
@@ -1623,6 +1612,165 @@ int launch_sort(const RunArgs& a) {
   const hipError_t e = launch(sort_rows_kernel, dim3((unsigned)grid), dim3(kSortThreads),
                               static_cast<hipStream_t>(a.stream), a.sparse_indices, a.sparse_values, k, np2,
                               h->rows);
+  return e == hipSuccess ? 0 : (int)e;
+}
+
+// ---------------------------------------------------------------------------
+// Bounded decode: the item table from the device key lengths (and, for BSND
+// with actual_seq_lengths_query, the query counts), so that a bounded run
+// splits each batch by its own length as qli_plan would.  One workgroup:
+//   1. the visible maximum m_b of each batch (its last used query row);
+//      for every candidate chunk c = 128, 256, .., kMaxChunk the item count
+//      sum ceil(m_b / c), one wave per two candidates (lanes stride the
+//      batches, then a wave reduction);
+//   2. the chunk: the smallest c whose items fit the decode slots (else
+//      kMaxChunk); when every batch has the same m_b, the c >= it that
+//      lowers ceil(items / CUs) * c, as for equal groups on the host;
+//   3. max(1, ceil(m_b / c)) items per batch at an exclusive prefix sum over
+//      the batches (1024 at a time with a carry), written as plan items:
+//      rows b*S1 .. +S1, key range, per-row visible ends (0 past the query
+//      count) and staged-score offsets r * bstride + key0 (rows seeing more
+//      than k entries), the first item of a batch writing its padding.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kItemsThreads = 1024;
+constexpr int kChunkSteps = kMaxChunk / 128;
+
+struct DecodeItemsParams {
+  const int32_t* aslk;
+  const int32_t* aslq;  // BSND query counts or null (every row used)
+  int32_t batch, s1, mode, cmp, k;
+  int64_t max_len, bstride;
+  Item* items;
+  int32_t* n_items;
+};
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__global__ __launch_bounds__(kItemsThreads) void decode_items_kernel(DecodeItemsParams D) {
+  constexpr int NW = kItemsThreads / 64;
+  static_assert(kChunkSteps == 2 * NW, "two candidate chunks per wave");
+  __shared__ int cnt[kChunkSteps];
+  __shared__ int m_lo, m_hi, total_s;
+  __shared__ int scan_tmp[NW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // batch b: used query rows s1b, clamped key length skb, visible maximum
+  auto batch_info = [&](int b, int& s1b, int64_t& skb) {
+    skb = min<int64_t>(max(D.aslk[b], 0), D.max_len);
+    s1b = D.aslq ? min(max(D.aslq[b], 0), D.s1) : D.s1;
+    return s1b > 0 ? (int)visible_entries(D.mode, D.cmp, skb, s1b, s1b - 1) : 0;
+  };
+  // 1. wave w sums the items of candidate chunks 128 (w + 1) and 128 (w + NW + 1)
+  //    over every batch (lanes stride the batches); wave 0 also takes the
+  //    smallest and largest visible maximum
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const int i = wave + NW * h, c = 128 * (i + 1);
+    int sum = 0, lo = INT32_MAX, hi = -1;
+    for (int b = lane; b < D.batch; b += 64) {
+      int s1b;
+      int64_t skb;
+      const int m = batch_info(b, s1b, skb);
+      sum += (m + c - 1) / c;
+      lo = min(lo, m);
+      hi = max(hi, m);
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) cnt[i] = sum;
+    if (h == 0 && wave == 0) {
+      lo = wave_min(lo);
+      hi = wave_max(hi);
+      if (lane == 0) {
+        m_lo = lo;
+        m_hi = hi;
+      }
+    }
+  }
+  __syncthreads();
+  // 2. the chunk (every thread reads the same counters)
+  int best = kChunkSteps - 1;
+  for (int i = 0; i < kChunkSteps; i++)
+    if (cnt[i] <= kDecodeSlots) {
+      best = i;
+      break;
+    }
+  if (m_hi >= 0 && m_lo == m_hi) {
+    auto busiest = [&](int i) { return (int64_t)((cnt[i] + kCUs - 1) / kCUs) * (128 * (i + 1)); };
+    for (int i = best + 1; i < kChunkSteps; i++)
+      if (busiest(i) < busiest(best)) best = i;
+  }
+  const int c = 128 * (best + 1);
+  // 3. the items, batch b's at the exclusive prefix sum of the batches before it
+  int carry = 0;
+  for (int b0 = 0; b0 < D.batch; b0 += kItemsThreads) {  // uniform
+    const int b = b0 + tid;
+    int s1b = 0, m = 0, n = 0;
+    int64_t skb = 0;
+    if (b < D.batch) {
+      m = batch_info(b, s1b, skb);
+      n = max(1, (m + c - 1) / c);
+    }
+    const int first = carry + block_exclusive_scan<kItemsThreads>(n, scan_tmp);
+    if (tid == kItemsThreads - 1) total_s = first + n;
+    Item it;
+    it.row0 = b * D.s1;
+    it.nrows = D.s1;
+    it.batch = b;
+    it.reserved[0] = it.reserved[1] = 0;
+#pragma unroll
+    for (int u = 0; u < kMaxItemRows; u++) {
+      it.vis[u] = u < s1b ? (int)visible_entries(D.mode, D.cmp, skb, s1b, u) : 0;
+      it.lo[u] = 0;
+    }
+    for (int i = 0; i < n; i++) {
+      it.key0 = i * c;
+      it.nkeys = max(0, min(c, m - i * c));
+      it.flags = i == 0 ? kItemPad : 0;
+#pragma unroll
+      for (int u = 0; u < kMaxItemRows; u++)
+        it.cand_off[u] = it.vis[u] > D.k ? (int64_t)(b * D.s1 + u) * D.bstride + it.key0 : -1;
+      D.items[first + i] = it;
+    }
+    __syncthreads();  // total_s written
+    carry = total_s;
+    __syncthreads();  // read before the next chunk of batches overwrites it
+  }
+  if (tid == 0) *D.n_items = carry;
+}
+
+}  // namespace
+
+int launch_decode_items(const RunArgs& a) {
+  if (a.items_off < 0) return 0;
+  DecodeItemsParams D{};
+  D.aslk = a.aslk;
+  D.aslq = a.aslq_bsnd;
+  D.batch = a.p->batch;
+  D.s1 = a.p->s1;
+  D.mode = a.p->sparse_mode;
+  D.cmp = a.p->cmp_ratio;
+  D.k = a.p->sparse_count;
+  D.max_len = a.max_len;
+  D.bstride = a.stride;
+  D.items = reinterpret_cast<Item*>(static_cast<uint8_t*>(a.workspace) + a.items_off);
+  D.n_items = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + a.count_off);
+  const hipError_t e =
+      launch(decode_items_kernel, dim3(1), dim3(kItemsThreads), static_cast<hipStream_t>(a.stream), D);
   return e == hipSuccess ? 0 : (int)e;
 }
 

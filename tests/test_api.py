@@ -336,10 +336,28 @@ def test_empty_problem_runs_without_device(qli):
 
 
 # --- bounded decode (no host plan) --------------------------------------------
+ITEM_BYTES = 96
+DECODE_SLOTS = 768   # decode workgroups resident at once (3 per CU x 256 CUs)
+
+
 def bounded_workspace_expected(p, max_len):
-    """Workspace of bounded decode, from its layout: rows that may see more than
-    k entries keep every score (16-byte aligned row stride); rows longer than one
-    selection segment also keep each segment's k winners for the merge, with
+    """Bounded BSND: the scores' layout below, then for decode problems (S1 <= 4)
+    the item table the device builds (16-byte aligned; room for every item any
+    lengths can give: max(slots + B, B * ceil(entries / 4096)) items of 96
+    bytes) and its 16-byte count."""
+    base = bounded_scores_expected(p, max_len)
+    rows, b = p["batch"] * p["s1"], p["batch"]
+    if rows == 0 or p["s1"] > 4:
+        return base
+    nmax = max_len // p["cmp_ratio"]
+    cap = max(DECODE_SLOTS + b, b * max(1, -(-nmax // 4096)))
+    return (base + 15) // 16 * 16 + ITEM_BYTES * cap + 16
+
+
+def bounded_scores_expected(p, max_len):
+    """Workspace of the bounded scores, from their layout: rows that may see more
+    than k entries keep every score (16-byte aligned row stride); rows longer than
+    one selection segment also keep each segment's k winners for the merge, with
     their key indices in an int32 region after every score (merge regions only)."""
     rows, k = p["batch"] * p["s1"], p["sparse_count"]
     nmax = max_len // p["cmp_ratio"]
@@ -357,7 +375,7 @@ def bounded_tnd_workspace_expected(p, max_len):
     tables: rows_end[B], group_start[B + 1], group_batch[T // 8 + B + 2] (each
     padded to 4 elements) and row_batch[T], int32."""
     b, t = p["batch"], p["s1"]
-    base = bounded_workspace_expected(dict(p, batch=1, s1=t), max_len)
+    base = bounded_scores_expected(dict(p, batch=1, s1=t), max_len)
     up4 = lambda n: (n + 3) // 4 * 4
     return (base + 15) // 16 * 16 + 4 * (up4(b) + up4(b + 1) + up4(t // 8 + b + 2) + t)
 

@@ -635,6 +635,76 @@ def test_bounded_tnd_graph_replay(ora):
         oracle_check(ora, dict(sub, aslk=np.asarray(lens, dtype=np.int32)), idx.cpu().numpy(), val.cpu().numpy())
 
 
+# --- bounded BSND with actual_seq_lengths_query on the device ---------------
+BOUNDED_ASLQ = {
+    # decode items built on the device: staged rows, merges, unused rows, an empty batch
+    "decode_s4": (synth.small(batch=4, s1=4, aslk=[20000] * 4, block_size=64, sparse_count=512, sparse_mode=3),
+                  [4, 2, 0, 3], [20000, 9000, 20000, 1]),
+    "decode_s1_fp8": (synth.small(qk=synth.FP8, batch=5, s1=1, aslk=[9000] * 5, block_size=32, sparse_count=300),
+                      [1, 0, 1, 1, 1], [9000, 9000, 150, 0, 4097]),
+    # prefill items (S1 > 4): rows past the count are padding
+    "prefill_s13": (synth.small(batch=3, s1=13, aslk=[12000] * 3, block_size=128, sparse_count=1024,
+                                sparse_mode=3), [13, 5, 9], [12000, 3000, 11999]),
+}
+
+
+@pytest.mark.parametrize("name", list(BOUNDED_ASLQ))
+def test_bounded_aslq_matches_planned(ora, name):
+    """qli_run_bounded_aslq gives exactly qli_plan + qli_run with the same host
+    query counts, and matches the oracle on every row."""
+    import torch
+    spec, aslq, lens = BOUNDED_ASLQ[name]
+    inp = synth.make_inputs(spec, 8)
+    dev = device_inputs(inp)
+    bound = int(spec.aslk[0])
+    log("bounded aslq %s: aslq %s lens %s" % (name, aslq, lens))
+    bix = qli_mod().BoundedIndexer(inp["problem"], bound)
+    idx, val = bix.alloc_outputs()
+    bix.run(torch.tensor(lens, dtype=torch.int32, device="cuda"), dev["query"], dev["key"], dev["weights"],
+            dev["q_scale"], dev["k_scale"], dev["block_table"], idx, val,
+            aslq_dev=torch.tensor(aslq, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    sub = dict(inp, aslq=np.asarray(aslq, dtype=np.int32))
+    p_idx, p_val = planned(sub, dev, lens)
+    assert np.array_equal(idx.cpu().numpy(), p_idx) and np.array_equal(val.cpu().numpy(), p_val)
+    oracle_check(ora, dict(sub, aslk=np.asarray(lens, dtype=np.int32)), idx.cpu().numpy(), val.cpu().numpy())
+
+
+def test_bounded_aslq_graph_replay(ora):
+    """qli_run_bounded_aslq captured once (device item table included);
+    between replays the query counts and key lengths change: every replay
+    equals qli_plan + qli_run for the new lengths."""
+    import torch
+    spec = BOUNDED_ASLQ["decode_s4"][0]
+    inp = synth.make_inputs(spec, 9)
+    dev = device_inputs(inp)
+    bound = int(spec.aslk[0])
+    bix = qli_mod().BoundedIndexer(inp["problem"], bound)
+    q = torch.tensor([4, 4, 4, 4], dtype=torch.int32, device="cuda")
+    k = torch.tensor([bound] * 4, dtype=torch.int32, device="cuda")
+    idx, val = bix.alloc_outputs()
+    args = (k, dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"], idx, val)
+    bix.run(*args, aslq_dev=q)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bix.run(*args, aslq_dev=q)
+    for aslq, lens in (([4, 4, 4, 4], [20000] * 4), ([1, 0, 3, 4], [700, 20000, 8193, 16000]),
+                       ([2, 2, 2, 2], [0, 12, 19999, 5000]), ([4, 3, 0, 1], [20000, 20000, 20000, 20000])):
+        q.copy_(torch.tensor(aslq, dtype=torch.int32))
+        k.copy_(torch.tensor(lens, dtype=torch.int32))
+        idx.fill_(-7)
+        val.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        sub = dict(inp, aslq=np.asarray(aslq, dtype=np.int32))
+        p_idx, p_val = planned(sub, dev, lens)
+        assert np.array_equal(idx.cpu().numpy(), p_idx), "aslq %s lens %s" % (aslq, lens)
+        assert np.array_equal(val.cpu().numpy(), p_val), "aslq %s lens %s" % (aslq, lens)
+        oracle_check(ora, dict(sub, aslk=np.asarray(lens, dtype=np.int32)), idx.cpu().numpy(), val.cpu().numpy())
+
+
 # --- seeded random problems -----------------------------------------------------
 def random_spec(i: int):
     """A random small problem (seeded by i): dtype, layout, batch, ragged key
