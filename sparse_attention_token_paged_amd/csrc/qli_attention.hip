@@ -15,17 +15,19 @@
 //
 // attention_kernel: one workgroup per (row, split of the row's list).  The
 // split's valid entries are compacted into LDS (block id and slot), then
-// streamed through a 2-stage LDS ring of 64 entries: keys land by
-// direct-to-LDS loads (XOR-swizzled 16-byte chunks, so the MFMA operand reads
-// are conflict-free), values go through registers into a transposed [d][key]
-// tile.  Wave w owns query heads [w*HPW, (w+1)*HPW); per 32 entries and 16
-// heads: S^T = K Q^T (8 x v_mfma_f32_16x16x32_bf16, lanes hold one head and 4
-// keys), an online softmax in the exp2 domain (max across the 4 lanes of a
-// head by permlane swaps), P^T packed to bf16 in place, O^T += V^T P^T (8
-// MFMAs over the 8 d-tiles; the key order inside the 32-entry K dimension is
-// the one the S^T lanes already hold, applied to V^T as well).  A row
-// finished by one workgroup writes bf16 out and fp32 lse; split rows write
-// fp32 partials (unnormalized O, running max, sum) that combine_kernel merges.
+// streamed through a 4-stage LDS ring of 32 entries (three stages load while
+// one is computed): keys and values both land by direct-to-LDS loads into
+// row-major tiles whose 16-byte chunks are XOR-swizzled by entry, so the
+// MFMA operand reads are conflict-free; the V^T operands are gathered from
+// the value tile with 2-byte LDS reads.  Wave w owns query heads
+// [w*HPW, (w+1)*HPW); per 32 entries and 16 heads: S^T = K Q^T
+// (8 x v_mfma_f32_16x16x32_bf16, lanes hold one head and 4 keys), an online
+// softmax in the exp2 domain (max across the 4 lanes of a head by permlane
+// swaps), P^T packed to bf16 in place, O^T += V^T P^T (8 MFMAs over the 8
+// d-tiles; the key order inside the 32-entry K dimension is the one the S^T
+// lanes already hold, applied to V^T as well).  A row finished by one
+// workgroup writes bf16 out and fp32 lse; split rows write fp32 partials
+// (unnormalized O, running max, sum) that combine_kernel merges.
 #include <hip/hip_runtime.h>
 
 #include <cmath>

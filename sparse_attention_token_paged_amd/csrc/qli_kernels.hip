@@ -542,6 +542,12 @@ __device__ __forceinline__ float key_value(uint32_t u) {
 // form) or in the lane's 4-byte slot m0 + lane * 4 (4- and 2-byte forms).
 // Callers wait with wait_vm<N>() (vmcnt counts them with every other vector
 // memory access; loads complete in issue order).
+// These helpers write m0 behind the compiler's back.  That is sound only
+// while no code in this file relies on m0 across them: gfx950 LDS accesses
+// do not use it, and this file has no LDS-DMA builtins, s_sendmsg or
+// dynamically indexed register arrays (the compiled code has no other m0
+// access).  Code that adds one of those must switch these loads to
+// __builtin_amdgcn_global_load_lds, whose m0 the compiler manages.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

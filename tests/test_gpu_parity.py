@@ -943,3 +943,35 @@ def test_sorted_output_bounded(ora):
     assert np.array_equal(idx.cpu().numpy(), p_idx) and np.array_equal(val.cpu().numpy(), p_val)
     rows = p_idx.shape[0]
     assert any(np.any(np.diff(p_idx[r][p_idx[r] >= 0]) < 0) for r in range(rows))   # really reordered
+
+
+def test_negative_query_scale_follows_the_documented_reading(ora):
+    """Out of contract: negative dequant scales.  The kernels fold ScaleQ into W
+    and take ScaleK out of the ReLU, so they compute
+    sum_g W_g ScaleQ_g ScaleK relu(dot_g), which equals the page's
+    sum_g W_g relu(ScaleQ_g ScaleK dot_g) only for non-negative scales.  This
+    test pins that documented behaviour: with some ScaleQ negated, the GPU's
+    scores match the factored form (from the exact int8 dots), and differ from
+    the literal formula that the oracle evaluates."""
+    import torch
+    spec = synth.small(batch=1, s1=1, aslk=[256], block_size=64, sparse_count=256)
+    inp = synth.make_inputs(spec, 41)
+    inp["q_scale"][0, ::3] = -inp["q_scale"][0, ::3]
+    p = inp["problem"]
+    ix = make_indexer(inp)
+    dev = device_inputs(inp)
+    _, _, dots, scores = ix.run_debug(dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"],
+                                      dev["block_table"], 0, 1, 256)
+    torch.cuda.synchronize()
+    dots, scores = dots.cpu().numpy()[0].astype(np.float64), scores.cpu().numpy()[0].astype(np.float64)
+    w = inp["weights"][0].astype(np.float64)
+    sq = inp["q_scale"][0].astype(np.float64)
+    blk = inp["block_table"][0]
+    sk = np.array([float(inp["k_scale"][blk[j // 64], j % 64]) for j in range(256)])
+    terms = (w * sq)[:, None] * np.maximum(dots, 0.0) * sk[None, :]
+    factored = terms.sum(axis=0)
+    # fp32 accumulation: error relative to the sum of the terms' magnitudes (they now cancel)
+    assert np.all(np.abs(scores - factored) <= ATOL + INT8_RTOL * np.abs(terms).sum(axis=0))
+    _, odots, literal = ora.row_detail(inp, 0, 0, 256)
+    assert np.array_equal(odots, dots)
+    assert np.max(np.abs(literal - factored)) > 1e-2 * np.max(np.abs(literal))
