@@ -199,7 +199,7 @@ SIMDS = 1024                   # 256 CUs x 4 SIMDs
 SHADER_ENGINES = 32            # 8 XCDs x 4; SQ_BUSY_CYCLES sums one count per engine
 
 
-def summarize_sq(workload: str, sq_dir: str) -> dict:
+def summarize_sq(workload: str, sq_dir: str, consumer: bool = False) -> dict:
     """Issue counters of the scoring kernel from one rocprofv3 --pmc run of
     the SQ_COUNTERS (medians over its dispatches).  MFMA busy
     (SQ_VALU_MFMA_BUSY_CYCLES, SIMD cycles) and VALU active
@@ -211,7 +211,9 @@ def summarize_sq(workload: str, sq_dir: str) -> dict:
     per = {}
     for r in rows:
         n = r["Kernel_Name"]
-        if "score_decode_kernel" not in n and "score_kernel" not in n:
+        if consumer and "attention_kernel" not in n:
+            continue
+        if not consumer and "score_decode_kernel" not in n and "score_kernel" not in n:
             continue
         d = per.setdefault(r["Dispatch_Id"], {"name": n})
         d[r["Counter_Name"]] = float(r["Counter_Value"])
@@ -224,7 +226,7 @@ def summarize_sq(workload: str, sq_dir: str) -> dict:
     nominal = SIMDS * ns * 2.4                          # SIMD cycles at 2.4 GHz over the dispatch
     busy = SIMDS * med("SQ_BUSY_CYCLES") / SHADER_ENGINES  # SIMD cycles while the sequencers were busy
     mfma, valu = med("SQ_VALU_MFMA_BUSY_CYCLES"), 4.0 * med("SQ_ACTIVE_INST_VALU")
-    res = {"workload": workload, "kernel_source_sha256_16": kernel_source_hash(),
+    res = {"workload": workload, "kernel_source_sha256_16": kernel_source_hash(consumer),
            "kernels": sorted(set(d["name"].replace("qli::(anonymous namespace)::", "").replace("void ", "")
                                  .split("(")[0] for d in disp)),
            "dispatches": len(disp), "dispatch_ns_median": ns}
@@ -540,8 +542,10 @@ def main() -> int:
                          + " ".join(SQ_COUNTERS))
     args = ap.parse_args()
     if args.summarize_sq:
-        res = summarize_sq(args.workload, args.summarize_sq)
-        with open(os.path.join(PROFILES, "issue_score_kernel_%s.json" % args.workload), "w") as f:
+        res = summarize_sq(args.workload, args.summarize_sq, consumer=args.consumer)
+        name = ("issue_attention_kernel_%s_h%d.json" % (args.workload, args.heads)) if args.consumer \
+            else "issue_score_kernel_%s.json" % args.workload
+        with open(os.path.join(PROFILES, name), "w") as f:
             json.dump(res, f, indent=1)
         print(json.dumps(res))
         return 0

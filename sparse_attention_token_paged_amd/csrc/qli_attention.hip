@@ -49,6 +49,7 @@ constexpr int kDim = 128;         // head dim (the same D as the indexer's)
 constexpr int kStage = 32;        // entries per LDS stage
 constexpr int kRing = 4;          // stages in the LDS ring (three load while one is computed)
 constexpr int kMaxList = 2048;    // entries one workgroup compacts (sparse_count <= 2048)
+constexpr int kMaxSplit = kMaxList / 256;  // splits of a row (each at least 256 entries)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -104,6 +105,21 @@ __device__ __forceinline__ void lds_barrier() {
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Direct-to-LDS load of 16 bytes per lane (landing at the wave-uniform LDS
+// address lds + lane * 16), issued from inline assembly: the compiler then
+// adds no waits of its own between these loads and the LDS reads of other
+// ring slots (with the builtin it put a vmcnt(0) into one slot's reads);
+// the ring's waits are the explicit wait_vm<N>() above.  The helper writes
+// m0 behind the compiler's back, which is sound only while nothing else in
+// this file relies on m0 (gfx950 LDS reads and writes do not use it, and
+// this file has no LDS-DMA builtin, s_sendmsg or dynamically indexed
+// register array).
+__device__ __forceinline__ void dma16(const void* g, const void* lds) {
+  const uint32_t m0 =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
 }
 
 template <int HPW, int NW>
@@ -209,10 +225,8 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(Params P) {
       const int kk = 4 * (i * NW + wave) + q4;
       const int e = min(st * kStage + kk, nvalid - 1);
       const int64_t off = (int64_t)lds_blk[e] * P.stride + (int64_t)lds_slot[e] * kDim + 8 * (c16 ^ (kk & 15));
-      __builtin_amdgcn_global_load_lds(P.kc + off, (__attribute__((address_space(3))) void*)&lds_k[S][(i * NW + wave) * 1024],
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds(P.vc + off, (__attribute__((address_space(3))) void*)&lds_v[S][(i * NW + wave) * 1024],
-                                       16, 0, 0);
+      dma16(P.kc + off, &lds_k[S][(i * NW + wave) * 1024]);
+      dma16(P.vc + off, &lds_v[S][(i * NW + wave) * 1024]);
     }
   };
 
@@ -235,16 +249,25 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(Params P) {
     }
     // V^T operands of the 8 d-tiles: row d = 16 t + lane % 16, K positions
     // 8 q .. 8 q + 7 <-> entries 4 q + {0..3} and 16 + 4 q + {0..3}; element
-    // (entry e, dim d) sits in chunk (d / 8) ^ (e % 16) of row e.
+    // (entry e, dim d) sits in chunk (d / 8) ^ (e % 16) of row e.  Two LDS
+    // transpose reads (ds_read_b64_tr_b16) per d-tile: within each group of
+    // 16 lanes, lane j receives as its element c element j % 4 of the four
+    // that lane 4 c + j / 4 addressed.  Lane i of group q addresses entry
+    // 4 q + i / 4 (then 16 + 4 q + i / 4), dims 16 t + 4 (i % 4) .. + 3 (8
+    // contiguous bytes of one chunk), so lane j receives V[4 q + c][16 t + j].
     bf16x8 va[8];
+    {
+      const int ea = 4 * q4 + (c16 >> 2), eb = ea + 16;
+      const uint8_t* ra = vt + ea * 256 + 8 * (c16 & 1);
+      const uint8_t* rb = vt + eb * 256 + 8 * (c16 & 1);
 #pragma unroll
-    for (int t = 0; t < 8; t++) {
-      const int d = 16 * t + c16;
-#pragma unroll
-      for (int x = 0; x < 8; x++) {
-        const int e = (x < 4 ? 0 : 16) + 4 * q4 + (x & 3);
-        const int pc = (d >> 3) ^ (e & 15);
-        va[t][x] = *reinterpret_cast<const __bf16*>(vt + e * 256 + pc * 16 + 2 * (d & 7));
+      for (int t = 0; t < 8; t++) {
+        const int lc = 2 * t + ((c16 & 3) >> 1);  // logical chunk of dims 16 t + 4 (i % 4)
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(ra + ((lc ^ (ea & 15)) << 4)));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(rb + ((lc ^ (eb & 15)) << 4)));
+        va[t] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     }
 #pragma unroll
@@ -363,18 +386,29 @@ __global__ __launch_bounds__(256) void combine_kernel(Params P) {
   const int64_t rows_heads = (int64_t)gridDim.x * 8;
   if (pair >= rows_heads) return;
   const int r = (int)(pair / P.heads), h = (int)(pair - (int64_t)r * P.heads);
+  // every split's (max, sum) and O slice requested at once (nsplit <= kMaxSplit)
+  float ms[kMaxSplit], ls[kMaxSplit];
+  v4f os[kMaxSplit];
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; s++) {
+    const int64_t slot = ((int64_t)r * P.nsplit + s) * P.heads + h;
+    const bool in = s < P.nsplit;
+    ms[s] = in ? P.part_ml[2 * slot] : -INFINITY;
+    ls[s] = in ? P.part_ml[2 * slot + 1] : 0.f;
+    os[s] = in ? *reinterpret_cast<const v4f*>(P.part_o + slot * kDim + 4 * d4) : v4f{0.f, 0.f, 0.f, 0.f};
+  }
   float M = -INFINITY;
-  for (int s = 0; s < P.nsplit; s++) M = fmaxf(M, P.part_ml[2 * (((int64_t)r * P.nsplit + s) * P.heads + h)]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; s++) M = fmaxf(M, ms[s]);
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < P.nsplit; s++) {
-      const int64_t slot = ((int64_t)r * P.nsplit + s) * P.heads + h;
-      const float ms = P.part_ml[2 * slot];
-      if (ms == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(ms - M);
-      L += P.part_ml[2 * slot + 1] * w;
-      acc += *reinterpret_cast<const v4f*>(P.part_o + slot * kDim + 4 * d4) * w;
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; s++) {
+      if (ms[s] == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(ms[s] - M);
+      L += ls[s] * w;
+      acc += os[s] * w;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -472,6 +506,7 @@ QLI_EXPORT int qli_sparse_attention(const qli_attn_problem* p, const int32_t* as
       !aligned(sparse_indices, 4) || !aligned(out, 8) || !aligned(lse, 4))
     return QLI_ERR_ARG;
   const Split s = choose_split(rows, p->sparse_count);
+  if (s.nsplit > kMaxSplit) return QLI_ERR_SIZE;  // combine_kernel holds at most kMaxSplit partials
   const size_t ws = workspace_bytes(p);
   if (ws > 0 && (!workspace || !aligned(workspace, 16))) return QLI_ERR_ARG;
   Params P{};
