@@ -760,16 +760,13 @@ def test_parity_random(ora, i):
 
 @pytest.mark.parametrize("i", range(12))
 def test_bounded_random(ora, i):
-    """Seeded random problems (the generator above; BSND with every query row
-    active) run without a host plan, lengths on the device and the bound at the
-    longest key: bit-identical to qli_plan + qli_run where the plan uses the
-    same tiles (every BSND problem, TND with a batch of more than 4 rows),
+    """Seeded random problems (the generator above) run without a host plan,
+    lengths (and query counts, BSND ones included) on the device and the bound
+    at the longest key: bit-identical to qli_plan + qli_run where the plan uses
+    the same tiles (every BSND problem, TND with a batch of more than 4 rows),
     else within the parity rule of the oracle."""
-    import dataclasses
     import torch
     spec = random_spec(100 + i)
-    if spec.layout == synth.BSND:
-        spec = dataclasses.replace(spec, aslq=None)
     inp = synth.make_inputs(spec, i)
     p = inp["problem"]
     log("bounded random %d: %s" % (i, spec))
@@ -777,7 +774,7 @@ def test_bounded_random(ora, i):
     bound = max(1, int(max(inp["aslk"])))
     bix = qli_mod().BoundedIndexer(p, bound)
     k_dev = torch.from_numpy(inp["aslk"].astype(np.int32)).cuda()
-    q_dev = torch.from_numpy(np.asarray(inp["aslq"], dtype=np.int32)).cuda() if spec.layout == synth.TND else None
+    q_dev = torch.from_numpy(np.asarray(inp["aslq"], dtype=np.int32)).cuda() if inp["aslq"] is not None else None
     idx, val = bix.alloc_outputs()
     bix.run(k_dev, dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
             idx, val, aslq_dev=q_dev)
@@ -975,3 +972,24 @@ def test_negative_query_scale_follows_the_documented_reading(ora):
     _, odots, literal = ora.row_detail(inp, 0, 0, 256)
     assert np.array_equal(odots, dots)
     assert np.max(np.abs(literal - factored)) > 1e-2 * np.max(np.abs(literal))
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_parity_random_windowed(ora, i):
+    """Seeded random problems with random pre/next_tokens windows (and, for
+    half of them, score-ordered output) against the oracle on every row."""
+    import dataclasses
+    rng = np.random.default_rng(777 + i)
+    spec = dataclasses.replace(random_spec(200 + i),
+                               pre_tokens=int(rng.choice([0, 1, 7, 100, 1000, 5000, synth.INT64_MAX])),
+                               next_tokens=int(rng.choice([0, 3, 50, synth.INT64_MAX])))
+    inp = synth.make_inputs(spec, i)
+    p = inp["problem"]
+    log("random windowed %d: %s" % (i, spec))
+    dev = device_inputs(inp)
+    gidx, gval, _ = run_gpu(inp, dev)
+    check_windowed(ora, inp, gidx, gval)
+    if i % 2:
+        sidx, sval, _ = run_gpu(dict(inp, problem=dict(p, sort_output=1)), dev)
+        want_i, want_v = by_score(gidx, gval)
+        assert np.array_equal(sidx, want_i) and np.array_equal(sval, want_v)
