@@ -147,6 +147,13 @@ def _counter_rows(directory: str):
     return rows
 
 
+def short_kernel_name(name: str) -> str:
+    """A kernel's name without its namespaces and arguments."""
+    for ns in ("qli::(anonymous namespace)::", "qla::(anonymous namespace)::", "void "):
+        name = name.replace(ns, "")
+    return name.split("(")[0]
+
+
 def summarize_counters(workload: str, fetch_dir: str, write_dir: str, consumer: bool = False) -> dict:
     """HBM bytes per scoring-kernel launch from two rocprofv3 --pmc runs of
     `bench.py --calibrate-copy` (FETCH_SIZE, then WRITE_SIZE; KiB per
@@ -180,8 +187,7 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str, consumer: 
     res = {
         "workload": workload,
         "kernel_source_sha256_16": kernel_source_hash(consumer),
-        "kernels": sorted(set(n.replace("qli::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
-                              for n in names)),
+        "kernels": sorted(set(short_kernel_name(n) for n in names)),
         "fetch_kib_per_launch_raw": f_score, "write_kib_per_launch_raw": w_score,
         "calibration": {"kernel": "torch.neg over %d MiB (reads and writes that much)" % (COPY_BYTES >> 20),
                         "fetch_kib_raw": f_neg, "write_kib_raw": w_neg,
@@ -227,8 +233,7 @@ def summarize_sq(workload: str, sq_dir: str, consumer: bool = False) -> dict:
     busy = SIMDS * med("SQ_BUSY_CYCLES") / SHADER_ENGINES  # SIMD cycles while the sequencers were busy
     mfma, valu = med("SQ_VALU_MFMA_BUSY_CYCLES"), 4.0 * med("SQ_ACTIVE_INST_VALU")
     res = {"workload": workload, "kernel_source_sha256_16": kernel_source_hash(consumer),
-           "kernels": sorted(set(d["name"].replace("qli::(anonymous namespace)::", "").replace("void ", "")
-                                 .split("(")[0] for d in disp)),
+           "kernels": sorted(set(short_kernel_name(d["name"]) for d in disp)),
            "dispatches": len(disp), "dispatch_ns_median": ns}
     res.update({c: med(c) for c in SQ_COUNTERS})
     res["mfma_busy_frac_of_dispatch_at_2p4ghz"] = round(mfma / nominal, 4)

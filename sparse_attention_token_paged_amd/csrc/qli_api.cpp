@@ -505,6 +505,7 @@ struct Bounded {
   int32_t nseg;
   int64_t tab_off;  // TND: byte offset of the row and group tables in the workspace
   int64_t items_off, count_off;  // decode: the device-built item table and its count (-1: none)
+  bool plan_in_kernel;           // decode with few batches: the scoring kernel splits the work itself
 };
 
 int bounded_geometry_scores(const qli_problem& p, int64_t max_len, Bounded& g) {
@@ -570,17 +571,29 @@ int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
   const int rc = bounded_geometry_scores(p, max_len, g);
   if (rc != QLI_OK) return rc;
   g.items_off = -1;
+  g.plan_in_kernel = false;
   PlanHeader& h = g.h;
   if (h.kind == kKindDecode && h.rows > 0) {
-    // decode: items built on the device from the lengths (decode_items_kernel),
+    // decode: items derived on the device from the lengths, by every scoring
+    // workgroup for few batches, else by decode_items_kernel into a table
     // after the scores; h.n_items bounds their number for the launch
     const int64_t cap = device_items_capacity(p.batch, max_len / p.cmp_ratio);
     if (cap > INT32_MAX) return QLI_ERR_SIZE;
-    g.items_off = align16(h.workspace_bytes);
-    g.count_off = g.items_off + (int64_t)sizeof(Item) * cap;
-    h.workspace_bytes = g.count_off + 16;
     h.n_items = (int32_t)cap;
     h.reg_chunks = 0;
+    if (p.batch <= kPlanInKernelBatches) {
+      // The launch only bounds the persistent grid: size it as for every batch
+      // at the bound (each workgroup runs the split's prologue, so idle ones
+      // are not free); items beyond it run in later rounds.
+      g.plan_in_kernel = true;
+      const int64_t nmax = max_len / p.cmp_ratio;
+      const int c = decode_chunk_equal(p.batch, (int32_t)nmax);
+      h.n_items = (int32_t)std::min<int64_t>(cap, std::max<int64_t>(1, (nmax + c - 1) / c) * p.batch);
+    } else {
+      g.items_off = align16(h.workspace_bytes);
+      g.count_off = g.items_off + (int64_t)sizeof(Item) * cap;
+      h.workspace_bytes = g.count_off + 16;
+    }
   }
   add_values_region(p, h);
   return QLI_OK;
@@ -722,6 +735,7 @@ static int run_bounded_common(const qli_problem* p, int64_t max_seq_len_key, con
   }
   a.items_off = g.items_off;
   a.count_off = g.count_off;
+  a.plan_in_kernel = g.plan_in_kernel;
   rc = check_run_args(a, static_ws);
   if (rc != QLI_OK) return rc;
   if (static_ws && g.h.workspace_bytes > 0 && scratch_address(&a.workspace) != 0) return QLI_ERR_HIP;

@@ -222,7 +222,14 @@ struct RunArgs {
   // Bounded decode: byte offsets in the workspace of the item table the device
   // planner builds (decode_items_kernel) and of its item count; -1 = none.
   int64_t items_off = -1, count_off = 0;
+  // Bounded decode with at most kPlanInKernelBatches batches: every scoring
+  // workgroup derives the same split itself (no table, no extra launch).
+  bool plan_in_kernel = false;
 };
+
+// Batches up to which bounded decode plans inside the scoring kernel (one
+// batch per thread of a 256-thread workgroup); larger batches use the table.
+constexpr int kPlanInKernelBatches = 256;
 
 // Bounded decode's device-built item table: one workgroup picks the chunk as
 // qli_plan does (the smallest multiple of 128 entries whose items fit the

@@ -55,6 +55,7 @@ struct ScoreParams {
   const Item* items;      // the plan's item table
   int32_t n_items;
   const int32_t* n_items_dev;  // bounded decode: the item count the device planner wrote (else null)
+  int32_t plan_batches;        // bounded decode planned in the kernel: the batch count (else 0)
   int32_t chunk;          // keys per item
   int32_t reg_chunks, reg_rows, reg_maxv;  // regular decode plans (0: not regular)
   const RowInfo* rinfo;   // the plan's row table
@@ -166,6 +167,26 @@ template <int QK>
 __device__ __forceinline__ int chunk_lo(int q) { return QK == QLI_QK_INT8 ? q : 2 * q; }
 template <int QK>
 __device__ __forceinline__ int chunk_hi(int q) { return QK == QLI_QK_INT8 ? q + 4 : 2 * q + 1; }
+
+// Reductions over a wave.
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Candidate decode chunks of the device-side split: 128, 256, .., kMaxChunk entries.
+constexpr int kChunkSteps = kMaxChunk / 128;
 
 // Workgroup barrier that orders LDS (waits for this wave's LDS accesses) but
 // leaves outstanding global loads in flight.
@@ -902,6 +923,76 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   float* ov = nullptr;
   bool direct = false;     // the row sees at most k entries: scores go straight to the outputs
 
+  // Bounded decode planned in the kernel (P.plan_batches > 0, at most one
+  // batch per thread): thread t holds batch t's visible maximum my_m (that of
+  // its last used query row), used rows my_s1b and clamped key length my_skb;
+  // plan_items() picks the chunk with the planner's rule (the smallest
+  // multiple of 128 entries whose items fit the resident decode workgroups;
+  // for equal batches the one that lowers the busiest CU's keys), gives each
+  // batch max(1, ceil(my_m / chunk)) items at the exclusive prefix my_first
+  // and returns their number.  Every workgroup derives the same split; its
+  // scratch lies in the ring, free until the first stage is issued.
+  __shared__ int plan_sh[8];
+  int my_m = 0, my_s1b = 0, my_first = 0, my_n = 0, plan_chunk = 0;
+  int64_t my_skb = 0;
+  auto plan_items = [&]() {
+    const int nb = P.plan_batches;
+    if (tid < nb) {
+      my_skb = min<int64_t>(max(P.aslk[tid], 0), P.max_len);
+      my_s1b = P.aslq_bsnd ? min(max(P.aslq_bsnd[tid], 0), P.reg_rows) : P.reg_rows;
+      my_m = my_s1b > 0 ? (int)visible_entries(P.mode, P.cmp, my_skb, my_s1b, my_s1b - 1) : 0;
+    }
+    int* sm = reinterpret_cast<int*>(&ring[0][0]);  // [256] visible maxima
+    int* part = sm + kScoreThreads;                 // [8][32] partial item counts
+    int* pmm = part + kScoreThreads;                // [8] partial minima, [8] maxima
+    int* scan_tmp = pmm + 16;                       // the block scan's
+    sm[tid] = tid < nb ? my_m : 0;
+    __syncthreads();
+    {  // candidate chunk 128 (tid % 32 + 1) over batches tid / 32, tid / 32 + 8, ...
+      static_assert(kChunkSteps == 32 && kScoreThreads == 256, "8 groups of the 32 candidates");
+      const int c = 128 * ((tid & 31) + 1);
+      int sum = 0, lo = INT32_MAX, hi = -1;
+      for (int b = tid >> 5; b < nb; b += 8) {
+        const int m = sm[b];
+        sum += (m + c - 1) / c;
+        lo = min(lo, m);
+        hi = max(hi, m);
+      }
+      part[tid] = sum;
+      if ((tid & 31) == 0) {
+        pmm[tid >> 5] = lo;
+        pmm[8 + (tid >> 5)] = hi;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {  // lane i < 32: candidate i's item count; the choice by ballot and a wave minimum
+      const int i = lane & 31;
+      int cnt = 0, lo = INT32_MAX, hi = -1;
+#pragma unroll
+      for (int g = 0; g < 8; g++) {
+        cnt += part[32 * g + i];
+        lo = min(lo, pmm[g]);
+        hi = max(hi, pmm[8 + g]);
+      }
+      const unsigned long long fit = __ballot(lane < 32 && cnt <= kDecodeSlots);
+      int best = fit ? __ffsll((long long)fit) - 1 : kChunkSteps - 1;
+      if (hi >= 0 && lo == hi) {  // equal batches: the chunk >= best that lowers the busiest CU's keys
+        // at most about 2^22 + 2^13 (256 batches of 2^22 entries): busiest * 32 + i fits 32 bits
+        const int busiest = (cnt + kCUs - 1) / kCUs * (128 * (i + 1));
+        best = wave_min(lane < 32 && i >= best ? busiest * 32 + i : INT32_MAX) & 31;
+      }
+      if (lane == 0) plan_sh[6] = best;
+    }
+    __syncthreads();
+    const int best = plan_sh[6];
+    plan_chunk = 128 * (best + 1);
+    my_n = tid < nb ? max(1, (my_m + plan_chunk - 1) / plan_chunk) : 0;
+    my_first = block_exclusive_scan<kScoreThreads>(my_n, scan_tmp);
+    if (tid == kScoreThreads - 1) plan_sh[7] = my_first + my_n;
+    __syncthreads();
+    return plan_sh[7];
+  };
+
   // Rows of an item that see fewer than k entries: slots count..k-1 are -1 / -inf.
   auto pad = [&](const Item& itp) __attribute__((always_inline)) {
     if (itp.flags & kItemPad) {
@@ -953,7 +1044,42 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   // stages 0 and 1.  False for an item without keys (padding only).
   auto begin = [&](int pos) __attribute__((always_inline)) {
     const Item* itp = P.items + pos;  // a plan's table or the one the bounded run built on the device
-    if (reg) {
+    if (P.plan_batches) {
+      // bounded decode planned in the kernel: the thread of the batch whose
+      // items hold pos publishes the item; the ring is free here
+      if (tid < P.plan_batches && pos >= my_first && pos < my_first + my_n) {
+        plan_sh[0] = tid;
+        plan_sh[1] = pos - my_first;
+        plan_sh[2] = my_m;
+        plan_sh[3] = my_s1b;
+        plan_sh[4] = (int)my_skb;
+      }
+      __syncthreads();
+      batch = plan_sh[0];
+      key0 = plan_sh[1] * plan_chunk;
+      const int m = plan_sh[2], s1b = plan_sh[3];
+      const int64_t skb = plan_sh[4];
+      __syncthreads();  // read by every thread before the next item's owner writes them
+      nkeys = min(plan_chunk, m - key0);
+      row0 = batch * P.reg_rows;
+      nrows = P.reg_rows;
+      // the row's visible count: 0 past the batch's used rows
+      auto vis_of = [&](int uu) { return uu < s1b ? (int)visible_entries(P.mode, P.cmp, skb, s1b, uu) : 0; };
+      if (key0 == 0)  // the batch's first item pads its rows
+        for (int uu = 0; uu < nrows; uu++) {
+          const int64_t rr = row0 + uu;
+          for (int e = vis_of(uu) + tid; e < k; e += kScoreThreads) {
+            P.idx_out[rr * k + e] = -1;
+            if (P.val_out) P.val_out[rr * k + e] = -INFINITY;
+          }
+        }
+      if (nkeys <= 0) return false;  // uniform across the workgroup
+      rok = u < nrows;
+      r = row0 + (rok ? u : 0);
+      rvis = rok ? vis_of(u) : 0;
+      rlo = 0;
+      coff = rvis > k ? r * P.bstride + key0 : -1;
+    } else if (reg) {
       batch = pos / P.reg_chunks;
       key0 = (pos - batch * P.reg_chunks) * P.chunk;
       nkeys = min(P.chunk, P.reg_maxv - key0);
@@ -978,11 +1104,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     const int32_t* bt = P.block_table + (int64_t)batch * P.max_blocks + fb;
     const int bt0 = tid < nblk ? bt[tid] : 0;
     const int bt1 = tid + kScoreThreads < nblk ? bt[tid + kScoreThreads] : 0;
-    rok = u < nrows;
-    r = row0 + (rok ? u : 0);
-    rvis = rok ? itp->vis[u] : 0;
-    rlo = rok ? itp->lo[u] : 0;
-    coff = rok ? itp->cand_off[u] : -1;
+    if (!P.plan_batches) {
+      rok = u < nrows;
+      r = row0 + (rok ? u : 0);
+      rvis = rok ? itp->vis[u] : 0;
+      rlo = rok ? itp->lo[u] : 0;
+      coff = rok ? itp->cand_off[u] : -1;
+    }
     {
       const uint8_t* qrow = P.query + r * (kHeads * kDim);
   #pragma unroll
@@ -1088,7 +1216,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   };
 
 
-  const int n_items = P.n_items_dev ? *P.n_items_dev : P.n_items;
+  int n_items = P.n_items_dev ? *P.n_items_dev : P.n_items;
+  if (P.plan_batches) n_items = plan_items();
   for (int round = 0;; round++) {
   const int pos = pos_of(round);
   if (pos >= n_items) break;  // uniform; positions grow with the round
@@ -1471,6 +1600,7 @@ int launch_score(const RunArgs& a, bool dump) {
     P.n_items_dev = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(a.workspace) + a.count_off);
     P.aslk = nullptr;
   }
+  if (a.plan_in_kernel) P.plan_batches = a.p->batch;
   P.chunk = h->chunk;
   P.reg_chunks = h->reg_chunks;
   P.reg_rows = h->reg_rows;
@@ -1641,7 +1771,6 @@ int launch_sort(const RunArgs& a) {
 namespace {
 
 constexpr int kItemsThreads = 1024;
-constexpr int kChunkSteps = kMaxChunk / 128;
 
 struct DecodeItemsParams {
   const int32_t* aslk;
@@ -1651,22 +1780,6 @@ struct DecodeItemsParams {
   Item* items;
   int32_t* n_items;
 };
-
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-  return v;
-}
 
 __global__ __launch_bounds__(kItemsThreads) void decode_items_kernel(DecodeItemsParams D) {
   constexpr int NW = kItemsThreads / 64;

@@ -342,12 +342,13 @@ DECODE_SLOTS = 768   # decode workgroups resident at once (3 per CU x 256 CUs)
 
 def bounded_workspace_expected(p, max_len):
     """Bounded BSND: the scores' layout below, then for decode problems (S1 <= 4)
-    the item table the device builds (16-byte aligned; room for every item any
-    lengths can give: max(slots + B, B * ceil(entries / 4096)) items of 96
-    bytes) and its 16-byte count."""
+    of more than 256 batches the item table the device builds (16-byte aligned;
+    room for every item any lengths can give: max(slots + B, B * ceil(entries /
+    4096)) items of 96 bytes) and its 16-byte count.  Up to 256 batches the
+    scoring kernel splits the work itself and needs no table."""
     base = bounded_scores_expected(p, max_len)
     rows, b = p["batch"] * p["s1"], p["batch"]
-    if rows == 0 or p["s1"] > 4:
+    if rows == 0 or p["s1"] > 4 or b <= 256:
         return base
     nmax = max_len // p["cmp_ratio"]
     cap = max(DECODE_SLOTS + b, b * max(1, -(-nmax // 4096)))
@@ -389,13 +390,14 @@ def test_bounded_tnd_workspace(qli, b, t, k, max_len):
     assert rc == 0 and ws == bounded_tnd_workspace_expected(p, max_len)
 
 
+@pytest.mark.parametrize("batch", [3, 300])
 @pytest.mark.parametrize("s1,k,cmp,max_len", [(1, 512, 1, 1000), (4, 2048, 1, 8192), (2, 256, 4, 70000),
                                                 (3, 100, 1, 0), (1, 2048, 1, 140000), (8, 256, 1, 3000),
                                                 (13, 2048, 1, 20000), (64, 512, 2, 10000)])
-def test_bounded_workspace(qli, s1, k, cmp, max_len):
+def test_bounded_workspace(qli, batch, s1, k, cmp, max_len):
     spec = synth.small(batch=3, s1=s1, aslk=[max(max_len, 1)] * 3, block_size=64, sparse_count=k,
                        sparse_mode=3, cmp_ratio=cmp)
-    p = synth.make_inputs(spec, 1)["problem"]
+    p = dict(synth.make_inputs(spec, 1)["problem"], batch=batch)   # the workspace depends on the fields only
     rc, ws = qli.qli_bounded_workspace(qli.Problem.from_dict(p), max_len)
     assert rc == 0 and ws == bounded_workspace_expected(p, max_len)
 

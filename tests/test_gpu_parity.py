@@ -705,6 +705,34 @@ def test_bounded_aslq_graph_replay(ora):
         oracle_check(ora, dict(sub, aslk=np.asarray(lens, dtype=np.int32)), idx.cpu().numpy(), val.cpu().numpy())
 
 
+def test_bounded_many_batches_table(ora):
+    """More batches than the scoring kernel splits by itself (256): the
+    separate planning kernel writes the item table.  Ragged lengths with
+    empty batches and query counts; bit-identical to qli_plan + qli_run and
+    oracle-checked, twice with different lengths from the same workspace."""
+    import torch
+    rng = np.random.default_rng(5)
+    lens0 = [int(x) for x in rng.integers(0, 3000, size=300)]
+    lens0[7] = 0
+    bound = 3000
+    # every batch's blocks cover the bound: the lengths below only ever read allocated blocks
+    spec = synth.small(batch=300, s1=2, aslk=[bound] * 300, block_size=32, sparse_count=256, sparse_mode=3)
+    inp = synth.make_inputs(spec, 12)
+    dev = device_inputs(inp)
+    bix = qli_mod().BoundedIndexer(inp["problem"], bound)
+    for lens, aslq in ((lens0, None), ([int(x) for x in rng.integers(0, 3001, size=300)],
+                                       [int(x) for x in rng.integers(0, 3, size=300)])):
+        idx, val = bix.alloc_outputs()
+        q = None if aslq is None else torch.tensor(aslq, dtype=torch.int32, device="cuda")
+        bix.run(torch.tensor(lens, dtype=torch.int32, device="cuda"), dev["query"], dev["key"], dev["weights"],
+                dev["q_scale"], dev["k_scale"], dev["block_table"], idx, val, aslq_dev=q)
+        torch.cuda.synchronize()
+        sub = dict(inp, aslq=None if aslq is None else np.asarray(aslq, dtype=np.int32))
+        p_idx, p_val = planned(sub, dev, lens)
+        assert np.array_equal(idx.cpu().numpy(), p_idx) and np.array_equal(val.cpu().numpy(), p_val)
+        oracle_check(ora, dict(sub, aslk=np.asarray(lens, dtype=np.int32)), idx.cpu().numpy(), val.cpu().numpy())
+
+
 # --- seeded random problems -----------------------------------------------------
 def random_spec(i: int):
     """A random small problem (seeded by i): dtype, layout, batch, ragged key
