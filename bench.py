@@ -246,6 +246,35 @@ def summarize_sq(workload: str, sq_dir: str, consumer: bool = False) -> dict:
     return res
 
 
+LDS_COUNTERS = ["SQ_WAVES", "SQ_INSTS_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT",
+                "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY"]
+
+
+def summarize_lds(workload: str, lds_dir: str, consumer: bool = False) -> dict:
+    """LDS counters of the dominant kernel from one rocprofv3 --pmc run of the
+    LDS_COUNTERS (medians over its dispatches): LDS instructions per wave and
+    the share of the LDS's active cycles lost to bank conflicts."""
+    rows = _counter_rows(lds_dir)
+    key = (lambda n: "attention_kernel" in n) if consumer else \
+        (lambda n: "score_decode_kernel" in n or "score_kernel" in n)
+    per = {}
+    for r in rows:
+        if not key(r["Kernel_Name"]):
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    disp = [d for d in per.values() if all(c in d for c in LDS_COUNTERS)]
+    if not disp:
+        raise SystemExit("no dispatch with every LDS counter under %s" % lds_dir)
+    med = lambda k: sorted(d[k] for d in disp)[len(disp) // 2]
+    res = {"workload": workload, "kernel_source_sha256_16": kernel_source_hash(consumer),
+           "kernels": sorted(set(short_kernel_name(d["name"]) for d in disp)), "dispatches": len(disp)}
+    res.update({c: med(c) for c in LDS_COUNTERS})
+    res["lds_insts_per_wave"] = round(med("SQ_INSTS_LDS") / med("SQ_WAVES"), 1)
+    res["bank_conflict_frac_of_lds_active"] = round(med("SQ_LDS_BANK_CONFLICT") / max(med("SQ_LDS_IDX_ACTIVE"), 1.0), 4)
+    return res
+
+
 def cpu_model() -> str:
     """The host CPU's model name (from /proc/cpuinfo), for the baseline record."""
     try:
@@ -542,6 +571,9 @@ def main() -> int:
                     help="time the sparse-attention consumer on the workload's shape (default: the headline "
                          "decode workload)")
     ap.add_argument("--heads", type=int, default=64, help="query heads of the consumer (16, 32, 64, 128)")
+    ap.add_argument("--summarize-lds", metavar="LDS_DIR",
+                    help="write profiles/lds_<kernel>_<workload>.json from a rocprofv3 --pmc run of "
+                         + " ".join(LDS_COUNTERS))
     ap.add_argument("--summarize-sq", metavar="SQ_DIR",
                     help="write profiles/issue_score_kernel_<workload>.json from a rocprofv3 --pmc run of "
                          + " ".join(SQ_COUNTERS))
@@ -550,6 +582,14 @@ def main() -> int:
         res = summarize_sq(args.workload, args.summarize_sq, consumer=args.consumer)
         name = ("issue_attention_kernel_%s_h%d.json" % (args.workload, args.heads)) if args.consumer \
             else "issue_score_kernel_%s.json" % args.workload
+        with open(os.path.join(PROFILES, name), "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res))
+        return 0
+    if args.summarize_lds:
+        res = summarize_lds(args.workload, args.summarize_lds, consumer=args.consumer)
+        name = ("lds_attention_kernel_%s_h%d.json" % (args.workload, args.heads)) if args.consumer \
+            else "lds_score_kernel_%s.json" % args.workload
         with open(os.path.join(PROFILES, name), "w") as f:
             json.dump(res, f, indent=1)
         print(json.dumps(res))
