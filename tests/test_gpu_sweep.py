@@ -60,3 +60,27 @@ def test_sweep(ora, i):
         if tiles_match:
             assert np.array_equal(idx, gidx) and np.array_equal(val, gval)
         oracle_check(ora, inp, idx, val)
+
+
+@pytest.mark.skipif(N <= 0, reason="extended sweep: set QLI_SWEEP=<problems> to run it")
+@pytest.mark.parametrize("i", range(max(N // 4, 1)))
+def test_sweep_consumer(i):
+    """The sparse-attention consumer on random problems (head count, layout,
+    lengths, block size, list length, holes punched into the lists, padded
+    strides, softmax scale) against its fp64 oracle within the parity rule of
+    its own tests."""
+    import oracle.attention as oa
+    from tests import test_gpu_attention as ga
+    rng = np.random.default_rng(70000 + i)
+    for attempt in range(50):  # problems the fp64 oracle finishes in about a second
+        spec = dataclasses.replace(random_spec(60000 + 50 * i + attempt), qk=synth.INT8, stride_pad=0)
+        inp = synth.make_inputs(spec, 2000 + i)
+        a = synth.attention_inputs(inp, int(rng.choice([16, 32, 64, 128])), 3000 + i,
+                                   kv_stride_pad=int(rng.choice([0, 0, 8, 40])),
+                                   scale=float(rng.choice([1.0 / np.sqrt(128), 0.3, 2.0])))
+        if int((a["indices"] >= 0).sum()) * a["heads"] <= 4_000_000:
+            break
+    holes = rng.random(a["indices"].shape) < 0.1
+    a["indices"][holes] = -1
+    log("consumer sweep %d: heads %d, %s" % (i, a["heads"], spec))
+    ga.compare(oa.get(), a)
