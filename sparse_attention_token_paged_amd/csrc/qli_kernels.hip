@@ -17,20 +17,27 @@
 //     M dimension (4 tiles of 16), 16 keys the N dimension, D=128 the K one;
 //   * fused epilogue: ScaleQ is folded into W once per row (w' = W*ScaleQ,
 //     exact in fp32 for fp16 inputs), so each (head, key) element costs
-//     max + convert + fma; the head sum finishes with permlane swaps and one
-//     multiply by ScaleK[s].  This reordering needs ScaleQ, ScaleK >= 0,
-//     which is the contract (dequant scales are magnitudes);
-//   * rows that see at most sparse_count entries return every visible index
-//     (the top-k of a set no larger than k is the set), so their indices and
-//     scores are written straight to the outputs; other rows stage fp32
-//     scores in the workspace.
+//     max + fma (an int8 dot enters the fma as the fp32 denormal its bits
+//     spell, with w' and ScaleK carried by powers of two); the head sum
+//     finishes with permlane swaps and one multiply by ScaleK[s].  This
+//     reordering needs ScaleQ, ScaleK >= 0, which is the contract (dequant
+//     scales are magnitudes);
+//   * a row sees the entries [lo, hi) of its batch (lo > 0 only under a
+//     pre_tokens window); rows that see at most sparse_count entries return
+//     every visible index (the top-k of a set no larger than k is the set),
+//     so their indices and scores are written straight to the outputs; other
+//     rows stage fp32 scores in the workspace;
+//   * bounded decode (no host plan) derives its items on the device: inside
+//     score_decode_kernel for up to 256 batches, else decode_items_kernel
+//     writes a plan-shaped table first.
 // Stage 2 selects (select_reg_kernel, select_global_kernel; one workgroup of
 // 1024 threads per selection): rows of at most 8192 staged scores, and each
 // 8192-score segment of longer rows, keep their top-k; a second launch
 // merges a long row's segment winners.  Radix select over order-preserving
 // uint32 keys held in registers (11-bit digits, starting below the bits
 // every key shares, LDS histograms, block scans); ties at the threshold go to
-// the lower index; the winners are written in ascending index order.
+// the lower index; the winners are written in ascending index order, and
+// sort_rows_kernel reorders them by score when the caller asks.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -72,7 +79,7 @@ struct ScoreParams {
   const int32_t* group_start;
   const int32_t* group_batch;
   int32_t nbatch, trows;       //   batches, rows T
-  const int32_t* aslk;  // bounded prefill-shaped runs: key lengths on the device (else null)
+  const int32_t* aslk;  // bounded runs: key lengths on the device (else null; decode with a table: null)
   const int32_t* aslq_bsnd;  // bounded BSND: per-batch query counts (else null: all S1 rows used)
   int64_t max_len;      //   clamp for them (original tokens)
   int64_t bstride;      //   workspace elements per row
@@ -1579,7 +1586,7 @@ int launch_score(const RunArgs& a, bool dump) {
     P.items = reinterpret_cast<const Item*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_items);
     P.rinfo = reinterpret_cast<const RowInfo*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_rows);
   }
-  P.aslk = a.aslk;  // bounded decode (the header then describes the bound)
+  P.aslk = a.aslk;  // bounded runs (the header then describes the bound)
   P.aslq_bsnd = a.aslq_bsnd;
   if (a.aslq) {
     const TndTables t = tnd_tables(a.p->batch, a.p->s1);
