@@ -1059,7 +1059,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
         plan_sh[1] = pos - my_first;
         plan_sh[2] = my_m;
         plan_sh[3] = my_s1b;
-        plan_sh[4] = (int)my_skb;
+        plan_sh[4] = (int)my_skb;  // clamped to the bound, below kMaxEntries * 128 = 2^29
       }
       __syncthreads();
       batch = plan_sh[0];
