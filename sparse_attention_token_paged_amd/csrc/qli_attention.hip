@@ -102,6 +102,23 @@ __device__ int row_batch(const Params& P, int r) {
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// Issue priority of this wave from its progress through its entries: 3 during
+// the first quarter of its stages, down to 0 during the last.  Waves of equal
+// priority issue oldest first, so the workgroups sharing a CU would otherwise
+// finish in dispatch order; this lets one that has fallen behind catch up.
+// All waves of a workgroup are at the same stage, so they share the level.
+__device__ __forceinline__ void progress_priority(int done, int total) {
+  const int p = 3 - min(3, 4 * done / total);
+  if (p == 3)
+    __builtin_amdgcn_s_setprio(3);
+  else if (p == 2)
+    __builtin_amdgcn_s_setprio(2);
+  else if (p == 1)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -341,6 +358,7 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(Params P) {
     compute(st, slot_);
   };
   for (int st = 0; st < nst; st += kRing) {
+    progress_priority(st, nst);
     step(st, S0{}, S3{});
     if (st + 1 < nst) step(st + 1, S1{}, S0{});
     if (st + 2 < nst) step(st + 2, S2{}, S1{});

@@ -201,6 +201,25 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Issue priority of this wave from its progress through the current item:
+// 3 during the first quarter of its stages, down to 0 during the last.  Waves
+// of equal priority issue oldest first, so without it the workgroups sharing
+// a CU finish in dispatch order (three decode workgroups on equal items: the
+// youngest ended up to 15 us after the oldest); with it a workgroup that has
+// fallen behind outranks the ones ahead of it.  All waves of a workgroup are
+// at the same stage, so they share the level.
+__device__ __forceinline__ void progress_priority(int done, int total) {
+  const int p = 3 - min(3, 4 * done / total);
+  if (p == 3)
+    __builtin_amdgcn_s_setprio(3);
+  else if (p == 2)
+    __builtin_amdgcn_s_setprio(2);
+  else if (p == 1)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // w'[4m + i] = W * ScaleQ (times w_scale) for heads 16m + 4q + i of row r
 // (i = 0..3 are consecutive, so one 8- or 16-byte load per tensor and m).
 template <int QK>
@@ -1236,6 +1255,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
 
   // Pipeline: stages st+1 and st+2 are in flight while st is computed.
   for (int st = 0; st < nstages; st++) {
+    progress_priority(st, nstages);
     if (st + 2 < nstages) issue(st + 2);
     const int newer = min(st + 2, nstages - 1) - st;  // stages issued after st
     if (newer >= 2)
