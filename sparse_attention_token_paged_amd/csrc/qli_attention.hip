@@ -18,8 +18,10 @@
 // streamed through a 4-stage LDS ring of 32 entries (three stages load while
 // one is computed): keys and values both land by direct-to-LDS loads into
 // row-major tiles whose 16-byte chunks are XOR-swizzled by entry, so the
-// MFMA operand reads are conflict-free; the V^T operands are gathered from
-// the value tile with 2-byte LDS reads.  Wave w owns query heads
+// MFMA operand reads are conflict-free; the V^T operands come from the value
+// tile by LDS transpose reads (ds_read_b64_tr_b16, two per d-tile).  Waves
+// raise their issue priority while behind in their stages, so the workgroups
+// sharing a CU keep pace.  Wave w owns query heads
 // [w*HPW, (w+1)*HPW); per 32 entries and 16 heads: S^T = K Q^T
 // (8 x v_mfma_f32_16x16x32_bf16, lanes hold one head and 4 keys), an online
 // softmax in the exp2 domain (max across the 4 lanes of a head by permlane

@@ -11,7 +11,9 @@
 //     used cache line) into a double-buffered, XOR-swizzled LDS tile;
 //   * score_decode_kernel (items of 1, 2 or 4 rows of one batch) streams the
 //     chunk through a 3-stage LDS ring filled by direct-to-LDS loads, so the
-//     rows share every key byte read from HBM;
+//     rows share every key byte read from HBM; its waves raise their issue
+//     priority while behind in their item, so the workgroups sharing a CU
+//     keep pace instead of finishing in dispatch order;
 //   * both: int8 keys use v_mfma_i32_16x16x64_i8 (exact int32 dots), e4m3fn
 //     keys v_mfma_f32_16x16x128_f8f6f4; the 64 query heads of a row are the
 //     M dimension (4 tiles of 16), 16 keys the N dimension, D=128 the K one;
