@@ -97,6 +97,25 @@ def test_plan_length_validation(qli):
     assert rc == 1                                                  # TND needs the prefix sums
 
 
+def test_maximum_key_length(qli):
+    """A sequence holds at most 2^22 - 1 stored (compressed) entries, the
+    range in which the kernels' reciprocal division is exact; one more is
+    QLI_ERR_SIZE from the planner and the bounded entry points alike, with
+    and without compression.  Only lengths are read, so no cache is needed."""
+    p = base_problem()["problem"]
+    for cmp in (1, 4):
+        for n, want in (((1 << 22) - 1, qli.QLI_OK), (1 << 22, qli.QLI_ERR_SIZE)):
+            q = dict(p, batch=1, s1=1, block_size=1024, num_blocks=4096, max_blocks_per_seq=4096,
+                     sparse_count=2048, sparse_mode=0, cmp_ratio=cmp)
+            prob = qli.Problem.from_dict(q)
+            rc, _, ws = qli.qli_plan(prob, None, np.array([n * cmp], dtype=np.int32))
+            assert rc == want, (cmp, n, rc)
+            if rc == qli.QLI_OK:  # every score staged once, the merge region of 512 segment winners
+                assert ws >= 4 * n
+            rc, _ = qli.qli_bounded_workspace(prob, n * cmp)
+            assert rc == want, (cmp, n, rc)
+
+
 def test_plan_capacity(qli):
     inp = base_problem()
     lib = qli.load()

@@ -204,6 +204,33 @@ def test_parity_long_dense_rows(ora, name):
         check_row(r, int(vis[r]), k, gidx[r], gval[r], osc[r, :vis[r]], rtol_of(inp))
 
 
+
+def test_parity_maximum_key_length(ora):
+    """One row at the longest key length the plan accepts, 2^22 - 1 entries
+    (512 MiB of int8 keys in blocks of 1024): 1024 decode items of 4096
+    entries, 512 first-pass segment selections and one merge of 1,048,576
+    candidates in the re-reading selection kernel, against the oracle; the
+    bounded run (device length) gives the same bits."""
+    import torch
+    n = (1 << 22) - 1
+    inp = synth.make_inputs(synth.small(batch=1, s1=1, aslk=[n], block_size=1024, sparse_count=2048), 23)
+    vis = vis_of(ora, inp)
+    assert int(vis[0]) == n
+    log("case max key length: %d entries" % n)
+    dev = device_inputs(inp)
+    gidx, gval, _ = run_gpu(inp, dev)
+    check_structure(gidx, gval, vis, 2048)
+    bix = qli_mod().BoundedIndexer(inp["problem"], n)
+    idx, val = bix.alloc_outputs()
+    bix.run(torch.tensor([n], dtype=torch.int32, device="cuda"), dev["query"], dev["key"], dev["weights"],
+            dev["q_scale"], dev["k_scale"], dev["block_table"], idx, val)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), gidx) and np.array_equal(val.cpu().numpy(), gval)
+    log("  oracle over %d entries" % n)
+    rc, _, _, osc = ora.indexer(inp, scores_cols=n)
+    assert rc == 0
+    check_row(0, n, 2048, gidx[0], gval[0], osc[0], rtol_of(inp))
+
 def _extreme_fp16(rng, shape):
     """fp16 values over the whole non-negative range: zeros, the smallest
     subnormal and normal, the largest finite value, and log-uniform values
