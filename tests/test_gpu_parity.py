@@ -625,6 +625,36 @@ def test_bounded_tnd_prefix_sums_out_of_contract(ora):
     oracle_check(ora, dict(sub, aslk=np.asarray(lens, dtype=np.int32)), idx, val)
 
 
+def test_bounded_tnd_most_batches(ora):
+    """TND at the table kernel's limit of 4096 batches: 0 to 3 query rows
+    each, one batch of 9 rows (so qli_plan takes the same 8-row tiles), key
+    lengths 0 to 300 with empty batches; bit-identical to qli_plan + qli_run
+    and oracle-checked on every row."""
+    import torch
+    nb, bound = 4096, 300
+    rng = np.random.default_rng(41)
+    counts = rng.integers(0, 4, size=nb)
+    counts[100] = 9
+    aslq = [int(x) for x in np.cumsum(counts)]
+    lens = [int(x) for x in rng.integers(0, bound + 1, size=nb)]
+    lens[5] = 0
+    spec = synth.small(layout=synth.TND, batch=nb, s1=aslq[-1], aslq=aslq, aslk=[bound] * nb, block_size=16,
+                       sparse_count=64, sparse_mode=3)
+    inp = synth.make_inputs(spec, 9)
+    dev = device_inputs(inp)
+    log("bounded tnd: %d batches, %d rows" % (nb, aslq[-1]))
+    bix = qli_mod().BoundedIndexer(inp["problem"], bound)
+    idx, val = bix.alloc_outputs()
+    bix.run(torch.tensor(lens, dtype=torch.int32, device="cuda"), dev["query"], dev["key"], dev["weights"],
+            dev["q_scale"], dev["k_scale"], dev["block_table"], idx, val,
+            aslq_dev=torch.tensor(aslq, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    p_idx, p_val = planned(inp, dev, lens)
+    assert np.array_equal(idx, p_idx) and np.array_equal(val, p_val)
+    oracle_check(ora, dict(inp, aslk=np.asarray(lens, dtype=np.int32)), idx, val)
+
+
 def test_bounded_tnd_graph_replay(ora):
     """qli_run_bounded_tnd captured once; between replays both the device query
     prefix sums and the key lengths change (rows move between batches, batches
@@ -732,23 +762,25 @@ def test_bounded_aslq_graph_replay(ora):
         oracle_check(ora, dict(sub, aslk=np.asarray(lens, dtype=np.int32)), idx.cpu().numpy(), val.cpu().numpy())
 
 
-def test_bounded_many_batches_table(ora):
-    """More batches than the scoring kernel splits by itself (256): the
-    separate planning kernel writes the item table.  Ragged lengths with
-    empty batches and query counts; bit-identical to qli_plan + qli_run and
-    oracle-checked, twice with different lengths from the same workspace."""
+@pytest.mark.parametrize("nb", [256, 257, 300])
+def test_bounded_many_batches_table(ora, nb):
+    """Around the scoring kernel's own split limit: at 256 batches it plans
+    the items itself, above that the separate planning kernel writes the item
+    table.  Ragged lengths with empty batches and query counts; bit-identical
+    to qli_plan + qli_run and oracle-checked, twice with different lengths
+    from the same workspace."""
     import torch
     rng = np.random.default_rng(5)
-    lens0 = [int(x) for x in rng.integers(0, 3000, size=300)]
+    lens0 = [int(x) for x in rng.integers(0, 3000, size=nb)]
     lens0[7] = 0
     bound = 3000
     # every batch's blocks cover the bound: the lengths below only ever read allocated blocks
-    spec = synth.small(batch=300, s1=2, aslk=[bound] * 300, block_size=32, sparse_count=256, sparse_mode=3)
+    spec = synth.small(batch=nb, s1=2, aslk=[bound] * nb, block_size=32, sparse_count=256, sparse_mode=3)
     inp = synth.make_inputs(spec, 12)
     dev = device_inputs(inp)
     bix = qli_mod().BoundedIndexer(inp["problem"], bound)
-    for lens, aslq in ((lens0, None), ([int(x) for x in rng.integers(0, 3001, size=300)],
-                                       [int(x) for x in rng.integers(0, 3, size=300)])):
+    for lens, aslq in ((lens0, None), ([int(x) for x in rng.integers(0, 3001, size=nb)],
+                                       [int(x) for x in rng.integers(0, 3, size=nb)])):
         idx, val = bix.alloc_outputs()
         q = None if aslq is None else torch.tensor(aslq, dtype=torch.int32, device="cuda")
         bix.run(torch.tensor(lens, dtype=torch.int32, device="cuda"), dev["query"], dev["key"], dev["weights"],
