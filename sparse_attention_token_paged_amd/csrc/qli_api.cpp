@@ -108,14 +108,15 @@ void add_values_region(const qli_problem& p, PlanHeader& h) {
 
 // Decode chunk for row groups with visible maxima maxv (all alike when
 // equal): the smallest multiple of 128 entries for which the items fit the
-// decode kernel's resident workgroups on one MI355X (256 CUs x 3) in a
-// single round; for equal groups, a longer chunk if it lowers the keys of the
-// busiest CU, the items being dealt evenly over the CUs (e.g. 512 items of
-// 512 keys, 2 per CU, rather than 688 of 384, 3 on most CUs).
+// kernel's resident workgroups on one MI355X (slots: 256 CUs x 3 for the
+// decode kernel) in a single round; for equal groups, a longer chunk if it
+// lowers the keys of the busiest CU, the items being dealt evenly over the
+// CUs (e.g. 512 items of 512 keys, 2 per CU, rather than 688 of 384, 3 on
+// most CUs).
 template <typename ItemsFor>
-int decode_chunk_for(ItemsFor&& items_for, bool equal) {
+int decode_chunk_for(ItemsFor&& items_for, bool equal, int64_t slots = kDecodeSlots) {
   int c = 128;
-  while (c < kMaxChunk && items_for(c) > kDecodeSlots) c += 128;
+  while (c < kMaxChunk && items_for(c) > slots) c += 128;
   if (equal) {
     auto busiest = [&](int cc) { return (items_for(cc) + kCUs - 1) / kCUs * cc; };
     int best = c;
@@ -199,11 +200,14 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   }
   const bool windowed = p.pre_tokens != INT64_MAX || p.next_tokens != INT64_MAX;
 
-  // Tile shape: decode-like problems (few query tokens per sequence) put
-  // 1, 2 or 4 rows in an item so the key chunk is read once for all of
-  // them; prefill-like problems use 8-row tiles.
-  const bool prefill = max_s1b > 4;
-  const int rt = prefill ? 8 : (max_s1b <= 1 ? 1 : (max_s1b <= 2 ? 2 : 4));
+  // Tile shape: items of 1, 2 or 4 rows of one batch (the most a batch has,
+  // up to 4), so the key chunk is read once for all of them; the decode
+  // kernel scores them.  Prefill-like problems take 4-row items too: their
+  // key chunks then follow the same slot-filling rule, which the 8-row tiles
+  // of bounded prefill runs cannot (measured: the 4 x 2048 TND prefill 113
+  // against 123 us, 16 sequences of 16 tokens over 8192 keys 28 against
+  // 107 us, with the same bits).
+  const int rt = max_s1b <= 1 ? 1 : (max_s1b <= 2 ? 2 : 4);
 
   // A group's items cover the entries [start, start + maxv) that some row of
   // it sees (start: the smallest lo rounded down to a 64-entry tile).
@@ -233,11 +237,10 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
     r = e;
   }
 
-  // Chunk size.  Prefill items walk up to kMaxChunk entries in 64-entry
-  // tiles; decode chunks follow decode_chunk.  Both write every score densely.
+  // Chunk size: decode_chunk (items fill the resident decode workgroups).
   const int k = p.sparse_count;
-  int chunk = kMaxChunk;
-  if (!prefill) {
+  int chunk;
+  {
     std::vector<int32_t> maxv;
     bool equal = !groups.empty();
     for (const Group& g : groups) {
@@ -319,11 +322,10 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
       base.lo[u] = 0;
       base.cand_off[u] = -1;
     }
-    if (!prefill)
-      for (int u = 0; u < g.nrows; u++) {
-        base.vis[u] = out.rows[g.row0 + u].vis;
-        base.lo[u] = out.rows[g.row0 + u].lo;
-      }
+    for (int u = 0; u < g.nrows; u++) {
+      base.vis[u] = out.rows[g.row0 + u].vis;
+      base.lo[u] = out.rows[g.row0 + u].lo;
+    }
     if (g.maxv == 0) {
       base.flags = kItemPad;
       out.items.push_back(base);
@@ -334,11 +336,9 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
       it.key0 = g.start + c0;
       it.nkeys = std::min(chunk, g.maxv - c0);
       it.flags = c0 == 0 ? kItemPad : 0;
-      if (!prefill) {
-        for (int u = 0; u < g.nrows; u++) {
-          const RowInfo& ri = out.rows[g.row0 + u];
-          if (ri.ws_off >= 0) it.cand_off[u] = ri.ws_off + it.key0 - ri.lo;
-        }
+      for (int u = 0; u < g.nrows; u++) {
+        const RowInfo& ri = out.rows[g.row0 + u];
+        if (ri.ws_off >= 0) it.cand_off[u] = ri.ws_off + it.key0 - ri.lo;
       }
       out.items.push_back(it);
     }
@@ -347,7 +347,7 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   // the same visible maximum, so an item's batch, key range and rows follow
   // from its position, and the kernel can start its block-table and query
   // loads without waiting for the item.  They keep batch-major order.
-  bool regular = !prefill && !windowed && p.layout_query == QLI_LAYOUT_BSND && p.batch > 0 &&
+  bool regular = !windowed && p.layout_query == QLI_LAYOUT_BSND && p.batch > 0 &&
                  (int64_t)groups.size() == p.batch;
   for (int b = 0; regular && b < p.batch; b++) {
     const Group& g = groups[b];
@@ -373,7 +373,7 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   // ws_index_offset + 4e (merge_start is a multiple of 4 elements).
   h.ws_index_offset = align16(ws * 4) - merge_start * 4;
   h.workspace_bytes = n_pass1 < out.select.size() ? align16(ws * 4) + (ws - merge_start) * 4 : ws * 4;
-  h.kind = prefill ? kKindPrefill : kKindDecode;
+  h.kind = kKindDecode;
   h.rows_per_item = rt;
   h.n_items = (int32_t)out.items.size();
   h.n_select = (int32_t)n_pass1;
@@ -528,12 +528,15 @@ int bounded_geometry_scores(const qli_problem& p, int64_t max_len, Bounded& g) {
   h.kind = prefill ? kKindPrefill : kKindDecode;
   h.rows_per_item = prefill ? 8 : (p.s1 <= 1 ? 1 : (p.s1 <= 2 ? 2 : 4));
   if (rows == 0) return QLI_OK;
-  h.chunk = prefill ? kMaxChunk : decode_chunk_equal(p.batch, (int32_t)nmax);
+  // prefill tiles: groups of 8 rows (for TND at most tnd_groups of them),
+  // chunked by the same rule for the prefill kernel's resident workgroups
+  const int64_t tiles = tnd ? tnd_groups(p.batch, p.s1) : (int64_t)p.batch * ((p.s1 + 7) / 8);
+  h.chunk = prefill ? decode_chunk_for([&](int c) { return tiles * ((nmax + c - 1) / c); }, true, kPrefillSlots)
+                    : decode_chunk_equal(p.batch, (int32_t)nmax);
   h.reg_chunks = (int32_t)std::max<int64_t>(1, (nmax + h.chunk - 1) / h.chunk);
   h.reg_rows = p.s1;
   h.reg_maxv = (int32_t)nmax;
-  const int64_t items = tnd ? tnd_groups(p.batch, p.s1) * h.reg_chunks
-                            : (int64_t)p.batch * h.reg_chunks * (prefill ? (p.s1 + 7) / 8 : 1);
+  const int64_t items = (prefill ? tiles : (int64_t)p.batch) * h.reg_chunks;
   if (items > INT32_MAX) return QLI_ERR_SIZE;
   h.n_items = (int32_t)items;
   // TND: the row and group tables follow whatever the selection needs

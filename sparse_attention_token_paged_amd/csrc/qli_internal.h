@@ -20,6 +20,7 @@ constexpr int kTileKeys = 64;    // keys per MFMA tile step (4 n-tiles of 16)
 constexpr int kMaxChunk = 4096;  // keys per work item, upper bound
 constexpr int kCUs = 256;                 // compute units of one MI355X
 constexpr int kDecodeSlots = 3 * kCUs;    // decode workgroups resident at once (3 per CU)
+constexpr int kPrefillSlots = 2 * kCUs;   // prefill-tile workgroups resident at once (2 per CU)
 constexpr int kMaxEntries = 1 << 22;      // compressed entries per sequence (exact reciprocal division)
 constexpr int kMaxItemRows = 4;           // rows carried inline by a decode item
 
