@@ -108,15 +108,14 @@ void add_values_region(const qli_problem& p, PlanHeader& h) {
 
 // Decode chunk for row groups with visible maxima maxv (all alike when
 // equal): the smallest multiple of 128 entries for which the items fit the
-// kernel's resident workgroups on one MI355X (slots: 256 CUs x 3 for the
-// decode kernel) in a single round; for equal groups, a longer chunk if it
-// lowers the keys of the busiest CU, the items being dealt evenly over the
-// CUs (e.g. 512 items of 512 keys, 2 per CU, rather than 688 of 384, 3 on
-// most CUs).
+// decode kernel's resident workgroups on one MI355X (256 CUs x 3) in a
+// single round; for equal groups, a longer chunk if it lowers the keys of the
+// busiest CU, the items being dealt evenly over the CUs (e.g. 512 items of
+// 512 keys, 2 per CU, rather than 688 of 384, 3 on most CUs).
 template <typename ItemsFor>
-int decode_chunk_for(ItemsFor&& items_for, bool equal, int64_t slots = kDecodeSlots) {
+int decode_chunk_for(ItemsFor&& items_for, bool equal) {
   int c = 128;
-  while (c < kMaxChunk && items_for(c) > slots) c += 128;
+  while (c < kMaxChunk && items_for(c) > kDecodeSlots) c += 128;
   if (equal) {
     auto busiest = [&](int cc) { return (items_for(cc) + kCUs - 1) / kCUs * cc; };
     int best = c;
@@ -201,12 +200,11 @@ int build_plan(const qli_problem& p, const int32_t* aslq, const int32_t* aslk, B
   const bool windowed = p.pre_tokens != INT64_MAX || p.next_tokens != INT64_MAX;
 
   // Tile shape: items of 1, 2 or 4 rows of one batch (the most a batch has,
-  // up to 4), so the key chunk is read once for all of them; the decode
-  // kernel scores them.  Prefill-like problems take 4-row items too: their
-  // key chunks then follow the same slot-filling rule, which the 8-row tiles
-  // of bounded prefill runs cannot (measured: the 4 x 2048 TND prefill 113
-  // against 123 us, 16 sequences of 16 tokens over 8192 keys 28 against
-  // 107 us, with the same bits).
+  // up to 4), so the key chunk is read once for all of them.  Prefill-like
+  // problems take 4-row items too, chunked by the same slot-filling rule
+  // (measured against 8-row tiles walking whole rows: the 4 x 2048 TND
+  // prefill 113 against 123 us, 16 sequences of 16 tokens over 8192 keys 28
+  // against 107 us, with the same bits).
   const int rt = max_s1b <= 1 ? 1 : (max_s1b <= 2 ? 2 : 4);
 
   // A group's items cover the entries [start, start + maxv) that some row of
@@ -522,21 +520,23 @@ int bounded_geometry_scores(const qli_problem& p, int64_t max_len, Bounded& g) {
   const int64_t rows = tnd ? (int64_t)p.s1 : (int64_t)p.batch * p.s1;
   const int k = p.sparse_count;
   h.rows = rows;
-  // 8-row prefill tiles as qli_plan would choose for S1 > 4; always for TND,
-  // whose rows per batch are known only on the device
-  const bool prefill = tnd || p.s1 > kMaxItemRows;
-  h.kind = prefill ? kKindPrefill : kKindDecode;
-  h.rows_per_item = prefill ? 8 : (p.s1 <= 1 ? 1 : (p.s1 <= 2 ? 2 : 4));
+  // More than 4 query rows per batch (and TND, whose rows per batch are known
+  // only on the device): groups of 4 rows that follow from the item's
+  // position, each chunked like the decode items of qli_plan, all batches
+  // sized for the bound.  Otherwise decode items derived on the device.
+  const bool tiles = tnd || p.s1 > kMaxItemRows;
+  h.kind = tiles ? kKindTiles : kKindDecode;
+  h.rows_per_item = tiles ? kMaxItemRows : (p.s1 <= 1 ? 1 : (p.s1 <= 2 ? 2 : 4));
   if (rows == 0) return QLI_OK;
-  // prefill tiles: groups of 8 rows (for TND at most tnd_groups of them),
-  // chunked by the same rule for the prefill kernel's resident workgroups
-  const int64_t tiles = tnd ? tnd_groups(p.batch, p.s1) : (int64_t)p.batch * ((p.s1 + 7) / 8);
-  h.chunk = prefill ? decode_chunk_for([&](int c) { return tiles * ((nmax + c - 1) / c); }, true, kPrefillSlots)
-                    : decode_chunk_equal(p.batch, (int32_t)nmax);
+  // TND: at most tnd_groups groups (the real ones, then padding-only ones)
+  const int64_t groups = tnd ? tnd_groups(p.batch, p.s1)
+                             : (int64_t)p.batch * ((p.s1 + kMaxItemRows - 1) / kMaxItemRows);
+  h.chunk = tiles ? decode_chunk_for([&](int c) { return groups * ((nmax + c - 1) / c); }, true)
+                  : decode_chunk_equal(p.batch, (int32_t)nmax);
   h.reg_chunks = (int32_t)std::max<int64_t>(1, (nmax + h.chunk - 1) / h.chunk);
   h.reg_rows = p.s1;
   h.reg_maxv = (int32_t)nmax;
-  const int64_t items = (prefill ? tiles : (int64_t)p.batch) * h.reg_chunks;
+  const int64_t items = (tiles ? groups : (int64_t)p.batch) * h.reg_chunks;
   if (items > INT32_MAX) return QLI_ERR_SIZE;
   h.n_items = (int32_t)items;
   // TND: the row and group tables follow whatever the selection needs

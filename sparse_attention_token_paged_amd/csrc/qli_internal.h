@@ -20,11 +20,14 @@ constexpr int kTileKeys = 64;    // keys per MFMA tile step (4 n-tiles of 16)
 constexpr int kMaxChunk = 4096;  // keys per work item, upper bound
 constexpr int kCUs = 256;                 // compute units of one MI355X
 constexpr int kDecodeSlots = 3 * kCUs;    // decode workgroups resident at once (3 per CU)
-constexpr int kPrefillSlots = 2 * kCUs;   // prefill-tile workgroups resident at once (2 per CU)
 constexpr int kMaxEntries = 1 << 22;      // compressed entries per sequence (exact reciprocal division)
 constexpr int kMaxItemRows = 4;           // rows carried inline by a decode item
 
-enum PlanKind : int32_t { kKindDecode = 0, kKindPrefill = 1 };
+// kKindDecode: items of 1, 2 or 4 rows from a plan's table, a device-built
+// table or the scoring kernel's own split.  kKindTiles: bounded runs of more
+// than 4 query rows per batch (and TND), whose 4-row groups follow from the
+// item's position.  One kernel scores both.
+enum PlanKind : int32_t { kKindDecode = 0, kKindTiles = 1 };
 enum ItemFlags : int32_t { kItemPad = 1 };
 
 struct PlanHeader {
@@ -159,16 +162,16 @@ static_assert(sizeof(Item) == 96, "item layout");
 // actual_seq_lengths_query, before the scoring kernel:
 //   rows_end[B]          running maximum of the prefix sums clamped to [0, T]:
 //                        batch b owns rows [rows_end[b-1], rows_end[b])
-//   group_start[B + 1]   8-row groups of the batches before b
+//   group_start[B + 1]   4-row groups of the batches before b
 //   group_batch[groups]  batch of each group, -1 past the last real group
 //   row_batch[T]         batch of each row, -1 for rows past rows_end[B-1]
-// groups = T / 8 + B + 2 bounds the real groups (at most T/8 + B) plus the
+// groups = T / 4 + B + 2 bounds the real groups (at most T/4 + B) plus the
 // groups of rows that belong to no batch (padding only).
 constexpr int kTndMaxBatch = 4096;  // the table kernel keeps both prefix tables in LDS
 struct TndTables {
   int64_t rows_end, group_start, group_batch, row_batch, total;  // element offsets, element count
 };
-inline int64_t tnd_groups(int64_t batch, int64_t t) { return t / 8 + batch + 2; }
+inline int64_t tnd_groups(int64_t batch, int64_t t) { return t / kMaxItemRows + batch + 2; }
 inline TndTables tnd_tables(int64_t batch, int64_t t) {
   TndTables x;
   x.rows_end = 0;

@@ -4,17 +4,16 @@
 // section 功能说明: score = sum_g W[g] * ReLU(ScaleQ[g] * ScaleK[s] * Q[g].K[s]),
 // then the Top-k key indices per query token.
 //
-// Stage 1 scores every visible (row, key) pair of a plan's work items:
-//   * score_kernel (prefill-shaped items of 8 rows) walks the item's key
-//     chunk in tiles of 64 entries, gathered through block_table with
-//     16-byte loads (8 lanes per 128-byte key row, so every row is one fully
-//     used cache line) into a double-buffered, XOR-swizzled LDS tile;
-//   * score_decode_kernel (items of 1, 2 or 4 rows of one batch) streams the
-//     chunk through a 3-stage LDS ring filled by direct-to-LDS loads, so the
-//     rows share every key byte read from HBM; its waves raise their issue
-//     priority while behind in their item, so the workgroups sharing a CU
-//     keep pace instead of finishing in dispatch order;
-//   * both: int8 keys use v_mfma_i32_16x16x64_i8 (exact int32 dots), e4m3fn
+// Stage 1 scores every visible (row, key) pair of the work items:
+//   * score_decode_kernel takes items of 1, 2 or 4 rows of one batch (from a
+//     plan's table, a device-built table, its own split of bounded decode, or
+//     for bounded runs of more rows 4-row groups that follow from the item's
+//     position) and streams the item's key chunk through a 3-stage LDS ring
+//     filled by direct-to-LDS loads, so the rows share every key byte read
+//     from HBM; its waves raise their issue priority while behind in their
+//     item, so the workgroups sharing a CU keep pace instead of finishing in
+//     dispatch order;
+//   * int8 keys use v_mfma_i32_16x16x64_i8 (exact int32 dots), e4m3fn
 //     keys v_mfma_f32_16x16x128_f8f6f4; the 64 query heads of a row are the
 //     M dimension (4 tiles of 16), 16 keys the N dimension, D=128 the K one;
 //   * fused epilogue: ScaleQ is folded into W once per row (w' = W*ScaleQ,
@@ -66,7 +65,9 @@ struct ScoreParams {
   const int32_t* n_items_dev;  // bounded decode: the item count the device planner wrote (else null)
   int32_t plan_batches;        // bounded decode planned in the kernel: the batch count (else 0)
   int32_t chunk;          // keys per item
-  int32_t reg_chunks, reg_rows, reg_maxv;  // regular decode plans (0: not regular)
+  int32_t reg_chunks, reg_rows, reg_maxv;  // regular decode plans (0: not regular); bounded tiles
+  int32_t tiles;          // bounded runs of 4-row groups by position: item p is chunk p % reg_chunks
+                          //   of group p / reg_chunks (BSND: reg_rows rows per batch; TND: the tables)
   const RowInfo* rinfo;   // the plan's row table
   const uint8_t* query;
   const uint8_t* key;
@@ -246,332 +247,6 @@ __device__ __forceinline__ void load_wq(const ScoreParams& P, int64_t r, int q, 
   }
 }
 
-template <int QK, int RW, int WPR, bool DUMP>
-__global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(RW == 1 ? 4 : 2)))
-void score_kernel(ScoreParams P) {
-  static_assert(WPR == 1, "each wave scores all four n-tiles of a tile");
-  const RowInfo* rinfo = P.rinfo;
-
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kTileKeys * kDim];
-  __shared__ float lds_sk[2][kTileKeys];
-  __shared__ int32_t lds_blk[kMaxChunk / 16 + 2];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int q = lane >> 4;
-  const int c16 = lane & 15;
-  const int k = P.k;
-
-  // Persistent workgroups: in round t, workgroup b takes item t*G + b (t
-  // even) or t*G + G-1-b (t odd) of the work-sorted item list, which
-  // balances the rounds.  Positions grow with t, so the first one past the
-  // end ends the loop.
-  const int G = gridDim.x;
-  auto pos_of = [&](int t) { return t * G + ((t & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x); };
-  for (int round = 0;; round++) {
-  const int pos = pos_of(round);
-  if (pos >= P.n_items) break;  // uniform
-  // Without a plan (key lengths on the device: aslk set) the item follows
-  // from its position: chunk pos % reg_chunks of an 8-row group.  BSND (all
-  // reg_rows query rows of every batch active): group (pos / reg_chunks) %
-  // groups of batch pos / (reg_chunks * groups).  TND (rows_end set): group
-  // pos / reg_chunks in the order of the row and group tables; groups past
-  // the real ones cover the rows that belong to no batch (padding only).
-  // Rows' visible counts follow from the batch's length, clamped to the
-  // bound, and a row that sees more than k entries stages its scores at
-  // r * bstride of the workspace.  With a plan, the item and the rows come
-  // from its tables.
-  Item it;
-  int64_t skb = 0;
-  int rstart = 0, s1b = 0;  // bounded: the item's batch starts at row rstart and has s1b rows,
-  int s1q = 0;              //   the first s1q of them used (BSND query counts)
-  if (P.aslk) {
-    int b, g, c;
-    if (P.rows_end) {
-      g = pos / P.reg_chunks;
-      c = pos - g * P.reg_chunks;
-      const int real = P.group_start[P.nbatch];
-      if (g < real) {
-        b = P.group_batch[g];
-        rstart = b > 0 ? P.rows_end[b - 1] : 0;
-        s1b = P.rows_end[b] - rstart;
-        g -= P.group_start[b];
-      } else {
-        b = -1;
-        rstart = P.nbatch > 0 ? P.rows_end[P.nbatch - 1] : 0;
-        s1b = P.trows - rstart;
-        g -= real;
-      }
-    } else {
-      const int groups = (P.reg_rows + 7) / 8;
-      b = pos / (P.reg_chunks * groups);
-      const int rem = pos - b * P.reg_chunks * groups;
-      g = rem / P.reg_chunks;
-      c = rem - g * P.reg_chunks;
-      rstart = b * P.reg_rows;
-      s1b = P.reg_rows;
-    }
-    s1q = P.aslq_bsnd && b >= 0 ? min(max(P.aslq_bsnd[b], 0), s1b) : s1b;
-    skb = b >= 0 ? min<int64_t>(max(P.aslk[b], 0), P.max_len) : 0;
-    it.batch = b;
-    it.row0 = rstart + 8 * g;
-    it.nrows = max(0, min(8, s1b - 8 * g));
-    int maxv = 0;
-    for (int u = 0; u < it.nrows && b >= 0 && 8 * g + u < s1q; u++)
-      maxv = max(maxv, (int)visible_entries(P.mode, P.cmp, skb, s1q, 8 * g + u));
-    it.key0 = c * P.chunk;
-    it.nkeys = min(P.chunk, maxv - it.key0);
-    it.flags = c == 0 ? kItemPad : 0;
-  } else {
-    it = P.items[pos];
-  }
-  // Row r sees entries [lo, hi): from the plan, or [0, visible count) when
-  // bounded (no window there).
-  auto row_range = [&](int64_t r, int& lo) __attribute__((always_inline)) {
-    if (!P.aslk) {
-      lo = rinfo[r].lo;
-      return rinfo[r].vis;
-    }
-    lo = 0;
-    return it.batch < 0 || r - rstart >= s1q ? 0 : (int)visible_entries(P.mode, P.cmp, skb, s1q, r - rstart);
-  };
-
-  // Rows that see fewer than k entries: slots count..k-1 are -1 / -inf.
-  if (it.flags & kItemPad) {
-    for (int u = 0; u < it.nrows; u++) {
-      const int64_t r = it.row0 + u;
-      int lo;
-      const int cnt = row_range(r, lo) - lo;
-      if (cnt >= k) continue;
-      for (int pos = cnt + tid; pos < k; pos += kScoreThreads) {
-        P.idx_out[r * k + pos] = -1;
-        if (P.val_out) P.val_out[r * k + pos] = -INFINITY;
-      }
-    }
-  }
-  if (it.nkeys <= 0) continue;  // uniform across the workgroup
-
-  const int bs = P.block_size;
-  const int key0 = it.key0;
-  const int kend = key0 + it.nkeys;
-  const int fb = key0 / bs;
-  const int nblk = (kend - 1) / bs - fb + 1;
-  {
-    const int32_t* bt = P.block_table + (int64_t)it.batch * P.max_blocks + fb;
-    for (int t = tid; t < nblk; t += kScoreThreads) lds_blk[t] = bt[t];
-  }
-
-  // This wave's rows: query fragments and folded weights w' = W * ScaleQ.
-  const int wr = wave / WPR;
-  const int wk = wave % WPR;
-  bool rok[RW];
-  int64_t rowid[RW];
-  int rvis[RW], rlo[RW];  // the row sees entries [rlo, rvis)
-  int64_t rws[RW];
-  Frag qa[RW][4];
-  float wq[RW][16];
-#pragma unroll
-  for (int rr = 0; rr < RW; rr++) {
-    const int u = wr * RW + rr;
-    rok[rr] = u < it.nrows;
-    const int64_t r = it.row0 + (rok[rr] ? u : 0);
-    rowid[rr] = r;
-    if (P.aslk) {
-      int lo;
-      const int v = row_range(r, lo);
-      rvis[rr] = rok[rr] ? v : 0;
-      rlo[rr] = 0;
-      rws[rr] = v > k ? r * P.bstride : -1;
-    } else {
-      const RowInfo ri = rinfo[r];
-      rvis[rr] = rok[rr] ? ri.vis : 0;
-      rlo[rr] = rok[rr] ? ri.lo : 0;
-      rws[rr] = ri.ws_off;
-    }
-    const uint8_t* qrow = P.query + r * (kHeads * kDim);
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-      const uint8_t* qh = qrow + (16 * m + c16) * kDim;
-      qa[rr][m].lo = *reinterpret_cast<const v4i*>(qh + 16 * chunk_lo<QK>(q));
-      qa[rr][m].hi = *reinterpret_cast<const v4i*>(qh + 16 * chunk_hi<QK>(q));
-    }
-    load_wq<QK>(P, r, q, wq[rr]);
-  }
-
-  // Loader: thread tid fetches two 16-byte pieces of each 64-key tile, at LDS
-  // bytes tid*16 and 4096 + tid*16, i.e. key rows tid/8 and 32 + tid/8, physical
-  // chunk tid%8.  The logical chunk stored there is XOR-swizzled with bits 1..3
-  // of the key row so that the MFMA-layout reads (16 rows, same chunk) hit
-  // distinct banks.  Block / slot positions advance incrementally per tile.
-  // Two register sets hold the tiles in flight (tile j uses set j % 2); the
-  // ScaleK bits stay raw until the stash so no wait is forced at issue time.
-  const int cfetch = (tid & 7) ^ ((tid >> 4) & 7);
-  int bi[2], slot[2];
-#pragma unroll
-  for (int p = 0; p < 2; p++) {
-    const int j = key0 + 32 * p + (tid >> 3);
-    bi[p] = j / bs - fb;
-    slot[p] = j % bs;
-  }
-  int sbi = 0, sslot = 0;
-  if (tid < kTileKeys) {
-    const int j = key0 + tid;
-    sbi = j / bs - fb;
-    sslot = j % bs;
-  }
-  int4 kr[2][2];
-  uint32_t skr[2] = {0u, 0u};
-  lds_barrier();  // lds_blk is ready; the row loads above stay in flight
-
-  auto fetch = [&](int t, auto set_) __attribute__((always_inline)) {
-    constexpr int S = decltype(set_)::value;
-    const int tb = key0 + t * kTileKeys;
-#pragma unroll
-    for (int p = 0; p < 2; p++) {
-      const int j = tb + 32 * p + (tid >> 3);
-      if (j < kend) {
-        const uint8_t* src = P.key + (int64_t)lds_blk[bi[p]] * P.stride + slot[p] * kDim + cfetch * 16;
-        kr[S][p] = *reinterpret_cast<const int4*>(src);
-      } else {
-        kr[S][p] = make_int4(0, 0, 0, 0);
-      }
-      slot[p] += kTileKeys;
-      while (slot[p] >= bs) {
-        slot[p] -= bs;
-        bi[p]++;
-      }
-    }
-    if (tid < kTileKeys) {
-      const int j = tb + tid;
-      skr[S] = j < kend ? load_scale_bits<QK>(P.k_scale, (int64_t)lds_blk[sbi] * bs + sslot) : 0u;
-      sslot += kTileKeys;
-      while (sslot >= bs) {
-        sslot -= bs;
-        sbi++;
-      }
-    }
-  };
-  auto stash = [&](int s, auto set_) __attribute__((always_inline)) {
-    constexpr int S = decltype(set_)::value;
-    int4* dst = reinterpret_cast<int4*>(&lds_k[s][0]);
-    dst[tid] = kr[S][0];
-    dst[kScoreThreads + tid] = kr[S][1];
-    if (tid < kTileKeys) lds_sk[s][tid] = scale_from_bits<QK>(skr[S]) * sk_scale<QK>();
-  };
-
-  // One 64-key tile: for each n-tile the B fragment is read once and feeds
-  // both rows; each row's four n-tile partials are combined with one
-  // reduce_scatter4, after which lane l holds key tb + l.  Direct-output rows
-  // store 64 consecutive slots per tile with no divergent branch (keys past
-  // the row's visible count get the padding values).
-  auto compute = [&](int t, int s) __attribute__((always_inline)) {
-    const int tb = key0 + t * kTileKeys;
-    float part[RW][4];
-#pragma unroll
-    for (int n = 0; n < 4; n++) {
-      const int kk = n * 16 + c16;
-      const uint8_t* krow = &lds_k[s][kk * kDim];
-      const int sw = (kk >> 1) & 7;
-      Frag b;
-      b.lo = *reinterpret_cast<const v4i*>(krow + ((chunk_lo<QK>(q) ^ sw) << 4));
-      b.hi = *reinterpret_cast<const v4i*>(krow + ((chunk_hi<QK>(q) ^ sw) << 4));
-#pragma unroll
-      for (int rr = 0; rr < RW; rr++) {
-        float acc = 0.f;
-        v4i di[4];
-        v4f df[4];
-        if constexpr (QK == QLI_QK_INT8) {
-#pragma unroll
-          for (int m = 0; m < 4; m++) {
-            di[m] = v4i{0, 0, 0, 0};
-            di[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[rr][m].lo, b.lo, di[m], 0, 0, 0);
-            di[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[rr][m].hi, b.hi, di[m], 0, 0, 0);
-          }
-#pragma unroll
-          for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-              acc = __builtin_fmaf(wq[rr][4 * m + i], relu_bits(di[m][i]), acc);
-        } else {
-          const v8i bb = __builtin_shufflevector(b.lo, b.hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int m = 0; m < 4; m++) {
-            const v8i aa = __builtin_shufflevector(qa[rr][m].lo, qa[rr][m].hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            df[m] = v4f{0.f, 0.f, 0.f, 0.f};
-            // format 0 = fp8 e4m3 for both operands; scale arguments 0 select the unscaled form
-            df[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa, bb, df[m], 0, 0, 0, 0, 0, 0);
-          }
-#pragma unroll
-          for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-              acc = __builtin_fmaf(wq[rr][4 * m + i], __builtin_fmaxf(df[m][i], 0.f), acc);
-        }
-        part[rr][n] = acc;
-        if constexpr (DUMP) {
-          const int64_t r = rowid[rr];
-          const int jd = tb + kk;
-          if (rok[rr] && r >= P.d_row0 && r < P.d_row1 && jd >= rlo[rr] && jd < rvis[rr] && jd < P.d_cols) {
-            const int64_t base = (r - P.d_row0) * kHeads;
-#pragma unroll
-            for (int m = 0; m < 4; m++)
-#pragma unroll
-              for (int i = 0; i < 4; i++) {
-                const int64_t o = (base + 16 * m + 4 * q + i) * P.d_cols + jd;
-                if constexpr (QK == QLI_QK_INT8)
-                  static_cast<int32_t*>(P.dots)[o] = di[m][i];
-                else
-                  static_cast<float*>(P.dots)[o] = df[m][i];
-              }
-          }
-        }
-      }
-    }
-    const int j = tb + lane;
-    const float skv = lds_sk[s][lane];
-#pragma unroll
-    for (int rr = 0; rr < RW; rr++) {
-      const float score = reduce_scatter4(part[rr][0], part[rr][1], part[rr][2], part[rr][3]) * skv;
-      if (!rok[rr]) break;  // uniform: valid rows of a wave are a prefix
-      const int64_t r = rowid[rr];
-      const int e = j - rlo[rr];  // position in the row's visible range
-      const bool live = e >= 0 && j < rvis[rr];
-      if (rws[rr] >= 0) {  // uniform: the row stages every score for a selection
-        if (live) P.ws[rws[rr] + e] = score;
-      } else if (j < kend && e >= 0 && e < k) {  // a row's k slots only
-        P.idx_out[r * k + e] = live ? j : -1;
-        if (P.val_out) P.val_out[r * k + e] = live ? score : -INFINITY;
-      }
-      if constexpr (DUMP) {
-        if (live && r >= P.d_row0 && r < P.d_row1 && j < P.d_cols) P.dscores[(r - P.d_row0) * P.d_cols + j] = score;
-      }
-    }
-  };
-
-  // Pipeline: LDS stages alternate per tile; while tile t is computed, the
-  // loads of tiles t+1 and t+2 are in flight in the two register sets.
-  using Set0 = std::integral_constant<int, 0>;
-  using Set1 = std::integral_constant<int, 1>;
-  const int ntiles = (it.nkeys + kTileKeys - 1) / kTileKeys;
-  fetch(0, Set0{});
-  if (ntiles > 1) fetch(1, Set1{});
-  stash(0, Set0{});
-  if (ntiles > 2) fetch(2, Set0{});
-  lds_barrier();
-  auto step = [&](int t, auto set_next) __attribute__((always_inline)) {
-    // set_next holds tile t+1; after its stash it receives tile t+3
-    compute(t, t & 1);
-    if (t + 1 < ntiles) stash((t + 1) & 1, set_next);
-    if (t + 3 < ntiles) fetch(t + 3, set_next);
-    lds_barrier();  // orders the LDS tiles only: the fetches of tiles t+2, t+3 stay in flight
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, Set1{});
-    if (t + 1 < ntiles) step(t + 1, Set0{});
-  }
-  }  // rounds (the last tile's barrier leaves the LDS free for the next item)
-}
 
 // ---------------------------------------------------------------------------
 // Shared pieces: lane-group reductions, order keys, LDS-DMA, block selection
@@ -909,8 +584,9 @@ __device__ __forceinline__ void select_topk_global(const float* src, int n, int 
 // arithmetic is exact); two stages are in flight while one is computed.
 // Each wave scores its row against its n-tiles of the stage:
 //   RT = 4: all 8 n-tiles, RT = 2: 4 n-tiles, RT = 1: 2 n-tiles.
-template <int QK, int RT, bool DUMP>
+template <int QK, int RT, bool DUMP, bool TILES = false>
 __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams P) {
+  static_assert(!TILES || (RT == kMaxItemRows && !DUMP), "4-row groups of bounded runs, no dump");
   constexpr int SC = 128;                     // entries per LDS stage
   constexpr int NSTAGE = 3;
   constexpr int WPR = 4 / RT;                 // waves per row
@@ -934,7 +610,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   // takes item t*G + b (t even) or t*G + G-1-b (t odd).
   const int G = gridDim.x;
   auto pos_of = [&](int t) { return t * G + ((t & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x); };
-  const bool reg = P.reg_chunks > 0;
+  const bool reg = !TILES && P.reg_chunks > 0;
   const int bs = P.block_size;
   const int u = wave / WPR;  // this wave's row of the item
   const int sub = wave % WPR;
@@ -1072,7 +748,62 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   // stages 0 and 1.  False for an item without keys (padding only).
   auto begin = [&](int pos) __attribute__((always_inline)) {
     const Item* itp = P.items + pos;  // a plan's table or the one the bounded run built on the device
-    if (P.plan_batches) {
+    if constexpr (TILES) {
+      // bounded runs of 4-row groups: chunk pos % reg_chunks of group
+      // pos / reg_chunks (BSND: ceil(reg_rows / 4) groups per batch; TND:
+      // through the tables, the groups past the real ones covering the rows
+      // that belong to no batch, which only receive padding)
+      int g = pos / P.reg_chunks;
+      key0 = (pos - g * P.reg_chunks) * P.chunk;
+      int b, rstart, s1b;
+      if (P.rows_end) {
+        const int real = P.group_start[P.nbatch];
+        if (g < real) {
+          b = P.group_batch[g];
+          rstart = b > 0 ? P.rows_end[b - 1] : 0;
+          s1b = P.rows_end[b] - rstart;
+          g -= P.group_start[b];
+        } else {
+          b = -1;
+          rstart = P.nbatch > 0 ? P.rows_end[P.nbatch - 1] : 0;
+          s1b = P.trows - rstart;
+          g -= real;
+        }
+      } else {
+        const int per = (P.reg_rows + kMaxItemRows - 1) / kMaxItemRows;
+        b = g / per;
+        g -= b * per;
+        rstart = b * P.reg_rows;
+        s1b = P.reg_rows;
+      }
+      // query rows of the batch in use (BSND counts), its clamped key length
+      const int s1q = P.aslq_bsnd && b >= 0 ? min(max(P.aslq_bsnd[b], 0), s1b) : s1b;
+      const int64_t skb = b >= 0 ? min<int64_t>(max(P.aslk[b], 0), P.max_len) : 0;
+      batch = b;
+      row0 = rstart + kMaxItemRows * g;
+      nrows = max(0, min(kMaxItemRows, s1b - kMaxItemRows * g));
+      auto vis_of = [&](int uu) {
+        const int i = kMaxItemRows * g + uu;
+        return b >= 0 && i < s1q ? (int)visible_entries(P.mode, P.cmp, skb, s1q, i) : 0;
+      };
+      int maxv = 0;
+      for (int uu = 0; uu < nrows; uu++) maxv = max(maxv, vis_of(uu));
+      nkeys = min(P.chunk, maxv - key0);
+      if (key0 == 0)  // the group's first chunk pads its rows
+        for (int uu = 0; uu < nrows; uu++) {
+          const int64_t rr = row0 + uu;
+          for (int e = vis_of(uu) + tid; e < k; e += kScoreThreads) {
+            P.idx_out[rr * k + e] = -1;
+            if (P.val_out) P.val_out[rr * k + e] = -INFINITY;
+          }
+        }
+      if (nkeys <= 0) return false;  // uniform across the workgroup
+      rok = u < nrows;
+      r = row0 + (rok ? u : 0);
+      rvis = rok ? vis_of(u) : 0;
+      rlo = 0;
+      coff = rvis > k ? r * P.bstride + key0 : -1;
+    } else if (P.plan_batches) {
       // bounded decode planned in the kernel: the thread of the batch whose
       // items hold pos publishes the item; the ring is free here
       if (tid < P.plan_batches && pos >= my_first && pos < my_first + my_n) {
@@ -1132,7 +863,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     const int32_t* bt = P.block_table + (int64_t)batch * P.max_blocks + fb;
     const int bt0 = tid < nblk ? bt[tid] : 0;
     const int bt1 = tid + kScoreThreads < nblk ? bt[tid + kScoreThreads] : 0;
-    if (!P.plan_batches) {
+    if (!TILES && !P.plan_batches) {
       rok = u < nrows;
       r = row0 + (rok ? u : 0);
       rvis = rok ? itp->vis[u] : 0;
@@ -1245,7 +976,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
 
 
   int n_items = P.n_items_dev ? *P.n_items_dev : P.n_items;
-  if (P.plan_batches) n_items = plan_items();
+  if (!TILES && P.plan_batches) n_items = plan_items();
   for (int round = 0;; round++) {
   const int pos = pos_of(round);
   if (pos >= n_items) break;  // uniform; positions grow with the round
@@ -1555,24 +1286,22 @@ hipError_t launch(void (*kernel)(Args...), dim3 grid, dim3 block, hipStream_t st
 
 template <int QK, bool DUMP>
 hipError_t launch_score_t(const ScoreParams& P, const PlanHeader* h, hipStream_t st) {
-  const dim3 grid(h->n_items), block(kScoreThreads);
-  if (h->kind == kKindDecode) {
-    auto go = [&](void (*kern)(ScoreParams)) {
-      const int slots = resident_slots(reinterpret_cast<const void*>(kern), kScoreThreads);
-      const dim3 pgrid(slots > 0 ? std::min<int>(h->n_items, slots) : h->n_items);
-      return launch(kern, pgrid, block, st, P);
-    };
-    switch (h->rows_per_item) {
-      case 1: return go(score_decode_kernel<QK, 1, DUMP>);
-      case 2: return go(score_decode_kernel<QK, 2, DUMP>);
-      case 4: return go(score_decode_kernel<QK, 4, DUMP>);
-      default: return hipErrorInvalidValue;
-    }
+  const dim3 block(kScoreThreads);
+  auto go = [&](void (*kern)(ScoreParams)) {
+    const int slots = resident_slots(reinterpret_cast<const void*>(kern), kScoreThreads);
+    const dim3 pgrid(slots > 0 ? std::min<int>(h->n_items, slots) : h->n_items);
+    return launch(kern, pgrid, block, st, P);
+  };
+  if (P.tiles) {  // bounded runs of 4-row groups (never dumped)
+    if constexpr (DUMP) return hipErrorInvalidValue;
+    else return go(score_decode_kernel<QK, kMaxItemRows, false, true>);
   }
-  if (h->rows_per_item != 8) return hipErrorInvalidValue;
-  const int slots = resident_slots(reinterpret_cast<const void*>(score_kernel<QK, 2, 1, DUMP>), kScoreThreads);
-  const dim3 pgrid(slots > 0 ? std::min<int>(h->n_items, slots) : h->n_items);
-  return launch(score_kernel<QK, 2, 1, DUMP>, pgrid, block, st, P);
+  switch (h->rows_per_item) {
+    case 1: return go(score_decode_kernel<QK, 1, DUMP>);
+    case 2: return go(score_decode_kernel<QK, 2, DUMP>);
+    case 4: return go(score_decode_kernel<QK, 4, DUMP>);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -1634,6 +1363,7 @@ int launch_score(const RunArgs& a, bool dump) {
   P.reg_chunks = h->reg_chunks;
   P.reg_rows = h->reg_rows;
   P.reg_maxv = h->reg_maxv;
+  P.tiles = h->kind == kKindTiles;
   P.query = static_cast<const uint8_t*>(a.query);
   P.key = static_cast<const uint8_t*>(a.key);
   P.weights = a.weights;
@@ -1964,7 +1694,7 @@ __global__ __launch_bounds__(kTabThreads) void tnd_tables_kernel(const int32_t* 
     __syncthreads();
     const int before = b == 0 ? 0 : (tid > 0 ? s_end[b - 1] : carry_end);
     const int rows_b = b < nb ? end - before : 0;
-    const int grp = block_incl_scan((rows_b + 7) / 8, false, buf) + carry_grp;
+    const int grp = block_incl_scan((rows_b + kMaxItemRows - 1) / kMaxItemRows, false, buf) + carry_grp;
     if (b < nb) s_grp[b + 1] = grp;
     __syncthreads();
     const int last = min(nb - 1, base + kTabThreads - 1);

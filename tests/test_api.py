@@ -392,12 +392,12 @@ def bounded_scores_expected(p, max_len):
 
 def bounded_tnd_workspace_expected(p, max_len):
     """TND: the BSND layout over T rows, then (16-byte aligned) the row and group
-    tables: rows_end[B], group_start[B + 1], group_batch[T // 8 + B + 2] (each
-    padded to 4 elements) and row_batch[T], int32."""
+    tables: rows_end[B], group_start[B + 1], group_batch[T // 4 + B + 2] (4-row
+    groups; each table padded to 4 elements) and row_batch[T], int32."""
     b, t = p["batch"], p["s1"]
     base = bounded_scores_expected(dict(p, batch=1, s1=t), max_len)
     up4 = lambda n: (n + 3) // 4 * 4
-    return (base + 15) // 16 * 16 + 4 * (up4(b) + up4(b + 1) + up4(t // 8 + b + 2) + t)
+    return (base + 15) // 16 * 16 + 4 * (up4(b) + up4(b + 1) + up4(t // 4 + b + 2) + t)
 
 
 @pytest.mark.parametrize("b,t,k,max_len", [(3, 40, 256, 5000), (1, 7, 2048, 100), (5, 300, 64, 20000)])
