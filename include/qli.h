@@ -150,7 +150,8 @@ typedef struct qli_plan_info {
     int32_t select_rows;     /* rows whose visible count exceeds sparse_count */
     int32_t rows_per_item;
     int32_t keys_per_chunk;
-    int32_t kind;            /* 0: decode-shaped tiles, 1: prefill-shaped tiles */
+    int32_t kind;            /* 0 (qli_plan's items: rows_per_item rows of one batch x a key
+                                chunk); other values are reserved */
     int32_t reserved;
 } qli_plan_info;
 
@@ -244,18 +245,19 @@ int qli_run_stage(const qli_problem *p, const void *plan_host,
  * kernels read the lengths themselves.
  *
  * Scope: qli_run_bounded takes the BSND query layout with every one of the
- * S1 query rows of every batch active (no actual_seq_lengths_query); any S1
- * (decode items for S1 <= 4, 8-row prefill tiles above, as qli_plan
- * chooses).  qli_run_bounded_aslq takes BSND with actual_seq_lengths_query
+ * S1 query rows of every batch active (no actual_seq_lengths_query); any S1.
+ * qli_run_bounded_aslq takes BSND with actual_seq_lengths_query
  * on the device; qli_run_bounded_tnd the TND layout with
  * actual_seq_lengths_query on the device too (batch <= 4096).  No
  * pre_tokens / next_tokens window (QLI_ERR_UNSUPPORTED).  Every other
  * parameter as for qli_plan.
  *
- * Decode problems (BSND, S1 <= 4): a first one-workgroup kernel splits every
- * batch by its own length into items, with the chunk rule of qli_plan, into
- * the workspace; the scoring kernel reads that item table as it reads a
- * plan's, so ragged lengths cost what they cost under qli_plan.
+ * Decode problems (BSND, S1 <= 4): every batch is split by its own length
+ * into items with the chunk rule of qli_plan, by the scoring kernel itself
+ * for up to 256 batches, else by a first one-workgroup kernel into an item
+ * table in the workspace, so ragged lengths cost what they cost under
+ * qli_plan.  More query rows per batch (and TND): groups of 4 rows whose
+ * place follows from the item's position, every batch sized for the bound.
  *
  * qli_bounded_workspace -- workspace bytes that qli_run_bounded needs for
  *   these problem sizes and any key lengths in [0, max_seq_len_key] original
@@ -308,7 +310,7 @@ int qli_run_bounded_aslq(const qli_problem *p, int64_t max_seq_len_key,
  *   in the workspace (the prefix sums are taken as their running maximum
  *   clamped to [0, T], so any contents give a valid partition of the T rows;
  *   rows past the last prefix sum are padding).  Query rows are scored in
- *   8-row tiles within each batch.  Returns QLI_ERR_UNSUPPORTED for BSND or
+ *   4-row groups within each batch.  Returns QLI_ERR_UNSUPPORTED for BSND or
  *   batch > 4096; otherwise as qli_run_bounded.
  */
 int qli_run_bounded_tnd(const qli_problem *p, int64_t max_seq_len_key,
