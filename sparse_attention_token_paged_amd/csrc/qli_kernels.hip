@@ -284,6 +284,17 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t m0) {
 __device__ __forceinline__ void dma2(const void* g, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(m0) : "memory");
 }
+// The same from a workgroup-uniform base (an SGPR pair) plus a 32-bit byte
+// offset per lane.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4s(const void* base, uint32_t off, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(m0) : "memory");
+}
+__device__ __forceinline__ void dma2s(const void* base, uint32_t off, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_ushort %0, %1" ::"v"(off), "s"(base), "s"(m0) : "memory");
+}
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -585,7 +596,10 @@ __device__ __forceinline__ void select_topk_global(const float* src, int n, int 
 // Each wave scores its row against its n-tiles of the stage:
 //   RT = 4: all 8 n-tiles, RT = 2: 4 n-tiles, RT = 1: 2 n-tiles.
 template <int QK, int RT, bool DUMP, bool TILES = false>
-__global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams P) {
+// Three workgroups per CU fit the LDS ring; the register budget follows (the
+// dump instantiations, for parity checks only, keep two).
+__global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(DUMP ? 2 : 3))) void
+score_decode_kernel(ScoreParams P) {
   static_assert(!TILES || (RT == kMaxItemRows && !DUMP), "4-row groups of bounded runs, no dump");
   constexpr int SC = 128;                     // entries per LDS stage
   constexpr int NSTAGE = 3;
@@ -626,6 +640,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   int32_t* oi = nullptr;   // this row's outputs
   float* ov = nullptr;
   bool direct = false;     // the row sees at most k entries: scores go straight to the outputs
+  bool whole = false;      // this item's stages each lie in one block (see issue)
+  uint32_t koff[KLOADS];   // the lane's byte offsets of its stage loads within such a block
+#pragma unroll
+  for (int i = 0; i < KLOADS; i++) {
+    const int kk = 8 * (4 * i + wave) + (lane >> 3);
+    koff[i] = (uint32_t)(kk * kDim + (((lane & 7) ^ ((kk >> 1) & 7)) << 4));
+  }
+  const uint32_t skoff = (uint32_t)((32 * wave + (lane & 31)) * SB);
 
   // Bounded decode planned in the kernel (P.plan_batches > 0, at most one
   // batch per thread): thread t holds batch t's visible maximum my_m (that of
@@ -715,9 +737,33 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
   // Stage loader: wave w's load i fills stage bytes [(4i + w) * 1024, +1024),
   // lane l the 16 bytes at l*16: entry kk = 8(4i + w) + l/8, physical chunk
   // l%8 holding logical chunk (l%8) ^ ((kk>>1)&7) (conflict-free MFMA reads).
+  // When a stage lies in one block (block size a multiple of SC and the
+  // item's chunk starting at a multiple of SC), every load takes the block's
+  // address as a uniform base plus the lane's fixed offset (koff, skoff):
+  // one block-table lookup per stage instead of one per lane and load.  A
+  // last, partial stage then reads past the chunk's end only inside the same
+  // block; those entries are never scored.
   auto issue = [&](int st) __attribute__((always_inline)) {
     const int slot_ = st % NSTAGE;
     const int e_base = key0 + st * SC;
+    if (whole) {
+      const int b = (int)__umulhi((uint32_t)e_base, P.bs_magic);
+      const int blk = __builtin_amdgcn_readfirstlane(lds_bt[b - fb]);
+      const int64_t at = (int64_t)blk * bs + (e_base - b * bs);  // the stage's first entry in the cache
+      const uint8_t* kb = P.key + (int64_t)blk * P.stride + (int64_t)(e_base - b * bs) * kDim;
+#pragma unroll
+      for (int i = 0; i < KLOADS; i++)
+        dma16s(kb, koff[i], __builtin_amdgcn_readfirstlane(lds_addr(&ring[slot_][(4 * i + wave) * 1024])));
+      if (lane < 32) {
+        const uint8_t* sb = static_cast<const uint8_t*>(P.k_scale) + at * SB;
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(&ring_sk[slot_][32 * wave]));
+        if constexpr (SB == 2)
+          dma2s(sb, skoff, m0);
+        else
+          dma4s(sb, skoff, m0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < KLOADS; i++) {
       const int kk = 8 * (4 * i + wave) + (lane >> 3);
@@ -855,6 +901,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreParams
     }
     kend = key0 + nkeys;
     fb = (int)__umulhi((uint32_t)key0, P.bs_magic);
+    whole = (bs % SC) == 0 && (key0 % SC) == 0;
     const int nblk = (int)__umulhi((uint32_t)(kend - 1), P.bs_magic) - fb + 1;
     // Block-table slice (nblk <= kMaxChunk / 16 + 2 <= 2 * kScoreThreads
     // entries): loaded now, written to LDS once the query and weight loads
