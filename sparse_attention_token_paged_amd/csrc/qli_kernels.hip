@@ -635,6 +635,24 @@ score_decode_kernel(ScoreParams P) {
   int64_t r = 0;
   int rvis = 0, rlo = 0;  // this wave's row sees entries [rlo, rvis)
   int64_t coff = -1;
+  // Padding deferred to the item's last stage: rows row0 + u (u < pad_n) get
+  // slots [pad_from[u], k) once that stage's loads have landed, so no later
+  // wait of the item drains these stores (vmcnt counts stores with loads, in
+  // order), and the last stage's compute covers their latency.
+  int pad_n = 0;
+  int pad_from[kMaxItemRows];
+  auto do_pad = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int uu = 0; uu < kMaxItemRows; uu++) {
+      if (uu >= pad_n) break;
+      const int64_t rr = row0 + uu;
+      for (int e = pad_from[uu] + tid; e < k; e += kScoreThreads) {
+        P.idx_out[rr * k + e] = -1;
+        if (P.val_out) P.val_out[rr * k + e] = -INFINITY;
+      }
+    }
+    pad_n = 0;
+  };
   Frag qa[4];
   float wq[16];
   int32_t* oi = nullptr;   // this row's outputs
@@ -719,18 +737,13 @@ score_decode_kernel(ScoreParams P) {
     return plan_sh[7];
   };
 
-  // Rows of an item that see fewer than k entries: slots count..k-1 are -1 / -inf.
-  auto pad = [&](const Item& itp) __attribute__((always_inline)) {
+  // Rows of an item that see fewer than k entries: slots count..k-1 are
+  // -1 / -inf, written by do_pad.
+  auto note_pad = [&](const Item& itp) __attribute__((always_inline)) {
     if (itp.flags & kItemPad) {
-      for (int uu = 0; uu < itp.nrows; uu++) {
-        const int64_t rr = itp.row0 + uu;
-        const int cnt = itp.vis[uu] - itp.lo[uu];
-        if (cnt >= k) continue;
-        for (int e = cnt + tid; e < k; e += kScoreThreads) {
-          P.idx_out[rr * k + e] = -1;
-          if (P.val_out) P.val_out[rr * k + e] = -INFINITY;
-        }
-      }
+      pad_n = itp.nrows;
+#pragma unroll
+      for (int uu = 0; uu < kMaxItemRows; uu++) pad_from[uu] = uu < itp.nrows ? itp.vis[uu] - itp.lo[uu] : k;
     }
   };
 
@@ -835,15 +848,15 @@ score_decode_kernel(ScoreParams P) {
       int maxv = 0;
       for (int uu = 0; uu < nrows; uu++) maxv = max(maxv, vis_of(uu));
       nkeys = min(P.chunk, maxv - key0);
-      if (key0 == 0)  // the group's first chunk pads its rows
-        for (int uu = 0; uu < nrows; uu++) {
-          const int64_t rr = row0 + uu;
-          for (int e = vis_of(uu) + tid; e < k; e += kScoreThreads) {
-            P.idx_out[rr * k + e] = -1;
-            if (P.val_out) P.val_out[rr * k + e] = -INFINITY;
-          }
-        }
-      if (nkeys <= 0) return false;  // uniform across the workgroup
+      if (key0 == 0) {  // the group's first chunk pads its rows
+        pad_n = nrows;
+#pragma unroll
+        for (int uu = 0; uu < kMaxItemRows; uu++) pad_from[uu] = uu < nrows ? vis_of(uu) : k;
+      }
+      if (nkeys <= 0) {  // uniform across the workgroup
+        do_pad();
+        return false;
+      }
       rok = u < nrows;
       r = row0 + (rok ? u : 0);
       rvis = rok ? vis_of(u) : 0;
@@ -870,15 +883,15 @@ score_decode_kernel(ScoreParams P) {
       nrows = P.reg_rows;
       // the row's visible count: 0 past the batch's used rows
       auto vis_of = [&](int uu) { return uu < s1b ? (int)visible_entries(P.mode, P.cmp, skb, s1b, uu) : 0; };
-      if (key0 == 0)  // the batch's first item pads its rows
-        for (int uu = 0; uu < nrows; uu++) {
-          const int64_t rr = row0 + uu;
-          for (int e = vis_of(uu) + tid; e < k; e += kScoreThreads) {
-            P.idx_out[rr * k + e] = -1;
-            if (P.val_out) P.val_out[rr * k + e] = -INFINITY;
-          }
-        }
-      if (nkeys <= 0) return false;  // uniform across the workgroup
+      if (key0 == 0) {  // the batch's first item pads its rows
+        pad_n = nrows;
+#pragma unroll
+        for (int uu = 0; uu < kMaxItemRows; uu++) pad_from[uu] = uu < nrows ? vis_of(uu) : k;
+      }
+      if (nkeys <= 0) {  // uniform across the workgroup
+        do_pad();
+        return false;
+      }
       rok = u < nrows;
       r = row0 + (rok ? u : 0);
       rvis = rok ? vis_of(u) : 0;
@@ -890,14 +903,18 @@ score_decode_kernel(ScoreParams P) {
       nkeys = min(P.chunk, P.reg_maxv - key0);
       row0 = batch * P.reg_rows;
       nrows = P.reg_rows;
+      note_pad(*itp);
     } else {
-      pad(*itp);
+      note_pad(*itp);
       batch = itp->batch;
       key0 = itp->key0;
       nkeys = itp->nkeys;
       row0 = itp->row0;
       nrows = itp->nrows;
-      if (nkeys <= 0) return false;  // uniform across the workgroup
+      if (nkeys <= 0) {  // uniform across the workgroup
+        do_pad();
+        return false;
+      }
     }
     kend = key0 + nkeys;
     fb = (int)__umulhi((uint32_t)key0, P.bs_magic);
@@ -1045,6 +1062,7 @@ score_decode_kernel(ScoreParams P) {
     else
       wait_vm<0>();
     lds_barrier();  // every wave's loads of stage st have landed
+    if (st == nstages - 1 && pad_n > 0) do_pad();
     const int slot_ = st % NSTAGE;
     const int sbase = key0 + st * SC;
     if (rok && sbase < rvis) {
@@ -1060,7 +1078,6 @@ score_decode_kernel(ScoreParams P) {
     lds_barrier();  // the slot is free for stage st + 3
   }
 
-  if (reg) pad(P.items[pos]);
   }  // rounds (the item's last barrier leaves the LDS free for the next one)
 }
 
