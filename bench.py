@@ -725,7 +725,7 @@ def main() -> int:
         achieved = alg["score_kernel"] / (score_avg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["kernel"] = "score_kernel" if info.kind == 1 else "score_decode_kernel"
+    roof["kernel"] = "score_decode_kernel"
     roof["kernel_ms"] = round(score_avg, 5)
     roof["algorithmic_bytes" if not mfma_bound else "algorithmic_ops"] = alg["score_kernel"] if not mfma_bound else alg["ops"]
     roof["traffic"] = traffic_from_profiles(args.workload)

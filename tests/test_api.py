@@ -440,7 +440,7 @@ def test_bounded_rejects_without_launching(qli):
     assert qli.qli_run_bounded_tnd(tnd, bound, fake + 2, *args) == qli.QLI_ERR_ARG
     many = qli.Problem.from_dict(dict(p, layout_query=synth.TND, batch=4097))
     assert qli.qli_bounded_workspace(many, bound)[0] == qli.QLI_ERR_UNSUPPORTED
-    wide = qli.Problem.from_dict(dict(p, s1=5))  # prefill tiles: supported, same workspace layout
+    wide = qli.Problem.from_dict(dict(p, s1=5))  # 4-row position groups: supported, same workspace layout
     assert qli.qli_bounded_workspace(wide, bound) == (qli.QLI_OK, bounded_workspace_expected(dict(p, s1=5), bound))
     a = list(args)
     a[0] = None                                                     # actual_seq_lengths_key

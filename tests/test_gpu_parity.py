@@ -457,7 +457,7 @@ BOUNDED = {
                                  sparse_mode=3, cmp_ratio=4), [40000, 39999]),
     "int8_s3_short": (synth.small(batch=2, s1=3, aslk=[1500] * 2, block_size=32, sparse_count=256,
                                   sparse_mode=3), [1500, 700]),
-    # more than 4 query rows per batch: the prefill tiles (8 rows, key chunks of 4096)
+    # more than 4 query rows per batch: 4-row groups that follow from the item's position
     "int8_s8_prefill": (synth.small(batch=2, s1=8, aslk=[3000] * 2, block_size=64, sparse_count=256,
                                     sparse_mode=3), [3000, 1200]),
     "int8_s13_chunks_merges": (synth.small(batch=2, s1=13, aslk=[20000] * 2, block_size=128, sparse_count=2048,
@@ -592,8 +592,8 @@ def bounded_tnd_run(name, aslq, lens, seed=4):
 @pytest.mark.parametrize("name", list(BOUNDED_TND))
 def test_bounded_tnd_matches_planned(ora, name):
     """qli_run_bounded_tnd (query and key lengths read on the device) against
-    qli_plan + qli_run: bit-identical where the plan also uses the 8-row tiles
-    (some batch has more than 4 rows), else within the parity rule of the
+    qli_plan + qli_run: bit-identical where the plan also takes 4-row items
+    (some batch has at least 3 rows), else within the parity rule of the
     oracle; every row's structure checked."""
     _, aslq, lens = BOUNDED_TND[name]
     log("bounded tnd %s: aslq %s lens %s" % (name, aslq, lens))
@@ -604,7 +604,7 @@ def test_bounded_tnd_matches_planned(ora, name):
     check_structure(idx, val, vis, p["sparse_count"])
     per_batch = np.diff(np.concatenate([[0], aq]))
     sub = dict(inp, aslq=aq, aslk=ak)
-    if per_batch.max() > 4:
+    if per_batch.max() >= 3:
         p_idx, p_val = planned(sub, dev, lens)
         assert np.array_equal(idx, p_idx) and np.array_equal(val, p_val)
     oracle_check(ora, sub, idx, val)
@@ -627,7 +627,7 @@ def test_bounded_tnd_prefix_sums_out_of_contract(ora):
 
 def test_bounded_tnd_most_batches(ora):
     """TND at the table kernel's limit of 4096 batches: 0 to 3 query rows
-    each, one batch of 9 rows (so qli_plan takes the same 8-row tiles), key
+    each, one batch of 9 rows (so qli_plan takes 4-row items too), key
     lengths 0 to 300 with empty batches; bit-identical to qli_plan + qli_run
     and oracle-checked on every row."""
     import torch
@@ -869,7 +869,7 @@ def test_bounded_random(ora, i):
     idx, val = idx.cpu().numpy(), val.cpu().numpy()
     vis = vis_of(ora, inp)
     check_structure(idx, val, vis, p["sparse_count"])
-    tiles_match = spec.layout == synth.BSND or np.diff(np.concatenate([[0], inp["aslq"]])).max() > 4
+    tiles_match = spec.layout == synth.BSND or np.diff(np.concatenate([[0], inp["aslq"]])).max() >= 3
     if tiles_match:
         p_idx, p_val, _ = run_gpu(inp, dev)
         assert np.array_equal(idx, p_idx) and np.array_equal(val, p_val)
