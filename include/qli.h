@@ -306,12 +306,13 @@ int qli_run_bounded_aslq(const qli_problem *p, int64_t max_seq_len_key,
  * qli_run_bounded_tnd -- the same for the TND layout: aslq_dev (device int32[B],
  *   actual_seq_lengths_query as prefix sums, 4-byte aligned) and aslk_dev are
  *   both read on the device, so a graph captured once replays correctly after
- *   either changes.  A first small kernel turns aslq into row and group tables
- *   in the workspace (the prefix sums are taken as their running maximum
+ *   either changes.  The prefix sums are taken as their running maximum
  *   clamped to [0, T], so any contents give a valid partition of the T rows;
- *   rows past the last prefix sum are padding).  Query rows are scored in
- *   4-row groups within each batch.  Returns QLI_ERR_UNSUPPORTED for BSND or
- *   batch > 4096; otherwise as qli_run_bounded.
+ *   rows past the last prefix sum are padding.  Up to 128 batches the kernels
+ *   derive the partition themselves; for more, a first small kernel turns
+ *   aslq into row and group tables in the workspace.  Query rows are scored
+ *   in 4-row groups within each batch.  Returns QLI_ERR_UNSUPPORTED for BSND
+ *   or batch > 4096; otherwise as qli_run_bounded.
  */
 int qli_run_bounded_tnd(const qli_problem *p, int64_t max_seq_len_key,
                         const int32_t *aslq_dev, const int32_t *aslk_dev,

@@ -501,7 +501,7 @@ struct Bounded {
   PlanHeader h;
   int64_t stride, mstride, merge_base;
   int32_t nseg;
-  int64_t tab_off;  // TND: byte offset of the row and group tables in the workspace
+  int64_t tab_off;  // TND of many batches: byte offset of the row and group tables in the workspace, else -1
   int64_t items_off, count_off;  // decode: the device-built item table and its count (-1: none)
   bool plan_in_kernel;           // decode with few batches: the scoring kernel splits the work itself
 };
@@ -516,6 +516,7 @@ int bounded_geometry_scores(const qli_problem& p, int64_t max_len, Bounded& g) {
   if (nmax >= kMaxEntries) return QLI_ERR_SIZE;
   if ((nmax + p.block_size - 1) / p.block_size > p.max_blocks_per_seq) return QLI_ERR_ARG;
   std::memset(&g, 0, sizeof(g));
+  g.tab_off = -1;
   PlanHeader& h = g.h;
   const int64_t rows = tnd ? (int64_t)p.s1 : (int64_t)p.batch * p.s1;
   const int k = p.sparse_count;
@@ -539,9 +540,10 @@ int bounded_geometry_scores(const qli_problem& p, int64_t max_len, Bounded& g) {
   const int64_t items = (tiles ? groups : (int64_t)p.batch) * h.reg_chunks;
   if (items > INT32_MAX) return QLI_ERR_SIZE;
   h.n_items = (int32_t)items;
-  // TND: the row and group tables follow whatever the selection needs
+  // TND of many batches: the row and group tables follow whatever the
+  // selection needs (fewer batches: the kernels derive the partition)
   auto add_tables = [&]() {
-    if (!tnd) return;
+    if (!tnd || p.batch <= kTndInKernelBatches) return;
     g.tab_off = align16(h.workspace_bytes);
     h.workspace_bytes = g.tab_off + 4 * tnd_tables(p.batch, p.s1).total;
   };
@@ -743,7 +745,7 @@ static int run_bounded_common(const qli_problem* p, int64_t max_seq_len_key, con
   if (rc != QLI_OK) return rc;
   if (static_ws && g.h.workspace_bytes > 0 && scratch_address(&a.workspace) != 0) return QLI_ERR_HIP;
   a.sparse_values = values_target(a, a.sparse_values);
-  if (tnd && launch_tnd_tables(a) != 0) return QLI_ERR_HIP;
+  if (tnd && g.tab_off >= 0 && launch_tnd_tables(a) != 0) return QLI_ERR_HIP;
   if (launch_decode_items(a) != 0) return QLI_ERR_HIP;
   if (launch_score(a, false) != 0) return QLI_ERR_HIP;
   if (g.h.n_select > 0 && launch_select(a) != 0) return QLI_ERR_HIP;

@@ -157,9 +157,12 @@ struct Item {
 };
 static_assert(sizeof(Item) == 96, "item layout");
 
-// Bounded TND runs: tables written into the workspace (at byte offset
-// tab_off, int32 elements) by a one-workgroup kernel from the device
-// actual_seq_lengths_query, before the scoring kernel:
+// Bounded TND runs of at most kTndInKernelBatches batches derive the batch
+// partition inside the kernels (the scoring kernel keeps row ends and group
+// starts in LDS, two per lane of a wave; the selection re-derives a row's
+// batch in one wave).  More batches (up to kTndMaxBatch): tables written into
+// the workspace (at byte offset tab_off, int32 elements) by a one-workgroup
+// kernel from the device actual_seq_lengths_query, before the scoring kernel:
 //   rows_end[B]          running maximum of the prefix sums clamped to [0, T]:
 //                        batch b owns rows [rows_end[b-1], rows_end[b])
 //   group_start[B + 1]   4-row groups of the batches before b
@@ -168,6 +171,8 @@ static_assert(sizeof(Item) == 96, "item layout");
 // groups = T / 4 + B + 2 bounds the real groups (at most T/4 + B) plus the
 // groups of rows that belong to no batch (padding only).
 constexpr int kTndMaxBatch = 4096;  // the table kernel keeps both prefix tables in LDS
+// 1 KB of LDS per scoring workgroup, which still fits three per CU
+constexpr int kTndInKernelBatches = 128;
 struct TndTables {
   int64_t rows_end, group_start, group_batch, row_batch, total;  // element offsets, element count
 };
@@ -217,9 +222,10 @@ struct RunArgs {
   int64_t stride = 0, mstride = 0, merge_base = 0;
   int32_t nseg = 0;
   // Bounded TND runs: device actual_seq_lengths_query and the byte offset of
-  // the tables (TndTables) in the workspace.
+  // the tables (TndTables) in the workspace, -1 for none (few batches: the
+  // kernels derive the partition themselves).
   const int32_t* aslq = nullptr;
-  int64_t tab_off = 0;
+  int64_t tab_off = -1;
   // Bounded BSND runs with actual_seq_lengths_query on the device (rows past a
   // batch's count see nothing), else null.
   const int32_t* aslq_bsnd = nullptr;

@@ -78,9 +78,10 @@ struct ScoreParams {
   float* ws;
   int32_t* idx_out;
   float* val_out;
-  const int32_t* rows_end;     // bounded TND: the tables (TndTables), else null
+  const int32_t* rows_end;     // bounded TND of many batches: the tables (TndTables), else null
   const int32_t* group_start;
   const int32_t* group_batch;
+  const int32_t* aslq_tnd;     // bounded TND of few batches: the device prefix sums (tables in LDS), else null
   int32_t nbatch, trows;       //   batches, rows T
   const int32_t* aslk;  // bounded runs: key lengths on the device (else null; decode with a table: null)
   const int32_t* aslq_bsnd;  // bounded BSND: per-batch query counts (else null: all S1 rows used)
@@ -318,6 +319,36 @@ __device__ int block_exclusive_scan(int v, int* tmp) {
   for (int w = 0; w < NW; w++) before += w < wave ? tmp[w] : 0;
   __syncthreads();
   return before + incl - v;
+}
+
+// Bounded TND of at most kTndInKernelBatches batches: the batch partition of
+// the T query rows from the device prefix sums, in one wave.  Batch b owns
+// rows [end(b - 1), end(b)), end the running maximum of the prefix sums
+// clamped to [0, T] (any input then partitions the rows; the first batch
+// starts at row 0, rows from end(nb - 1) on belong to none).  Lane l holds
+// e0 = end(2l) and e1 = end(2l + 1); past the last batch they repeat its end.
+__device__ __forceinline__ void tnd_wave_ends(const int32_t* aslq, int nb, int t, int& e0, int& e1) {
+  static_assert(kTndInKernelBatches == 128, "two batches per lane");
+  const int lane = threadIdx.x & 63;
+  const int b0 = 2 * lane;
+  const int v0 = b0 < nb ? min(max(aslq[b0], 0), t) : 0;
+  const int v1 = b0 + 1 < nb ? min(max(aslq[b0 + 1], 0), t) : 0;
+  int incl = max(v0, v1);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl = max(incl, o);
+  }
+  int before = __shfl_up(incl, 1, 64);  // end of batch 2l - 1
+  if (lane == 0) before = 0;
+  e0 = max(before, v0);
+  e1 = max(e0, v1);
+}
+
+// The value x of batch b (uniform, < 2 * 64) from the pair (x0, x1) that lane
+// b / 2 holds for batches 2l, 2l + 1.
+__device__ __forceinline__ int tnd_pick(int x0, int x1, int b) {
+  return __builtin_amdgcn_readlane((b & 1) ? x1 : x0, b >> 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -612,6 +643,9 @@ score_decode_kernel(ScoreParams P) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSTAGE][SC * kDim];
   __shared__ uint32_t ring_sk[NSTAGE][SC];   // ScaleK bits, one 4-byte slot per entry
   __shared__ int32_t lds_bt[kMaxChunk / 16 + 2];
+  // bounded TND of few batches: row ends, then inclusive group ends (INT32_MAX
+  // past the last batch), one entry per batch
+  __shared__ __attribute__((aligned(8))) int32_t tnd_tab[TILES ? 2 * kTndInKernelBatches : 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -815,7 +849,22 @@ score_decode_kernel(ScoreParams P) {
       int g = pos / P.reg_chunks;
       key0 = (pos - g * P.reg_chunks) * P.chunk;
       int b, rstart, s1b;
-      if (P.rows_end) {
+      if (P.aslq_tnd) {
+        // the batch of group g: the number of batches whose groups all lie
+        // before it (the wave's lanes hold two group ends each)
+        const int2 ge = *reinterpret_cast<const int2*>(&tnd_tab[kTndInKernelBatches + 2 * lane]);
+        b = (int)(__popcll(__ballot(ge.x <= g)) + __popcll(__ballot(ge.y <= g)));
+        const int nb = P.nbatch;
+        const int last = b < nb ? b : nb;  // rows and groups before those of batch `last`
+        rstart = last > 0 ? tnd_tab[last - 1] : 0;
+        g -= last > 0 ? tnd_tab[kTndInKernelBatches + last - 1] : 0;
+        if (b < nb) {
+          s1b = tnd_tab[b] - rstart;
+        } else {  // past the real groups: rows that belong to no batch
+          b = -1;
+          s1b = P.trows - rstart;
+        }
+      } else if (P.rows_end) {
         const int real = P.group_start[P.nbatch];
         if (g < real) {
           b = P.group_batch[g];
@@ -1041,6 +1090,24 @@ score_decode_kernel(ScoreParams P) {
 
   int n_items = P.n_items_dev ? *P.n_items_dev : P.n_items;
   if (!TILES && P.plan_batches) n_items = plan_items();
+  if constexpr (TILES) {
+    if (P.aslq_tnd) {  // the partition's tables, once per workgroup
+    if (wave == 0) {
+      int e0, e1;
+      tnd_wave_ends(P.aslq_tnd, P.nbatch, P.trows, e0, e1);
+      int before = __shfl_up(e1, 1, 64);
+      if (lane == 0) before = 0;
+      const int g0 = (e0 - before + kMaxItemRows - 1) / kMaxItemRows;  // groups of batches 2l, 2l + 1
+      const int g1 = (e1 - e0 + kMaxItemRows - 1) / kMaxItemRows;
+      const int ge1 = wave_incl_scan(g0 + g1);
+      const int b0 = 2 * lane;
+      *reinterpret_cast<int2*>(&tnd_tab[b0]) = int2{e0, e1};
+      *reinterpret_cast<int2*>(&tnd_tab[kTndInKernelBatches + b0]) =
+          int2{b0 < P.nbatch ? ge1 - g1 : INT32_MAX, b0 + 1 < P.nbatch ? ge1 : INT32_MAX};
+    }
+    __syncthreads();
+    }
+  }
   for (int round = 0;; round++) {
   const int pos = pos_of(round);
   if (pos >= n_items) break;  // uniform; positions grow with the round
@@ -1102,8 +1169,10 @@ struct SelectParams {
   const int32_t* aslk;
   int64_t max_len, stride, mstride, merge_base;
   int32_t s1, mode, cmp, nseg, pass;
-  const int32_t* rows_end;   // bounded TND: the tables (TndTables), else null
+  const int32_t* rows_end;   // bounded TND of many batches: the tables (TndTables), else null
   const int32_t* row_batch;
+  const int32_t* aslq_tnd;   // bounded TND of few batches: the device prefix sums, else null
+  int32_t nbatch;            //   their count
   const int32_t* aslq_bsnd;  // bounded BSND: per-batch query counts, else null (all S1 rows)
 };
 
@@ -1118,7 +1187,17 @@ __device__ __forceinline__ bool bounded_entry(const SelectParams& S, SelectEntry
   const int r = S.pass == 1 ? w / S.nseg : w;
   const int s = S.pass == 1 ? w - r * S.nseg : 0;
   int b, i, s1b;
-  if (S.row_batch) {  // TND: the row's batch from the tables; rows of no batch need no selection
+  if (S.aslq_tnd) {  // TND of few batches: the row's batch derived by each wave
+    int e0, e1;
+    tnd_wave_ends(S.aslq_tnd, S.nbatch, S.s1, e0, e1);
+    const int lane = threadIdx.x & 63;
+    b = (int)(__popcll(__ballot(2 * lane < S.nbatch && e0 <= r)) +
+              __popcll(__ballot(2 * lane + 1 < S.nbatch && e1 <= r)));
+    if (b >= S.nbatch) return false;  // rows of no batch need no selection
+    const int rstart = b > 0 ? tnd_pick(e0, e1, b - 1) : 0;
+    s1b = tnd_pick(e0, e1, b) - rstart;
+    i = r - rstart;
+  } else if (S.row_batch) {  // TND: the row's batch from the tables; rows of no batch need no selection
     b = S.row_batch[r];
     if (b < 0) return false;
     const int rstart = b > 0 ? S.rows_end[b - 1] : 0;
@@ -1403,12 +1482,17 @@ int launch_score(const RunArgs& a, bool dump) {
   }
   P.aslk = a.aslk;  // bounded runs (the header then describes the bound)
   P.aslq_bsnd = a.aslq_bsnd;
-  if (a.aslq) {
+  if (a.aslq && a.tab_off >= 0) {
     const TndTables t = tnd_tables(a.p->batch, a.p->s1);
     const int32_t* tab = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(a.workspace) + a.tab_off);
     P.rows_end = tab + t.rows_end;
     P.group_start = tab + t.group_start;
     P.group_batch = tab + t.group_batch;
+  } else if (a.aslq) {
+    if (a.p->batch > kTndInKernelBatches) return (int)hipErrorInvalidValue;  // needs the tables
+    P.aslq_tnd = a.aslq;
+  }
+  if (a.aslq) {
     P.nbatch = a.p->batch;
     P.trows = a.p->s1;
   }
@@ -1466,11 +1550,15 @@ int launch_select(const RunArgs& a) {
       a.plan_dev ? reinterpret_cast<const SelectEntry*>(static_cast<const uint8_t*>(a.plan_dev) + h->off_select)
                  : nullptr;
   S.aslk = a.aslk;
-  if (a.aslq) {
+  if (a.aslq && a.tab_off >= 0) {
     const TndTables t = tnd_tables(a.p->batch, a.p->s1);
     const int32_t* tab = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(a.workspace) + a.tab_off);
     S.rows_end = tab + t.rows_end;
     S.row_batch = tab + t.row_batch;
+  } else if (a.aslq) {
+    if (a.p->batch > kTndInKernelBatches) return (int)hipErrorInvalidValue;  // needs the tables
+    S.aslq_tnd = a.aslq;
+    S.nbatch = a.p->batch;
   }
   S.aslq_bsnd = a.aslq_bsnd;
   S.max_len = a.max_len;

@@ -390,17 +390,25 @@ def bounded_scores_expected(p, max_len):
     return ((4 * total + 15) // 16 * 16) + 4 * merges if nseg > 1 else 4 * total
 
 
+TND_IN_KERNEL_BATCHES = 128  # up to this many batches the kernels derive the row partition themselves
+
+
 def bounded_tnd_workspace_expected(p, max_len):
-    """TND: the BSND layout over T rows, then (16-byte aligned) the row and group
-    tables: rows_end[B], group_start[B + 1], group_batch[T // 4 + B + 2] (4-row
-    groups; each table padded to 4 elements) and row_batch[T], int32."""
+    """TND: the BSND layout over T rows; for more than 128 batches then
+    (16-byte aligned) the row and group tables: rows_end[B], group_start[B + 1],
+    group_batch[T // 4 + B + 2] (4-row groups; each table padded to 4
+    elements) and row_batch[T], int32."""
     b, t = p["batch"], p["s1"]
     base = bounded_scores_expected(dict(p, batch=1, s1=t), max_len)
+    if b <= TND_IN_KERNEL_BATCHES:
+        return base
     up4 = lambda n: (n + 3) // 4 * 4
     return (base + 15) // 16 * 16 + 4 * (up4(b) + up4(b + 1) + up4(t // 4 + b + 2) + t)
 
 
-@pytest.mark.parametrize("b,t,k,max_len", [(3, 40, 256, 5000), (1, 7, 2048, 100), (5, 300, 64, 20000)])
+@pytest.mark.parametrize("b,t,k,max_len", [(3, 40, 256, 5000), (1, 7, 2048, 100), (5, 300, 64, 20000),
+                                           (128, 300, 64, 20000), (129, 300, 64, 20000), (129, 7, 2048, 100),
+                                           (4096, 9000, 256, 5000)])
 def test_bounded_tnd_workspace(qli, b, t, k, max_len):
     spec = synth.small(layout=synth.TND, batch=b, s1=t, aslq=[t] * b, aslk=[max(max_len, 1)] * b, block_size=64,
                        sparse_count=k, sparse_mode=3)

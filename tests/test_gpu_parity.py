@@ -625,19 +625,25 @@ def test_bounded_tnd_prefix_sums_out_of_contract(ora):
     oracle_check(ora, dict(sub, aslk=np.asarray(lens, dtype=np.int32)), idx, val)
 
 
-def test_bounded_tnd_most_batches(ora):
-    """TND at the table kernel's limit of 4096 batches: 0 to 3 query rows
-    each, one batch of 9 rows (so qli_plan takes 4-row items too), key
-    lengths 0 to 300 with empty batches; bit-identical to qli_plan + qli_run
-    and oracle-checked on every row."""
-    import torch
-    nb, bound = 4096, 300
-    rng = np.random.default_rng(41)
+def tnd_many_batches(nb, bound, seed):
+    """nb batches of 0 to 3 query rows (batch 100 % nb has 9, so qli_plan
+    takes 4-row items too) and key lengths 0 to bound, batch 5 empty."""
+    rng = np.random.default_rng(seed)
     counts = rng.integers(0, 4, size=nb)
-    counts[100] = 9
-    aslq = [int(x) for x in np.cumsum(counts)]
-    lens = [int(x) for x in rng.integers(0, bound + 1, size=nb)]
+    counts[100 % nb] = 9
+    lens = rng.integers(0, bound + 1, size=nb)
     lens[5] = 0
+    return [int(x) for x in np.cumsum(counts)], [int(x) for x in lens]
+
+
+@pytest.mark.parametrize("nb", [128, 129, 4096])
+def test_bounded_tnd_most_batches(ora, nb):
+    """TND around the kernels' own partition (up to 128 batches) and the
+    table kernel (129 up to its limit of 4096): bit-identical to qli_plan +
+    qli_run and oracle-checked on every row."""
+    import torch
+    bound = 300
+    aslq, lens = tnd_many_batches(nb, bound, 41)
     spec = synth.small(layout=synth.TND, batch=nb, s1=aslq[-1], aslq=aslq, aslk=[bound] * nb, block_size=16,
                        sparse_count=64, sparse_mode=3)
     inp = synth.make_inputs(spec, 9)
@@ -653,6 +659,47 @@ def test_bounded_tnd_most_batches(ora):
     p_idx, p_val = planned(inp, dev, lens)
     assert np.array_equal(idx, p_idx) and np.array_equal(val, p_val)
     oracle_check(ora, dict(inp, aslk=np.asarray(lens, dtype=np.int32)), idx, val)
+
+
+@pytest.mark.parametrize("nb", [128, 129])
+def test_bounded_tnd_many_batches_graph_replay(ora, nb):
+    """Both ways to the TND partition (in the kernels, through the table
+    kernel) captured once and replayed with new query prefix sums and key
+    lengths (the row count T fixed, later batches' rows past the last prefix
+    sum in one set): every replay equals qli_plan + qli_run."""
+    import torch
+    bound = 2500
+    sets = [tnd_many_batches(nb, bound, s) for s in (51, 52, 53)]
+    t = max(q[-1] for q, _ in sets)
+    sets[2] = ([min(x, t // 2) for x in sets[2][0]], sets[2][1])  # rows from t // 2 on belong to no batch
+    spec = synth.small(layout=synth.TND, batch=nb, s1=t, aslq=sets[0][0][:-1] + [t], aslk=[bound] * nb,
+                       block_size=64, sparse_count=1024, sparse_mode=3)
+    inp = synth.make_inputs(spec, 10)
+    dev = device_inputs(inp)
+    log("bounded tnd graph: %d batches, %d rows" % (nb, t))
+    bix = qli_mod().BoundedIndexer(inp["problem"], bound)
+    q = torch.tensor(spec.aslq, dtype=torch.int32, device="cuda")
+    k = torch.tensor([bound] * nb, dtype=torch.int32, device="cuda")
+    idx, val = bix.alloc_outputs()
+    args = (k, dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"], idx, val)
+    bix.run(*args, aslq_dev=q)  # first launches outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bix.run(*args, aslq_dev=q)
+    for aslq, lens in sets:
+        q.copy_(torch.tensor(aslq, dtype=torch.int32))
+        k.copy_(torch.tensor(lens, dtype=torch.int32))
+        idx.fill_(-7)
+        val.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        sub = dict(inp, aslq=np.asarray(aslq, dtype=np.int32))
+        p_idx, p_val = planned(sub, dev, lens)
+        assert np.array_equal(idx.cpu().numpy(), p_idx), "aslq %s" % aslq[:8]
+        assert np.array_equal(val.cpu().numpy(), p_val), "aslq %s" % aslq[:8]
+        oracle_check(ora, dict(sub, aslk=np.asarray(lens, dtype=np.int32)), idx.cpu().numpy(), val.cpu().numpy())
 
 
 def test_bounded_tnd_graph_replay(ora):
