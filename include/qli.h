@@ -77,8 +77,7 @@ typedef enum qli_layout { QLI_LAYOUT_BSND = 0, QLI_LAYOUT_TND = 1 } qli_layout;
  * compressed entry only when sparse_mode lets it and every token the entry
  * covers lies in [pos - pre_tokens, pos + next_tokens].  A row's visible
  * entries are then consecutive, [lo, hi); its outputs list the top
- * min(k, hi - lo) of them, padded as usual.  qli_plan / qli_run only: the
- * bounded entry points return QLI_ERR_UNSUPPORTED for a window. */
+ * min(k, hi - lo) of them, padded as usual.  Planned and bounded runs. */
 typedef struct qli_problem {
     int32_t batch;              /* B.  TND: number of entries of actual_seq_lengths_query */
     int32_t s1;                 /* BSND: S1 (query tokens per batch); TND: T (total tokens) */
@@ -248,9 +247,9 @@ int qli_run_stage(const qli_problem *p, const void *plan_host,
  * S1 query rows of every batch active (no actual_seq_lengths_query); any S1.
  * qli_run_bounded_aslq takes BSND with actual_seq_lengths_query
  * on the device; qli_run_bounded_tnd the TND layout with
- * actual_seq_lengths_query on the device too (batch <= 4096).  No
- * pre_tokens / next_tokens window (QLI_ERR_UNSUPPORTED).  Every other
- * parameter as for qli_plan.
+ * actual_seq_lengths_query on the device too (batch <= 4096).  Every other
+ * parameter as for qli_plan, pre_tokens / next_tokens windows included:
+ * each row's range [lo, hi) is derived on the device from its position.
  *
  * Decode problems (BSND, S1 <= 4): every batch is split by its own length
  * into items with the chunk rule of qli_plan, by the scoring kernel itself
@@ -258,6 +257,9 @@ int qli_run_stage(const qli_problem *p, const void *plan_host,
  * table in the workspace, so ragged lengths cost what they cost under
  * qli_plan.  More query rows per batch (and TND): groups of 4 rows whose
  * place follows from the item's position, every batch sized for the bound.
+ * Under a window a batch's or group's items start at the smallest lo of its
+ * rows (rounded down to 128 entries), and the workspace holds a row's window
+ * rather than every entry up to the bound.
  *
  * qli_bounded_workspace -- workspace bytes that qli_run_bounded needs for
  *   these problem sizes and any key lengths in [0, max_seq_len_key] original

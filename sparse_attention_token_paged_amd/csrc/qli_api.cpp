@@ -504,12 +504,27 @@ struct Bounded {
   int64_t tab_off;  // TND of many batches: byte offset of the row and group tables in the workspace, else -1
   int64_t items_off, count_off;  // decode: the device-built item table and its count (-1: none)
   bool plan_in_kernel;           // decode with few batches: the scoring kernel splits the work itself
+  int64_t span;                  // the most entries an item's rows see together
 };
+
+// Bounded runs: the most entries that `rows` consecutive query rows of a
+// batch see together (nmax without a token window).  Row i sees entries in
+// [ceil((pos_i - pre) / cmp), floor((pos_i + next' + 1) / cmp)) with next' = 0
+// under mode 3, whose causal cut binds first (visible_window), so rows
+// pos_0 .. pos_0 + rows - 1 see at most (pre + next' + rows) / cmp + 1
+// entries; items, which start at a multiple of kSpanAlign below the first of
+// them (aligned), cover up to kSpanAlign - 1 more.
+int64_t window_span(const qli_problem& p, int64_t nmax, int64_t rows, bool aligned) {
+  if (p.pre_tokens == INT64_MAX && p.next_tokens == INT64_MAX) return nmax;
+  const int64_t next = p.sparse_mode == 3 ? 0 : p.next_tokens;
+  constexpr int64_t kBeyond = int64_t(1) << 40;  // past any key length: the window bounds nothing
+  if (p.pre_tokens >= kBeyond || next >= kBeyond) return nmax;
+  const int64_t span = (p.pre_tokens + next + rows) / p.cmp_ratio + 1 + (aligned ? kSpanAlign - 1 : 0);
+  return std::min(nmax, span);
+}
 
 int bounded_geometry_scores(const qli_problem& p, int64_t max_len, Bounded& g) {
   if (max_len < 0) return QLI_ERR_ARG;
-  // Visible ranges computed on the device start at entry 0: no window.
-  if (p.pre_tokens != INT64_MAX || p.next_tokens != INT64_MAX) return QLI_ERR_UNSUPPORTED;
   const bool tnd = p.layout_query == QLI_LAYOUT_TND;
   if (tnd && p.batch > kTndMaxBatch) return QLI_ERR_UNSUPPORTED;
   const int64_t nmax = max_len / p.cmp_ratio;
@@ -529,12 +544,17 @@ int bounded_geometry_scores(const qli_problem& p, int64_t max_len, Bounded& g) {
   h.kind = tiles ? kKindTiles : kKindDecode;
   h.rows_per_item = tiles ? kMaxItemRows : (p.s1 <= 1 ? 1 : (p.s1 <= 2 ? 2 : 4));
   if (rows == 0) return QLI_OK;
+  // Entries one row sees (its workspace region) and an item's rows see
+  // together (its chunks, from the item's start): nmax without a window.
+  const int64_t row_span = window_span(p, nmax, 1, false);
+  const int64_t span = window_span(p, nmax, tiles ? kMaxItemRows : p.s1, true);
+  g.span = span;
   // TND: at most tnd_groups groups (the real ones, then padding-only ones)
   const int64_t groups = tnd ? tnd_groups(p.batch, p.s1)
                              : (int64_t)p.batch * ((p.s1 + kMaxItemRows - 1) / kMaxItemRows);
-  h.chunk = tiles ? decode_chunk_for([&](int c) { return groups * ((nmax + c - 1) / c); }, true)
-                  : decode_chunk_equal(p.batch, (int32_t)nmax);
-  h.reg_chunks = (int32_t)std::max<int64_t>(1, (nmax + h.chunk - 1) / h.chunk);
+  h.chunk = tiles ? decode_chunk_for([&](int c) { return groups * ((span + c - 1) / c); }, true)
+                  : decode_chunk_equal(p.batch, (int32_t)span);
+  h.reg_chunks = (int32_t)std::max<int64_t>(1, (span + h.chunk - 1) / h.chunk);
   h.reg_rows = p.s1;
   h.reg_maxv = (int32_t)nmax;
   const int64_t items = (tiles ? groups : (int64_t)p.batch) * h.reg_chunks;
@@ -547,22 +567,23 @@ int bounded_geometry_scores(const qli_problem& p, int64_t max_len, Bounded& g) {
     g.tab_off = align16(h.workspace_bytes);
     h.workspace_bytes = g.tab_off + 4 * tnd_tables(p.batch, p.s1).total;
   };
-  if (nmax <= k) {  // every row is written by the scoring kernel
+  if (row_span <= k) {  // every row is written by the scoring kernel
     add_tables();
     return QLI_OK;
   }
   auto pad4 = [](int64_t n) { return (n + 3) & ~int64_t(3); };
-  g.nseg = (int32_t)((nmax + kSelSegment - 1) / kSelSegment);
-  g.stride = pad4(nmax);
+  g.nseg = (int32_t)((row_span + kSelSegment - 1) / kSelSegment);
+  g.stride = pad4(row_span);
   g.merge_base = rows * g.stride;
   g.mstride = g.nseg > 1 ? pad4((int64_t)g.nseg * k) : 0;
   const int64_t total = g.merge_base + rows * g.mstride;
   if (rows * g.nseg > INT32_MAX) return QLI_ERR_SIZE;
   h.n_select = (int32_t)(rows * g.nseg);
-  h.max_cand = (int32_t)std::min<int64_t>(nmax, kSelSegment);
+  h.max_cand = (int32_t)std::min<int64_t>(row_span, kSelSegment);
   if (g.nseg > 1) {
     h.n_select2 = (int32_t)rows;
-    h.max_cand2 = (g.nseg - 1) * k + (int32_t)std::min<int64_t>(k, nmax - (int64_t)(g.nseg - 1) * kSelSegment);
+    h.max_cand2 =
+        (g.nseg - 1) * k + (int32_t)std::min<int64_t>(k, row_span - (int64_t)(g.nseg - 1) * kSelSegment);
   }
   h.ws_scores = total;
   // key indices for the merge regions only (see build_plan)
@@ -582,7 +603,7 @@ int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
     // decode: items derived on the device from the lengths, by every scoring
     // workgroup for few batches, else by decode_items_kernel into a table
     // after the scores; h.n_items bounds their number for the launch
-    const int64_t cap = device_items_capacity(p.batch, max_len / p.cmp_ratio);
+    const int64_t cap = device_items_capacity(p.batch, g.span);
     if (cap > INT32_MAX) return QLI_ERR_SIZE;
     h.n_items = (int32_t)cap;
     h.reg_chunks = 0;
@@ -591,9 +612,8 @@ int bounded_geometry(const qli_problem& p, int64_t max_len, Bounded& g) {
       // at the bound (each workgroup runs the split's prologue, so idle ones
       // are not free); items beyond it run in later rounds.
       g.plan_in_kernel = true;
-      const int64_t nmax = max_len / p.cmp_ratio;
-      const int c = decode_chunk_equal(p.batch, (int32_t)nmax);
-      h.n_items = (int32_t)std::min<int64_t>(cap, std::max<int64_t>(1, (nmax + c - 1) / c) * p.batch);
+      const int c = decode_chunk_equal(p.batch, (int32_t)g.span);
+      h.n_items = (int32_t)std::min<int64_t>(cap, std::max<int64_t>(1, (g.span + c - 1) / c) * p.batch);
     } else {
       g.items_off = align16(h.workspace_bytes);
       g.count_off = g.items_off + (int64_t)sizeof(Item) * cap;

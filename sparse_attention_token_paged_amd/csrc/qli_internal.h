@@ -96,6 +96,7 @@ struct SelectEntry {
   int32_t indexed;  // 1: the candidates carry key indices (pass-2 merges)
 };
 constexpr int kSelSegment = 8192;  // candidates per first-pass selection of a long row
+constexpr int kSpanAlign = 128;    // bounded runs: items start at a multiple of this many entries (one stage)
 
 // Visible compressed entries of query i (of s1b) in a batch with skb original
 // key tokens (QLI-README 参数说明 cmp_ratio and sparse_mode; the planner and
@@ -129,18 +130,25 @@ __host__ __device__
 #endif
 inline int64_t visible_window(int mode, int cmp, int64_t skb, int64_t s1b, int64_t i, int64_t pre, int64_t next,
                               int64_t& lo) {
+  const int sh = __builtin_ctz((unsigned)cmp);  // the divisions below take positive operands
   int64_t hi = visible_entries(mode, cmp, skb, s1b, i);
   const int64_t pos = skb - s1b + i;
-  lo = pre < pos ? (pos - pre + cmp - 1) / cmp : 0;
+  lo = pre < pos ? (pos - pre + cmp - 1) >> sh : 0;
   if (next < s1b) {
     const int64_t end = pos + next + 1;  // tokens before end are inside the window
-    const int64_t cut = end > 0 ? end / cmp : 0;
+    const int64_t cut = end > 0 ? end >> sh : 0;
     if (cut < hi) hi = cut;
   }
   if (hi <= lo) lo = hi = 0;
   return hi;
 }
 static_assert(sizeof(SelectEntry) == 32, "select table layout");
+
+// Window sides as the bounded kernels take them: clamped to 2^30, which
+// changes no visible range, since positions and row counts stay below it
+// (keys below 2^22 entries of at most 128 tokens; rows below 2^30).
+constexpr int32_t kWindowCap = int32_t(1) << 30;
+inline int32_t window_side(int64_t v) { return v < kWindowCap ? (int32_t)v : kWindowCap; }
 
 struct Item {
   int32_t row0;    // first global row
@@ -244,10 +252,11 @@ constexpr int kPlanInKernelBatches = 256;
 // Bounded decode's device-built item table: one workgroup picks the chunk as
 // qli_plan does (the smallest multiple of 128 entries whose items fit the
 // decode slots; for equal batches the one that lowers the busiest CU's keys)
-// and writes max(1, ceil(visible maximum / chunk)) items per batch.  Upper
-// bound on their number, for the workspace.
-inline int64_t device_items_capacity(int64_t batch, int64_t nmax) {
-  const int64_t most = batch * std::max<int64_t>(1, (nmax + kMaxChunk - 1) / kMaxChunk);
+// and writes max(1, ceil(span / chunk)) items per batch, span being the
+// entries its rows see together.  Upper bound on their number, for the
+// workspace, when no batch's span exceeds `span`.
+inline int64_t device_items_capacity(int64_t batch, int64_t span) {
+  const int64_t most = batch * std::max<int64_t>(1, (span + kMaxChunk - 1) / kMaxChunk);
   return std::max<int64_t>(kDecodeSlots + batch, most);
 }
 int launch_score(const RunArgs& a, bool dump);

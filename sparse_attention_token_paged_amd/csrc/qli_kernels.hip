@@ -29,8 +29,10 @@
 //     so their indices and scores are written straight to the outputs; other
 //     rows stage fp32 scores in the workspace;
 //   * bounded decode (no host plan) derives its items on the device: inside
-//     score_decode_kernel for up to 256 batches, else decode_items_kernel
-//     writes a plan-shaped table first.
+//     score_decode_kernel for up to 256 batches (an instantiation of its
+//     own, so planned runs carry none of its state), else decode_items_kernel
+//     writes a plan-shaped table first; under a token window each row's range
+//     is derived from its position as the planner does.
 // Stage 2 selects (select_reg_kernel, select_global_kernel; one workgroup of
 // 1024 threads per selection): rows of at most 8192 staged scores, and each
 // 8192-score segment of longer rows, keep their top-k; a second launch
@@ -88,6 +90,7 @@ struct ScoreParams {
   int64_t max_len;      //   clamp for them (original tokens)
   int64_t bstride;      //   workspace elements per row
   int32_t mode, cmp;    //   sparse_mode, cmp_ratio
+  int32_t pre, next;    //   pre_tokens, next_tokens clamped to kWindowCap
   int64_t stride;
   int32_t block_size;
   int32_t max_blocks;
@@ -349,6 +352,26 @@ __device__ __forceinline__ void tnd_wave_ends(const int32_t* aslq, int nb, int t
 // b / 2 holds for batches 2l, 2l + 1.
 __device__ __forceinline__ int tnd_pick(int x0, int x1, int b) {
   return __builtin_amdgcn_readlane((b & 1) ? x1 : x0, b >> 1);
+}
+
+// Bounded runs: the entries [lo, hi) that query i of a batch (s1b used rows,
+// skb key tokens after the clamp to the bound) sees under the token window
+// (sides clamped to kWindowCap); without one lo = 0 and hi = visible_entries.
+// Below 2^22 entries.
+__device__ __forceinline__ int row_window(int mode, int cmp, int64_t skb, int s1b, int i, int pre, int next,
+                                          int& lo) {
+  int64_t l;
+  const int64_t h = visible_window(mode, cmp, skb, s1b, i, pre, next, l);
+  lo = (int)l;
+  return (int)h;
+}
+
+// The entries that rows of one item see together: [start, end), start being
+// the smallest lo of a row that sees something, rounded down to a multiple
+// of kSpanAlign (whole stages), [0, 0) when no row does.  Chunks from start
+// cover every row's range.
+__device__ __forceinline__ int span_start(int lo_min, int hi_max) {
+  return hi_max > 0 ? lo_min / kSpanAlign * kSpanAlign : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -626,13 +649,17 @@ __device__ __forceinline__ void select_topk_global(const float* src, int n, int 
 // arithmetic is exact); two stages are in flight while one is computed.
 // Each wave scores its row against its n-tiles of the stage:
 //   RT = 4: all 8 n-tiles, RT = 2: 4 n-tiles, RT = 1: 2 n-tiles.
-template <int QK, int RT, bool DUMP, bool TILES = false>
+template <int QK, int RT, bool DUMP, bool TILES = false, bool PLAN = false>
 // Three workgroups per CU fit the LDS ring; the register budget follows (the
-// dump instantiations, for parity checks only, keep two).
+// dump instantiations, for parity checks only, keep two).  TILES: bounded
+// runs of 4-row groups; PLAN: bounded decode planned in the kernel (planned
+// runs carry neither).
 __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(DUMP ? 2 : 3))) void
 score_decode_kernel(ScoreParams P) {
   static_assert(!TILES || (RT == kMaxItemRows && !DUMP), "4-row groups of bounded runs, no dump");
+  static_assert(!PLAN || (!TILES && !DUMP), "in-kernel planning of bounded decode, no dump");
   constexpr int SC = 128;                     // entries per LDS stage
+  static_assert(SC == kSpanAlign, "bounded items start on a stage");
   constexpr int NSTAGE = 3;
   constexpr int WPR = 4 / RT;                 // waves per row
   constexpr int NPW = 8 / WPR;                // n-tiles per wave per stage
@@ -658,7 +685,7 @@ score_decode_kernel(ScoreParams P) {
   // takes item t*G + b (t even) or t*G + G-1-b (t odd).
   const int G = gridDim.x;
   auto pos_of = [&](int t) { return t * G + ((t & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x); };
-  const bool reg = !TILES && P.reg_chunks > 0;
+  const bool reg = !TILES && !PLAN && P.reg_chunks > 0;
   const int bs = P.block_size;
   const int u = wave / WPR;  // this wave's row of the item
   const int sub = wave % WPR;
@@ -701,30 +728,41 @@ score_decode_kernel(ScoreParams P) {
   }
   const uint32_t skoff = (uint32_t)((32 * wave + (lane & 31)) * SB);
 
-  // Bounded decode planned in the kernel (P.plan_batches > 0, at most one
-  // batch per thread): thread t holds batch t's visible maximum my_m (that of
-  // its last used query row), used rows my_s1b and clamped key length my_skb;
-  // plan_items() picks the chunk with the planner's rule (the smallest
-  // multiple of 128 entries whose items fit the resident decode workgroups;
-  // for equal batches the one that lowers the busiest CU's keys), gives each
-  // batch max(1, ceil(my_m / chunk)) items at the exclusive prefix my_first
+  // Bounded decode planned in the kernel (PLAN; P.plan_batches, at most one
+  // batch per thread): thread t holds the entries [my_start, my_m) that batch
+  // t's rows see (from entry 0 to the last used row's end without a window),
+  // its used rows my_s1b and clamped key length my_skb; plan_items() picks
+  // the chunk with the planner's rule (the smallest multiple of 128 entries
+  // whose items fit the resident decode workgroups; for equal batches the one
+  // that lowers the busiest CU's keys), gives each batch max(1,
+  // ceil((my_m - my_start) / chunk)) items at the exclusive prefix my_first
   // and returns their number.  Every workgroup derives the same split; its
   // scratch lies in the ring, free until the first stage is issued.
   __shared__ int plan_sh[8];
-  int my_m = 0, my_s1b = 0, my_first = 0, my_n = 0, plan_chunk = 0;
+  int my_m = 0, my_start = 0, my_s1b = 0, my_first = 0, my_n = 0, plan_chunk = 0;
   int64_t my_skb = 0;
   auto plan_items = [&]() {
     const int nb = P.plan_batches;
     if (tid < nb) {
       my_skb = min<int64_t>(max(P.aslk[tid], 0), P.max_len);
       my_s1b = P.aslq_bsnd ? min(max(P.aslq_bsnd[tid], 0), P.reg_rows) : P.reg_rows;
-      my_m = my_s1b > 0 ? (int)visible_entries(P.mode, P.cmp, my_skb, my_s1b, my_s1b - 1) : 0;
+      int lo_min = INT32_MAX, hi_max = 0;
+      for (int uu = 0; uu < my_s1b; uu++) {  // at most kMaxItemRows rows
+        int lo;
+        const int hi = row_window(P.mode, P.cmp, my_skb, my_s1b, uu, P.pre, P.next, lo);
+        if (hi > lo) {
+          lo_min = min(lo_min, lo);
+          hi_max = max(hi_max, hi);
+        }
+      }
+      my_start = span_start(lo_min, hi_max);
+      my_m = hi_max;
     }
-    int* sm = reinterpret_cast<int*>(&ring[0][0]);  // [256] visible maxima
+    int* sm = reinterpret_cast<int*>(&ring[0][0]);  // [256] the batches' spans
     int* part = sm + kScoreThreads;                 // [8][32] partial item counts
     int* pmm = part + kScoreThreads;                // [8] partial minima, [8] maxima
     int* scan_tmp = pmm + 16;                       // the block scan's
-    sm[tid] = tid < nb ? my_m : 0;
+    sm[tid] = tid < nb ? my_m - my_start : 0;
     __syncthreads();
     {  // candidate chunk 128 (tid % 32 + 1) over batches tid / 32, tid / 32 + 8, ...
       static_assert(kChunkSteps == 32 && kScoreThreads == 256, "8 groups of the 32 candidates");
@@ -764,7 +802,7 @@ score_decode_kernel(ScoreParams P) {
     __syncthreads();
     const int best = plan_sh[6];
     plan_chunk = 128 * (best + 1);
-    my_n = tid < nb ? max(1, (my_m + plan_chunk - 1) / plan_chunk) : 0;
+    my_n = tid < nb ? max(1, (my_m - my_start + plan_chunk - 1) / plan_chunk) : 0;
     my_first = block_exclusive_scan<kScoreThreads>(my_n, scan_tmp);
     if (tid == kScoreThreads - 1) plan_sh[7] = my_first + my_n;
     __syncthreads();
@@ -847,7 +885,7 @@ score_decode_kernel(ScoreParams P) {
       // through the tables, the groups past the real ones covering the rows
       // that belong to no batch, which only receive padding)
       int g = pos / P.reg_chunks;
-      key0 = (pos - g * P.reg_chunks) * P.chunk;
+      const int cidx = pos - g * P.reg_chunks;  // the chunk's index from the group's start
       int b, rstart, s1b;
       if (P.aslq_tnd) {
         // the batch of group g: the number of batches whose groups all lie
@@ -890,17 +928,29 @@ score_decode_kernel(ScoreParams P) {
       batch = b;
       row0 = rstart + kMaxItemRows * g;
       nrows = max(0, min(kMaxItemRows, s1b - kMaxItemRows * g));
-      auto vis_of = [&](int uu) {
+      // row uu's entries [lo, hi): none past the batch's used rows
+      auto range_of = [&](int uu, int& lo) {
         const int i = kMaxItemRows * g + uu;
-        return b >= 0 && i < s1q ? (int)visible_entries(P.mode, P.cmp, skb, s1q, i) : 0;
+        lo = 0;
+        return uu < nrows && b >= 0 && i < s1q ? row_window(P.mode, P.cmp, skb, s1q, i, P.pre, P.next, lo) : 0;
       };
-      int maxv = 0;
-      for (int uu = 0; uu < nrows; uu++) maxv = max(maxv, vis_of(uu));
+      int lo_min = INT32_MAX, maxv = 0, pad_to[kMaxItemRows];
+#pragma unroll
+      for (int uu = 0; uu < kMaxItemRows; uu++) {
+        int lo;
+        const int hi = range_of(uu, lo);
+        pad_to[uu] = hi - lo;
+        if (hi > lo) {
+          lo_min = min(lo_min, lo);
+          maxv = max(maxv, hi);
+        }
+      }
+      key0 = span_start(lo_min, maxv) + cidx * P.chunk;
       nkeys = min(P.chunk, maxv - key0);
-      if (key0 == 0) {  // the group's first chunk pads its rows
+      if (cidx == 0) {  // the group's first chunk pads its rows
         pad_n = nrows;
 #pragma unroll
-        for (int uu = 0; uu < kMaxItemRows; uu++) pad_from[uu] = uu < nrows ? vis_of(uu) : k;
+        for (int uu = 0; uu < kMaxItemRows; uu++) pad_from[uu] = uu < nrows ? pad_to[uu] : k;
       }
       if (nkeys <= 0) {  // uniform across the workgroup
         do_pad();
@@ -908,10 +958,11 @@ score_decode_kernel(ScoreParams P) {
       }
       rok = u < nrows;
       r = row0 + (rok ? u : 0);
-      rvis = rok ? vis_of(u) : 0;
-      rlo = 0;
-      coff = rvis > k ? r * P.bstride + key0 : -1;
-    } else if (P.plan_batches) {
+      int lo_u;
+      rvis = rok ? range_of(u, lo_u) : 0;
+      rlo = rok ? lo_u : 0;
+      coff = rvis - rlo > k ? r * P.bstride + key0 - rlo : -1;  // entry j at slot j - lo of the row
+    } else if constexpr (PLAN) {
       // bounded decode planned in the kernel: the thread of the batch whose
       // items hold pos publishes the item; the ring is free here
       if (tid < P.plan_batches && pos >= my_first && pos < my_first + my_n) {
@@ -920,22 +971,31 @@ score_decode_kernel(ScoreParams P) {
         plan_sh[2] = my_m;
         plan_sh[3] = my_s1b;
         plan_sh[4] = (int)my_skb;  // clamped to the bound, below kMaxEntries * 128 = 2^29
+        plan_sh[5] = my_start;
       }
       __syncthreads();
       batch = plan_sh[0];
-      key0 = plan_sh[1] * plan_chunk;
+      const int idx = plan_sh[1];
       const int m = plan_sh[2], s1b = plan_sh[3];
       const int64_t skb = plan_sh[4];
+      key0 = plan_sh[5] + idx * plan_chunk;
       __syncthreads();  // read by every thread before the next item's owner writes them
       nkeys = min(plan_chunk, m - key0);
       row0 = batch * P.reg_rows;
       nrows = P.reg_rows;
-      // the row's visible count: 0 past the batch's used rows
-      auto vis_of = [&](int uu) { return uu < s1b ? (int)visible_entries(P.mode, P.cmp, skb, s1b, uu) : 0; };
-      if (key0 == 0) {  // the batch's first item pads its rows
+      // the row's entries [lo, hi): none past the batch's used rows
+      auto range_of = [&](int uu, int& lo) {
+        lo = 0;
+        return uu < s1b ? row_window(P.mode, P.cmp, skb, s1b, uu, P.pre, P.next, lo) : 0;
+      };
+      if (idx == 0) {  // the batch's first item pads its rows
         pad_n = nrows;
 #pragma unroll
-        for (int uu = 0; uu < kMaxItemRows; uu++) pad_from[uu] = uu < nrows ? vis_of(uu) : k;
+        for (int uu = 0; uu < kMaxItemRows; uu++) {
+          int lo;
+          const int hi = range_of(uu, lo);
+          pad_from[uu] = uu < nrows ? hi - lo : k;
+        }
       }
       if (nkeys <= 0) {  // uniform across the workgroup
         do_pad();
@@ -943,9 +1003,10 @@ score_decode_kernel(ScoreParams P) {
       }
       rok = u < nrows;
       r = row0 + (rok ? u : 0);
-      rvis = rok ? vis_of(u) : 0;
-      rlo = 0;
-      coff = rvis > k ? r * P.bstride + key0 : -1;
+      int lo_u;
+      rvis = rok ? range_of(u, lo_u) : 0;
+      rlo = rok ? lo_u : 0;
+      coff = rvis - rlo > k ? r * P.bstride + key0 - rlo : -1;  // entry j at slot j - lo of the row
     } else if (reg) {
       batch = pos / P.reg_chunks;
       key0 = (pos - batch * P.reg_chunks) * P.chunk;
@@ -976,7 +1037,7 @@ score_decode_kernel(ScoreParams P) {
     const int32_t* bt = P.block_table + (int64_t)batch * P.max_blocks + fb;
     const int bt0 = tid < nblk ? bt[tid] : 0;
     const int bt1 = tid + kScoreThreads < nblk ? bt[tid + kScoreThreads] : 0;
-    if (!TILES && !P.plan_batches) {
+    if constexpr (!TILES && !PLAN) {
       rok = u < nrows;
       r = row0 + (rok ? u : 0);
       rvis = rok ? itp->vis[u] : 0;
@@ -1089,7 +1150,7 @@ score_decode_kernel(ScoreParams P) {
 
 
   int n_items = P.n_items_dev ? *P.n_items_dev : P.n_items;
-  if (!TILES && P.plan_batches) n_items = plan_items();
+  if constexpr (PLAN) n_items = plan_items();
   if constexpr (TILES) {
     if (P.aslq_tnd) {  // the partition's tables, once per workgroup
     if (wave == 0) {
@@ -1168,6 +1229,7 @@ struct SelectParams {
   // segment w % nseg of row w / nseg, workgroup r of pass 2 the merge of row r.
   const int32_t* aslk;
   int64_t max_len, stride, mstride, merge_base;
+  int32_t pre, next;  // pre_tokens, next_tokens clamped to kWindowCap
   int32_t s1, mode, cmp, nseg, pass;
   const int32_t* rows_end;   // bounded TND of many batches: the tables (TndTables), else null
   const int32_t* row_batch;
@@ -1213,30 +1275,32 @@ __device__ __forceinline__ bool bounded_entry(const SelectParams& S, SelectEntry
     }
   }
   const int64_t skb = min<int64_t>(max(S.aslk[b], 0), S.max_len);
-  const int vis = (int)visible_entries(S.mode, S.cmp, skb, s1b, i);
-  if (vis <= S.k) return false;
-  const int nsr = (vis + kSelSegment - 1) / kSelSegment;  // segments of this row
+  int lo;
+  const int nv = row_window(S.mode, S.cmp, skb, s1b, i, S.pre, S.next, lo) - lo;  // entries lo.. at slots 0..
+  if (nv <= S.k) return false;
+  const int nsr = (nv + kSelSegment - 1) / kSelSegment;  // segments of this row
   se.row = r;
-  se.base = 0;
+  se.base = lo;
   se.indexed = 0;
   se.dst_off = -1;
   if (S.pass == 2) {
     if (nsr == 1) return false;
     se.src_off = S.merge_base + (int64_t)r * S.mstride;
-    se.n = (nsr - 1) * S.k + min(S.k, vis - (nsr - 1) * kSelSegment);
+    se.n = (nsr - 1) * S.k + min(S.k, nv - (nsr - 1) * kSelSegment);
+    se.base = 0;  // the candidates carry their key indices
     se.indexed = 1;
     return true;
   }
   if (nsr == 1) {
     se.src_off = (int64_t)r * S.stride;
-    se.n = vis;
+    se.n = nv;
     return s == 0;
   }
   if (s >= nsr) return false;
   se.src_off = (int64_t)r * S.stride + (int64_t)s * kSelSegment;
   se.dst_off = S.merge_base + (int64_t)r * S.mstride + (int64_t)s * S.k;
-  se.n = min(kSelSegment, vis - s * kSelSegment);
-  se.base = s * kSelSegment;
+  se.n = min(kSelSegment, nv - s * kSelSegment);
+  se.base = lo + s * kSelSegment;
   return true;
 }
 
@@ -1439,6 +1503,18 @@ hipError_t launch_score_t(const ScoreParams& P, const PlanHeader* h, hipStream_t
     if constexpr (DUMP) return hipErrorInvalidValue;
     else return go(score_decode_kernel<QK, kMaxItemRows, false, true>);
   }
+  if (P.plan_batches > 0) {  // bounded decode planned in the kernel (never dumped)
+    if constexpr (DUMP) {
+      return hipErrorInvalidValue;
+    } else {
+      switch (h->rows_per_item) {
+        case 1: return go(score_decode_kernel<QK, 1, false, false, true>);
+        case 2: return go(score_decode_kernel<QK, 2, false, false, true>);
+        case 4: return go(score_decode_kernel<QK, 4, false, false, true>);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
   switch (h->rows_per_item) {
     case 1: return go(score_decode_kernel<QK, 1, DUMP>);
     case 2: return go(score_decode_kernel<QK, 2, DUMP>);
@@ -1500,6 +1576,8 @@ int launch_score(const RunArgs& a, bool dump) {
   P.bstride = a.stride;
   P.mode = a.p->sparse_mode;
   P.cmp = a.p->cmp_ratio;
+  P.pre = window_side(a.p->pre_tokens);
+  P.next = window_side(a.p->next_tokens);
   P.n_items = h->n_items;
   if (a.items_off >= 0) {  // bounded decode with a device-built item table: it reads like a plan's
     P.items = reinterpret_cast<const Item*>(static_cast<const uint8_t*>(a.workspace) + a.items_off);
@@ -1568,6 +1646,8 @@ int launch_select(const RunArgs& a) {
   S.s1 = a.p->s1;
   S.mode = a.p->sparse_mode;
   S.cmp = a.p->cmp_ratio;
+  S.pre = window_side(a.p->pre_tokens);
+  S.next = window_side(a.p->next_tokens);
   S.nseg = a.nseg;
   S.ws = static_cast<float*>(a.workspace);
   S.ws_idx = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + h->ws_index_offset);
@@ -1666,18 +1746,20 @@ int launch_sort(const RunArgs& a) {
 // Bounded decode: the item table from the device key lengths (and, for BSND
 // with actual_seq_lengths_query, the query counts), so that a bounded run
 // splits each batch by its own length as qli_plan would.  One workgroup:
-//   1. the visible maximum m_b of each batch (its last used query row);
+//   1. the entries [start_b, start_b + m_b) that each batch's rows see
+//      (from 0 to its last used row's visible end without a token window);
 //      for every candidate chunk c = 128, 256, .., kMaxChunk the item count
 //      sum ceil(m_b / c), one wave per two candidates (lanes stride the
 //      batches, then a wave reduction);
 //   2. the chunk: the smallest c whose items fit the decode slots (else
 //      kMaxChunk); when every batch has the same m_b, the c >= it that
 //      lowers ceil(items / CUs) * c, as for equal groups on the host;
-//   3. max(1, ceil(m_b / c)) items per batch at an exclusive prefix sum over
-//      the batches (1024 at a time with a carry), written as plan items:
-//      rows b*S1 .. +S1, key range, per-row visible ends (0 past the query
-//      count) and staged-score offsets r * bstride + key0 (rows seeing more
-//      than k entries), the first item of a batch writing its padding.
+//   3. max(1, ceil(m_b / c)) items per batch from start_b at an exclusive
+//      prefix sum over the batches (1024 at a time with a carry), written as
+//      plan items: rows b*S1 .. +S1, key range, per-row visible ranges
+//      [lo, vis) (empty past the query count) and staged-score offsets
+//      r * bstride + key0 - lo (rows seeing more than k entries), the first
+//      item of a batch writing its padding.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -1688,6 +1770,7 @@ struct DecodeItemsParams {
   const int32_t* aslq;  // BSND query counts or null (every row used)
   int32_t batch, s1, mode, cmp, k;
   int64_t max_len, bstride;
+  int32_t pre, next;    // pre_tokens, next_tokens clamped to kWindowCap
   Item* items;
   int32_t* n_items;
 };
@@ -1699,11 +1782,22 @@ __global__ __launch_bounds__(kItemsThreads) void decode_items_kernel(DecodeItems
   __shared__ int m_lo, m_hi, total_s;
   __shared__ int scan_tmp[NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // batch b: used query rows s1b, clamped key length skb, visible maximum
-  auto batch_info = [&](int b, int& s1b, int64_t& skb) {
+  // batch b: used query rows s1b, clamped key length skb, and the entries
+  // [start, start + span) its rows see (span_start)
+  auto batch_info = [&](int b, int& s1b, int64_t& skb, int& start) {
     skb = min<int64_t>(max(D.aslk[b], 0), D.max_len);
     s1b = D.aslq ? min(max(D.aslq[b], 0), D.s1) : D.s1;
-    return s1b > 0 ? (int)visible_entries(D.mode, D.cmp, skb, s1b, s1b - 1) : 0;
+    int lo_min = INT32_MAX, hi_max = 0;
+    for (int u = 0; u < s1b; u++) {  // at most kMaxItemRows rows
+      int lo;
+      const int hi = row_window(D.mode, D.cmp, skb, s1b, u, D.pre, D.next, lo);
+      if (hi > lo) {
+        lo_min = min(lo_min, lo);
+        hi_max = max(hi_max, hi);
+      }
+    }
+    start = span_start(lo_min, hi_max);
+    return hi_max - start;
   };
   // 1. wave w sums the items of candidate chunks 128 (w + 1) and 128 (w + NW + 1)
   //    over every batch (lanes stride the batches); wave 0 also takes the
@@ -1713,9 +1807,9 @@ __global__ __launch_bounds__(kItemsThreads) void decode_items_kernel(DecodeItems
     const int i = wave + NW * h, c = 128 * (i + 1);
     int sum = 0, lo = INT32_MAX, hi = -1;
     for (int b = lane; b < D.batch; b += 64) {
-      int s1b;
+      int s1b, start;
       int64_t skb;
-      const int m = batch_info(b, s1b, skb);
+      const int m = batch_info(b, s1b, skb, start);
       sum += (m + c - 1) / c;
       lo = min(lo, m);
       hi = max(hi, m);
@@ -1749,10 +1843,10 @@ __global__ __launch_bounds__(kItemsThreads) void decode_items_kernel(DecodeItems
   int carry = 0;
   for (int b0 = 0; b0 < D.batch; b0 += kItemsThreads) {  // uniform
     const int b = b0 + tid;
-    int s1b = 0, m = 0, n = 0;
+    int s1b = 0, m = 0, n = 0, start = 0;
     int64_t skb = 0;
     if (b < D.batch) {
-      m = batch_info(b, s1b, skb);
+      m = batch_info(b, s1b, skb, start);
       n = max(1, (m + c - 1) / c);
     }
     const int first = carry + block_exclusive_scan<kItemsThreads>(n, scan_tmp);
@@ -1764,16 +1858,18 @@ __global__ __launch_bounds__(kItemsThreads) void decode_items_kernel(DecodeItems
     it.reserved[0] = it.reserved[1] = 0;
 #pragma unroll
     for (int u = 0; u < kMaxItemRows; u++) {
-      it.vis[u] = u < s1b ? (int)visible_entries(D.mode, D.cmp, skb, s1b, u) : 0;
-      it.lo[u] = 0;
+      int lo = 0;
+      it.vis[u] = u < s1b ? row_window(D.mode, D.cmp, skb, s1b, u, D.pre, D.next, lo) : 0;
+      it.lo[u] = lo;
     }
     for (int i = 0; i < n; i++) {
-      it.key0 = i * c;
+      it.key0 = start + i * c;
       it.nkeys = max(0, min(c, m - i * c));
       it.flags = i == 0 ? kItemPad : 0;
 #pragma unroll
-      for (int u = 0; u < kMaxItemRows; u++)
-        it.cand_off[u] = it.vis[u] > D.k ? (int64_t)(b * D.s1 + u) * D.bstride + it.key0 : -1;
+      for (int u = 0; u < kMaxItemRows; u++)  // entry j of a staged row at slot j - lo
+        it.cand_off[u] = it.vis[u] - it.lo[u] > D.k
+                             ? (int64_t)(b * D.s1 + u) * D.bstride + it.key0 - it.lo[u] : -1;
       D.items[first + i] = it;
     }
     __syncthreads();  // total_s written
@@ -1797,6 +1893,8 @@ int launch_decode_items(const RunArgs& a) {
   D.k = a.p->sparse_count;
   D.max_len = a.max_len;
   D.bstride = a.stride;
+  D.pre = window_side(a.p->pre_tokens);
+  D.next = window_side(a.p->next_tokens);
   D.items = reinterpret_cast<Item*>(static_cast<uint8_t*>(a.workspace) + a.items_off);
   D.n_items = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a.workspace) + a.count_off);
   const hipError_t e =

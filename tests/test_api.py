@@ -369,8 +369,8 @@ def bounded_workspace_expected(p, max_len):
     rows, b = p["batch"] * p["s1"], p["batch"]
     if rows == 0 or p["s1"] > 4 or b <= 256:
         return base
-    nmax = max_len // p["cmp_ratio"]
-    cap = max(DECODE_SLOTS + b, b * max(1, -(-nmax // 4096)))
+    span = window_span(p, max_len // p["cmp_ratio"], p["s1"], True)
+    cap = max(DECODE_SLOTS + b, b * max(1, -(-span // 4096)))
     return (base + 15) // 16 * 16 + ITEM_BYTES * cap + 16
 
 
@@ -380,7 +380,7 @@ def bounded_scores_expected(p, max_len):
     one selection segment also keep each segment's k winners for the merge, with
     their key indices in an int32 region after every score (merge regions only)."""
     rows, k = p["batch"] * p["s1"], p["sparse_count"]
-    nmax = max_len // p["cmp_ratio"]
+    nmax = window_span(p, max_len // p["cmp_ratio"], 1, False)  # entries one row may see
     if rows == 0 or nmax <= k:
         return 0
     pad4 = lambda n: (n + 3) // 4 * 4
@@ -592,20 +592,70 @@ def test_sparse_attention_rejects_without_launching(qli):
     assert rc == qli.QLI_OK and ws == 0
 
 
-def test_bounded_entry_points_reject_windows(qli):
-    """Bounded runs derive visible ranges on the device from entry 0: a
-    pre_tokens / next_tokens window is QLI_ERR_UNSUPPORTED there (qli_plan
-    accepts it)."""
-    spec = synth.small(batch=2, s1=2, aslk=[3000] * 2, block_size=64, sparse_count=256, sparse_mode=3,
-                       pre_tokens=500)
-    p = synth.make_inputs(spec, 1)["problem"]
-    rc, _ = qli.qli_bounded_workspace(qli.Problem.from_dict(p), 3000)
-    assert rc == qli.QLI_ERR_UNSUPPORTED
-    rc, _ = qli.qli_bounded_workspace(qli.Problem.from_dict(dict(p, pre_tokens=synth.INT64_MAX, next_tokens=9)),
-                                      3000)
-    assert rc == qli.QLI_ERR_UNSUPPORTED
-    rc, _ = qli.qli_bounded_workspace(qli.Problem.from_dict(dict(p, pre_tokens=synth.INT64_MAX)), 3000)
-    assert rc == qli.QLI_OK
+BEYOND = 1 << 40  # a window side at least this long bounds nothing
+
+
+def window_span(p, nmax, rows, aligned):
+    """Bounded runs under a pre_tokens / next_tokens window: the most entries
+    `rows` consecutive query rows of a batch see together, (pre + next' + rows)
+    // cmp + 1 with next' = 0 under mode 3 (the causal cut binds first), plus
+    127 when the items start at a multiple of 128 below the first of them;
+    never more than nmax, and nmax without a window."""
+    pre, nxt = p.get("pre_tokens", synth.INT64_MAX), p.get("next_tokens", synth.INT64_MAX)
+    if pre == synth.INT64_MAX and nxt == synth.INT64_MAX:
+        return nmax
+    nxt = 0 if p["sparse_mode"] == 3 else nxt
+    if pre >= BEYOND or nxt >= BEYOND:
+        return nmax
+    return min(nmax, (pre + nxt + rows) // p["cmp_ratio"] + 1 + (127 if aligned else 0))
+
+
+@pytest.mark.parametrize("mode", [3, 0])
+@pytest.mark.parametrize("pre,nxt", [(500, synth.INT64_MAX), (synth.INT64_MAX, 9), (0, 0), (3000, 40),
+                                     (100000, 0), (BEYOND, 7)])
+@pytest.mark.parametrize("s1,batch", [(2, 2), (4, 300), (9, 3)])
+def test_bounded_windowed_workspace(qli, mode, pre, nxt, s1, batch):
+    """Bounded runs take a pre_tokens / next_tokens window: each row's scores
+    need only the window's entries, so the row stride, the selection segments
+    and the device item table follow the window's span."""
+    spec = synth.small(batch=3, s1=s1, aslk=[20000] * 3, block_size=64, sparse_count=256, sparse_mode=mode,
+                       pre_tokens=pre, next_tokens=nxt)
+    p = dict(synth.make_inputs(spec, 1)["problem"], batch=batch)
+    rc, ws = qli.qli_bounded_workspace(qli.Problem.from_dict(p), 20000)
+    assert rc == qli.QLI_OK and ws == bounded_workspace_expected(p, 20000)
+    if pre < 20000 and (mode == 3 or nxt < 20000):  # the rows see fewer entries than without a window
+        assert ws < bounded_workspace_expected(dict(p, pre_tokens=synth.INT64_MAX, next_tokens=synth.INT64_MAX),
+                                               20000)
+    tnd = dict(p, layout_query=synth.TND, batch=min(batch, 3), s1=s1 * 3)
+    rc, ws = qli.qli_bounded_workspace(qli.Problem.from_dict(tnd), 20000)
+    assert rc == qli.QLI_OK and ws == bounded_tnd_workspace_expected(tnd, 20000)
+
+
+def test_window_span_bounds_every_row(ora):
+    """The spans above bound what the oracle's windows give (visible ranges
+    computed independently, in C, from the page's reading of the window): every
+    row's count of entries, and the entries of every decode batch (S1 <= 4 rows)
+    and 4-row group from its first entry rounded down to 128, over seeded
+    random problems (modes, cmp_ratio, windows, lengths)."""
+    rng = np.random.default_rng(5)
+    for _ in range(400):
+        mode, cmp = int(rng.choice([0, 3])), int(rng.choice([1, 2, 4, 16, 128]))
+        pre = int(rng.choice([0, 1, 5, 100, 1000, 7000, synth.INT64_MAX]))
+        nxt = int(rng.choice([0, 1, 3, 50, 4000, synth.INT64_MAX]))
+        s1, batch = int(rng.integers(1, 13)), int(rng.integers(1, 4))
+        aslk = rng.integers(0, 20000, size=batch).astype(np.int32)
+        p = dict(sparse_mode=mode, cmp_ratio=cmp, pre_tokens=pre, next_tokens=nxt)
+        nmax = int(aslk.max()) // cmp
+        lo, hi = ora.row_range(0, batch, s1, mode, cmp, None, aslk, pre, nxt)
+        assert (hi - lo).max() <= window_span(p, nmax, 1, False)
+        for size in ([s1] if s1 <= 4 else []) + [4]:
+            for b in range(batch):
+                for g0 in range(0, s1, size):
+                    rr = slice(b * s1 + g0, b * s1 + min(g0 + size, s1))
+                    seen = hi[rr] > lo[rr]
+                    if seen.any():
+                        start = lo[rr][seen].min() // 128 * 128
+                        assert hi[rr][seen].max() - start <= window_span(p, nmax, size, True), (p, s1, aslk)
 
 
 @pytest.mark.parametrize("return_value", [1, 0])

@@ -923,6 +923,37 @@ def test_bounded_random(ora, i):
     oracle_check(ora, inp, idx, val)
 
 
+@pytest.mark.parametrize("i", range(10))
+def test_bounded_random_windowed(ora, i):
+    """The random problems above with random pre/next_tokens windows, run
+    without a host plan: bit-identical to qli_plan + qli_run where the plan
+    uses the same tiles, and every row against the oracle's window."""
+    import dataclasses
+    import torch
+    rng = np.random.default_rng(991 + i)
+    spec = dataclasses.replace(random_spec(300 + i),
+                               pre_tokens=int(rng.choice([0, 1, 7, 100, 1000, 5000, synth.INT64_MAX])),
+                               next_tokens=int(rng.choice([0, 3, 50, synth.INT64_MAX])))
+    inp = synth.make_inputs(spec, i)
+    p = inp["problem"]
+    log("bounded random windowed %d: %s" % (i, spec))
+    dev = device_inputs(inp)
+    bound = max(1, int(max(inp["aslk"])))
+    bix = qli_mod().BoundedIndexer(p, bound)
+    k_dev = torch.from_numpy(inp["aslk"].astype(np.int32)).cuda()
+    q_dev = torch.from_numpy(np.asarray(inp["aslq"], dtype=np.int32)).cuda() if inp["aslq"] is not None else None
+    idx, val = bix.alloc_outputs()
+    bix.run(k_dev, dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"],
+            idx, val, aslq_dev=q_dev)
+    torch.cuda.synchronize()
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    tiles_match = spec.layout == synth.BSND or np.diff(np.concatenate([[0], inp["aslq"]])).max() >= 3
+    if tiles_match:
+        p_idx, p_val, _ = run_gpu(inp, dev)
+        assert np.array_equal(idx, p_idx) and np.array_equal(val, p_val)
+    check_windowed(ora, inp, idx, val)
+
+
 @pytest.mark.parametrize("case", ["bsnd_int8_causal_bs48_pad", "long_rt2_causal", "tnd_int8_prefill_mixed"])
 def test_without_values(case):
     """return_value = 0 (参数说明: sparse_values optional): no value buffer, the
@@ -1003,6 +1034,94 @@ def test_parity_windowed(ora, name):
     gidx, gval, _ = run_gpu(inp)
     lo, hi = check_windowed(ora, inp, gidx, gval)
     assert lo.max() > 0   # every case has rows whose window starts past entry 0
+
+
+# --- windows in bounded runs (qli_run_bounded* with pre/next_tokens) ---------
+BOUNDED_WINDOWED = dict(WINDOWED)
+# decode of more than 256 batches: the device item table carries each row's window start
+BOUNDED_WINDOWED["win_decode_table_300"] = synth.small(
+    batch=300, s1=2, aslk=[int(x) for x in np.random.default_rng(61).integers(0, 3000, size=300)], block_size=64,
+    sparse_count=128, sparse_mode=3, pre_tokens=700, next_tokens=0)
+# prefill groups whose windows start past several chunks of the bound
+BOUNDED_WINDOWED["win_prefill_far_start"] = synth.small(batch=2, s1=24, aslk=[9000, 6000], block_size=128,
+                                                        sparse_count=256, sparse_mode=3, pre_tokens=600)
+
+
+def bounded_windowed_run(inp, dev, lens, bound, aslq=None):
+    import torch
+    bix = qli_mod().BoundedIndexer(inp["problem"], bound)
+    idx, val = bix.alloc_outputs()
+    q = None if aslq is None else torch.tensor(aslq, dtype=torch.int32, device="cuda")
+    bix.run(torch.tensor(lens, dtype=torch.int32, device="cuda"), dev["query"], dev["key"], dev["weights"],
+            dev["q_scale"], dev["k_scale"], dev["block_table"], idx, val, aslq_dev=q)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), val.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", list(BOUNDED_WINDOWED))
+def test_bounded_windowed_matches_planned(ora, name):
+    """Windows in bounded runs: each row's range [lo, hi) is derived on the
+    device (decode items planned in the kernel or by the item-table kernel,
+    4-row groups, TND), scores land at entry - lo of the row's region and the
+    selection is based at lo.  Bit-identical to qli_plan + qli_run and checked
+    against the oracle's window on every row."""
+    inp = synth.make_inputs(BOUNDED_WINDOWED[name], 17)
+    p = inp["problem"]
+    bound = int(max(inp["aslk"])) if p["batch"] else 0
+    log("bounded windowed %s: rows=%d pre=%d next=%d bound=%d" % (name, rows_of(p), p["pre_tokens"],
+                                                                   p["next_tokens"], bound))
+    dev = device_inputs(inp)
+    tnd = p["layout_query"] == synth.TND
+    idx, val = bounded_windowed_run(inp, dev, [int(x) for x in inp["aslk"]], bound,
+                                    aslq=[int(x) for x in inp["aslq"]] if tnd else None)
+    p_idx, p_val, _ = run_gpu(inp, dev)
+    assert np.array_equal(idx, p_idx) and np.array_equal(val, p_val)
+    check_windowed(ora, inp, idx, val)
+
+
+@pytest.mark.parametrize("name", ["win_decode_rt4_staged", "win_decode_table_300", "win_tnd_prefill_direct"])
+def test_bounded_windowed_graph_replay(ora, name):
+    """A windowed bounded run captured once, replayed with other key lengths
+    (and TND prefix sums): the windows follow each row's new position; every
+    replay equals qli_plan + qli_run and the oracle."""
+    import dataclasses
+    import torch
+    spec = BOUNDED_WINDOWED[name]
+    bound = int(max(spec.aslk))
+    spec = dataclasses.replace(spec, aslk=[bound] * spec.batch)  # every batch's cache holds the bound
+    inp = synth.make_inputs(spec, 18)
+    p = inp["problem"]
+    dev = device_inputs(inp)
+    tnd = p["layout_query"] == synth.TND
+    bix = qli_mod().BoundedIndexer(p, bound)
+    k = torch.tensor([bound] * p["batch"], dtype=torch.int32, device="cuda")
+    q = torch.tensor(inp["aslq"], dtype=torch.int32, device="cuda") if tnd else None
+    idx, val = bix.alloc_outputs()
+    args = (k, dev["query"], dev["key"], dev["weights"], dev["q_scale"], dev["k_scale"], dev["block_table"], idx, val)
+    bix.run(*args, aslq_dev=q)  # first launches outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bix.run(*args, aslq_dev=q)
+    rng = np.random.default_rng(19)
+    for rep in range(3):
+        lens = [int(x) for x in rng.integers(0, bound + 1, size=p["batch"])]
+        lens[0] = bound if rep == 0 else lens[0]
+        sub = dict(inp, aslk=np.asarray(lens, dtype=np.int32))
+        if tnd:
+            cuts = np.sort(rng.integers(0, p["s1"] + 1, size=p["batch"]))
+            sub["aslq"] = cuts.astype(np.int32)
+            q.copy_(torch.from_numpy(sub["aslq"]))
+        k.copy_(torch.tensor(lens, dtype=torch.int32))
+        idx.fill_(-7)
+        val.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        p_idx, p_val, _ = run_gpu(sub, dev)
+        assert np.array_equal(idx.cpu().numpy(), p_idx), "replay %d" % rep
+        assert np.array_equal(val.cpu().numpy(), p_val), "replay %d" % rep
+        check_windowed(ora, sub, idx.cpu().numpy(), val.cpu().numpy())
 
 
 # --- score-ordered output (sort_output = 1) -----------------------------------
