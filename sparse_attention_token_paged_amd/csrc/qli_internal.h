@@ -43,10 +43,10 @@ struct PlanHeader {
   int64_t off_items;         // byte offset of Item[n_items]
   int64_t off_select;        // byte offset of SelectEntry[n_select]
   int32_t kind;              // PlanKind
-  int32_t rows_per_item;     // 1, 2, 4 (decode) or 8 (prefill)
+  int32_t rows_per_item;     // 1, 2 or 4
   int32_t n_items;
   int32_t n_select;
-  int32_t chunk;             // keys per work item
+  int32_t chunk;             // the chunk rule's length: no work item covers more keys
   int32_t max_vis;
   int32_t reserved1;
   int32_t max_cand;          // largest candidate count of a pass-1 selection

@@ -182,6 +182,36 @@ PLAN_CASES = [
 ]
 
 
+@pytest.mark.parametrize("equal", [False, True])
+def test_plan_items_of_ragged_batches_fill_the_slots(qli, equal):
+    """64 one-row batches of 4k..64k keys (the ragged fp8 decode shape): each
+    batch's entries are cut into near-equal runs of 128-entry blocks, none
+    longer than the chunk, and the free decode slots (768) go to the batches
+    with the longest items, so every slot holds an item.  Equal batches keep
+    whole chunks and a remainder."""
+    spec = synth.small(qk=synth.FP8, batch=2, s1=1, aslk=[100, 100], block_size=64, sparse_count=2048)
+    p = dict(synth.make_inputs(spec, 1)["problem"], batch=64, max_blocks_per_seq=1024, num_blocks=1 << 16)
+    rng = np.random.default_rng(7)
+    aslk = np.full(64, 50000, np.int32) if equal else rng.integers(4096, 65537, size=64).astype(np.int32)
+    rc, plan, _ = qli.qli_plan(qli.Problem.from_dict(p), None, aslk)
+    assert rc == 0
+    h, rows, items, _ = parse(plan)
+    chunk = int(h["chunk"])
+    assert items["nkeys"].max() <= chunk
+    for b in range(64):
+        it = np.sort(items[items["batch"] == b], order="key0")
+        n = it["nkeys"]
+        assert it["key0"][0] == 0 and np.array_equal(it["key0"][1:], np.cumsum(n)[:-1])
+        assert n.sum() == aslk[b]
+        if equal:
+            assert np.all(n[:-1] == chunk)
+        else:
+            assert np.all(n[:-1] % 128 == 0) and (len(n) < 3 or n[:-1].max() - n[:-1].min() <= 128)
+    if not equal:
+        assert h["n_items"] == DECODE_SLOTS                         # every slot holds an item
+        assert sum(-(-int(v) // chunk) for v in aslk) < DECODE_SLOTS  # whole chunks would leave some free
+
+
 @pytest.mark.parametrize("spec", PLAN_CASES, ids=range(len(PLAN_CASES)))
 def test_plan_covers_each_visible_pair_once(qli, ora, spec):
     inp = synth.make_inputs(spec, 3)
