@@ -1225,12 +1225,15 @@ struct SelectParams {
   int32_t* idx_out;
   float* val_out;
   int32_t k;
-  // Bounded decode (aslk != null): no table; workgroup w of pass 1 takes
-  // segment w % nseg of row w / nseg, workgroup r of pass 2 the merge of row r.
+  // Bounded runs (aslk != null): no table; workgroup w of pass 1 takes
+  // segment w / nrows of row w % nrows (every row's first segment, which exists
+  // whenever the row is staged, is dispatched before any later one), workgroup
+  // r of pass 2 the merge of row r.
   const int32_t* aslk;
   int64_t max_len, stride, mstride, merge_base;
   int32_t pre, next;  // pre_tokens, next_tokens clamped to kWindowCap
   int32_t s1, mode, cmp, nseg, pass;
+  int32_t nrows;      //   output rows
   const int32_t* rows_end;   // bounded TND of many batches: the tables (TndTables), else null
   const int32_t* row_batch;
   const int32_t* aslq_tnd;   // bounded TND of few batches: the device prefix sums, else null
@@ -1246,8 +1249,8 @@ struct SelectParams {
 // kSelSegment >= k scores).
 __device__ __forceinline__ bool bounded_entry(const SelectParams& S, SelectEntry& se) {
   const int w = (int)blockIdx.x;
-  const int r = S.pass == 1 ? w / S.nseg : w;
-  const int s = S.pass == 1 ? w - r * S.nseg : 0;
+  const int s = S.pass == 1 ? w / S.nrows : 0;  // segment-major: every row's first segment goes first
+  const int r = S.pass == 1 ? w - s * S.nrows : w;
   int b, i, s1b;
   if (S.aslq_tnd) {  // TND of few batches: the row's batch derived by each wave
     int e0, e1;
@@ -1644,6 +1647,7 @@ int launch_select(const RunArgs& a) {
   S.mstride = a.mstride;
   S.merge_base = a.merge_base;
   S.s1 = a.p->s1;
+  S.nrows = (int32_t)h->rows;
   S.mode = a.p->sparse_mode;
   S.cmp = a.p->cmp_ratio;
   S.pre = window_side(a.p->pre_tokens);
