@@ -1045,6 +1045,13 @@ BOUNDED_WINDOWED["win_decode_table_300"] = synth.small(
 # prefill groups whose windows start past several chunks of the bound
 BOUNDED_WINDOWED["win_prefill_far_start"] = synth.small(batch=2, s1=24, aslk=[9000, 6000], block_size=128,
                                                         sparse_count=256, sparse_mode=3, pre_tokens=600)
+# TND of more than 128 batches (the table kernel's partition) under a window, mode 0 with a lookahead
+_tnd_counts = np.random.default_rng(62).integers(0, 4, size=160)
+_tnd_counts[7] = 9
+BOUNDED_WINDOWED["win_tnd_table_160"] = synth.small(
+    layout=synth.TND, batch=160, s1=int(_tnd_counts.sum()), aslq=[int(x) for x in np.cumsum(_tnd_counts)],
+    aslk=[int(x) for x in np.random.default_rng(63).integers(0, 2500, size=160)], block_size=32,
+    sparse_count=96, sparse_mode=0, pre_tokens=400, next_tokens=30)
 
 
 def bounded_windowed_run(inp, dev, lens, bound, aslq=None):
